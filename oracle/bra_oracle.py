@@ -1,0 +1,216 @@
+"""Plain fp64 CPU oracle of the Bi-Level Routing Attention (BRA) forward pass.
+
+TEST INFRASTRUCTURE ONLY. This module is the checker the GPU path is compared
+against. Only the test suite, the smoke check and the benchmark's CPU-baseline
+leg may import it; the product path never does. It shares no code with the
+HIP kernels or their host library, and imports nothing from that package.
+
+What it computes follows the walk-through of the authors' code at
+TRANSFORMER.niftyadmin.cn/n/347023.html, section "BRA模块" (the equation bodies
+of the paper are lost from that page; the code lines it pairs with Eq. 3-7 and
+with Algorithm 1 survive), and page bernice.tw/posts/biformer, section
+"Bi-Level Routing Attention" (its three parts: region partition, region-to-
+region routing, token-to-token attention plus LCE).
+
+Every step is written the plain way, in float64, in the page's order:
+
+1. region partition      "n (j h) (i w) c -> n (j i) h w c"   (Algorithm 1)
+2. region means          mean over each region's tokens        (Q^r, K^r)
+3. region affinity       A = (Q^r * C^-1/2) @ K^r^T            (Eq. 4)
+4. top-k routing         indices of the topk largest A per row (Eq. 5)
+5. key/value gather      routed regions' tokens, rank-major    (Eq. 6)
+6. token attention       per head softmax(q k^T hd^-1/2) v     (Eq. 7, 1st term)
+7. LCE                   5x5 depthwise conv of V, zero pad 2   (Eq. 7, 2nd term)
+8. merge                 out = attention + LCE
+
+Readings taken where the pages are silent or garbled (each also listed in the
+design notes of the repository):
+* routing scale is C^-1/2 and attention scale head_dim^-1/2;
+* one routing for all heads (the walk-through's route index has no head axis);
+* the routing weights (softmax of the top-k logits) are not applied to the
+  gathered keys/values: the gather is a pure index gather;
+* top-k order is descending logit, exact ties go to the lower region index;
+* the softmax runs jointly over all topk * T gathered keys;
+* LCE runs on V over the whole re-assembled image (not per region), with zero
+  padding and a bias, as a cross-correlation (no kernel flip), like a
+  Conv2d(C, C, 5, padding=2, groups=C);
+* H and W must be divisible by S (no padding branch);
+* the key/value downsampling hook is the identity and qk_dim = C.
+
+Parity pins for every function live in tests/test_oracle.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "check_shapes", "partition", "unpartition", "region_means",
+    "region_affinity", "topk_routes", "gather_regions", "token_attention",
+    "lce", "bra_forward",
+]
+
+
+def check_shapes(N, H, W, C, heads, S, topk):
+    """Preconditions: the walk-through asserts H % S == 0 and W % S == 0
+    (section BRA模块); the head split "(m c)" needs C % heads == 0; top-k needs
+    1 <= topk <= S^2."""
+    if min(N, H, W, C, heads, S) <= 0:
+        raise ValueError("sizes must be positive")
+    if H % S or W % S:
+        raise ValueError("H and W must be divisible by S")
+    if C % heads:
+        raise ValueError("C must be divisible by heads")
+    if not 1 <= topk <= S * S:
+        raise ValueError("topk must lie in [1, S*S]")
+
+
+def partition(x: np.ndarray, S: int) -> np.ndarray:
+    """Algorithm 1 "patchify": (N, H, W, C) -> (N, S*S, (H/S)*(W/S), C).
+
+    Region r = j*S + i, with j the region row (along H) and i the region column;
+    inside a region the tokens are row-major, t = y'*(W/S) + x'. This is the
+    walk-through's rearrange "n (j h) (i w) c -> n (j i) h w c" followed by
+    "n p2 h w c -> n p2 (h w) c"."""
+    N, H, W, C = x.shape
+    rh, rw = H // S, W // S
+    y = x.reshape(N, S, rh, S, rw, C)          # n j h i w c
+    y = y.transpose(0, 1, 3, 2, 4, 5)          # n j i h w c
+    return y.reshape(N, S * S, rh * rw, C)
+
+
+def unpartition(xp: np.ndarray, S: int, H: int, W: int) -> np.ndarray:
+    """Inverse of `partition`: (N, S*S, T, C) -> (N, H, W, C), the walk-through's
+    "(n j i) m (h w) c -> n (j h) (i w) (m c)" without the head axis."""
+    N, R, T, C = xp.shape
+    rh, rw = H // S, W // S
+    y = xp.reshape(N, S, S, rh, rw, C)          # n j i h w c
+    y = y.transpose(0, 1, 3, 2, 4, 5)           # n j h i w c
+    return y.reshape(N, H, W, C)
+
+
+def region_means(xp: np.ndarray) -> np.ndarray:
+    """Q^r or K^r: the mean over each region's tokens, per channel -- "not an
+    average over channels but over the region's vectors" (section BRA模块,
+    q_win / k_win). (N, R, T, C) -> (N, R, C)."""
+    return xp.sum(axis=2) / xp.shape[2]
+
+
+def region_affinity(qr: np.ndarray, kr: np.ndarray) -> np.ndarray:
+    """Eq. 4: A = (Q^r * scale) @ K^r^T with scale = C^-1/2; the routing
+    embedding is the identity. (N, R, C) x (N, R, C) -> (N, R, R)."""
+    C = qr.shape[-1]
+    return (qr * (1.0 / np.sqrt(C))) @ np.swapaxes(kr, -1, -2)
+
+
+def topk_routes(A: np.ndarray, topk: int) -> np.ndarray:
+    """Eq. 5: per row, the indices of the topk largest affinities, in
+    descending order of affinity; equal affinities keep the lower region index
+    first (a stable sort on the negated key). (N, R, R) -> (N, R, topk) int."""
+    order = np.argsort(-A, axis=-1, kind="stable")
+    return order[..., :topk].astype(np.int64)
+
+
+def gather_regions(xp: np.ndarray, route: np.ndarray) -> np.ndarray:
+    """Eq. 6: for every query region, the tokens of its routed regions,
+    concatenated rank-major, token-minor (the "(k w2)" order of the
+    walk-through). (N, R, T, C), (N, R, topk) -> (N, R, topk*T, C)."""
+    N, R, T, C = xp.shape
+    g = xp[np.arange(N)[:, None, None], route]       # (N, R, topk, T, C)
+    return g.reshape(N, R, route.shape[-1] * T, C)
+
+
+def token_attention(qp: np.ndarray, kg: np.ndarray, vg: np.ndarray, heads: int,
+                    return_probs: bool = False):
+    """Eq. 7, first term: multi-head softmax attention of each region's
+    queries over its gathered keys/values. Head m owns channels
+    [m*hd, (m+1)*hd) (the "(m c)" split); scores are (q * hd^-1/2) @ k^T; the
+    softmax runs over the last axis, i.e. jointly over all gathered keys.
+    qp (N, R, T, C), kg/vg (N, R, L, C) -> (N, R, T, C)."""
+    N, R, T, C = qp.shape
+    hd = C // heads
+    scale = 1.0 / np.sqrt(hd)
+    out = np.empty_like(qp)
+    probs = [] if return_probs else None
+    for m in range(heads):
+        sl = slice(m * hd, (m + 1) * hd)
+        s = (qp[..., sl] * scale) @ np.swapaxes(kg[..., sl], -1, -2)   # (N,R,T,L)
+        s = s - s.max(axis=-1, keepdims=True)
+        e = np.exp(s)
+        p = e / e.sum(axis=-1, keepdims=True)
+        out[..., sl] = p @ vg[..., sl]
+        if return_probs:
+            probs.append(p)
+    if return_probs:
+        return out, probs
+    return out
+
+
+def lce(v: np.ndarray, w: np.ndarray, b: np.ndarray | None) -> np.ndarray:
+    """Eq. 7, second term, LCE(V): a 5x5 depthwise convolution of V over the
+    whole (N, H, W, C) map, stride 1, zero padding 2, plus a per-channel bias
+    -- the Conv2d(C, C, kernel_size=5, padding=2, groups=C) of the module
+    print (section 网络结构). Cross-correlation orientation:
+    l[n,y,x,c] = b[c] + sum_{a,e in 0..4} w[c,a,e] * v[n, y+a-2, x+e-2, c]."""
+    N, H, W, C = v.shape
+    vp = np.zeros((N, H + 4, W + 4, C))
+    vp[:, 2:H + 2, 2:W + 2, :] = v
+    out = np.zeros((N, H, W, C))
+    for a in range(5):
+        for e in range(5):
+            out += w[:, a, e] * vp[:, a:a + H, e:e + W, :]
+    if b is not None:
+        out += b
+    return out
+
+
+def bra_forward(q, k, v, lce_w, lce_b, heads: int, S: int, topk: int,
+                route_override: np.ndarray | None = None,
+                return_probs: bool = False):
+    """The whole forward pass on float64 copies of the inputs.
+
+    q, k, v: (N, H, W, C); lce_w: (C, 5, 5); lce_b: (C,) or None.
+    route_override: optional (N, S*S, topk) route indices to use instead of
+    the ones this oracle selects (the near-tie protocol feeds the GPU's
+    choice back here).
+    Returns a dict with "out" (N,H,W,C), "route_idx" (N,R,topk) (the routes
+    actually used), "route_oracle" (the oracle's own choice), "logits"
+    (N,R,R) and, if asked, "probs" (per image, per head (R,T,L)).
+
+    Images are independent (routing never crosses images), so the attention
+    is evaluated one image at a time to bound memory."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    N, H, W, C = q.shape
+    check_shapes(N, H, W, C, heads, S, topk)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    w = np.asarray(lce_w, dtype=np.float64).reshape(C, 5, 5)
+    b = None if lce_b is None else np.asarray(lce_b, dtype=np.float64).reshape(C)
+
+    qp, kp, vp = partition(q, S), partition(k, S), partition(v, S)
+    A = region_affinity(region_means(qp), region_means(kp))
+    route_own = topk_routes(A, topk)
+    if route_override is not None:
+        route = np.asarray(route_override, dtype=np.int64).reshape(N, S * S, topk)
+        if route.min() < 0 or route.max() >= S * S:
+            raise ValueError("route_override holds an index outside [0, S*S)")
+    else:
+        route = route_own
+
+    att = np.empty_like(qp)
+    probs = [] if return_probs else None
+    for n in range(N):
+        kg = gather_regions(kp[n:n + 1], route[n:n + 1])
+        vg = gather_regions(vp[n:n + 1], route[n:n + 1])
+        res = token_attention(qp[n:n + 1], kg, vg, heads, return_probs)
+        if return_probs:
+            att[n:n + 1], pr = res
+            probs.append([p[0] for p in pr])
+        else:
+            att[n:n + 1] = res
+    out = unpartition(att, S, H, W) + lce(v, w, b)
+    res = {"out": out, "route_idx": route, "route_oracle": route_own, "logits": A}
+    if return_probs:
+        res["probs"] = probs
+    return res
