@@ -1,0 +1,149 @@
+/*
+ * bra.h -- C ABI of the MI355X (gfx950) Bi-Level Routing Attention forward pass.
+ *
+ * The operation is the BRA operator of BiFormer as walked through at
+ * TRANSFORMER.niftyadmin.cn/n/347023.html, section "BRA模块" (Algorithm 1 and
+ * Eqs. 3-7 of the paper, whose code survives on that page), and summarised on
+ * bernice.tw/posts/biformer, section "Bi-Level Routing Attention":
+ *
+ *   1. partition the (H, W) map into S x S regions of T = (H/S)(W/S) tokens;
+ *      region r = j*S + i (j along H), tokens row-major inside a region;
+ *   2. Q^r, K^r = per-region means of q and k over the region's tokens;
+ *   3. A = (Q^r * C^-1/2) K^r^T, an S^2 x S^2 region affinity (Eq. 4);
+ *   4. route_idx = per-row indices of the topk largest A, descending, exact
+ *      ties to the lower region index (Eq. 5);
+ *   5. each query region gathers the tokens of its routed regions (Eq. 6);
+ *   6. per head (channels [h*hd, (h+1)*hd), hd = C/heads), softmax attention
+ *      of the region's queries over all topk*T gathered keys, scale hd^-1/2
+ *      (Eq. 7, first term);
+ *   7. LCE(V): 5x5 depthwise cross-correlation of v over the whole image,
+ *      zero padding 2, plus bias (Eq. 7, second term; the Conv2d(C, C, 5,
+ *      padding=2, groups=C) of the module print);
+ *   8. out = attention + LCE, rounded once to the storage dtype.
+ *
+ * The query/key/value projections and the output projection that surround
+ * the operator in BiFormer are not part of this call: q, k, v are inputs.
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are caller-owned DEVICE pointers (hipMalloc'd or a
+ *     framework tensor's data pointer) of contiguous arrays. Host pointers are
+ *     rejected with BRA_ERR_POINTER.
+ *   - q, k, v, out are NHWC: [N][H][W][C] of `dtype`.
+ *   - lce_w is [C][5][5] of `dtype` (a depthwise Conv2d weight (C,1,5,5)
+ *     flattened); lce_b is [C] of `dtype`, or NULL for a zero bias.
+ *   - route_idx is int32 [N][S*S][topk], each row in descending-affinity order.
+ *   - Outputs must not alias inputs.
+ *   - Work is enqueued asynchronously on the stream set by bra_set_stream
+ *     (per host thread; the null stream by default). No entry point
+ *     synchronises the device; kernel faults surface at the caller's next
+ *     synchronisation.
+ *   - Every argument check runs before any launch. On a non-zero return no
+ *     work was enqueued (except BRA_ERR_HIP, which reports a failed launch or
+ *     allocation) and the outputs are untouched.
+ *
+ * Compiled envelope: head_dim = C/heads = 32 (every BiFormer stage), S*S <=
+ * 1024, topk * T <= 65536. Outside it the calls return BRA_ERR_UNSUPPORTED.
+ */
+#ifndef BRA_H_
+#define BRA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum bra_dtype {
+  BRA_F32 = 0,  /* IEEE binary32 */
+  BRA_BF16 = 1  /* bfloat16 (attention products on bf16 matrix cores) */
+};
+
+enum bra_status {
+  BRA_OK = 0,
+  BRA_ERR_NULL = -1,        /* a required pointer is NULL */
+  BRA_ERR_SHAPE = -2,       /* a size <= 0, H % S, W % S or C % heads != 0 */
+  BRA_ERR_TOPK = -3,        /* topk outside [1, S*S] */
+  BRA_ERR_DTYPE = -4,       /* unknown dtype */
+  BRA_ERR_UNSUPPORTED = -5, /* outside the compiled envelope (see above) */
+  BRA_ERR_HIP = -6,         /* a HIP launch or allocation failed */
+  BRA_ERR_POINTER = -7      /* a tensor pointer is not device memory */
+};
+
+/* The whole forward pass, steps 1-8 above.
+ * Uses a library-owned fp32 workspace of bra_workspace_bytes(N, C, S) bytes
+ * per device (grow-only, allocated on first need, freed by bra_release).
+ * Calls on one device that use the library workspace must not overlap: the
+ * library serialises them on the host, but two streams would race on the
+ * device. */
+int bra_forward(const void* q, const void* k, const void* v,
+                const void* lce_w, const void* lce_b,
+                int N, int H, int W, int C, int heads, int S, int topk,
+                int dtype, void* out, int32_t* route_idx);
+
+/* Step 2 alone: qr, kr = region means of q and k, fp32 [N][S*S][C] each
+ * (caller-owned device buffers). Same checks as bra_forward (heads and topk
+ * are not involved). */
+int bra_region_means(const void* q, const void* k, int N, int H, int W, int C,
+                     int S, int dtype, float* qr, float* kr);
+
+/* Steps 3-4 alone: route_idx [N][R][topk] from fp32 region means qr, kr
+ * [N][R][C] (R = S*S, R <= 1024). */
+int bra_route(const float* qr, const float* kr, int N, int R, int C, int topk,
+              int32_t* route_idx);
+
+/* Steps 5-8 with given routes: out = attention over the regions listed in
+ * route_idx [N][S*S][topk] (device, int32, every entry in [0, S*S); entries
+ * are not checked on the device and an index outside that range is undefined
+ * behaviour) plus LCE. */
+int bra_attend(const void* q, const void* k, const void* v,
+               const void* lce_w, const void* lce_b, const int32_t* route_idx,
+               int N, int H, int W, int C, int heads, int S, int topk,
+               int dtype, void* out);
+
+/* Step 7 alone: LCE(v) into a caller-owned fp32 buffer [N][H][W][C]. */
+int bra_lce(const void* v, const void* lce_w, const void* lce_b,
+            int N, int H, int W, int C, int dtype, float* out);
+
+/* Stream used by every later call from this host thread (a hipStream_t;
+ * NULL = the null stream). Always returns BRA_OK. */
+int bra_set_stream(void* stream);
+void* bra_get_stream(void);
+
+/* Bytes of library workspace bra_forward needs: two fp32 [N][S*S][C]
+ * arrays (region means). Returns 0 for invalid sizes. */
+size_t bra_workspace_bytes(int N, int C, int S);
+
+/* Frees the library workspace of every device (synchronises each device
+ * that holds one first). The next bra_forward allocates again. */
+void bra_release(void);
+
+/* Static text for a status code; for BRA_ERR_HIP it includes the last HIP
+ * error seen by this thread. */
+const char* bra_error_string(int code);
+
+/* Library version: 100 * major + minor. */
+int bra_version(void);
+
+/* Per-kernel timing with HIP events recorded on the launch stream.
+ * bra_profile_begin(1) starts recording (up to 4096 launches per kernel
+ * kind, later ones are not recorded); bra_profile_read synchronises the
+ * stream, then writes for each kernel kind k < n (BRA_K_* below) the summed
+ * milliseconds and the launch count, and clears the record. bra_profile_begin(0)
+ * stops recording. */
+enum bra_kernel_kind {
+  BRA_K_POOL = 0, BRA_K_ROUTE = 1, BRA_K_ATTN = 2, BRA_K_LCE = 3, BRA_K_COUNT = 4
+};
+int bra_profile_begin(int enable);
+int bra_profile_read(double* ms, int* counts, int n);
+
+/* A plain device-to-device copy kernel (bytes % 16 == 0, both pointers
+ * 16-byte aligned), used to calibrate hardware byte counters against a
+ * kernel of known traffic. */
+int bra_calib_copy(const void* src, void* dst, size_t bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BRA_H_ */

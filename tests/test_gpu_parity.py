@@ -1,0 +1,206 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Every case prints its name before touching the GPU. Inputs come from the
+seeded generator in synth/, which both sides read bit for bit.
+"""
+from __future__ import annotations
+
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import bra_oracle as O
+from synth import CONFIGS, draw, draw_config
+from tests.parity import check_output, compare_routes
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+def dev(x, dtype):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.float32)))
+    return t.to(device="cuda", dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+
+
+def host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.float().cpu().numpy().astype(np.float64) if t.is_floating_point() else t.cpu().numpy()
+
+
+def oracle_routing(inp, S, topk):
+    A = O.region_affinity(O.region_means(O.partition(inp["q"], S)),
+                          O.region_means(O.partition(inp["k"], S)))
+    return A, O.topk_routes(A, topk)
+
+
+def run_forward(bra, inp, heads, S, topk, dtype, images=None, name=""):
+    say(name, "forward", inp["q"].shape, f"heads={heads} S={S} topk={topk} {dtype}")
+    out, route = bra.forward(dev(inp["q"], dtype), dev(inp["k"], dtype), dev(inp["v"], dtype),
+                             dev(inp["lce_w"], dtype), dev(inp["lce_b"], dtype), heads, S, topk)
+    out, route = host(out), host(route)
+    A, own = oracle_routing(inp, S, topk)
+    exact, near, fails = compare_routes(route, A, own)
+    assert not fails, fails[:5]
+    N = inp["q"].shape[0]
+    imgs = list(range(N)) if images is None else images
+    ref = oracle.bra_forward(inp["q"][imgs], inp["k"][imgs], inp["v"][imgs], inp["lce_w"],
+                             inp["lce_b"], heads, S, topk, route_override=route[imgs])
+    rep = check_output(out[imgs], ref["out"], dtype)
+    rep.update(exact_rows=exact, near_tie_rows=near)
+    say(name, rep)
+    return out, route, rep
+
+
+SMALL_CASES = [
+    # name, N, H, W, C, heads, S, topk, dtype, offset_std
+    ("c1_like_b2", 2, 28, 28, 128, 4, 7, 4, "bf16", 0.0),
+    ("c2_like_b3", 3, 14, 14, 256, 8, 7, 16, "bf16", 0.0),
+    ("t64_l192", 1, 32, 32, 64, 2, 4, 3, "bf16", 0.7),
+    ("t256_l512", 1, 64, 64, 64, 2, 4, 2, "bf16", 0.7),
+    ("ragged_t6_l18", 2, 15, 10, 64, 2, 5, 3, "bf16", 0.0),
+    ("t20_qblocks", 1, 20, 25, 64, 2, 5, 2, "bf16", 0.0),
+    ("t1_single_token", 1, 8, 8, 32, 1, 8, 5, "bf16", 0.0),
+    ("dense_topk_eq_R", 1, 12, 12, 64, 2, 3, 9, "bf16", 0.0),
+    ("s1_one_region", 2, 8, 8, 32, 1, 1, 1, "bf16", 0.0),
+    ("nonsquare_t24", 1, 16, 24, 96, 3, 4, 5, "bf16", 0.0),
+    ("r1024_router", 1, 32, 32, 32, 1, 32, 16, "bf16", 0.0),
+    ("r400_router", 1, 40, 40, 64, 2, 20, 7, "bf16", 0.7),
+    ("f32_c0_like", 1, 56, 56, 64, 2, 7, 1, "f32", 0.0),
+    ("f32_ragged", 2, 15, 10, 64, 2, 5, 3, "f32", 0.0),
+    ("f32_t256", 1, 64, 64, 64, 2, 4, 2, "f32", 0.7),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
+def test_forward_small(gpu_lib, case):
+    name, N, H, W, C, heads, S, topk, dtype, off = case
+    inp = draw(N, H, W, C, S, dtype, seed=zlib.crc32(name.encode()) % 10000, offset_std=off)
+    run_forward(gpu_lib, inp, heads, S, topk, dtype, name=name)
+
+
+# Full-size workloads, the launch configuration the benchmark times; the
+# oracle evaluates a sample of the images (images are independent), routes
+# are checked on every image.
+FULL_SAMPLE = {"c0": [0], "c1": [0, 77, 127], "c2": [0, 64, 127], "c3": [0, 1], "c4": [0, 7]}
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=[c.name for c in CONFIGS])
+def test_forward_full_config(gpu_lib, cfg):
+    inp = draw_config(cfg)
+    run_forward(gpu_lib, inp, cfg.heads, cfg.S, cfg.topk, cfg.dtype,
+                images=FULL_SAMPLE[cfg.name], name=cfg.name)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=[c.name for c in CONFIGS])
+def test_region_means(gpu_lib, cfg):
+    inp = draw_config(cfg, N=min(cfg.N, 4))
+    say(cfg.name, "region_means")
+    qr, kr = gpu_lib.region_means(dev(inp["q"], cfg.dtype), dev(inp["k"], cfg.dtype), cfg.S)
+    qr, kr = host(qr), host(kr)
+    want_q = O.region_means(O.partition(inp["q"], cfg.S))
+    want_k = O.region_means(O.partition(inp["k"], cfg.S))
+    assert np.allclose(qr, want_q, rtol=1e-5, atol=1e-6), np.abs(qr - want_q).max()
+    assert np.allclose(kr, want_k, rtol=1e-5, atol=1e-6), np.abs(kr - want_k).max()
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=[c.name for c in CONFIGS])
+def test_router_from_oracle_means(gpu_lib, cfg):
+    """Routing alone, fed the oracle's means rounded to fp32."""
+    import torch
+    inp = draw_config(cfg, N=min(cfg.N, 8))
+    qr = O.region_means(O.partition(inp["q"], cfg.S)).astype(np.float32)
+    kr = O.region_means(O.partition(inp["k"], cfg.S)).astype(np.float32)
+    say(cfg.name, "route")
+    ri = host(gpu_lib.route(torch.from_numpy(qr).cuda(), torch.from_numpy(kr).cuda(), cfg.topk))
+    A = O.region_affinity(qr.astype(np.float64), kr.astype(np.float64))
+    exact, near, fails = compare_routes(ri, A, O.topk_routes(A, cfg.topk))
+    assert not fails, fails[:5]
+
+
+@pytest.mark.parametrize("case", [SMALL_CASES[i] for i in (0, 1, 2, 4, 12)], ids=lambda c: c[0])
+def test_attend_with_oracle_routes(gpu_lib, case):
+    """Attention + LCE alone, on the oracle's own routes."""
+    import torch
+    name, N, H, W, C, heads, S, topk, dtype, off = case
+    inp = draw(N, H, W, C, S, dtype, seed=7 + zlib.crc32(name.encode()) % 1000, offset_std=off)
+    ref = oracle.bra_forward(inp["q"], inp["k"], inp["v"], inp["lce_w"], inp["lce_b"], heads, S, topk)
+    say(name, "attend")
+    out = gpu_lib.attend(dev(inp["q"], dtype), dev(inp["k"], dtype), dev(inp["v"], dtype),
+                         dev(inp["lce_w"], dtype), dev(inp["lce_b"], dtype),
+                         torch.from_numpy(ref["route_idx"].astype(np.int32)).cuda(), heads, S)
+    check_output(host(out), ref["out"], dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_lce_alone(gpu_lib, dtype):
+    inp = draw(2, 20, 12, 96, 4, dtype, seed=55)
+    say("lce", dtype)
+    got = host(gpu_lib.lce(dev(inp["v"], dtype), dev(inp["lce_w"], dtype), dev(inp["lce_b"], dtype)))
+    want = O.lce(inp["v"], inp["lce_w"], inp["lce_b"])
+    assert np.allclose(got, want, rtol=0, atol=2e-5), np.abs(got - want).max()
+    say("lce no bias", dtype)
+    got = host(gpu_lib.lce(dev(inp["v"], dtype), dev(inp["lce_w"], dtype), None))
+    want = O.lce(inp["v"], inp["lce_w"], None)
+    assert np.allclose(got, want, rtol=0, atol=2e-5)
+
+
+def test_exact_ties_go_to_lower_index(gpu_lib):
+    """Bit-identical regions of k tie exactly on both sides: the lower index
+    must win, with no near-tie slack."""
+    N, H, W, C, heads, S = 2, 16, 16, 64, 2, 4
+    inp = draw(N, H, W, C, S, "bf16", seed=99)
+    k = inp["k"]
+    k[:, 4:8, 8:12, :] = k[:, 0:4, 4:8, :]      # region 6 := region 1
+    k[:, 12:16, 0:4, :] = k[:, 0:4, 4:8, :]     # region 12 := region 1
+    say("ties")
+    _, route = gpu_lib.forward(dev(inp["q"], "bf16"), dev(k, "bf16"), dev(inp["v"], "bf16"),
+                              dev(inp["lce_w"], "bf16"), None, heads, S, 16)
+    route = host(route)
+    for n in range(N):
+        for r in range(16):
+            lst = list(route[n, r])
+            assert sorted(lst) == list(range(16))
+            assert lst.index(1) < lst.index(6) < lst.index(12), (n, r, lst)
+
+
+def test_deterministic(gpu_lib):
+    cfg = CONFIGS[1]
+    inp = draw_config(cfg, N=16)
+    args = [dev(inp[x], cfg.dtype) for x in ("q", "k", "v", "lce_w", "lce_b")]
+    say("determinism")
+    o1, r1 = gpu_lib.forward(*args, cfg.heads, cfg.S, cfg.topk)
+    o2, r2 = gpu_lib.forward(*args, cfg.heads, cfg.S, cfg.topk)
+    import torch
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(r1, r2)
+
+
+def test_host_pointer_rejected(gpu_lib):
+    import ctypes
+    lib = gpu_lib.load()
+    buf = np.zeros(8 * 8 * 32, dtype=np.float32)
+    hp = ctypes.c_void_p(buf.ctypes.data)
+    say("host pointer")
+    assert lib.bra_lce(hp, hp, None, 1, 8, 8, 32, 0, hp) == -7
+
+
+def test_profile_counts(gpu_lib):
+    cfg = CONFIGS[1]
+    inp = draw_config(cfg, N=4)
+    args = [dev(inp[x], cfg.dtype) for x in ("q", "k", "v", "lce_w", "lce_b")]
+    say("profile")
+    gpu_lib.profile_begin(True)
+    for _ in range(3):
+        gpu_lib.forward(*args, cfg.heads, cfg.S, cfg.topk)
+    rec = gpu_lib.profile_read()
+    gpu_lib.profile_begin(False)
+    assert rec["pool"][1] == 3 and rec["route"][1] == 3 and rec["attn"][1] == 3
+    assert rec["attn"][0] > 0

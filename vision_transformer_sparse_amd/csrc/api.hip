@@ -1,0 +1,344 @@
+// Host side of the C ABI declared in include/bra.h: argument checks, the
+// library-owned workspace, stream selection, kernel dispatch, error text and
+// event-based per-kernel timing. No kernel lives here.
+#include "../../include/bra.h"
+
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "bra_internal.h"
+
+namespace bra {
+hipError_t launch_attend_valu(const void* q, const void* k, const void* v,
+                              const void* w, const void* b, const int32_t* route,
+                              const Shape& s, int dtype, void* out, hipStream_t st);
+hipError_t launch_attend_mfma(const void* q, const void* k, const void* v,
+                              const void* w, const void* b, const int32_t* route,
+                              const Shape& s, void* out, hipStream_t st);
+bool mfma_supports(const Shape& s);
+}  // namespace bra
+
+namespace {
+
+thread_local hipStream_t g_stream = nullptr;
+thread_local hipError_t g_last_hip = hipSuccess;
+thread_local char g_msg[256];
+
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::vector<Workspace> g_ws;  // indexed by device ordinal
+
+// ---- event timing ---------------------------------------------------------
+constexpr int kMaxEvents = 4096;
+struct KindRecord {
+  std::vector<hipEvent_t> start, stop;
+  int used = 0;
+};
+std::mutex g_prof_mutex;
+bool g_prof_on = false;
+KindRecord g_prof[BRA_K_COUNT];
+
+struct ProfScope {
+  int kind;
+  hipStream_t st;
+  int slot = -1;
+  ProfScope(int kind_, hipStream_t st_) : kind(kind_), st(st_) {
+    if (!g_prof_on) return;
+    std::lock_guard<std::mutex> lk(g_prof_mutex);
+    KindRecord& rec = g_prof[kind];
+    if (rec.used >= kMaxEvents) return;
+    if ((int)rec.start.size() <= rec.used) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess) return;
+      if (hipEventCreate(&b) != hipSuccess) { hipEventDestroy(a); return; }
+      rec.start.push_back(a);
+      rec.stop.push_back(b);
+    }
+    slot = rec.used++;
+    hipEventRecord(rec.start[slot], st);
+  }
+  ~ProfScope() {
+    if (slot >= 0) hipEventRecord(g_prof[kind].stop[slot], st);
+  }
+};
+
+int hip_fail(hipError_t e) {
+  g_last_hip = e;
+  return BRA_ERR_HIP;
+}
+
+int check_dims(int N, int H, int W, int C, int heads, int S, int topk, int dtype,
+               bool use_heads, bool use_topk, bra::Shape* out) {
+  if (dtype != BRA_F32 && dtype != BRA_BF16) return BRA_ERR_DTYPE;
+  if (N <= 0 || H <= 0 || W <= 0 || C <= 0 || S <= 0) return BRA_ERR_SHAPE;
+  if (use_heads && heads <= 0) return BRA_ERR_SHAPE;
+  if (H % S != 0 || W % S != 0) return BRA_ERR_SHAPE;
+  if (use_heads && C % heads != 0) return BRA_ERR_SHAPE;
+  const long long R = (long long)S * S;
+  if (use_topk && (topk < 1 || topk > R)) return BRA_ERR_TOPK;
+  // compiled envelope
+  if (R > bra::kMaxRegions) return BRA_ERR_UNSUPPORTED;
+  if (C % bra::kHeadDim != 0 || C > 1024) return BRA_ERR_UNSUPPORTED;
+  if (use_heads && C / heads != bra::kHeadDim) return BRA_ERR_UNSUPPORTED;
+  const long long T = (long long)(H / S) * (W / S);
+  if (use_topk && T * topk > 65536) return BRA_ERR_UNSUPPORTED;
+  if ((long long)N * H * W * C >= (1ll << 40)) return BRA_ERR_UNSUPPORTED;
+  bra::Shape& s = *out;
+  s.N = N; s.H = H; s.W = W; s.C = C; s.heads = use_heads ? heads : 1;
+  s.S = S; s.topk = use_topk ? topk : 1;
+  s.R = (int)R; s.rh = H / S; s.rw = W / S; s.T = (int)T;
+  s.hd = use_heads ? C / heads : bra::kHeadDim;
+  s.L = s.topk * s.T;
+  return BRA_OK;
+}
+
+// Rejects host or unknown pointers (a kernel dereferencing one would fault).
+int check_device_ptr(const void* p) {
+  if (p == nullptr) return BRA_OK;
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return BRA_ERR_POINTER;
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+    return BRA_ERR_POINTER;
+  return BRA_OK;
+}
+
+int check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps) {
+    int rc = check_device_ptr(p);
+    if (rc) return rc;
+  }
+  return BRA_OK;
+}
+
+int workspace(size_t bytes, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0) return hip_fail(hipErrorInvalidDevice);
+  if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
+  Workspace& ws = g_ws[dev];
+  if (ws.bytes < bytes) {
+    if (ws.ptr) {
+      e = hipDeviceSynchronize();  // earlier calls may still read the old buffer
+      if (e != hipSuccess) return hip_fail(e);
+      (void)hipFree(ws.ptr);
+      ws.ptr = nullptr;
+      ws.bytes = 0;
+    }
+    e = hipMalloc(&ws.ptr, bytes);
+    if (e != hipSuccess) {
+      ws.ptr = nullptr;
+      return hip_fail(e);
+    }
+    ws.bytes = bytes;
+  }
+  *ptr = ws.ptr;
+  return BRA_OK;
+}
+
+int attend(const void* q, const void* k, const void* v, const void* w, const void* b,
+           const int32_t* route, const bra::Shape& s, int dtype, void* out, hipStream_t st) {
+  hipError_t e;
+  {
+    ProfScope ps(BRA_K_ATTN, st);
+    if (dtype == BRA_BF16 && bra::mfma_supports(s))
+      e = bra::launch_attend_mfma(q, k, v, w, b, route, s, out, st);
+    else
+      e = bra::launch_attend_valu(q, k, v, w, b, route, s, dtype, out, st);
+  }
+  return e == hipSuccess ? BRA_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int bra_forward(const void* q, const void* k, const void* v, const void* lce_w,
+                const void* lce_b, int N, int H, int W, int C, int heads, int S,
+                int topk, int dtype, void* out, int32_t* route_idx) {
+  if (!q || !k || !v || !lce_w || !out || !route_idx) return BRA_ERR_NULL;
+  bra::Shape s;
+  int rc = check_dims(N, H, W, C, heads, S, topk, dtype, true, true, &s);
+  if (rc) return rc;
+  rc = check_ptrs({q, k, v, lce_w, lce_b, out, route_idx});
+  if (rc) return rc;
+  std::lock_guard<std::mutex> lk(g_ws_mutex);
+  void* ws = nullptr;
+  rc = workspace(bra_workspace_bytes(N, C, S), &ws);
+  if (rc) return rc;
+  float* qr = static_cast<float*>(ws);
+  float* kr = qr + (size_t)N * s.R * C;
+  hipStream_t st = g_stream;
+  hipError_t e;
+  {
+    ProfScope ps(BRA_K_POOL, st);
+    e = bra::launch_region_pool(q, k, s, dtype, qr, kr, st);
+  }
+  if (e != hipSuccess) return hip_fail(e);
+  {
+    ProfScope ps(BRA_K_ROUTE, st);
+    e = bra::launch_route(qr, kr, N, s.R, C, topk, route_idx, st);
+  }
+  if (e != hipSuccess) return hip_fail(e);
+  return attend(q, k, v, lce_w, lce_b, route_idx, s, dtype, out, st);
+}
+
+int bra_region_means(const void* q, const void* k, int N, int H, int W, int C, int S,
+                     int dtype, float* qr, float* kr) {
+  if (!q || !k || !qr || !kr) return BRA_ERR_NULL;
+  bra::Shape s;
+  int rc = check_dims(N, H, W, C, 1, S, 1, dtype, false, false, &s);
+  if (rc) return rc;
+  rc = check_ptrs({q, k, qr, kr});
+  if (rc) return rc;
+  hipStream_t st = g_stream;
+  hipError_t e;
+  {
+    ProfScope ps(BRA_K_POOL, st);
+    e = bra::launch_region_pool(q, k, s, dtype, qr, kr, st);
+  }
+  return e == hipSuccess ? BRA_OK : hip_fail(e);
+}
+
+int bra_route(const float* qr, const float* kr, int N, int R, int C, int topk,
+              int32_t* route_idx) {
+  if (!qr || !kr || !route_idx) return BRA_ERR_NULL;
+  if (N <= 0 || R <= 0 || C <= 0) return BRA_ERR_SHAPE;
+  if (topk < 1 || topk > R) return BRA_ERR_TOPK;
+  if (R > bra::kMaxRegions || C % bra::kHeadDim != 0 || C > 1024) return BRA_ERR_UNSUPPORTED;
+  int rc = check_ptrs({qr, kr, route_idx});
+  if (rc) return rc;
+  hipStream_t st = g_stream;
+  hipError_t e;
+  {
+    ProfScope ps(BRA_K_ROUTE, st);
+    e = bra::launch_route(qr, kr, N, R, C, topk, route_idx, st);
+  }
+  return e == hipSuccess ? BRA_OK : hip_fail(e);
+}
+
+int bra_attend(const void* q, const void* k, const void* v, const void* lce_w,
+               const void* lce_b, const int32_t* route_idx, int N, int H, int W, int C,
+               int heads, int S, int topk, int dtype, void* out) {
+  if (!q || !k || !v || !lce_w || !route_idx || !out) return BRA_ERR_NULL;
+  bra::Shape s;
+  int rc = check_dims(N, H, W, C, heads, S, topk, dtype, true, true, &s);
+  if (rc) return rc;
+  rc = check_ptrs({q, k, v, lce_w, lce_b, route_idx, out});
+  if (rc) return rc;
+  return attend(q, k, v, lce_w, lce_b, route_idx, s, dtype, out, g_stream);
+}
+
+int bra_lce(const void* v, const void* lce_w, const void* lce_b, int N, int H, int W,
+            int C, int dtype, float* out) {
+  if (!v || !lce_w || !out) return BRA_ERR_NULL;
+  bra::Shape s;
+  int rc = check_dims(N, H, W, C, 1, 1, 1, dtype, false, false, &s);
+  if (rc) return rc;
+  rc = check_ptrs({v, lce_w, lce_b, out});
+  if (rc) return rc;
+  hipStream_t st = g_stream;
+  hipError_t e;
+  {
+    ProfScope ps(BRA_K_LCE, st);
+    e = bra::launch_lce(v, lce_w, lce_b, s, dtype, out, st);
+  }
+  return e == hipSuccess ? BRA_OK : hip_fail(e);
+}
+
+int bra_set_stream(void* stream) {
+  g_stream = static_cast<hipStream_t>(stream);
+  return BRA_OK;
+}
+
+void* bra_get_stream(void) { return g_stream; }
+
+size_t bra_workspace_bytes(int N, int C, int S) {
+  if (N <= 0 || C <= 0 || S <= 0) return 0;
+  return (size_t)2 * N * S * S * C * sizeof(float);
+}
+
+void bra_release(void) {
+  std::lock_guard<std::mutex> lk(g_ws_mutex);
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) cur = -1;
+  for (size_t d = 0; d < g_ws.size(); ++d) {
+    if (!g_ws[d].ptr) continue;
+    if (hipSetDevice((int)d) == hipSuccess) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(g_ws[d].ptr);
+    }
+    g_ws[d].ptr = nullptr;
+    g_ws[d].bytes = 0;
+  }
+  if (cur >= 0) (void)hipSetDevice(cur);
+}
+
+const char* bra_error_string(int code) {
+  switch (code) {
+    case BRA_OK: return "ok";
+    case BRA_ERR_NULL: return "a required pointer is NULL";
+    case BRA_ERR_SHAPE: return "invalid sizes: a size <= 0, H or W not divisible by S, or C not divisible by heads";
+    case BRA_ERR_TOPK: return "topk outside [1, S*S]";
+    case BRA_ERR_DTYPE: return "unknown dtype (0 = f32, 1 = bf16)";
+    case BRA_ERR_UNSUPPORTED: return "outside the compiled envelope (head_dim 32, C <= 1024, S*S <= 1024, topk*T <= 65536)";
+    case BRA_ERR_POINTER: return "a tensor pointer is not device memory";
+    case BRA_ERR_HIP:
+      snprintf(g_msg, sizeof g_msg, "HIP failure: %s", hipGetErrorString(g_last_hip));
+      return g_msg;
+    default: return "unknown status code";
+  }
+}
+
+int bra_version(void) { return 100; }
+
+int bra_profile_begin(int enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mutex);
+  g_prof_on = enable != 0;
+  for (auto& r : g_prof) r.used = 0;
+  return BRA_OK;
+}
+
+int bra_profile_read(double* ms, int* counts, int n) {
+  if (!ms || !counts) return BRA_ERR_NULL;
+  std::lock_guard<std::mutex> lk(g_prof_mutex);
+  for (int kd = 0; kd < n; ++kd) {
+    ms[kd] = 0.0;
+    counts[kd] = 0;
+    if (kd >= BRA_K_COUNT) continue;
+    KindRecord& rec = g_prof[kd];
+    for (int i = 0; i < rec.used; ++i) {
+      hipError_t e = hipEventSynchronize(rec.stop[i]);
+      if (e != hipSuccess) return hip_fail(e);
+      float t = 0.f;
+      e = hipEventElapsedTime(&t, rec.start[i], rec.stop[i]);
+      if (e != hipSuccess) return hip_fail(e);
+      ms[kd] += t;
+      counts[kd] += 1;
+    }
+    rec.used = 0;
+  }
+  return BRA_OK;
+}
+
+int bra_calib_copy(const void* src, void* dst, size_t bytes) {
+  if (!src || !dst) return BRA_ERR_NULL;
+  if (bytes % 16 != 0 || ((uintptr_t)src % 16) || ((uintptr_t)dst % 16)) return BRA_ERR_SHAPE;
+  int rc = check_ptrs({src, dst});
+  if (rc) return rc;
+  hipError_t e = bra::launch_copy(src, dst, bytes, g_stream);
+  return e == hipSuccess ? BRA_OK : hip_fail(e);
+}
+
+}  // extern "C"

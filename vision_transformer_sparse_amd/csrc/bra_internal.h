@@ -1,0 +1,62 @@
+// Internal declarations shared by the host library and the kernel files.
+// Not part of the public ABI (include/bra.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bra {
+
+// Problem sizes, derived once on the host after validation.
+struct Shape {
+  int N, H, W, C, heads, S, topk;
+  int R;       // S*S regions
+  int rh, rw;  // region height / width in tokens
+  int T;       // tokens per region
+  int hd;      // head dim (C / heads)
+  int L;       // gathered keys per query region (topk * T)
+};
+
+constexpr int kHeadDim = 32;     // compiled head dimension
+constexpr int kMaxRegions = 1024;
+
+hipError_t launch_region_pool(const void* q, const void* k, const Shape& s,
+                              int dtype, float* qr, float* kr, hipStream_t st);
+hipError_t launch_route(const float* qr, const float* kr, int N, int R, int C,
+                        int topk, int32_t* route, hipStream_t st);
+hipError_t launch_attend(const void* q, const void* k, const void* v,
+                         const void* w, const void* b, const int32_t* route,
+                         const Shape& s, int dtype, void* out, hipStream_t st);
+hipError_t launch_lce(const void* v, const void* w, const void* b,
+                      const Shape& s, int dtype, float* out, hipStream_t st);
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
+
+// Device helpers ------------------------------------------------------------
+#if defined(__HIPCC__)
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+// Low / high bf16 of a 32-bit word, as float.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ static float load(const float* p, size_t i) { return p[i]; }
+  __device__ static void store(float* p, size_t i, float x) { p[i] = x; }
+};
+template <> struct Elem<uint16_t> {  // bf16 storage
+  __device__ static float load(const uint16_t* p, size_t i) { return bf16_bits_to_float(p[i]); }
+  __device__ static void store(uint16_t* p, size_t i, float x) { p[i] = (uint16_t)float_to_bf16_bits(x); }
+};
+#endif
+
+}  // namespace bra
