@@ -1,0 +1,228 @@
+"""Throughput of the BRA forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1]
+
+A step is one bra_forward call -- region pooling, routing, gathered attention
+and LCE -- over one batch of seeded synthetic input already resident in HBM.
+W untimed steps, then K steps timed between two device synchronisations.
+One JSON line is printed. It carries:
+  value      whole-job queries/s (a query is one token position, N*H*W per step)
+  roofline   the dominant kernel's algorithmic bytes (or flops) per launch over
+             its mean launch time, measured with HIP events that the library
+             records on the launch stream inside the timed region
+  cpu_baseline  the fp64 CPU oracle timed on whole-batch passes of the same
+             workload (about 10 s of CPU work)
+Other workloads: --config c0..c4 (c1 is the default).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "BRA forward queries/sec at 1 MI355X; % of MFMA peak (attn) and HBM GB/s (route)"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
+ATTN_SOURCES = ("attn_mfma.hip", "attn_valu.hip")
+
+
+def algorithmic(cfg):
+    """Per-launch algorithmic traffic / work of each kernel (what the method
+    must move or compute, not what a dense method would)."""
+    b = 2 if cfg.dtype == "bf16" else 4
+    E = cfg.N * cfg.H * cfg.W * cfg.C
+    means = 2 * cfg.N * cfg.R * cfg.C * 4
+    routes = cfg.N * cfg.R * cfg.topk * 4
+    lce_params = cfg.C * 26 * b
+    return {
+        "pool": {"bytes": 2 * E * b + means},
+        "route": {"bytes": means + routes, "flops": 2 * cfg.N * cfg.R * cfg.R * cfg.C},
+        "attn": {"bytes": 4 * E * b + routes + lce_params, "flops": 4 * E * cfg.L + 50 * E},
+    }
+
+
+def roofline_for(kind, cfg, ms_per_launch, traffic):
+    alg = algorithmic(cfg)[kind]
+    t = ms_per_launch * 1e-3
+    if kind == "attn":
+        mfma_flops = 4 * cfg.N * cfg.H * cfg.W * cfg.C * cfg.L
+        if cfg.dtype == "bf16":
+            ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+            if mfma_flops / alg["bytes"] > ridge:
+                achieved = mfma_flops / t / 1e12
+                return {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                        "traffic": traffic, "kernel": kind}
+    achieved = alg["bytes"] / t / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": kind}
+
+
+def source_digest(names=ATTN_SOURCES) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "vision_transformer_sparse_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cfg_name: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, or None if it is absent or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"attn_{cfg_name}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("attention_source_sha256_16") != source_digest():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, cfg, budget_s: float):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    ncores = len(os.sched_getaffinity(0))
+    ncores = min(ncores, 16)
+    ctx = threadpool_limits(limits=ncores) if threadpool_limits else None
+    passes, t0 = 0, time.perf_counter()
+    try:
+        while True:
+            oracle.bra_forward(inp["q"], inp["k"], inp["v"], inp["lce_w"], inp["lce_b"],
+                               cfg.heads, cfg.S, cfg.topk)
+            passes += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    dt = time.perf_counter() - t0
+    return {"value": passes * cfg.queries / dt, "unit": "queries/s", "cores": ncores,
+            "kind": "oracle",
+            "sample": f"{passes} full pass(es) of the {cfg.name} batch (N={cfg.N}, "
+                      f"{cfg.queries} queries each), fp64 numpy, {dt:.1f} s"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c1")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after timing, run one copy kernel of this many MiB (counter calibration)")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(each image is independent, so batch sharding needs no collective, "
+              "but this build runs on one device)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from synth import CONFIGS, draw_config
+    from vision_transformer_sparse_amd import bra
+
+    cfg = {c.name: c for c in CONFIGS}[a.config]
+    bra.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = draw_config(cfg)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    t = {k: torch.from_numpy(v.astype(np.float32)).to(dev, tdt) for k, v in inp.items()}
+    out = torch.empty_like(t["q"])
+    route = torch.empty((cfg.N, cfg.R, cfg.topk), dtype=torch.int32, device=dev)
+
+    def step():
+        bra.forward(t["q"], t["k"], t["v"], t["lce_w"], t["lce_b"], cfg.heads, cfg.S, cfg.topk,
+                    out=out, route_idx=route)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] {cfg.name} warmup done", file=sys.stderr, flush=True)
+    bra.profile_begin(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = bra.profile_read()
+    bra.profile_begin(False)
+    print(f"[bench] {cfg.name} timed {a.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+
+    if a.calib_copy_mb > 0:
+        nbytes = a.calib_copy_mb * 1024 * 1024
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        bra.calib_copy(src, dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ms_step = elapsed * 1e3 / a.steps
+    kernels = {}
+    for kind, (ms, cnt) in prof.items():
+        if cnt:
+            kernels[kind] = {"us_per_launch": ms * 1e3 / cnt, "launches": cnt}
+    dominant = max(kernels, key=lambda k: kernels[k]["us_per_launch"])
+    traffic = measured_traffic(cfg.name) if dominant == "attn" else None
+    roof = roofline_for(dominant, cfg, kernels[dominant]["us_per_launch"] * 1e-3, traffic)
+    for kind in kernels:
+        r = roofline_for(kind, cfg, kernels[kind]["us_per_launch"] * 1e-3, None)
+        kernels[kind].update(bound=r["bound"], achieved=round(r["achieved"], 2), unit=r["unit"],
+                             frac=round(r["frac"], 4))
+
+    cpu = cpu_baseline(inp, cfg, a.cpu_budget) if a.cpu_budget > 0 else None
+    value = cfg.queries * a.steps / elapsed
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v; see synth/)",
+        "config": {"workload": f"{cfg.name}: {cfg.what}", "N": cfg.N, "H": cfg.H, "W": cfg.W,
+                   "C": cfg.C, "heads": cfg.heads, "S": cfg.S, "topk": cfg.topk,
+                   "queries_per_step": cfg.queries, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "attention_source_sha256_16": source_digest(),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

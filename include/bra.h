@@ -27,7 +27,9 @@
  * Conventions for every entry point
  *   - Tensor pointers are caller-owned DEVICE pointers (hipMalloc'd or a
  *     framework tensor's data pointer) of contiguous arrays. Host pointers are
- *     rejected with BRA_ERR_POINTER.
+ *     rejected with BRA_ERR_POINTER. q, k, v, out, lce_w and the fp32 region
+ *     means must be 16-byte aligned, lce_b and route_idx 4-byte aligned
+ *     (BRA_ERR_ALIGN otherwise).
  *   - q, k, v, out are NHWC: [N][H][W][C] of `dtype`.
  *   - lce_w is [C][5][5] of `dtype` (a depthwise Conv2d weight (C,1,5,5)
  *     flattened); lce_b is [C] of `dtype`, or NULL for a zero bias.
@@ -41,8 +43,9 @@
  *     work was enqueued (except BRA_ERR_HIP, which reports a failed launch or
  *     allocation) and the outputs are untouched.
  *
- * Compiled envelope: head_dim = C/heads = 32 (every BiFormer stage), S*S <=
- * 1024, topk * T <= 65536. Outside it the calls return BRA_ERR_UNSUPPORTED.
+ * Compiled envelope: head_dim = C/heads = 32 (every BiFormer stage), C <=
+ * 1024, S*S <= 1024, topk * T <= 65536. Outside it the calls return
+ * BRA_ERR_UNSUPPORTED.
  */
 #ifndef BRA_H_
 #define BRA_H_
@@ -67,7 +70,8 @@ enum bra_status {
   BRA_ERR_DTYPE = -4,       /* unknown dtype */
   BRA_ERR_UNSUPPORTED = -5, /* outside the compiled envelope (see above) */
   BRA_ERR_HIP = -6,         /* a HIP launch or allocation failed */
-  BRA_ERR_POINTER = -7      /* a tensor pointer is not device memory */
+  BRA_ERR_POINTER = -7,     /* a tensor pointer is not device memory */
+  BRA_ERR_ALIGN = -8        /* a tensor pointer is misaligned (see above) */
 };
 
 /* The whole forward pass, steps 1-8 above.
@@ -111,7 +115,8 @@ int bra_set_stream(void* stream);
 void* bra_get_stream(void);
 
 /* Bytes of library workspace bra_forward needs: two fp32 [N][S*S][C]
- * arrays (region means). Returns 0 for invalid sizes. */
+ * arrays (region means), 256-byte aligned, then 120*C bytes of LCE weights
+ * repacked for the small-region kernel. Returns 0 for invalid sizes. */
 size_t bra_workspace_bytes(int N, int C, int S);
 
 /* Frees the library workspace of every device (synchronises each device

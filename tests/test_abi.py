@@ -50,7 +50,7 @@ def test_version_and_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.bra_workspace_bytes(128, 128, 7) == 2 * 128 * 49 * 128 * 4
+    assert lib.bra_workspace_bytes(128, 128, 7) == 2 * 128 * 49 * 128 * 4 + 120 * 128
     assert lib.bra_workspace_bytes(0, 128, 7) == 0
 
 
@@ -76,6 +76,14 @@ P = ctypes.c_void_p(4096)  # never dereferenced: every case fails before HIP
 ])
 def test_forward_rejects(lib, args, code):
     assert lib.bra_forward(*args) == code
+
+
+def test_misaligned_pointers_rejected(lib):
+    M = ctypes.c_void_p(4096 + 2)
+    assert lib.bra_forward(M, P, P, P, None, 1, 8, 8, 64, 2, 2, 1, 1, P, P) == -8
+    assert lib.bra_forward(P, P, P, P, ctypes.c_void_p(4097), 1, 8, 8, 64, 2, 2, 1, 1, P, P) == -8
+    assert lib.bra_forward(P, P, P, P, None, 1, 8, 8, 64, 2, 2, 1, 1, P, ctypes.c_void_p(4098)) == -8
+    assert lib.bra_lce(P, P, None, 1, 8, 8, 64, 1, M) == -8
 
 
 def test_stage_entry_points_reject(lib):

@@ -20,6 +20,16 @@ hipError_t launch_attend_mfma(const void* q, const void* k, const void* v,
                               const void* w, const void* b, const int32_t* route,
                               const Shape& s, void* out, hipStream_t st);
 bool mfma_supports(const Shape& s);
+bool region_kernel_supports(const Shape& s);
+hipError_t launch_attend_region(const void* q, const void* k, const void* v, const uint32_t* wpk,
+                                const void* b, const int32_t* route, const Shape& s, void* out,
+                                hipStream_t st);
+bool tile_kernel_supports(const Shape& s);
+hipError_t launch_attend_tile(const void* q, const void* k, const void* v, const uint32_t* wpk,
+                              const void* b, const int32_t* route, const Shape& s, void* out,
+                              hipStream_t st);
+size_t lce_pack_bytes(int C);
+hipError_t launch_lce_pack(const void* w, int C, uint32_t* wpk, hipStream_t st);
 }  // namespace bra
 
 namespace {
@@ -121,6 +131,16 @@ int check_ptrs(std::initializer_list<const void*> ps) {
   return BRA_OK;
 }
 
+// Kernels read tensors with 16-byte vector loads (the bias and route
+// indices with 4-byte loads).
+int check_align(std::initializer_list<const void*> p16, std::initializer_list<const void*> p4) {
+  for (const void* p : p16)
+    if (p && ((uintptr_t)p & 15u)) return BRA_ERR_ALIGN;
+  for (const void* p : p4)
+    if (p && ((uintptr_t)p & 3u)) return BRA_ERR_ALIGN;
+  return BRA_OK;
+}
+
 int workspace(size_t bytes, void** ptr) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -147,12 +167,32 @@ int workspace(size_t bytes, void** ptr) {
   return BRA_OK;
 }
 
+// Workspace layout: fp32 region means of q and k ([N][S*S][C] each), then the
+// LCE weights packed for the small-region kernel (30*C dwords).
+struct WsLayout {
+  size_t means, wpk, total;
+};
+WsLayout ws_layout(int N, int C, int S) {
+  WsLayout l;
+  l.means = (size_t)2 * N * S * S * C * sizeof(float);
+  l.wpk = (l.means + 255) & ~(size_t)255;
+  l.total = l.wpk + bra::lce_pack_bytes(C);
+  return l;
+}
+
+// Attention + LCE over given routes (wpk: packed LCE weights, required by the
+// small-region kernel).
 int attend(const void* q, const void* k, const void* v, const void* w, const void* b,
-           const int32_t* route, const bra::Shape& s, int dtype, void* out, hipStream_t st) {
+           const int32_t* route, const bra::Shape& s, int dtype, void* out, const uint32_t* wpk,
+           hipStream_t st) {
   hipError_t e;
   {
     ProfScope ps(BRA_K_ATTN, st);
-    if (dtype == BRA_BF16 && bra::mfma_supports(s))
+    if (dtype == BRA_BF16 && wpk && bra::region_kernel_supports(s))
+      e = bra::launch_attend_region(q, k, v, wpk, b, route, s, out, st);
+    else if (dtype == BRA_BF16 && wpk && bra::tile_kernel_supports(s))
+      e = bra::launch_attend_tile(q, k, v, wpk, b, route, s, out, st);
+    else if (dtype == BRA_BF16 && bra::mfma_supports(s))
       e = bra::launch_attend_mfma(q, k, v, w, b, route, s, out, st);
     else
       e = bra::launch_attend_valu(q, k, v, w, b, route, s, dtype, out, st);
@@ -171,19 +211,23 @@ int bra_forward(const void* q, const void* k, const void* v, const void* lce_w,
   bra::Shape s;
   int rc = check_dims(N, H, W, C, heads, S, topk, dtype, true, true, &s);
   if (rc) return rc;
+  rc = check_align({q, k, v, lce_w, out}, {lce_b, route_idx});
+  if (rc) return rc;
   rc = check_ptrs({q, k, v, lce_w, lce_b, out, route_idx});
   if (rc) return rc;
   std::lock_guard<std::mutex> lk(g_ws_mutex);
+  const WsLayout wl = ws_layout(N, C, S);
   void* ws = nullptr;
-  rc = workspace(bra_workspace_bytes(N, C, S), &ws);
+  rc = workspace(wl.total, &ws);
   if (rc) return rc;
   float* qr = static_cast<float*>(ws);
   float* kr = qr + (size_t)N * s.R * C;
+  uint32_t* wpk = dtype == BRA_BF16 ? reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + wl.wpk) : nullptr;
   hipStream_t st = g_stream;
   hipError_t e;
   {
     ProfScope ps(BRA_K_POOL, st);
-    e = bra::launch_region_pool(q, k, s, dtype, qr, kr, st);
+    e = bra::launch_region_pool(q, k, s, dtype, qr, kr, lce_w, wpk, st);
   }
   if (e != hipSuccess) return hip_fail(e);
   {
@@ -191,7 +235,7 @@ int bra_forward(const void* q, const void* k, const void* v, const void* lce_w,
     e = bra::launch_route(qr, kr, N, s.R, C, topk, route_idx, st);
   }
   if (e != hipSuccess) return hip_fail(e);
-  return attend(q, k, v, lce_w, lce_b, route_idx, s, dtype, out, st);
+  return attend(q, k, v, lce_w, lce_b, route_idx, s, dtype, out, wpk, st);
 }
 
 int bra_region_means(const void* q, const void* k, int N, int H, int W, int C, int S,
@@ -200,13 +244,15 @@ int bra_region_means(const void* q, const void* k, int N, int H, int W, int C, i
   bra::Shape s;
   int rc = check_dims(N, H, W, C, 1, S, 1, dtype, false, false, &s);
   if (rc) return rc;
+  rc = check_align({q, k, qr, kr}, {});
+  if (rc) return rc;
   rc = check_ptrs({q, k, qr, kr});
   if (rc) return rc;
   hipStream_t st = g_stream;
   hipError_t e;
   {
     ProfScope ps(BRA_K_POOL, st);
-    e = bra::launch_region_pool(q, k, s, dtype, qr, kr, st);
+    e = bra::launch_region_pool(q, k, s, dtype, qr, kr, nullptr, nullptr, st);
   }
   return e == hipSuccess ? BRA_OK : hip_fail(e);
 }
@@ -217,7 +263,9 @@ int bra_route(const float* qr, const float* kr, int N, int R, int C, int topk,
   if (N <= 0 || R <= 0 || C <= 0) return BRA_ERR_SHAPE;
   if (topk < 1 || topk > R) return BRA_ERR_TOPK;
   if (R > bra::kMaxRegions || C % bra::kHeadDim != 0 || C > 1024) return BRA_ERR_UNSUPPORTED;
-  int rc = check_ptrs({qr, kr, route_idx});
+  int rc = check_align({qr, kr}, {route_idx});
+  if (rc) return rc;
+  rc = check_ptrs({qr, kr, route_idx});
   if (rc) return rc;
   hipStream_t st = g_stream;
   hipError_t e;
@@ -235,9 +283,22 @@ int bra_attend(const void* q, const void* k, const void* v, const void* lce_w,
   bra::Shape s;
   int rc = check_dims(N, H, W, C, heads, S, topk, dtype, true, true, &s);
   if (rc) return rc;
+  rc = check_align({q, k, v, lce_w, out}, {lce_b, route_idx});
+  if (rc) return rc;
   rc = check_ptrs({q, k, v, lce_w, lce_b, route_idx, out});
   if (rc) return rc;
-  return attend(q, k, v, lce_w, lce_b, route_idx, s, dtype, out, g_stream);
+  hipStream_t st = g_stream;
+  if (dtype == BRA_BF16 && (bra::region_kernel_supports(s) || bra::tile_kernel_supports(s))) {
+    std::lock_guard<std::mutex> lk(g_ws_mutex);
+    void* ws = nullptr;
+    rc = workspace(bra::lce_pack_bytes(C), &ws);
+    if (rc) return rc;
+    uint32_t* wpk = static_cast<uint32_t*>(ws);
+    hipError_t e = bra::launch_lce_pack(lce_w, C, wpk, st);
+    if (e != hipSuccess) return hip_fail(e);
+    return attend(q, k, v, lce_w, lce_b, route_idx, s, dtype, out, wpk, st);
+  }
+  return attend(q, k, v, lce_w, lce_b, route_idx, s, dtype, out, nullptr, st);
 }
 
 int bra_lce(const void* v, const void* lce_w, const void* lce_b, int N, int H, int W,
@@ -245,6 +306,8 @@ int bra_lce(const void* v, const void* lce_w, const void* lce_b, int N, int H, i
   if (!v || !lce_w || !out) return BRA_ERR_NULL;
   bra::Shape s;
   int rc = check_dims(N, H, W, C, 1, 1, 1, dtype, false, false, &s);
+  if (rc) return rc;
+  rc = check_align({v, out}, {lce_b});
   if (rc) return rc;
   rc = check_ptrs({v, lce_w, lce_b, out});
   if (rc) return rc;
@@ -266,7 +329,7 @@ void* bra_get_stream(void) { return g_stream; }
 
 size_t bra_workspace_bytes(int N, int C, int S) {
   if (N <= 0 || C <= 0 || S <= 0) return 0;
-  return (size_t)2 * N * S * S * C * sizeof(float);
+  return ws_layout(N, C, S).total;
 }
 
 void bra_release(void) {
@@ -294,6 +357,7 @@ const char* bra_error_string(int code) {
     case BRA_ERR_DTYPE: return "unknown dtype (0 = f32, 1 = bf16)";
     case BRA_ERR_UNSUPPORTED: return "outside the compiled envelope (head_dim 32, C <= 1024, S*S <= 1024, topk*T <= 65536)";
     case BRA_ERR_POINTER: return "a tensor pointer is not device memory";
+    case BRA_ERR_ALIGN: return "a tensor pointer is misaligned (16 bytes for q, k, v, out, lce_w and region means; 4 for lce_b and route_idx)";
     case BRA_ERR_HIP:
       snprintf(g_msg, sizeof g_msg, "HIP failure: %s", hipGetErrorString(g_last_hip));
       return g_msg;

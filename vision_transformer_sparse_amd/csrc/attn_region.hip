@@ -1,0 +1,400 @@
+// Gathered attention + LCE for small regions (T = RH*RW <= 16 tokens), bf16
+// tensors -- the classification stages of BiFormer (4x4 and 2x2 regions of a
+// 7x7 grid). Eqs. 6-7 of the BRA walk-through at
+// TRANSFORMER.niftyadmin.cn/n/347023.html, section BRA模块.
+//
+// One workgroup owns one query region (n, r) and all its heads, one wave per
+// head (64 * HEADS threads, C = 32 * HEADS channels, both compile-time, as
+// are the region sides RH x RW). Every global load it needs is issued up
+// front, so a workgroup pays about one memory latency:
+//
+//   A. each wave reads the region's route indices with scalar loads and,
+//      as soon as they land, issues its head's gathered K and V rows (the
+//      16-key tiles of the MFMA, 16 bytes per lane); meanwhile the V halo
+//      (RH+4 x RW+4 pixels, zero outside the image) is staged in LDS as
+//      horizontal pixel pairs per channel ([row][pair][C] dwords), the LCE
+//      weights (pre-packed as dot2 pairs) are staged in LDS and the head's
+//      16 query columns are loaded;
+//   B. per head, S^T = K Q^T and O^T = V^T P^T on 16x16x32 bf16 MFMAs (V^T
+//      produced on the matrix cores by a 0/1 selector; the softmax row sums
+//      by an all-ones operand, so they sum exactly the bf16 P that multiplies
+//      V), fp32 online softmax in base 2; the head output goes to LDS;
+//   C. LCE on packed bf16 dot products: a thread owns a channel pair and a
+//      region column; each halo row gives three pixel-pair dot2s per channel
+//      to each of the (up to five) output rows it touches. Added to the
+//      attention output and stored as bf16 pairs.
+//
+// Workgroups are numbered so that all regions of one image go to the same
+// XCD (dispatch is round-robin over the 8 XCDs), keeping an image's K/V in
+// that XCD's L2 while its regions gather from each other.
+#include "bra_internal.h"
+
+namespace bra {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 load8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
+  bf16x4 r;
+  r[0] = (__bf16)x[0]; r[1] = (__bf16)x[1]; r[2] = (__bf16)x[2]; r[3] = (__bf16)x[3];
+  return r;
+}
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+// Raw buffer access: a uniform base in SGPRs, a 32-bit byte offset per lane;
+// offsets at or past `bytes` read as zero (used for pixels outside the image).
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOut = 0x80000000u;  // an offset past every image
+__device__ __forceinline__ Rsrc rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld16(Rsrc r, uint32_t off) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ bf16x8 ld16_bf16(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(bf16x8, ld16(r, off));
+}
+
+struct RegionArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint32_t* wpk;     // LCE weights packed for dot2: [2 parity][5 rows][3 pairs][C]
+  const uint16_t* b;
+  const int32_t* route;    // [N][S*S][topk]
+  uint16_t* out;
+  int N, H, W, S, topk;
+  float qscale;            // head_dim^-1/2 * log2(e) (attention, base 2)
+};
+
+__host__ __device__ constexpr size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+struct Lds {
+  size_t halo, wts, att, total;
+};
+__host__ __device__ inline Lds lds_layout(int RH, int RW, int C) {
+  Lds l;
+  size_t o = 0;
+  l.halo = o; o += align16((size_t)(RH + 4) * ((RW + 5) / 2) * C * 4);
+  l.wts = o; o += align16((size_t)30 * C * 4);
+  l.att = o; o += align16((size_t)RH * RW * C * 4);
+  l.total = o;
+  return l;
+}
+
+template <int RH, int RW, int HEADS>
+__global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a) {
+  constexpr int C = 32 * HEADS;  // channels (head_dim 32)
+  constexpr int T = RH * RW;     // divides 16: a 16-key tile holds whole regions
+  constexpr int HP = RH + 4, WP = RW + 4;
+  constexpr int NPAIR = (WP + 1) / 2;  // halo column pairs (an odd width gets a zero column)
+  constexpr int nthreads = 2 * C;      // one wave per head
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int W = a.W, H = a.H, S = a.S, R = S * S, topk = a.topk;
+  const int L = topk * T;
+  const Lds lay = lds_layout(RH, RW, C);
+  uint32_t* halo = reinterpret_cast<uint32_t*>(smem + lay.halo);  // [HP][NPAIR][C]
+  uint32_t* wts = reinterpret_cast<uint32_t*>(smem + lay.wts);    // [2][5][3][C]
+  float* att = reinterpret_cast<float*>(smem + lay.att);          // [T][C]
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+
+  // XCD-aware numbering: consecutive units (one image's regions) share blockIdx % 8.
+  const int units = a.N * R;
+  const int per = (units + 7) / 8;
+  const int u = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (u >= units) return;  // the whole workgroup leaves together
+  const int n = u / R, r = u - n * R;
+  const int jr = r / S, ir = r - jr * S;
+  const int y0 = jr * RH, x0 = ir * RW;
+  const size_t img = (size_t)n * H * W * C;
+  const uint32_t img_bytes = (uint32_t)H * W * C * 2;
+  const Rsrc qb = rsrc(a.q + img, img_bytes), kbuf = rsrc(a.k + img, img_bytes);
+  const Rsrc vbuf = rsrc(a.v + img, img_bytes);
+  const uint32_t rowb = (uint32_t)W * C * 2;  // bytes per image row
+  constexpr uint32_t pixb = C * 2;            // bytes per pixel
+  const int c0 = wave * 32;                   // this wave's head
+  const uint32_t chb = (uint32_t)(c0 + 8 * grp) * 2;  // this lane's 8 channels
+
+  // ---- A: every load of the workgroup ------------------------------------
+  // gathered K/V rows, addressed through the route indices (uniform loads)
+  const int32_t* rrow = a.route + (size_t)u * topk;
+  auto region_base = [&](int s) -> uint32_t {
+    const int js = s / S, is = s - js * S;
+    return (uint32_t)(js * RH) * rowb + (uint32_t)(is * RW) * pixb;
+  };
+  const uint32_t ltok = (uint32_t)(col % T);  // token of this lane's key row within its region
+  const uint32_t toff = (ltok / RW) * rowb + (ltok % RW) * pixb + chb;
+  bf16x8 ak[4], av[4];
+  auto fetch = [&](int base) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int k0 = base + 16 * t;  // first key of the tile (uniform)
+      uint32_t off = kOut;           // keys past L read as zero (their scores are masked)
+      if (k0 < L) {
+        if constexpr (T == 16) {
+          off = region_base(rrow[k0 / 16]) + toff;
+        } else {
+          constexpr int NR = 16 / T;  // regions per tile, lane col/T picks one
+          const int p0 = k0 / T;
+#pragma unroll
+          for (int j = 0; j < NR; ++j) {
+            const int p = p0 + j;
+            if (p < topk && col / T == j) off = region_base(rrow[p]) + toff;
+          }
+        }
+      }
+      ak[t] = ld16_bf16(kbuf, off);
+      av[t] = ld16_bf16(vbuf, off);
+    }
+  };
+  fetch(0);
+  const uint32_t qt = col < T ? col : T - 1;
+  const bf16x8 bq = ld16_bf16(qb, (y0 + qt / RW) * rowb + (x0 + qt % RW) * pixb + chb);
+  {
+    // the V halo: 2C threads = 16 per 8-channel chunk -> (chunk, pair slots slot0 + 16 i)
+    constexpr int NSLOT = HP * NPAIR, NIT = (NSLOT + 15) / 16;
+    constexpr uint32_t chunks = C / 8;
+    const uint32_t ch = tid % chunks, slot0 = tid / chunks;
+    uint4 va[NIT], vb[NIT];
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+      const int pp = slot0 + 16 * i;
+      const int pr = pp % NPAIR, py = pp / NPAIR;
+      const int y = y0 - 2 + py, x = x0 - 2 + 2 * pr;
+      const bool rowok = pp < NSLOT && y >= 0 && y < H;
+      const uint32_t base = (uint32_t)y * rowb + ch * 16;
+      va[i] = ld16(vbuf, rowok && x >= 0 && x < W ? base + (uint32_t)x * pixb : kOut);
+      vb[i] = ld16(vbuf, rowok && x + 1 >= 0 && x + 1 < W && 2 * pr + 1 < WP ? base + (uint32_t)(x + 1) * pixb : kOut);
+    }
+    // the LCE weights (already packed for dot2) -> LDS
+    constexpr int pieces = 30 * C / 4;  // 16-byte pieces, < 4 * nthreads
+    const Rsrc wb = rsrc(a.wpk, (uint32_t)pieces * 16);
+    uint4 wv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[i] = ld16(wb, (uint32_t)(tid + i * nthreads) * 16);
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+      const int pp = slot0 + 16 * i;
+      if (pp < NSLOT) {
+        // channel c of the pair: low half = left pixel, high half = right pixel
+        uint4 lo, hi;
+        lo.x = (va[i].x & 0xffffu) | (vb[i].x << 16); lo.y = (va[i].x >> 16) | (vb[i].x & 0xffff0000u);
+        lo.z = (va[i].y & 0xffffu) | (vb[i].y << 16); lo.w = (va[i].y >> 16) | (vb[i].y & 0xffff0000u);
+        hi.x = (va[i].z & 0xffffu) | (vb[i].z << 16); hi.y = (va[i].z >> 16) | (vb[i].z & 0xffff0000u);
+        hi.z = (va[i].w & 0xffffu) | (vb[i].w << 16); hi.w = (va[i].w >> 16) | (vb[i].w & 0xffff0000u);
+        uint32_t* dst = halo + (size_t)pp * C + 8 * ch;
+        *reinterpret_cast<uint4*>(dst) = lo;
+        *reinterpret_cast<uint4*>(dst + 4) = hi;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + i * nthreads;
+      if (e < pieces) reinterpret_cast<uint4*>(wts)[e] = wv[i];
+    }
+  }
+
+  // ---- B: attention, head = wave -----------------------------------------
+  {
+    bf16x8 sel0, sel1, ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sel0[e] = (__bf16)((grp == (col >> 3) && e == (col & 7)) ? 1.0f : 0.0f);
+      sel1[e] = (__bf16)((grp == 2 + (col >> 3) && e == (col & 7)) ? 1.0f : 0.0f);
+      ones[e] = (__bf16)1.0f;
+    }
+    float m = -INFINITY;  // running max of the scaled (base-2) logits
+    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0, ls = o0;
+    for (int base = 0; base < L; base += 64) {
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      f32x4 s[4];
+      bf16x4 vt[4][2];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        s[t] = mfma(ak[t], bq, z);
+        vt[t][0] = to_bf16x4(mfma(av[t], sel0, z));
+        vt[t][1] = to_bf16x4(mfma(av[t], sel1, z));
+      }
+      if (base + 64 < L) fetch(base + 64);  // next chunk in flight during the softmax
+      if (base + 64 > L) {                  // ragged last chunk: mask keys past L
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (base + 16 * t + 4 * grp + e >= L) s[t][e] = -INFINITY;
+      }
+      float cm = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cm = fmaxf(cm, s[t][e]);
+      cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+      cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+      const float mn = fmaxf(m, cm * a.qscale);  // qscale > 0 commutes with max
+      if (base > 0) {                            // rescale what earlier chunks summed
+        const float corr = __builtin_amdgcn_exp2f(m - mn);
+        o0 *= corr;
+        o1 *= corr;
+        ls *= corr;
+      }
+      m = mn;
+      bf16x4 pb[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        f32x4 pv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(s[t][e], a.qscale, -mn));
+        pb[t] = to_bf16x4(pv);
+      }
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        const bf16x8 pt = cat(pb[2 * bb], pb[2 * bb + 1]);
+        o0 = mfma(cat(vt[2 * bb][0], vt[2 * bb + 1][0]), pt, o0);
+        o1 = mfma(cat(vt[2 * bb][1], vt[2 * bb + 1][1]), pt, o1);
+        ls = mfma(ones, pt, ls);  // every row of ones x P^T is the row sum of P
+      }
+    }
+    const float inv = 1.0f / ls[0];
+    if (col < T) {
+      float* ap = att + col * C + c0;
+      *reinterpret_cast<float4*>(ap + 4 * grp) = make_float4(o0[0] * inv, o0[1] * inv, o0[2] * inv, o0[3] * inv);
+      *reinterpret_cast<float4*>(ap + 16 + 4 * grp) = make_float4(o1[0] * inv, o1[1] * inv, o1[2] * inv, o1[3] * inv);
+    }
+  }
+  __syncthreads();
+
+  // ---- C: LCE (dot2 sliding window), merge, store --------------------------
+  for (int it = tid; it < (C / 2) * RW; it += nthreads) {
+    const int cp = it % (C / 2), xcol = it / (C / 2);
+    const int c = 2 * cp;
+    const uint32_t* wp = wts + (xcol & 1) * 15 * C + c;
+    uint2 wv[5][3];
+#pragma unroll
+    for (int ay = 0; ay < 5; ++ay)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) wv[ay][j] = *reinterpret_cast<const uint2*>(wp + (ay * 3 + j) * C);
+    float b0 = 0.f, b1 = 0.f;
+    if (a.b) {
+      const uint32_t bb = *reinterpret_cast<const uint32_t*>(a.b + c);
+      b0 = bf16_lo(bb);
+      b1 = bf16_hi(bb);
+    }
+    float acc0[RH], acc1[RH];
+#pragma unroll
+    for (int i = 0; i < RH; ++i) { acc0[i] = b0; acc1[i] = b1; }
+    const uint32_t* hc = halo + (xcol >> 1) * C + c;
+#pragma unroll
+    for (int yy = 0; yy < HP; ++yy) {
+      const uint32_t* hr = hc + yy * NPAIR * C;
+      const uint2 h0 = *reinterpret_cast<const uint2*>(hr);
+      const uint2 h1 = *reinterpret_cast<const uint2*>(hr + C);
+      const uint2 h2 = *reinterpret_cast<const uint2*>(hr + 2 * C);
+#pragma unroll
+      for (int ay = 0; ay < 5; ++ay) {
+        const int yo = yy - ay;
+        if (yo >= 0 && yo < RH) {
+          acc0[yo] = dot2(h0.x, wv[ay][0].x, acc0[yo]);
+          acc0[yo] = dot2(h1.x, wv[ay][1].x, acc0[yo]);
+          acc0[yo] = dot2(h2.x, wv[ay][2].x, acc0[yo]);
+          acc1[yo] = dot2(h0.y, wv[ay][0].y, acc1[yo]);
+          acc1[yo] = dot2(h1.y, wv[ay][1].y, acc1[yo]);
+          acc1[yo] = dot2(h2.y, wv[ay][2].y, acc1[yo]);
+        }
+      }
+    }
+#pragma unroll
+    for (int yo = 0; yo < RH; ++yo) {
+      const float2 at = *reinterpret_cast<const float2*>(att + (yo * RW + xcol) * C + c);
+      const uint32_t packed = float_to_bf16_bits(at.x + acc0[yo]) | (float_to_bf16_bits(at.y + acc1[yo]) << 16);
+      *reinterpret_cast<uint32_t*>(a.out + img + ((size_t)(y0 + yo) * W + x0 + xcol) * C + c) = packed;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void lce_pack_kernel(const uint16_t* __restrict__ w, int C,
+                                                       uint32_t* __restrict__ wpk) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < 15 * C) pack_lce_entry(w, C, e, wpk);
+}
+
+template <int RH, int RW, int HEADS>
+hipError_t launch_shape(const RegionArgs& a, int R, size_t lds, hipStream_t st) {
+  const int units = a.N * R;
+  const unsigned blocks = (unsigned)(((units + 7) / 8) * 8);
+  hipLaunchKernelGGL((attn_region_kernel<RH, RW, HEADS>), dim3(blocks), dim3(64 * HEADS), lds, st, a);
+  return hipGetLastError();
+}
+
+// Compiled shapes: regions of 1x1 .. 4x4 tokens with 2, 4 or 8 heads.
+bool shape_compiled(int rh, int rw, int heads) {
+  auto side = [](int v) { return v == 1 || v == 2 || v == 4; };
+  return side(rh) && side(rw) && (heads == 2 || heads == 4 || heads == 8);
+}
+
+template <int HEADS>
+hipError_t dispatch_shape(const RegionArgs& a, const Shape& s, size_t lds, hipStream_t st) {
+  switch (s.rh * 8 + s.rw) {
+#define BRA_CASE(RH, RW) \
+    case RH * 8 + RW: return launch_shape<RH, RW, HEADS>(a, s.R, lds, st);
+    BRA_CASE(1, 1) BRA_CASE(1, 2) BRA_CASE(1, 4) BRA_CASE(2, 1) BRA_CASE(2, 2)
+    BRA_CASE(2, 4) BRA_CASE(4, 1) BRA_CASE(4, 2) BRA_CASE(4, 4)
+#undef BRA_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+size_t lce_pack_bytes(int C) { return (size_t)30 * C * 4; }
+
+hipError_t launch_lce_pack(const void* w, int C, uint32_t* wpk, hipStream_t st) {
+  hipLaunchKernelGGL(lce_pack_kernel, dim3((unsigned)((15 * C + 255) / 256)), dim3(256), 0, st,
+                     (const uint16_t*)w, C, wpk);
+  return hipGetLastError();
+}
+
+bool region_kernel_supports(const Shape& s) {
+  if (s.hd != 32 || !shape_compiled(s.rh, s.rw, s.heads)) return false;
+  if ((long long)s.H * s.W * s.C >= (1ll << 30)) return false;  // 32-bit byte offsets within an image
+  return lds_layout(s.rh, s.rw, s.C).total <= 65536;
+}
+
+hipError_t launch_attend_region(const void* q, const void* k, const void* v, const uint32_t* wpk,
+                                const void* b, const int32_t* route, const Shape& s, void* out,
+                                hipStream_t st) {
+  RegionArgs a;
+  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
+  a.wpk = wpk; a.b = (const uint16_t*)b;
+  a.route = route;
+  a.out = (uint16_t*)out;
+  a.N = s.N; a.H = s.H; a.W = s.W; a.S = s.S; a.topk = s.topk;
+  a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
+  const size_t lds = lds_layout(s.rh, s.rw, s.C).total;
+  switch (s.heads) {
+    case 2: return dispatch_shape<2>(a, s, lds, st);
+    case 4: return dispatch_shape<4>(a, s, lds, st);
+    case 8: return dispatch_shape<8>(a, s, lds, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace bra

@@ -21,8 +21,11 @@ struct Shape {
 constexpr int kHeadDim = 32;     // compiled head dimension
 constexpr int kMaxRegions = 1024;
 
+// Region means; for bf16 (wpk non-null) also repacks the LCE weights for the
+// small-region attention kernel.
 hipError_t launch_region_pool(const void* q, const void* k, const Shape& s,
-                              int dtype, float* qr, float* kr, hipStream_t st);
+                              int dtype, float* qr, float* kr, const void* lce_w,
+                              uint32_t* wpk, hipStream_t st);
 hipError_t launch_route(const float* qr, const float* kr, int N, int R, int C,
                         int topk, int32_t* route, hipStream_t st);
 hipError_t launch_attend(const void* q, const void* k, const void* v,
@@ -46,6 +49,22 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
+}
+
+// One entry of the LCE weights repacked for packed-bf16 dot products:
+// [C][5][5] bf16 -> [parity][row][pair][C] pairs. For an even output column
+// the pixel pairs start at tap 0 ((w0,w1),(w2,w3),(w4,0)); for an odd one a
+// pixel earlier ((0,w0),(w1,w2),(w3,w4)). e indexes row*3+pair major, C minor.
+__device__ __forceinline__ void pack_lce_entry(const uint16_t* __restrict__ lw, int C, int e,
+                                               uint32_t* __restrict__ wpk) {
+  const int c = e % C, rest = e / C;
+  const int ay = rest / 3, d0 = 2 * (rest % 3);
+  const uint16_t* wr = lw + (size_t)c * 25 + ay * 5;
+  const uint32_t t0 = wr[d0];
+  const uint32_t t1 = d0 + 1 < 5 ? (uint32_t)wr[d0 + 1] : 0u;
+  const uint32_t tm = d0 > 0 ? (uint32_t)wr[d0 - 1] : 0u;
+  wpk[rest * C + c] = t0 | (t1 << 16);
+  wpk[(15 + rest) * C + c] = tm | (t0 << 16);
 }
 
 template <typename T> struct Elem;

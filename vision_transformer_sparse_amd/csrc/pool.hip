@@ -2,25 +2,24 @@
 // region's tokens (not over channels) -- the q_win / k_win step of the BRA
 // walk-through at TRANSFORMER.niftyadmin.cn/n/347023.html, section BRA模块.
 //
-// One workgroup per (image, region). Each thread owns one 16-byte channel
-// chunk of a token and walks a fixed subset of the region's tokens, so every
-// load is a coalesced 16-byte NHWC read; the per-thread partial sums are then
-// combined in LDS in a fixed order. The result is bit-reproducible from run
-// to run (the routing that follows compares it with an exact tie rule).
+// One workgroup per (image, region), sized to the region (64-256 threads).
+// A thread owns one 16-byte channel chunk and up to TPT tokens of the region;
+// it issues 2*TPT coalesced NHWC loads at a time before adding any of them,
+// so a whole region is in flight at once (the kernel is bound by memory
+// latency x bytes in flight, not by arithmetic). Per-thread partial sums are
+// combined in LDS in a fixed order, so the means are reproducible bit for bit
+// (the routing that follows breaks ties exactly).
 #include "bra_internal.h"
 
 namespace bra {
 namespace {
-
-constexpr int kPoolThreads = 256;
 
 template <typename T>
 struct Vec16;
 template <>
 struct Vec16<uint16_t> {
   static constexpr int n = 8;
-  __device__ static void add(const uint16_t* p, float* acc) {
-    uint4 w = *reinterpret_cast<const uint4*>(p);
+  __device__ static void add(const uint4 w, float* acc) {
     acc[0] += bf16_lo(w.x); acc[1] += bf16_hi(w.x);
     acc[2] += bf16_lo(w.y); acc[3] += bf16_hi(w.y);
     acc[4] += bf16_lo(w.z); acc[5] += bf16_hi(w.z);
@@ -30,16 +29,17 @@ struct Vec16<uint16_t> {
 template <>
 struct Vec16<float> {
   static constexpr int n = 4;
-  __device__ static void add(const float* p, float* acc) {
-    float4 w = *reinterpret_cast<const float4*>(p);
-    acc[0] += w.x; acc[1] += w.y; acc[2] += w.z; acc[3] += w.w;
+  __device__ static void add(const uint4 w, float* acc) {
+    acc[0] += __uint_as_float(w.x); acc[1] += __uint_as_float(w.y);
+    acc[2] += __uint_as_float(w.z); acc[3] += __uint_as_float(w.w);
   }
 };
 
-template <typename T>
-__global__ __launch_bounds__(kPoolThreads) void region_pool_kernel(
+template <typename T, int TPT>
+__global__ __launch_bounds__(256) void region_pool_kernel(
     const T* __restrict__ q, const T* __restrict__ k, int H, int W, int C, int S,
-    float* __restrict__ qr, float* __restrict__ kr) {
+    float* __restrict__ qr, float* __restrict__ kr, const uint16_t* __restrict__ lw,
+    uint32_t* __restrict__ wpk) {
   constexpr int V = Vec16<T>::n;
   extern __shared__ float part[];  // [2][lanes][C]
   const int R = S * S;
@@ -48,21 +48,39 @@ __global__ __launch_bounds__(kPoolThreads) void region_pool_kernel(
   const int j = r / S, i = r - j * S;
   const int rh = H / S, rw = W / S, T_ = rh * rw;
   const int nchunk = C / V;
-  const int lanes = kPoolThreads / nchunk;  // tokens walked in parallel
+  const int lanes = blockDim.x / nchunk;  // tokens walked in parallel
   const int tid = threadIdx.x;
   const int chunk = tid % nchunk, tl = tid / nchunk;
+  const size_t img = (size_t)n * H * W;
+
+  // Side job: the LCE weights repacked for the attention kernel's dot2s.
+  if (wpk)
+    for (int e = blockIdx.x * blockDim.x + tid; e < 15 * C; e += gridDim.x * blockDim.x)
+      pack_lce_entry(lw, C, e, wpk);
 
   float aq[V], ak[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) { aq[e] = 0.f; ak[e] = 0.f; }
   if (tl < lanes) {
-    const size_t img = (size_t)n * H * W;
-#pragma unroll 4
-    for (int t = tl; t < T_; t += lanes) {
-      const int y = j * rh + t / rw, x = i * rw + t % rw;
-      const size_t off = ((img + (size_t)y * W + x) * C) + (size_t)chunk * V;
-      Vec16<T>::add(q + off, aq);
-      Vec16<T>::add(k + off, ak);
+    for (int t0 = tl; t0 < T_; t0 += TPT * lanes) {
+      uint4 bq[TPT], bk[TPT];
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        const int t = t0 + u * lanes;
+        if (t < T_) {
+          const int y = j * rh + t / rw, x = i * rw + t % rw;
+          const size_t off = ((img + (size_t)y * W + x) * C) + (size_t)chunk * V;
+          bq[u] = *reinterpret_cast<const uint4*>(q + off);
+          bk[u] = *reinterpret_cast<const uint4*>(k + off);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        if (t0 + u * lanes < T_) {
+          Vec16<T>::add(bq[u], aq);
+          Vec16<T>::add(bk[u], ak);
+        }
+      }
     }
     float* pq = part + (size_t)tl * C + chunk * V;
     float* pk = part + (size_t)(lanes + tl) * C + chunk * V;
@@ -71,7 +89,7 @@ __global__ __launch_bounds__(kPoolThreads) void region_pool_kernel(
   }
   __syncthreads();
   const float count = (float)T_;
-  for (int c = tid; c < C; c += kPoolThreads) {
+  for (int c = tid; c < C; c += blockDim.x) {
     float sq = 0.f, sk = 0.f;
     for (int l = 0; l < lanes; ++l) {
       sq += part[(size_t)l * C + c];
@@ -82,22 +100,40 @@ __global__ __launch_bounds__(kPoolThreads) void region_pool_kernel(
   }
 }
 
+template <typename T>
+hipError_t launch_t(const void* q, const void* k, const Shape& s, float* qr, float* kr,
+                    const void* lw, uint32_t* wpk, hipStream_t st) {
+  constexpr int V = Vec16<T>::n;
+  const int nchunk = s.C / V;                 // <= 256 (C <= 1024)
+  // threads: a multiple of 64 holding whole token lanes, aiming at <= 8 tokens per thread
+  int lanes_wanted = (s.T + 7) / 8;
+  int threads = nchunk * lanes_wanted;
+  threads = threads < 64 ? 64 : threads;
+  threads = threads > 256 ? 256 : threads;
+  threads = ((threads + 63) / 64) * 64;
+  int lanes = threads / nchunk;
+  if (lanes < 1) lanes = 1;
+  const int tpt = (s.T + lanes - 1) / lanes;  // tokens per thread (looped in batches of <= 8)
+  const size_t lds = (size_t)2 * lanes * s.C * sizeof(float);
+  dim3 grid((unsigned)(s.N * s.R)), block(threads);
+#define BRA_POOL(TP)                                                                    \
+  hipLaunchKernelGGL((region_pool_kernel<T, TP>), grid, block, lds, st, (const T*)q,    \
+                     (const T*)k, s.H, s.W, s.C, s.S, qr, kr, (const uint16_t*)lw, wpk)
+  if (tpt <= 1) BRA_POOL(1);
+  else if (tpt <= 2) BRA_POOL(2);
+  else if (tpt <= 4) BRA_POOL(4);
+  else BRA_POOL(8);
+#undef BRA_POOL
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_region_pool(const void* q, const void* k, const Shape& s,
-                              int dtype, float* qr, float* kr, hipStream_t st) {
-  const int V = dtype == 1 ? 8 : 4;
-  const int nchunk = s.C / V;
-  const int lanes = kPoolThreads / nchunk;
-  const size_t lds = (size_t)2 * lanes * s.C * sizeof(float);
-  dim3 grid((unsigned)(s.N * s.R)), block(kPoolThreads);
-  if (dtype == 1)
-    hipLaunchKernelGGL(region_pool_kernel<uint16_t>, grid, block, lds, st,
-                       (const uint16_t*)q, (const uint16_t*)k, s.H, s.W, s.C, s.S, qr, kr);
-  else
-    hipLaunchKernelGGL(region_pool_kernel<float>, grid, block, lds, st,
-                       (const float*)q, (const float*)k, s.H, s.W, s.C, s.S, qr, kr);
-  return hipGetLastError();
+hipError_t launch_region_pool(const void* q, const void* k, const Shape& s, int dtype,
+                              float* qr, float* kr, const void* lce_w, uint32_t* wpk,
+                              hipStream_t st) {
+  return dtype == 1 ? launch_t<uint16_t>(q, k, s, qr, kr, lce_w, wpk, st)
+                    : launch_t<float>(q, k, s, qr, kr, nullptr, nullptr, st);
 }
 
 }  // namespace bra
