@@ -131,15 +131,16 @@ const char* bra_error_string(int code);
 int bra_version(void);
 
 /* Per-kernel timing with HIP events recorded on the launch stream.
- * bra_profile_begin(1) starts recording (up to 4096 launches per kernel
- * kind, later ones are not recorded); bra_profile_read synchronises the
- * stream, then writes for each kernel kind k < n (BRA_K_* below) the summed
- * milliseconds and the launch count, and clears the record. bra_profile_begin(0)
- * stops recording. */
+ * bra_profile_begin(mask) records events around the kernels of every kind k
+ * with bit (1 << k) set in mask (BRA_K_* below; up to 4096 launches per kind,
+ * later ones are not recorded) and clears earlier records; mask 0 stops
+ * recording. bra_profile_read waits for the recorded events, then writes for
+ * each kind k < n the summed milliseconds and the launch count, and clears
+ * the record. Each recorded kernel costs two event records on the stream. */
 enum bra_kernel_kind {
   BRA_K_POOL = 0, BRA_K_ROUTE = 1, BRA_K_ATTN = 2, BRA_K_LCE = 3, BRA_K_COUNT = 4
 };
-int bra_profile_begin(int enable);
+int bra_profile_begin(int mask);
 int bra_profile_read(double* ms, int* counts, int n);
 
 /* A plain device-to-device copy kernel (bytes % 16 == 0, both pointers

@@ -197,11 +197,11 @@ def test_profile_counts(gpu_lib):
     inp = draw_config(cfg, N=4)
     args = [dev(inp[x], cfg.dtype) for x in ("q", "k", "v", "lce_w", "lce_b")]
     say("profile")
-    gpu_lib.profile_begin(True)
+    gpu_lib.profile_begin()
     for _ in range(3):
         gpu_lib.forward(*args, cfg.heads, cfg.S, cfg.topk)
     rec = gpu_lib.profile_read()
-    gpu_lib.profile_begin(False)
+    gpu_lib.profile_begin(())
     # small regions (this workload) run the routing inside the attention kernel
     assert rec["pool"][1] == 3 and rec["route"][1] in (0, 3) and rec["attn"][1] == 3
     assert rec["attn"][0] > 0

@@ -210,8 +210,15 @@ def version() -> int:
     return int(load().bra_version())
 
 
-def profile_begin(enable: bool = True) -> None:
-    _call("bra_profile_begin", 1 if enable else 0)
+def profile_begin(kinds=KERNEL_NAMES) -> None:
+    """Records HIP events around the named kernel kinds ("pool", "route",
+    "attn", "lce"); an empty sequence (or False) stops recording."""
+    if kinds is True:
+        kinds = KERNEL_NAMES
+    mask = 0
+    for k in (kinds or ()):
+        mask |= 1 << KERNEL_NAMES.index(k)
+    _call("bra_profile_begin", mask)
 
 
 def profile_read() -> dict:

@@ -52,7 +52,7 @@ struct KindRecord {
   int used = 0;
 };
 std::mutex g_prof_mutex;
-bool g_prof_on = false;
+int g_prof_mask = 0;  // bit k: record events around kernels of kind k
 KindRecord g_prof[BRA_K_COUNT];
 
 struct ProfScope {
@@ -60,7 +60,7 @@ struct ProfScope {
   hipStream_t st;
   int slot = -1;
   ProfScope(int kind_, hipStream_t st_) : kind(kind_), st(st_) {
-    if (!g_prof_on) return;
+    if (!(g_prof_mask & (1 << kind))) return;
     std::lock_guard<std::mutex> lk(g_prof_mutex);
     KindRecord& rec = g_prof[kind];
     if (rec.used >= kMaxEvents) return;
@@ -367,9 +367,9 @@ const char* bra_error_string(int code) {
 
 int bra_version(void) { return 100; }
 
-int bra_profile_begin(int enable) {
+int bra_profile_begin(int mask) {
   std::lock_guard<std::mutex> lk(g_prof_mutex);
-  g_prof_on = enable != 0;
+  g_prof_mask = mask & ((1 << BRA_K_COUNT) - 1);
   for (auto& r : g_prof) r.used = 0;
   return BRA_OK;
 }
