@@ -73,6 +73,8 @@ SMALL_CASES = [
     ("nonsquare_t24", 1, 16, 24, 96, 3, 4, 5, "bf16", 0.0),
     ("r1024_router", 1, 32, 32, 32, 1, 32, 16, "bf16", 0.0),
     ("r400_router", 1, 40, 40, 64, 2, 20, 7, "bf16", 0.7),
+    ("r100_router", 2, 20, 20, 64, 2, 10, 6, "bf16", 0.0),
+    ("r36_three_col_tiles", 2, 24, 24, 96, 3, 6, 5, "bf16", 0.0),
     ("f32_c0_like", 1, 56, 56, 64, 2, 7, 1, "f32", 0.0),
     ("f32_ragged", 2, 15, 10, 64, 2, 5, 3, "f32", 0.0),
     ("f32_t256", 1, 64, 64, 64, 2, 4, 2, "f32", 0.7),

@@ -55,18 +55,8 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
                                          __builtin_bit_cast(bf16x2, b), c, false);
 }
-// Raw buffer access: a uniform base in SGPRs, a 32-bit byte offset per lane;
-// offsets at or past `bytes` read as zero (used for pixels outside the image).
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-constexpr uint32_t kOut = 0x80000000u;  // an offset past every image
-__device__ __forceinline__ Rsrc rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 ld16(Rsrc r, uint32_t off) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
+// Buffer loads (rsrc, ld16) read offsets past the image (kOut) as zero:
+// used for pixels outside the image.
 __device__ __forceinline__ bf16x8 ld16_bf16(Rsrc r, uint32_t off) {
   return __builtin_bit_cast(bf16x8, ld16(r, off));
 }

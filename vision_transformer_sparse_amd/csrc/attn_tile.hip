@@ -35,20 +35,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __amdgpu_buffer_rsrc_t Rsrc;
 
-constexpr uint32_t kOut = 0x80000000u;  // a byte offset past every image
 constexpr int kKStr = 40;               // K tile row stride (bf16): 32 dims + 8 pad
 constexpr int kVStr = 72;               // V^T tile row stride (bf16): 64 keys + 8 pad
 
-__device__ __forceinline__ Rsrc rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 ld16(Rsrc r, uint32_t off) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
   bf16x4 r;

@@ -44,6 +44,26 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Raw buffer access: a uniform base in SGPRs, a 32-bit byte offset per lane;
+// offsets at or past `bytes` read as zero.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOut = 0x80000000u;  // an offset past every buffer this library builds
+__device__ __forceinline__ Rsrc rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld16(Rsrc r, uint32_t off) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Workgroup b -> logical unit u such that consecutive units share b % 8,
+// the XCD that dispatch sends workgroup b to. Bijective on [0, blocks).
+__device__ __forceinline__ int xcd_unit(int b, int blocks) {
+  const int per = blocks / 8, rem = blocks % 8, x = b % 8;
+  return x * per + min(x, rem) + b / 8;
+}
+
 // float -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);

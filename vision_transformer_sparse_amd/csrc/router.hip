@@ -5,27 +5,40 @@
 // embedding is the identity; the softmax of the selected logits (routing
 // weights) is not consumed by the gather and is not computed.
 //
-// One workgroup (4 waves) per (image, block of 4*RPW query regions), RPW
-// query rows per wave (4 when there are at most 64 regions, else 1). K^r of the image is staged through LDS in channel slices
-// with coalesced 16-byte loads (whole, when it fits), the 4 Q^r rows next to
-// it; lane l owns the candidate regions l, l+64, ... and reads K^r and Q^r
-// four channels at a time. Each logit is one fp32 fma chain in ascending
-// channel order, then one multiply by C^-1/2 -- a fixed order, so the result
-// is reproducible bit for bit.
+// Each shape is served by one kernel, in a fixed accumulation order, so its
+// logits (and routes) are reproducible bit for bit:
+//  * R <= 64 (route_kernel): affinities on fp32 matrix cores
+//    (v_mfma_f32_16x16x4_f32: fp32 operands, fp32 accumulation). One
+//    workgroup per 16 query rows of one image, one wave per 16-column tile.
+//    Lane (i, g) of a tile takes the 16-byte pieces at channels 16j+4g of
+//    row i of its A (Q^r) and B (K^r) operands -- the same channels on both
+//    sides -- straight from memory with buffer loads (pieces past C read as
+//    zero), 64 channels per batch with the next batch in flight. The scaled
+//    logits go to LDS.
+//  * R > 64 (route_wide_kernel): one workgroup per 4 query rows, one wave per
+//    64 candidates; each lane streams its own candidate's K^r row from L2
+//    into registers (double-buffered 32-channel batches) and reads the 4 Q^r
+//    rows as LDS broadcasts; each logit is one fp32 fma chain in ascending
+//    channel order. The 4 rows of logits go to LDS. (This spreads a few
+//    large images over many more CUs than 16-row tiles would.)
+// The workgroups of one image are numbered onto one XCD, so K^r comes from
+// memory once per image and then from that XCD's L2.
 //
 // Top-k with an exact tie rule: every (A, s) becomes a 64-bit key whose
 // unsigned order is "larger A first, then lower s first". With at most 64
-// candidates each lane ranks its own key against all others (broadcast LDS
-// reads, no cross-lane chain) and lanes of rank < topk write their index at
-// that rank. With more candidates, topk rounds of a wave-wide maximum pick
-// the winners in descending order.
+// candidates each lane ranks its own key against all others (LDS broadcast
+// reads, four rows interleaved per wave) and the lanes of rank < topk write
+// their index at that rank. With more, topk rounds of a wave-wide maximum
+// (DPP row reductions, then the last lane's value) emit the winners in
+// descending order.
 #include "bra_internal.h"
 
 namespace bra {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr size_t kLdsBudget = 48 * 1024;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunk = 64;  // channels per load batch: 4 pieces of A and 4 of B per lane
 
 __device__ __forceinline__ uint64_t route_key(float a, int s) {
   if (a == 0.0f) a = 0.0f;  // -0 and +0 are the same logit
@@ -34,127 +47,217 @@ __device__ __forceinline__ uint64_t route_key(float a, int s) {
   return ((uint64_t)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)s);
 }
 
+// max of x and the DPP-moved copy of x (lanes the pattern leaves out keep x)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t x) {
+  const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+  const uint32_t ylo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, ROW_MASK, 0xf, false);
+  const uint32_t yhi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, ROW_MASK, 0xf, false);
+  const uint64_t y = ((uint64_t)yhi << 32) | ylo;
+  return y > x ? y : x;
+}
+
+// Maximum over the 64 lanes, returned wave-uniform: quad swaps, half-row and
+// row mirrors (each row of 16 then holds its maximum), then row broadcasts
+// 15 and 31 carry it into lane 63, which is read out.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t y = __shfl_xor(x, off, 64);
-    x = y > x ? y : x;
-  }
-  return x;
+  x = dpp_max_step<0xb1, 0xf>(x);   // quad_perm [1,0,3,2]
+  x = dpp_max_step<0x4e, 0xf>(x);   // quad_perm [2,3,0,1]
+  x = dpp_max_step<0x141, 0xf>(x);  // row_half_mirror
+  x = dpp_max_step<0x140, 0xf>(x);  // row_mirror
+  x = dpp_max_step<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x = dpp_max_step<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// Channel slice staged per pass: the whole of C when K^r fits the budget
-// (C is a multiple of 32; the slice stays a multiple of 4 dividing C). K^r
-// rows are padded by 4 floats so the lanes' 16-byte reads spread over banks.
-__host__ __device__ inline int slice_channels(int R, int C, int rows) {
-  int ck = C;
-  while (ck % 8 == 0 && ((size_t)R * (ck + 4) + (size_t)rows * ck) * 4 > kLdsBudget) ck /= 2;
-  return ck;
+// ---------------------------------------------------------------- R <= 64
+__host__ __device__ inline int col_tiles(int R) { return (R + 15) / 16; }  // also waves
+__host__ __device__ inline size_t route_lds(int R) {
+  return (size_t)16 * 16 * col_tiles(R) * sizeof(float) +
+         (size_t)col_tiles(R) * 4 * 64 * sizeof(uint64_t);
 }
 
-template <int MPL, int RPW>
-__global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict__ qr,
-                                                         const float* __restrict__ kr, int R, int C,
-                                                         int topk, float scale,
-                                                         int32_t* __restrict__ route) {
-  constexpr int kRowsPerBlock = RPW * kThreads / 64;
-  extern __shared__ __attribute__((aligned(16))) float smem[];
-  const int ck = slice_channels(R, C, kRowsPerBlock), ks_stride = ck + 4;
-  float* ks = smem;                            // [R][ck + 4]
-  float* qs = smem + (size_t)R * ks_stride;    // [rows][ck]
-  __shared__ uint64_t keys[kThreads / 64][64];
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ qr,
+                                                    const float* __restrict__ kr, int R, int C,
+                                                    int topk, float scale,
+                                                    int32_t* __restrict__ route) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int CT = col_tiles(R), RP = 16 * CT;  // padded logit row
+  const int waves = blockDim.x >> 6;
+  float* logit = reinterpret_cast<float*>(smem);                    // [16][RP]
+  uint64_t* keys = reinterpret_cast<uint64_t*>(logit + 16 * RP);    // [waves][4][64]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int blocks_per_img = (R + kRowsPerBlock - 1) / kRowsPerBlock;
-  const int n = blockIdx.x / blocks_per_img;
-  const int r0 = (blockIdx.x - n * blocks_per_img) * kRowsPerBlock;
-  const int rw0 = r0 + wave * RPW;  // this wave's first query row (rows past R: not stored)
+  const int col = lane & 15, grp = lane >> 4;
+  const int u = xcd_unit(blockIdx.x, gridDim.x);
+  const int n = u / CT;
+  const int r0 = (u - n * CT) * 16;
+  const uint32_t img_bytes = (uint32_t)R * C * 4;
+  const Rsrc qb = rsrc(qr + (size_t)n * R * C, img_bytes);
+  const Rsrc kb = rsrc(kr + (size_t)n * R * C, img_bytes);
+  const uint32_t qrow = (uint32_t)min(r0 + col, R - 1) * C * 4;
+
+  // ---- affinities: wave ct computes column tile ct
+  for (int ct = wave; ct < CT; ct += waves) {
+    const uint32_t krow = (uint32_t)min(16 * ct + col, R - 1) * C * 4;
+    uint4 a[4], b[4], an[4], bn[4];
+    auto fetch = [&](int c0, uint4* aa, uint4* bb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = c0 + 16 * j + 4 * grp;
+        aa[j] = ld16(qb, c < C ? qrow + 4 * c : kOut);
+        bb[j] = ld16(kb, c < C ? krow + 4 * c : kOut);
+      }
+    };
+    auto mfma4 = [&](f32x4 acc) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].x), __uint_as_float(b[j].x), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].y), __uint_as_float(b[j].y), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].z), __uint_as_float(b[j].z), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].w), __uint_as_float(b[j].w), acc, 0, 0, 0);
+      }
+      return acc;
+    };
+    // the next batch is always in flight while one is multiplied (the last
+    // batch is peeled off, so no branch guards the loads)
+    fetch(0, a, b);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    int c0 = 0;
+    for (; c0 + kChunk < C; c0 += kChunk) {
+      fetch(c0 + kChunk, an, bn);
+      acc = mfma4(acc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { a[j] = an[j]; b[j] = bn[j]; }
+    }
+    acc = mfma4(acc);
+    // lane (col, grp) holds rows 4grp..4grp+3 of the tile at column col
+#pragma unroll
+    for (int e = 0; e < 4; ++e) logit[(4 * grp + e) * RP + 16 * ct + col] = acc[e] * scale;
+  }
+  __syncthreads();
+
+  // ---- rank selection, rows wave, wave + waves, ... in groups of four
+  {
+    uint64_t* kw = keys + (size_t)wave * 4 * 64;  // read by this wave only
+    const int s_rd = min(lane, R - 1);
+    const int R2 = (R + 1) & ~1;
+    for (int i0 = wave; i0 < 16; i0 += 4 * waves) {
+      uint64_t key[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = i0 + q * waves;
+        const bool ok = lane < R && i < 16 && r0 + i < R;
+        key[q] = ok ? route_key(logit[min(i, 15) * RP + s_rd], lane) : 0ull;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();  // the previous group's reads of kw are done
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int q = 0; q < 4; ++q) kw[q * 64 + lane] = key[q];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // every real key is nonzero and the keys past R are 0, so the pairs
+      // may run over the padded row
+      int rank[4] = {0, 0, 0, 0};
+#pragma unroll 4
+      for (int s2 = 0; s2 < R2; s2 += 2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 two = *reinterpret_cast<const uint4*>(kw + q * 64 + s2);  // keys s2, s2+1
+          const uint64_t k0 = ((uint64_t)two.y << 32) | two.x;
+          const uint64_t k1 = ((uint64_t)two.w << 32) | two.z;
+          rank[q] += (k0 > key[q]) + (k1 > key[q]);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = i0 + q * waves;
+        if (key[q] != 0ull && rank[q] < topk)
+          route[((size_t)n * R + r0 + i) * topk + rank[q]] = lane;
+      }
+    }
+  }
+}
+
+hipError_t launch_small(const float* qr, const float* kr, int N, int R, int C, int topk,
+                        int32_t* route, hipStream_t st) {
+  const float scale = (float)(1.0 / __builtin_sqrt((double)C));
+  const unsigned blocks = (unsigned)(N * col_tiles(R));
+  hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(64 * col_tiles(R)), route_lds(R), st, qr, kr,
+                     R, C, topk, scale, route);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- R > 64
+constexpr int kWideRows = 4;   // query rows per workgroup
+constexpr int kWideBatch = 8;  // 16-byte loads per lane per batch (32 channels)
+
+template <int MPL>
+__global__ __launch_bounds__(64 * MPL) void route_wide_kernel(
+    const float* __restrict__ qr, const float* __restrict__ kr, int R, int C, int topk,
+    float scale, int32_t* __restrict__ route) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* qs = reinterpret_cast<float*>(smem);  // [4][C]
+  float* logit = qs + kWideRows * C;           // [4][64 * MPL]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int blocks_per_img = (R + kWideRows - 1) / kWideRows;
+  const int u = xcd_unit(blockIdx.x, gridDim.x);
+  const int n = u / blocks_per_img;
+  const int r0 = (u - n * blocks_per_img) * kWideRows;
   const float* krn = kr + (size_t)n * R * C;
   const float* qrn = qr + (size_t)n * R * C;
 
-  float acc[RPW][MPL];
+  // candidate s's first batch, then the Q^r rows r0..r0+3 (clamped) into LDS
+  const int s = 64 * wave + lane;
+  const float* krow = krn + (size_t)min(s, R - 1) * C;
+  float4 cur[kWideBatch], nxt[kWideBatch];
 #pragma unroll
-  for (int i = 0; i < RPW; ++i)
-#pragma unroll
-    for (int m = 0; m < MPL; ++m) acc[i][m] = 0.f;
-
-  for (int c0 = 0; c0 < C; c0 += ck) {
-    if (c0) __syncthreads();
-    const int q4 = ck / 4;  // float4 pieces per row slice
-    // batches of 8 loads in flight per thread, then their LDS stores
-    for (int e0 = tid; e0 < R * q4; e0 += 8 * kThreads) {
-      float4 buf[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int e = min(e0 + i * kThreads, R * q4 - 1);
-        const int s = e / q4, j = e - s * q4;
-        buf[i] = *reinterpret_cast<const float4*>(krn + (size_t)s * C + c0 + 4 * j);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int e = e0 + i * kThreads;
-        if (e < R * q4) {
-          const int s = e / q4, j = e - s * q4;
-          *reinterpret_cast<float4*>(ks + (size_t)s * ks_stride + 4 * j) = buf[i];
-        }
-      }
-    }
-    for (int e = tid; e < kRowsPerBlock * q4; e += kThreads) {
-      const int rr = e / q4, j = e - rr * q4;
-      const int rq = min(r0 + rr, R - 1);
-      *reinterpret_cast<float4*>(qs + (size_t)rr * ck + 4 * j) =
-          *reinterpret_cast<const float4*>(qrn + (size_t)rq * C + c0 + 4 * j);
-    }
-    __syncthreads();
-    const float* qw = qs + (size_t)wave * RPW * ck;
-#pragma unroll 4
-    for (int c = 0; c < ck; c += 4) {
-      float4 qv[RPW];
-#pragma unroll
-      for (int i = 0; i < RPW; ++i) qv[i] = *reinterpret_cast<const float4*>(qw + i * ck + c);
-#pragma unroll
-      for (int m = 0; m < MPL; ++m) {
-        const int s = min(lane + 64 * m, R - 1);
-        const float4 kv = *reinterpret_cast<const float4*>(ks + (size_t)s * ks_stride + c);
-#pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-          acc[i][m] = fmaf(qv[i].x, kv.x, acc[i][m]);
-          acc[i][m] = fmaf(qv[i].y, kv.y, acc[i][m]);
-          acc[i][m] = fmaf(qv[i].z, kv.z, acc[i][m]);
-          acc[i][m] = fmaf(qv[i].w, kv.w, acc[i][m]);
-        }
-      }
-    }
+  for (int b = 0; b < kWideBatch; ++b) cur[b] = *reinterpret_cast<const float4*>(krow + 4 * b);
+  for (int e = tid; e < kWideRows * C / 4; e += 64 * MPL) {
+    const int rr = e / (C / 4), j = e - rr * (C / 4);
+    *reinterpret_cast<float4*>(qs + rr * C + 4 * j) =
+        *reinterpret_cast<const float4*>(qrn + (size_t)min(r0 + rr, R - 1) * C + 4 * j);
   }
+  __syncthreads();
 
+  float acc[kWideRows];
 #pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-  const int r = rw0 + i;
-  if (r >= R) break;  // wave-uniform; no barrier follows
-  int32_t* out = route + ((size_t)n * R + r) * topk;
-  uint64_t key[MPL];
+  for (int i = 0; i < kWideRows; ++i) acc[i] = 0.f;
+  for (int c0 = 0; c0 < C; c0 += 4 * kWideBatch) {
+    const int cn = min(c0 + 4 * kWideBatch, C - 4 * kWideBatch);  // the last batch reloads itself
 #pragma unroll
-  for (int m = 0; m < MPL; ++m) {
-    const int s = lane + 64 * m;
-    key[m] = s < R ? route_key(acc[i][m] * scale, s) : 0ull;
-  }
-  if (MPL == 1) {
-    uint64_t* kw = keys[wave];
-    __builtin_amdgcn_wave_barrier();  // the previous row's reads of kw are done
-    kw[lane] = key[0];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (lane < R) {
-      int rank = 0;
-#pragma unroll 8
-      for (int s2 = 0; s2 < R; s2 += 2) {
-        const uint4 two = *reinterpret_cast<const uint4*>(kw + s2);  // keys s2, s2+1
-        const uint64_t k0 = ((uint64_t)two.y << 32) | two.x, k1 = ((uint64_t)two.w << 32) | two.z;
-        rank += (k0 > key[0]) + (s2 + 1 < R && k1 > key[0]);
+    for (int b = 0; b < kWideBatch; ++b) nxt[b] = *reinterpret_cast<const float4*>(krow + cn + 4 * b);
+#pragma unroll
+    for (int b = 0; b < kWideBatch; ++b) {
+#pragma unroll
+      for (int i = 0; i < kWideRows; ++i) {
+        const float4 qv = *reinterpret_cast<const float4*>(qs + i * C + c0 + 4 * b);
+        acc[i] = fmaf(qv.x, cur[b].x, acc[i]);
+        acc[i] = fmaf(qv.y, cur[b].y, acc[i]);
+        acc[i] = fmaf(qv.z, cur[b].z, acc[i]);
+        acc[i] = fmaf(qv.w, cur[b].w, acc[i]);
       }
-      if (rank < topk) out[rank] = lane;
     }
-  } else {
+#pragma unroll
+    for (int b = 0; b < kWideBatch; ++b) cur[b] = nxt[b];
+  }
+#pragma unroll
+  for (int i = 0; i < kWideRows; ++i) logit[i * 64 * MPL + s] = acc[i] * scale;
+  __syncthreads();
+
+  // rows wave, wave + MPL, ... (no barrier follows)
+  for (int i = wave; i < kWideRows && r0 + i < R; i += MPL) {
+    const float* lrow = logit + i * 64 * MPL;
+    uint64_t key[MPL];
+#pragma unroll
+    for (int m = 0; m < MPL; ++m) {
+      const int sm = lane + 64 * m;
+      key[m] = sm < R ? route_key(lrow[sm], sm) : 0ull;
+    }
+    int32_t* out = route + ((size_t)n * R + r0 + i) * topk;
     for (int p = 0; p < topk; ++p) {
       uint64_t best = 0ull;
 #pragma unroll
@@ -167,18 +270,15 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict
       if (lane == 0) out[p] = win;
     }
   }
-  }
 }
 
-template <int MPL, int RPW>
-hipError_t launch_t(const float* qr, const float* kr, int N, int R, int C, int topk,
-                    int32_t* route, hipStream_t st) {
-  constexpr int rows = RPW * kThreads / 64;
+template <int MPL>
+hipError_t launch_wide(const float* qr, const float* kr, int N, int R, int C, int topk,
+                       int32_t* route, hipStream_t st) {
   const float scale = (float)(1.0 / __builtin_sqrt((double)C));
-  const int ck = slice_channels(R, C, rows);
-  const size_t lds = ((size_t)R * (ck + 4) + (size_t)rows * ck) * sizeof(float);
-  const unsigned blocks = (unsigned)(N * ((R + rows - 1) / rows));
-  hipLaunchKernelGGL((route_kernel<MPL, RPW>), dim3(blocks), dim3(kThreads), lds, st, qr, kr, R,
+  const unsigned blocks = (unsigned)(N * ((R + kWideRows - 1) / kWideRows));
+  const size_t lds = ((size_t)kWideRows * C + (size_t)kWideRows * 64 * MPL) * sizeof(float);
+  hipLaunchKernelGGL((route_wide_kernel<MPL>), dim3(blocks), dim3(64 * MPL), lds, st, qr, kr, R,
                      C, topk, scale, route);
   return hipGetLastError();
 }
@@ -187,11 +287,11 @@ hipError_t launch_t(const float* qr, const float* kr, int N, int R, int C, int t
 
 hipError_t launch_route(const float* qr, const float* kr, int N, int R, int C, int topk,
                         int32_t* route, hipStream_t st) {
-  if (R <= 64) return launch_t<1, 4>(qr, kr, N, R, C, topk, route, st);
-  if (R <= 128) return launch_t<2, 1>(qr, kr, N, R, C, topk, route, st);
-  if (R <= 256) return launch_t<4, 1>(qr, kr, N, R, C, topk, route, st);
-  if (R <= 512) return launch_t<8, 1>(qr, kr, N, R, C, topk, route, st);
-  return launch_t<16, 1>(qr, kr, N, R, C, topk, route, st);
+  if (R <= 64) return launch_small(qr, kr, N, R, C, topk, route, st);
+  if (R <= 128) return launch_wide<2>(qr, kr, N, R, C, topk, route, st);
+  if (R <= 256) return launch_wide<4>(qr, kr, N, R, C, topk, route, st);
+  if (R <= 512) return launch_wide<8>(qr, kr, N, R, C, topk, route, st);
+  return launch_wide<16>(qr, kr, N, R, C, topk, route, st);
 }
 
 }  // namespace bra
