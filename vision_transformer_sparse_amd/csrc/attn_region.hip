@@ -71,12 +71,13 @@ struct RegionArgs {
   uint16_t* out;
   int N, H, W, S, topk;
   float qscale;            // head_dim^-1/2 * log2(e) (attention, base 2)
+  float inv_s;             // 1 / S
 };
 
 __host__ __device__ constexpr size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 struct Lds {
-  size_t halo, wts, att, total;
+  size_t halo, wts, att, sink, total;
 };
 __host__ __device__ inline Lds lds_layout(int RH, int RW, int C) {
   Lds l;
@@ -84,6 +85,7 @@ __host__ __device__ inline Lds lds_layout(int RH, int RW, int C) {
   l.halo = o; o += align16((size_t)(RH + 4) * ((RW + 5) / 2) * C * 4);
   l.wts = o; o += align16((size_t)30 * C * 4);
   l.att = o; o += align16((size_t)RH * RW * C * 4);
+  l.sink = o; o += 32;  // target of the stores of out-of-range slots; never read
   l.total = o;
   return l;
 }
@@ -102,6 +104,7 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
   uint32_t* halo = reinterpret_cast<uint32_t*>(smem + lay.halo);  // [HP][NPAIR][C]
   uint32_t* wts = reinterpret_cast<uint32_t*>(smem + lay.wts);    // [2][5][3][C]
   float* att = reinterpret_cast<float*>(smem + lay.att);          // [T][C]
+  uint32_t* sink = reinterpret_cast<uint32_t*>(smem + lay.sink);  // [8]
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -125,82 +128,86 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
   const uint32_t chb = (uint32_t)(c0 + 8 * grp) * 2;  // this lane's 8 channels
 
   // ---- A: every load of the workgroup ------------------------------------
-  // gathered K/V rows, addressed through the route indices (uniform loads)
-  const int32_t* rrow = a.route + (size_t)u * topk;
-  auto region_base = [&](int s) -> uint32_t {
-    const int js = s / S, is = s - js * S;
-    return (uint32_t)(js * RH) * rowb + (uint32_t)(is * RW) * pixb;
+  // Route indices first (one 4-byte load per lane and key tile: the index of
+  // the region that holds this lane's key), then the loads that do not depend
+  // on them (V halo, LCE weights, queries), then the gathered K/V rows they
+  // address.
+  const Rsrc rtb = rsrc(a.route + (size_t)u * topk, (uint32_t)topk * 4);
+  constexpr int NR = 16 / T;  // regions per 16-key tile
+  int rv[4];
+  auto read_routes = [&](int base) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int p = base / T + t * NR + (int)(col / T);  // past topk: read as 0, masked below
+      rv[t] = (int)__builtin_amdgcn_raw_buffer_load_b32(rtb, (uint32_t)p * 4, 0, 0);
+    }
   };
+  read_routes(0);
+
+  constexpr int NSLOT = HP * NPAIR, NIT = (NSLOT + 15) / 16;
+  constexpr uint32_t chunks = C / 8;
+  const uint32_t hch = tid % chunks, slot0 = tid / chunks;  // 16 threads per 8-channel chunk
+  uint4 va[NIT], vb[NIT];
+#pragma unroll
+  for (int i = 0; i < NIT; ++i) {
+    const int pp = slot0 + 16 * i;
+    const int pr = pp % NPAIR, py = pp / NPAIR;
+    const int y = y0 - 2 + py, x = x0 - 2 + 2 * pr;
+    const bool rowok = pp < NSLOT && y >= 0 && y < H;
+    const uint32_t hbase = (uint32_t)y * rowb + hch * 16;
+    va[i] = ld16(vbuf, rowok && x >= 0 && x < W ? hbase + (uint32_t)x * pixb : kOut);
+    vb[i] = ld16(vbuf, rowok && x + 1 >= 0 && x + 1 < W && 2 * pr + 1 < WP ? hbase + (uint32_t)(x + 1) * pixb : kOut);
+  }
+  constexpr int pieces = 30 * C / 4;  // 16-byte pieces of the packed weights, < 4 * nthreads
+  const Rsrc wb = rsrc(a.wpk, (uint32_t)pieces * 16);
+  uint4 wv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wv[i] = ld16(wb, (uint32_t)(tid + i * nthreads) * 16);
+  const uint32_t qt = col < T ? col : T - 1;
+  const bf16x8 bq = ld16_bf16(qb, (y0 + qt / RW) * rowb + (x0 + qt % RW) * pixb + chb);
+  // keep this issue order: the gathered loads below wait for the routes only
+  __builtin_amdgcn_sched_barrier(0);
+
   const uint32_t ltok = (uint32_t)(col % T);  // token of this lane's key row within its region
   const uint32_t toff = (ltok / RW) * rowb + (ltok % RW) * pixb + chb;
   bf16x8 ak[4], av[4];
-  auto fetch = [&](int base) {
+  auto fetch = [&](int base) {  // rv holds the routes of keys base .. base + 63
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int k0 = base + 16 * t;  // first key of the tile (uniform)
-      uint32_t off = kOut;           // keys past L read as zero (their scores are masked)
-      if (k0 < L) {
-        if constexpr (T == 16) {
-          off = region_base(rrow[k0 / 16]) + toff;
-        } else {
-          constexpr int NR = 16 / T;  // regions per tile, lane col/T picks one
-          const int p0 = k0 / T;
-#pragma unroll
-          for (int j = 0; j < NR; ++j) {
-            const int p = p0 + j;
-            if (p < topk && col / T == j) off = region_base(rrow[p]) + toff;
-          }
-        }
-      }
-      ak[t] = ld16_bf16(kbuf, off);
-      av[t] = ld16_bf16(vbuf, off);
+      // region (js, is) of index rv[t]: (rv + 1/2) / S is at least 1/(2S) away
+      // from an integer, so the float quotient floors exactly
+      const int js = (int)(((float)rv[t] + 0.5f) * a.inv_s), is = rv[t] - js * S;
+      const uint32_t rb = (uint32_t)(js * RH) * rowb + (uint32_t)(is * RW) * pixb;
+      // keys past L read as zero (their scores are masked)
+      const bool live = base + 16 * t + (int)(col / T) * T < L;
+      ak[t] = ld16_bf16(kbuf, live ? rb + toff : kOut);
+      av[t] = ld16_bf16(vbuf, live ? rb + toff : kOut);
     }
   };
   fetch(0);
-  const uint32_t qt = col < T ? col : T - 1;
-  const bf16x8 bq = ld16_bf16(qb, (y0 + qt / RW) * rowb + (x0 + qt % RW) * pixb + chb);
-  {
-    // the V halo: 2C threads = 16 per 8-channel chunk -> (chunk, pair slots slot0 + 16 i)
-    constexpr int NSLOT = HP * NPAIR, NIT = (NSLOT + 15) / 16;
-    constexpr uint32_t chunks = C / 8;
-    const uint32_t ch = tid % chunks, slot0 = tid / chunks;
-    uint4 va[NIT], vb[NIT];
+  __builtin_amdgcn_sched_barrier(0);  // all loads issued before the first LDS store waits
+
+  // V halo as horizontal pixel pairs per channel, weights -> LDS
+  // (stores of slots past the end go to `sink`, not behind a branch: a
+  // guarded store lets the compiler sink its load under the guard and then
+  // wait there for every load issued before it)
 #pragma unroll
-    for (int i = 0; i < NIT; ++i) {
-      const int pp = slot0 + 16 * i;
-      const int pr = pp % NPAIR, py = pp / NPAIR;
-      const int y = y0 - 2 + py, x = x0 - 2 + 2 * pr;
-      const bool rowok = pp < NSLOT && y >= 0 && y < H;
-      const uint32_t base = (uint32_t)y * rowb + ch * 16;
-      va[i] = ld16(vbuf, rowok && x >= 0 && x < W ? base + (uint32_t)x * pixb : kOut);
-      vb[i] = ld16(vbuf, rowok && x + 1 >= 0 && x + 1 < W && 2 * pr + 1 < WP ? base + (uint32_t)(x + 1) * pixb : kOut);
-    }
-    // the LCE weights (already packed for dot2) -> LDS
-    constexpr int pieces = 30 * C / 4;  // 16-byte pieces, < 4 * nthreads
-    const Rsrc wb = rsrc(a.wpk, (uint32_t)pieces * 16);
-    uint4 wv[4];
+  for (int i = 0; i < NIT; ++i) {
+    const int pp = slot0 + 16 * i;
+    // channel c of the pair: low half = left pixel, high half = right pixel
+    uint4 lo, hi;
+    lo.x = (va[i].x & 0xffffu) | (vb[i].x << 16); lo.y = (va[i].x >> 16) | (vb[i].x & 0xffff0000u);
+    lo.z = (va[i].y & 0xffffu) | (vb[i].y << 16); lo.w = (va[i].y >> 16) | (vb[i].y & 0xffff0000u);
+    hi.x = (va[i].z & 0xffffu) | (vb[i].z << 16); hi.y = (va[i].z >> 16) | (vb[i].z & 0xffff0000u);
+    hi.z = (va[i].w & 0xffffu) | (vb[i].w << 16); hi.w = (va[i].w >> 16) | (vb[i].w & 0xffff0000u);
+    uint32_t* dst = NSLOT % 16 == 0 || pp < NSLOT ? halo + (size_t)pp * C + 8 * hch : sink;
+    *reinterpret_cast<uint4*>(dst) = lo;
+    *reinterpret_cast<uint4*>(dst + 4) = hi;
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wv[i] = ld16(wb, (uint32_t)(tid + i * nthreads) * 16);
-#pragma unroll
-    for (int i = 0; i < NIT; ++i) {
-      const int pp = slot0 + 16 * i;
-      if (pp < NSLOT) {
-        // channel c of the pair: low half = left pixel, high half = right pixel
-        uint4 lo, hi;
-        lo.x = (va[i].x & 0xffffu) | (vb[i].x << 16); lo.y = (va[i].x >> 16) | (vb[i].x & 0xffff0000u);
-        lo.z = (va[i].y & 0xffffu) | (vb[i].y << 16); lo.w = (va[i].y >> 16) | (vb[i].y & 0xffff0000u);
-        hi.x = (va[i].z & 0xffffu) | (vb[i].z << 16); hi.y = (va[i].z >> 16) | (vb[i].z & 0xffff0000u);
-        hi.z = (va[i].w & 0xffffu) | (vb[i].w << 16); hi.w = (va[i].w >> 16) | (vb[i].w & 0xffff0000u);
-        uint32_t* dst = halo + (size_t)pp * C + 8 * ch;
-        *reinterpret_cast<uint4*>(dst) = lo;
-        *reinterpret_cast<uint4*>(dst + 4) = hi;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + i * nthreads;
-      if (e < pieces) reinterpret_cast<uint4*>(wts)[e] = wv[i];
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + i * nthreads;
+    *reinterpret_cast<uint4*>(e < pieces ? wts + 4 * e : sink) = wv[i];
   }
 
   // ---- B: attention, head = wave -----------------------------------------
@@ -224,7 +231,10 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
         vt[t][0] = to_bf16x4(mfma(av[t], sel0, z));
         vt[t][1] = to_bf16x4(mfma(av[t], sel1, z));
       }
-      if (base + 64 < L) fetch(base + 64);  // next chunk in flight during the softmax
+      if (base + 64 < L) {  // next chunk in flight during the softmax
+        read_routes(base + 64);
+        fetch(base + 64);
+      }
       if (base + 64 > L) {                  // ragged last chunk: mask keys past L
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -378,6 +388,7 @@ hipError_t launch_attend_region(const void* q, const void* k, const void* v, con
   a.out = (uint16_t*)out;
   a.N = s.N; a.H = s.H; a.W = s.W; a.S = s.S; a.topk = s.topk;
   a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
+  a.inv_s = 1.0f / (float)s.S;
   const size_t lds = lds_layout(s.rh, s.rw, s.C).total;
   switch (s.heads) {
     case 2: return dispatch_shape<2>(a, s, lds, st);
