@@ -103,7 +103,7 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
   const Lds lay = lds_layout(RH, RW, C);
   uint32_t* halo = reinterpret_cast<uint32_t*>(smem + lay.halo);  // [HP][NPAIR][C]
   uint32_t* wts = reinterpret_cast<uint32_t*>(smem + lay.wts);    // [2][5][3][C]
-  float* att = reinterpret_cast<float*>(smem + lay.att);          // [T][C]
+  float* lce = reinterpret_cast<float*>(smem + lay.att);          // [T][C] fp32: LCE or attention
   uint32_t* sink = reinterpret_cast<uint32_t*>(smem + lay.sink);  // [8]
 
   const int tid = threadIdx.x;
@@ -165,6 +165,9 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
   for (int i = 0; i < 4; ++i) wv[i] = ld16(wb, (uint32_t)(tid + i * nthreads) * 16);
   const uint32_t qt = col < T ? col : T - 1;
   const bf16x8 bq = ld16_bf16(qb, (y0 + qt / RW) * rowb + (x0 + qt % RW) * pixb + chb);
+  // LCE bias of this thread's channel pair (no bias: zeros)
+  const uint32_t bias2 = __builtin_amdgcn_raw_buffer_load_b32(
+      rsrc(a.b, a.b ? (uint32_t)C * 2 : 0u), (uint32_t)(tid % (C / 2)) * 4, 0, 0);
   // keep this issue order: the gathered loads below wait for the routes only
   __builtin_amdgcn_sched_barrier(0);
 
@@ -210,6 +213,61 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
     *reinterpret_cast<uint4*>(e < pieces ? wts + 4 * e : sink) = wv[i];
   }
 
+  // The LCE of this thread's item: (C/2) channel pairs x RW columns <= 2C,
+  // so at most one item per thread; acc0/acc1 get its channels c and c+1 for
+  // the RH rows of column xcol.
+  const bool has_item = tid < (C / 2) * RW;
+  const int cp = tid % (C / 2), xcol = has_item ? tid / (C / 2) : 0;
+  const int c = 2 * cp;
+  auto lce_item = [&](float* acc0, float* acc1) {
+    const uint32_t* wp = wts + (xcol & 1) * 15 * C + c;
+    uint2 wv[5][3];
+#pragma unroll
+    for (int ay = 0; ay < 5; ++ay)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) wv[ay][j] = *reinterpret_cast<const uint2*>(wp + (ay * 3 + j) * C);
+#pragma unroll
+    for (int i = 0; i < RH; ++i) { acc0[i] = bf16_lo(bias2); acc1[i] = bf16_hi(bias2); }
+    const uint32_t* hc = halo + (xcol >> 1) * C + c;
+#pragma unroll
+    for (int yy = 0; yy < HP; ++yy) {
+      const uint32_t* hr = hc + yy * NPAIR * C;
+      const uint2 h0 = *reinterpret_cast<const uint2*>(hr);
+      const uint2 h1 = *reinterpret_cast<const uint2*>(hr + C);
+      const uint2 h2 = *reinterpret_cast<const uint2*>(hr + 2 * C);
+#pragma unroll
+      for (int ay = 0; ay < 5; ++ay) {
+        const int yo = yy - ay;
+        if (yo >= 0 && yo < RH) {
+          acc0[yo] = dot2(h0.x, wv[ay][0].x, acc0[yo]);
+          acc0[yo] = dot2(h1.x, wv[ay][1].x, acc0[yo]);
+          acc0[yo] = dot2(h2.x, wv[ay][2].x, acc0[yo]);
+          acc1[yo] = dot2(h0.y, wv[ay][0].y, acc1[yo]);
+          acc1[yo] = dot2(h1.y, wv[ay][1].y, acc1[yo]);
+          acc1[yo] = dot2(h2.y, wv[ay][2].y, acc1[yo]);
+        }
+      }
+    }
+  };
+
+  // Two orders of the phases, fixed per shape. With eight heads (512
+  // threads, two workgroups per CU) the LCE runs first, while the gathered
+  // K/V are still in flight, and the attention waves add it to their output;
+  // with fewer heads (four workgroups per CU, which already cover each
+  // other's latency) the attention runs first and the LCE threads merge.
+  constexpr bool kLceFirst = HEADS >= 8;
+  if constexpr (kLceFirst) {
+    __syncthreads();  // halo and weights staged
+    if (has_item) {
+      float acc0[RH], acc1[RH];
+      lce_item(acc0, acc1);
+#pragma unroll
+      for (int yo = 0; yo < RH; ++yo)
+        *reinterpret_cast<float2*>(lce + (yo * RW + xcol) * C + c) = make_float2(acc0[yo], acc1[yo]);
+    }
+    __syncthreads();  // the LCE of every channel staged
+  }
+
   // ---- B: attention, head = wave -----------------------------------------
   {
     bf16x8 sel0, sel1, ones;
@@ -222,6 +280,13 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
     float m = -INFINITY;  // running max of the scaled (base-2) logits
     f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0, ls = o0;
     for (int base = 0; base < L; base += 64) {
+      // keys past the first 64 (topk * T > 64): their routes, then their
+      // rows, loaded in turn (prefetching them during the softmax would cost
+      // about 30 more registers per lane in every shape)
+      if (base > 0) {
+        read_routes(base);
+        fetch(base);
+      }
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
       f32x4 s[4];
       bf16x4 vt[4][2];
@@ -230,10 +295,6 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
         s[t] = mfma(ak[t], bq, z);
         vt[t][0] = to_bf16x4(mfma(av[t], sel0, z));
         vt[t][1] = to_bf16x4(mfma(av[t], sel1, z));
-      }
-      if (base + 64 < L) {  // next chunk in flight during the softmax
-        read_routes(base + 64);
-        fetch(base + 64);
       }
       if (base + 64 > L) {                  // ragged last chunk: mask keys past L
 #pragma unroll
@@ -275,57 +336,40 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
     }
     const float inv = 1.0f / ls[0];
     if (col < T) {
-      float* ap = att + col * C + c0;
-      *reinterpret_cast<float4*>(ap + 4 * grp) = make_float4(o0[0] * inv, o0[1] * inv, o0[2] * inv, o0[3] * inv);
-      *reinterpret_cast<float4*>(ap + 16 + 4 * grp) = make_float4(o1[0] * inv, o1[1] * inv, o1[2] * inv, o1[3] * inv);
-    }
-  }
-  __syncthreads();
-
-  // ---- C: LCE (dot2 sliding window), merge, store --------------------------
-  for (int it = tid; it < (C / 2) * RW; it += nthreads) {
-    const int cp = it % (C / 2), xcol = it / (C / 2);
-    const int c = 2 * cp;
-    const uint32_t* wp = wts + (xcol & 1) * 15 * C + c;
-    uint2 wv[5][3];
-#pragma unroll
-    for (int ay = 0; ay < 5; ++ay)
-#pragma unroll
-      for (int j = 0; j < 3; ++j) wv[ay][j] = *reinterpret_cast<const uint2*>(wp + (ay * 3 + j) * C);
-    float b0 = 0.f, b1 = 0.f;
-    if (a.b) {
-      const uint32_t bb = *reinterpret_cast<const uint32_t*>(a.b + c);
-      b0 = bf16_lo(bb);
-      b1 = bf16_hi(bb);
-    }
-    float acc0[RH], acc1[RH];
-#pragma unroll
-    for (int i = 0; i < RH; ++i) { acc0[i] = b0; acc1[i] = b1; }
-    const uint32_t* hc = halo + (xcol >> 1) * C + c;
-#pragma unroll
-    for (int yy = 0; yy < HP; ++yy) {
-      const uint32_t* hr = hc + yy * NPAIR * C;
-      const uint2 h0 = *reinterpret_cast<const uint2*>(hr);
-      const uint2 h1 = *reinterpret_cast<const uint2*>(hr + C);
-      const uint2 h2 = *reinterpret_cast<const uint2*>(hr + 2 * C);
-#pragma unroll
-      for (int ay = 0; ay < 5; ++ay) {
-        const int yo = yy - ay;
-        if (yo >= 0 && yo < RH) {
-          acc0[yo] = dot2(h0.x, wv[ay][0].x, acc0[yo]);
-          acc0[yo] = dot2(h1.x, wv[ay][1].x, acc0[yo]);
-          acc0[yo] = dot2(h2.x, wv[ay][2].x, acc0[yo]);
-          acc1[yo] = dot2(h0.y, wv[ay][0].y, acc1[yo]);
-          acc1[yo] = dot2(h1.y, wv[ay][1].y, acc1[yo]);
-          acc1[yo] = dot2(h2.y, wv[ay][2].y, acc1[yo]);
-        }
+      if constexpr (kLceFirst) {
+        // out = attention + LCE for query col, channels c0+4grp.. and c0+16+4grp..
+        const float* lp = lce + col * C + c0 + 4 * grp;
+        const float4 l0 = *reinterpret_cast<const float4*>(lp);
+        const float4 l1 = *reinterpret_cast<const float4*>(lp + 16);
+        uint2 p0, p1;
+        p0.x = float_to_bf16_bits(fmaf(o0[0], inv, l0.x)) | (float_to_bf16_bits(fmaf(o0[1], inv, l0.y)) << 16);
+        p0.y = float_to_bf16_bits(fmaf(o0[2], inv, l0.z)) | (float_to_bf16_bits(fmaf(o0[3], inv, l0.w)) << 16);
+        p1.x = float_to_bf16_bits(fmaf(o1[0], inv, l1.x)) | (float_to_bf16_bits(fmaf(o1[1], inv, l1.y)) << 16);
+        p1.y = float_to_bf16_bits(fmaf(o1[2], inv, l1.z)) | (float_to_bf16_bits(fmaf(o1[3], inv, l1.w)) << 16);
+        uint16_t* op = a.out + img + ((size_t)(y0 + col / RW) * W + x0 + col % RW) * C + c0 + 4 * grp;
+        *reinterpret_cast<uint2*>(op) = p0;
+        *reinterpret_cast<uint2*>(op + 16) = p1;
+      } else {
+        // the head's output -> LDS, for the LCE threads to merge
+        float* ap = lce + col * C + c0;
+        *reinterpret_cast<float4*>(ap + 4 * grp) = make_float4(o0[0] * inv, o0[1] * inv, o0[2] * inv, o0[3] * inv);
+        *reinterpret_cast<float4*>(ap + 16 + 4 * grp) = make_float4(o1[0] * inv, o1[1] * inv, o1[2] * inv, o1[3] * inv);
       }
     }
+  }
+
+  if constexpr (!kLceFirst) {
+    __syncthreads();  // every head's output staged
+    // ---- C: LCE, merged with the attention output, stored as bf16 pairs
+    if (has_item) {
+      float acc0[RH], acc1[RH];
+      lce_item(acc0, acc1);
 #pragma unroll
-    for (int yo = 0; yo < RH; ++yo) {
-      const float2 at = *reinterpret_cast<const float2*>(att + (yo * RW + xcol) * C + c);
-      const uint32_t packed = float_to_bf16_bits(at.x + acc0[yo]) | (float_to_bf16_bits(at.y + acc1[yo]) << 16);
-      *reinterpret_cast<uint32_t*>(a.out + img + ((size_t)(y0 + yo) * W + x0 + xcol) * C + c) = packed;
+      for (int yo = 0; yo < RH; ++yo) {
+        const float2 at = *reinterpret_cast<const float2*>(lce + (yo * RW + xcol) * C + c);
+        const uint32_t packed = float_to_bf16_bits(at.x + acc0[yo]) | (float_to_bf16_bits(at.y + acc1[yo]) << 16);
+        *reinterpret_cast<uint32_t*>(a.out + img + ((size_t)(y0 + yo) * W + x0 + xcol) * C + c) = packed;
+      }
     }
   }
 }
