@@ -115,8 +115,9 @@ int bra_set_stream(void* stream);
 void* bra_get_stream(void);
 
 /* Bytes of library workspace bra_forward needs: two fp32 [N][S*S][C]
- * arrays (region means), 256-byte aligned, then 120*C bytes of LCE weights
- * repacked for the small-region kernel. Returns 0 for invalid sizes. */
+ * arrays (region means), 256-byte aligned, then 170*C bytes of LCE weights
+ * repacked for the attention kernels (pixel-pair and tap-major layouts).
+ * Returns 0 for invalid sizes. */
 size_t bra_workspace_bytes(int N, int C, int S);
 
 /* Frees the library workspace of every device (synchronises each device

@@ -50,7 +50,8 @@ def test_version_and_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.bra_workspace_bytes(128, 128, 7) == 2 * 128 * 49 * 128 * 4 + 120 * 128
+    # region means of q and k, then the packed LCE weights (30*C + 25*C/2 dwords)
+    assert lib.bra_workspace_bytes(128, 128, 7) == 2 * 128 * 49 * 128 * 4 + 170 * 128
     assert lib.bra_workspace_bytes(0, 128, 7) == 0
 
 

@@ -83,7 +83,7 @@ __host__ __device__ inline Lds lds_layout(int RH, int RW, int C) {
   Lds l;
   size_t o = 0;
   l.halo = o; o += align16((size_t)(RH + 4) * ((RW + 5) / 2) * C * 4);
-  l.wts = o; o += align16((size_t)30 * C * 4);
+  l.wts = o; o += align16((size_t)25 * (C / 2) * 4);
   l.att = o; o += align16((size_t)RH * RW * C * 4);
   l.sink = o; o += 32;  // target of the stores of out-of-range slots; never read
   l.total = o;
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
   const int L = topk * T;
   const Lds lay = lds_layout(RH, RW, C);
   uint32_t* halo = reinterpret_cast<uint32_t*>(smem + lay.halo);  // [HP][NPAIR][C]
-  uint32_t* wts = reinterpret_cast<uint32_t*>(smem + lay.wts);    // [2][5][3][C]
+  uint32_t* wts = reinterpret_cast<uint32_t*>(smem + lay.wts);    // [25 taps][C/2] channel pairs
   float* lce = reinterpret_cast<float*>(smem + lay.att);          // [T][C] fp32: LCE or attention
   uint32_t* sink = reinterpret_cast<uint32_t*>(smem + lay.sink);  // [8]
 
@@ -158,11 +158,12 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
     va[i] = ld16(vbuf, rowok && x >= 0 && x < W ? hbase + (uint32_t)x * pixb : kOut);
     vb[i] = ld16(vbuf, rowok && x + 1 >= 0 && x + 1 < W && 2 * pr + 1 < WP ? hbase + (uint32_t)(x + 1) * pixb : kOut);
   }
-  constexpr int pieces = 30 * C / 4;  // 16-byte pieces of the packed weights, < 4 * nthreads
-  const Rsrc wb = rsrc(a.wpk, (uint32_t)pieces * 16);
-  uint4 wv[4];
+  // the LCE weights, tap-major channel pairs (after the pixel-pair layout)
+  constexpr int pieces = 25 * C / 8;  // 16-byte pieces, < 2 * nthreads
+  const Rsrc wb = rsrc(a.wpk + 30 * C, (uint32_t)pieces * 16);
+  uint4 wv[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) wv[i] = ld16(wb, (uint32_t)(tid + i * nthreads) * 16);
+  for (int i = 0; i < 2; ++i) wv[i] = ld16(wb, (uint32_t)(tid + i * nthreads) * 16);
   const uint32_t qt = col < T ? col : T - 1;
   const bf16x8 bq = ld16_bf16(qb, (y0 + qt / RW) * rowb + (x0 + qt % RW) * pixb + chb);
   // LCE bias of this thread's channel pair (no bias: zeros)
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
     *reinterpret_cast<uint4*>(dst + 4) = hi;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
     const int e = tid + i * nthreads;
     *reinterpret_cast<uint4*>(e < pieces ? wts + 4 * e : sink) = wv[i];
   }
@@ -220,12 +221,24 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
   const int cp = tid % (C / 2), xcol = has_item ? tid / (C / 2) : 0;
   const int c = 2 * cp;
   auto lce_item = [&](float* acc0, float* acc1) {
-    const uint32_t* wp = wts + (xcol & 1) * 15 * C + c;
+    // pixel-pair weights from the tap weights: an even column pairs taps
+    // (0,1) (2,3) (4,-); an odd one starts a pixel earlier: (-,0) (1,2) (3,4).
+    // x: channel c (low halves), y: channel c+1 (high halves).
+    const bool even = (xcol & 1) == 0;
     uint2 wv[5][3];
 #pragma unroll
-    for (int ay = 0; ay < 5; ++ay)
+    for (int ay = 0; ay < 5; ++ay) {
+      uint32_t d[5];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) wv[ay][j] = *reinterpret_cast<const uint2*>(wp + (ay * 3 + j) * C);
+      for (int ax = 0; ax < 5; ++ax) d[ax] = wts[(5 * ay + ax) * (C / 2) + cp];
+      const uint32_t e6[6] = {even ? d[0] : 0u, even ? d[1] : d[0], even ? d[2] : d[1],
+                              even ? d[3] : d[2], even ? d[4] : d[3], even ? 0u : d[4]};
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        wv[ay][j].x = __builtin_amdgcn_perm(e6[2 * j + 1], e6[2 * j], 0x05040100u);
+        wv[ay][j].y = __builtin_amdgcn_perm(e6[2 * j + 1], e6[2 * j], 0x07060302u);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < RH; ++i) { acc0[i] = bf16_lo(bias2); acc1[i] = bf16_hi(bias2); }
     const uint32_t* hc = halo + (xcol >> 1) * C + c;
@@ -377,7 +390,7 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
 __global__ __launch_bounds__(256) void lce_pack_kernel(const uint16_t* __restrict__ w, int C,
                                                        uint32_t* __restrict__ wpk) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e < 15 * C) pack_lce_entry(w, C, e, wpk);
+  if (e < lce_pack_items(C)) pack_lce_item(w, C, e, wpk);
 }
 
 template <int RH, int RW, int HEADS>
@@ -408,10 +421,10 @@ hipError_t dispatch_shape(const RegionArgs& a, const Shape& s, size_t lds, hipSt
 
 }  // namespace
 
-size_t lce_pack_bytes(int C) { return (size_t)30 * C * 4; }
+size_t lce_pack_bytes(int C) { return ((size_t)30 * C + (size_t)25 * (C / 2)) * 4; }
 
 hipError_t launch_lce_pack(const void* w, int C, uint32_t* wpk, hipStream_t st) {
-  hipLaunchKernelGGL(lce_pack_kernel, dim3((unsigned)((15 * C + 255) / 256)), dim3(256), 0, st,
+  hipLaunchKernelGGL(lce_pack_kernel, dim3((unsigned)((lce_pack_items(C) + 255) / 256)), dim3(256), 0, st,
                      (const uint16_t*)w, C, wpk);
   return hipGetLastError();
 }

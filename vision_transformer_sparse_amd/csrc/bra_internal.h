@@ -71,20 +71,31 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
   return u >> 16;
 }
 
-// One entry of the LCE weights repacked for packed-bf16 dot products:
-// [C][5][5] bf16 -> [parity][row][pair][C] pairs. For an even output column
-// the pixel pairs start at tap 0 ((w0,w1),(w2,w3),(w4,0)); for an odd one a
-// pixel earlier ((0,w0),(w1,w2),(w3,w4)). e indexes row*3+pair major, C minor.
-__device__ __forceinline__ void pack_lce_entry(const uint16_t* __restrict__ lw, int C, int e,
-                                               uint32_t* __restrict__ wpk) {
-  const int c = e % C, rest = e / C;
-  const int ay = rest / 3, d0 = 2 * (rest % 3);
-  const uint16_t* wr = lw + (size_t)c * 25 + ay * 5;
-  const uint32_t t0 = wr[d0];
-  const uint32_t t1 = d0 + 1 < 5 ? (uint32_t)wr[d0 + 1] : 0u;
-  const uint32_t tm = d0 > 0 ? (uint32_t)wr[d0 - 1] : 0u;
-  wpk[rest * C + c] = t0 | (t1 << 16);
-  wpk[(15 + rest) * C + c] = tm | (t0 << 16);
+// The LCE weights repacked for packed-bf16 dot products, two layouts in one
+// buffer of lce_pack_items(C) entries:
+//  * [parity][row][pair][C] dwords (30*C): pixel-pair weights. For an even
+//    output column the pixel pairs start at tap 0 ((w0,w1),(w2,w3),(w4,0));
+//    for an odd one a pixel earlier ((0,w0),(w1,w2),(w3,w4)). Entry e < 15*C
+//    (row*3+pair major, C minor) writes one dword of each parity.
+//  * then [tap][C/2] dwords (25*C/2): the weights of channels 2p and 2p+1
+//    for tap t (= 5*row + column) in one dword (low half: channel 2p).
+__host__ __device__ inline int lce_pack_items(int C) { return 15 * C + 25 * (C / 2); }
+__device__ __forceinline__ void pack_lce_item(const uint16_t* __restrict__ lw, int C, int e,
+                                              uint32_t* __restrict__ wpk) {
+  if (e < 15 * C) {
+    const int c = e % C, rest = e / C;
+    const int ay = rest / 3, d0 = 2 * (rest % 3);
+    const uint16_t* wr = lw + (size_t)c * 25 + ay * 5;
+    const uint32_t t0 = wr[d0];
+    const uint32_t t1 = d0 + 1 < 5 ? (uint32_t)wr[d0 + 1] : 0u;
+    const uint32_t tm = d0 > 0 ? (uint32_t)wr[d0 - 1] : 0u;
+    wpk[rest * C + c] = t0 | (t1 << 16);
+    wpk[(15 + rest) * C + c] = tm | (t0 << 16);
+  } else {
+    const int e2 = e - 15 * C;
+    const int t = e2 / (C / 2), p = e2 - t * (C / 2);
+    wpk[30 * C + e2] = (uint32_t)lw[(size_t)(2 * p) * 25 + t] | ((uint32_t)lw[(size_t)(2 * p + 1) * 25 + t] << 16);
+  }
 }
 
 template <typename T> struct Elem;

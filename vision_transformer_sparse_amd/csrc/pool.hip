@@ -55,8 +55,8 @@ __global__ __launch_bounds__(256) void region_pool_kernel(
 
   // Side job: the LCE weights repacked for the attention kernel's dot2s.
   if (wpk)
-    for (int e = blockIdx.x * blockDim.x + tid; e < 15 * C; e += gridDim.x * blockDim.x)
-      pack_lce_entry(lw, C, e, wpk);
+    for (int e = blockIdx.x * blockDim.x + tid; e < lce_pack_items(C); e += gridDim.x * blockDim.x)
+      pack_lce_item(lw, C, e, wpk);
 
   float aq[V], ak[V];
 #pragma unroll
