@@ -137,11 +137,14 @@ int bra_version(void);
  * later ones are not recorded) and clears earlier records; mask 0 stops
  * recording. bra_profile_read waits for the recorded events, then writes for
  * each kind k < n the summed milliseconds and the launch count, and clears
- * the record. Each recorded kernel costs two event records on the stream. */
+ * the record. Each recorded kernel costs two event records on the stream.
+ * bra_profile_set_mask(mask) changes which kinds are recorded from the next
+ * launch on without clearing the record (to sample some launches of a run). */
 enum bra_kernel_kind {
   BRA_K_POOL = 0, BRA_K_ROUTE = 1, BRA_K_ATTN = 2, BRA_K_LCE = 3, BRA_K_COUNT = 4
 };
 int bra_profile_begin(int mask);
+int bra_profile_set_mask(int mask);
 int bra_profile_read(double* ms, int* counts, int n);
 
 /* A plain device-to-device copy kernel (bytes % 16 == 0, both pointers

@@ -204,8 +204,24 @@ def test_profile_counts(gpu_lib):
         gpu_lib.forward(*args, cfg.heads, cfg.S, cfg.topk)
     rec = gpu_lib.profile_read()
     gpu_lib.profile_begin(())
-    # small regions (this workload) run the routing inside the attention kernel
-    assert rec["pool"][1] == 3 and rec["route"][1] in (0, 3) and rec["attn"][1] == 3
+    assert rec["pool"][1] == 3 and rec["route"][1] == 3 and rec["attn"][1] == 3
+    assert rec["attn"][0] > 0
+
+
+def test_profile_sampling(gpu_lib):
+    """profile_set_mask switches recording on and off between launches
+    without discarding the record: only the sampled launches are counted."""
+    cfg = CONFIGS[1]
+    inp = draw_config(cfg, N=2)
+    args = [dev(inp[x], cfg.dtype) for x in ("q", "k", "v", "lce_w", "lce_b")]
+    say("profile sampling")
+    gpu_lib.profile_begin(())
+    for i in range(6):
+        gpu_lib.profile_set_mask(["attn"] if i % 3 == 0 else ())
+        gpu_lib.forward(*args, cfg.heads, cfg.S, cfg.topk)
+    gpu_lib.profile_set_mask(())
+    rec = gpu_lib.profile_read()
+    assert rec["attn"][1] == 2 and rec["pool"][1] == 0 and rec["route"][1] == 0
     assert rec["attn"][0] > 0
 
 

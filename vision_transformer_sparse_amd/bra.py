@@ -36,6 +36,7 @@ _SIGS = {
     "bra_error_string": (ctypes.c_char_p, [_i]),
     "bra_version": (_i, []),
     "bra_profile_begin": (_i, [_i]),
+    "bra_profile_set_mask": (_i, [_i]),
     "bra_profile_read": (_i, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int), _i]),
     "bra_calib_copy": (_i, [_vp, _vp, _sz]),
 }
@@ -219,6 +220,15 @@ def profile_begin(kinds=KERNEL_NAMES) -> None:
     for k in (kinds or ()):
         mask |= 1 << KERNEL_NAMES.index(k)
     _call("bra_profile_begin", mask)
+
+
+def profile_set_mask(kinds=KERNEL_NAMES) -> None:
+    """Changes which kernel kinds are recorded from the next launch on,
+    keeping what was recorded so far."""
+    mask = 0
+    for k in (kinds or ()):
+        mask |= 1 << KERNEL_NAMES.index(k)
+    _call("bra_profile_set_mask", mask)
 
 
 def profile_read() -> dict:

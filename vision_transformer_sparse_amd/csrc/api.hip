@@ -374,6 +374,12 @@ int bra_profile_begin(int mask) {
   return BRA_OK;
 }
 
+int bra_profile_set_mask(int mask) {
+  std::lock_guard<std::mutex> lk(g_prof_mutex);
+  g_prof_mask = mask & ((1 << BRA_K_COUNT) - 1);
+  return BRA_OK;
+}
+
 int bra_profile_read(double* ms, int* counts, int n) {
   if (!ms || !counts) return BRA_ERR_NULL;
   std::lock_guard<std::mutex> lk(g_prof_mutex);
