@@ -8,8 +8,10 @@
 // One workgroup (4 waves) per (image, region, head). The gathered keys are
 // walked in 64-key tiles: all 256 threads fetch a tile's K and V rows by
 // route index (16 bytes each) one tile ahead into registers, then park them
-// in LDS -- K row-major, V transposed (keys contiguous per channel), so both
-// MFMA operands are single 16-byte LDS reads. Each wave owns T/64 blocks of
+// in LDS row-major. A K operand is one 16-byte LDS read; a V^T operand (eight
+// consecutive keys of one channel per lane) is two transposing LDS reads
+// (ds_read_b64_tr_b16: the 16 lanes of a group read a 4-key x 16-channel
+// block and each gets one channel's 4 keys). Each wave owns T/64 blocks of
 // 16 queries and reuses every K / V^T operand read for all of them:
 //
 //   S^T(16 keys x 16 queries) = K (A: lane = key row) x Q^T (B: lane = query)
@@ -18,9 +20,12 @@
 // Inside each 32-key block the K rows fed to the two score tiles are
 // permuted (tile 0 row 4g+e <- key 8g+e, tile 1 row 4g+e <- key 8g+4+e) so
 // that a lane's eight scores are eight CONSECUTIVE keys: P^T needs no
-// shuffle and V^T is one ds_read_b128. Softmax in fp32, base 2, online
-// across tiles; P is rounded to bf16 for the products and the row sums are
-// taken over that same bf16 P on the matrix cores.
+// shuffle. Softmax in fp32, base 2, online across tiles; P is rounded to
+// bf16 for the products and the row sums are taken over that same bf16 P on
+// the matrix cores. The running maximum is raised only when a tile's maximum
+// exceeds it by more than kTau (then P may reach 2^kTau, which bf16 and the
+// fp32 sums hold), so the rescale of the accumulators is rare; the tile
+// maximum is a maximum3 tree and two cross-half lane swaps.
 //
 // LCE (5x5 depthwise, zero padding 2, bias): the head's 32 channels of the
 // V halo (RH+4 x RW+4 pixels) are staged as horizontal pixel pairs and the
@@ -36,8 +41,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kKStr = 40;               // K tile row stride (bf16): 32 dims + 8 pad
-constexpr int kVStr = 72;               // V^T tile row stride (bf16): 64 keys + 8 pad
+constexpr int kKStr = 40;   // K and V tile row stride (bf16): 32 dims + 8 pad
+constexpr float kTau = 8.f;  // slack of the running maximum (log2 units)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
@@ -50,6 +55,27 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
 }
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+// maximum over the lanes l, l^16, l^32, l^48 (the four key groups of a query)
+__device__ __forceinline__ float group_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // {x[l & ~16], x[l | 16]}
+  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);  // {x[l & 31], x[l | 32]}
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// Transposing LDS read: within each group of 16 lanes, lanes 4r..4r+3 give
+// the address of row r's 16 consecutive bf16 (4 each); lane i gets element i
+// of rows 0..3.
+__device__ __forceinline__ bf16x4 ld_tr(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<uint16_t*>(p)));
+  return __builtin_bit_cast(bf16x4, v);
 }
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
@@ -71,13 +97,13 @@ struct TileArgs {
 __host__ __device__ constexpr size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 struct TileLds {
-  size_t ks, vt, halo, wts, total;
+  size_t ks, vs, halo, wts, total;
 };
 __host__ __device__ inline TileLds tile_lds(int RH, int RW) {
   TileLds l;
   size_t o = 0;
   l.ks = o; o += align16((size_t)2 * 64 * kKStr * 2);
-  l.vt = o; o += align16((size_t)2 * 32 * kVStr * 2);
+  l.vs = o; o += align16((size_t)2 * 64 * kKStr * 2);
   l.halo = o; o += align16((size_t)(RH + 4) * ((RW + 5) / 2) * 32 * 4);
   l.wts = o; o += align16((size_t)2 * 15 * 32 * 4);
   l.total = o;
@@ -92,7 +118,7 @@ __global__ __launch_bounds__(256, 2) void attn_tile_kernel(TileArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const TileLds lay = tile_lds(RH, RW);
   uint16_t* ks = reinterpret_cast<uint16_t*>(smem + lay.ks);    // [2][64][kKStr]
-  uint16_t* vt = reinterpret_cast<uint16_t*>(smem + lay.vt);    // [2][32][kVStr]
+  uint16_t* vs = reinterpret_cast<uint16_t*>(smem + lay.vs);    // [2][64][kKStr]
   uint32_t* halo = reinterpret_cast<uint32_t*>(smem + lay.halo);  // [HP][NPAIR][32]
   uint32_t* wts = reinterpret_cast<uint32_t*>(smem + lay.wts);    // [2][15][32]
 
@@ -133,13 +159,7 @@ __global__ __launch_bounds__(256, 2) void attn_tile_kernel(TileArgs a) {
   };
   auto park = [&](int buf) {
     *reinterpret_cast<uint4*>(ks + (buf * 64 + ld_key) * kKStr + ld_g * 8) = kreg;
-    uint16_t* vd = vt + buf * 32 * kVStr + (ld_g * 8) * kVStr + ld_key;
-    const uint32_t w4[4] = {vreg.x, vreg.y, vreg.z, vreg.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      vd[(2 * i) * kVStr] = (uint16_t)(w4[i] & 0xffffu);
-      vd[(2 * i + 1) * kVStr] = (uint16_t)(w4[i] >> 16);
-    }
+    *reinterpret_cast<uint4*>(vs + (buf * 64 + ld_key) * kKStr + ld_g * 8) = vreg;
   };
 
   fetch(0);
@@ -207,6 +227,9 @@ __global__ __launch_bounds__(256, 2) void attn_tile_kernel(TileArgs a) {
 
   // A-operand rows of the two score tiles of a 32-key block (see header)
   const int krow0 = 8 * (col >> 2) + (col & 3), krow1 = krow0 + 4;
+  // V^T operand addresses: this lane gives row 8grp + col/4 (+4), channels
+  // 4*(col%4) .. +3 of each 16-channel half
+  const int vrow = 8 * grp + (col >> 2), vch = 4 * (col & 3);
 
   const int ntiles = L / 64;
   park(0);
@@ -215,14 +238,16 @@ __global__ __launch_bounds__(256, 2) void attn_tile_kernel(TileArgs a) {
     __syncthreads();  // tile `buf` parked; the other buffer is free
     if (tile + 1 < ntiles) fetch(tile + 1);
     const uint16_t* kt = ks + buf * 64 * kKStr;
-    const uint16_t* vtt = vt + buf * 32 * kVStr;
+    const uint16_t* vtl = vs + buf * 64 * kKStr;
     bf16x8 ka[4], va0[2], va1[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       ka[2 * b] = as_bf16x8(*reinterpret_cast<const uint4*>(kt + (32 * b + krow0) * kKStr + grp * 8));
       ka[2 * b + 1] = as_bf16x8(*reinterpret_cast<const uint4*>(kt + (32 * b + krow1) * kKStr + grp * 8));
-      va0[b] = as_bf16x8(*reinterpret_cast<const uint4*>(vtt + col * kVStr + 32 * b + 8 * grp));
-      va1[b] = as_bf16x8(*reinterpret_cast<const uint4*>(vtt + (16 + col) * kVStr + 32 * b + 8 * grp));
+      // keys 32b + 8grp .. +7 of channel col (va0) and 16 + col (va1)
+      const uint16_t* vr = vtl + (32 * b + vrow) * kKStr + vch;
+      va0[b] = cat(ld_tr(vr), ld_tr(vr + 4 * kKStr));
+      va1[b] = cat(ld_tr(vr + 16), ld_tr(vr + 4 * kKStr + 16));
     }
 #pragma unroll
     for (int i = 0; i < QBW; ++i) {
@@ -230,15 +255,16 @@ __global__ __launch_bounds__(256, 2) void attn_tile_kernel(TileArgs a) {
       f32x4 s[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) s[t] = mfma(ka[t], bq[i], z);
-      float cm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-      cm = fmaxf(cm, fmaxf(fmaxf(fmaxf(s[2][0], s[2][1]), fmaxf(s[2][2], s[2][3])),
-                           fmaxf(fmaxf(s[3][0], s[3][1]), fmaxf(s[3][2], s[3][3]))));
-      cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-      cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-      const float mn = fmaxf(m[i], cm * a.qscale);
-      if (mn > m[i]) {  // rescale only when the running max grows (first tile: from zero)
-        const float corr = __builtin_amdgcn_exp2f(m[i] - mn);
+      // this tile's maximum for the lane's query (16 scores here, 64 in all)
+      const float c0 = max3(s[0][0], s[0][1], s[0][2]), c1 = max3(s[0][3], s[1][0], s[1][1]);
+      const float c2 = max3(s[1][2], s[1][3], s[2][0]), c3 = max3(s[2][1], s[2][2], s[2][3]);
+      const float c4 = max3(s[3][0], s[3][1], s[3][2]);
+      const float cm = group_max(max3(max3(c0, c1, c2), max3(c3, c4, s[3][3]), c4)) * a.qscale;
+      // raise the running maximum (and rescale) only when the tile's exceeds
+      // it by more than kTau somewhere in the wave (first tile: always)
+      if (__builtin_amdgcn_ballot_w64(cm > m[i] + kTau) != 0) {
+        const float mn = __builtin_elementwise_maximum(m[i], cm);
+        const float corr = __builtin_amdgcn_exp2f(m[i] - mn);  // 0 on the first tile
         o0[i] *= corr;
         o1[i] *= corr;
         ls[i] *= corr;
