@@ -5,10 +5,12 @@
 // BRA模块: each query region attends, per head, to the tokens of its topk
 // routed regions (topk*T keys, one joint softmax), plus LCE(V).
 //
-// One workgroup (4 waves) per (image, region, head). The gathered keys are
-// walked in 64-key tiles: all 256 threads fetch a tile's K and V rows by
-// route index (16 bytes each) one tile ahead into registers, then park them
-// in LDS row-major. A K operand is one 16-byte LDS read; a V^T operand (eight
+// One workgroup per (image, region, head): 8 waves for regions of 128 or
+// more tokens (so that a wave keeps at most two 16-query blocks in registers
+// and four waves share a SIMD), else 4. The gathered keys are walked in
+// 64-key tiles: 256 threads fetch a tile's K and V rows by route index (16
+// bytes each) one tile ahead into registers, then park them in LDS
+// row-major. A K operand is one 16-byte LDS read; a V^T operand (eight
 // consecutive keys of one channel per lane) is two transposing LDS reads
 // (ds_read_b64_tr_b16: the 16 lanes of a group read a 4-key x 16-channel
 // block and each gets one channel's 4 keys). Each wave owns T/64 blocks of
@@ -22,10 +24,14 @@
 // that a lane's eight scores are eight CONSECUTIVE keys: P^T needs no
 // shuffle. Softmax in fp32, base 2, online across tiles; P is rounded to
 // bf16 for the products and the row sums are taken over that same bf16 P on
-// the matrix cores. The running maximum is raised only when a tile's maximum
-// exceeds it by more than kTau (then P may reach 2^kTau, which bf16 and the
-// fp32 sums hold), so the rescale of the accumulators is rare; the tile
-// maximum is a maximum3 tree and two cross-half lane swaps.
+// the matrix cores. The running maximum m is raised only when a score may
+// exceed it by more than kTau (then P may reach 2^kTau, which bf16 and the
+// fp32 sums hold). Whether one may is first decided from norms: a scaled
+// score is at most qscale*|q|*max|k| (Cauchy-Schwarz), with |q| computed
+// once and max|k| per tile by the waves that load it; only when that bound
+// exceeds m + kTau somewhere in the wave (always on the first tile) is the
+// tile's exact maximum taken (a maximum3 tree and two cross-half lane
+// swaps) and the accumulators rescaled.
 //
 // LCE (5x5 depthwise, zero padding 2, bias): the head's 32 channels of the
 // V halo (RH+4 x RW+4 pixels) are staged as horizontal pixel pairs and the
@@ -42,7 +48,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kKStr = 40;   // K and V tile row stride (bf16): 32 dims + 8 pad
-constexpr float kTau = 8.f;  // slack of the running maximum (log2 units)
+constexpr float kTau = 64.f;  // slack of the running maximum (log2 units); 2^64 * keys << FLT_MAX
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
@@ -67,6 +73,41 @@ __device__ __forceinline__ float group_max(float x) {
   const uint32_t w = __float_as_uint(x);
   const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);  // {x[l & 31], x[l | 32]}
   return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+// sum over the lanes l, l^16, l^32, l^48
+__device__ __forceinline__ float group_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t w = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// max of x and its DPP-moved copy (lanes the pattern leaves out keep x)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max(float x) {
+  const int y = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK, 0xf, false);
+  return __builtin_elementwise_maximum(x, __int_as_float(y));
+}
+// maximum over the 64 lanes, wave-uniform: quad swaps, half-row and row
+// mirrors, then row broadcasts 15 and 31 carry it into lane 63
+__device__ __forceinline__ float wave_max(float x) {
+  x = dpp_max<0xb1, 0xf>(x);   // quad_perm [1,0,3,2]
+  x = dpp_max<0x4e, 0xf>(x);   // quad_perm [2,3,0,1]
+  x = dpp_max<0x141, 0xf>(x);  // row_half_mirror
+  x = dpp_max<0x140, 0xf>(x);  // row_mirror
+  x = dpp_max<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x = dpp_max<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+// squared norm of eight bf16 (a 16-byte piece)
+__device__ __forceinline__ float sq8(uint4 v) {
+  float r = 0.f;
+  r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.x), __builtin_bit_cast(bf16x2, v.x), r, false);
+  r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.y), __builtin_bit_cast(bf16x2, v.y), r, false);
+  r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.z), __builtin_bit_cast(bf16x2, v.z), r, false);
+  r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v.w), __builtin_bit_cast(bf16x2, v.w), r, false);
+  return r;
 }
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 // Transposing LDS read: within each group of 16 lanes, lanes 4r..4r+3 give
@@ -97,13 +138,14 @@ struct TileArgs {
 __host__ __device__ constexpr size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 struct TileLds {
-  size_t ks, vs, halo, wts, total;
+  size_t ks, vs, knorm, halo, wts, total;
 };
 __host__ __device__ inline TileLds tile_lds(int RH, int RW) {
   TileLds l;
   size_t o = 0;
   l.ks = o; o += align16((size_t)2 * 64 * kKStr * 2);
   l.vs = o; o += align16((size_t)2 * 64 * kKStr * 2);
+  l.knorm = o; o += align16((size_t)2 * 4 * 4);
   l.halo = o; o += align16((size_t)(RH + 4) * ((RW + 5) / 2) * 32 * 4);
   l.wts = o; o += align16((size_t)2 * 15 * 32 * 4);
   l.total = o;
@@ -111,14 +153,19 @@ __host__ __device__ inline TileLds tile_lds(int RH, int RW) {
 }
 
 template <int RH, int RW>
-__global__ __launch_bounds__(256, 2) void attn_tile_kernel(TileArgs a) {
+constexpr int tile_waves() { return RH * RW >= 128 ? 8 : 4; }
+
+template <int RH, int RW>
+__global__ __launch_bounds__((64 * tile_waves<RH, RW>()), 4) void attn_tile_kernel(TileArgs a) {
   constexpr int T = RH * RW;
-  constexpr int QBW = T / 64;  // query blocks of 16 per wave
+  constexpr int WAVES = tile_waves<RH, RW>();
+  constexpr int QBW = T / (16 * WAVES);  // query blocks of 16 per wave
   constexpr int HP = RH + 4, WP = RW + 4, NPAIR = (WP + 1) / 2;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const TileLds lay = tile_lds(RH, RW);
   uint16_t* ks = reinterpret_cast<uint16_t*>(smem + lay.ks);    // [2][64][kKStr]
   uint16_t* vs = reinterpret_cast<uint16_t*>(smem + lay.vs);    // [2][64][kKStr]
+  float* knorm = reinterpret_cast<float*>(smem + lay.knorm);     // [2][4] max |k|^2 per loader wave
   uint32_t* halo = reinterpret_cast<uint32_t*>(smem + lay.halo);  // [HP][NPAIR][32]
   uint32_t* wts = reinterpret_cast<uint32_t*>(smem + lay.wts);    // [2][15][32]
 
@@ -146,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void attn_tile_kernel(TileArgs a) {
 
   // ---- tile loader: thread -> (key ld_key of the tile, 8-dim chunk ld_g)
   const int ld_key = tid >> 2, ld_g = tid & 3;
-  uint4 kreg, vreg;
+  uint4 kreg, vreg;  // the next tile, in flight during this one
   auto fetch = [&](int tile) {
     const int key = tile * 64 + ld_key;
     const int p = key / T, tt = key - p * T;   // T is compile-time
@@ -157,23 +204,31 @@ __global__ __launch_bounds__(256, 2) void attn_tile_kernel(TileArgs a) {
     kreg = ld16(kb, off);
     vreg = ld16(vb, off);
   };
+  const bool loader = tid < 256;  // waves 0-3 move the tiles
   auto park = [&](int buf) {
     *reinterpret_cast<uint4*>(ks + (buf * 64 + ld_key) * kKStr + ld_g * 8) = kreg;
     *reinterpret_cast<uint4*>(vs + (buf * 64 + ld_key) * kKStr + ld_g * 8) = vreg;
+    // |k|^2 of the key (its four 8-dim pieces sit in one quad of lanes),
+    // then the largest of this wave's 16 keys
+    float n2 = sq8(kreg);
+    n2 += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(n2), 0xb1, 0xf, 0xf, false));
+    n2 += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(n2), 0x4e, 0xf, 0xf, false));
+    const float wmax = wave_max(n2);
+    if (lane == 0) knorm[buf * 4 + wave] = wmax;
   };
 
-  fetch(0);
+  if (loader) fetch(0);
 
   // ---- halo (the head's 32 channels) and LCE weights -> LDS
   {
-    // 4 chunks of 8 channels per pixel pair; 256 threads -> 64 pair slots per pass
-    constexpr int NSLOT = HP * NPAIR;
+    // 4 chunks of 8 channels per pixel pair; 16 pair slots per wave and pass
+    constexpr int NSLOT = HP * NPAIR, SLOTS = 16 * WAVES;
     const int ch = tid & 3, slot0 = tid >> 2;
-    for (int pp0 = 0; pp0 < NSLOT; pp0 += 128) {
+    for (int pp0 = 0; pp0 < NSLOT; pp0 += 2 * SLOTS) {
       uint4 va[2], vb2[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int pp = pp0 + slot0 + 64 * i;
+        const int pp = pp0 + slot0 + SLOTS * i;
         const int pr = pp % NPAIR, py = pp / NPAIR;
         const int y = y0 - 2 + py, x = x0 - 2 + 2 * pr;
         const bool rowok = pp < NSLOT && y >= 0 && y < H;
@@ -183,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void attn_tile_kernel(TileArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int pp = pp0 + slot0 + 64 * i;
+        const int pp = pp0 + slot0 + SLOTS * i;
         if (pp < NSLOT) {
           uint4 lo, hi;
           lo.x = (va[i].x & 0xffffu) | (vb2[i].x << 16); lo.y = (va[i].x >> 16) | (vb2[i].x & 0xffff0000u);
@@ -212,10 +267,11 @@ __global__ __launch_bounds__(256, 2) void attn_tile_kernel(TileArgs a) {
     bq[i] = as_bf16x8(ld16(qb, (uint32_t)(y0 + t / RW) * rowb + (uint32_t)(x0 + t % RW) * pixb + hb + grp * 16));
   }
 
-  float m[QBW];
+  float m[QBW], qn[QBW];  // running maximum; qscale * |q| of the lane's query
   f32x4 o0[QBW], o1[QBW], ls[QBW];
 #pragma unroll
   for (int i = 0; i < QBW; ++i) {
+    qn[i] = a.qscale * __builtin_sqrtf(group_sum(sq8(__builtin_bit_cast(uint4, bq[i]))));
     m[i] = -INFINITY;
     o0[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     o1[i] = o0[i];
@@ -232,13 +288,16 @@ __global__ __launch_bounds__(256, 2) void attn_tile_kernel(TileArgs a) {
   const int vrow = 8 * grp + (col >> 2), vch = 4 * (col & 3);
 
   const int ntiles = L / 64;
-  park(0);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
+  if (loader) park(0);
+  // one 64-key tile, from LDS buffer buf = tile & 1
+  auto step = [&](int tile, int buf) {
     __syncthreads();  // tile `buf` parked; the other buffer is free
-    if (tile + 1 < ntiles) fetch(tile + 1);
+    if (loader && tile + 1 < ntiles) fetch(tile + 1);
     const uint16_t* kt = ks + buf * 64 * kKStr;
     const uint16_t* vtl = vs + buf * 64 * kKStr;
+    const float kmax = __builtin_sqrtf(__builtin_elementwise_maximum(
+        __builtin_elementwise_maximum(knorm[buf * 4 + 0], knorm[buf * 4 + 1]),
+        __builtin_elementwise_maximum(knorm[buf * 4 + 2], knorm[buf * 4 + 3])));
     bf16x8 ka[4], va0[2], va1[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -255,20 +314,23 @@ __global__ __launch_bounds__(256, 2) void attn_tile_kernel(TileArgs a) {
       f32x4 s[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) s[t] = mfma(ka[t], bq[i], z);
-      // this tile's maximum for the lane's query (16 scores here, 64 in all)
-      const float c0 = max3(s[0][0], s[0][1], s[0][2]), c1 = max3(s[0][3], s[1][0], s[1][1]);
-      const float c2 = max3(s[1][2], s[1][3], s[2][0]), c3 = max3(s[2][1], s[2][2], s[2][3]);
-      const float c4 = max3(s[3][0], s[3][1], s[3][2]);
-      const float cm = group_max(max3(max3(c0, c1, c2), max3(c3, c4, s[3][3]), c4)) * a.qscale;
-      // raise the running maximum (and rescale) only when the tile's exceeds
-      // it by more than kTau somewhere in the wave (first tile: always)
-      if (__builtin_amdgcn_ballot_w64(cm > m[i] + kTau) != 0) {
-        const float mn = __builtin_elementwise_maximum(m[i], cm);
-        const float corr = __builtin_amdgcn_exp2f(m[i] - mn);  // 0 on the first tile
-        o0[i] *= corr;
-        o1[i] *= corr;
-        ls[i] *= corr;
-        m[i] = mn;
+      // Can a score of this tile exceed m + kTau? Not if the norm bound says
+      // so for every query of the wave (the common case after the first tile).
+      if (__builtin_amdgcn_ballot_w64(qn[i] * kmax > m[i] + kTau) != 0) {
+        // this tile's exact maximum for the lane's query (16 scores here, 64 in all)
+        const float c0 = max3(s[0][0], s[0][1], s[0][2]), c1 = max3(s[0][3], s[1][0], s[1][1]);
+        const float c2 = max3(s[1][2], s[1][3], s[2][0]), c3 = max3(s[2][1], s[2][2], s[2][3]);
+        const float c4 = max3(s[3][0], s[3][1], s[3][2]);
+        const float cm = group_max(max3(max3(c0, c1, c2), max3(c3, c4, s[3][3]), c4)) * a.qscale;
+        // raise the running maximum (and rescale) only where the tile's exceeds
+        // it by more than kTau (first tile: everywhere)
+        if (cm > m[i] + kTau) {
+          const float corr = __builtin_amdgcn_exp2f(m[i] - cm);  // 0 on the first tile
+          o0[i] *= corr;
+          o1[i] *= corr;
+          ls[i] *= corr;
+          m[i] = cm;
+        }
       }
       bf16x4 pb[4];
 #pragma unroll
@@ -286,45 +348,66 @@ __global__ __launch_bounds__(256, 2) void attn_tile_kernel(TileArgs a) {
         ls[i] = mfma(ones, pt, ls[i]);
       }
     }
-    if (tile + 1 < ntiles) park(buf ^ 1);
-  }
+    if (loader && tile + 1 < ntiles) park(buf ^ 1);
+    };
+  for (int tile = 0; tile < ntiles; ++tile) step(tile, tile & 1);
   __syncthreads();  // halo and weights were parked before the first barrier; all reads below
 
-  // ---- LCE + merge + store: lane = (query col, channel group grp)
+  // ---- LCE + merge + store: lane = (query col, channel group grp); the
+  // lane's query rows i = 0..QBW-1 are stacked in one column when RW == 16
+  // (one query otherwise), so each halo row is read once for all of them
   const uint32_t* w32 = wts;
+  static_assert(QBW == 1 || RW == 16, "stacked queries need 16-token rows");
+  const int t0 = wave * QBW * 16 + col;
+  const int ty0 = t0 / RW, tx = t0 % RW;
+  const int par = tx & 1, p0 = tx >> 1;
+  float acc[QBW][8];
+  {
+    // bias of the lane's channels 4grp.. and 16+4grp.. (no bias: zeros)
+    const Rsrc bb = rsrc(a.b, a.b ? (uint32_t)C * 2 : 0u);
+    const uint32_t hoff = (uint32_t)(h * 32 + 4 * grp) * 2;
+    const uint32_t b01 = __builtin_amdgcn_raw_buffer_load_b32(bb, hoff, 0, 0);
+    const uint32_t b23 = __builtin_amdgcn_raw_buffer_load_b32(bb, hoff + 4, 0, 0);
+    const uint32_t b45 = __builtin_amdgcn_raw_buffer_load_b32(bb, hoff + 32, 0, 0);
+    const uint32_t b67 = __builtin_amdgcn_raw_buffer_load_b32(bb, hoff + 36, 0, 0);
 #pragma unroll
-  for (int i = 0; i < QBW; ++i) {
-    const int t = (wave * QBW + i) * 16 + col;
-    const int ty = t / RW, tx = t % RW;
-    const int par = tx & 1, p0 = tx >> 1;
-    float acc[8];
-    const float inv = 1.0f / ls[i][0];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[e] = a.b ? bf16_bits_to_float(a.b[h * 32 + 4 * grp + e]) : 0.f;
-      acc[4 + e] = a.b ? bf16_bits_to_float(a.b[h * 32 + 16 + 4 * grp + e]) : 0.f;
+    for (int i = 0; i < QBW; ++i) {
+      acc[i][0] = bf16_lo(b01); acc[i][1] = bf16_hi(b01);
+      acc[i][2] = bf16_lo(b23); acc[i][3] = bf16_hi(b23);
+      acc[i][4] = bf16_lo(b45); acc[i][5] = bf16_hi(b45);
+      acc[i][6] = bf16_lo(b67); acc[i][7] = bf16_hi(b67);
     }
+  }
 #pragma unroll
-    for (int ay = 0; ay < 5; ++ay) {
+  for (int yy = 0; yy < QBW + 4; ++yy) {  // halo rows ty0 + yy
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const uint32_t* hp = halo + ((ty + ay) * NPAIR + p0 + j) * 32;
+    for (int j = 0; j < 3; ++j) {
+      const uint32_t* hp = halo + ((ty0 + yy) * NPAIR + p0 + j) * 32;
+      const uint4 h0 = *reinterpret_cast<const uint4*>(hp + 4 * grp);
+      const uint4 h1 = *reinterpret_cast<const uint4*>(hp + 16 + 4 * grp);
+#pragma unroll
+      for (int i = 0; i < QBW; ++i) {
+        const int ay = yy - i;  // compile-time after unrolling
+        if (ay < 0 || ay >= 5) continue;
         const uint32_t* wp = w32 + (par * 15 + ay * 3 + j) * 32;
-        const uint4 h0 = *reinterpret_cast<const uint4*>(hp + 4 * grp);
-        const uint4 h1 = *reinterpret_cast<const uint4*>(hp + 16 + 4 * grp);
         const uint4 w0 = *reinterpret_cast<const uint4*>(wp + 4 * grp);
         const uint4 w1 = *reinterpret_cast<const uint4*>(wp + 16 + 4 * grp);
-        acc[0] = dot2(h0.x, w0.x, acc[0]); acc[1] = dot2(h0.y, w0.y, acc[1]);
-        acc[2] = dot2(h0.z, w0.z, acc[2]); acc[3] = dot2(h0.w, w0.w, acc[3]);
-        acc[4] = dot2(h1.x, w1.x, acc[4]); acc[5] = dot2(h1.y, w1.y, acc[5]);
-        acc[6] = dot2(h1.z, w1.z, acc[6]); acc[7] = dot2(h1.w, w1.w, acc[7]);
+        acc[i][0] = dot2(h0.x, w0.x, acc[i][0]); acc[i][1] = dot2(h0.y, w0.y, acc[i][1]);
+        acc[i][2] = dot2(h0.z, w0.z, acc[i][2]); acc[i][3] = dot2(h0.w, w0.w, acc[i][3]);
+        acc[i][4] = dot2(h1.x, w1.x, acc[i][4]); acc[i][5] = dot2(h1.y, w1.y, acc[i][5]);
+        acc[i][6] = dot2(h1.z, w1.z, acc[i][6]); acc[i][7] = dot2(h1.w, w1.w, acc[i][7]);
       }
     }
+  }
+#pragma unroll
+  for (int i = 0; i < QBW; ++i) {
+    const int ty = ty0 + i;
+    const float inv = 1.0f / ls[i][0];
     uint2 lo, hi;
-    lo.x = float_to_bf16_bits(fmaf(o0[i][0], inv, acc[0])) | (float_to_bf16_bits(fmaf(o0[i][1], inv, acc[1])) << 16);
-    lo.y = float_to_bf16_bits(fmaf(o0[i][2], inv, acc[2])) | (float_to_bf16_bits(fmaf(o0[i][3], inv, acc[3])) << 16);
-    hi.x = float_to_bf16_bits(fmaf(o1[i][0], inv, acc[4])) | (float_to_bf16_bits(fmaf(o1[i][1], inv, acc[5])) << 16);
-    hi.y = float_to_bf16_bits(fmaf(o1[i][2], inv, acc[6])) | (float_to_bf16_bits(fmaf(o1[i][3], inv, acc[7])) << 16);
+    lo.x = float_to_bf16_bits(fmaf(o0[i][0], inv, acc[i][0])) | (float_to_bf16_bits(fmaf(o0[i][1], inv, acc[i][1])) << 16);
+    lo.y = float_to_bf16_bits(fmaf(o0[i][2], inv, acc[i][2])) | (float_to_bf16_bits(fmaf(o0[i][3], inv, acc[i][3])) << 16);
+    hi.x = float_to_bf16_bits(fmaf(o1[i][0], inv, acc[i][4])) | (float_to_bf16_bits(fmaf(o1[i][1], inv, acc[i][5])) << 16);
+    hi.y = float_to_bf16_bits(fmaf(o1[i][2], inv, acc[i][6])) | (float_to_bf16_bits(fmaf(o1[i][3], inv, acc[i][7])) << 16);
     uint16_t* po = a.out + img + ((size_t)(y0 + ty) * W + x0 + tx) * C + h * 32;
     *reinterpret_cast<uint2*>(po + 4 * grp) = lo;
     *reinterpret_cast<uint2*>(po + 16 + 4 * grp) = hi;
@@ -335,8 +418,9 @@ template <int RH, int RW>
 hipError_t launch_t(const TileArgs& a, hipStream_t st) {
   const int units = a.N * a.S * a.S * a.heads;
   const unsigned blocks = (unsigned)(((units + 7) / 8) * 8);
-  hipLaunchKernelGGL((attn_tile_kernel<RH, RW>), dim3(blocks), dim3(256), tile_lds(RH, RW).total,
-                     st, a);
+  constexpr int threads = 64 * tile_waves<RH, RW>();
+  hipLaunchKernelGGL((attn_tile_kernel<RH, RW>), dim3(blocks), dim3(threads),
+                     tile_lds(RH, RW).total, st, a);
   return hipGetLastError();
 }
 
