@@ -141,6 +141,35 @@ def test_attend_with_oracle_routes(gpu_lib, case):
     check_output(host(out), ref["out"], dtype)
 
 
+@pytest.mark.parametrize("H,rside", [(32, 8), (64, 16)], ids=["8x8_regions", "16x16_regions"])
+def test_attend_late_large_scores(gpu_lib, H, rside):
+    """The last routed region holds keys whose scaled scores exceed all
+    earlier ones by about 163 (base-2 exponent units): past fp32's range, so
+    the large-region kernel must raise its running maximum after the first
+    key tile (the rescale path that ordinary inputs never take) to match the
+    oracle rather than overflow."""
+    import torch
+    N, C, heads, S, topk = 1, 64, 2, 4, 4
+    R = S * S
+    inp = draw(N, H, H, C, S, "bf16", seed=4242)
+    q = np.full_like(inp["q"], 1.0)      # every score = sum of the key's channels
+    k = inp["k"].copy()
+    X = 5                                # region routed last, half its keys at +20
+    jx, ix = divmod(X, S)
+    k[:, jx * rside:(jx + 1) * rside, ix * rside:ix * rside + rside // 2, :] = 20.0
+    others = [s_ for s_ in range(R) if s_ != X]
+    route = np.array([[others[(r + 1) % (R - 1)], others[(r + 2) % (R - 1)],
+                       others[(r + 7) % (R - 1)], X] for r in range(R)], dtype=np.int32)[None]
+    assert all(len(set(row)) == topk for row in route[0])
+    ref = oracle.bra_forward(q, k, inp["v"], inp["lce_w"], inp["lce_b"], heads, S, topk,
+                             route_override=route)
+    say("late large scores", H)
+    out = gpu_lib.attend(dev(q, "bf16"), dev(k, "bf16"), dev(inp["v"], "bf16"),
+                         dev(inp["lce_w"], "bf16"), dev(inp["lce_b"], "bf16"),
+                         torch.from_numpy(route).cuda(), heads, S)
+    check_output(host(out), ref["out"], "bf16")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_lce_alone(gpu_lib, dtype):
     inp = draw(2, 20, 12, 96, 4, dtype, seed=55)
