@@ -9,10 +9,11 @@ One JSON line is printed. It carries:
   value      whole-job queries/s (a query is one token position, N*H*W per step)
   roofline   the attention kernel's (the dominant kernel's) algorithmic bytes
              (or flops) per launch over its mean launch time, measured with HIP
-             events that the library records around that kernel on the launch
-             stream, on every PROFILE_EVERY-th step of the timed region; the
-             other kernels are timed the same way in a separate pass after it
-             (the "kernels" object)
+             events on the launch stream on every PROFILE_EVERY-th step of the
+             timed region (the library launches a timed kernel with
+             hipExtLaunchKernelGGL, which ties the event pair to that dispatch);
+             the other kernels are timed the same way in a separate pass after
+             it (the "kernels" object)
   cpu_baseline  the fp64 CPU oracle timed on whole-batch passes of the same
              workload (about 10 s of CPU work)
 Other workloads: --config c0..c4 (c1 is the default).
@@ -128,8 +129,10 @@ def cpu_baseline(inp, cfg, budget_s: float):
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # the GPU's clocks settle over tens of milliseconds of load: the defaults
+    # warm up for ~50 ms and time ~100 ms
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--config", default="c1")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")

@@ -131,13 +131,15 @@ const char* bra_error_string(int code);
 /* Library version: 100 * major + minor. */
 int bra_version(void);
 
-/* Per-kernel timing with HIP events recorded on the launch stream.
+/* Per-kernel timing with HIP events tied to the kernel dispatches.
  * bra_profile_begin(mask) records events around the kernels of every kind k
  * with bit (1 << k) set in mask (BRA_K_* below; up to 4096 launches per kind,
  * later ones are not recorded) and clears earlier records; mask 0 stops
  * recording. bra_profile_read waits for the recorded events, then writes for
  * each kind k < n the summed milliseconds and the launch count, and clears
- * the record. Each recorded kernel costs two event records on the stream.
+ * the record. A recorded kernel is launched with hipExtLaunchKernelGGL, whose
+ * start and stop events take the time stamps of that kernel's own dispatch
+ * (no extra stream commands between kernels).
  * bra_profile_set_mask(mask) changes which kinds are recorded from the next
  * launch on without clearing the record (to sample some launches of a run). */
 enum bra_kernel_kind {

@@ -30,6 +30,11 @@ hipError_t launch_attend_tile(const void* q, const void* k, const void* v, const
                               hipStream_t st);
 size_t lce_pack_bytes(int C);
 hipError_t launch_lce_pack(const void* w, int C, uint32_t* wpk, hipStream_t st);
+
+ProfEvents& prof_events() {
+  thread_local ProfEvents pe;
+  return pe;
+}
 }  // namespace bra
 
 namespace {
@@ -55,6 +60,9 @@ std::mutex g_prof_mutex;
 int g_prof_mask = 0;  // bit k: record events around kernels of kind k
 KindRecord g_prof[BRA_K_COUNT];
 
+// Arms the event pair of one record slot for the next kernel this thread
+// launches (bra::launch stamps them with that dispatch's start and end). If
+// no kernel took them, both are recorded on the stream when the scope ends.
 struct ProfScope {
   int kind;
   hipStream_t st;
@@ -66,16 +74,28 @@ struct ProfScope {
     if (rec.used >= kMaxEvents) return;
     if ((int)rec.start.size() <= rec.used) {
       hipEvent_t a, b;
-      if (hipEventCreate(&a) != hipSuccess) return;
-      if (hipEventCreate(&b) != hipSuccess) { hipEventDestroy(a); return; }
+      // device-scope release: no L2 write-back to memory is timed with the kernel
+      if (hipEventCreateWithFlags(&a, hipEventReleaseToDevice) != hipSuccess) return;
+      if (hipEventCreateWithFlags(&b, hipEventReleaseToDevice) != hipSuccess) {
+        hipEventDestroy(a);
+        return;
+      }
       rec.start.push_back(a);
       rec.stop.push_back(b);
     }
     slot = rec.used++;
-    hipEventRecord(rec.start[slot], st);
+    bra::ProfEvents& pe = bra::prof_events();
+    pe.start = rec.start[slot];
+    pe.stop = rec.stop[slot];
   }
   ~ProfScope() {
-    if (slot >= 0) hipEventRecord(g_prof[kind].stop[slot], st);
+    if (slot < 0) return;
+    bra::ProfEvents& pe = bra::prof_events();
+    if (pe.start) {
+      hipEventRecord(pe.start, st);
+      hipEventRecord(pe.stop, st);
+      pe.start = pe.stop = nullptr;
+    }
   }
 };
 

@@ -235,12 +235,12 @@ hipError_t launch_attend_mfma(const void* q, const void* k, const void* v,
   const float qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
   if (s.T <= 16) {
     const unsigned blocks = (unsigned)((units + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL(attn_mfma_kernel<true>, dim3(blocks), dim3(256), 0, st,
+    launch(attn_mfma_kernel<true>, dim3(blocks), dim3(256), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                        (const uint16_t*)w, (const uint16_t*)b, route, g, s.heads, units,
                        qscale, (uint16_t*)out);
   } else {
-    hipLaunchKernelGGL(attn_mfma_kernel<false>, dim3((unsigned)units), dim3(256), 0, st,
+    launch(attn_mfma_kernel<false>, dim3((unsigned)units), dim3(256), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                        (const uint16_t*)w, (const uint16_t*)b, route, g, s.heads, units,
                        qscale, (uint16_t*)out);

@@ -397,7 +397,7 @@ template <int RH, int RW, int HEADS>
 hipError_t launch_shape(const RegionArgs& a, int R, size_t lds, hipStream_t st) {
   const int units = a.N * R;
   const unsigned blocks = (unsigned)(((units + 7) / 8) * 8);
-  hipLaunchKernelGGL((attn_region_kernel<RH, RW, HEADS>), dim3(blocks), dim3(64 * HEADS), lds, st, a);
+  launch((attn_region_kernel<RH, RW, HEADS>), dim3(blocks), dim3(64 * HEADS), lds, st, a);
   return hipGetLastError();
 }
 
@@ -424,7 +424,7 @@ hipError_t dispatch_shape(const RegionArgs& a, const Shape& s, size_t lds, hipSt
 size_t lce_pack_bytes(int C) { return ((size_t)30 * C + (size_t)25 * (C / 2)) * 4; }
 
 hipError_t launch_lce_pack(const void* w, int C, uint32_t* wpk, hipStream_t st) {
-  hipLaunchKernelGGL(lce_pack_kernel, dim3((unsigned)((lce_pack_items(C) + 255) / 256)), dim3(256), 0, st,
+  launch(lce_pack_kernel, dim3((unsigned)((lce_pack_items(C) + 255) / 256)), dim3(256), 0, st,
                      (const uint16_t*)w, C, wpk);
   return hipGetLastError();
 }

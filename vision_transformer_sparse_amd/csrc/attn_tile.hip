@@ -419,7 +419,7 @@ hipError_t launch_t(const TileArgs& a, hipStream_t st) {
   const int units = a.N * a.S * a.S * a.heads;
   const unsigned blocks = (unsigned)(((units + 7) / 8) * 8);
   constexpr int threads = 64 * tile_waves<RH, RW>();
-  hipLaunchKernelGGL((attn_tile_kernel<RH, RW>), dim3(blocks), dim3(threads),
+  launch((attn_tile_kernel<RH, RW>), dim3(blocks), dim3(threads),
                      tile_lds(RH, RW).total, st, a);
   return hipGetLastError();
 }

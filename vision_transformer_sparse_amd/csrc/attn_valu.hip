@@ -186,12 +186,12 @@ hipError_t launch_attend_valu(const void* q, const void* k, const void* v,
   const size_t blocks = (size_t)s.N * s.R * s.heads * qslices;
   const float qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
   if (dtype == 1)
-    hipLaunchKernelGGL(attn_valu_kernel<uint16_t>, dim3((unsigned)blocks), dim3(threads), 0, st,
+    launch(attn_valu_kernel<uint16_t>, dim3((unsigned)blocks), dim3(threads), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                        (const uint16_t*)w, (const uint16_t*)b, route, s.H, s.W, s.C,
                        s.heads, s.S, s.topk, qslices, qscale, (uint16_t*)out);
   else
-    hipLaunchKernelGGL(attn_valu_kernel<float>, dim3((unsigned)blocks), dim3(threads), 0, st,
+    launch(attn_valu_kernel<float>, dim3((unsigned)blocks), dim3(threads), 0, st,
                        (const float*)q, (const float*)k, (const float*)v,
                        (const float*)w, (const float*)b, route, s.H, s.W, s.C,
                        s.heads, s.S, s.topk, qslices, qscale, (float*)out);
@@ -203,11 +203,11 @@ hipError_t launch_lce(const void* v, const void* w, const void* b, const Shape& 
   const size_t groups = (size_t)s.N * s.H * s.W * (s.C / kHD);
   const unsigned blocks = (unsigned)((groups + 255) / 256);
   if (dtype == 1)
-    hipLaunchKernelGGL(lce_kernel<uint16_t>, dim3(blocks), dim3(256), 0, st,
+    launch(lce_kernel<uint16_t>, dim3(blocks), dim3(256), 0, st,
                        (const uint16_t*)v, (const uint16_t*)w, (const uint16_t*)b,
                        s.N, s.H, s.W, s.C, out);
   else
-    hipLaunchKernelGGL(lce_kernel<float>, dim3(blocks), dim3(256), 0, st,
+    launch(lce_kernel<float>, dim3(blocks), dim3(256), 0, st,
                        (const float*)v, (const float*)w, (const float*)b,
                        s.N, s.H, s.W, s.C, out);
   return hipGetLastError();

@@ -2,11 +2,35 @@
 // Not part of the public ABI (include/bra.h is).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace bra {
+
+// Timing of the next kernel launched on this host thread: when the library
+// profiles a kernel kind it leaves a pair of events here; launch() hands them
+// to hipExtLaunchKernelGGL, which stamps them with that dispatch's own start
+// and end, and clears them.
+struct ProfEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+ProfEvents& prof_events();  // per host thread
+
+// Every kernel of the library is launched through here. Errors are left for
+// the caller's hipGetLastError().
+template <typename... Args, typename F = void (*)(Args...)>
+void launch(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t st, Args... args) {
+  ProfEvents& pe = prof_events();
+  if (pe.start) {
+    const hipEvent_t a = pe.start, b = pe.stop;
+    pe.start = pe.stop = nullptr;
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, a, b, 0u, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+  }
+}
 
 // Problem sizes, derived once on the host after validation.
 struct Shape {

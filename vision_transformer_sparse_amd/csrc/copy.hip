@@ -20,7 +20,7 @@ hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t st)
   if (n == 0) return hipSuccess;
   size_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+  launch(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
                      (const uint4*)src, (uint4*)dst, n);
   return hipGetLastError();
 }

@@ -117,7 +117,7 @@ hipError_t launch_t(const void* q, const void* k, const Shape& s, float* qr, flo
   const size_t lds = (size_t)2 * lanes * s.C * sizeof(float);
   dim3 grid((unsigned)(s.N * s.R)), block(threads);
 #define BRA_POOL(TP)                                                                    \
-  hipLaunchKernelGGL((region_pool_kernel<T, TP>), grid, block, lds, st, (const T*)q,    \
+  launch((region_pool_kernel<T, TP>), grid, block, lds, st, (const T*)q,    \
                      (const T*)k, s.H, s.W, s.C, s.S, qr, kr, (const uint16_t*)lw, wpk)
   if (tpt <= 1) BRA_POOL(1);
   else if (tpt <= 2) BRA_POOL(2);

@@ -186,7 +186,7 @@ hipError_t launch_small(const float* qr, const float* kr, int N, int R, int C, i
                         int32_t* route, hipStream_t st) {
   const float scale = (float)(1.0 / __builtin_sqrt((double)C));
   const unsigned blocks = (unsigned)(N * col_tiles(R));
-  hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(64 * col_tiles(R)), route_lds(R), st, qr, kr,
+  launch(route_kernel, dim3(blocks), dim3(64 * col_tiles(R)), route_lds(R), st, qr, kr,
                      R, C, topk, scale, route);
   return hipGetLastError();
 }
@@ -278,7 +278,7 @@ hipError_t launch_wide(const float* qr, const float* kr, int N, int R, int C, in
   const float scale = (float)(1.0 / __builtin_sqrt((double)C));
   const unsigned blocks = (unsigned)(N * ((R + kWideRows - 1) / kWideRows));
   const size_t lds = ((size_t)kWideRows * C + (size_t)kWideRows * 64 * MPL) * sizeof(float);
-  hipLaunchKernelGGL((route_wide_kernel<MPL>), dim3(blocks), dim3(64 * MPL), lds, st, qr, kr, R,
+  launch((route_wide_kernel<MPL>), dim3(blocks), dim3(64 * MPL), lds, st, qr, kr, R,
                      C, topk, scale, route);
   return hipGetLastError();
 }
