@@ -75,6 +75,13 @@ SMALL_CASES = [
     ("r400_router", 1, 40, 40, 64, 2, 20, 7, "bf16", 0.7),
     ("r100_router", 2, 20, 20, 64, 2, 10, 6, "bf16", 0.0),
     ("r36_three_col_tiles", 2, 24, 24, 96, 3, 6, 5, "bf16", 0.0),
+    # small-region kernel: T = 16 / G key tiles side by side in the score columns
+    ("t8_2x4_regions_l24", 1, 8, 16, 128, 4, 4, 3, "bf16", 0.0),
+    ("t8_4x2_regions_h8_l40", 2, 16, 8, 256, 8, 4, 5, "bf16", 0.7),
+    ("t8_l128_two_chunks", 1, 16, 32, 64, 2, 8, 16, "bf16", 0.7),
+    ("t4_l96_two_chunks", 1, 16, 16, 128, 4, 8, 24, "bf16", 0.7),
+    ("t2_1x2_regions_l14", 1, 6, 12, 64, 2, 6, 7, "bf16", 0.0),
+    ("t1_1x1_regions_l40", 1, 8, 8, 64, 2, 8, 40, "bf16", 0.7),
     ("f32_c0_like", 1, 56, 56, 64, 2, 7, 1, "f32", 0.0),
     ("f32_ragged", 2, 15, 10, 64, 2, 5, 3, "f32", 0.0),
     ("f32_t256", 1, 64, 64, 64, 2, 4, 2, "f32", 0.7),

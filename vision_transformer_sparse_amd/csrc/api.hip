@@ -24,6 +24,10 @@ bool region_kernel_supports(const Shape& s);
 hipError_t launch_attend_region(const void* q, const void* k, const void* v, const uint32_t* wpk,
                                 const void* b, const int32_t* route, const Shape& s, void* out,
                                 hipStream_t st);
+bool image_kernel_supports(const Shape& s);
+hipError_t launch_attend_image(const void* q, const void* k, const void* v, const uint32_t* wpk,
+                               const void* b, const int32_t* route, const Shape& s, void* out,
+                               hipStream_t st);
 bool tile_kernel_supports(const Shape& s);
 hipError_t launch_attend_tile(const void* q, const void* k, const void* v, const uint32_t* wpk,
                               const void* b, const int32_t* route, const Shape& s, void* out,
@@ -208,7 +212,9 @@ int attend(const void* q, const void* k, const void* v, const void* w, const voi
   hipError_t e;
   {
     ProfScope ps(BRA_K_ATTN, st);
-    if (dtype == BRA_BF16 && wpk && bra::region_kernel_supports(s))
+    if (dtype == BRA_BF16 && wpk && bra::image_kernel_supports(s))
+      e = bra::launch_attend_image(q, k, v, wpk, b, route, s, out, st);
+    else if (dtype == BRA_BF16 && wpk && bra::region_kernel_supports(s))
       e = bra::launch_attend_region(q, k, v, wpk, b, route, s, out, st);
     else if (dtype == BRA_BF16 && wpk && bra::tile_kernel_supports(s))
       e = bra::launch_attend_tile(q, k, v, wpk, b, route, s, out, st);
@@ -308,7 +314,8 @@ int bra_attend(const void* q, const void* k, const void* v, const void* lce_w,
   rc = check_ptrs({q, k, v, lce_w, lce_b, route_idx, out});
   if (rc) return rc;
   hipStream_t st = g_stream;
-  if (dtype == BRA_BF16 && (bra::region_kernel_supports(s) || bra::tile_kernel_supports(s))) {
+  if (dtype == BRA_BF16 && (bra::image_kernel_supports(s) || bra::region_kernel_supports(s) ||
+                            bra::tile_kernel_supports(s))) {
     std::lock_guard<std::mutex> lk(g_ws_mutex);
     void* ws = nullptr;
     rc = workspace(bra::lce_pack_bytes(C), &ws);

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
   uint4 wv[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) wv[i] = ld16(wb, (uint32_t)(tid + i * nthreads) * 16);
-  const uint32_t qt = col < T ? col : T - 1;
+  const uint32_t qt = col % T;  // the query of this lane's score column
   const bf16x8 bq = ld16_bf16(qb, (y0 + qt / RW) * rowb + (x0 + qt % RW) * pixb + chb);
   // LCE bias of this thread's channel pair (no bias: zeros)
   const uint32_t bias2 = __builtin_amdgcn_raw_buffer_load_b32(
@@ -221,11 +221,14 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
   const int cp = tid % (C / 2), xcol = has_item ? tid / (C / 2) : 0;
   const int c = 2 * cp;
   auto lce_item = [&](float* acc0, float* acc1) {
-    // pixel-pair weights from the tap weights: an even column pairs taps
-    // (0,1) (2,3) (4,-); an odd one starts a pixel earlier: (-,0) (1,2) (3,4).
-    // x: channel c (low halves), y: channel c+1 (high halves).
+#pragma unroll
+    for (int i = 0; i < RH; ++i) { acc0[i] = bf16_lo(bias2); acc1[i] = bf16_hi(bias2); }
+    // One weight row at a time (few live registers while the gathered K/V
+    // are in flight). Pixel-pair weights from the tap weights: an even
+    // column pairs taps (0,1) (2,3) (4,-); an odd one starts a pixel earlier:
+    // (-,0) (1,2) (3,4). x: channel c (low halves), y: channel c+1.
     const bool even = (xcol & 1) == 0;
-    uint2 wv[5][3];
+    const uint32_t* hc = halo + (xcol >> 1) * C + c;
 #pragma unroll
     for (int ay = 0; ay < 5; ++ay) {
       uint32_t d[5];
@@ -233,32 +236,24 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
       for (int ax = 0; ax < 5; ++ax) d[ax] = wts[(5 * ay + ax) * (C / 2) + cp];
       const uint32_t e6[6] = {even ? d[0] : 0u, even ? d[1] : d[0], even ? d[2] : d[1],
                               even ? d[3] : d[2], even ? d[4] : d[3], even ? 0u : d[4]};
+      uint2 wv[3];
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
-        wv[ay][j].x = __builtin_amdgcn_perm(e6[2 * j + 1], e6[2 * j], 0x05040100u);
-        wv[ay][j].y = __builtin_amdgcn_perm(e6[2 * j + 1], e6[2 * j], 0x07060302u);
+        wv[j].x = __builtin_amdgcn_perm(e6[2 * j + 1], e6[2 * j], 0x05040100u);
+        wv[j].y = __builtin_amdgcn_perm(e6[2 * j + 1], e6[2 * j], 0x07060302u);
       }
-    }
 #pragma unroll
-    for (int i = 0; i < RH; ++i) { acc0[i] = bf16_lo(bias2); acc1[i] = bf16_hi(bias2); }
-    const uint32_t* hc = halo + (xcol >> 1) * C + c;
-#pragma unroll
-    for (int yy = 0; yy < HP; ++yy) {
-      const uint32_t* hr = hc + yy * NPAIR * C;
-      const uint2 h0 = *reinterpret_cast<const uint2*>(hr);
-      const uint2 h1 = *reinterpret_cast<const uint2*>(hr + C);
-      const uint2 h2 = *reinterpret_cast<const uint2*>(hr + 2 * C);
-#pragma unroll
-      for (int ay = 0; ay < 5; ++ay) {
-        const int yo = yy - ay;
-        if (yo >= 0 && yo < RH) {
-          acc0[yo] = dot2(h0.x, wv[ay][0].x, acc0[yo]);
-          acc0[yo] = dot2(h1.x, wv[ay][1].x, acc0[yo]);
-          acc0[yo] = dot2(h2.x, wv[ay][2].x, acc0[yo]);
-          acc1[yo] = dot2(h0.y, wv[ay][0].y, acc1[yo]);
-          acc1[yo] = dot2(h1.y, wv[ay][1].y, acc1[yo]);
-          acc1[yo] = dot2(h2.y, wv[ay][2].y, acc1[yo]);
-        }
+      for (int yo = 0; yo < RH; ++yo) {
+        const uint32_t* hr = hc + (yo + ay) * NPAIR * C;
+        const uint2 h0 = *reinterpret_cast<const uint2*>(hr);
+        const uint2 h1 = *reinterpret_cast<const uint2*>(hr + C);
+        const uint2 h2 = *reinterpret_cast<const uint2*>(hr + 2 * C);
+        acc0[yo] = dot2(h0.x, wv[0].x, acc0[yo]);
+        acc0[yo] = dot2(h1.x, wv[1].x, acc0[yo]);
+        acc0[yo] = dot2(h2.x, wv[2].x, acc0[yo]);
+        acc1[yo] = dot2(h0.y, wv[0].y, acc1[yo]);
+        acc1[yo] = dot2(h1.y, wv[1].y, acc1[yo]);
+        acc1[yo] = dot2(h2.y, wv[2].y, acc1[yo]);
       }
     }
   };
@@ -282,7 +277,18 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
   }
 
   // ---- B: attention, head = wave -----------------------------------------
+  // A 16-column score tile holds only T queries, so for T < 16 it carries
+  // G = min(16 / T, 4) key tiles side by side: column j is query j % T
+  // against key tile j / T of its group (the K tiles multiply copies of Q^T
+  // masked to their own columns, summed into one accumulator), and every
+  // score computed is a real one. P keeps that layout through P.V -- each
+  // column sums the keys of its own tile -- and the G column partials of a
+  // query are added after the last chunk.
   {
+    constexpr int NR = 16 / T;
+    constexpr int G = NR < 4 ? NR : 4;  // key tiles per score tile
+    constexpr int NO = 4 / G;           // score tiles per 64-key chunk
+    const int tq = col / T;             // this column's tile in its group (>= G: no tile)
     bf16x8 sel0, sel1, ones;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -290,6 +296,7 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
       sel1[e] = (__bf16)((grp == 2 + (col >> 3) && e == (col & 7)) ? 1.0f : 0.0f);
       ones[e] = (__bf16)1.0f;
     }
+    const bf16x8 zero8 = {};
     float m = -INFINITY;  // running max of the scaled (base-2) logits
     f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0, ls = o0;
     for (int base = 0; base < L; base += 64) {
@@ -300,29 +307,32 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
         read_routes(base);
         fetch(base);
       }
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      f32x4 s[4];
+      f32x4 s[NO];
       bf16x4 vt[4][2];
 #pragma unroll
+      for (int o = 0; o < NO; ++o) {
+        s[o] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < G; ++g) s[o] = mfma(ak[o * G + g], G == 1 || tq == g ? bq : zero8, s[o]);
+      }
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
       for (int t = 0; t < 4; ++t) {
-        s[t] = mfma(ak[t], bq, z);
         vt[t][0] = to_bf16x4(mfma(av[t], sel0, z));
         vt[t][1] = to_bf16x4(mfma(av[t], sel1, z));
       }
-      if (base + 64 > L) {                  // ragged last chunk: mask keys past L
+      // mask keys past L (ragged last chunk) and columns of no tile (T < 4)
+      if (T < 4 || base + 64 > L) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int o = 0; o < NO; ++o)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (base + 16 * t + 4 * grp + e >= L) s[t][e] = -INFINITY;
+            if (tq >= G || base + 16 * (o * G + tq) + 4 * grp + e >= L) s[o][e] = -INFINITY;
       }
       float cm = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) cm = fmaxf(cm, s[t][e]);
-      cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-      cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+      for (int o = 0; o < NO; ++o) cm = max3(cm, max3(s[o][0], s[o][1], s[o][2]), s[o][3]);
+      cm = row_class_max<T>(group_max(cm));     // over the key rows, then the tiles of a query
       const float mn = fmaxf(m, cm * a.qscale);  // qscale > 0 commutes with max
       if (base > 0) {                            // rescale what earlier chunks summed
         const float corr = __builtin_amdgcn_exp2f(m - mn);
@@ -331,21 +341,38 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
         ls *= corr;
       }
       m = mn;
-      bf16x4 pb[4];
+      bf16x4 pb[NO];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int o = 0; o < NO; ++o) {
         f32x4 pv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(s[t][e], a.qscale, -mn));
-        pb[t] = to_bf16x4(pv);
+        for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(s[o][e], a.qscale, -mn));
+        pb[o] = to_bf16x4(pv);
       }
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb) {
-        const bf16x8 pt = cat(pb[2 * bb], pb[2 * bb + 1]);
-        o0 = mfma(cat(vt[2 * bb][0], vt[2 * bb + 1][0]), pt, o0);
-        o1 = mfma(cat(vt[2 * bb][1], vt[2 * bb + 1][1]), pt, o1);
+        // k slots: keys of tiles 2bb and 2bb+1; a column takes P only for its own tile
+        const int t0 = 2 * bb;
+        bf16x8 pt;
+        if constexpr (G == 1) {
+          pt = cat(pb[t0], pb[t0 + 1]);
+        } else {
+          const bf16x4 zero4 = {};
+          const bf16x4 p = pb[t0 / G];
+          pt = cat(tq == t0 % G ? p : zero4, tq == (t0 + 1) % G ? p : zero4);
+        }
+        o0 = mfma(cat(vt[t0][0], vt[t0 + 1][0]), pt, o0);
+        o1 = mfma(cat(vt[t0][1], vt[t0 + 1][1]), pt, o1);
         ls = mfma(ones, pt, ls);  // every row of ones x P^T is the row sum of P
       }
+    }
+    if constexpr (G > 1) {  // add the tile partials of each query
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o0[e] = row_class_sum<T>(o0[e]);
+        o1[e] = row_class_sum<T>(o1[e]);
+      }
+      ls[0] = row_class_sum<T>(ls[0]);
     }
     const float inv = 1.0f / ls[0];
     if (col < T) {

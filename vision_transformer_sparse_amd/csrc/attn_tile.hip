@@ -62,33 +62,6 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
-}
-// maximum over the lanes l, l^16, l^32, l^48 (the four key groups of a query)
-__device__ __forceinline__ float group_max(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // {x[l & ~16], x[l | 16]}
-  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const uint32_t w = __float_as_uint(x);
-  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);  // {x[l & 31], x[l | 32]}
-  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-// sum over the lanes l, l^16, l^32, l^48
-__device__ __forceinline__ float group_sum(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const uint32_t w = __float_as_uint(x);
-  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-// max of x and its DPP-moved copy (lanes the pattern leaves out keep x)
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_max(float x) {
-  const int y = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK, 0xf, false);
-  return __builtin_elementwise_maximum(x, __int_as_float(y));
-}
 // maximum over the 64 lanes, wave-uniform: quad swaps, half-row and row
 // mirrors, then row broadcasts 15 and 31 carry it into lane 63
 __device__ __forceinline__ float wave_max(float x) {

@@ -95,6 +95,52 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+// maximum over the lanes l, l^16, l^32, l^48 (the four key groups of a query)
+__device__ __forceinline__ float group_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // {x[l & ~16], x[l | 16]}
+  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);  // {x[l & 31], x[l | 32]}
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+// sum over the lanes l, l^16, l^32, l^48
+__device__ __forceinline__ float group_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t w = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// max of x and its DPP-moved copy (lanes the pattern leaves out keep x)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max(float x) {
+  const int y = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK, 0xf, false);
+  return __builtin_elementwise_maximum(x, __int_as_float(y));
+}
+// maximum / sum over the lanes of a 16-lane row that share l % P (P a power
+// of two dividing 16): DPP row rotations by P, 2P, .. 8
+template <int P>
+__device__ __forceinline__ float row_class_max(float x) {
+  if constexpr (P < 16) {
+    x = dpp_max<0x120 + P, 0xf>(x);  // row_ror:P
+    return row_class_max<2 * P>(x);
+  }
+  return x;
+}
+template <int P>
+__device__ __forceinline__ float row_class_sum(float x) {
+  if constexpr (P < 16) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x120 + P, 0xf, 0xf, false));
+    return row_class_sum<2 * P>(x);
+  }
+  return x;
+}
+
 // The LCE weights repacked for packed-bf16 dot products, two layouts in one
 // buffer of lce_pack_items(C) entries:
 //  * [parity][row][pair][C] dwords (30*C): pixel-pair weights. For an even
