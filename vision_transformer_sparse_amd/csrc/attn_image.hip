@@ -16,13 +16,14 @@
 //   LCE         the 5x5 window of the query pixel, read from the bordered V
 //               without bounds checks
 //
-// Scores use the column-stacked layout of the small-region kernel: a 16x16
-// score tile holds 4 key tiles x 4 queries (column j = query j % 4 against
-// key tile j / 4), so every score computed is a real one; each P.V column
-// sums its own tile's keys and the four column partials of a query are added
-// after the last chunk. A lane then owns one (query, channel pair): the four
-// copies of a query's 32 dims are split into 16 channel pairs, and the lane
-// adds the LCE of its pair and stores it.
+// Scores are column-stacked: a 16x16 score tile holds 4 key tiles x 4
+// queries (column j = key tile j % 4 for query j / 4; each lane keeps its
+// column's tile from the four K x Q^T products), so every exponential is a
+// real one and a query's four columns form a lane quad. For P.V each tile's
+// P is broadcast over the quad (quad_perm DPP), so every column sums all the
+// keys of its query and the quad holds four copies of the result. A lane
+// then owns one (query, channel pair) -- the copies split the query's 32
+// dims into 16 channel pairs -- and adds the LCE of its pair and stores it.
 #include "bra_internal.h"
 
 namespace bra {
@@ -58,6 +59,30 @@ __device__ __forceinline__ bf16x4 ld_tr(const uint16_t* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// the 4 bf16 of quad lane FROM (0..3), in every lane of the quad
+template <int FROM>
+__device__ __forceinline__ bf16x4 quad_bcast(bf16x4 x) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_bit_cast(u32x2, x);
+  constexpr int ctrl = FROM * 0x55;  // quad_perm [FROM, FROM, FROM, FROM]
+  u32x2 r;
+  r[0] = __builtin_amdgcn_update_dpp(v[0], v[0], ctrl, 0xf, 0xf, false);
+  r[1] = __builtin_amdgcn_update_dpp(v[1], v[1], ctrl, 0xf, 0xf, false);
+  return __builtin_bit_cast(bf16x4, r);
+}
+// one of four values by the two bits of i
+__device__ __forceinline__ float pick4(bool b0, bool b1, float v0, float v1, float v2, float v3) {
+  return b1 ? (b0 ? v3 : v2) : (b0 ? v1 : v0);
+}
+
+// LDS bank swizzles (16-byte piece index XOR). K token (y, x): piece ^ (y & 1
+// | ((x >> 1) & 1) << 1) -- the eight K rows an 8-lane group reads (two
+// routed 2x2 regions) spread over the banks. Bordered V row py: piece ^ 3 on
+// odd rows -- a region's two token rows, and the LCE windows of vertically
+// adjacent queries, fall on different banks.
+__device__ __forceinline__ int kswz(int y, int x) { return (y & 1) | (((x >> 1) & 1) << 1); }
+__device__ __forceinline__ int vswz(int py) { return 3 * (py & 1); }
+
 struct ImageArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -72,17 +97,25 @@ struct ImageArgs {
 
 __host__ __device__ constexpr size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
+// route slots per region in LDS: topk rounded up to a whole 64-key chunk
+__host__ __device__ constexpr int route_stride(int topk) { return (topk + 15) & ~15; }
+
 struct ImgLds {
-  size_t k, v, rb, sink, total;
+  size_t k, v, rk, rv, w, sink, total;
 };
-// K [H*W][32] and bordered V [(H+4)*(W+4)][32] bf16 of one head, the route
-// table as packed token bases [S*S*topk], a sink for out-of-range stores.
+// K [H*W][32] and bordered V [(H+4)*(W+4)][32] bf16 of one head; the routes
+// as LDS byte addresses of each routed region's first K and V token
+// [S*S][route_stride] (16-bit: the layout stays under 64 KB); the head's LCE
+// weights as dot2 operands [16 pairs][5 rows][8 dwords]; a sink for unused
+// stores.
 __host__ __device__ inline ImgLds img_lds(int H, int W, int R, int topk) {
   ImgLds l;
   size_t o = 0;
   l.k = o; o += (size_t)H * W * 64;
   l.v = o; o += (size_t)(H + 4) * (W + 4) * 64;
-  l.rb = o; o += align16((size_t)R * topk * 4);
+  l.rk = o; o += align16((size_t)R * route_stride(topk) * 2);
+  l.rv = o; o += align16((size_t)R * route_stride(topk) * 2);
+  l.w = o; o += 16 * 5 * 32;
   l.sink = o; o += 16;
   l.total = o;
   return l;
@@ -94,11 +127,13 @@ __global__ __launch_bounds__(64 * NW) void attn_image_kernel(ImageArgs a) {
   constexpr int nthreads = 64 * NW;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int H = a.H, W = a.W, C = a.C, S = a.S, R = S * S, topk = a.topk;
-  const int L = topk * T, WP = W + 4;
+  const int L = topk * T, WP = W + 4, RS = route_stride(topk);
   const ImgLds lay = img_lds(H, W, R, topk);
   uint16_t* kh = reinterpret_cast<uint16_t*>(smem + lay.k);
   uint16_t* vh = reinterpret_cast<uint16_t*>(smem + lay.v);
-  uint32_t* rb = reinterpret_cast<uint32_t*>(smem + lay.rb);
+  uint16_t* rk = reinterpret_cast<uint16_t*>(smem + lay.rk);
+  uint16_t* rv = reinterpret_cast<uint16_t*>(smem + lay.rv);
+  uint32_t* wl = reinterpret_cast<uint32_t*>(smem + lay.w);
   uint16_t* sink = reinterpret_cast<uint16_t*>(smem + lay.sink);
 
   const int tid = threadIdx.x;
@@ -136,61 +171,76 @@ __global__ __launch_bounds__(64 * NW) void attn_image_kernel(ImageArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = i0 + j * nthreads + tid;
-        *reinterpret_cast<uint4*>(i < kp ? kh + (size_t)i * 8 : sink) = kbuf[j];
+        const int tok = i >> 2, y = tok / W, x = tok - y * W;
+        const int pc = (i & 3) ^ kswz(y, x);
+        *reinterpret_cast<uint4*>(i < kp ? kh + (size_t)(4 * tok + pc) * 8 : sink) = kbuf[j];
       }
 #pragma unroll
       for (int j = 0; j < 6; ++j) {
         const int i = j0 + j * nthreads + tid;
-        *reinterpret_cast<uint4*>(i < vp ? vh + (size_t)i * 8 : sink) = vbuf[j];
+        const int pix = i >> 2, py = pix / WP;
+        const int pc = (i & 3) ^ vswz(py);
+        *reinterpret_cast<uint4*>(i < vp ? vh + (size_t)(4 * pix + pc) * 8 : sink) = vbuf[j];
       }
     }
-    // route p of region r -> K token base | bordered-V token base << 16
+    // route slot p of region r -> LDS addresses of the routed region's first
+    // K and V token (slots past topk: region 0, their keys are masked)
     const int32_t* rt = a.route + (size_t)n * R * topk;
-    for (int p = tid; p < R * topk; p += nthreads) {
-      const int rr = rt[p];
+    for (int i = tid; i < R * RS; i += nthreads) {
+      const int r = i / RS, p = i - r * RS;
+      const int rr = p < topk ? rt[r * topk + p] : 0;
       const int js = rr / S, is = rr - js * S;
-      const uint32_t kbase = (uint32_t)(js * RH * W + is * RW);
-      const uint32_t vbase = (uint32_t)((js * RH + 2) * WP + is * RW + 2);
-      rb[p] = kbase | (vbase << 16);
+      // bit 5: the region-column parity of the K swizzle (token bases are 64-byte aligned)
+      rk[i] = (uint16_t)((lay.k + (size_t)(js * RH * W + is * RW) * 64) | (size_t)((is & 1) << 5));
+      rv[i] = (uint16_t)(lay.v + (size_t)((js * RH + 2) * WP + is * RW + 2) * 64);
+    }
+    // LCE weights of the head's 16 channel pairs as dot2 operands, per kernel
+    // row: pixels (0,1) and (2,3) paired per channel (c, then c+1), pixel 4
+    // alone with the other half zero
+    if (tid < 80) {
+      const int cp = tid / 5, ay = tid - cp * 5;
+      const uint32_t* wt = a.wpk + 30 * C + h * 16 + cp + 5 * ay * (C / 2);  // tap-major pairs
+      uint32_t e[5];
+#pragma unroll
+      for (int ax = 0; ax < 5; ++ax) e[ax] = wt[ax * (C / 2)];
+      uint4 w0, w1;
+      w0.x = __builtin_amdgcn_perm(e[1], e[0], 0x05040100u);
+      w0.y = __builtin_amdgcn_perm(e[1], e[0], 0x07060302u);
+      w0.z = __builtin_amdgcn_perm(e[3], e[2], 0x05040100u);
+      w0.w = __builtin_amdgcn_perm(e[3], e[2], 0x07060302u);
+      w1.x = e[4] & 0xffffu;
+      w1.y = e[4] & 0xffff0000u;
+      w1.z = 0u;
+      w1.w = 0u;
+      *reinterpret_cast<uint4*>(wl + tid * 8) = w0;
+      *reinterpret_cast<uint4*>(wl + tid * 8 + 4) = w1;
     }
   }
 
   // ---- per-lane constants ---------------------------------------------------
-  const int tq = col >> 2;   // key tile of this score column
-  const int qt = col & 3;    // query (token of the region) of this score column
-  const uint32_t offK = (uint32_t)((qt / RW) * W + qt % RW);     // K row token: col % 4
-  const uint32_t offV = (uint32_t)((tq / RW) * WP + tq % RW);    // V^T row token: col >> 2
+  const int tq = col & 3;    // key tile of this score column
+  const int qt = col >> 2;   // query (token of the region) of this score column
+  // K row of this lane: token col % 4 of a routed region, piece grp; address
+  // = (route entry ^ kx) + kt (the entry carries the region-column bit of the
+  // piece swizzle, kx the row bit and the piece)
+  const uint32_t kx = 16u * (uint32_t)(grp ^ ((col & 3) >> 1));
+  const uint32_t kt = (uint32_t)(((col & 3) / RW) * W + (col & 3) % RW) * 64;
+  // V^T row of this lane: token col / 4 (padded row parity col / 8), dims
+  // 16hh + 4(col % 4) .. +3 = dwords 8hh + 2(col % 4), +1
+  const int vpar = col >> 3, c4 = col & 3;
+  const uint32_t vt = (uint32_t)(((col >> 2) / RW) * WP + (col >> 2) % RW) * 64;
+  const uint32_t offV0 = vt + 16u * (uint32_t)((c4 >> 1) ^ (3 * vpar)) + 8u * (uint32_t)(c4 & 1);
+  const uint32_t offV1 = vt + 16u * (uint32_t)((2 + (c4 >> 1)) ^ (3 * vpar)) + 8u * (uint32_t)(c4 & 1);
   // this lane's output: query qt, channel pair cp of the head
   const int cp = 2 * grp + (tq & 1) + 8 * (tq >> 1);
-  const int gpair = h * 16 + cp;  // channel pair index in the image (channels 2gpair, +1)
-  // LCE weights of the pair as dot2 operands, per kernel row: pixels (0,1)
-  // and (2,3) paired per channel, pixel 4 alone (the other half zero)
-  uint32_t w01c[5], w01d[5], w23c[5], w23d[5], w4c[5], w4d[5];
-  {
-    const uint32_t* wt = a.wpk + 30 * C + gpair;  // tap-major pairs, [25][C/2]
-    uint32_t d[25];
-#pragma unroll
-    for (int t = 0; t < 25; ++t) d[t] = wt[t * (C / 2)];
-#pragma unroll
-    for (int ay = 0; ay < 5; ++ay) {
-      const uint32_t* e = d + 5 * ay;
-      w01c[ay] = __builtin_amdgcn_perm(e[1], e[0], 0x05040100u);
-      w01d[ay] = __builtin_amdgcn_perm(e[1], e[0], 0x07060302u);
-      w23c[ay] = __builtin_amdgcn_perm(e[3], e[2], 0x05040100u);
-      w23d[ay] = __builtin_amdgcn_perm(e[3], e[2], 0x07060302u);
-      w4c[ay] = e[4] & 0xffffu;
-      w4d[ay] = e[4] & 0xffff0000u;
-    }
-  }
-  const uint32_t bias2 = a.b ? reinterpret_cast<const uint32_t*>(a.b)[gpair] : 0u;
+  const uint32_t bias2 = a.b ? reinterpret_cast<const uint32_t*>(a.b)[h * 16 + cp] : 0u;
 
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
-  const bf16x8 zero8 = {};
-  const bf16x4 zero4 = {};
 
-  // query pixel of column qt in region r, and its Q load (prefetched a region ahead)
+  // query pixel of this lane's column in region r (r wave-uniform), and the
+  // head's Q row there, prefetched a region ahead
   auto qpix = [&](int r, int& y, int& x) {
     const int js = r / S, is = r - js * S;
     y = js * RH + qt / RW;
@@ -202,39 +252,53 @@ __global__ __launch_bounds__(64 * NW) void attn_image_kernel(ImageArgs a) {
     const uint32_t off = r < R ? (uint32_t)(y * W + x) * pixb + hoff + (uint32_t)grp * 16 : kOut;
     return __builtin_bit_cast(bf16x8, ld16(qb, off));
   };
-  bf16x8 bq_next = qload(wave);
-  __syncthreads();  // K, V, routes staged
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  bf16x8 bq_next = qload(wave_u);
+  __syncthreads();  // K, V, routes, weights staged
 
-  for (int r = wave; r < R; r += NW) {
+  // this lane's LCE weights, kept in registers for all its regions
+  uint4 wr0[5];
+  uint2 wr1[5];
+#pragma unroll
+  for (int ay = 0; ay < 5; ++ay) {
+    wr0[ay] = *reinterpret_cast<const uint4*>(wl + cp * 40 + 8 * ay);
+    wr1[ay] = *reinterpret_cast<const uint2*>(wl + cp * 40 + 8 * ay + 4);
+  }
+
+  for (int r = wave_u; r < R; r += NW) {
     const bf16x8 bq = bq_next;
     bq_next = qload(r + NW);
-    const uint32_t* rbr = rb + r * topk;
+    const uint16_t* rkr = rk + r * RS;
+    const uint16_t* rvr = rv + r * RS;
 
     float m = -INFINITY;  // running max of the scaled (base-2) logits
     f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0, ls = o0;
     for (int base = 0; base < L; base += 64) {
-      // K rows: key base + 16t + col; V^T rows: key base + 16t + 4grp + (col >> 2)
+      // K rows: key base + 16t + col; V^T rows: key base + 16t + 4grp + col / 4
       bf16x8 ak[4];
-      const uint16_t* vrow[4];
+      uint32_t va[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int pk = (base >> 2) + 4 * t + (col >> 2);
-        const int pv = (base >> 2) + 4 * t + grp;
-        const uint32_t ek = rbr[pk < topk ? pk : 0];  // keys past L: any row, masked below
-        const uint32_t ev = rbr[pv < topk ? pv : 0];
-        ak[t] = *reinterpret_cast<const bf16x8*>(kh + ((ek & 0xffffu) + offK) * 32 + 8 * grp);
-        vrow[t] = vh + ((ev >> 16) + offV) * 32 + 4 * (col & 3);
+        const uint32_t ka = ((uint32_t)rkr[(base >> 2) + 4 * t + (col >> 2)] ^ kx) + kt;
+        va[t] = rvr[(base >> 2) + 4 * t + grp];
+        ak[t] = *reinterpret_cast<const bf16x8*>(smem + ka);
       }
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      auto vtr = [&](int t, uint32_t off) { return ld_tr(reinterpret_cast<const uint16_t*>(smem + va[t] + off)); };
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      f32x4 st[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) s = mfma(ak[g], tq == g ? bq : zero8, s);
+      for (int g = 0; g < 4; ++g) st[g] = mfma(ak[g], bq, z);
+      f32x4 s;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] = pick4(tq & 1, tq & 2, st[0][e], st[1][e], st[2][e], st[3][e]);
       if (base + 64 > L) {  // ragged last chunk
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (base + 16 * tq + 4 * grp + e >= L) s[e] = -INFINITY;
       }
       float cm = max3(max3(s[0], s[1], s[2]), s[3], -INFINITY);
-      cm = row_class_max<T>(group_max(cm));     // over the key rows, then the tiles of a query
+      cm = group_max(cm);                        // over the key rows
+      cm = dpp_max<0x4e, 0xf>(dpp_max<0xb1, 0xf>(cm));  // over the quad's tiles
       const float mn = fmaxf(m, cm * a.qscale);  // qscale > 0 commutes with max
       if (base > 0) {                            // rescale what earlier chunks summed
         const float corr = __builtin_amdgcn_exp2f(m - mn);
@@ -247,49 +311,51 @@ __global__ __launch_bounds__(64 * NW) void attn_image_kernel(ImageArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(s[e], a.qscale, -mn));
       const bf16x4 pb = to_bf16x4(pv);
-#pragma unroll
-      for (int bb = 0; bb < 2; ++bb) {
-        // k slots: keys 4g..4g+3 of tiles 2bb and 2bb+1; a column takes P only for its own tile
-        const bf16x8 pt = cat(tq == 2 * bb ? pb : zero4, tq == 2 * bb + 1 ? pb : zero4);
-        o0 = mfma(cat(ld_tr(vrow[2 * bb]), ld_tr(vrow[2 * bb + 1])), pt, o0);
-        o1 = mfma(cat(ld_tr(vrow[2 * bb] + 16), ld_tr(vrow[2 * bb + 1] + 16)), pt, o1);
-        ls = mfma(ones, pt, ls);  // every row of ones x P^T is the row sum of P
-      }
+      // k slots: keys 4g..4g+3 of tiles 2bb and 2bb+1, their P broadcast
+      // from the quad lanes that hold them
+      const bf16x8 pt0 = cat(quad_bcast<0>(pb), quad_bcast<1>(pb));
+      const bf16x8 pt1 = cat(quad_bcast<2>(pb), quad_bcast<3>(pb));
+      o0 = mfma(cat(vtr(0, offV0), vtr(1, offV0)), pt0, o0);
+      o1 = mfma(cat(vtr(0, offV1), vtr(1, offV1)), pt0, o1);
+      ls = mfma(ones, pt0, ls);  // every row of ones x P^T is the row sum of P
+      o0 = mfma(cat(vtr(2, offV0), vtr(3, offV0)), pt1, o0);
+      o1 = mfma(cat(vtr(2, offV1), vtr(3, offV1)), pt1, o1);
+      ls = mfma(ones, pt1, ls);
     }
-    // add the tile partials of each query
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      o0[e] = row_class_sum<T>(o0[e]);
-      o1[e] = row_class_sum<T>(o1[e]);
-    }
-    const float inv = 1.0f / row_class_sum<T>(ls[0]);
     // this lane's pair: channels 4grp + 2(tq & 1) (+16 if tq >= 2), +1
-    const f32x4 oh = tq >= 2 ? o1 : o0;
-    const float at0 = ((tq & 1) ? oh[2] : oh[0]) * inv;
-    const float at1 = ((tq & 1) ? oh[3] : oh[1]) * inv;
+    const float inv = __builtin_amdgcn_rcpf(ls[0]);
+    const float at0 = pick4(tq & 1, tq & 2, o0[0], o0[2], o1[0], o1[2]) * inv;
+    const float at1 = pick4(tq & 1, tq & 2, o0[1], o0[3], o1[1], o1[3]) * inv;
 
     // LCE of (query pixel, pair): 5x5 window of the bordered V
     int y, x;
     qpix(r, y, x);
-    float acc0 = bf16_lo(bias2), acc1 = bf16_hi(bias2);
-    const uint32_t* vw = reinterpret_cast<const uint32_t*>(vh) + (size_t)(y * WP + x) * 16 + cp;
+    float acc0 = bf16_lo(bias2), acc1 = bf16_hi(bias2), acc2 = 0.f, acc3 = 0.f;
+    // window row ay is padded row y + ay; its dwords are swizzled by 12 on odd rows
+    const uint32_t* vw = reinterpret_cast<const uint32_t*>(vh) + (size_t)(y * WP + x) * 16;
+    const int cpe = cp ^ (12 * (y & 1)), cpo = cp ^ (12 * ((y + 1) & 1));
 #pragma unroll
     for (int ay = 0; ay < 5; ++ay) {
-      const uint32_t* vr = vw + ay * WP * 16;
+      const uint4 w0 = wr0[ay];
+      const uint2 w1 = wr1[ay];
+      const uint32_t* vr = vw + ay * WP * 16 + ((ay & 1) ? cpo : cpe);
       const uint32_t p0 = vr[0], p1 = vr[16], p2 = vr[32], p3 = vr[48], p4 = vr[64];
-      acc0 = dot2(__builtin_amdgcn_perm(p1, p0, 0x05040100u), w01c[ay], acc0);
-      acc1 = dot2(__builtin_amdgcn_perm(p1, p0, 0x07060302u), w01d[ay], acc1);
-      acc0 = dot2(__builtin_amdgcn_perm(p3, p2, 0x05040100u), w23c[ay], acc0);
-      acc1 = dot2(__builtin_amdgcn_perm(p3, p2, 0x07060302u), w23d[ay], acc1);
-      acc0 = dot2(p4, w4c[ay], acc0);
-      acc1 = dot2(p4, w4d[ay], acc1);
+      acc0 = dot2(__builtin_amdgcn_perm(p1, p0, 0x05040100u), w0.x, acc0);
+      acc1 = dot2(__builtin_amdgcn_perm(p1, p0, 0x07060302u), w0.y, acc1);
+      acc2 = dot2(__builtin_amdgcn_perm(p3, p2, 0x05040100u), w0.z, acc2);
+      acc3 = dot2(__builtin_amdgcn_perm(p3, p2, 0x07060302u), w0.w, acc3);
+      acc0 = dot2(p4, w1.x, acc0);
+      acc1 = dot2(p4, w1.y, acc1);
     }
-    const uint32_t packed = float_to_bf16_bits(at0 + acc0) | (float_to_bf16_bits(at1 + acc1) << 16);
-    *reinterpret_cast<uint32_t*>(a.out + img + (size_t)(y * W + x) * C + 2 * gpair) = packed;
+    const uint32_t packed = float_to_bf16_bits(at0 + (acc0 + acc2)) | (float_to_bf16_bits(at1 + (acc1 + acc3)) << 16);
+    *reinterpret_cast<uint32_t*>(a.out + img + (size_t)(y * W + x) * C + 32 * h + 2 * cp) = packed;
   }
 }
 
 }  // namespace
+
+// four waves: four workgroups per CU (the LDS budget), 16 wave slots
+constexpr int kImageWaves = 4;
 
 bool image_kernel_supports(const Shape& s) {
   if (s.hd != 32 || s.rh != 2 || s.rw != 2) return false;
@@ -308,7 +374,7 @@ hipError_t launch_attend_image(const void* q, const void* k, const void* v, cons
   a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
   const size_t lds = img_lds(s.H, s.W, s.R, s.topk).total;
   const unsigned blocks = (unsigned)(s.N * s.heads);
-  launch(attn_image_kernel<4>, dim3(blocks), dim3(256), lds, st, a);
+  launch(attn_image_kernel<kImageWaves>, dim3(blocks), dim3(64 * kImageWaves), lds, st, a);
   return hipGetLastError();
 }
 

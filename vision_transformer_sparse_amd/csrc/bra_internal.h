@@ -122,6 +122,16 @@ __device__ __forceinline__ float dpp_max(float x) {
   const int y = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK, 0xf, false);
   return __builtin_elementwise_maximum(x, __int_as_float(y));
 }
+// x of another lane by a DPP pattern (every lane of the pattern is valid)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// sum over the four lanes of a quad (quad_perm swaps [1,0,3,2], [2,3,0,1])
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0xb1, 0xf, 0xf, false));
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x4e, 0xf, 0xf, false));
+}
 // maximum / sum over the lanes of a 16-lane row that share l % P (P a power
 // of two dividing 16): DPP row rotations by P, 2P, .. 8
 template <int P>
