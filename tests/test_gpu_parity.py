@@ -82,6 +82,8 @@ SMALL_CASES = [
     ("t4_l96_two_chunks", 1, 16, 16, 128, 4, 8, 24, "bf16", 0.7),
     ("t2_1x2_regions_l14", 1, 6, 12, 64, 2, 6, 7, "bf16", 0.0),
     ("t1_1x1_regions_l40", 1, 8, 8, 64, 2, 8, 40, "bf16", 0.7),
+    # 4x4 regions of an image too large for the image-resident kernel
+    ("t16_region_kernel_64px", 1, 64, 64, 128, 4, 16, 4, "bf16", 0.7),
     ("f32_c0_like", 1, 56, 56, 64, 2, 7, 1, "f32", 0.0),
     ("f32_ragged", 2, 15, 10, 64, 2, 5, 3, "f32", 0.0),
     ("f32_t256", 1, 64, 64, 64, 2, 4, 2, "f32", 0.7),
@@ -124,7 +126,7 @@ def test_region_means(gpu_lib, cfg):
 def test_router_from_oracle_means(gpu_lib, cfg):
     """Routing alone, fed the oracle's means rounded to fp32."""
     import torch
-    inp = draw_config(cfg, N=min(cfg.N, 8))
+    inp = draw_config(cfg)  # full batch: large batches take the per-image routing kernel
     qr = O.region_means(O.partition(inp["q"], cfg.S)).astype(np.float32)
     kr = O.region_means(O.partition(inp["k"], cfg.S)).astype(np.float32)
     say(cfg.name, "route")
@@ -266,7 +268,7 @@ def test_stage_routes_equal_forward_routes(gpu_lib, cfg):
     """bra_route(bra_region_means(q, k)) gives the same route bits as the
     routing inside bra_forward."""
     import torch
-    inp = draw_config(cfg, N=min(cfg.N, 8))
+    inp = draw_config(cfg)  # full batch: large batches take the per-image routing kernel
     args = [dev(inp[x], cfg.dtype) for x in ("q", "k", "v", "lce_w", "lce_b")]
     say(cfg.name, "stage routes")
     _, r_fwd = gpu_lib.forward(*args, cfg.heads, cfg.S, cfg.topk)

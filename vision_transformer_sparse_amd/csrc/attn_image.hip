@@ -97,38 +97,43 @@ struct ImageArgs {
 
 __host__ __device__ constexpr size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-// route slots per region in LDS: topk rounded up to a whole 64-key chunk
-__host__ __device__ constexpr int route_stride(int topk) { return (topk + 15) & ~15; }
+// route slots per region in LDS: topk rounded up to whole 64-key chunks
+// (64 / T slots per chunk)
+__host__ __device__ constexpr int route_stride(int topk, int T) {
+  return (topk + 64 / T - 1) / (64 / T) * (64 / T);
+}
 
 struct ImgLds {
-  size_t k, v, rk, rv, w, sink, total;
+  size_t k, v, rk, rv, w, x, sink, total;
 };
 // K [H*W][32] and bordered V [(H+4)*(W+4)][32] bf16 of one head; the routes
-// as LDS byte addresses of each routed region's first K and V token
-// [S*S][route_stride] (16-bit: the layout stays under 64 KB); the head's LCE
-// weights as dot2 operands [16 pairs][5 rows][8 dwords]; a sink for unused
-// stores.
-__host__ __device__ inline ImgLds img_lds(int H, int W, int R, int topk) {
+// as byte offsets of each routed region's first K and V token within those
+// arrays [S*S][route_stride] (16-bit: each array stays under 64 KB); the
+// head's LCE weights as dot2 operands [16 pairs][5 rows][8 dwords]; for 4x4
+// regions each wave's hand-over of the attention output [16 queries][36]
+// fp32; a sink for unused stores.
+__host__ __device__ inline ImgLds img_lds(int RS, int NW, int H, int W, int R, int topk) {
   ImgLds l;
   size_t o = 0;
   l.k = o; o += (size_t)H * W * 64;
   l.v = o; o += (size_t)(H + 4) * (W + 4) * 64;
-  l.rk = o; o += align16((size_t)R * route_stride(topk) * 2);
-  l.rv = o; o += align16((size_t)R * route_stride(topk) * 2);
+  l.rk = o; o += align16((size_t)R * route_stride(topk, RS * RS) * 2);
+  l.rv = o; o += align16((size_t)R * route_stride(topk, RS * RS) * 2);
   l.w = o; o += 16 * 5 * 32;
+  l.x = o; o += RS == 4 ? (size_t)NW * 16 * 36 * 4 : 0;
   l.sink = o; o += 16;
   l.total = o;
   return l;
 }
 
-template <int NW>
+template <int RS, int NW>
 __global__ __launch_bounds__(64 * NW) void attn_image_kernel(ImageArgs a) {
-  constexpr int RH = 2, RW = 2, T = RH * RW;  // 2x2 regions: 4 key tiles x 4 queries
+  constexpr int RH = RS, RW = RS, T = RS * RS;  // RS x RS regions
   constexpr int nthreads = 64 * NW;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int H = a.H, W = a.W, C = a.C, S = a.S, R = S * S, topk = a.topk;
-  const int L = topk * T, WP = W + 4, RS = route_stride(topk);
-  const ImgLds lay = img_lds(H, W, R, topk);
+  const int L = topk * T, WP = W + 4, RSTR = route_stride(topk, T);
+  const ImgLds lay = img_lds(RS, NW, H, W, R, topk);
   uint16_t* kh = reinterpret_cast<uint16_t*>(smem + lay.k);
   uint16_t* vh = reinterpret_cast<uint16_t*>(smem + lay.v);
   uint16_t* rk = reinterpret_cast<uint16_t*>(smem + lay.rk);
@@ -183,16 +188,17 @@ __global__ __launch_bounds__(64 * NW) void attn_image_kernel(ImageArgs a) {
         *reinterpret_cast<uint4*>(i < vp ? vh + (size_t)(4 * pix + pc) * 8 : sink) = vbuf[j];
       }
     }
-    // route slot p of region r -> LDS addresses of the routed region's first
-    // K and V token (slots past topk: region 0, their keys are masked)
+    // route slot p of region r -> offsets of the routed region's first K and
+    // bordered-V token (slots past topk: region 0, their keys are masked)
     const int32_t* rt = a.route + (size_t)n * R * topk;
-    for (int i = tid; i < R * RS; i += nthreads) {
-      const int r = i / RS, p = i - r * RS;
+    for (int i = tid; i < R * RSTR; i += nthreads) {
+      const int r = i / RSTR, p = i - r * RSTR;
       const int rr = p < topk ? rt[r * topk + p] : 0;
       const int js = rr / S, is = rr - js * S;
-      // bit 5: the region-column parity of the K swizzle (token bases are 64-byte aligned)
-      rk[i] = (uint16_t)((lay.k + (size_t)(js * RH * W + is * RW) * 64) | (size_t)((is & 1) << 5));
-      rv[i] = (uint16_t)(lay.v + (size_t)((js * RH + 2) * WP + is * RW + 2) * 64);
+      // 2x2 regions: bit 5 carries the region-column parity of the K swizzle
+      // (token offsets are 64-byte aligned)
+      rk[i] = (uint16_t)(((size_t)(js * RH * W + is * RW) * 64) | (size_t)(RS == 2 ? (is & 1) << 5 : 0));
+      rv[i] = (uint16_t)((size_t)((js * RH + 2) * WP + is * RW + 2) * 64);
     }
     // LCE weights of the head's 16 channel pairs as dot2 operands, per kernel
     // row: pixels (0,1) and (2,3) paired per channel (c, then c+1), pixel 4
@@ -217,6 +223,12 @@ __global__ __launch_bounds__(64 * NW) void attn_image_kernel(ImageArgs a) {
     }
   }
 
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  if constexpr (RS == 2) {
   // ---- per-lane constants ---------------------------------------------------
   const int tq = col & 3;    // key tile of this score column
   const int qt = col >> 2;   // query (token of the region) of this score column
@@ -224,20 +236,16 @@ __global__ __launch_bounds__(64 * NW) void attn_image_kernel(ImageArgs a) {
   // = (route entry ^ kx) + kt (the entry carries the region-column bit of the
   // piece swizzle, kx the row bit and the piece)
   const uint32_t kx = 16u * (uint32_t)(grp ^ ((col & 3) >> 1));
-  const uint32_t kt = (uint32_t)(((col & 3) / RW) * W + (col & 3) % RW) * 64;
+  const uint32_t kt = (uint32_t)lay.k + (uint32_t)(((col & 3) / RW) * W + (col & 3) % RW) * 64;
   // V^T row of this lane: token col / 4 (padded row parity col / 8), dims
   // 16hh + 4(col % 4) .. +3 = dwords 8hh + 2(col % 4), +1
   const int vpar = col >> 3, c4 = col & 3;
-  const uint32_t vt = (uint32_t)(((col >> 2) / RW) * WP + (col >> 2) % RW) * 64;
+  const uint32_t vt = (uint32_t)lay.v + (uint32_t)(((col >> 2) / RW) * WP + (col >> 2) % RW) * 64;
   const uint32_t offV0 = vt + 16u * (uint32_t)((c4 >> 1) ^ (3 * vpar)) + 8u * (uint32_t)(c4 & 1);
   const uint32_t offV1 = vt + 16u * (uint32_t)((2 + (c4 >> 1)) ^ (3 * vpar)) + 8u * (uint32_t)(c4 & 1);
   // this lane's output: query qt, channel pair cp of the head
   const int cp = 2 * grp + (tq & 1) + 8 * (tq >> 1);
   const uint32_t bias2 = a.b ? reinterpret_cast<const uint32_t*>(a.b)[h * 16 + cp] : 0u;
-
-  bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
   // query pixel of this lane's column in region r (r wave-uniform), and the
   // head's Q row there, prefetched a region ahead
@@ -252,7 +260,6 @@ __global__ __launch_bounds__(64 * NW) void attn_image_kernel(ImageArgs a) {
     const uint32_t off = r < R ? (uint32_t)(y * W + x) * pixb + hoff + (uint32_t)grp * 16 : kOut;
     return __builtin_bit_cast(bf16x8, ld16(qb, off));
   };
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   bf16x8 bq_next = qload(wave_u);
   __syncthreads();  // K, V, routes, weights staged
 
@@ -268,8 +275,8 @@ __global__ __launch_bounds__(64 * NW) void attn_image_kernel(ImageArgs a) {
   for (int r = wave_u; r < R; r += NW) {
     const bf16x8 bq = bq_next;
     bq_next = qload(r + NW);
-    const uint16_t* rkr = rk + r * RS;
-    const uint16_t* rvr = rv + r * RS;
+    const uint16_t* rkr = rk + r * RSTR;
+    const uint16_t* rvr = rv + r * RSTR;
 
     float m = -INFINITY;  // running max of the scaled (base-2) logits
     f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0, ls = o0;
@@ -350,18 +357,163 @@ __global__ __launch_bounds__(64 * NW) void attn_image_kernel(ImageArgs a) {
     const uint32_t packed = float_to_bf16_bits(at0 + (acc0 + acc2)) | (float_to_bf16_bits(at1 + (acc1 + acc3)) << 16);
     *reinterpret_cast<uint32_t*>(a.out + img + (size_t)(y * W + x) * C + 32 * h + 2 * cp) = packed;
   }
+  } else {
+  // ---- 4x4 regions: a score tile is one routed region (16 keys) against the
+  // region's 16 queries (lane column = query); the output goes through LDS to
+  // the LCE layout, a lane per (region column, channel pair) walking a
+  // vertical window of the bordered V
+  static_assert(RS == 4, "2x2 or 4x4 regions");
+  // K row of this lane: token (col / 4, col % 4) of a routed region (whose
+  // origin is a multiple of 4, so its swizzle depends on col only)
+  const int f = ((col >> 2) & 1) | (((col & 3) >> 1) << 1);
+  const uint32_t kt = (uint32_t)lay.k + (uint32_t)((col >> 2) * W + (col & 3)) * 64 + 16u * (uint32_t)(grp ^ f);
+  // V^T row of this lane: key 4grp + col / 4 of a tile = token (grp, col / 4),
+  // padded row parity grp & 1; dims 16hh + 4(col % 4) .. +3
+  const int c4 = col & 3, vpar = grp & 1;
+  const uint32_t vt = (uint32_t)lay.v + (uint32_t)(grp * WP + (col >> 2)) * 64;
+  const uint32_t offV0 = vt + 16u * (uint32_t)((c4 >> 1) ^ (3 * vpar)) + 8u * (uint32_t)(c4 & 1);
+  const uint32_t offV1 = vt + 16u * (uint32_t)((2 + (c4 >> 1)) ^ (3 * vpar)) + 8u * (uint32_t)(c4 & 1);
+  // LCE item of this lane: channel pair pp of the head, region column xc
+  const int pp = lane & 15, xc = lane >> 4;
+  const uint32_t bias2 = a.b ? reinterpret_cast<const uint32_t*>(a.b)[h * 16 + pp] : 0u;
+  float* xw = reinterpret_cast<float*>(smem + lay.x) + wave * (16 * 36);  // this wave's hand-over
+
+  auto qload = [&](int r) {
+    const int js = r / S, is = r - js * S;
+    const int y = js * RH + (col >> 2), x = is * RW + (col & 3);
+    const uint32_t off = r < R ? (uint32_t)(y * W + x) * pixb + hoff + (uint32_t)grp * 16 : kOut;
+    return __builtin_bit_cast(bf16x8, ld16(qb, off));
+  };
+  bf16x8 bq_next = qload(wave_u);
+  __syncthreads();  // K, V, routes, weights staged
+
+  uint4 wr0[5];
+  uint2 wr1[5];
+#pragma unroll
+  for (int ay = 0; ay < 5; ++ay) {
+    wr0[ay] = *reinterpret_cast<const uint4*>(wl + pp * 40 + 8 * ay);
+    wr1[ay] = *reinterpret_cast<const uint2*>(wl + pp * 40 + 8 * ay + 4);
+  }
+
+  for (int r = wave_u; r < R; r += NW) {
+    const bf16x8 bq = bq_next;
+    bq_next = qload(r + NW);
+    const uint16_t* rkr = rk + r * RSTR;
+    const uint16_t* rvr = rv + r * RSTR;
+
+    float m = -INFINITY;  // running max of the scaled (base-2) logits
+    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0, ls = o0;
+    for (int base = 0; base < L; base += 64) {
+      bf16x8 ak[4];
+      uint32_t va[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {  // tile t = route slot base / 16 + t
+        const int slot = (base >> 4) + t;
+        ak[t] = *reinterpret_cast<const bf16x8*>(smem + rkr[slot] + kt);
+        va[t] = rvr[slot];
+      }
+      auto vtr = [&](int t, uint32_t off) { return ld_tr(reinterpret_cast<const uint16_t*>(smem + va[t] + off)); };
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      f32x4 sc[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sc[t] = mfma(ak[t], bq, z);
+      if (base + 64 > L) {  // ragged last chunk
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (base + 16 * t + 4 * grp + e >= L) sc[t][e] = -INFINITY;
+      }
+      float cm = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) cm = max3(cm, max3(sc[t][0], sc[t][1], sc[t][2]), sc[t][3]);
+      cm = group_max(cm);                        // over the key rows
+      const float mn = fmaxf(m, cm * a.qscale);  // qscale > 0 commutes with max
+      if (base > 0) {                            // rescale what earlier chunks summed
+        const float corr = __builtin_amdgcn_exp2f(m - mn);
+        o0 *= corr;
+        o1 *= corr;
+        ls *= corr;
+      }
+      m = mn;
+      bf16x4 pb[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        f32x4 pv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[t][e], a.qscale, -mn));
+        pb[t] = to_bf16x4(pv);
+      }
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        // k slots: keys 4g..4g+3 of tiles 2bb and 2bb+1
+        const bf16x8 pt = cat(pb[2 * bb], pb[2 * bb + 1]);
+        o0 = mfma(cat(vtr(2 * bb, offV0), vtr(2 * bb + 1, offV0)), pt, o0);
+        o1 = mfma(cat(vtr(2 * bb, offV1), vtr(2 * bb + 1, offV1)), pt, o1);
+        ls = mfma(ones, pt, ls);  // every row of ones x P^T is the row sum of P
+      }
+    }
+    // hand the output of query col (dims 4grp.., 16 + 4grp..) to the LCE layout
+    const float inv = __builtin_amdgcn_rcpf(ls[0]);
+    *reinterpret_cast<f32x4*>(xw + col * 36 + 4 * grp) = o0 * inv;
+    *reinterpret_cast<f32x4*>(xw + col * 36 + 16 + 4 * grp) = o1 * inv;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float2 at[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) at[i] = *reinterpret_cast<const float2*>(xw + (4 * i + xc) * 36 + 2 * pp);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // read before the next region's hand-over
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // LCE of column xc, rows 0..3 of the region, channel pair pp: window rows
+    // wr = 0..7 are bordered rows 4js + wr (parity wr & 1), columns 4is + xc ..
+    const int js = r / S, is = r - js * S;
+    float acc0[4], acc1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { acc0[i] = bf16_lo(bias2); acc1[i] = bf16_hi(bias2); }
+    const uint32_t* vw = reinterpret_cast<const uint32_t*>(vh) + (size_t)((4 * js) * WP + 4 * is + xc) * 16;
+#pragma unroll
+    for (int wr = 0; wr < 8; ++wr) {
+      const uint32_t* vr = vw + wr * WP * 16 + (pp ^ (12 * (wr & 1)));
+      const uint32_t p0 = vr[0], p1 = vr[16], p2 = vr[32], p3 = vr[48], p4 = vr[64];
+      const uint32_t h01c = __builtin_amdgcn_perm(p1, p0, 0x05040100u), h01d = __builtin_amdgcn_perm(p1, p0, 0x07060302u);
+      const uint32_t h23c = __builtin_amdgcn_perm(p3, p2, 0x05040100u), h23d = __builtin_amdgcn_perm(p3, p2, 0x07060302u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ay = wr - i;
+        if (ay >= 0 && ay < 5) {
+          acc0[i] = dot2(h01c, wr0[ay].x, acc0[i]);
+          acc1[i] = dot2(h01d, wr0[ay].y, acc1[i]);
+          acc0[i] = dot2(h23c, wr0[ay].z, acc0[i]);
+          acc1[i] = dot2(h23d, wr0[ay].w, acc1[i]);
+          acc0[i] = dot2(p4, wr1[ay].x, acc0[i]);
+          acc1[i] = dot2(p4, wr1[ay].y, acc1[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t packed = float_to_bf16_bits(at[i].x + acc0[i]) | (float_to_bf16_bits(at[i].y + acc1[i]) << 16);
+      *reinterpret_cast<uint32_t*>(a.out + img + ((size_t)(4 * js + i) * W + 4 * is + xc) * C + 32 * h + 2 * pp) = packed;
+    }
+  }
+  }
 }
 
 }  // namespace
 
-// four waves: four workgroups per CU (the LDS budget), 16 wave slots
-constexpr int kImageWaves = 4;
+// 2x2 regions: four waves, four workgroups per CU (the LDS budget); 4x4
+// regions: sixteen waves, one workgroup per CU
+template <int RS> constexpr int image_waves() { return RS == 2 ? 4 : 16; }
 
 bool image_kernel_supports(const Shape& s) {
-  if (s.hd != 32 || s.rh != 2 || s.rw != 2) return false;
-  if ((long long)s.H * s.W * s.C >= (1ll << 30)) return false;  // 32-bit byte offsets in an image
-  if ((long long)(s.H + 4) * (s.W + 4) >= 65536) return false;   // 16-bit token bases
-  return img_lds(s.H, s.W, s.R, s.topk).total <= 40 * 1024;      // four workgroups per CU
+  if (s.hd != 32 || s.rh != s.rw || (s.rh != 2 && s.rh != 4)) return false;
+  if ((long long)s.H * s.W * s.C >= (1ll << 30)) return false;    // 32-bit byte offsets in an image
+  if ((long long)(s.H + 4) * (s.W + 4) * 64 > 65536) return false;  // 16-bit token offsets
+  if (s.rh == 2) return img_lds(2, image_waves<2>(), s.H, s.W, s.R, s.topk).total <= 40 * 1024;  // four per CU
+  return img_lds(4, image_waves<4>(), s.H, s.W, s.R, s.topk).total <= 160 * 1024;
 }
 
 hipError_t launch_attend_image(const void* q, const void* k, const void* v, const uint32_t* wpk,
@@ -372,9 +524,14 @@ hipError_t launch_attend_image(const void* q, const void* k, const void* v, cons
   a.wpk = wpk; a.b = (const uint16_t*)b; a.route = route; a.out = (uint16_t*)out;
   a.N = s.N; a.H = s.H; a.W = s.W; a.C = s.C; a.heads = s.heads; a.S = s.S; a.topk = s.topk;
   a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
-  const size_t lds = img_lds(s.H, s.W, s.R, s.topk).total;
   const unsigned blocks = (unsigned)(s.N * s.heads);
-  launch(attn_image_kernel<kImageWaves>, dim3(blocks), dim3(64 * kImageWaves), lds, st, a);
+  if (s.rh == 2) {
+    constexpr int nw = image_waves<2>();
+    launch(attn_image_kernel<2, nw>, dim3(blocks), dim3(64 * nw), img_lds(2, nw, s.H, s.W, s.R, s.topk).total, st, a);
+  } else {
+    constexpr int nw = image_waves<4>();
+    launch(attn_image_kernel<4, nw>, dim3(blocks), dim3(64 * nw), img_lds(4, nw, s.H, s.W, s.R, s.topk).total, st, a);
+  }
   return hipGetLastError();
 }
 
