@@ -88,7 +88,8 @@ int bra_forward(const void* q, const void* k, const void* v,
 /* Step 2 alone: qr, kr = region means of q and k, fp32 [N][S*S][C] each
  * (caller-owned device buffers). Same checks as bra_forward (heads and topk
  * are not involved). The means are bit-identical to the ones bra_forward
- * routes on, so bra_route(bra_region_means(...)) reproduces its routes. */
+ * routes on (the same kernel), so bra_route(bra_region_means(...)) reproduces
+ * its routes. */
 int bra_region_means(const void* q, const void* k, int N, int H, int W, int C,
                      int S, int dtype, float* qr, float* kr);
 
@@ -142,10 +143,7 @@ int bra_version(void);
  * start and stop events take the time stamps of that kernel's own dispatch
  * (no extra stream commands between kernels).
  * bra_profile_set_mask(mask) changes which kinds are recorded from the next
- * launch on without clearing the record (to sample some launches of a run).
- * For a batch of at least 64 images with S*S <= 64, bra_forward computes the
- * region means inside its routing kernel: that kernel is recorded as
- * BRA_K_ROUTE and BRA_K_POOL records nothing. */
+ * launch on without clearing the record (to sample some launches of a run). */
 enum bra_kernel_kind {
   BRA_K_POOL = 0, BRA_K_ROUTE = 1, BRA_K_ATTN = 2, BRA_K_LCE = 3, BRA_K_COUNT = 4
 };

@@ -32,9 +32,6 @@ bool tile_kernel_supports(const Shape& s);
 hipError_t launch_attend_tile(const void* q, const void* k, const void* v, const uint32_t* wpk,
                               const void* b, const int32_t* route, const Shape& s, void* out,
                               hipStream_t st);
-bool route_image_supports(const Shape& s);
-hipError_t launch_route_image(const void* q, const void* k, const Shape& s, int dtype, int32_t* route,
-                              float* qr, float* kr, const void* lce_w, uint32_t* wpk, hipStream_t st);
 size_t lce_pack_bytes(int C);
 hipError_t launch_lce_pack(const void* w, int C, uint32_t* wpk, hipStream_t st);
 
@@ -254,16 +251,12 @@ int bra_forward(const void* q, const void* k, const void* v, const void* lce_w,
   uint32_t* wpk = dtype == BRA_BF16 ? reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + wl.wpk) : nullptr;
   hipStream_t st = g_stream;
   hipError_t e;
-  if (bra::route_image_supports(s)) {
-    // batches of small images: region means and routing in one kernel
-    ProfScope ps(BRA_K_ROUTE, st);
-    e = bra::launch_route_image(q, k, s, dtype, route_idx, nullptr, nullptr, lce_w, wpk, st);
-  } else {
-    {
-      ProfScope ps(BRA_K_POOL, st);
-      e = bra::launch_region_pool(q, k, s, dtype, qr, kr, lce_w, wpk, st);
-    }
-    if (e != hipSuccess) return hip_fail(e);
+  {
+    ProfScope ps(BRA_K_POOL, st);
+    e = bra::launch_region_pool(q, k, s, dtype, qr, kr, lce_w, wpk, st);
+  }
+  if (e != hipSuccess) return hip_fail(e);
+  {
     ProfScope ps(BRA_K_ROUTE, st);
     e = bra::launch_route(qr, kr, N, s.R, C, topk, route_idx, st);
   }
@@ -284,11 +277,8 @@ int bra_region_means(const void* q, const void* k, int N, int H, int W, int C, i
   hipStream_t st = g_stream;
   hipError_t e;
   {
-    // the same means arithmetic as bra_forward uses for this shape
     ProfScope ps(BRA_K_POOL, st);
-    e = bra::route_image_supports(s)
-            ? bra::launch_route_image(q, k, s, dtype, nullptr, qr, kr, nullptr, nullptr, st)
-            : bra::launch_region_pool(q, k, s, dtype, qr, kr, nullptr, nullptr, st);
+    e = bra::launch_region_pool(q, k, s, dtype, qr, kr, nullptr, nullptr, st);
   }
   return e == hipSuccess ? BRA_OK : hip_fail(e);
 }

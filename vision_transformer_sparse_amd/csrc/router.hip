@@ -13,8 +13,8 @@
 //    Lane (i, g) of a tile takes the 16-byte pieces at channels 16j+4g of
 //    row i of its A (Q^r) and B (K^r) operands -- the same channels on both
 //    sides -- straight from memory with buffer loads (pieces past C read as
-//    zero), 64 channels per batch with the next batch in flight. The scaled
-//    logits go to LDS.
+//    zero), up to 256 channels in flight at once, multiplied in four
+//    independent accumulation chains. The scaled logits go to LDS.
 //  * R > 64 (route_wide_kernel): one workgroup per 4 query rows, one wave per
 //    64 candidates; each lane streams its own candidate's K^r row from L2
 //    into registers (double-buffered 32-channel batches) and reads the 4 Q^r
@@ -82,41 +82,40 @@ __host__ __device__ inline size_t route_lds(int R) {
 // One 16 x 16 logit tile: rows r0.., columns 16ct.. of (Q^r K^r^T) * scale,
 // lane (col, grp) returning rows 4grp..4grp+3 at column col. get(row, c)
 // returns the 16-byte piece of channels c..c+3 of a Q^r (a) / K^r (b) row
-// (rows clamped to R-1, pieces past C zero). The fp32 MFMA sequence is the
-// same wherever the operands come from, so the logits are too.
-template <typename GetA, typename GetB>
+// (rows clamped to R-1, pieces past C zero). Channels are loaded NB x 64 at
+// a time (every load of a group in flight; pieces past C read as zero and
+// add nothing) and multiplied in four independent fp32 MFMA chains (channel
+// offsets 16j + 4grp, j = 0..3), added at the end; the order is fixed, so
+// the logits are reproducible bit for bit.
+template <int NB, typename GetA, typename GetB>
 __device__ __forceinline__ f32x4 logit_tile(int col, int grp, int C, GetA geta, GetB getb) {
-  uint4 a[4], b[4], an[4], bn[4];
-  auto fetch = [&](int c0, uint4* aa, uint4* bb) {
+  constexpr int kGroup = NB;  // 64-channel batches per load group
+  f32x4 acc[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = c0 + 16 * j + 4 * grp;
-      aa[j] = geta(c);
-      bb[j] = getb(c);
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int g0 = 0; g0 < C; g0 += kGroup * kChunk) {
+    uint4 a[kGroup][4], b[kGroup][4];
+#pragma unroll
+    for (int bt = 0; bt < kGroup; ++bt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = g0 + bt * kChunk + 16 * j + 4 * grp;
+        a[bt][j] = geta(c);
+        b[bt][j] = getb(c);
+      }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the group before the first product
+#pragma unroll
+    for (int bt = 0; bt < kGroup; ++bt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[bt][j].x), __uint_as_float(b[bt][j].x), acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[bt][j].y), __uint_as_float(b[bt][j].y), acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[bt][j].z), __uint_as_float(b[bt][j].z), acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[bt][j].w), __uint_as_float(b[bt][j].w), acc[j], 0, 0, 0);
+      }
     }
-  };
-  auto mfma4 = [&](f32x4 acc) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].x), __uint_as_float(b[j].x), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].y), __uint_as_float(b[j].y), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].z), __uint_as_float(b[j].z), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].w), __uint_as_float(b[j].w), acc, 0, 0, 0);
-    }
-    return acc;
-  };
-  // the next batch is always in flight while one is multiplied (the last
-  // batch is peeled off, so no branch guards the loads)
-  fetch(0, a, b);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  int c0 = 0;
-  for (; c0 + kChunk < C; c0 += kChunk) {
-    fetch(c0 + kChunk, an, bn);
-    acc = mfma4(acc);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { a[j] = an[j]; b[j] = bn[j]; }
   }
-  return mfma4(acc);
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
 // Top-k of rows i0, i0 + step, ... (four at a time) of the logit block
@@ -165,6 +164,7 @@ __device__ __forceinline__ void rank_rows(const float* logit, int RP, int R, int
   }
 }
 
+template <int NB>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ qr,
                                                     const float* __restrict__ kr, int R, int C,
                                                     int topk, float scale,
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ qr
   // ---- affinities: wave ct computes column tile ct
   for (int ct = wave; ct < CT; ct += waves) {
     const uint32_t krow = (uint32_t)min(16 * ct + col, R - 1) * C * 4;
-    const f32x4 acc = logit_tile(
+    const f32x4 acc = logit_tile<NB>(
         col, grp, C, [&](int c) { return ld16(qb, c < C ? qrow + 4 * c : kOut); },
         [&](int c) { return ld16(kb, c < C ? krow + 4 * c : kOut); });
     // lane (col, grp) holds rows 4grp..4grp+3 of the tile at column col
@@ -205,136 +205,15 @@ hipError_t launch_small(const float* qr, const float* kr, int N, int R, int C, i
                         int32_t* route, hipStream_t st) {
   const float scale = (float)(1.0 / __builtin_sqrt((double)C));
   const unsigned blocks = (unsigned)(N * col_tiles(R));
-  launch(route_kernel, dim3(blocks), dim3(64 * col_tiles(R)), route_lds(R), st, qr, kr,
-                     R, C, topk, scale, route);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------- one workgroup per image
-// For batches of small images (R <= 64) the region means and the routing
-// of an image are one workgroup: its threads sum q and k over every region
-// (each (region, 16-byte channel chunk) sequentially over the region's tokens
-// in row-major order, then divided by T), keep Q^r and K^r in LDS, and its
-// waves then take the logit tiles and the rank selection of route_kernel
-// with the operands read from LDS. Saves the means' round trip through
-// memory and a launch. With `means` set it writes Q^r, K^r instead of routes
-// (the region-means entry point, so both paths share one arithmetic).
-constexpr int kImgThreads = 1024;
-
-// LDS row of a region mean: C floats + 4, so the 16-byte pieces that the 16
-// lanes of a logit tile read (one row each) fall on different banks
-__host__ __device__ inline int mean_stride(int C) { return C + 4; }
-
-__host__ __device__ inline size_t route_image_lds(int R, int C) {
-  const size_t means = (size_t)2 * R * mean_stride(C) * sizeof(float);
-  const size_t keys = (size_t)(kImgThreads / 64) * 4 * 64 * sizeof(uint64_t);
-  return (means > keys ? means : keys) + (size_t)R * 16 * col_tiles(R) * sizeof(float);
-}
-
-template <typename T>
-__global__ __launch_bounds__(kImgThreads) void route_image_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, int H, int W, int C, int S, int topk,
-    float scale, int32_t* __restrict__ route, float* __restrict__ qr_out, float* __restrict__ kr_out,
-    const uint16_t* __restrict__ lw, uint32_t* __restrict__ wpk) {
-  constexpr int V = 16 / sizeof(T);  // channels per 16-byte chunk
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int R = S * S, rh = H / S, rw = W / S, T_ = rh * rw;
-  const int CT = col_tiles(R), RP = 16 * CT;
-  const int MS = mean_stride(C);
-  float* qs = reinterpret_cast<float*>(smem);           // [R][MS]
-  float* ks = qs + (size_t)R * MS;                      // [R][MS]
-  uint64_t* keys = reinterpret_cast<uint64_t*>(smem);   // [16][4][64], after the logits
-  const size_t mbytes = (size_t)2 * R * MS * sizeof(float);
-  const size_t kbytes = (size_t)(kImgThreads / 64) * 4 * 64 * sizeof(uint64_t);
-  float* logit = reinterpret_cast<float*>(smem + (mbytes > kbytes ? mbytes : kbytes));  // [R][RP]
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int col = lane & 15, grp = lane >> 4;
-  const int n = xcd_unit(blockIdx.x, gridDim.x);
-  const uint32_t img_bytes = (uint32_t)H * W * C * sizeof(T);
-  const Rsrc qb = rsrc(q + (size_t)n * H * W * C, img_bytes);
-  const Rsrc kb = rsrc(k + (size_t)n * H * W * C, img_bytes);
-
-  if (wpk)  // side job: the LCE weights repacked for the attention kernels
-    for (int e = blockIdx.x * kImgThreads + tid; e < lce_pack_items(C); e += gridDim.x * kImgThreads)
-      pack_lce_item(lw, C, e, wpk);
-
-  // ---- region means: item (region, chunk), tokens in batches of 8
-  const int nchunk = C / V;
-  for (int it = tid; it < R * nchunk; it += kImgThreads) {
-    const int r = it / nchunk, ch = it - r * nchunk;
-    const int js = r / S, is = r - js * S;
-    const uint32_t base = ((uint32_t)(js * rh) * W + (uint32_t)(is * rw)) * C * sizeof(T) + ch * 16;
-    float aq[V], ak[V];
-#pragma unroll
-    for (int e = 0; e < V; ++e) { aq[e] = 0.f; ak[e] = 0.f; }
-    for (int t0 = 0; t0 < T_; t0 += 8) {
-      uint4 bq[8], bk[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int t = t0 + u;
-        const uint32_t off = t < T_ ? base + ((uint32_t)(t / rw) * W + (uint32_t)(t % rw)) * C * sizeof(T) : kOut;
-        bq[u] = ld16(qb, off);
-        bk[u] = ld16(kb, off);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (t0 + u < T_) {
-          if constexpr (V == 8) {
-            const uint32_t wq[4] = {bq[u].x, bq[u].y, bq[u].z, bq[u].w};
-            const uint32_t wk[4] = {bk[u].x, bk[u].y, bk[u].z, bk[u].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              aq[2 * e] += bf16_lo(wq[e]); aq[2 * e + 1] += bf16_hi(wq[e]);
-              ak[2 * e] += bf16_lo(wk[e]); ak[2 * e + 1] += bf16_hi(wk[e]);
-            }
-          } else {
-            aq[0] += __uint_as_float(bq[u].x); aq[1] += __uint_as_float(bq[u].y);
-            aq[2] += __uint_as_float(bq[u].z); aq[3] += __uint_as_float(bq[u].w);
-            ak[0] += __uint_as_float(bk[u].x); ak[1] += __uint_as_float(bk[u].y);
-            ak[2] += __uint_as_float(bk[u].z); ak[3] += __uint_as_float(bk[u].w);
-          }
-        }
-      }
-    }
-    const float count = (float)T_;
-    float* dq = qr_out ? qr_out + ((size_t)n * R + r) * C + ch * V : qs + (size_t)r * MS + ch * V;
-    float* dk = qr_out ? kr_out + ((size_t)n * R + r) * C + ch * V : ks + (size_t)r * MS + ch * V;
-#pragma unroll
-    for (int e = 0; e < V; ++e) { dq[e] = aq[e] / count; dk[e] = ak[e] / count; }
-  }
-  if (qr_out) return;  // means only
-  __syncthreads();
-
-  // ---- logits: wave w takes tile (w / CT, w % CT)
-  for (int tile = wave; tile < CT * CT; tile += kImgThreads / 64) {
-    const int rt = tile / CT, ct = tile - rt * CT;
-    const float* qrow = qs + (size_t)min(16 * rt + col, R - 1) * MS;
-    const float* krow = ks + (size_t)min(16 * ct + col, R - 1) * MS;
-    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-    const f32x4 acc = logit_tile(
-        col, grp, C,
-        [&](int c) { return c < C ? *reinterpret_cast<const uint4*>(qrow + c) : zero; },
-        [&](int c) { return c < C ? *reinterpret_cast<const uint4*>(krow + c) : zero; });
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 16 * rt + 4 * grp + e;
-      if (row < R) logit[row * RP + 16 * ct + col] = acc[e] * scale;
-    }
-  }
-  __syncthreads();  // logits ready; the means are dead (the key buffers reuse them)
-
-  // ---- rank selection: rows wave, wave + 16, ...
-  rank_rows(logit, RP, R, R, wave, kImgThreads / 64, topk, keys + (size_t)wave * 4 * 64, lane,
-            [&](int i) { return route + ((size_t)n * R + i) * topk; });
-}
-
-template <typename T>
-hipError_t launch_image(const void* q, const void* k, int N, int H, int W, int C, int S, int topk,
-                        int32_t* route, float* qr, float* kr, const void* lw, uint32_t* wpk,
-                        hipStream_t st) {
-  const float scale = (float)(1.0 / __builtin_sqrt((double)C));
-  launch(route_image_kernel<T>, dim3((unsigned)N), dim3(kImgThreads), qr ? 0 : route_image_lds(S * S, C),
-         st, (const T*)q, (const T*)k, H, W, C, S, topk, scale, route, qr, kr, (const uint16_t*)lw, wpk);
+  // 64-channel batches per load group: all of C up to 256 channels
+  const int nb = (C + kChunk - 1) / kChunk;
+#define BRA_ROUTE(NB) \
+  launch(route_kernel<NB>, dim3(blocks), dim3(64 * col_tiles(R)), route_lds(R), st, qr, kr, R, C, topk, scale, route)
+  if (nb <= 1) BRA_ROUTE(1);
+  else if (nb <= 2) BRA_ROUTE(2);
+  else if (nb <= 3) BRA_ROUTE(3);
+  else BRA_ROUTE(4);
+#undef BRA_ROUTE
   return hipGetLastError();
 }
 
@@ -431,18 +310,6 @@ hipError_t launch_wide(const float* qr, const float* kr, int N, int R, int C, in
 }
 
 }  // namespace
-
-bool route_image_supports(const Shape& s) {
-  if (s.R > 64 || s.N < 64) return false;  // a batch of small images: one workgroup each
-  if ((long long)s.H * s.W * s.C * 4 >= (1ll << 31)) return false;  // 32-bit offsets in an image
-  return route_image_lds(s.R, s.C) <= 160 * 1024;
-}
-
-hipError_t launch_route_image(const void* q, const void* k, const Shape& s, int dtype, int32_t* route,
-                              float* qr, float* kr, const void* lce_w, uint32_t* wpk, hipStream_t st) {
-  return dtype == 1 ? launch_image<uint16_t>(q, k, s.N, s.H, s.W, s.C, s.S, s.topk, route, qr, kr, lce_w, wpk, st)
-                    : launch_image<float>(q, k, s.N, s.H, s.W, s.C, s.S, s.topk, route, qr, kr, nullptr, nullptr, st);
-}
 
 hipError_t launch_route(const float* qr, const float* kr, int N, int R, int C, int topk,
                         int32_t* route, hipStream_t st) {
