@@ -29,6 +29,10 @@ hipError_t launch_attend_image(const void* q, const void* k, const void* v, cons
                                const void* b, const int32_t* route, const Shape& s, void* out,
                                hipStream_t st);
 bool tile_kernel_supports(const Shape& s);
+bool f32_kernel_supports(const Shape& s);
+hipError_t launch_attend_f32(const void* q, const void* k, const void* v, const void* w,
+                             const void* b, const int32_t* route, const Shape& s, void* out,
+                             hipStream_t st);
 hipError_t launch_attend_tile(const void* q, const void* k, const void* v, const uint32_t* wpk,
                               const void* b, const int32_t* route, const Shape& s, void* out,
                               hipStream_t st);
@@ -220,6 +224,8 @@ int attend(const void* q, const void* k, const void* v, const void* w, const voi
       e = bra::launch_attend_tile(q, k, v, wpk, b, route, s, out, st);
     else if (dtype == BRA_BF16 && bra::mfma_supports(s))
       e = bra::launch_attend_mfma(q, k, v, w, b, route, s, out, st);
+    else if (dtype == BRA_F32 && bra::f32_kernel_supports(s))
+      e = bra::launch_attend_f32(q, k, v, w, b, route, s, out, st);
     else
       e = bra::launch_attend_valu(q, k, v, w, b, route, s, dtype, out, st);
   }
