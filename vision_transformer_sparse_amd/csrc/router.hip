@@ -13,8 +13,8 @@
 //    Lane (i, g) of a tile takes the 16-byte pieces at channels 16j+4g of
 //    row i of its A (Q^r) and B (K^r) operands -- the same channels on both
 //    sides -- straight from memory with buffer loads (pieces past C read as
-//    zero), up to 256 channels in flight at once, multiplied in four
-//    independent accumulation chains. The scaled logits go to LDS.
+//    zero), 64 channels per batch with the next batch in flight. The scaled
+//    logits go to LDS.
 //  * R > 64 (route_wide_kernel): one workgroup per 4 query rows, one wave per
 //    64 candidates; each lane streams its own candidate's K^r row from L2
 //    into registers (double-buffered 32-channel batches) and reads the 4 Q^r
@@ -82,40 +82,41 @@ __host__ __device__ inline size_t route_lds(int R) {
 // One 16 x 16 logit tile: rows r0.., columns 16ct.. of (Q^r K^r^T) * scale,
 // lane (col, grp) returning rows 4grp..4grp+3 at column col. get(row, c)
 // returns the 16-byte piece of channels c..c+3 of a Q^r (a) / K^r (b) row
-// (rows clamped to R-1, pieces past C zero). Channels are loaded NB x 64 at
-// a time (every load of a group in flight; pieces past C read as zero and
-// add nothing) and multiplied in four independent fp32 MFMA chains (channel
-// offsets 16j + 4grp, j = 0..3), added at the end; the order is fixed, so
-// the logits are reproducible bit for bit.
-template <int NB, typename GetA, typename GetB>
+// (rows clamped to R-1, pieces past C zero). The fp32 MFMA sequence is the
+// same wherever the operands come from, so the logits are too.
+template <typename GetA, typename GetB>
 __device__ __forceinline__ f32x4 logit_tile(int col, int grp, int C, GetA geta, GetB getb) {
-  constexpr int kGroup = NB;  // 64-channel batches per load group
-  f32x4 acc[4];
+  uint4 a[4], b[4], an[4], bn[4];
+  auto fetch = [&](int c0, uint4* aa, uint4* bb) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int g0 = 0; g0 < C; g0 += kGroup * kChunk) {
-    uint4 a[kGroup][4], b[kGroup][4];
-#pragma unroll
-    for (int bt = 0; bt < kGroup; ++bt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = g0 + bt * kChunk + 16 * j + 4 * grp;
-        a[bt][j] = geta(c);
-        b[bt][j] = getb(c);
-      }
-    __builtin_amdgcn_sched_barrier(0);  // every load of the group before the first product
-#pragma unroll
-    for (int bt = 0; bt < kGroup; ++bt) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[bt][j].x), __uint_as_float(b[bt][j].x), acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[bt][j].y), __uint_as_float(b[bt][j].y), acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[bt][j].z), __uint_as_float(b[bt][j].z), acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[bt][j].w), __uint_as_float(b[bt][j].w), acc[j], 0, 0, 0);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int c = c0 + 16 * j + 4 * grp;
+      aa[j] = geta(c);
+      bb[j] = getb(c);
     }
+  };
+  auto mfma4 = [&](f32x4 acc) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].x), __uint_as_float(b[j].x), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].y), __uint_as_float(b[j].y), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].z), __uint_as_float(b[j].z), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].w), __uint_as_float(b[j].w), acc, 0, 0, 0);
+    }
+    return acc;
+  };
+  // the next batch is always in flight while one is multiplied (the last
+  // batch is peeled off, so no branch guards the loads)
+  fetch(0, a, b);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int c0 = 0;
+  for (; c0 + kChunk < C; c0 += kChunk) {
+    fetch(c0 + kChunk, an, bn);
+    acc = mfma4(acc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { a[j] = an[j]; b[j] = bn[j]; }
   }
-  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  return mfma4(acc);
 }
 
 // Top-k of rows i0, i0 + step, ... (four at a time) of the logit block
@@ -164,7 +165,6 @@ __device__ __forceinline__ void rank_rows(const float* logit, int RP, int R, int
   }
 }
 
-template <int NB>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ qr,
                                                     const float* __restrict__ kr, int R, int C,
                                                     int topk, float scale,
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ qr
   // ---- affinities: wave ct computes column tile ct
   for (int ct = wave; ct < CT; ct += waves) {
     const uint32_t krow = (uint32_t)min(16 * ct + col, R - 1) * C * 4;
-    const f32x4 acc = logit_tile<NB>(
+    const f32x4 acc = logit_tile(
         col, grp, C, [&](int c) { return ld16(qb, c < C ? qrow + 4 * c : kOut); },
         [&](int c) { return ld16(kb, c < C ? krow + 4 * c : kOut); });
     // lane (col, grp) holds rows 4grp..4grp+3 of the tile at column col
@@ -205,15 +205,7 @@ hipError_t launch_small(const float* qr, const float* kr, int N, int R, int C, i
                         int32_t* route, hipStream_t st) {
   const float scale = (float)(1.0 / __builtin_sqrt((double)C));
   const unsigned blocks = (unsigned)(N * col_tiles(R));
-  // 64-channel batches per load group: all of C up to 256 channels
-  const int nb = (C + kChunk - 1) / kChunk;
-#define BRA_ROUTE(NB) \
-  launch(route_kernel<NB>, dim3(blocks), dim3(64 * col_tiles(R)), route_lds(R), st, qr, kr, R, C, topk, scale, route)
-  if (nb <= 1) BRA_ROUTE(1);
-  else if (nb <= 2) BRA_ROUTE(2);
-  else if (nb <= 3) BRA_ROUTE(3);
-  else BRA_ROUTE(4);
-#undef BRA_ROUTE
+  launch(route_kernel, dim3(blocks), dim3(64 * col_tiles(R)), route_lds(R), st, qr, kr, R, C, topk, scale, route);
   return hipGetLastError();
 }
 
