@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -42,6 +43,20 @@ hipError_t launch_lce_pack(const void* w, int C, uint32_t* wpk, hipStream_t st);
 ProfEvents& prof_events() {
   thread_local ProfEvents pe;
   return pe;
+}
+
+int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+  if (dev < 64 && cus > 0) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 }  // namespace bra
 

@@ -26,6 +26,8 @@
 // dims into 16 channel pairs -- and adds the LCE of its pair and stores it.
 #include "bra_internal.h"
 
+#include <type_traits>
+
 namespace bra {
 namespace {
 
@@ -112,11 +114,15 @@ struct ImgLds {
 // head's LCE weights as dot2 operands [16 pairs][5 rows][8 dwords]; for 4x4
 // regions each wave's hand-over of the attention output [16 queries][36]
 // fp32; a sink for unused stores.
+// Bordered-V row pitch in pixels: W + 4, or for 4x4 regions a fixed 32 (the
+// LCE window then sits at constant offsets from one address).
+constexpr int kVRow4 = 32;
+__host__ __device__ constexpr int vrow(int RS, int W) { return RS == 4 ? kVRow4 : W + 4; }
 __host__ __device__ inline ImgLds img_lds(int RS, int NW, int H, int W, int R, int topk) {
   ImgLds l;
   size_t o = 0;
   l.k = o; o += (size_t)H * W * 64;
-  l.v = o; o += (size_t)(H + 4) * (W + 4) * 64;
+  l.v = o; o += (size_t)(H + 4) * vrow(RS, W) * 64;
   l.rk = o; o += align16((size_t)R * route_stride(topk, RS * RS) * 2);
   l.rv = o; o += align16((size_t)R * route_stride(topk, RS * RS) * 2);
   l.w = o; o += 16 * 5 * 32;
@@ -126,9 +132,9 @@ __host__ __device__ inline ImgLds img_lds(int RS, int NW, int H, int W, int R, i
   return l;
 }
 
-template <int RS, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_image_kernel(ImageArgs a) {
-  constexpr int RH = RS, RW = RS, T = RS * RS;  // RS x RS regions
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void attn_image2_kernel(ImageArgs a) {
+  constexpr int RS = 2, RH = RS, RW = RS, T = RS * RS;  // 2x2 regions
   constexpr int nthreads = 64 * NW;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int H = a.H, W = a.W, C = a.C, S = a.S, R = S * S, topk = a.topk;
@@ -228,7 +234,6 @@ __global__ __launch_bounds__(64 * NW) void attn_image_kernel(ImageArgs a) {
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
-  if constexpr (RS == 2) {
   // ---- per-lane constants ---------------------------------------------------
   const int tq = col & 3;    // key tile of this score column
   const int qt = col >> 2;   // query (token of the region) of this score column
@@ -357,12 +362,186 @@ __global__ __launch_bounds__(64 * NW) void attn_image_kernel(ImageArgs a) {
     const uint32_t packed = float_to_bf16_bits(at0 + (acc0 + acc2)) | (float_to_bf16_bits(at1 + (acc1 + acc3)) << 16);
     *reinterpret_cast<uint32_t*>(a.out + img + (size_t)(y * W + x) * C + 32 * h + 2 * cp) = packed;
   }
-  } else {
-  // ---- 4x4 regions: a score tile is one routed region (16 keys) against the
-  // region's 16 queries (lane column = query); the output goes through LDS to
-  // the LCE layout, a lane per (region column, channel pair) walking a
-  // vertical window of the bordered V
-  static_assert(RS == 4, "2x2 or 4x4 regions");
+}
+
+// ---- 4x4 regions: persistent workgroups ------------------------------------
+// One workgroup per CU walks (image, head) units with sixteen waves. While
+// the waves work on one unit's regions, every lane holds seven 16-byte pieces
+// of the next unit's K, V and LCE weights (and one route entry) in registers,
+// loaded right after the lane's own query rows; at the end of the unit, between
+// two barriers, they are written to LDS. A unit's staging thus overlaps the
+// previous unit's arithmetic instead of following it. (Loads complete in issue
+// order as far as the wait counter goes, so the query rows of all of a wave's
+// regions are requested first: no query wait ever waits for the prefetch.)
+//
+// A score tile is one routed region (16 keys) against the region's 16
+// queries (lane column = query); the output goes through LDS to the LCE
+// layout, a lane per (region column, channel pair) walking a vertical window
+// of the bordered V.
+constexpr int kNW4 = 16;                 // waves
+constexpr int kThreads4 = 64 * kNW4;
+constexpr int kPF = 7;                   // prefetch pieces per lane: 8*H*W + 160 <= 7*1024
+constexpr int kWPieces = 16 * 5 * 8 / 4; // a head's LCE dot2 operands in 16-byte pieces
+
+// LDS-only workgroup barrier: orders LDS accesses across it without waiting
+// for global loads and stores still in flight
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
+  constexpr int RH = 4, RW = 4, T = 16;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int H = a.H, W = a.W, C = a.C, S = a.S, R = S * S, topk = a.topk;
+  const int L = topk * T, HW = H * W, RSTR = route_stride(topk, T);
+  constexpr int WP = kVRow4;  // bordered-V row pitch (pixels)
+  const ImgLds lay = img_lds(4, kNW4, H, W, R, topk);
+  uint16_t* kh = reinterpret_cast<uint16_t*>(smem + lay.k);
+  uint16_t* vh = reinterpret_cast<uint16_t*>(smem + lay.v);
+  uint16_t* rk = reinterpret_cast<uint16_t*>(smem + lay.rk);
+  uint16_t* rv = reinterpret_cast<uint16_t*>(smem + lay.rv);
+  const uint32_t* wl = reinterpret_cast<const uint32_t*>(smem + lay.w);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int units = a.N * a.heads, G = (int)gridDim.x;
+  const uint32_t pixb = (uint32_t)C * 2;  // bytes per pixel
+  const uint32_t img_bytes = (uint32_t)HW * C * 2;
+  const int nroute = R * RSTR;
+  const float inv_w = 1.0f / (float)W;
+
+  // ---- the next unit's K, V, weights and routes ------------------------------
+  // piece i = tid + 1024j: [0, 4HW) K, [4HW, 8HW) V (pixel, 16-byte chunk),
+  // then the head's LCE operands; route slot tid
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 pf[kPF];
+  uint32_t rq = 0;
+  auto route_off = [&](int i) {  // byte offset of route slot i's entry, or kOut
+    const int r = i / RSTR, p = i - r * RSTR;
+    return i < nroute && p < topk ? (uint32_t)(r * topk + p) * 4 : kOut;
+  };
+  // The lane's piece indices are rederived from an opaque copy of its thread
+  // index in each call: hoisted out of the unit loop, the addresses would
+  // hold dozens of registers next to the prefetched data.
+  auto opaque_tid = [&]() {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    return t;
+  };
+  // (real == false: the same loads, all of one valid address and discarded,
+  // so that every path through the unit loop issues the same loads)
+  auto prefetch = [&](int u, bool real) {
+    const int tid = opaque_tid();
+    const int n = u / a.heads, h = u - n * a.heads;
+    const size_t img = (size_t)n * HW * C;
+    const char* kp = reinterpret_cast<const char*>(a.k + img) + h * 64;
+    const char* vp = reinterpret_cast<const char*>(a.v + img) + h * 64;
+    const char* wp = reinterpret_cast<const char*>(a.wpk + lce_pair_ops_offset(C)) + (size_t)h * kWPieces * 16;
+    int keep = real ? 1 : 0;  // a lane value: selects below, not a branch
+    asm volatile("" : "+v"(keep));
+#pragma unroll
+    for (int j = 0; j < kPF; ++j) {
+      const int i = tid + kThreads4 * j;
+      const bool isk = i < 4 * HW, isv = !isk && i < 8 * HW;
+      const int i2 = isk ? i : i - 4 * HW;
+      const size_t po = (size_t)(i2 >> 2) * pixb + (size_t)(i2 & 3) * 16;
+      const int iw = i - 8 * HW;
+      // pieces past the operands re-read the first K piece (never written)
+      const char* src = !keep ? kp : isk ? kp + po : isv ? vp + po : iw < kWPieces ? wp + (size_t)iw * 16 : kp;
+      pf[j] = *reinterpret_cast<const u32x4*>(src);
+    }
+    const Rsrc rrs = rsrc(a.route + (size_t)n * R * topk, (uint32_t)(R * topk) * 4);
+    rq = __builtin_amdgcn_raw_buffer_load_b32(rrs, keep ? route_off(tid) : kOut, 0, 0);
+  };
+  auto route_put = [&](int i, int rr) {  // slot i -> offsets of the routed region's first K and V token
+    const int js = rr / S, is = rr - js * S;
+    rk[i] = (uint16_t)((js * RH * W + is * RW) * 64);
+    rv[i] = (uint16_t)(((js * RH + 2) * WP + is * RW + 2) * 64);
+  };
+  auto commit = [&](int u) {
+    const int tid = opaque_tid();
+#pragma unroll
+    for (int j = 0; j < kPF; ++j) {
+      const int i = tid + kThreads4 * j;
+      const bool isk = i < 4 * HW, isv = !isk && i < 8 * HW;
+      const int i2 = isk ? i : i - 4 * HW;
+      const int pix = i2 >> 2, c = i2 & 3;
+      const int y = (int)(((float)pix + 0.5f) * inv_w), x = pix - y * W;  // exact: pix < 2^12
+      const uint32_t ko = (uint32_t)lay.k + (uint32_t)(4 * pix + (c ^ ((((x >> 1) & 1) << 1) | (y & 1)))) * 16;
+      const uint32_t vo = (uint32_t)lay.v + (uint32_t)(4 * ((y + 2) * WP + x + 2) + (c ^ (3 * (y & 1)))) * 16;
+      // weights: global [pair][row][2 pieces] -> LDS [piece][row][pair] (reads conflict-free)
+      const int iw = i - 8 * HW, wpair = iw / 10, wrow = (iw - wpair * 10) >> 1;
+      const uint32_t wo = (uint32_t)lay.w + (uint32_t)(((iw & 1) * 5 + wrow) * 16 + wpair) * 16;
+      if (i < 8 * HW + kWPieces) *reinterpret_cast<u32x4*>(smem + (isk ? ko : isv ? vo : wo)) = pf[j];
+    }
+    if (tid < nroute) route_put(tid, (int)rq);
+    // retire the prefetch registers on every path (the writes above are
+    // guarded; left pending on the path that skips them, they would make the
+    // next unit's first load wait on its own query rows)
+#pragma unroll
+    for (int j = 0; j < kPF; ++j) asm volatile("" : "+v"(pf[j]));
+    asm volatile("" : "+v"(rq));
+    if (nroute > kThreads4) {  // large route tables: the rest read here
+      const int n = u / a.heads;
+      const Rsrc rrs = rsrc(a.route + (size_t)n * R * topk, (uint32_t)(R * topk) * 4);
+      for (int i = tid + kThreads4; i < nroute; i += kThreads4)
+        route_put(i, (int)__builtin_amdgcn_raw_buffer_load_b32(rrs, route_off(i), 0, 0));
+    }
+  };
+
+  // the V border (two pixels around the image) stays zero for every unit
+  {
+    const int top = 2 * 2 * WP * 4;  // rows 0, 1, H + 2, H + 3
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = tid; i < top + H * 16; i += kThreads4) {
+      int py, px;
+      if (i < top) {
+        const int rr = i / (WP * 4);
+        py = rr < 2 ? rr : H + rr;
+        px = (i - rr * WP * 4) >> 2;
+      } else {
+        const int i2 = i - top, k = (i2 >> 2) & 3;
+        py = 2 + (i2 >> 4);
+        px = k < 2 ? k : W + k;
+      }
+      *reinterpret_cast<uint4*>(vh + (size_t)(4 * (py * WP + px) + (i & 3)) * 8) = z4;
+    }
+  }
+  // ---- the query rows and LCE bias of a unit --------------------------------
+  // A wave takes regions first, first + 16, ... (at most four: R <= 64); the
+  // start rotates with the unit so the waves that take an extra region change.
+  // The loads are issued a unit ahead, before that unit's staging is written.
+  const int pp = lane & 15, xc = lane >> 4;  // LCE item: channel pair, region column
+  bf16x8 q0, q1, q2, q3;
+  uint32_t bias2;
+  auto qrows = [&](int vb, int it) {
+    const int u = xcd_unit(vb, units);
+    const int n = u / a.heads, h = u - n * a.heads;
+    const Rsrc qb = rsrc(a.q + (size_t)n * HW * C, img_bytes);
+    const int first = (wave + kNW4 - it % kNW4) % kNW4;
+    auto qload = [&](int r) {
+      const int js = r / S, is = r - js * S;
+      const int y = js * RH + (col >> 2), x = is * RW + (col & 3);
+      const uint32_t off = r < R ? (uint32_t)(y * W + x) * pixb + (uint32_t)h * 64 + (uint32_t)grp * 16 : kOut;
+      return __builtin_bit_cast(bf16x8, ld16(qb, off));
+    };
+    q0 = qload(first);
+    q1 = qload(first + kNW4);
+    q2 = qload(first + 2 * kNW4);
+    q3 = qload(first + 3 * kNW4);
+    bias2 = a.b ? reinterpret_cast<const uint32_t*>(a.b)[h * 16 + pp] : 0u;
+  };
+
+  prefetch(xcd_unit((int)blockIdx.x, units), true);
+  qrows((int)blockIdx.x, 0);
+  asm volatile("" ::: "memory");
+  commit(xcd_unit((int)blockIdx.x, units));
+  lds_barrier();  // the first unit staged
+
+  // ---- per-lane constants -----------------------------------------------------
   // K row of this lane: token (col / 4, col % 4) of a routed region (whose
   // origin is a multiple of 4, so its swizzle depends on col only)
   const int f = ((col >> 2) & 1) | (((col & 3) >> 1) << 1);
@@ -373,147 +552,174 @@ __global__ __launch_bounds__(64 * NW) void attn_image_kernel(ImageArgs a) {
   const uint32_t vt = (uint32_t)lay.v + (uint32_t)(grp * WP + (col >> 2)) * 64;
   const uint32_t offV0 = vt + 16u * (uint32_t)((c4 >> 1) ^ (3 * vpar)) + 8u * (uint32_t)(c4 & 1);
   const uint32_t offV1 = vt + 16u * (uint32_t)((2 + (c4 >> 1)) ^ (3 * vpar)) + 8u * (uint32_t)(c4 & 1);
-  // LCE item of this lane: channel pair pp of the head, region column xc
-  const int pp = lane & 15, xc = lane >> 4;
-  const uint32_t bias2 = a.b ? reinterpret_cast<const uint32_t*>(a.b)[h * 16 + pp] : 0u;
   float* xw = reinterpret_cast<float*>(smem + lay.x) + wave * (16 * 36);  // this wave's hand-over
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
-  auto qload = [&](int r) {
-    const int js = r / S, is = r - js * S;
-    const int y = js * RH + (col >> 2), x = is * RW + (col & 3);
-    const uint32_t off = r < R ? (uint32_t)(y * W + x) * pixb + hoff + (uint32_t)grp * 16 : kOut;
-    return __builtin_bit_cast(bf16x8, ld16(qb, off));
-  };
-  bf16x8 bq_next = qload(wave_u);
-  __syncthreads();  // K, V, routes, weights staged
+  for (int it = 0, vb = (int)blockIdx.x; vb < units; ++it, vb += G) {
+    const int u = xcd_unit(vb, units);
+    const int n = u / a.heads, h = u - n * a.heads;
+    const Rsrc ob = rsrc(a.out + (size_t)n * HW * C, img_bytes);
+    const int first = (wave + kNW4 - it % kNW4) % kNW4;
+    const bool more = vb + G < units;
+    prefetch(more ? xcd_unit(vb + G, units) : u, more);
+    // Take delivery of the query rows and the bias right after the prefetch
+    // was issued: the wait covers just these loads, and the region loop holds
+    // no value still in flight (a loop that used one would have the compiler
+    // wait for every outstanding load, the prefetch too, before entering it).
+    asm volatile("" : "+v"(q0), "+v"(q1), "+v"(q2), "+v"(q3), "+v"(bias2));
 
-  uint4 wr0[5];
-  uint2 wr1[5];
-#pragma unroll
-  for (int ay = 0; ay < 5; ++ay) {
-    wr0[ay] = *reinterpret_cast<const uint4*>(wl + pp * 40 + 8 * ay);
-    wr1[ay] = *reinterpret_cast<const uint2*>(wl + pp * 40 + 8 * ay + 4);
-  }
+    for (int r = first; r < R; r += kNW4) {
+      const bf16x8 bq = q0;
+      q0 = q1;
+      q1 = q2;
+      q2 = q3;
+      const uint16_t* rkr = rk + r * RSTR;
+      const uint16_t* rvr = rv + r * RSTR;
 
-  for (int r = wave_u; r < R; r += NW) {
-    const bf16x8 bq = bq_next;
-    bq_next = qload(r + NW);
-    const uint16_t* rkr = rk + r * RSTR;
-    const uint16_t* rvr = rv + r * RSTR;
+      float m = -INFINITY;  // running max of the scaled (base-2) logits
+      f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0, ls = o0;
+      // one 64-key chunk (four routed regions); Ragged: the last, partly past L
+      auto chunk = [&](const int base, auto ragged) {
+        bf16x8 ak[4];
+        uint32_t va[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {  // tile t = route slot base / 16 + t
+          const int slot = (base >> 4) + t;
+          ak[t] = *reinterpret_cast<const bf16x8*>(smem + rkr[slot] + kt);
+          va[t] = rvr[slot];
+        }
+        auto vtr = [&](int t, uint32_t off) { return ld_tr(reinterpret_cast<const uint16_t*>(smem + va[t] + off)); };
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 sc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sc[t] = mfma(ak[t], bq, z);
+        if constexpr (decltype(ragged)::value) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (base + 16 * t + 4 * grp + e >= L) sc[t][e] = -INFINITY;
+        }
+        float cm = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) cm = max3(cm, max3(sc[t][0], sc[t][1], sc[t][2]), sc[t][3]);
+        cm = group_max(cm);                        // over the key rows
+        const float mn = fmaxf(m, cm * a.qscale);  // qscale > 0 commutes with max
+        if (base > 0) {                            // rescale what earlier chunks summed
+          const float corr = __builtin_amdgcn_exp2f(m - mn);
+          o0 *= corr;
+          o1 *= corr;
+          ls *= corr;
+        }
+        m = mn;
+        bf16x4 pb[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          f32x4 pv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[t][e], a.qscale, -mn));
+          pb[t] = to_bf16x4(pv);
+        }
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          // k slots: keys 4g..4g+3 of tiles 2bb and 2bb+1
+          const bf16x8 pt = cat(pb[2 * bb], pb[2 * bb + 1]);
+          o0 = mfma(cat(vtr(2 * bb, offV0), vtr(2 * bb + 1, offV0)), pt, o0);
+          o1 = mfma(cat(vtr(2 * bb, offV1), vtr(2 * bb + 1, offV1)), pt, o1);
+          ls = mfma(ones, pt, ls);  // every row of ones x P^T is the row sum of P
+        }
+      };
+      int base = 0;
+      for (; base + 64 <= L; base += 64) chunk(base, std::false_type{});
+      if (base < L) chunk(base, std::true_type{});  // a separate path: whole chunks select nothing
+      // hand the output of query col (dims 4grp.., 16 + 4grp..) to the LCE layout
+      const float inv = __builtin_amdgcn_rcpf(ls[0]);
+      *reinterpret_cast<f32x4*>(xw + col * 36 + 4 * grp) = o0 * inv;
+      *reinterpret_cast<f32x4*>(xw + col * 36 + 16 + 4 * grp) = o1 * inv;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float2 at[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) at[i] = *reinterpret_cast<const float2*>(xw + (4 * i + xc) * 36 + 2 * pp);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();  // read before the next region's hand-over
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    float m = -INFINITY;  // running max of the scaled (base-2) logits
-    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0, ls = o0;
-    for (int base = 0; base < L; base += 64) {
-      bf16x8 ak[4];
-      uint32_t va[4];
+      // LCE of column xc, rows 0..3 of the region, channel pair pp: window rows
+      // wr = 0..7 are bordered rows 4js + wr (parity wr & 1), columns 4is + xc ..;
+      // kernel row ay's dot2 operands for the pair come from LDS
+      uint4 wr0[5];
+      uint2 wr1[5];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {  // tile t = route slot base / 16 + t
-        const int slot = (base >> 4) + t;
-        ak[t] = *reinterpret_cast<const bf16x8*>(smem + rkr[slot] + kt);
-        va[t] = rvr[slot];
+      for (int ay = 0; ay < 5; ++ay) {
+        wr0[ay] = *reinterpret_cast<const uint4*>(wl + (ay * 16 + pp) * 4);
+        wr1[ay] = *reinterpret_cast<const uint2*>(wl + ((5 + ay) * 16 + pp) * 4);
       }
-      auto vtr = [&](int t, uint32_t off) { return ld_tr(reinterpret_cast<const uint16_t*>(smem + va[t] + off)); };
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      f32x4 sc[4];
+      const int js = r / S, is = r - js * S;
+      float acc0[4], acc1[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) sc[t] = mfma(ak[t], bq, z);
-      if (base + 64 > L) {  // ragged last chunk
+      for (int i = 0; i < 4; ++i) { acc0[i] = bf16_lo(bias2); acc1[i] = bf16_hi(bias2); }
+      const uint32_t* vw = reinterpret_cast<const uint32_t*>(vh) + (size_t)((4 * js) * WP + 4 * is + xc) * 16;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+      for (int wr = 0; wr < 8; ++wr) {
+        const uint32_t* vr = vw + wr * WP * 16 + (pp ^ (12 * (wr & 1)));
+        const uint32_t p0 = vr[0], p1 = vr[16], p2 = vr[32], p3 = vr[48], p4 = vr[64];
+        const uint32_t h01c = __builtin_amdgcn_perm(p1, p0, 0x05040100u), h01d = __builtin_amdgcn_perm(p1, p0, 0x07060302u);
+        const uint32_t h23c = __builtin_amdgcn_perm(p3, p2, 0x05040100u), h23d = __builtin_amdgcn_perm(p3, p2, 0x07060302u);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (base + 16 * t + 4 * grp + e >= L) sc[t][e] = -INFINITY;
-      }
-      float cm = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) cm = max3(cm, max3(sc[t][0], sc[t][1], sc[t][2]), sc[t][3]);
-      cm = group_max(cm);                        // over the key rows
-      const float mn = fmaxf(m, cm * a.qscale);  // qscale > 0 commutes with max
-      if (base > 0) {                            // rescale what earlier chunks summed
-        const float corr = __builtin_amdgcn_exp2f(m - mn);
-        o0 *= corr;
-        o1 *= corr;
-        ls *= corr;
-      }
-      m = mn;
-      bf16x4 pb[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        f32x4 pv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[t][e], a.qscale, -mn));
-        pb[t] = to_bf16x4(pv);
-      }
-#pragma unroll
-      for (int bb = 0; bb < 2; ++bb) {
-        // k slots: keys 4g..4g+3 of tiles 2bb and 2bb+1
-        const bf16x8 pt = cat(pb[2 * bb], pb[2 * bb + 1]);
-        o0 = mfma(cat(vtr(2 * bb, offV0), vtr(2 * bb + 1, offV0)), pt, o0);
-        o1 = mfma(cat(vtr(2 * bb, offV1), vtr(2 * bb + 1, offV1)), pt, o1);
-        ls = mfma(ones, pt, ls);  // every row of ones x P^T is the row sum of P
-      }
-    }
-    // hand the output of query col (dims 4grp.., 16 + 4grp..) to the LCE layout
-    const float inv = __builtin_amdgcn_rcpf(ls[0]);
-    *reinterpret_cast<f32x4*>(xw + col * 36 + 4 * grp) = o0 * inv;
-    *reinterpret_cast<f32x4*>(xw + col * 36 + 16 + 4 * grp) = o1 * inv;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float2 at[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) at[i] = *reinterpret_cast<const float2*>(xw + (4 * i + xc) * 36 + 2 * pp);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();  // read before the next region's hand-over
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // LCE of column xc, rows 0..3 of the region, channel pair pp: window rows
-    // wr = 0..7 are bordered rows 4js + wr (parity wr & 1), columns 4is + xc ..
-    const int js = r / S, is = r - js * S;
-    float acc0[4], acc1[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { acc0[i] = bf16_lo(bias2); acc1[i] = bf16_hi(bias2); }
-    const uint32_t* vw = reinterpret_cast<const uint32_t*>(vh) + (size_t)((4 * js) * WP + 4 * is + xc) * 16;
-#pragma unroll
-    for (int wr = 0; wr < 8; ++wr) {
-      const uint32_t* vr = vw + wr * WP * 16 + (pp ^ (12 * (wr & 1)));
-      const uint32_t p0 = vr[0], p1 = vr[16], p2 = vr[32], p3 = vr[48], p4 = vr[64];
-      const uint32_t h01c = __builtin_amdgcn_perm(p1, p0, 0x05040100u), h01d = __builtin_amdgcn_perm(p1, p0, 0x07060302u);
-      const uint32_t h23c = __builtin_amdgcn_perm(p3, p2, 0x05040100u), h23d = __builtin_amdgcn_perm(p3, p2, 0x07060302u);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ay = wr - i;
-        if (ay >= 0 && ay < 5) {
-          acc0[i] = dot2(h01c, wr0[ay].x, acc0[i]);
-          acc1[i] = dot2(h01d, wr0[ay].y, acc1[i]);
-          acc0[i] = dot2(h23c, wr0[ay].z, acc0[i]);
-          acc1[i] = dot2(h23d, wr0[ay].w, acc1[i]);
-          acc0[i] = dot2(p4, wr1[ay].x, acc0[i]);
-          acc1[i] = dot2(p4, wr1[ay].y, acc1[i]);
+        for (int i = 0; i < 4; ++i) {
+          const int ay = wr - i;
+          if (ay >= 0 && ay < 5) {
+            acc0[i] = dot2(h01c, wr0[ay].x, acc0[i]);
+            acc1[i] = dot2(h01d, wr0[ay].y, acc1[i]);
+            acc0[i] = dot2(h23c, wr0[ay].z, acc0[i]);
+            acc1[i] = dot2(h23d, wr0[ay].w, acc1[i]);
+            acc0[i] = dot2(p4, wr1[ay].x, acc0[i]);
+            acc1[i] = dot2(p4, wr1[ay].y, acc1[i]);
+          }
         }
       }
-    }
+      const uint32_t oo = (uint32_t)((4 * js) * W + 4 * is + xc) * pixb + (uint32_t)h * 64 + (uint32_t)pp * 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t packed = float_to_bf16_bits(at[i].x + acc0[i]) | (float_to_bf16_bits(at[i].y + acc1[i]) << 16);
-      *reinterpret_cast<uint32_t*>(a.out + img + ((size_t)(4 * js + i) * W + 4 * is + xc) * C + 32 * h + 2 * pp) = packed;
+      for (int i = 0; i < 4; ++i) {
+        bf16x2 o2;
+        o2[0] = (__bf16)(at[i].x + acc0[i]);  // round to nearest even
+        o2[1] = (__bf16)(at[i].y + acc1[i]);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o2), ob, oo, (uint32_t)i * W * pixb, 0);
+      }
     }
-  }
+    if (more) {
+      qrows(vb + G, it + 1);
+      asm volatile("" ::: "memory");  // issued here, ahead of the staging below
+      lds_barrier();  // every wave is done with this unit's LDS
+      commit(xcd_unit(vb + G, units));
+      lds_barrier();  // the next unit staged
+    } else {
+      // the discarded loads of the last unit retired as well: no path around
+      // the loop leaves a prefetch register in flight
+#pragma unroll
+      for (int j = 0; j < kPF; ++j) asm volatile("" : "+v"(pf[j]));
+      asm volatile("" : "+v"(rq));
+    }
   }
 }
 
 }  // namespace
 
-// 2x2 regions: four waves, four workgroups per CU (the LDS budget); 4x4
-// regions: sixteen waves, one workgroup per CU
-template <int RS> constexpr int image_waves() { return RS == 2 ? 4 : 16; }
+// 2x2 regions: four waves, four workgroups per CU (the LDS budget)
+constexpr int kImage2Waves = 4;
 
 bool image_kernel_supports(const Shape& s) {
   if (s.hd != 32 || s.rh != s.rw || (s.rh != 2 && s.rh != 4)) return false;
   if ((long long)s.H * s.W * s.C >= (1ll << 30)) return false;    // 32-bit byte offsets in an image
   if ((long long)(s.H + 4) * (s.W + 4) * 64 > 65536) return false;  // 16-bit token offsets
-  if (s.rh == 2) return img_lds(2, image_waves<2>(), s.H, s.W, s.R, s.topk).total <= 40 * 1024;  // four per CU
-  return img_lds(4, image_waves<4>(), s.H, s.W, s.R, s.topk).total <= 160 * 1024;
+  if (s.rh == 2) return img_lds(2, kImage2Waves, s.H, s.W, s.R, s.topk).total <= 40 * 1024;  // four per CU
+  if (8 * s.H * s.W + kWPieces > kPF * kThreads4 || s.R > 4 * kNW4) return false;  // prefetch, regions per wave
+  if (s.W + 4 > kVRow4 || (long long)(s.H + 4) * kVRow4 * 64 > 65536) return false;  // row pitch, 16-bit offsets
+  return img_lds(4, kNW4, s.H, s.W, s.R, s.topk).total <= 160 * 1024;
 }
 
 hipError_t launch_attend_image(const void* q, const void* k, const void* v, const uint32_t* wpk,
@@ -524,13 +730,17 @@ hipError_t launch_attend_image(const void* q, const void* k, const void* v, cons
   a.wpk = wpk; a.b = (const uint16_t*)b; a.route = route; a.out = (uint16_t*)out;
   a.N = s.N; a.H = s.H; a.W = s.W; a.C = s.C; a.heads = s.heads; a.S = s.S; a.topk = s.topk;
   a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
-  const unsigned blocks = (unsigned)(s.N * s.heads);
+  const int units = s.N * s.heads;
   if (s.rh == 2) {
-    constexpr int nw = image_waves<2>();
-    launch(attn_image_kernel<2, nw>, dim3(blocks), dim3(64 * nw), img_lds(2, nw, s.H, s.W, s.R, s.topk).total, st, a);
+    launch(attn_image2_kernel<kImage2Waves>, dim3((unsigned)units), dim3(64 * kImage2Waves),
+           img_lds(2, kImage2Waves, s.H, s.W, s.R, s.topk).total, st, a);
   } else {
-    constexpr int nw = image_waves<4>();
-    launch(attn_image_kernel<4, nw>, dim3(blocks), dim3(64 * nw), img_lds(4, nw, s.H, s.W, s.R, s.topk).total, st, a);
+    // one persistent workgroup per CU (a multiple of 8, so a workgroup's
+    // units stay on its XCD), at most one per unit
+    int cus = device_cu_count();
+    cus = cus >= 8 ? cus / 8 * 8 : 8;
+    const int grid = units < cus ? units : cus;
+    launch(attn_image4_kernel, dim3((unsigned)grid), dim3(kThreads4), img_lds(4, kNW4, s.H, s.W, s.R, s.topk).total, st, a);
   }
   return hipGetLastError();
 }

@@ -18,6 +18,9 @@ struct ProfEvents {
 };
 ProfEvents& prof_events();  // per host thread
 
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
 // Every kernel of the library is launched through here. Errors are left for
 // the caller's hipGetLastError().
 template <typename... Args, typename F = void (*)(Args...)>
@@ -159,7 +162,12 @@ __device__ __forceinline__ float row_class_sum(float x) {
 //    (row*3+pair major, C minor) writes one dword of each parity.
 //  * then [tap][C/2] dwords (25*C/2): the weights of channels 2p and 2p+1
 //    for tap t (= 5*row + column) in one dword (low half: channel 2p).
-__host__ __device__ inline int lce_pack_items(int C) { return 15 * C + 25 * (C / 2); }
+//  * then [C/2 pairs][5 rows][8] dwords (20*C): the dot2 operands of channel
+//    pair p (channels c = 2p, d = 2p+1) for one kernel row, taps 0..4:
+//    (c0,c1) (d0,d1) (c2,c3) (d2,d3) (c4,0) (0,d4) 0 0.
+constexpr int kLcePairOps = 8;
+__host__ __device__ inline int lce_pack_items(int C) { return 15 * C + 25 * (C / 2) + 20 * C; }
+__host__ __device__ inline int lce_pair_ops_offset(int C) { return 30 * C + 25 * (C / 2); }
 __device__ __forceinline__ void pack_lce_item(const uint16_t* __restrict__ lw, int C, int e,
                                               uint32_t* __restrict__ wpk) {
   if (e < 15 * C) {
@@ -171,10 +179,27 @@ __device__ __forceinline__ void pack_lce_item(const uint16_t* __restrict__ lw, i
     const uint32_t tm = d0 > 0 ? (uint32_t)wr[d0 - 1] : 0u;
     wpk[rest * C + c] = t0 | (t1 << 16);
     wpk[(15 + rest) * C + c] = tm | (t0 << 16);
-  } else {
+  } else if (e < 15 * C + 25 * (C / 2)) {
     const int e2 = e - 15 * C;
     const int t = e2 / (C / 2), p = e2 - t * (C / 2);
     wpk[30 * C + e2] = (uint32_t)lw[(size_t)(2 * p) * 25 + t] | ((uint32_t)lw[(size_t)(2 * p + 1) * 25 + t] << 16);
+  } else {
+    const int e3 = e - 15 * C - 25 * (C / 2);
+    const int k = e3 % kLcePairOps, pr = e3 / kLcePairOps;  // pr = 5p + row
+    const int p = pr / 5, ay = pr - 5 * p;
+    const uint16_t* wc = lw + (size_t)(2 * p) * 25 + ay * 5;  // channel 2p, row ay
+    const uint16_t* wd = wc + 25;                              // channel 2p+1
+    uint32_t lo = 0u, hi = 0u;
+    switch (k) {
+      case 0: lo = wc[0]; hi = wc[1]; break;
+      case 1: lo = wd[0]; hi = wd[1]; break;
+      case 2: lo = wc[2]; hi = wc[3]; break;
+      case 3: lo = wd[2]; hi = wd[3]; break;
+      case 4: lo = wc[4]; break;
+      case 5: hi = wd[4]; break;
+      default: break;
+    }
+    wpk[lce_pair_ops_offset(C) + e3] = lo | (hi << 16);
   }
 }
 
