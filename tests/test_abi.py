@@ -51,8 +51,8 @@ def test_version_and_strings(lib):
 
 def test_workspace_bytes(lib):
     # region means of q and k, then the packed LCE weights (30*C + 25*C/2 +
-    # 20*C dwords)
-    assert lib.bra_workspace_bytes(128, 128, 7) == 2 * 128 * 49 * 128 * 4 + 250 * 128
+    # 80*C dwords)
+    assert lib.bra_workspace_bytes(128, 128, 7) == 2 * 128 * 49 * 128 * 4 + 490 * 128
     assert lib.bra_workspace_bytes(0, 128, 7) == 0
 
 

@@ -125,7 +125,7 @@ __host__ __device__ inline ImgLds img_lds(int RS, int NW, int H, int W, int R, i
   l.v = o; o += (size_t)(H + 4) * vrow(RS, W) * 64;
   l.rk = o; o += align16((size_t)R * route_stride(topk, RS * RS) * 2);
   l.rv = o; o += align16((size_t)R * route_stride(topk, RS * RS) * 2);
-  l.w = o; o += 16 * 5 * 32;
+  l.w = o; o += RS == 4 ? (size_t)kLceToepDwords * 4 : 16 * 5 * 32;  // Toeplitz LCE blocks / dot2 operands
   l.x = o; o += RS == 4 ? (size_t)NW * 16 * 36 * 4 : 0;
   l.sink = o; o += 16;
   l.total = o;
@@ -375,13 +375,28 @@ __global__ __launch_bounds__(64 * NW) void attn_image2_kernel(ImageArgs a) {
 // regions are requested first: no query wait ever waits for the prefetch.)
 //
 // A score tile is one routed region (16 keys) against the region's 16
-// queries (lane column = query); the output goes through LDS to the LCE
-// layout, a lane per (region column, channel pair) walking a vertical window
-// of the bordered V.
-constexpr int kNW4 = 16;                 // waves
+// queries (lane column = query); P.V reads V^T straight from LDS, where the
+// bordered V is stored as horizontal pixel pairs per channel. The LCE runs on
+// the matrix cores: a 4x4x4 product with 16 independent blocks gives each
+// block one channel's 4x4 output tile, each window row adding its 8 pixels
+// (two chunks of 4) times a Toeplitz block of that row's 5 weights; the
+// attention output, handed over through LDS, is the accumulator's start.
+constexpr int kNW4 = 16;                       // waves
 constexpr int kThreads4 = 64 * kNW4;
-constexpr int kPF = 7;                   // prefetch pieces per lane: 8*H*W + 160 <= 7*1024
-constexpr int kWPieces = 16 * 5 * 8 / 4; // a head's LCE dot2 operands in 16-byte pieces
+constexpr int kPF = 7;                         // prefetch pieces per lane
+constexpr int kWPieces = kLceToepDwords / 4;   // a head's Toeplitz LCE blocks in 16-byte pieces
+constexpr int kVPitch4 = kVRow4 / 2 * 128;     // bytes per bordered-V row: 16 pixel pairs x 32 channels
+
+// Bordered V row Y, pixel pair P, channel c: the dword (pixel 2P, pixel 2P+1)
+// at byte (Y * 16 + P) * 128 + 4 * (c ^ vsw(Y)). The swizzle flips channel
+// bits 4 and 3 by row: the two rows of a P.V read's 32-lane pass (16 dims
+// each) and the four rows of a window read's 16-lane pass (8 dwords each)
+// fall on different banks.
+__host__ __device__ constexpr int vsw(int Y) { return 16 * (Y & 1) + 8 * ((Y >> 1) & 1); }
+
+__device__ __forceinline__ f32x4 mfma4(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, b, c, 0, 0, 0);
+}
 
 // LDS-only workgroup barrier: orders LDS accesses across it without waiting
 // for global loads and stores still in flight
@@ -391,18 +406,18 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// FK: whole K/V slot pairs of the prefetch (4 H W / 1024, rounded down)
+template <int FK>
 __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
   constexpr int RH = 4, RW = 4, T = 16;
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int H = a.H, W = a.W, C = a.C, S = a.S, R = S * S, topk = a.topk;
   const int L = topk * T, HW = H * W, RSTR = route_stride(topk, T);
-  constexpr int WP = kVRow4;  // bordered-V row pitch (pixels)
   const ImgLds lay = img_lds(4, kNW4, H, W, R, topk);
-  uint16_t* kh = reinterpret_cast<uint16_t*>(smem + lay.k);
-  uint16_t* vh = reinterpret_cast<uint16_t*>(smem + lay.v);
   uint16_t* rk = reinterpret_cast<uint16_t*>(smem + lay.rk);
   uint16_t* rv = reinterpret_cast<uint16_t*>(smem + lay.rv);
-  const uint32_t* wl = reinterpret_cast<const uint32_t*>(smem + lay.w);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -414,11 +429,16 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
   const float inv_w = 1.0f / (float)W;
 
   // ---- the next unit's K, V, weights and routes ------------------------------
-  // piece i = tid + 1024j: [0, 4HW) K, [4HW, 8HW) V (pixel, 16-byte chunk),
-  // then the head's LCE operands; route slot tid
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  // Slots 2jj and 2jj+1 (jj < FK) hold K and V of pixel tid / 4 + 256jj, chunk
+  // tid % 4: whole slots of one tensor at a fixed pixel stride, so a load is a
+  // per-lane base plus a uniform offset. The remaining slots are mixed: the
+  // last remK K pieces, the same V pieces, then the head's LCE blocks. Route
+  // slot tid rides along. (A V pixel's horizontal partner is always in lane
+  // tid ^ 4 of the same slot: pixel pairs are even-aligned, remK is a multiple
+  // of 8.)
   u32x4 pf[kPF];
   uint32_t rq = 0;
+  const int remK = 4 * HW - FK * kThreads4;
   auto route_off = [&](int i) {  // byte offset of route slot i's entry, or kOut
     const int r = i / RSTR, p = i - r * RSTR;
     return i < nroute && p < topk ? (uint32_t)(r * topk + p) * 4 : kOut;
@@ -431,51 +451,92 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
     asm volatile("" : "+v"(t));
     return t;
   };
-  // (real == false: the same loads, all of one valid address and discarded,
-  // so that every path through the unit loop issues the same loads)
+  // (real == false: the same loads, past the buffers or all of one address,
+  // discarded: every path issues the same loads)
   auto prefetch = [&](int u, bool real) {
     const int tid = opaque_tid();
     const int n = u / a.heads, h = u - n * a.heads;
     const size_t img = (size_t)n * HW * C;
-    const char* kp = reinterpret_cast<const char*>(a.k + img) + h * 64;
-    const char* vp = reinterpret_cast<const char*>(a.v + img) + h * 64;
-    const char* wp = reinterpret_cast<const char*>(a.wpk + lce_pair_ops_offset(C)) + (size_t)h * kWPieces * 16;
-    int keep = real ? 1 : 0;  // a lane value: selects below, not a branch
+    const Rsrc kb = rsrc(a.k + img, img_bytes), vb = rsrc(a.v + img, img_bytes);
+    const char* kp = reinterpret_cast<const char*>(a.k + img);
+    const char* vp = reinterpret_cast<const char*>(a.v + img);
+    const char* wp = reinterpret_cast<const char*>(a.wpk + lce_toep_offset(C) + (size_t)h * kLceToepDwords);
+    int keep = real ? 1 : 0;  // a lane value: the selects below stay selects, not branches
     asm volatile("" : "+v"(keep));
+    const uint32_t lb = keep ? (uint32_t)(tid >> 2) * pixb + (uint32_t)(tid & 3) * 16 : kOut;
 #pragma unroll
     for (int j = 0; j < kPF; ++j) {
-      const int i = tid + kThreads4 * j;
-      const bool isk = i < 4 * HW, isv = !isk && i < 8 * HW;
-      const int i2 = isk ? i : i - 4 * HW;
-      const size_t po = (size_t)(i2 >> 2) * pixb + (size_t)(i2 & 3) * 16;
-      const int iw = i - 8 * HW;
-      // pieces past the operands re-read the first K piece (never written)
-      const char* src = !keep ? kp : isk ? kp + po : isv ? vp + po : iw < kWPieces ? wp + (size_t)iw * 16 : kp;
-      pf[j] = *reinterpret_cast<const u32x4*>(src);
+      if (j < 2 * FK) {
+        const uint32_t so = (uint32_t)h * 64 + (uint32_t)(j >> 1) * 256 * pixb;
+        pf[j] = __builtin_bit_cast(u32x4, ld16s((j & 1) ? vb : kb, lb, so));
+      } else {
+        const int m = tid + kThreads4 * (j - 2 * FK);
+        const bool isk = m < remK, isv = !isk && m < 2 * remK;
+        const int i2 = FK * kThreads4 + (isk ? m : m - remK);  // piece of K or V
+        const size_t po = (size_t)(i2 >> 2) * pixb + (size_t)h * 64 + (size_t)(i2 & 3) * 16;
+        const int iw = m - 2 * remK;
+        // one load from a per-lane address (a tensor per lane); pieces past
+        // the operands, and every piece of a discarded prefetch, re-read the
+        // first K piece of the unit
+        const char* src = !keep ? kp : isk ? kp + po : isv ? vp + po : iw < kWPieces ? wp + (size_t)iw * 16 : kp;
+        pf[j] = *reinterpret_cast<const u32x4*>(src);
+      }
     }
     const Rsrc rrs = rsrc(a.route + (size_t)n * R * topk, (uint32_t)(R * topk) * 4);
     rq = __builtin_amdgcn_raw_buffer_load_b32(rrs, keep ? route_off(tid) : kOut, 0, 0);
+    asm volatile("" ::: "memory");  // issued here: not sunk toward their use
   };
-  auto route_put = [&](int i, int rr) {  // slot i -> offsets of the routed region's first K and V token
+  auto route_put = [&](int i, int rr) {  // slot i -> the routed region's first K token, first V pixel pair
     const int js = rr / S, is = rr - js * S;
     rk[i] = (uint16_t)((js * RH * W + is * RW) * 64);
-    rv[i] = (uint16_t)(((js * RH + 2) * WP + is * RW + 2) * 64);
+    rv[i] = (uint16_t)(((js * RH + 2) * 16 + is * (RW / 2) + 1) * 128);
+  };
+  // K piece (pixel, chunk c) -> its swizzled 16 bytes
+  auto k_put = [&](int pix, int c, u32x4 d) {
+    const int y = (int)(((float)pix + 0.5f) * inv_w), x = pix - y * W;  // exact: pix < 2^12
+    *reinterpret_cast<u32x4*>(smem + lay.k + (4 * pix + (c ^ ((((x >> 1) & 1) << 1) | (y & 1)))) * 16) = d;
+  };
+  // V piece (pixel, chunk c: channels 8c..8c+7), its partner pixel's same
+  // piece in lane ^ 4: the even pixel's lane writes channels 8c..8c+3 of the
+  // pair, the odd one 8c+4..8c+7 (each as four (even, odd) dwords)
+  auto v_put = [&](int pix, int c, u32x4 d) {
+    const bool odd = pix & 1;
+    const uint32_t s0 = odd ? d[0] : d[2], s1 = odd ? d[1] : d[3];
+    const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 4), r1 = (uint32_t)__shfl_xor((int)s1, 4);
+    const uint32_t a0 = odd ? r0 : d[0], a1 = odd ? r1 : d[1];  // even pixel's dwords
+    const uint32_t b0 = odd ? d[2] : r0, b1 = odd ? d[3] : r1;  // odd pixel's
+    const int y = (int)(((float)pix + 0.5f) * inv_w), x = pix - y * W;
+    const int Y = y + 2, P = (x + 2) >> 1, sw = vsw(Y);
+    u32x4 o;
+    o[0] = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
+    o[1] = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
+    o[2] = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
+    o[3] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
+    const int cg = (8 * c + 4 * (int)odd) ^ sw;  // the swizzle moves whole 4-dword groups
+    *reinterpret_cast<u32x4*>(smem + lay.v + (Y * 16 + P) * 128 + cg * 4) = o;
   };
   auto commit = [&](int u) {
     const int tid = opaque_tid();
+    const int c = tid & 3;
+#pragma unroll
+    for (int jj = 0; 2 * jj + 1 < kPF; ++jj) {
+      if (jj < FK) {
+        const int pix = (tid >> 2) + 256 * jj;
+        k_put(pix, c, pf[2 * jj]);
+        v_put(pix, c, pf[2 * jj + 1]);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < kPF; ++j) {
-      const int i = tid + kThreads4 * j;
-      const bool isk = i < 4 * HW, isv = !isk && i < 8 * HW;
-      const int i2 = isk ? i : i - 4 * HW;
-      const int pix = i2 >> 2, c = i2 & 3;
-      const int y = (int)(((float)pix + 0.5f) * inv_w), x = pix - y * W;  // exact: pix < 2^12
-      const uint32_t ko = (uint32_t)lay.k + (uint32_t)(4 * pix + (c ^ ((((x >> 1) & 1) << 1) | (y & 1)))) * 16;
-      const uint32_t vo = (uint32_t)lay.v + (uint32_t)(4 * ((y + 2) * WP + x + 2) + (c ^ (3 * (y & 1)))) * 16;
-      // weights: global [pair][row][2 pieces] -> LDS [piece][row][pair] (reads conflict-free)
-      const int iw = i - 8 * HW, wpair = iw / 10, wrow = (iw - wpair * 10) >> 1;
-      const uint32_t wo = (uint32_t)lay.w + (uint32_t)(((iw & 1) * 5 + wrow) * 16 + wpair) * 16;
-      if (i < 8 * HW + kWPieces) *reinterpret_cast<u32x4*>(smem + (isk ? ko : isv ? vo : wo)) = pf[j];
+      if (j >= 2 * FK) {
+        const int m = tid + kThreads4 * (j - 2 * FK);
+        const bool isk = m < remK, isv = !isk && m < 2 * remK;
+        const int i2 = FK * kThreads4 + (isk ? m : m - remK);
+        const int iw = m - 2 * remK;
+        if (isk) k_put(i2 >> 2, c, pf[j]);
+        if (isv) v_put(i2 >> 2, c, pf[j]);  // partners share the branch (8-aligned pairs)
+        if (!isk && !isv && iw < kWPieces) *reinterpret_cast<u32x4*>(smem + lay.w + iw * 16) = pf[j];
+      }
     }
     if (tid < nroute) route_put(tid, (int)rq);
     // retire the prefetch registers on every path (the writes above are
@@ -492,29 +553,31 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
     }
   };
 
-  // the V border (two pixels around the image) stays zero for every unit
+  // the V border (two pixels around the image) stays zero for every unit:
+  // rows 0, 1, H + 2, H + 3 whole, and pixel pairs 0 and W / 2 + 1 of the rest
   {
-    const int top = 2 * 2 * WP * 4;  // rows 0, 1, H + 2, H + 3
+    const int top = 4 * 16 * 8;  // 16-byte pieces
     const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
     for (int i = tid; i < top + H * 16; i += kThreads4) {
-      int py, px;
+      int Y, P;
       if (i < top) {
-        const int rr = i / (WP * 4);
-        py = rr < 2 ? rr : H + rr;
-        px = (i - rr * WP * 4) >> 2;
+        const int rr = i >> 7;
+        Y = rr < 2 ? rr : H + rr;
+        P = (i >> 3) & 15;
       } else {
-        const int i2 = i - top, k = (i2 >> 2) & 3;
-        py = 2 + (i2 >> 4);
-        px = k < 2 ? k : W + k;
+        const int i2 = i - top;
+        Y = 2 + (i2 >> 4);
+        P = (i2 & 8) ? W / 2 + 1 : 0;
       }
-      *reinterpret_cast<uint4*>(vh + (size_t)(4 * (py * WP + px) + (i & 3)) * 8) = z4;
+      *reinterpret_cast<uint4*>(smem + lay.v + (Y * 16 + P) * 128 + (i & 7) * 16) = z4;
     }
   }
+
   // ---- the query rows and LCE bias of a unit --------------------------------
   // A wave takes regions first, first + 16, ... (at most four: R <= 64); the
   // start rotates with the unit so the waves that take an extra region change.
   // The loads are issued a unit ahead, before that unit's staging is written.
-  const int pp = lane & 15, xc = lane >> 4;  // LCE item: channel pair, region column
+  const int lb4 = lane >> 2, lq = lane & 3;  // LCE: matrix block (channels 2lb4, +1), row / column lq
   bf16x8 q0, q1, q2, q3;
   uint32_t bias2;
   auto qrows = [&](int vb, int it) {
@@ -532,7 +595,7 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
     q1 = qload(first + kNW4);
     q2 = qload(first + 2 * kNW4);
     q3 = qload(first + 3 * kNW4);
-    bias2 = a.b ? reinterpret_cast<const uint32_t*>(a.b)[h * 16 + pp] : 0u;
+    bias2 = a.b ? reinterpret_cast<const uint32_t*>(a.b)[h * 16 + lb4] : 0u;
   };
 
   prefetch(xcd_unit((int)blockIdx.x, units), true);
@@ -546,12 +609,16 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
   // origin is a multiple of 4, so its swizzle depends on col only)
   const int f = ((col >> 2) & 1) | (((col & 3) >> 1) << 1);
   const uint32_t kt = (uint32_t)lay.k + (uint32_t)((col >> 2) * W + (col & 3)) * 64 + 16u * (uint32_t)(grp ^ f);
-  // V^T row of this lane: key 4grp + col / 4 of a tile = token (grp, col / 4),
-  // padded row parity grp & 1; dims 16hh + 4(col % 4) .. +3
-  const int c4 = col & 3, vpar = grp & 1;
-  const uint32_t vt = (uint32_t)lay.v + (uint32_t)(grp * WP + (col >> 2)) * 64;
-  const uint32_t offV0 = vt + 16u * (uint32_t)((c4 >> 1) ^ (3 * vpar)) + 8u * (uint32_t)(c4 & 1);
-  const uint32_t offV1 = vt + 16u * (uint32_t)((2 + (c4 >> 1)) ^ (3 * vpar)) + 8u * (uint32_t)(c4 & 1);
+  // V^T of P.V: dim col (+16) at routed-region row grp (bordered row 2 + grp
+  // modulo 4), pixel pairs 0 and 1 of the region 128 bytes apart
+  const uint32_t offV0 = (uint32_t)lay.v + (uint32_t)grp * kVPitch4 + 4u * (uint32_t)(col ^ vsw(2 + grp));
+  const uint32_t offV1 = (uint32_t)lay.v + (uint32_t)grp * kVPitch4 + 4u * (uint32_t)((16 + col) ^ vsw(2 + grp));
+  // LCE window rows dy = 0..4 of this lane's output row lq: the dword pair of
+  // channels 2lb4, 2lb4 + 1 in bordered row lq + dy (modulo 4) of the region
+  uint32_t offA[5];
+#pragma unroll
+  for (int dy = 0; dy < 5; ++dy) offA[dy] = (uint32_t)(lq + dy) * kVPitch4 + 4u * (uint32_t)((2 * lb4) ^ vsw(lq + dy));
+  const uint32_t offB = (uint32_t)lay.w + (uint32_t)(lb4 * 4 + lq) * 8;  // Toeplitz block of (lb4, column lq)
   float* xw = reinterpret_cast<float*>(smem + lay.x) + wave * (16 * 36);  // this wave's hand-over
   bf16x8 ones;
 #pragma unroll
@@ -580,7 +647,7 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
 
       float m = -INFINITY;  // running max of the scaled (base-2) logits
       f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0, ls = o0;
-      // one 64-key chunk (four routed regions); Ragged: the last, partly past L
+      // one 64-key chunk (four routed regions); ragged: the last, partly past L
       auto chunk = [&](const int base, auto ragged) {
         bf16x8 ak[4];
         uint32_t va[4];
@@ -590,7 +657,14 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
           ak[t] = *reinterpret_cast<const bf16x8*>(smem + rkr[slot] + kt);
           va[t] = rvr[slot];
         }
-        auto vtr = [&](int t, uint32_t off) { return ld_tr(reinterpret_cast<const uint16_t*>(smem + va[t] + off)); };
+        // V^T operand: tile t's keys 4grp..4grp+3 (region row grp) for one dim
+        auto vtr = [&](int t, uint32_t off) {
+          const uint32_t* p = reinterpret_cast<const uint32_t*>(smem + va[t] + off);
+          u32x2 d;
+          d[0] = p[0];
+          d[1] = p[32];
+          return __builtin_bit_cast(bf16x4, d);
+        };
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         f32x4 sc[4];
 #pragma unroll
@@ -634,6 +708,7 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
       int base = 0;
       for (; base + 64 <= L; base += 64) chunk(base, std::false_type{});
       if (base < L) chunk(base, std::true_type{});  // a separate path: whole chunks select nothing
+
       // hand the output of query col (dims 4grp.., 16 + 4grp..) to the LCE layout
       const float inv = __builtin_amdgcn_rcpf(ls[0]);
       *reinterpret_cast<f32x4*>(xw + col * 36 + 4 * grp) = o0 * inv;
@@ -641,54 +716,45 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      float2 at[4];
+      // LCE accumulators start at attention output + bias: block lb4, column
+      // lq, rows 0..3 (query 4 row + lq), channels 2lb4 (d0) and 2lb4 + 1 (d1)
+      f32x4 d0, d1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) at[i] = *reinterpret_cast<const float2*>(xw + (4 * i + xc) * 36 + 2 * pp);
+      for (int p = 0; p < 4; ++p) {
+        const float2 at = *reinterpret_cast<const float2*>(xw + (4 * p + lq) * 36 + 2 * lb4);
+        d0[p] = at.x + bf16_lo(bias2);
+        d1[p] = at.y + bf16_hi(bias2);
+      }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();  // read before the next region's hand-over
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-      // LCE of column xc, rows 0..3 of the region, channel pair pp: window rows
-      // wr = 0..7 are bordered rows 4js + wr (parity wr & 1), columns 4is + xc ..;
-      // kernel row ay's dot2 operands for the pair come from LDS
-      uint4 wr0[5];
-      uint2 wr1[5];
-#pragma unroll
-      for (int ay = 0; ay < 5; ++ay) {
-        wr0[ay] = *reinterpret_cast<const uint4*>(wl + (ay * 16 + pp) * 4);
-        wr1[ay] = *reinterpret_cast<const uint2*>(wl + ((5 + ay) * 16 + pp) * 4);
-      }
+      // window: bordered rows 4js + lq + dy, pixel pairs 2is + 2ch, + 1
       const int js = r / S, is = r - js * S;
-      float acc0[4], acc1[4];
+      const uint32_t rb = (uint32_t)lay.v + (uint32_t)(4 * js * 16 + 2 * is) * 128;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { acc0[i] = bf16_lo(bias2); acc1[i] = bf16_hi(bias2); }
-      const uint32_t* vw = reinterpret_cast<const uint32_t*>(vh) + (size_t)((4 * js) * WP + 4 * is + xc) * 16;
+      for (int dy = 0; dy < 5; ++dy) {
 #pragma unroll
-      for (int wr = 0; wr < 8; ++wr) {
-        const uint32_t* vr = vw + wr * WP * 16 + (pp ^ (12 * (wr & 1)));
-        const uint32_t p0 = vr[0], p1 = vr[16], p2 = vr[32], p3 = vr[48], p4 = vr[64];
-        const uint32_t h01c = __builtin_amdgcn_perm(p1, p0, 0x05040100u), h01d = __builtin_amdgcn_perm(p1, p0, 0x07060302u);
-        const uint32_t h23c = __builtin_amdgcn_perm(p3, p2, 0x05040100u), h23d = __builtin_amdgcn_perm(p3, p2, 0x07060302u);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ay = wr - i;
-          if (ay >= 0 && ay < 5) {
-            acc0[i] = dot2(h01c, wr0[ay].x, acc0[i]);
-            acc1[i] = dot2(h01d, wr0[ay].y, acc1[i]);
-            acc0[i] = dot2(h23c, wr0[ay].z, acc0[i]);
-            acc1[i] = dot2(h23d, wr0[ay].w, acc1[i]);
-            acc0[i] = dot2(p4, wr1[ay].x, acc0[i]);
-            acc1[i] = dot2(p4, wr1[ay].y, acc1[i]);
-          }
+        for (int ch = 0; ch < 2; ++ch) {
+          const uint32_t* pa = reinterpret_cast<const uint32_t*>(smem + rb + offA[dy] + ch * 256);
+          const u32x2 x0 = *reinterpret_cast<const u32x2*>(pa);       // pair 2is + 2ch: (c, c + 1)
+          const u32x2 x1 = *reinterpret_cast<const u32x2*>(pa + 32);  // pair + 1
+          u32x2 a0, a1;
+          a0[0] = x0[0]; a0[1] = x1[0];
+          a1[0] = x0[1]; a1[1] = x1[1];
+          const bf16x4 b0 = *reinterpret_cast<const bf16x4*>(smem + offB + ((0 * 5 + dy) * 2 + ch) * 512);
+          const bf16x4 b1 = *reinterpret_cast<const bf16x4*>(smem + offB + ((1 * 5 + dy) * 2 + ch) * 512);
+          d0 = mfma4(__builtin_bit_cast(bf16x4, a0), b0, d0);
+          d1 = mfma4(__builtin_bit_cast(bf16x4, a1), b1, d1);
         }
       }
-      const uint32_t oo = (uint32_t)((4 * js) * W + 4 * is + xc) * pixb + (uint32_t)h * 64 + (uint32_t)pp * 4;
+      const uint32_t oo = (uint32_t)((4 * js) * W + 4 * is + lq) * pixb + (uint32_t)h * 64 + (uint32_t)lb4 * 4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int p = 0; p < 4; ++p) {
         bf16x2 o2;
-        o2[0] = (__bf16)(at[i].x + acc0[i]);  // round to nearest even
-        o2[1] = (__bf16)(at[i].y + acc1[i]);
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o2), ob, oo, (uint32_t)i * W * pixb, 0);
+        o2[0] = (__bf16)d0[p];  // round to nearest even
+        o2[1] = (__bf16)d1[p];
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o2), ob, oo, (uint32_t)p * W * pixb, 0);
       }
     }
     if (more) {
@@ -717,7 +783,11 @@ bool image_kernel_supports(const Shape& s) {
   if ((long long)s.H * s.W * s.C >= (1ll << 30)) return false;    // 32-bit byte offsets in an image
   if ((long long)(s.H + 4) * (s.W + 4) * 64 > 65536) return false;  // 16-bit token offsets
   if (s.rh == 2) return img_lds(2, kImage2Waves, s.H, s.W, s.R, s.topk).total <= 40 * 1024;  // four per CU
-  if (8 * s.H * s.W + kWPieces > kPF * kThreads4 || s.R > 4 * kNW4) return false;  // prefetch, regions per wave
+  {  // prefetch slots: whole K/V pairs, then the mixed remainder
+    const int fk = 4 * s.H * s.W / kThreads4, rem = 4 * s.H * s.W - fk * kThreads4;
+    if (2 * fk + (2 * rem + kWPieces + kThreads4 - 1) / kThreads4 > kPF) return false;
+  }
+  if (s.R > 4 * kNW4) return false;  // regions per wave
   if (s.W + 4 > kVRow4 || (long long)(s.H + 4) * kVRow4 * 64 > 65536) return false;  // row pitch, 16-bit offsets
   return img_lds(4, kNW4, s.H, s.W, s.R, s.topk).total <= 160 * 1024;
 }
@@ -740,7 +810,13 @@ hipError_t launch_attend_image(const void* q, const void* k, const void* v, cons
     int cus = device_cu_count();
     cus = cus >= 8 ? cus / 8 * 8 : 8;
     const int grid = units < cus ? units : cus;
-    launch(attn_image4_kernel, dim3((unsigned)grid), dim3(kThreads4), img_lds(4, kNW4, s.H, s.W, s.R, s.topk).total, st, a);
+    const size_t lds = img_lds(4, kNW4, s.H, s.W, s.R, s.topk).total;
+    switch (4 * s.H * s.W / kThreads4) {
+      case 0: launch(attn_image4_kernel<0>, dim3((unsigned)grid), dim3(kThreads4), lds, st, a); break;
+      case 1: launch(attn_image4_kernel<1>, dim3((unsigned)grid), dim3(kThreads4), lds, st, a); break;
+      case 2: launch(attn_image4_kernel<2>, dim3((unsigned)grid), dim3(kThreads4), lds, st, a); break;
+      default: launch(attn_image4_kernel<3>, dim3((unsigned)grid), dim3(kThreads4), lds, st, a); break;
+    }
   }
   return hipGetLastError();
 }

@@ -448,7 +448,7 @@ hipError_t dispatch_shape(const RegionArgs& a, const Shape& s, size_t lds, hipSt
 
 }  // namespace
 
-size_t lce_pack_bytes(int C) { return ((size_t)lce_pair_ops_offset(C) + (size_t)20 * C) * 4; }
+size_t lce_pack_bytes(int C) { return ((size_t)lce_toep_offset(C) + (size_t)(C / 32) * kLceToepDwords) * 4; }
 
 hipError_t launch_lce_pack(const void* w, int C, uint32_t* wpk, hipStream_t st) {
   launch(lce_pack_kernel, dim3((unsigned)((lce_pack_items(C) + 255) / 256)), dim3(256), 0, st,

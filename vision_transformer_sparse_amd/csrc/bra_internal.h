@@ -83,6 +83,12 @@ __device__ __forceinline__ uint4 ld16(Rsrc r, uint32_t off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+// the same with a uniform (scalar) offset added to the lane's
+__device__ __forceinline__ uint4 ld16s(Rsrc r, uint32_t off, uint32_t soff) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 // Workgroup b -> logical unit u such that consecutive units share b % 8,
 // the XCD that dispatch sends workgroup b to. Bijective on [0, blocks).
@@ -162,12 +168,18 @@ __device__ __forceinline__ float row_class_sum(float x) {
 //    (row*3+pair major, C minor) writes one dword of each parity.
 //  * then [tap][C/2] dwords (25*C/2): the weights of channels 2p and 2p+1
 //    for tap t (= 5*row + column) in one dword (low half: channel 2p).
-//  * then [C/2 pairs][5 rows][8] dwords (20*C): the dot2 operands of channel
-//    pair p (channels c = 2p, d = 2p+1) for one kernel row, taps 0..4:
-//    (c0,c1) (d0,d1) (c2,c3) (d2,d3) (c4,0) (0,d4) 0 0.
-constexpr int kLcePairOps = 8;
-__host__ __device__ inline int lce_pack_items(int C) { return 15 * C + 25 * (C / 2) + 20 * C; }
-__host__ __device__ inline int lce_pair_ops_offset(int C) { return 30 * C + 25 * (C / 2); }
+//  * then, per head of 32 channels, the 5x5 weights as Toeplitz blocks of a
+//    4x4x4 product (2560 dwords a head, 80*C in all): bf16 entry
+//    [h][dy][ch][b][j][k] (h, ch < 2; dy < 5; b < 16; j, k < 4) is
+//    w_c[dy][4 ch + k - j] for channel c = 2b + h of the head, zero where that
+//    tap index leaves 0..4. Block b, chunk ch multiplies four bordered pixels
+//    4ch..4ch+3 of a window row into output columns j = 0..3.
+constexpr int kLceToepDwords = 2560;  // per head (32 channels)
+__host__ __device__ inline int lce_toep_offset(int C) { return 30 * C + 25 * (C / 2); }
+__host__ __device__ inline int lce_pack_items(int C) { return 15 * C + 25 * (C / 2) + C / 32 * kLceToepDwords; }
+__device__ __forceinline__ uint32_t lce_toep_entry(const uint16_t* __restrict__ lw, int c, int dy, int tap) {
+  return tap >= 0 && tap < 5 ? (uint32_t)lw[(size_t)c * 25 + dy * 5 + tap] : 0u;
+}
 __device__ __forceinline__ void pack_lce_item(const uint16_t* __restrict__ lw, int C, int e,
                                               uint32_t* __restrict__ wpk) {
   if (e < 15 * C) {
@@ -184,22 +196,13 @@ __device__ __forceinline__ void pack_lce_item(const uint16_t* __restrict__ lw, i
     const int t = e2 / (C / 2), p = e2 - t * (C / 2);
     wpk[30 * C + e2] = (uint32_t)lw[(size_t)(2 * p) * 25 + t] | ((uint32_t)lw[(size_t)(2 * p + 1) * 25 + t] << 16);
   } else {
-    const int e3 = e - 15 * C - 25 * (C / 2);
-    const int k = e3 % kLcePairOps, pr = e3 / kLcePairOps;  // pr = 5p + row
-    const int p = pr / 5, ay = pr - 5 * p;
-    const uint16_t* wc = lw + (size_t)(2 * p) * 25 + ay * 5;  // channel 2p, row ay
-    const uint16_t* wd = wc + 25;                              // channel 2p+1
-    uint32_t lo = 0u, hi = 0u;
-    switch (k) {
-      case 0: lo = wc[0]; hi = wc[1]; break;
-      case 1: lo = wd[0]; hi = wd[1]; break;
-      case 2: lo = wc[2]; hi = wc[3]; break;
-      case 3: lo = wd[2]; hi = wd[3]; break;
-      case 4: lo = wc[4]; break;
-      case 5: hi = wd[4]; break;
-      default: break;
-    }
-    wpk[lce_pair_ops_offset(C) + e3] = lo | (hi << 16);
+    const int e3 = e - 15 * C - 25 * (C / 2);  // dword of the Toeplitz section
+    const int head = e3 / kLceToepDwords, f = 2 * (e3 - head * kLceToepDwords);  // bf16 index, even
+    const int k = f & 3, j = (f >> 2) & 3, b = (f >> 4) & 15, ch = (f >> 8) & 1;
+    const int dy = (f >> 9) % 5, h = (f >> 9) / 5;
+    const int c = 32 * head + 2 * b + h;
+    const int tap = 4 * ch + k - j;
+    wpk[lce_toep_offset(C) + e3] = lce_toep_entry(lw, c, dy, tap) | (lce_toep_entry(lw, c, dy, tap + 1) << 16);
   }
 }
 
