@@ -156,6 +156,7 @@ __global__ __launch_bounds__(64 * NW) void attn_image2_kernel(ImageArgs a) {
   const size_t img = (size_t)n * H * W * C;
   const uint32_t img_bytes = (uint32_t)H * W * C * 2;
   const Rsrc qb = rsrc(a.q + img, img_bytes), kb = rsrc(a.k + img, img_bytes);
+  const Rsrc ob = rsrc(a.out + img, img_bytes);
   const Rsrc vb = rsrc(a.v + img, img_bytes);
   const uint32_t pixb = (uint32_t)C * 2;   // bytes per pixel
   const uint32_t hoff = (uint32_t)h * 64;  // byte offset of the head in a pixel
@@ -360,7 +361,7 @@ __global__ __launch_bounds__(64 * NW) void attn_image2_kernel(ImageArgs a) {
       acc1 = dot2(p4, w1.y, acc1);
     }
     const uint32_t packed = float_to_bf16_bits(at0 + (acc0 + acc2)) | (float_to_bf16_bits(at1 + (acc1 + acc3)) << 16);
-    *reinterpret_cast<uint32_t*>(a.out + img + (size_t)(y * W + x) * C + 32 * h + 2 * cp) = packed;
+    st_nt(ob, (uint32_t)((y * W + x) * C + 32 * h + 2 * cp) * 2, packed);
   }
 }
 
@@ -754,7 +755,7 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
         bf16x2 o2;
         o2[0] = (__bf16)d0[p];  // round to nearest even
         o2[1] = (__bf16)d1[p];
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o2), ob, oo, (uint32_t)p * W * pixb, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o2), ob, oo, (uint32_t)p * W * pixb, 2);  // nt: streamed, not kept in L2
       }
     }
     if (more) {

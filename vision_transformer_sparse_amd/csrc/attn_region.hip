@@ -122,6 +122,7 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
   const uint32_t img_bytes = (uint32_t)H * W * C * 2;
   const Rsrc qb = rsrc(a.q + img, img_bytes), kbuf = rsrc(a.k + img, img_bytes);
   const Rsrc vbuf = rsrc(a.v + img, img_bytes);
+  const Rsrc ob = rsrc(a.out + img, img_bytes);
   const uint32_t rowb = (uint32_t)W * C * 2;  // bytes per image row
   constexpr uint32_t pixb = C * 2;            // bytes per pixel
   const int c0 = wave * 32;                   // this wave's head
@@ -386,9 +387,9 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
         p0.y = float_to_bf16_bits(fmaf(o0[2], inv, l0.z)) | (float_to_bf16_bits(fmaf(o0[3], inv, l0.w)) << 16);
         p1.x = float_to_bf16_bits(fmaf(o1[0], inv, l1.x)) | (float_to_bf16_bits(fmaf(o1[1], inv, l1.y)) << 16);
         p1.y = float_to_bf16_bits(fmaf(o1[2], inv, l1.z)) | (float_to_bf16_bits(fmaf(o1[3], inv, l1.w)) << 16);
-        uint16_t* op = a.out + img + ((size_t)(y0 + col / RW) * W + x0 + col % RW) * C + c0 + 4 * grp;
-        *reinterpret_cast<uint2*>(op) = p0;
-        *reinterpret_cast<uint2*>(op + 16) = p1;
+        const uint32_t oo = (uint32_t)(((y0 + col / RW) * W + x0 + col % RW) * C + c0 + 4 * grp) * 2;
+        st_nt(ob, oo, p0);
+        st_nt(ob, oo + 32, p1);
       } else {
         // the head's output -> LDS, for the LCE threads to merge
         float* ap = lce + col * C + c0;
@@ -408,7 +409,7 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
       for (int yo = 0; yo < RH; ++yo) {
         const float2 at = *reinterpret_cast<const float2*>(lce + (yo * RW + xcol) * C + c);
         const uint32_t packed = float_to_bf16_bits(at.x + acc0[yo]) | (float_to_bf16_bits(at.y + acc1[yo]) << 16);
-        *reinterpret_cast<uint32_t*>(a.out + img + ((size_t)(y0 + yo) * W + x0 + xcol) * C + c) = packed;
+        st_nt(ob, (uint32_t)(((y0 + yo) * W + x0 + xcol) * C + c) * 2, packed);
       }
     }
   }

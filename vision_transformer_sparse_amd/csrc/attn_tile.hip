@@ -381,9 +381,10 @@ __global__ __launch_bounds__((64 * tile_waves<RH, RW>()), 4) void attn_tile_kern
     lo.y = float_to_bf16_bits(fmaf(o0[i][2], inv, acc[i][2])) | (float_to_bf16_bits(fmaf(o0[i][3], inv, acc[i][3])) << 16);
     hi.x = float_to_bf16_bits(fmaf(o1[i][0], inv, acc[i][4])) | (float_to_bf16_bits(fmaf(o1[i][1], inv, acc[i][5])) << 16);
     hi.y = float_to_bf16_bits(fmaf(o1[i][2], inv, acc[i][6])) | (float_to_bf16_bits(fmaf(o1[i][3], inv, acc[i][7])) << 16);
-    uint16_t* po = a.out + img + ((size_t)(y0 + ty) * W + x0 + tx) * C + h * 32;
-    *reinterpret_cast<uint2*>(po + 4 * grp) = lo;
-    *reinterpret_cast<uint2*>(po + 16 + 4 * grp) = hi;
+    const Rsrc ob = rsrc(a.out + img, img_bytes);
+    const uint32_t oo = (uint32_t)(((y0 + ty) * W + x0 + tx) * C + h * 32) * 2;
+    st_nt(ob, oo + 8 * grp, lo);
+    st_nt(ob, oo + 32 + 8 * grp, hi);
   }
 }
 

@@ -90,6 +90,23 @@ __device__ __forceinline__ uint4 ld16s(Rsrc r, uint32_t off, uint32_t soff) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Streaming (non-temporal) stores for outputs that nothing in the kernel
+// reads back: they leave without staying dirty in L2, which the end of the
+// kernel would otherwise have to write back. (Buffer stores carry the
+// cache policy as an operand; a plain store's hint can be lost when the
+// compiler merges stores.)
+constexpr int kNt = 2;  // cache-policy bit: non-temporal
+__device__ __forceinline__ void st_nt(Rsrc r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kNt);
+}
+__device__ __forceinline__ void st_nt(Rsrc r, uint32_t off, uint2 v) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 x;
+  x[0] = v.x;
+  x[1] = v.y;
+  __builtin_amdgcn_raw_buffer_store_b64(x, r, off, 0, kNt);
+}
+
 // Workgroup b -> logical unit u such that consecutive units share b % 8,
 // the XCD that dispatch sends workgroup b to. Bijective on [0, blocks).
 __device__ __forceinline__ int xcd_unit(int b, int blocks) {
