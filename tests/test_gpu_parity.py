@@ -232,17 +232,21 @@ def test_host_pointer_rejected(gpu_lib):
     assert lib.bra_lce(hp, hp, None, 1, 8, 8, 32, 0, hp) == -7
 
 
-def test_profile_counts(gpu_lib):
-    cfg = CONFIGS[1]
+@pytest.mark.parametrize("ci,routes", [(2, 3), (1, 0)])
+def test_profile_counts(gpu_lib, ci, routes):
+    """One pool, route and attention launch per forward; with 4x4 regions
+    (the classification stage-2 shape) the attention kernel routes the images
+    itself, so no route kernel runs."""
+    cfg = CONFIGS[ci]
     inp = draw_config(cfg, N=4)
     args = [dev(inp[x], cfg.dtype) for x in ("q", "k", "v", "lce_w", "lce_b")]
-    say("profile")
+    say(f"profile {cfg.name}")
     gpu_lib.profile_begin()
     for _ in range(3):
         gpu_lib.forward(*args, cfg.heads, cfg.S, cfg.topk)
     rec = gpu_lib.profile_read()
     gpu_lib.profile_begin(())
-    assert rec["pool"][1] == 3 and rec["route"][1] == 3 and rec["attn"][1] == 3
+    assert rec["pool"][1] == 3 and rec["route"][1] == routes and rec["attn"][1] == 3
     assert rec["attn"][0] > 0
 
 

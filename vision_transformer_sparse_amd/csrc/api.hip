@@ -26,9 +26,14 @@ hipError_t launch_attend_region(const void* q, const void* k, const void* v, con
                                 const void* b, const int32_t* route, const Shape& s, void* out,
                                 hipStream_t st);
 bool image_kernel_supports(const Shape& s);
+bool image_kernel_routes(const Shape& s);
+// qr, kr, route_out non-null (4x4 regions, image_kernel_routes): the kernel
+// computes the routes itself from the region means and reports them to
+// route_out; route is then unused
 hipError_t launch_attend_image(const void* q, const void* k, const void* v, const uint32_t* wpk,
                                const void* b, const int32_t* route, const Shape& s, void* out,
-                               hipStream_t st);
+                               hipStream_t st, const float* qr = nullptr, const float* kr = nullptr,
+                               int32_t* route_out = nullptr);
 bool tile_kernel_supports(const Shape& s);
 bool f32_kernel_supports(const Shape& s);
 hipError_t launch_attend_f32(const void* q, const void* k, const void* v, const void* w,
@@ -277,6 +282,15 @@ int bra_forward(const void* q, const void* k, const void* v, const void* lce_w,
     e = bra::launch_region_pool(q, k, s, dtype, qr, kr, lce_w, wpk, st);
   }
   if (e != hipSuccess) return hip_fail(e);
+  if (dtype == BRA_BF16 && bra::image_kernel_routes(s)) {
+    // the attention kernel routes its own images (same code as the route
+    // kernel, so the same routes) and reports them to route_idx
+    {
+      ProfScope ps(BRA_K_ATTN, st);
+      e = bra::launch_attend_image(q, k, v, wpk, lce_b, nullptr, s, out, st, qr, kr, route_idx);
+    }
+    return e == hipSuccess ? BRA_OK : hip_fail(e);
+  }
   {
     ProfScope ps(BRA_K_ROUTE, st);
     e = bra::launch_route(qr, kr, N, s.R, C, topk, route_idx, st);

@@ -25,6 +25,7 @@
 // then owns one (query, channel pair) -- the copies split the query's 32
 // dims into 16 channel pairs -- and adds the LCE of its pair and stores it.
 #include "bra_internal.h"
+#include "route_common.h"
 
 #include <type_traits>
 
@@ -91,10 +92,16 @@ struct ImageArgs {
   const uint16_t* v;
   const uint32_t* wpk;     // packed LCE weights; the tap-major part is used
   const uint16_t* b;       // LCE bias or null
-  const int32_t* route;    // [N][S*S][topk]
+  const int32_t* route;    // [N][S*S][topk] (null: the kernel routes itself)
   uint16_t* out;
   int N, H, W, C, heads, S, topk;
   float qscale;            // head_dim^-1/2 * log2(e)
+  // routing inside the kernel (4x4 regions): region means, C^-1/2, and where
+  // the routes are reported
+  const float* qr;
+  const float* kr;
+  int32_t* route_out;
+  float rscale;
 };
 
 __host__ __device__ constexpr size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
@@ -407,8 +414,20 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// FK: whole K/V slot pairs of the prefetch (4 H W / 1024, rounded down)
-template <int FK>
+// Routing inside the kernel (C <= 128): the region means of two images, in
+// kRouteSlots 16-byte pieces a lane, then in LDS as split bf16 rows
+constexpr int kRouteMaxC = 128;
+constexpr int kRouteSlots = 4;
+// LDS the in-kernel routing borrows from the weight and hand-over areas: the
+// logits [R][16 ceil(R/16) + 1] fp32 and the partial top-4 lists
+__host__ __device__ inline size_t route_scratch(int R) {
+  return (size_t)R * (16 * ((R + 15) / 16) + 1) * 4 + (size_t)4 * 8 * 64 * 4;
+}
+
+// FK: whole K/V slot pairs of the prefetch (4 H W / 1024, rounded down);
+// FUSE: the kernel computes its units' routes from the region means (a
+// workgroup then has at most two units)
+template <int FK, bool FUSE>
 __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
   constexpr int RH = 4, RW = 4, T = 16;
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -483,8 +502,10 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
         pf[j] = *reinterpret_cast<const u32x4*>(src);
       }
     }
-    const Rsrc rrs = rsrc(a.route + (size_t)n * R * topk, (uint32_t)(R * topk) * 4);
-    rq = __builtin_amdgcn_raw_buffer_load_b32(rrs, keep ? route_off(tid) : kOut, 0, 0);
+    if constexpr (!FUSE) {  // (routed in the kernel: rq already holds the routes)
+      const Rsrc rrs = rsrc(a.route + (size_t)n * R * topk, (uint32_t)(R * topk) * 4);
+      rq = __builtin_amdgcn_raw_buffer_load_b32(rrs, keep ? route_off(tid) : kOut, 0, 0);
+    }
     asm volatile("" ::: "memory");  // issued here: not sunk toward their use
   };
   auto route_put = [&](int i, int rr) {  // slot i -> the routed region's first K token, first V pixel pair
@@ -516,7 +537,7 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
     const int cg = (8 * c + 4 * (int)odd) ^ sw;  // the swizzle moves whole 4-dword groups
     *reinterpret_cast<u32x4*>(smem + lay.v + (Y * 16 + P) * 128 + cg * 4) = o;
   };
-  auto commit = [&](int u) {
+  auto commit = [&](int u, bool with_routes) {
     const int tid = opaque_tid();
     const int c = tid & 3;
 #pragma unroll
@@ -539,14 +560,14 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
         if (!isk && !isv && iw < kWPieces) *reinterpret_cast<u32x4*>(smem + lay.w + iw * 16) = pf[j];
       }
     }
-    if (tid < nroute) route_put(tid, (int)rq);
+    if (with_routes && tid < nroute) route_put(tid, (int)rq);
     // retire the prefetch registers on every path (the writes above are
     // guarded; left pending on the path that skips them, they would make the
     // next unit's first load wait on its own query rows)
 #pragma unroll
     for (int j = 0; j < kPF; ++j) asm volatile("" : "+v"(pf[j]));
     asm volatile("" : "+v"(rq));
-    if (nroute > kThreads4) {  // large route tables: the rest read here
+    if (!FUSE && nroute > kThreads4) {  // large route tables: the rest read here
       const int n = u / a.heads;
       const Rsrc rrs = rsrc(a.route + (size_t)n * R * topk, (uint32_t)(R * topk) * 4);
       for (int i = tid + kThreads4; i < nroute; i += kThreads4)
@@ -554,9 +575,11 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
     }
   };
 
+
   // the V border (two pixels around the image) stays zero for every unit:
   // rows 0, 1, H + 2, H + 3 whole, and pixel pairs 0 and W / 2 + 1 of the rest
-  {
+  // (written once, just before the first unit is staged)
+  auto zero_border = [&]() {
     const int top = 4 * 16 * 8;  // 16-byte pieces
     const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
     for (int i = tid; i < top + H * 16; i += kThreads4) {
@@ -572,7 +595,7 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
       }
       *reinterpret_cast<uint4*>(smem + lay.v + (Y * 16 + P) * 128 + (i & 7) * 16) = z4;
     }
-  }
+  };
 
   // ---- the query rows and LCE bias of a unit --------------------------------
   // A wave takes regions first, first + 16, ... (at most four: R <= 64); the
@@ -581,8 +604,7 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
   const int lb4 = lane >> 2, lq = lane & 3;  // LCE: matrix block (channels 2lb4, +1), row / column lq
   bf16x8 q0, q1, q2, q3;
   uint32_t bias2;
-  auto qrows = [&](int vb, int it) {
-    const int u = xcd_unit(vb, units);
+  auto qrows = [&](int u, int it) {
     const int n = u / a.heads, h = u - n * a.heads;
     const Rsrc qb = rsrc(a.q + (size_t)n * HW * C, img_bytes);
     const int first = (wave + kNW4 - it % kNW4) % kNW4;
@@ -599,11 +621,167 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
     bias2 = a.b ? reinterpret_cast<const uint32_t*>(a.b)[h * 16 + lb4] : 0u;
   };
 
-  prefetch(xcd_unit((int)blockIdx.x, units), true);
-  qrows((int)blockIdx.x, 0);
-  asm volatile("" ::: "memory");
-  commit(xcd_unit((int)blockIdx.x, units));
+  // ---- the units of this workgroup: unit_of(it), it < nits. Routing in the
+  // kernel, a workgroup takes heads h and h + heads/2 of one image (the image
+  // is routed once for both; the workgroups of heads h, h + 1 run side by
+  // side on one XCD and share the cache lines of their channels); else units
+  // b, b + G, ... Either way neighbouring units share an XCD.
+  const int nits = FUSE ? 2 : (units - (int)blockIdx.x + G - 1) / G;
+  auto unit_of = [&](int it) {
+    if constexpr (FUSE) {
+      const int hh = a.heads / 2, pi = xcd_unit((int)blockIdx.x, units / 2);
+      const int n = pi / hh;
+      return n * a.heads + (pi - n * hh) + it * hh;
+    } else {
+      return xcd_unit((int)blockIdx.x + it * G, units);
+    }
+  };
+  const int u0 = unit_of(0);
+  if constexpr (FUSE) {
+    // ---- the image's routes, from its region means. The Q^r and K^r rows
+    // are loaded into the K/V area first, split into bf16 hi and lo rows
+    // as the route kernel splits them (rows C + 8 apart to spread the banks),
+    // and wave w computes logit tile (w / CT, w % CT) with the route kernel's
+    // split-bf16 steps, from LDS. The top k (k <= 4) of a row is found by a
+    // lane scanning candidates in index order (four waves a quarter each, then
+    // merged), which picks what the route kernel's ranks pick. The routes go
+    // straight to the route table (both units share it); the workgroup with
+    // head 0 reports them. The logits and partial lists use the weight and
+    // hand-over areas; all of it is overwritten when the first unit is staged.
+    const int CT = (R + 15) / 16, RP = 16 * CT + 1;  // odd pitch: a lane per row reads without conflicts
+    float* logits = reinterpret_cast<float*>(smem + lay.w);            // [R][RP]
+    uint32_t* part = reinterpret_cast<uint32_t*>(logits + R * RP);      // [4][8][64] partial top 4
+    const int rt = wave / CT, ct = wave - rt * CT;
+    const bool has_tile = wave < CT * CT;
+    const int n0 = u0 / a.heads;
+    const int c4n = C / 4, mpieces = R * c4n;  // 16-byte pieces of one matrix
+    const int RS = C + 8;                      // bf16 per LDS row
+    // matrix m (0: Q^r, 1: K^r), part 0 (hi) / 1 (lo): R rows of RS bf16
+    auto mat_lds = [&](int m, int part) { return (__bf16*)(smem + lay.k) + (size_t)(2 * m + part) * R * RS; };
+    u32x4 ro[kRouteSlots];
+#pragma unroll
+    for (int j = 0; j < kRouteSlots; ++j) {
+      const int P = tid + kThreads4 * j, m = P / mpieces, pm = P - m * mpieces;
+      const float* src = m < 2 ? (m ? a.kr : a.qr) + (size_t)n0 * R * C + (size_t)pm * 4 : a.qr;  // (past the end: piece 0 again)
+      ro[j] = *reinterpret_cast<const u32x4*>(src);
+    }
+    // (the means are staged before the K/V prefetch is issued: in flight
+    // together with it they would arrive as late as it does)
+#pragma unroll
+    for (int j = 0; j < kRouteSlots; ++j) {
+      const int P = tid + kThreads4 * j, m = P / mpieces, pm = P - m * mpieces;
+      const int row = pm / c4n, c4 = pm - row * c4n;
+      if (m < 2) {
+        typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+        b4 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {  // as route::split_bf16
+          const float x = __uint_as_float(ro[j][e]);
+          hi[e] = (__bf16)x;
+          lo[e] = (__bf16)(x - (float)hi[e]);
+        }
+        *reinterpret_cast<b4*>(mat_lds(m, 0) + row * RS + 4 * c4) = hi;
+        *reinterpret_cast<b4*>(mat_lds(m, 1) + row * RS + 4 * c4) = lo;
+      }
+    }
+    lds_barrier();  // the means in LDS
+    {  // logit tile (rt, ct): the route kernel's steps in its order (C a multiple of 32)
+      const int qrow = min(16 * rt + col, R - 1), krow = min(16 * ct + col, R - 1);
+      const __bf16* ah = mat_lds(0, 0) + qrow * RS + 8 * grp;
+      const __bf16* al = mat_lds(0, 1) + qrow * RS + 8 * grp;
+      const __bf16* bh = mat_lds(1, 0) + krow * RS + 8 * grp;
+      const __bf16* bl = mat_lds(1, 1) + krow * RS + 8 * grp;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < C; k0 += 32)
+        acc = route::logit_step_x3(acc, *reinterpret_cast<const route::rbf16x8*>(ah + k0),
+                                   *reinterpret_cast<const route::rbf16x8*>(al + k0),
+                                   *reinterpret_cast<const route::rbf16x8*>(bh + k0),
+                                   *reinterpret_cast<const route::rbf16x8*>(bl + k0));
+      if (has_tile) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * rt + 4 * grp + e;
+          if (row < R) logits[row * RP + 16 * ct + col] = acc[e] * a.rscale;
+        }
+      }
+    }
+    // the K/V prefetch goes out now; the rank selection below runs while it
+    // is in flight
+    asm volatile("" ::: "memory");
+    prefetch(u0, true);
+    qrows(u0, 0);
+    asm volatile("" ::: "memory");
+    lds_barrier();  // the logits in LDS
+    // top-k (k <= 4), a lane per row: wave q < 4 keeps the top 4 of candidates
+    // [q cq, (q + 1) cq) of every row, in index order (cq <= 16: R <= 64)
+    const int cq = (R + 3) / 4;
+    if (wave < 4) {
+      const float* lg = logits + min(lane, R - 1) * RP + wave * cq;
+      const int nc = min(R, (wave + 1) * cq) - wave * cq;
+      uint32_t kv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) kv[j] = j < nc ? route::key_u32(lg[j]) : 0u;  // all reads first
+      uint32_t t[4] = {0u, 0u, 0u, 0u};
+      int ix[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 16; ++j) route::top4_insert(t, ix, kv[j], wave * cq + j);  // (key 0 never enters)
+      uint32_t* pw = part + (size_t)wave * 8 * 64 + lane;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        pw[k * 64] = t[k];
+        pw[(4 + k) * 64] = (uint32_t)ix[k];
+      }
+    }
+    lds_barrier();
+    // wave 0 merges the four lists in candidate order and writes the routes
+    // of every row (slots past topk: region 0, masked)
+    if (wave == 0) {
+      uint32_t t[4];
+      int ix[4];
+      uint32_t pk[16];
+      int pi[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {  // all reads first
+          pk[4 * q + k] = part[(size_t)q * 8 * 64 + k * 64 + lane];
+          pi[4 * q + k] = (int)part[(size_t)q * 8 * 64 + (4 + k) * 64 + lane];
+        }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) { t[k] = pk[k]; ix[k] = pi[k]; }
+#pragma unroll
+      for (int j = 4; j < 16; ++j) route::top4_insert(t, ix, pk[j], pi[j]);
+      if (lane < R) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (k < topk) route_put(lane * RSTR + k, ix[k]);
+        for (int k = topk; k < RSTR; ++k) route_put(lane * RSTR + k, 0);
+      }
+    }
+    lds_barrier();  // every read of the means and logits done before staging
+    zero_border();
+    commit(u0, false);
+  } else {
+    zero_border();
+    prefetch(u0, true);
+    qrows(u0, 0);
+    asm volatile("" ::: "memory");
+    commit(u0, true);
+  }
   lds_barrier();  // the first unit staged
+  if constexpr (FUSE) {
+    // the workgroup with head 0 reports the image's routes, read back from
+    // the route table (K offset 256 (j W + i) for region (j, i)); stores
+    // issued now, not while the prefetch still fills the memory queues
+    const int n0 = u0 / a.heads;
+    if (u0 - n0 * a.heads == 0) {
+      for (int i = tid; i < R * topk; i += kThreads4) {
+        const int r = i / topk, k = i - r * topk;
+        const int ji = rk[r * RSTR + k] >> 8, js = ji / W;
+        a.route_out[(size_t)n0 * R * topk + i] = js * S + (ji - js * W);
+      }
+    }
+  }
 
   // ---- per-lane constants -----------------------------------------------------
   // K row of this lane: token (col / 4, col % 4) of a routed region (whose
@@ -625,13 +803,13 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
-  for (int it = 0, vb = (int)blockIdx.x; vb < units; ++it, vb += G) {
-    const int u = xcd_unit(vb, units);
+  for (int it = 0; it < nits; ++it) {
+    const int u = unit_of(it);
     const int n = u / a.heads, h = u - n * a.heads;
     const Rsrc ob = rsrc(a.out + (size_t)n * HW * C, img_bytes);
     const int first = (wave + kNW4 - it % kNW4) % kNW4;
-    const bool more = vb + G < units;
-    prefetch(more ? xcd_unit(vb + G, units) : u, more);
+    const bool more = it + 1 < nits;
+    prefetch(more ? unit_of(it + 1) : u, more);
     // Take delivery of the query rows and the bias right after the prefetch
     // was issued: the wait covers just these loads, and the region loop holds
     // no value still in flight (a loop that used one would have the compiler
@@ -759,10 +937,10 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
       }
     }
     if (more) {
-      qrows(vb + G, it + 1);
+      qrows(unit_of(it + 1), it + 1);
       asm volatile("" ::: "memory");  // issued here, ahead of the staging below
       lds_barrier();  // every wave is done with this unit's LDS
-      commit(xcd_unit(vb + G, units));
+      commit(unit_of(it + 1), !FUSE);  // (two heads of one image share the routes)
       lds_barrier();  // the next unit staged
     } else {
       // the discarded loads of the last unit retired as well: no path around
@@ -793,31 +971,63 @@ bool image_kernel_supports(const Shape& s) {
   return img_lds(4, kNW4, s.H, s.W, s.R, s.topk).total <= 160 * 1024;
 }
 
+// one persistent workgroup per CU (a multiple of 8, so a workgroup's units
+// stay on its XCD), at most one per unit
+static int image4_grid(int units) {
+  int cus = device_cu_count();
+  cus = cus >= 8 ? cus / 8 * 8 : 8;
+  return units < cus ? units : cus;
+}
+
+bool image_kernel_routes(const Shape& s) {
+  if (s.rh != 4 || !image_kernel_supports(s)) return false;
+  if (s.heads % 2) return false;                           // head pairs
+  if (s.C > kRouteMaxC || s.C % 32 || s.R > 64) return false;  // split steps, 64 candidates
+  if (s.topk > 4) return false;                            // top 4 by insertion
+  const int units = s.N * s.heads;
+  if (units / 2 > image4_grid(units)) return false;        // a workgroup per head pair, in one round
+  if (2 * s.R * (s.C / 4) > kRouteSlots * kThreads4) return false;  // the means' pieces a lane
+  const ImgLds l = img_lds(4, kNW4, s.H, s.W, s.R, s.topk);
+  if ((size_t)4 * s.R * (s.C + 8) * 2 > l.rk - l.k) return false;  // the split means in the K/V area
+  return route_scratch(s.R) <= l.sink - l.w;               // the weight and hand-over areas
+}
+
 hipError_t launch_attend_image(const void* q, const void* k, const void* v, const uint32_t* wpk,
                                const void* b, const int32_t* route, const Shape& s, void* out,
-                               hipStream_t st) {
+                               hipStream_t st, const float* qr, const float* kr, int32_t* route_out) {
   ImageArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.wpk = wpk; a.b = (const uint16_t*)b; a.route = route; a.out = (uint16_t*)out;
   a.N = s.N; a.H = s.H; a.W = s.W; a.C = s.C; a.heads = s.heads; a.S = s.S; a.topk = s.topk;
   a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
+  a.qr = qr; a.kr = kr; a.route_out = route_out;
+  a.rscale = (float)(1.0 / __builtin_sqrt((double)s.C));  // as the route kernels
   const int units = s.N * s.heads;
   if (s.rh == 2) {
     launch(attn_image2_kernel<kImage2Waves>, dim3((unsigned)units), dim3(64 * kImage2Waves),
            img_lds(2, kImage2Waves, s.H, s.W, s.R, s.topk).total, st, a);
   } else {
-    // one persistent workgroup per CU (a multiple of 8, so a workgroup's
-    // units stay on its XCD), at most one per unit
-    int cus = device_cu_count();
-    cus = cus >= 8 ? cus / 8 * 8 : 8;
-    const int grid = units < cus ? units : cus;
+    const int grid = qr ? units / 2 : image4_grid(units);  // routing in the kernel: a workgroup per head pair
     const size_t lds = img_lds(4, kNW4, s.H, s.W, s.R, s.topk).total;
-    switch (4 * s.H * s.W / kThreads4) {
-      case 0: launch(attn_image4_kernel<0>, dim3((unsigned)grid), dim3(kThreads4), lds, st, a); break;
-      case 1: launch(attn_image4_kernel<1>, dim3((unsigned)grid), dim3(kThreads4), lds, st, a); break;
-      case 2: launch(attn_image4_kernel<2>, dim3((unsigned)grid), dim3(kThreads4), lds, st, a); break;
-      default: launch(attn_image4_kernel<3>, dim3((unsigned)grid), dim3(kThreads4), lds, st, a); break;
+    const dim3 g((unsigned)grid), blk(kThreads4);
+#define BRA_IMG4(FKV, FU) launch(attn_image4_kernel<FKV, FU>, g, blk, lds, st, a)
+    const int fk = 4 * s.H * s.W / kThreads4;
+    if (qr) {
+      switch (fk) {
+        case 0: BRA_IMG4(0, true); break;
+        case 1: BRA_IMG4(1, true); break;
+        case 2: BRA_IMG4(2, true); break;
+        default: BRA_IMG4(3, true); break;
+      }
+    } else {
+      switch (fk) {
+        case 0: BRA_IMG4(0, false); break;
+        case 1: BRA_IMG4(1, false); break;
+        case 2: BRA_IMG4(2, false); break;
+        default: BRA_IMG4(3, false); break;
+      }
     }
+#undef BRA_IMG4
   }
   return hipGetLastError();
 }

@@ -1,0 +1,208 @@
+// Routing pieces shared by the route kernels and the attention kernel that
+// routes its own images: the 64-bit top-k key, the fp32 matrix-core logit
+// tile and the rank selection. One definition, so every caller computes the
+// same logits in the same order and picks the same routes, bit for bit.
+#pragma once
+#include "bra_internal.h"
+
+namespace bra {
+namespace route {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunk = 64;  // channels per load batch: 4 pieces of A and 4 of B per lane
+
+// order-preserving map of a logit to unsigned (-0 and +0 are the same logit;
+// every value maps above 0)
+__device__ __forceinline__ uint32_t key_u32(float a) {
+  if (a == 0.0f) a = 0.0f;
+  const uint32_t u = __float_as_uint(a);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t route_key(float a, int s) {
+  return ((uint64_t)key_u32(a) << 32) | (uint32_t)(0xffffffffu - (uint32_t)s);
+}
+// Keeps the 4 largest (key, index) pairs seen, largest first, when the
+// candidates arrive in ascending index order: a key enters above another only
+// when strictly larger, so equal keys stay in index order -- the same order
+// as route_key's.
+__device__ __forceinline__ void top4_insert(uint32_t* t, int* ix, uint32_t u, int s) {
+  const bool c0 = u > t[0], c1 = u > t[1], c2 = u > t[2], c3 = u > t[3];
+  t[3] = c2 ? t[2] : (c3 ? u : t[3]);
+  ix[3] = c2 ? ix[2] : (c3 ? s : ix[3]);
+  t[2] = c1 ? t[1] : (c2 ? u : t[2]);
+  ix[2] = c1 ? ix[1] : (c2 ? s : ix[2]);
+  t[1] = c0 ? t[0] : (c1 ? u : t[1]);
+  ix[1] = c0 ? ix[0] : (c1 ? s : ix[1]);
+  t[0] = c0 ? u : t[0];
+  ix[0] = c0 ? s : ix[0];
+}
+
+// One 16 x 16 logit tile: rows r0.., columns 16ct.. of (Q^r K^r^T) * scale,
+// lane (col, grp) returning rows 4grp..4grp+3 at column col. get(row, c)
+// returns the 16-byte piece of channels c..c+3 of a Q^r (a) / K^r (b) row
+// (rows clamped to R-1, pieces past C zero). The fp32 MFMA sequence is the
+// same wherever the operands come from, so the logits are too.
+// one 64-channel batch of the tile: lane (col, grp) holds channels
+// 16j + 4grp .. +3 of its A and B rows in a[j], b[j]
+__device__ __forceinline__ f32x4 logit_batch(f32x4 acc, const uint4* a, const uint4* b) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].x), __uint_as_float(b[j].x), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].y), __uint_as_float(b[j].y), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].z), __uint_as_float(b[j].z), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].w), __uint_as_float(b[j].w), acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+template <typename GetA, typename GetB>
+__device__ __forceinline__ f32x4 logit_tile(int col, int grp, int C, GetA geta, GetB getb) {
+  uint4 a[4], b[4], an[4], bn[4];
+  auto fetch = [&](int c0, uint4* aa, uint4* bb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = c0 + 16 * j + 4 * grp;
+      aa[j] = geta(c);
+      bb[j] = getb(c);
+    }
+  };
+  // the next batch is always in flight while one is multiplied (the last
+  // batch is peeled off, so no branch guards the loads)
+  fetch(0, a, b);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int c0 = 0;
+  for (; c0 + kChunk < C; c0 += kChunk) {
+    fetch(c0 + kChunk, an, bn);
+    acc = logit_batch(acc, a, b);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { a[j] = an[j]; b[j] = bn[j]; }
+  }
+  return logit_batch(acc, a, b);
+}
+
+// The same tile in two steps, for a caller that must issue the operand loads
+// early: all NB = ceil(C / 64) batches into registers, then the batches in
+// logit_tile's order (so the logits are the same bit for bit).
+template <int NB>
+struct LogitOps {
+  uint4 a[NB][4], b[NB][4];
+};
+template <int NB, typename GetA, typename GetB>
+__device__ __forceinline__ void logit_load(LogitOps<NB>& o, int grp, GetA geta, GetB getb) {
+#pragma unroll
+  for (int k = 0; k < NB; ++k)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = kChunk * k + 16 * j + 4 * grp;
+      o.a[k][j] = geta(c);
+      o.b[k][j] = getb(c);
+    }
+}
+template <int NB>
+__device__ __forceinline__ f32x4 logit_mma(const LogitOps<NB>& o) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < NB; ++k) acc = logit_batch(acc, o.a[k], o.b[k]);
+  return acc;
+}
+
+// ---- split-bf16 logit tiles (R <= 64) --------------------------------------
+// A logit Q^r_i . K^r_s in fp32 from bf16 matrix products: each fp32 operand
+// is split as x = hi + lo (hi = bf16(x), lo = bf16(x - hi), both rounded to
+// nearest even; the remainder is below 2^-16 |x|), and per 32-channel step
+// the tile accumulates hi.lo + lo.hi + hi.hi (each bf16 product exact in the
+// fp32 accumulator). The dropped lo.lo and remainder terms are ~2^-16 of the
+// products, far inside the 1e-5 near-tie margin of the routing; the order is
+// fixed, so every caller gets the same logits bit for bit.
+typedef __bf16 rbf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void split_bf16(const float* x, rbf16x8& hi, rbf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    hi[e] = (__bf16)x[e];
+    lo[e] = (__bf16)(x[e] - (float)hi[e]);
+  }
+}
+__device__ __forceinline__ f32x4 logit_step_x3(f32x4 acc, rbf16x8 ah, rbf16x8 al, rbf16x8 bh, rbf16x8 bl) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+}
+// One 16 x 16 tile with the operands in memory as fp32: lane (col, grp) of
+// the tile holds row col of A and of B, channels k0 + 8 grp .. + 7 of each
+// 32-channel step; get(c) returns the fp32 piece of channels c..c+3 of its A
+// (geta) / B (getb) row (zero past C). Returns rows 4grp..4grp+3 at column
+// col, as logit_tile.
+template <typename GetA, typename GetB>
+__device__ __forceinline__ f32x4 logit_tile_x3(int grp, int C, GetA geta, GetB getb) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  uint4 a0 = geta(8 * grp), a1 = geta(8 * grp + 4), b0 = getb(8 * grp), b1 = getb(8 * grp + 4);
+  for (int k0 = 0; k0 < C; k0 += 32) {
+    const uint4 ca0 = a0, ca1 = a1, cb0 = b0, cb1 = b1;
+    if (k0 + 32 < C) {  // the next step in flight
+      a0 = geta(k0 + 32 + 8 * grp);
+      a1 = geta(k0 + 32 + 8 * grp + 4);
+      b0 = getb(k0 + 32 + 8 * grp);
+      b1 = getb(k0 + 32 + 8 * grp + 4);
+    }
+    const float fa[8] = {__uint_as_float(ca0.x), __uint_as_float(ca0.y), __uint_as_float(ca0.z), __uint_as_float(ca0.w),
+                         __uint_as_float(ca1.x), __uint_as_float(ca1.y), __uint_as_float(ca1.z), __uint_as_float(ca1.w)};
+    const float fb[8] = {__uint_as_float(cb0.x), __uint_as_float(cb0.y), __uint_as_float(cb0.z), __uint_as_float(cb0.w),
+                         __uint_as_float(cb1.x), __uint_as_float(cb1.y), __uint_as_float(cb1.z), __uint_as_float(cb1.w)};
+    rbf16x8 ah, al, bh, bl;
+    split_bf16(fa, ah, al);
+    split_bf16(fb, bh, bl);
+    acc = logit_step_x3(acc, ah, al, bh, bl);
+  }
+  return acc;
+}
+
+// Top-k of rows i0, i0 + step, ... (four at a time) of the logit block
+// logit[row][RP] (rows past nrows skipped): each lane ranks its candidate's
+// key against all R others through kw (this wave's [4][64] key buffer) and
+// the lanes of rank < topk hand their index to emit(row, rank, index).
+template <typename Emit>
+__device__ __forceinline__ void rank_rows(const float* logit, int RP, int R, int nrows, int i0,
+                                          int step, int topk, uint64_t* kw, int lane, Emit emit) {
+  const int s_rd = min(lane, R - 1);
+  const int R2 = (R + 1) & ~1;
+  for (; i0 < nrows; i0 += 4 * step) {
+    uint64_t key[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = i0 + q * step;
+      const bool ok = lane < R && i < nrows;
+      key[q] = ok ? route_key(logit[min(i, nrows - 1) * RP + s_rd], lane) : 0ull;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // the previous group's reads of kw are done
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int q = 0; q < 4; ++q) kw[q * 64 + lane] = key[q];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // every real key is nonzero and the keys past R are 0, so the pairs
+    // may run over the padded row
+    int rank[4] = {0, 0, 0, 0};
+#pragma unroll 4
+    for (int s2 = 0; s2 < R2; s2 += 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 two = *reinterpret_cast<const uint4*>(kw + q * 64 + s2);  // keys s2, s2+1
+        const uint64_t k0 = ((uint64_t)two.y << 32) | two.x;
+        const uint64_t k1 = ((uint64_t)two.w << 32) | two.z;
+        rank[q] += (k0 > key[q]) + (k1 > key[q]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = i0 + q * step;
+      if (key[q] != 0ull && rank[q] < topk) emit(i, rank[q], lane);
+    }
+  }
+}
+
+}  // namespace route
+}  // namespace bra

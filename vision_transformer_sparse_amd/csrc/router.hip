@@ -7,14 +7,15 @@
 //
 // Each shape is served by one kernel, in a fixed accumulation order, so its
 // logits (and routes) are reproducible bit for bit:
-//  * R <= 64 (route_kernel): affinities on fp32 matrix cores
-//    (v_mfma_f32_16x16x4_f32: fp32 operands, fp32 accumulation). One
-//    workgroup per 16 query rows of one image, one wave per 16-column tile.
-//    Lane (i, g) of a tile takes the 16-byte pieces at channels 16j+4g of
-//    row i of its A (Q^r) and B (K^r) operands -- the same channels on both
-//    sides -- straight from memory with buffer loads (pieces past C read as
-//    zero), 64 channels per batch with the next batch in flight. The scaled
-//    logits go to LDS.
+//  * R <= 64 (route_kernel): affinities on the bf16 matrix cores with split
+//    operands (x = hi + lo, products hi.lo + lo.hi + hi.hi accumulated in
+//    fp32; see route_common.h). One workgroup per 16 query rows of one
+//    image, one wave per 16-column tile. Lane (i, g) of a tile takes
+//    channels k0+8g..+7 of row i of its A (Q^r) and B (K^r) operands -- the
+//    same channels on both sides -- straight from memory with buffer loads
+//    (pieces past C read as zero), 32 channels per step with the next step
+//    in flight. The scaled logits go to LDS. The attention kernel for 4x4
+//    regions routes its own images with the same tile code.
 //  * R > 64 (route_wide_kernel): one workgroup per 4 query rows, one wave per
 //    64 candidates; each lane streams its own candidate's K^r row from L2
 //    into registers (double-buffered 32-channel batches) and reads the 4 Q^r
@@ -32,20 +33,12 @@
 // (DPP row reductions, then the last lane's value) emit the winners in
 // descending order.
 #include "bra_internal.h"
+#include "route_common.h"
 
 namespace bra {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kChunk = 64;  // channels per load batch: 4 pieces of A and 4 of B per lane
-
-__device__ __forceinline__ uint64_t route_key(float a, int s) {
-  if (a == 0.0f) a = 0.0f;  // -0 and +0 are the same logit
-  uint32_t u = __float_as_uint(a);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // order-preserving map to unsigned
-  return ((uint64_t)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)s);
-}
+using namespace route;
 
 // max of x and the DPP-moved copy of x (lanes the pattern leaves out keep x)
 template <int CTRL, int ROW_MASK>
@@ -79,92 +72,6 @@ __host__ __device__ inline size_t route_lds(int R) {
          (size_t)col_tiles(R) * 4 * 64 * sizeof(uint64_t);
 }
 
-// One 16 x 16 logit tile: rows r0.., columns 16ct.. of (Q^r K^r^T) * scale,
-// lane (col, grp) returning rows 4grp..4grp+3 at column col. get(row, c)
-// returns the 16-byte piece of channels c..c+3 of a Q^r (a) / K^r (b) row
-// (rows clamped to R-1, pieces past C zero). The fp32 MFMA sequence is the
-// same wherever the operands come from, so the logits are too.
-template <typename GetA, typename GetB>
-__device__ __forceinline__ f32x4 logit_tile(int col, int grp, int C, GetA geta, GetB getb) {
-  uint4 a[4], b[4], an[4], bn[4];
-  auto fetch = [&](int c0, uint4* aa, uint4* bb) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = c0 + 16 * j + 4 * grp;
-      aa[j] = geta(c);
-      bb[j] = getb(c);
-    }
-  };
-  auto mfma4 = [&](f32x4 acc) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].x), __uint_as_float(b[j].x), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].y), __uint_as_float(b[j].y), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].z), __uint_as_float(b[j].z), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j].w), __uint_as_float(b[j].w), acc, 0, 0, 0);
-    }
-    return acc;
-  };
-  // the next batch is always in flight while one is multiplied (the last
-  // batch is peeled off, so no branch guards the loads)
-  fetch(0, a, b);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  int c0 = 0;
-  for (; c0 + kChunk < C; c0 += kChunk) {
-    fetch(c0 + kChunk, an, bn);
-    acc = mfma4(acc);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { a[j] = an[j]; b[j] = bn[j]; }
-  }
-  return mfma4(acc);
-}
-
-// Top-k of rows i0, i0 + step, ... (four at a time) of the logit block
-// logit[row][RP] (rows past nrows skipped): each lane ranks its candidate's
-// key against all R others through kw (this wave's [4][64] key buffer) and
-// the lanes of rank < topk write their index; row i goes to out(i).
-template <typename Out>
-__device__ __forceinline__ void rank_rows(const float* logit, int RP, int R, int nrows, int i0,
-                                          int step, int topk, uint64_t* kw, int lane, Out out) {
-  const int s_rd = min(lane, R - 1);
-  const int R2 = (R + 1) & ~1;
-  for (; i0 < nrows; i0 += 4 * step) {
-    uint64_t key[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = i0 + q * step;
-      const bool ok = lane < R && i < nrows;
-      key[q] = ok ? route_key(logit[min(i, nrows - 1) * RP + s_rd], lane) : 0ull;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();  // the previous group's reads of kw are done
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int q = 0; q < 4; ++q) kw[q * 64 + lane] = key[q];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // every real key is nonzero and the keys past R are 0, so the pairs
-    // may run over the padded row
-    int rank[4] = {0, 0, 0, 0};
-#pragma unroll 4
-    for (int s2 = 0; s2 < R2; s2 += 2) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 two = *reinterpret_cast<const uint4*>(kw + q * 64 + s2);  // keys s2, s2+1
-        const uint64_t k0 = ((uint64_t)two.y << 32) | two.x;
-        const uint64_t k1 = ((uint64_t)two.w << 32) | two.z;
-        rank[q] += (k0 > key[q]) + (k1 > key[q]);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = i0 + q * step;
-      if (key[q] != 0ull && rank[q] < topk) out(i)[rank[q]] = lane;
-    }
-  }
-}
-
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ qr,
                                                     const float* __restrict__ kr, int R, int C,
                                                     int topk, float scale,
@@ -187,8 +94,8 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ qr
   // ---- affinities: wave ct computes column tile ct
   for (int ct = wave; ct < CT; ct += waves) {
     const uint32_t krow = (uint32_t)min(16 * ct + col, R - 1) * C * 4;
-    const f32x4 acc = logit_tile(
-        col, grp, C, [&](int c) { return ld16(qb, c < C ? qrow + 4 * c : kOut); },
+    const f32x4 acc = logit_tile_x3(
+        grp, C, [&](int c) { return ld16(qb, c < C ? qrow + 4 * c : kOut); },
         [&](int c) { return ld16(kb, c < C ? krow + 4 * c : kOut); });
     // lane (col, grp) holds rows 4grp..4grp+3 of the tile at column col
 #pragma unroll
@@ -198,7 +105,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ qr
 
   // ---- rank selection, rows wave, wave + waves, ... in groups of four
   rank_rows(logit, RP, R, min(16, R - r0), wave, waves, topk, keys + (size_t)wave * 4 * 64, lane,
-            [&](int i) { return route + ((size_t)n * R + r0 + i) * topk; });
+            [&](int i, int k, int s) { route[((size_t)n * R + r0 + i) * topk + k] = s; });
 }
 
 hipError_t launch_small(const float* qr, const float* kr, int N, int R, int C, int topk,
