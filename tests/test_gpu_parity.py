@@ -232,11 +232,11 @@ def test_host_pointer_rejected(gpu_lib):
     assert lib.bra_lce(hp, hp, None, 1, 8, 8, 32, 0, hp) == -7
 
 
-@pytest.mark.parametrize("ci,routes", [(2, 3), (1, 0)])
-def test_profile_counts(gpu_lib, ci, routes):
+@pytest.mark.parametrize("ci,pools,routes", [(2, 3, 3), (1, 0, 0)])
+def test_profile_counts(gpu_lib, ci, pools, routes):
     """One pool, route and attention launch per forward; with 4x4 regions
-    (the classification stage-2 shape) the attention kernel routes the images
-    itself, so no route kernel runs."""
+    (the classification stage-2 shape) one kernel pools, routes and attends,
+    so neither the pool nor the route kernel runs."""
     cfg = CONFIGS[ci]
     inp = draw_config(cfg, N=4)
     args = [dev(inp[x], cfg.dtype) for x in ("q", "k", "v", "lce_w", "lce_b")]
@@ -246,7 +246,7 @@ def test_profile_counts(gpu_lib, ci, routes):
         gpu_lib.forward(*args, cfg.heads, cfg.S, cfg.topk)
     rec = gpu_lib.profile_read()
     gpu_lib.profile_begin(())
-    assert rec["pool"][1] == 3 and rec["route"][1] == routes and rec["attn"][1] == 3
+    assert rec["pool"][1] == pools and rec["route"][1] == routes and rec["attn"][1] == 3
     assert rec["attn"][0] > 0
 
 

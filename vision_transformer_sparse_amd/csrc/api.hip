@@ -27,13 +27,15 @@ hipError_t launch_attend_region(const void* q, const void* k, const void* v, con
                                 hipStream_t st);
 bool image_kernel_supports(const Shape& s);
 bool image_kernel_routes(const Shape& s);
-// qr, kr, route_out non-null (4x4 regions, image_kernel_routes): the kernel
-// computes the routes itself from the region means and reports them to
-// route_out; route is then unused
 hipError_t launch_attend_image(const void* q, const void* k, const void* v, const uint32_t* wpk,
                                const void* b, const int32_t* route, const Shape& s, void* out,
-                               hipStream_t st, const float* qr = nullptr, const float* kr = nullptr,
-                               int32_t* route_out = nullptr);
+                               hipStream_t st);
+// The whole forward in one kernel (4x4 regions, image_kernel_routes): region
+// means, routes (reported to route_out), attention and LCE from the weights
+// as given; no workspace
+hipError_t launch_forward_image(const void* q, const void* k, const void* v, const void* lce_w,
+                                const void* b, const Shape& s, void* out, int32_t* route_out,
+                                hipStream_t st);
 bool tile_kernel_supports(const Shape& s);
 bool f32_kernel_supports(const Shape& s);
 hipError_t launch_attend_f32(const void* q, const void* k, const void* v, const void* w,
@@ -267,6 +269,17 @@ int bra_forward(const void* q, const void* k, const void* v, const void* lce_w,
   if (rc) return rc;
   rc = check_ptrs({q, k, v, lce_w, lce_b, out, route_idx});
   if (rc) return rc;
+  hipStream_t st = g_stream;
+  hipError_t e;
+  if (dtype == BRA_BF16 && bra::image_kernel_routes(s)) {
+    // one kernel: it pools and routes its own images (the route kernel's
+    // logit and selection code) and reports the routes to route_idx
+    {
+      ProfScope ps(BRA_K_ATTN, st);
+      e = bra::launch_forward_image(q, k, v, lce_w, lce_b, s, out, route_idx, st);
+    }
+    return e == hipSuccess ? BRA_OK : hip_fail(e);
+  }
   std::lock_guard<std::mutex> lk(g_ws_mutex);
   const WsLayout wl = ws_layout(N, C, S);
   void* ws = nullptr;
@@ -275,22 +288,11 @@ int bra_forward(const void* q, const void* k, const void* v, const void* lce_w,
   float* qr = static_cast<float*>(ws);
   float* kr = qr + (size_t)N * s.R * C;
   uint32_t* wpk = dtype == BRA_BF16 ? reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + wl.wpk) : nullptr;
-  hipStream_t st = g_stream;
-  hipError_t e;
   {
     ProfScope ps(BRA_K_POOL, st);
     e = bra::launch_region_pool(q, k, s, dtype, qr, kr, lce_w, wpk, st);
   }
   if (e != hipSuccess) return hip_fail(e);
-  if (dtype == BRA_BF16 && bra::image_kernel_routes(s)) {
-    // the attention kernel routes its own images (same code as the route
-    // kernel, so the same routes) and reports them to route_idx
-    {
-      ProfScope ps(BRA_K_ATTN, st);
-      e = bra::launch_attend_image(q, k, v, wpk, lce_b, nullptr, s, out, st, qr, kr, route_idx);
-    }
-    return e == hipSuccess ? BRA_OK : hip_fail(e);
-  }
   {
     ProfScope ps(BRA_K_ROUTE, st);
     e = bra::launch_route(qr, kr, N, s.R, C, topk, route_idx, st);

@@ -96,10 +96,9 @@ struct ImageArgs {
   uint16_t* out;
   int N, H, W, C, heads, S, topk;
   float qscale;            // head_dim^-1/2 * log2(e)
-  // routing inside the kernel (4x4 regions): region means, C^-1/2, and where
-  // the routes are reported
-  const float* qr;
-  const float* kr;
+  // the whole forward inside the kernel (4x4 regions): the raw LCE weights
+  // [C][5][5], where the routes are reported, and C^-1/2
+  const uint16_t* lw;
   int32_t* route_out;
   float rscale;
 };
@@ -393,6 +392,7 @@ constexpr int kNW4 = 16;                       // waves
 constexpr int kThreads4 = 64 * kNW4;
 constexpr int kPF = 7;                         // prefetch pieces per lane
 constexpr int kWPieces = kLceToepDwords / 4;   // a head's Toeplitz LCE blocks in 16-byte pieces
+constexpr int kWRawPieces = 32 * 25 * 2 / 16;  // a head's 5x5 weights as given, in 16-byte pieces
 constexpr int kVPitch4 = kVRow4 / 2 * 128;     // bytes per bordered-V row: 16 pixel pairs x 32 channels
 
 // Bordered V row Y, pixel pair P, channel c: the dword (pixel 2P, pixel 2P+1)
@@ -414,10 +414,9 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Routing inside the kernel (C <= 128): the region means of two images, in
-// kRouteSlots 16-byte pieces a lane, then in LDS as split bf16 rows
+// Routing inside the kernel (C <= 128): the region means, as split bf16 rows
+// in LDS
 constexpr int kRouteMaxC = 128;
-constexpr int kRouteSlots = 4;
 // LDS the in-kernel routing borrows from the weight and hand-over areas: the
 // logits [R][16 ceil(R/16) + 1] fp32 and the partial top-4 lists
 __host__ __device__ inline size_t route_scratch(int R) {
@@ -459,6 +458,7 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
   u32x4 pf[kPF];
   uint32_t rq = 0;
   const int remK = 4 * HW - FK * kThreads4;
+  constexpr int kWP = FUSE ? kWRawPieces : kWPieces;  // weight pieces
   auto route_off = [&](int i) {  // byte offset of route slot i's entry, or kOut
     const int r = i / RSTR, p = i - r * RSTR;
     return i < nroute && p < topk ? (uint32_t)(r * topk + p) * 4 : kOut;
@@ -480,7 +480,10 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
     const Rsrc kb = rsrc(a.k + img, img_bytes), vb = rsrc(a.v + img, img_bytes);
     const char* kp = reinterpret_cast<const char*>(a.k + img);
     const char* vp = reinterpret_cast<const char*>(a.v + img);
-    const char* wp = reinterpret_cast<const char*>(a.wpk + lce_toep_offset(C) + (size_t)h * kLceToepDwords);
+    // the head's LCE weights: as given (built into Toeplitz blocks in LDS), or
+    // packed beforehand
+    const char* wp = FUSE ? reinterpret_cast<const char*>(a.lw + (size_t)h * 32 * 25)
+                          : reinterpret_cast<const char*>(a.wpk + lce_toep_offset(C) + (size_t)h * kLceToepDwords);
     int keep = real ? 1 : 0;  // a lane value: the selects below stay selects, not branches
     asm volatile("" : "+v"(keep));
     const uint32_t lb = keep ? (uint32_t)(tid >> 2) * pixb + (uint32_t)(tid & 3) * 16 : kOut;
@@ -498,7 +501,7 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
         // one load from a per-lane address (a tensor per lane); pieces past
         // the operands, and every piece of a discarded prefetch, re-read the
         // first K piece of the unit
-        const char* src = !keep ? kp : isk ? kp + po : isv ? vp + po : iw < kWPieces ? wp + (size_t)iw * 16 : kp;
+        const char* src = !keep ? kp : isk ? kp + po : isv ? vp + po : iw < kWP ? wp + (size_t)iw * 16 : kp;
         pf[j] = *reinterpret_cast<const u32x4*>(src);
       }
     }
@@ -557,7 +560,7 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
         const int iw = m - 2 * remK;
         if (isk) k_put(i2 >> 2, c, pf[j]);
         if (isv) v_put(i2 >> 2, c, pf[j]);  // partners share the branch (8-aligned pairs)
-        if (!isk && !isv && iw < kWPieces) *reinterpret_cast<u32x4*>(smem + lay.w + iw * 16) = pf[j];
+        if (!isk && !isv && iw < kWP) *reinterpret_cast<u32x4*>(smem + (FUSE ? lay.x : lay.w) + iw * 16) = pf[j];
       }
     }
     if (with_routes && tid < nroute) route_put(tid, (int)rq);
@@ -575,6 +578,14 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
     }
   };
 
+
+  // FUSE: the head's Toeplitz LCE blocks, built from the weights that commit
+  // left in the hand-over area (between two barriers)
+  auto toep_build = [&]() {
+    const uint16_t* raw = reinterpret_cast<const uint16_t*>(smem + lay.x);
+    uint32_t* wl = reinterpret_cast<uint32_t*>(smem + lay.w);
+    for (int e = tid; e < kLceToepDwords; e += kThreads4) wl[e] = lce_toep_dword(raw, e);
+  };
 
   // the V border (two pixels around the image) stays zero for every unit:
   // rows 0, 1, H + 2, H + 3 whole, and pixel pairs 0 and W / 2 + 1 of the rest
@@ -638,52 +649,115 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
   };
   const int u0 = unit_of(0);
   if constexpr (FUSE) {
-    // ---- the image's routes, from its region means. The Q^r and K^r rows
-    // are loaded into the K/V area first, split into bf16 hi and lo rows
-    // as the route kernel splits them (rows C + 8 apart to spread the banks),
-    // and wave w computes logit tile (w / CT, w % CT) with the route kernel's
-    // split-bf16 steps, from LDS. The top k (k <= 4) of a row is found by a
-    // lane scanning candidates in index order (four waves a quarter each, then
-    // merged), which picks what the route kernel's ranks pick. The routes go
-    // straight to the route table (both units share it); the workgroup with
-    // head 0 reports them. The logits and partial lists use the weight and
-    // hand-over areas; all of it is overwritten when the first unit is staged.
+    // ---- the image's routes, from q and k. The region means Q^r and K^r
+    // are computed here and written to the K/V area as bf16 hi and lo rows,
+    // split as the route kernel splits them (rows C + 8 apart to spread the
+    // banks); wave w computes logit tile (w / CT, w % CT) with the route
+    // kernel's split-bf16 steps, from LDS. The top k (k <= 4) of a row is
+    // found by a lane scanning candidates in index order (four waves a quarter
+    // each, then merged), which picks what the route kernel's ranks pick from
+    // the same logits. The routes go straight to the route table (both units
+    // share it); the workgroup with head 0 reports them. The logits and
+    // partial lists use the weight and hand-over areas; all of it is
+    // overwritten when the first unit is staged.
     const int CT = (R + 15) / 16, RP = 16 * CT + 1;  // odd pitch: a lane per row reads without conflicts
     float* logits = reinterpret_cast<float*>(smem + lay.w);            // [R][RP]
     uint32_t* part = reinterpret_cast<uint32_t*>(logits + R * RP);      // [4][8][64] partial top 4
     const int rt = wave / CT, ct = wave - rt * CT;
     const bool has_tile = wave < CT * CT;
     const int n0 = u0 / a.heads;
-    const int c4n = C / 4, mpieces = R * c4n;  // 16-byte pieces of one matrix
     const int RS = C + 8;                      // bf16 per LDS row
     // matrix m (0: Q^r, 1: K^r), part 0 (hi) / 1 (lo): R rows of RS bf16
     auto mat_lds = [&](int m, int part) { return (__bf16*)(smem + lay.k) + (size_t)(2 * m + part) * R * RS; };
-    u32x4 ro[kRouteSlots];
+    // The means over all C channels, from q and k: a task is one region of
+    // q (task < R) or of k (task - R); the lane sums 16-byte chunk pc
+    // (channels 8 pc..8 pc + 7) of tasks psl and psl + slots in fp32, in the
+    // pool kernel's order: each region column top to bottom, then the four
+    // column sums left to right (so both give the same means, bit for bit).
+    // Its 32 loads go out as eight batches of four (one region column),
+    // three batches in flight. (Lanes without a task read the image's first
+    // piece and drop it.)
+    const int nch = C / 8, slots = kThreads4 / nch;
+    const int pc = tid % nch, psl = tid / nch;
+    const char* qimg = reinterpret_cast<const char*>(a.q + (size_t)n0 * HW * C);
+    const char* kimg = reinterpret_cast<const char*>(a.k + (size_t)n0 * HW * C);
+    const char* tb[2];
+    uint32_t rstep[2], cstep[2];
+    bool tok[2];
+    int tmat[2], treg[2];
 #pragma unroll
-    for (int j = 0; j < kRouteSlots; ++j) {
-      const int P = tid + kThreads4 * j, m = P / mpieces, pm = P - m * mpieces;
-      const float* src = m < 2 ? (m ? a.kr : a.qr) + (size_t)n0 * R * C + (size_t)pm * 4 : a.qr;  // (past the end: piece 0 again)
-      ro[j] = *reinterpret_cast<const u32x4*>(src);
+    for (int p = 0; p < 2; ++p) {
+      const int tk = psl + slots * p;
+      tok[p] = psl < slots && tk < 2 * R;
+      tmat[p] = tk >= R ? 1 : 0;
+      treg[p] = tk - tmat[p] * R;
+      const int js = treg[p] / S, is = treg[p] - js * S;
+      tb[p] = tok[p] ? (tmat[p] ? kimg : qimg) + (size_t)(4 * js * W + 4 * is) * pixb + (size_t)pc * 16 : qimg;
+      rstep[p] = tok[p] ? (uint32_t)W * pixb : 0u;
+      cstep[p] = tok[p] ? pixb : 0u;
     }
-    // (the means are staged before the K/V prefetch is issued: in flight
-    // together with it they would arrive as late as it does)
+    float acc[2][8];
 #pragma unroll
-    for (int j = 0; j < kRouteSlots; ++j) {
-      const int P = tid + kThreads4 * j, m = P / mpieces, pm = P - m * mpieces;
-      const int row = pm / c4n, c4 = pm - row * c4n;
-      if (m < 2) {
-        typedef __bf16 b4 __attribute__((ext_vector_type(4)));
-        b4 hi, lo;
+    for (int p = 0; p < 2; ++p)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {  // as route::split_bf16
-          const float x = __uint_as_float(ro[j][e]);
+      for (int e = 0; e < 8; ++e) acc[p][e] = 0.f;
+    auto pool_issue = [&](int i, u32x4* b) {  // batch i: task i / 4, region column i % 4
+      const int p = i >> 2;
+      const char* src = tb[p] + (i & 3) * cstep[p];
+#pragma unroll
+      for (int py = 0; py < 4; ++py) b[py] = *reinterpret_cast<const u32x4*>(src + py * rstep[p]);
+    };
+    auto pool_add = [&](int i, const u32x4* b) {
+      float col[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) col[e] = 0.f;
+#pragma unroll
+      for (int py = 0; py < 4; ++py)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          col[2 * e] += bf16_lo(b[py][e]);
+          col[2 * e + 1] += bf16_hi(b[py][e]);
+        }
+      float* sm = acc[i >> 2];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm[e] += col[e];
+    };
+    auto pool_put = [&](int p) {  // mean -> hi and lo bf16 rows (as route::split_bf16)
+      // (the sums taken on every path: sunk into the branch below, they
+      // would leave the task's loads unretired for lanes without a task)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(acc[p][e]));
+      if (tok[p]) {
+        typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+        b8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = acc[p][e] * (1.0f / (RH * RW));  // exact: a power of two
           hi[e] = (__bf16)x;
           lo[e] = (__bf16)(x - (float)hi[e]);
         }
-        *reinterpret_cast<b4*>(mat_lds(m, 0) + row * RS + 4 * c4) = hi;
-        *reinterpret_cast<b4*>(mat_lds(m, 1) + row * RS + 4 * c4) = lo;
+        *reinterpret_cast<b8*>(mat_lds(tmat[p], 0) + treg[p] * RS + 8 * pc) = hi;
+        *reinterpret_cast<b8*>(mat_lds(tmat[p], 1) + treg[p] * RS + 8 * pc) = lo;
       }
+    };
+    u32x4 pbuf[3][4];
+    pool_issue(0, pbuf[0]);
+    pool_issue(1, pbuf[1]);
+    pool_issue(2, pbuf[2]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      asm volatile("" ::: "memory");  // each batch issued where it stands
+      pool_add(i, pbuf[i % 3]);
+      if (i == 3) pool_put(0);
+      if (i + 3 < 8) pool_issue(i + 3, pbuf[i % 3]);
     }
+    pool_put(1);
+    // the first unit's K/V prefetch goes out now; the routing below runs
+    // while it is in flight
+    asm volatile("" ::: "memory");
+    prefetch(u0, true);
+    qrows(u0, 0);
+    asm volatile("" ::: "memory");
     lds_barrier();  // the means in LDS
     {  // logit tile (rt, ct): the route kernel's steps in its order (C a multiple of 32)
       const int qrow = min(16 * rt + col, R - 1), krow = min(16 * ct + col, R - 1);
@@ -705,12 +779,6 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
         }
       }
     }
-    // the K/V prefetch goes out now; the rank selection below runs while it
-    // is in flight
-    asm volatile("" ::: "memory");
-    prefetch(u0, true);
-    qrows(u0, 0);
-    asm volatile("" ::: "memory");
     lds_barrier();  // the logits in LDS
     // top-k (k <= 4), a lane per row: wave q < 4 keeps the top 4 of candidates
     // [q cq, (q + 1) cq) of every row, in index order (cq <= 16: R <= 64)
@@ -761,6 +829,8 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
     lds_barrier();  // every read of the means and logits done before staging
     zero_border();
     commit(u0, false);
+    lds_barrier();
+    toep_build();
   } else {
     zero_border();
     prefetch(u0, true);
@@ -941,6 +1011,10 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
       asm volatile("" ::: "memory");  // issued here, ahead of the staging below
       lds_barrier();  // every wave is done with this unit's LDS
       commit(unit_of(it + 1), !FUSE);  // (two heads of one image share the routes)
+      if constexpr (FUSE) {
+        lds_barrier();
+        toep_build();
+      }
       lds_barrier();  // the next unit staged
     } else {
       // the discarded loads of the last unit retired as well: no path around
@@ -986,50 +1060,61 @@ bool image_kernel_routes(const Shape& s) {
   if (s.topk > 4) return false;                            // top 4 by insertion
   const int units = s.N * s.heads;
   if (units / 2 > image4_grid(units)) return false;        // a workgroup per head pair, in one round
-  if (2 * s.R * (s.C / 4) > kRouteSlots * kThreads4) return false;  // the means' pieces a lane
+  if (2 * s.R > 2 * (kThreads4 / (s.C / 8))) return false;  // the pooling's two tasks a lane
   const ImgLds l = img_lds(4, kNW4, s.H, s.W, s.R, s.topk);
   if ((size_t)4 * s.R * (s.C + 8) * 2 > l.rk - l.k) return false;  // the split means in the K/V area
+  if ((size_t)kWRawPieces * 16 > l.sink - l.x) return false;        // the raw weights in the hand-over area
   return route_scratch(s.R) <= l.sink - l.w;               // the weight and hand-over areas
 }
 
-hipError_t launch_attend_image(const void* q, const void* k, const void* v, const uint32_t* wpk,
-                               const void* b, const int32_t* route, const Shape& s, void* out,
-                               hipStream_t st, const float* qr, const float* kr, int32_t* route_out) {
-  ImageArgs a;
+static ImageArgs image_args(const void* q, const void* k, const void* v, const void* b,
+                            const Shape& s, void* out) {
+  ImageArgs a = {};
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
-  a.wpk = wpk; a.b = (const uint16_t*)b; a.route = route; a.out = (uint16_t*)out;
+  a.b = (const uint16_t*)b; a.out = (uint16_t*)out;
   a.N = s.N; a.H = s.H; a.W = s.W; a.C = s.C; a.heads = s.heads; a.S = s.S; a.topk = s.topk;
   a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
-  a.qr = qr; a.kr = kr; a.route_out = route_out;
   a.rscale = (float)(1.0 / __builtin_sqrt((double)s.C));  // as the route kernels
+  return a;
+}
+
+#define BRA_IMG4(FKV, FU) launch(attn_image4_kernel<FKV, FU>, g, blk, lds, st, a)
+#define BRA_IMG4_FK(FU)                  \
+  switch (4 * s.H * s.W / kThreads4) {   \
+    case 0: BRA_IMG4(0, FU); break;      \
+    case 1: BRA_IMG4(1, FU); break;      \
+    case 2: BRA_IMG4(2, FU); break;      \
+    default: BRA_IMG4(3, FU); break;     \
+  }
+
+hipError_t launch_attend_image(const void* q, const void* k, const void* v, const uint32_t* wpk,
+                               const void* b, const int32_t* route, const Shape& s, void* out,
+                               hipStream_t st) {
+  ImageArgs a = image_args(q, k, v, b, s, out);
+  a.wpk = wpk; a.route = route;
   const int units = s.N * s.heads;
   if (s.rh == 2) {
     launch(attn_image2_kernel<kImage2Waves>, dim3((unsigned)units), dim3(64 * kImage2Waves),
            img_lds(2, kImage2Waves, s.H, s.W, s.R, s.topk).total, st, a);
   } else {
-    const int grid = qr ? units / 2 : image4_grid(units);  // routing in the kernel: a workgroup per head pair
     const size_t lds = img_lds(4, kNW4, s.H, s.W, s.R, s.topk).total;
-    const dim3 g((unsigned)grid), blk(kThreads4);
-#define BRA_IMG4(FKV, FU) launch(attn_image4_kernel<FKV, FU>, g, blk, lds, st, a)
-    const int fk = 4 * s.H * s.W / kThreads4;
-    if (qr) {
-      switch (fk) {
-        case 0: BRA_IMG4(0, true); break;
-        case 1: BRA_IMG4(1, true); break;
-        case 2: BRA_IMG4(2, true); break;
-        default: BRA_IMG4(3, true); break;
-      }
-    } else {
-      switch (fk) {
-        case 0: BRA_IMG4(0, false); break;
-        case 1: BRA_IMG4(1, false); break;
-        case 2: BRA_IMG4(2, false); break;
-        default: BRA_IMG4(3, false); break;
-      }
-    }
-#undef BRA_IMG4
+    const dim3 g((unsigned)image4_grid(units)), blk(kThreads4);
+    BRA_IMG4_FK(false)
   }
   return hipGetLastError();
 }
+
+hipError_t launch_forward_image(const void* q, const void* k, const void* v, const void* lce_w,
+                                const void* b, const Shape& s, void* out, int32_t* route_out,
+                                hipStream_t st) {
+  ImageArgs a = image_args(q, k, v, b, s, out);
+  a.lw = (const uint16_t*)lce_w; a.route_out = route_out;
+  const size_t lds = img_lds(4, kNW4, s.H, s.W, s.R, s.topk).total;
+  const dim3 g((unsigned)(s.N * s.heads / 2)), blk(kThreads4);  // a workgroup per head pair
+  BRA_IMG4_FK(true)
+  return hipGetLastError();
+}
+#undef BRA_IMG4_FK
+#undef BRA_IMG4
 
 }  // namespace bra

@@ -197,6 +197,15 @@ __host__ __device__ inline int lce_pack_items(int C) { return 15 * C + 25 * (C /
 __device__ __forceinline__ uint32_t lce_toep_entry(const uint16_t* __restrict__ lw, int c, int dy, int tap) {
   return tap >= 0 && tap < 5 ? (uint32_t)lw[(size_t)c * 25 + dy * 5 + tap] : 0u;
 }
+// dword e (< kLceToepDwords) of one head's Toeplitz blocks, from that head's
+// 32 channels of 5x5 weights (global memory or LDS)
+__device__ __forceinline__ uint32_t lce_toep_dword(const uint16_t* __restrict__ lw_head, int e) {
+  const int f = 2 * e;  // bf16 index, even
+  const int k = f & 3, j = (f >> 2) & 3, b = (f >> 4) & 15, ch = (f >> 8) & 1;
+  const int dy = (f >> 9) % 5, h = (f >> 9) / 5;
+  const int c = 2 * b + h, tap = 4 * ch + k - j;
+  return lce_toep_entry(lw_head, c, dy, tap) | (lce_toep_entry(lw_head, c, dy, tap + 1) << 16);
+}
 __device__ __forceinline__ void pack_lce_item(const uint16_t* __restrict__ lw, int C, int e,
                                               uint32_t* __restrict__ wpk) {
   if (e < 15 * C) {
@@ -214,12 +223,8 @@ __device__ __forceinline__ void pack_lce_item(const uint16_t* __restrict__ lw, i
     wpk[30 * C + e2] = (uint32_t)lw[(size_t)(2 * p) * 25 + t] | ((uint32_t)lw[(size_t)(2 * p + 1) * 25 + t] << 16);
   } else {
     const int e3 = e - 15 * C - 25 * (C / 2);  // dword of the Toeplitz section
-    const int head = e3 / kLceToepDwords, f = 2 * (e3 - head * kLceToepDwords);  // bf16 index, even
-    const int k = f & 3, j = (f >> 2) & 3, b = (f >> 4) & 15, ch = (f >> 8) & 1;
-    const int dy = (f >> 9) % 5, h = (f >> 9) / 5;
-    const int c = 32 * head + 2 * b + h;
-    const int tap = 4 * ch + k - j;
-    wpk[lce_toep_offset(C) + e3] = lce_toep_entry(lw, c, dy, tap) | (lce_toep_entry(lw, c, dy, tap + 1) << 16);
+    const int head = e3 / kLceToepDwords;
+    wpk[lce_toep_offset(C) + e3] = lce_toep_dword(lw + (size_t)head * 32 * 25, e3 - head * kLceToepDwords);
   }
 }
 

@@ -105,14 +105,23 @@ hipError_t launch_t(const void* q, const void* k, const Shape& s, float* qr, flo
                     const void* lw, uint32_t* wpk, hipStream_t st) {
   constexpr int V = Vec16<T>::n;
   const int nchunk = s.C / V;                 // <= 256 (C <= 1024)
-  // threads: a multiple of 64 holding whole token lanes, aiming at <= 8 tokens per thread
-  int lanes_wanted = (s.T + 7) / 8;
-  int threads = nchunk * lanes_wanted;
-  threads = threads < 64 ? 64 : threads;
-  threads = threads > 256 ? 256 : threads;
-  threads = ((threads + 63) / 64) * 64;
-  int lanes = threads / nchunk;
-  if (lanes < 1) lanes = 1;
+  int threads, lanes;
+  if (s.rh == 4 && s.rw == 4 && nchunk * 4 <= 256) {
+    // 4x4 regions: a token lane per region column, so the sum runs down each
+    // column and then across the four columns -- the order the one-kernel
+    // forward pools in
+    lanes = 4;
+    threads = nchunk * 4;
+  } else {
+    // threads: a multiple of 64 holding whole token lanes, aiming at <= 8 tokens per thread
+    int lanes_wanted = (s.T + 7) / 8;
+    threads = nchunk * lanes_wanted;
+    threads = threads < 64 ? 64 : threads;
+    threads = threads > 256 ? 256 : threads;
+    threads = ((threads + 63) / 64) * 64;
+    lanes = threads / nchunk;
+    if (lanes < 1) lanes = 1;
+  }
   const int tpt = (s.T + lanes - 1) / lanes;  // tokens per thread (looped in batches of <= 8)
   const size_t lds = (size_t)2 * lanes * s.C * sizeof(float);
   dim3 grid((unsigned)(s.N * s.R)), block(threads);
