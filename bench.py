@@ -35,7 +35,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
 PROFILE_EVERY = 4
-ATTN_SOURCES = ("attn_region.hip", "attn_tile.hip", "attn_mfma.hip", "attn_valu.hip", "bra_internal.h")
+ATTN_SOURCES = ("attn_image.hip", "attn_region.hip", "attn_tile.hip", "attn_mfma.hip", "attn_valu.hip",
+                "attn_f32.hip", "bra_internal.h", "route_common.h")
 
 
 def algorithmic(cfg):

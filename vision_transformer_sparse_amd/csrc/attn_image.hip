@@ -419,9 +419,8 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr int kRouteMaxC = 128;
 // LDS the in-kernel routing borrows from the weight and hand-over areas: the
 // logits [R][16 ceil(R/16) + 1] fp32 and the partial top-4 lists
-__host__ __device__ inline size_t route_scratch(int R) {
-  return (size_t)R * (16 * ((R + 15) / 16) + 1) * 4 + (size_t)4 * 8 * 64 * 4;
-}
+__host__ __device__ inline size_t route_logits_bytes(int R) { return align16((size_t)R * (16 * ((R + 15) / 16) + 1) * 4); }
+__host__ __device__ inline size_t route_scratch(int R) { return route_logits_bytes(R) + (size_t)4 * 4 * 64 * 8; }
 
 // FK: whole K/V slot pairs of the prefetch (4 H W / 1024, rounded down);
 // FUSE: the kernel computes its units' routes from the region means (a
@@ -662,7 +661,6 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
     // overwritten when the first unit is staged.
     const int CT = (R + 15) / 16, RP = 16 * CT + 1;  // odd pitch: a lane per row reads without conflicts
     float* logits = reinterpret_cast<float*>(smem + lay.w);            // [R][RP]
-    uint32_t* part = reinterpret_cast<uint32_t*>(logits + R * RP);      // [4][8][64] partial top 4
     const int rt = wave / CT, ct = wave - rt * CT;
     const bool has_tile = wave < CT * CT;
     const int n0 = u0 / a.heads;
@@ -781,48 +779,35 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
     }
     lds_barrier();  // the logits in LDS
     // top-k (k <= 4), a lane per row: wave q < 4 keeps the top 4 of candidates
-    // [q cq, (q + 1) cq) of every row, in index order (cq <= 16: R <= 64)
+    // [q cq, (q + 1) cq) of every row (cq <= 16: R <= 64), as rank codes
     const int cq = (R + 3) / 4;
+    double* part = reinterpret_cast<double*>(smem + lay.w + route_logits_bytes(R));  // [4][4][64] partial top 4
     if (wave < 4) {
       const float* lg = logits + min(lane, R - 1) * RP + wave * cq;
       const int nc = min(R, (wave + 1) * cq) - wave * cq;
       uint32_t kv[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) kv[j] = j < nc ? route::key_u32(lg[j]) : 0u;  // all reads first
-      uint32_t t[4] = {0u, 0u, 0u, 0u};
-      int ix[4] = {0, 0, 0, 0};
+      double t[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int j = 0; j < 16; ++j) route::top4_insert(t, ix, kv[j], wave * cq + j);  // (key 0 never enters)
-      uint32_t* pw = part + (size_t)wave * 8 * 64 + lane;
+      for (int j = 0; j < 16; ++j) route::top4_code(t, route::rank_code(kv[j], wave * cq + j));  // (key 0 never enters)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        pw[k * 64] = t[k];
-        pw[(4 + k) * 64] = (uint32_t)ix[k];
-      }
+      for (int k = 0; k < 4; ++k) part[((size_t)wave * 4 + k) * 64 + lane] = t[k];
     }
     lds_barrier();
-    // wave 0 merges the four lists in candidate order and writes the routes
-    // of every row (slots past topk: region 0, masked)
+    // wave 0 merges the four lists and writes the routes of every row (slots
+    // past topk: region 0, masked)
     if (wave == 0) {
-      uint32_t t[4];
-      int ix[4];
-      uint32_t pk[16];
-      int pi[16];
+      double pk[16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int j = 0; j < 16; ++j) pk[j] = part[(size_t)j * 64 + lane];  // all reads first
+      double t[4] = {pk[0], pk[1], pk[2], pk[3]};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {  // all reads first
-          pk[4 * q + k] = part[(size_t)q * 8 * 64 + k * 64 + lane];
-          pi[4 * q + k] = (int)part[(size_t)q * 8 * 64 + (4 + k) * 64 + lane];
-        }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) { t[k] = pk[k]; ix[k] = pi[k]; }
-#pragma unroll
-      for (int j = 4; j < 16; ++j) route::top4_insert(t, ix, pk[j], pi[j]);
+      for (int j = 4; j < 16; ++j) route::top4_code(t, pk[j]);
       if (lane < R) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          if (k < topk) route_put(lane * RSTR + k, ix[k]);
+          if (k < topk) route_put(lane * RSTR + k, route::rank_code_index(t[k]));
         for (int k = topk; k < RSTR; ++k) route_put(lane * RSTR + k, 0);
       }
     }

@@ -22,20 +22,26 @@ __device__ __forceinline__ uint32_t key_u32(float a) {
 __device__ __forceinline__ uint64_t route_key(float a, int s) {
   return ((uint64_t)key_u32(a) << 32) | (uint32_t)(0xffffffffu - (uint32_t)s);
 }
-// Keeps the 4 largest (key, index) pairs seen, largest first, when the
-// candidates arrive in ascending index order: a key enters above another only
-// when strictly larger, so equal keys stay in index order -- the same order
-// as route_key's.
-__device__ __forceinline__ void top4_insert(uint32_t* t, int* ix, uint32_t u, int s) {
-  const bool c0 = u > t[0], c1 = u > t[1], c2 = u > t[2], c3 = u > t[3];
-  t[3] = c2 ? t[2] : (c3 ? u : t[3]);
-  ix[3] = c2 ? ix[2] : (c3 ? s : ix[3]);
-  t[2] = c1 ? t[1] : (c2 ? u : t[2]);
-  ix[2] = c1 ? ix[1] : (c2 ? s : ix[2]);
-  t[1] = c0 ? t[0] : (c1 ? u : t[1]);
-  ix[1] = c0 ? ix[0] : (c1 ? s : ix[1]);
-  t[0] = c0 ? u : t[0];
-  ix[0] = c0 ? s : ix[0];
+// A (key, index) pair as one double, exactly: key * 64 + (63 - index)
+// (< 2^38, so every code is an integer a double holds exactly). Codes order
+// as route_key orders the pairs -- larger key first, equal keys in index
+// order -- for indices below 64, and every key above 0 codes above any
+// index-only (key 0) code.
+__device__ __forceinline__ double rank_code(uint32_t key, int idx) {
+  return __builtin_fma((double)key, 64.0, (double)(63 - idx));
+}
+__device__ __forceinline__ int rank_code_index(double c) {
+  return 63 - (int)__builtin_fma(-64.0, __builtin_floor(c * (1.0 / 64.0)), c);
+}
+// Keeps the 4 largest codes seen, largest first (t[0] >= ... >= t[3]): each
+// slot takes the larger of itself and the smaller of the slot above and the
+// new code. Max and min only, so no compare-and-select chains.
+__device__ __forceinline__ void top4_code(double* t, double u) {
+  const double m0 = __builtin_fmin(t[0], u), m1 = __builtin_fmin(t[1], u), m2 = __builtin_fmin(t[2], u);
+  t[0] = __builtin_fmax(t[0], u);
+  t[1] = __builtin_fmax(t[1], m0);
+  t[2] = __builtin_fmax(t[2], m1);
+  t[3] = __builtin_fmax(t[3], m2);
 }
 
 // One 16 x 16 logit tile: rows r0.., columns 16ct.. of (Q^r K^r^T) * scale,
