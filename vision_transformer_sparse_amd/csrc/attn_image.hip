@@ -560,6 +560,7 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
         if (isk) k_put(i2 >> 2, c, pf[j]);
         if (isv) v_put(i2 >> 2, c, pf[j]);  // partners share the branch (8-aligned pairs)
         if (!isk && !isv && iw < kWP) *reinterpret_cast<u32x4*>(smem + (FUSE ? lay.x : lay.w) + iw * 16) = pf[j];
+        if (FUSE && iw == kWP) *reinterpret_cast<uint32_t*>(smem + lay.x + kWP * 16) = 0u;  // the zero weight
       }
     }
     if (with_routes && tid < nroute) route_put(tid, (int)rq);
@@ -579,11 +580,34 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
 
 
   // FUSE: the head's Toeplitz LCE blocks, built from the weights that commit
-  // left in the hand-over area (between two barriers)
+  // left in the hand-over area (between two barriers). Which two weights a
+  // lane's dwords e = tid + 1024 i take is the same for every head, so it is
+  // worked out once (u16 indices into the weights; 800 is a zero just past
+  // them).
+  constexpr int kToepPer = (kLceToepDwords + kThreads4 - 1) / kThreads4;  // 3
+  uint32_t tsrc[kToepPer];
+  if constexpr (FUSE) {
+#pragma unroll
+    for (int i = 0; i < kToepPer; ++i) {
+      const int e = tid + kThreads4 * i, f = 2 * (e < kLceToepDwords ? e : 0);
+      const int k = f & 3, j = (f >> 2) & 3, b = (f >> 4) & 15, ch = (f >> 8) & 1;
+      const int dy = (f >> 9) % 5, hh = (f >> 9) / 5;
+      const int c = 2 * b + hh, tap = 4 * ch + k - j, base = c * 25 + dy * 5;
+      const uint32_t lo = tap >= 0 && tap < 5 ? (uint32_t)(base + tap) : 800u;
+      const uint32_t hi = tap + 1 >= 0 && tap + 1 < 5 ? (uint32_t)(base + tap + 1) : 800u;
+      tsrc[i] = lo | (hi << 16);
+    }
+  }
   auto toep_build = [&]() {
     const uint16_t* raw = reinterpret_cast<const uint16_t*>(smem + lay.x);
     uint32_t* wl = reinterpret_cast<uint32_t*>(smem + lay.w);
-    for (int e = tid; e < kLceToepDwords; e += kThreads4) wl[e] = lce_toep_dword(raw, e);
+    uint32_t v[kToepPer];
+#pragma unroll
+    for (int i = 0; i < kToepPer; ++i)
+      v[i] = (uint32_t)raw[tsrc[i] & 0xffffu] | ((uint32_t)raw[tsrc[i] >> 16] << 16);
+#pragma unroll
+    for (int i = 0; i < kToepPer; ++i)
+      if (tid + kThreads4 * i < kLceToepDwords) wl[tid + kThreads4 * i] = v[i];
   };
 
   // the V border (two pixels around the image) stays zero for every unit:
@@ -788,22 +812,29 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
       uint32_t kv[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) kv[j] = j < nc ? route::key_u32(lg[j]) : 0u;  // all reads first
-      double t[4] = {0.0, 0.0, 0.0, 0.0};
+      // four sorted groups of four, merged in a tree (key 0 never enters)
+      double g[4][4];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) route::top4_code(t, route::rank_code(kv[j], wave * cq + j));  // (key 0 never enters)
+      for (int j = 0; j < 16; ++j) g[j >> 2][j & 3] = route::rank_code(kv[j], wave * cq + j);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) part[((size_t)wave * 4 + k) * 64 + lane] = t[k];
+      for (int q = 0; q < 4; ++q) route::sort4_code(g[q]);
+      route::merge4_code(g[0], g[1]);
+      route::merge4_code(g[2], g[3]);
+      route::merge4_code(g[0], g[2]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) part[((size_t)wave * 4 + k) * 64 + lane] = g[0][k];
     }
     lds_barrier();
     // wave 0 merges the four lists and writes the routes of every row (slots
     // past topk: region 0, masked)
     if (wave == 0) {
-      double pk[16];
+      double pk[4][4];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) pk[j] = part[(size_t)j * 64 + lane];  // all reads first
-      double t[4] = {pk[0], pk[1], pk[2], pk[3]};
-#pragma unroll
-      for (int j = 4; j < 16; ++j) route::top4_code(t, pk[j]);
+      for (int j = 0; j < 16; ++j) pk[j >> 2][j & 3] = part[(size_t)j * 64 + lane];  // all reads first
+      route::merge4_code(pk[0], pk[1]);
+      route::merge4_code(pk[2], pk[3]);
+      route::merge4_code(pk[0], pk[2]);
+      const double* t = pk[0];
       if (lane < R) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)

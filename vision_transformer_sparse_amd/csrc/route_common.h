@@ -33,15 +33,30 @@ __device__ __forceinline__ double rank_code(uint32_t key, int idx) {
 __device__ __forceinline__ int rank_code_index(double c) {
   return 63 - (int)__builtin_fma(-64.0, __builtin_floor(c * (1.0 / 64.0)), c);
 }
-// Keeps the 4 largest codes seen, largest first (t[0] >= ... >= t[3]): each
-// slot takes the larger of itself and the smaller of the slot above and the
-// new code. Max and min only, so no compare-and-select chains.
-__device__ __forceinline__ void top4_code(double* t, double u) {
-  const double m0 = __builtin_fmin(t[0], u), m1 = __builtin_fmin(t[1], u), m2 = __builtin_fmin(t[2], u);
-  t[0] = __builtin_fmax(t[0], u);
-  t[1] = __builtin_fmax(t[1], m0);
-  t[2] = __builtin_fmax(t[2], m1);
-  t[3] = __builtin_fmax(t[3], m2);
+// Sorting networks on codes (max and min only, no compare-and-select
+// chains); codes of one row are distinct, so the order is exact.
+__device__ __forceinline__ void code_ce(double& hi, double& lo) {  // larger to hi
+  const double a = hi, b = lo;
+  hi = __builtin_fmax(a, b);
+  lo = __builtin_fmin(a, b);
+}
+__device__ __forceinline__ void sort4_code(double* c) {  // largest first
+  code_ce(c[0], c[1]);
+  code_ce(c[2], c[3]);
+  code_ce(c[0], c[2]);
+  code_ce(c[1], c[3]);
+  code_ce(c[1], c[2]);
+}
+// the 4 largest of two lists sorted largest first, into a: the larger of
+// a[i] and b[3 - i] holds them (in a V-shaped order), which a 4-element
+// bitonic sorter puts in order
+__device__ __forceinline__ void merge4_code(double* a, const double* b) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = __builtin_fmax(a[i], b[3 - i]);
+  code_ce(a[0], a[2]);
+  code_ce(a[1], a[3]);
+  code_ce(a[0], a[1]);
+  code_ce(a[2], a[3]);
 }
 
 // One 16 x 16 logit tile: rows r0.., columns 16ct.. of (Q^r K^r^T) * scale,
