@@ -420,7 +420,7 @@ constexpr int kRouteMaxC = 128;
 // LDS the in-kernel routing borrows from the weight and hand-over areas: the
 // logits [R][16 ceil(R/16) + 1] fp32 and the partial top-4 lists
 __host__ __device__ inline size_t route_logits_bytes(int R) { return align16((size_t)R * (16 * ((R + 15) / 16) + 1) * 4); }
-__host__ __device__ inline size_t route_scratch(int R) { return route_logits_bytes(R) + (size_t)4 * 4 * 64 * 8; }
+__host__ __device__ inline size_t route_scratch(int R) { return route_logits_bytes(R); }
 
 // FK: whole K/V slot pairs of the prefetch (4 H W / 1024, rounded down);
 // FUSE: the kernel computes its units' routes from the region means (a
@@ -685,8 +685,6 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
     // overwritten when the first unit is staged.
     const int CT = (R + 15) / 16, RP = 16 * CT + 1;  // odd pitch: a lane per row reads without conflicts
     float* logits = reinterpret_cast<float*>(smem + lay.w);            // [R][RP]
-    const int rt = wave / CT, ct = wave - rt * CT;
-    const bool has_tile = wave < CT * CT;
     const int n0 = u0 / a.heads;
     const int RS = C + 8;                      // bf16 per LDS row
     // matrix m (0: Q^r, 1: K^r), part 0 (hi) / 1 (lo): R rows of RS bf16
@@ -774,75 +772,116 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
       if (i + 3 < 8) pool_issue(i + 3, pbuf[i % 3]);
     }
     pool_put(1);
-    // the first unit's K/V prefetch goes out now; the routing below runs
-    // while it is in flight
+    lds_barrier();  // the means in LDS
+    // Wave rb < 4 routes rows 16 rb .. 16 rb + 15 on its own -- logit tiles
+    // (rb, 0..3), then the top k of its rows -- so the routing needs no
+    // workgroup barrier, and waves 4.. issue their share of the first unit's
+    // prefetch at once (a wave blocked issuing loads holds up no other);
+    // waves 0..3 issue theirs when their rows are routed.
+    if (wave < 4 && 16 * wave < R) {
+      const int rb = wave;
+      // logit tiles (rb, ct): each the route kernel's steps in its order (C a
+      // multiple of 32); the A rows serve all four tiles, and the next
+      // step's operands are read while this step's products run
+      const int qrow = min(16 * rb + col, R - 1);
+      const __bf16* ah = mat_lds(0, 0) + qrow * RS + 8 * grp;
+      const __bf16* al = mat_lds(0, 1) + qrow * RS + 8 * grp;
+      uint32_t boff[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) boff[ct] = (uint32_t)(min(16 * ct + col, R - 1) * RS + 8 * grp);
+      const __bf16* bh = mat_lds(1, 0);
+      const __bf16* bl = mat_lds(1, 1);
+      typedef route::rbf16x8 R8;
+      f32x4 acc[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      R8 xah = *reinterpret_cast<const R8*>(ah), xal = *reinterpret_cast<const R8*>(al);
+      R8 xbh[4], xbl[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        xbh[ct] = *reinterpret_cast<const R8*>(bh + boff[ct]);
+        xbl[ct] = *reinterpret_cast<const R8*>(bl + boff[ct]);
+      }
+      for (int k0 = 0; k0 < C; k0 += 32) {
+        const int kn = k0 + 32 < C ? k0 + 32 : k0;  // (the last step re-reads its own operands)
+        const R8 nah = *reinterpret_cast<const R8*>(ah + kn), nal = *reinterpret_cast<const R8*>(al + kn);
+        R8 nbh[4], nbl[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          nbh[ct] = *reinterpret_cast<const R8*>(bh + boff[ct] + kn);
+          nbl[ct] = *reinterpret_cast<const R8*>(bl + boff[ct] + kn);
+        }
+        // route::logit_step_x3 for the four tiles, its products interleaved
+        // across them
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xah, xbl[ct], acc[ct], 0, 0, 0);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xal, xbh[ct], acc[ct], 0, 0, 0);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xah, xbh[ct], acc[ct], 0, 0, 0);
+        xah = nah;
+        xal = nal;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          xbh[ct] = nbh[ct];
+          xbl[ct] = nbl[ct];
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * rb + 4 * grp + e;
+          if (row < R && ct < CT) logits[row * RP + 16 * ct + col] = acc[ct][e] * a.rscale;
+        }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // top k (k <= 4) of row 16 rb + lane / 4: lane q = lane % 4 keeps the
+      // top 4 of candidates [q cq, (q + 1) cq) (cq <= 16: R <= 64) as rank
+      // codes, then the quad merges its four lists (DPP exchanges)
+      const int cq = (R + 3) / 4, q = lane & 3, row = 16 * rb + (lane >> 2);
+      const float* lg = logits + min(row, R - 1) * RP + q * cq;
+      const int nc = min(R, (q + 1) * cq) - q * cq;
+      uint32_t kv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float x = lg[min(j, nc - 1)];  // all reads first
+        kv[j] = j < nc ? route::key_u32(x) : 0u;
+      }
+      double g[4][4];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) g[j >> 2][j & 3] = route::rank_code(kv[j], q * cq + j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) route::sort4_code(g[i]);
+      route::merge4_code(g[0], g[1]);
+      route::merge4_code(g[2], g[3]);
+      route::merge4_code(g[0], g[2]);
+      auto quad_merge = [&](auto ctrl) {  // merge with the list of the quad lane ctrl names
+        double o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint64_t u = __builtin_bit_cast(uint64_t, g[0][k]);
+          const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, decltype(ctrl)::value, 0xF, 0xF, false);
+          const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), decltype(ctrl)::value, 0xF, 0xF, false);
+          o[k] = __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+        }
+        route::merge4_code(g[0], o);
+      };
+      quad_merge(std::integral_constant<int, 0xB1>{});  // quad_perm [1,0,3,2]
+      quad_merge(std::integral_constant<int, 0x4E>{});  // quad_perm [2,3,0,1]
+      if (row < R) {  // lane q writes slot q (slots past topk: region 0, masked)
+        double tq = g[0][0];
+#pragma unroll
+        for (int k = 1; k < 4; ++k) tq = q == k ? g[0][k] : tq;
+        route_put(row * RSTR + q, q < topk ? route::rank_code_index(tq) : 0);
+      }
+    }
     asm volatile("" ::: "memory");
     prefetch(u0, true);
     qrows(u0, 0);
     asm volatile("" ::: "memory");
-    lds_barrier();  // the means in LDS
-    {  // logit tile (rt, ct): the route kernel's steps in its order (C a multiple of 32)
-      const int qrow = min(16 * rt + col, R - 1), krow = min(16 * ct + col, R - 1);
-      const __bf16* ah = mat_lds(0, 0) + qrow * RS + 8 * grp;
-      const __bf16* al = mat_lds(0, 1) + qrow * RS + 8 * grp;
-      const __bf16* bh = mat_lds(1, 0) + krow * RS + 8 * grp;
-      const __bf16* bl = mat_lds(1, 1) + krow * RS + 8 * grp;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < C; k0 += 32)
-        acc = route::logit_step_x3(acc, *reinterpret_cast<const route::rbf16x8*>(ah + k0),
-                                   *reinterpret_cast<const route::rbf16x8*>(al + k0),
-                                   *reinterpret_cast<const route::rbf16x8*>(bh + k0),
-                                   *reinterpret_cast<const route::rbf16x8*>(bl + k0));
-      if (has_tile) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 16 * rt + 4 * grp + e;
-          if (row < R) logits[row * RP + 16 * ct + col] = acc[e] * a.rscale;
-        }
-      }
-    }
-    lds_barrier();  // the logits in LDS
-    // top-k (k <= 4), a lane per row: wave q < 4 keeps the top 4 of candidates
-    // [q cq, (q + 1) cq) of every row (cq <= 16: R <= 64), as rank codes
-    const int cq = (R + 3) / 4;
-    double* part = reinterpret_cast<double*>(smem + lay.w + route_logits_bytes(R));  // [4][4][64] partial top 4
-    if (wave < 4) {
-      const float* lg = logits + min(lane, R - 1) * RP + wave * cq;
-      const int nc = min(R, (wave + 1) * cq) - wave * cq;
-      uint32_t kv[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) kv[j] = j < nc ? route::key_u32(lg[j]) : 0u;  // all reads first
-      // four sorted groups of four, merged in a tree (key 0 never enters)
-      double g[4][4];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) g[j >> 2][j & 3] = route::rank_code(kv[j], wave * cq + j);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) route::sort4_code(g[q]);
-      route::merge4_code(g[0], g[1]);
-      route::merge4_code(g[2], g[3]);
-      route::merge4_code(g[0], g[2]);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) part[((size_t)wave * 4 + k) * 64 + lane] = g[0][k];
-    }
-    lds_barrier();
-    // wave 0 merges the four lists and writes the routes of every row (slots
-    // past topk: region 0, masked)
-    if (wave == 0) {
-      double pk[4][4];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) pk[j >> 2][j & 3] = part[(size_t)j * 64 + lane];  // all reads first
-      route::merge4_code(pk[0], pk[1]);
-      route::merge4_code(pk[2], pk[3]);
-      route::merge4_code(pk[0], pk[2]);
-      const double* t = pk[0];
-      if (lane < R) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (k < topk) route_put(lane * RSTR + k, route::rank_code_index(t[k]));
-        for (int k = topk; k < RSTR; ++k) route_put(lane * RSTR + k, 0);
-      }
-    }
-    lds_barrier();  // every read of the means and logits done before staging
+    lds_barrier();  // routed; every read of the means and logits done before staging
     zero_border();
     commit(u0, false);
     lds_barrier();
