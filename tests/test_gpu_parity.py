@@ -84,6 +84,15 @@ SMALL_CASES = [
     ("t1_1x1_regions_l40", 1, 8, 8, 64, 2, 8, 40, "bf16", 0.7),
     # 4x4 regions of an image too large for the image-resident kernel
     ("t16_region_kernel_64px", 1, 64, 64, 128, 4, 16, 4, "bf16", 0.7),
+    # the one-kernel 4x4 path (pooling and routing in the attention kernel):
+    # region counts 1..36, topk 1..4 (= S^2 too), C 64/128, 2 and 4 heads,
+    # whole and partial prefetch slots
+    ("fused_s4_c64_t2", 2, 16, 16, 64, 2, 4, 2, "bf16", 0.7),
+    ("fused_s5_c128_t3", 3, 20, 20, 128, 4, 5, 3, "bf16", 0.0),
+    ("fused_s3_c64_t1", 2, 12, 12, 64, 2, 3, 1, "bf16", 0.7),
+    ("fused_s6_c64_t4", 1, 24, 24, 64, 2, 6, 4, "bf16", 0.0),
+    ("fused_s2_topk_eq_R", 1, 8, 8, 128, 4, 2, 4, "bf16", 0.0),
+    ("fused_s1_one_region", 2, 4, 4, 64, 2, 1, 1, "bf16", 0.0),
     ("f32_c0_like", 1, 56, 56, 64, 2, 7, 1, "f32", 0.0),
     ("f32_ragged", 2, 15, 10, 64, 2, 5, 3, "f32", 0.0),
     ("f32_t256", 1, 64, 64, 64, 2, 4, 2, "f32", 0.7),
@@ -209,6 +218,26 @@ def test_exact_ties_go_to_lower_index(gpu_lib):
             lst = list(route[n, r])
             assert sorted(lst) == list(range(16))
             assert lst.index(1) < lst.index(6) < lst.index(12), (n, r, lst)
+
+
+def test_exact_ties_one_kernel_path(gpu_lib):
+    """The routing inside the 4x4-region attention kernel on exact ties:
+    regions 6 and 12 of k are copies of region 1 and outweigh every other
+    region for every query (q is all ones), so each row's first three routes
+    are exactly 1, 6, 12 in that order and the fourth is the best of the rest."""
+    N, H, W, C, heads, S, topk = 2, 16, 16, 64, 2, 4, 4
+    inp = draw(N, H, W, C, S, "bf16", seed=1234)
+    q = np.ones_like(inp["q"])
+    k = inp["k"].copy()
+    k[:, 0:4, 4:8, :] = 3.0 + 0.25 * np.sign(k[:, 0:4, 4:8, :])  # region 1: large means
+    k[:, 4:8, 8:12, :] = k[:, 0:4, 4:8, :]      # region 6 := region 1
+    k[:, 12:16, 0:4, :] = k[:, 0:4, 4:8, :]     # region 12 := region 1
+    inp = dict(inp, q=q, k=k)
+    say("ties, one-kernel path")
+    _, route, _ = run_forward(gpu_lib, inp, heads, S, topk, "bf16", name="ties_one_kernel")
+    for n in range(N):
+        for r in range(S * S):
+            assert list(route[n, r, :3]) == [1, 6, 12], (n, r, list(route[n, r]))
 
 
 def test_deterministic(gpu_lib):
