@@ -391,6 +391,7 @@ __global__ __launch_bounds__(64 * NW) void attn_image2_kernel(ImageArgs a) {
 constexpr int kNW4 = 16;                       // waves
 constexpr int kThreads4 = 64 * kNW4;
 constexpr int kPF = 7;                         // prefetch pieces per lane
+constexpr int kPFA = 4;                        // of which issued at a unit's start
 constexpr int kWPieces = kLceToepDwords / 4;   // a head's Toeplitz LCE blocks in 16-byte pieces
 constexpr int kWRawPieces = 32 * 25 * 2 / 16;  // a head's 5x5 weights as given, in 16-byte pieces
 constexpr int kVPitch4 = kVRow4 / 2 * 128;     // bytes per bordered-V row: 16 pixel pairs x 32 channels
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
   };
   // (real == false: the same loads, past the buffers or all of one address,
   // discarded: every path issues the same loads)
-  auto prefetch = [&](int u, bool real) {
+  auto prefetch = [&](int u, bool real, int j0 = 0, int j1 = kPF) {  // slots [j0, j1)
     const int tid = opaque_tid();
     const int n = u / a.heads, h = u - n * a.heads;
     const size_t img = (size_t)n * HW * C;
@@ -488,6 +489,7 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
     const uint32_t lb = keep ? (uint32_t)(tid >> 2) * pixb + (uint32_t)(tid & 3) * 16 : kOut;
 #pragma unroll
     for (int j = 0; j < kPF; ++j) {
+      if (j < j0 || j >= j1) continue;
       if (j < 2 * FK) {
         const uint32_t so = (uint32_t)h * 64 + (uint32_t)(j >> 1) * 256 * pixb;
         pf[j] = __builtin_bit_cast(u32x4, ld16s((j & 1) ? vb : kb, lb, so));
@@ -504,7 +506,7 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
         pf[j] = *reinterpret_cast<const u32x4*>(src);
       }
     }
-    if constexpr (!FUSE) {  // (routed in the kernel: rq already holds the routes)
+    if (!FUSE && j0 == 0) {  // (routed in the kernel: rq already holds the routes)
       const Rsrc rrs = rsrc(a.route + (size_t)n * R * topk, (uint32_t)(R * topk) * 4);
       rq = __builtin_amdgcn_raw_buffer_load_b32(rrs, keep ? route_off(tid) : kOut, 0, 0);
     }
@@ -934,14 +936,19 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
     const Rsrc ob = rsrc(a.out + (size_t)n * HW * C, img_bytes);
     const int first = (wave + kNW4 - it % kNW4) % kNW4;
     const bool more = it + 1 < nits;
-    prefetch(more ? unit_of(it + 1) : u, more);
+    // The next unit's prefetch goes out in two parts, the second after the
+    // wave's first region: a wave blocks while the memory queues take its
+    // loads, and split this way the waves of a SIMD block at different times.
+    // (The first region is peeled so the second part has one definition.)
+    const int un = more ? unit_of(it + 1) : u;
+    prefetch(un, more, 0, kPFA);
     // Take delivery of the query rows and the bias right after the prefetch
     // was issued: the wait covers just these loads, and the region loop holds
     // no value still in flight (a loop that used one would have the compiler
     // wait for every outstanding load, the prefetch too, before entering it).
     asm volatile("" : "+v"(q0), "+v"(q1), "+v"(q2), "+v"(q3), "+v"(bias2));
 
-    for (int r = first; r < R; r += kNW4) {
+    auto region = [&](const int r) {
       const bf16x8 bq = q0;
       q0 = q1;
       q1 = q2;
@@ -1060,7 +1067,12 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
         o2[1] = (__bf16)d1[p];
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o2), ob, oo, (uint32_t)p * W * pixb, 2);  // nt: streamed, not kept in L2
       }
-    }
+    };
+    if (first < R) region(first);
+    asm volatile("" ::: "memory");
+    prefetch(un, more, kPFA, kPF);
+    asm volatile("" ::: "memory");
+    for (int r = first + kNW4; r < R; r += kNW4) region(r);
     if (more) {
       qrows(unit_of(it + 1), it + 1);
       asm volatile("" ::: "memory");  // issued here, ahead of the staging below
