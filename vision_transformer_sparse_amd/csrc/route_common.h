@@ -157,24 +157,39 @@ __device__ __forceinline__ f32x4 logit_step_x3(f32x4 acc, rbf16x8 ah, rbf16x8 al
 // col, as logit_tile.
 template <typename GetA, typename GetB>
 __device__ __forceinline__ f32x4 logit_tile_x3(int grp, int C, GetA geta, GetB getb) {
+  // the operands of the next kAhead steps are in flight while a step's
+  // products run (loads past C read nothing and are never used)
+  constexpr int kAhead = 3;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  uint4 a0 = geta(8 * grp), a1 = geta(8 * grp + 4), b0 = getb(8 * grp), b1 = getb(8 * grp + 4);
-  for (int k0 = 0; k0 < C; k0 += 32) {
-    const uint4 ca0 = a0, ca1 = a1, cb0 = b0, cb1 = b1;
-    if (k0 + 32 < C) {  // the next step in flight
-      a0 = geta(k0 + 32 + 8 * grp);
-      a1 = geta(k0 + 32 + 8 * grp + 4);
-      b0 = getb(k0 + 32 + 8 * grp);
-      b1 = getb(k0 + 32 + 8 * grp + 4);
+  uint4 ra[kAhead][2], rb[kAhead][2];
+#pragma unroll
+  for (int d = 0; d < kAhead; ++d) {
+    ra[d][0] = geta(32 * d + 8 * grp);
+    ra[d][1] = geta(32 * d + 8 * grp + 4);
+    rb[d][0] = getb(32 * d + 8 * grp);
+    rb[d][1] = getb(32 * d + 8 * grp + 4);
+  }
+  for (int k0 = 0; k0 < C; k0 += 32 * kAhead) {
+#pragma unroll
+    for (int d = 0; d < kAhead; ++d) {
+      const int k = k0 + 32 * d;
+      const uint4 ca0 = ra[d][0], ca1 = ra[d][1], cb0 = rb[d][0], cb1 = rb[d][1];
+      const int kn = k + 32 * kAhead;  // this slot's next step
+      ra[d][0] = geta(kn + 8 * grp);
+      ra[d][1] = geta(kn + 8 * grp + 4);
+      rb[d][0] = getb(kn + 8 * grp);
+      rb[d][1] = getb(kn + 8 * grp + 4);
+      if (k < C) {
+        const float fa[8] = {__uint_as_float(ca0.x), __uint_as_float(ca0.y), __uint_as_float(ca0.z), __uint_as_float(ca0.w),
+                             __uint_as_float(ca1.x), __uint_as_float(ca1.y), __uint_as_float(ca1.z), __uint_as_float(ca1.w)};
+        const float fb[8] = {__uint_as_float(cb0.x), __uint_as_float(cb0.y), __uint_as_float(cb0.z), __uint_as_float(cb0.w),
+                             __uint_as_float(cb1.x), __uint_as_float(cb1.y), __uint_as_float(cb1.z), __uint_as_float(cb1.w)};
+        rbf16x8 ah, al, bh, bl;
+        split_bf16(fa, ah, al);
+        split_bf16(fb, bh, bl);
+        acc = logit_step_x3(acc, ah, al, bh, bl);
+      }
     }
-    const float fa[8] = {__uint_as_float(ca0.x), __uint_as_float(ca0.y), __uint_as_float(ca0.z), __uint_as_float(ca0.w),
-                         __uint_as_float(ca1.x), __uint_as_float(ca1.y), __uint_as_float(ca1.z), __uint_as_float(ca1.w)};
-    const float fb[8] = {__uint_as_float(cb0.x), __uint_as_float(cb0.y), __uint_as_float(cb0.z), __uint_as_float(cb0.w),
-                         __uint_as_float(cb1.x), __uint_as_float(cb1.y), __uint_as_float(cb1.z), __uint_as_float(cb1.w)};
-    rbf16x8 ah, al, bh, bl;
-    split_bf16(fa, ah, al);
-    split_bf16(fb, bh, bl);
-    acc = logit_step_x3(acc, ah, al, bh, bl);
   }
   return acc;
 }
