@@ -1,7 +1,9 @@
-// Gathered attention + LCE for small images with 2x2-token regions, bf16
-// tensors -- the third classification stage of BiFormer (a 14x14 map, S = 7,
-// topk = 16). Eqs. 6-7 of the BRA walk-through at
-// TRANSFORMER.niftyadmin.cn/n/347023.html, section BRA模块.
+// Gathered attention + LCE for small images, bf16 tensors: 2x2-token regions
+// -- the third classification stage of BiFormer (a 14x14 map, S = 7, topk =
+// 16) -- and 4x4-token regions -- the second stage (28x28, S = 7, topk = 4),
+// where one kernel also pools the region means and routes (Eqs. 3-7 of the
+// BRA walk-through at TRANSFORMER.niftyadmin.cn/n/347023.html, section
+// BRA模块). The 2x2 kernel first:
 //
 // With 4-token regions a region's own work is tiny next to the latency of
 // fetching its 64 routed keys, so this kernel makes the image, not the
@@ -388,6 +390,16 @@ __global__ __launch_bounds__(64 * NW) void attn_image2_kernel(ImageArgs a) {
 // block one channel's 4x4 output tile, each window row adding its 8 pixels
 // (two chunks of 4) times a Toeplitz block of that row's 5 weights; the
 // attention output, handed over through LDS, is the accumulator's start.
+//
+// The whole forward in one kernel (FUSE): a workgroup takes heads h and
+// h + heads/2 of one image. It pools the image's q and k into the region
+// means -- in the pool kernel's summation order, so the means, and so the
+// routes, are the stage-by-stage path's bit for bit -- and routes: waves 0-3
+// take 16 rows each (logit tiles with the route kernel's split-bf16 steps,
+// then the top k of every row as fp64 codes through sorting networks, merged
+// across lane quads) with no workgroup barrier, while the other waves already
+// issue the first unit's prefetch. The LCE weights come as given and are built
+// into the Toeplitz blocks in LDS for each unit.
 constexpr int kNW4 = 16;                       // waves
 constexpr int kThreads4 = 64 * kNW4;
 constexpr int kPF = 7;                         // prefetch pieces per lane
