@@ -431,9 +431,8 @@ __device__ __forceinline__ void lds_barrier() {
 // in LDS
 constexpr int kRouteMaxC = 128;
 // LDS the in-kernel routing borrows from the weight and hand-over areas: the
-// logits [R][16 ceil(R/16) + 1] fp32 and the partial top-4 lists
+// logits [R][16 ceil(R/16) + 1] fp32
 __host__ __device__ inline size_t route_logits_bytes(int R) { return align16((size_t)R * (16 * ((R + 15) / 16) + 1) * 4); }
-__host__ __device__ inline size_t route_scratch(int R) { return route_logits_bytes(R); }
 
 // FK: whole K/V slot pairs of the prefetch (4 H W / 1024, rounded down);
 // FUSE: the kernel computes its units' routes from the region means (a
@@ -689,14 +688,12 @@ __global__ __launch_bounds__(kThreads4) void attn_image4_kernel(ImageArgs a) {
     // ---- the image's routes, from q and k. The region means Q^r and K^r
     // are computed here and written to the K/V area as bf16 hi and lo rows,
     // split as the route kernel splits them (rows C + 8 apart to spread the
-    // banks); wave w computes logit tile (w / CT, w % CT) with the route
-    // kernel's split-bf16 steps, from LDS. The top k (k <= 4) of a row is
-    // found by a lane scanning candidates in index order (four waves a quarter
-    // each, then merged), which picks what the route kernel's ranks pick from
-    // the same logits. The routes go straight to the route table (both units
-    // share it); the workgroup with head 0 reports them. The logits and
-    // partial lists use the weight and hand-over areas; all of it is
-    // overwritten when the first unit is staged.
+    // banks); the logits (the route kernel's split-bf16 steps, so the same
+    // logits) and the top k follow below, and pick what the route kernel's
+    // ranks pick. The routes go straight to the route table (both units share
+    // it); the workgroup with head 0 reports them. The logits use the weight
+    // and hand-over areas; the means and logits are overwritten when the
+    // first unit is staged.
     const int CT = (R + 15) / 16, RP = 16 * CT + 1;  // odd pitch: a lane per row reads without conflicts
     float* logits = reinterpret_cast<float*>(smem + lay.w);            // [R][RP]
     const int n0 = u0 / a.heads;
@@ -1143,7 +1140,7 @@ bool image_kernel_routes(const Shape& s) {
   const ImgLds l = img_lds(4, kNW4, s.H, s.W, s.R, s.topk);
   if ((size_t)4 * s.R * (s.C + 8) * 2 > l.rk - l.k) return false;  // the split means in the K/V area
   if ((size_t)kWRawPieces * 16 > l.sink - l.x) return false;        // the raw weights in the hand-over area
-  return route_scratch(s.R) <= l.sink - l.w;               // the weight and hand-over areas
+  return route_logits_bytes(s.R) <= l.sink - l.w;          // the logits in the weight and hand-over areas
 }
 
 static ImageArgs image_args(const void* q, const void* k, const void* v, const void* b,
