@@ -240,6 +240,22 @@ def test_exact_ties_one_kernel_path(gpu_lib):
             assert list(route[n, r, :3]) == [1, 6, 12], (n, r, list(route[n, r]))
 
 
+def test_one_kernel_path_without_bias(gpu_lib):
+    """The 4x4-region one-kernel path with lce_b = None (no LCE bias)."""
+    N, H, W, C, heads, S, topk = 2, 20, 20, 128, 4, 5, 4
+    inp = draw(N, H, W, C, S, "bf16", seed=4321, offset_std=0.7)
+    say("one-kernel path, no bias")
+    out, route = gpu_lib.forward(dev(inp["q"], "bf16"), dev(inp["k"], "bf16"), dev(inp["v"], "bf16"),
+                                 dev(inp["lce_w"], "bf16"), None, heads, S, topk)
+    out, route = host(out), host(route)
+    A, own = oracle_routing(inp, S, topk)
+    exact, near, fails = compare_routes(route, A, own)
+    assert not fails, fails[:5]
+    ref = oracle.bra_forward(inp["q"], inp["k"], inp["v"], inp["lce_w"], None, heads, S, topk,
+                             route_override=route)
+    check_output(out, ref["out"], "bf16")
+
+
 def test_deterministic(gpu_lib):
     cfg = CONFIGS[1]
     inp = draw_config(cfg, N=16)
