@@ -46,7 +46,7 @@ import numpy as np
 __all__ = [
     "check_shapes", "partition", "unpartition", "region_means",
     "region_affinity", "topk_routes", "gather_regions", "token_attention",
-    "lce", "bra_forward",
+    "lce", "bra_forward", "linear", "round_bf16", "bra_block_forward",
 ]
 
 
@@ -213,4 +213,52 @@ def bra_forward(q, k, v, lce_w, lce_b, heads: int, S: int, topk: int,
     res = {"out": out, "route_idx": route, "route_oracle": route_own, "logits": A}
     if return_probs:
         res["probs"] = probs
+    return res
+
+
+def linear(x, w, b=None) -> np.ndarray:
+    """A Linear layer over the last axis: y = x w^T + b, in float64.
+
+    x: (..., K); w: (Nout, K) as a Linear layer stores it; b: (Nout,) or None.
+    The walk-through (section "BRA模块") projects the tokens with one
+    Linear(C, 3C) (its module print in section "网络结构": QKVLinear holding
+    Linear(64, 192)) and ends the block with wo = Linear(C, C)."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    y = x @ w.T
+    if b is not None:
+        y = y + np.asarray(b, dtype=np.float64)
+    return y
+
+
+def round_bf16(x) -> np.ndarray:
+    """Rounds to bfloat16 (via float32, then to nearest even on the upper 16
+    bits) and returns float64: the storage precision of a bf16 tensor between
+    two steps of the block."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return (u.astype(np.uint32)).view(np.float32).astype(np.float64)
+
+
+def bra_block_forward(x, wqkv, bqkv, lce_w, lce_b, wo, bo, heads: int, S: int, topk: int,
+                      store: str | None = None, route_override=None):
+    """The BRA block around the operator, as the walk-through's forward pass
+    (section "BRA模块") runs it: q, k, v = split(qkv(x)) in that order along the
+    channels, the operator on them (steps 1-8 above), then wo.
+
+    x: (N, H, W, C); wqkv: (3C, C); bqkv: (3C,) or None; wo: (C, C); bo: (C,)
+    or None. store="bf16" rounds the tensors handed from one step to the next
+    (q, k, v and the operator's output) to bfloat16, as a bf16 pipeline stores
+    them; None keeps float64 throughout. Returns the operator's result dict
+    with "out" replaced by the block output and "attn_out" added."""
+    x = np.asarray(x, dtype=np.float64)
+    C = x.shape[-1]
+    keep = round_bf16 if store == "bf16" else (lambda t: t)
+    qkv = linear(x, wqkv, bqkv)
+    q, k, v = (keep(qkv[..., i * C:(i + 1) * C]) for i in range(3))
+    res = bra_forward(q, k, v, lce_w, lce_b, heads, S, topk, route_override=route_override)
+    o = keep(res["out"])
+    res["attn_out"] = o
+    res["out"] = linear(o, wo, bo)
     return res

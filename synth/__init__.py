@@ -21,7 +21,8 @@ import math
 
 import numpy as np
 
-__all__ = ["Config", "CONFIGS", "draw", "round_to_bf16", "draw_config"]
+__all__ = ["Config", "CONFIGS", "draw", "round_to_bf16", "draw_config", "draw_linear",
+           "draw_block"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -130,3 +131,43 @@ def draw_config(cfg: Config | int, seed: int | None = None, N: int | None = None
         seed = 1000 + idx
     return draw(N if N is not None else cfg.N, cfg.H, cfg.W, cfg.C, cfg.S,
                 cfg.dtype, seed, cfg.offset_std, cfg.w_std, cfg.b_std)
+
+
+def _linear_init(rng, nout: int, nin: int):
+    """A Linear layer's weight (nout, nin) and bias (nout,), each uniform on
+    [-1/sqrt(nin), 1/sqrt(nin)] (the usual default initialisation of such a
+    layer; the pages train their weights, which no synthetic run has)."""
+    bound = 1.0 / math.sqrt(nin)
+    w = rng.uniform(-bound, bound, (nout, nin))
+    b = rng.uniform(-bound, bound, (nout,))
+    return w, b
+
+
+def draw_linear(M: int, K: int, Nout: int, dtype: str, seed: int):
+    """x (M, K) standard normal, then w (Nout, K) and b (Nout,) as a Linear
+    layer's initialisation, from PCG64(seed), rounded to `dtype`."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K))
+    w, b = _linear_init(rng, Nout, K)
+    return {"x": _round(x, dtype), "w": _round(w, dtype), "b": _round(b, dtype)}
+
+
+def draw_block(N: int, H: int, W: int, C: int, S: int, dtype: str, seed: int,
+               offset_std: float = 0.0, w_std: float = 0.2, b_std: float = 0.1):
+    """Inputs of the block around the operator, from PCG64(seed): x
+    (N, H, W, C) standard normal (plus, if offset_std > 0, one offset per
+    image, region and channel added to the region's tokens), then the qkv
+    Linear(C, 3C), then the output Linear(C, C), then lce_w (C,5,5) ~
+    N(0, w_std^2) and lce_b (C,) ~ N(0, b_std^2) (zeros if b_std is 0). Every
+    array is rounded to `dtype`."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((N, H, W, C))
+    if offset_std > 0.0:
+        off = rng.standard_normal((N, S, S, C)) * offset_std
+        x += np.repeat(np.repeat(off, H // S, axis=1), W // S, axis=2)
+    wqkv, bqkv = _linear_init(rng, 3 * C, C)
+    wo, bo = _linear_init(rng, C, C)
+    w = rng.standard_normal((C, 5, 5)) * w_std
+    b = rng.standard_normal((C,)) * b_std if b_std > 0.0 else np.zeros((C,))
+    out = {"x": x, "wqkv": wqkv, "bqkv": bqkv, "wo": wo, "bo": bo, "lce_w": w, "lce_b": b}
+    return {name: _round(a, dtype) for name, a in out.items()}

@@ -366,4 +366,98 @@ def pin_c0_shape_trace(O):
     assert tuple(res["out"].shape) == tuple(trace["out"])
 
 
+# ---------------------------------------------------------------- projections
+def pin_linear_hand_example(O):
+    """A Linear layer computes x w^T + b with w stored (out, in) (the
+    walk-through's Linear(64, 192) maps 64 channels to 192): worked by hand
+    for a 2 x 3 input, a 2 x 3 weight and a bias."""
+    x = np.array([[1.0, 2.0, 3.0], [4.0, 5.0, 6.0]])
+    w = np.array([[1.0, 0.0, -1.0], [2.0, 1.0, 0.0]])
+    b = np.array([0.5, -1.0])
+    want = np.array([[-1.5, 3.0], [-1.5, 12.0]])
+    assert np.array_equal(O.linear(x, w, b), want)
+    assert np.array_equal(O.linear(x, w, None), want - b)
+
+
+def pin_linear_brute_force(O):
+    """Every output of a small Linear equals its sum of products written out
+    one term at a time (leading axes kept: (2, 3, K) tokens)."""
+    rng = _rng(41)
+    x = rng.standard_normal((2, 3, 5))
+    w = rng.standard_normal((7, 5))
+    b = rng.standard_normal(7)
+    y = O.linear(x, w, b)
+    assert y.shape == (2, 3, 7)
+    for i in range(2):
+        for j in range(3):
+            for f in range(7):
+                acc = b[f]
+                for c in range(5):
+                    acc += x[i, j, c] * w[f, c]
+                assert abs(y[i, j, f] - acc) < 1e-12
+
+
+def pin_round_bf16_known_values(O):
+    """bfloat16 keeps 8 significant bits and rounds to nearest, ties to even:
+    at 1 the spacing is 2^-7, so 1 + 2^-8 (a tie) stays 1, 1 + 3*2^-8 (a tie)
+    goes to the even 1 + 2^-6, anything above a half spacing rounds up, and
+    the sign is kept."""
+    x = np.array([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -20,
+                  -(1 + 2.0 ** -8 + 2.0 ** -20), 3.0, 0.0, 2.0 ** -130])
+    want = np.array([1.0, 1.0, 1 + 2.0 ** -6, 1 + 2.0 ** -7, -(1 + 2.0 ** -7), 3.0, 0.0, 2.0 ** -130])
+    assert np.array_equal(O.round_bf16(x), want)
+
+
+def _block_inputs(seed, N=1, H=8, W=8, C=8):
+    rng = _rng(seed)
+    x = rng.standard_normal((N, H, W, C))
+    lw = rng.standard_normal((C, 5, 5)) * 0.2
+    lb = rng.standard_normal(C) * 0.1
+    return x, lw, lb
+
+
+def pin_block_identity_projections(O):
+    """With qkv = three stacked identities (zero bias) and wo = diag(d) plus a
+    bias, the block is the operator on (x, x, x), scaled per channel and
+    shifted (section BRA模块: q, kv = qkv(x), then the operator, then wo)."""
+    x, lw, lb = _block_inputs(42)
+    C = x.shape[-1]
+    eye = np.eye(C)
+    d = np.arange(1.0, C + 1)
+    bo = np.linspace(-1, 1, C)
+    res = O.bra_block_forward(x, np.vstack([eye, eye, eye]), None, lw, lb, np.diag(d), bo,
+                              heads=2, S=2, topk=2)
+    op = O.bra_forward(x, x, x, lw, lb, 2, 2, 2)
+    assert np.allclose(res["out"], op["out"] * d + bo, rtol=0, atol=1e-12)
+    assert np.array_equal(res["route_idx"], op["route_idx"])
+
+
+def pin_block_split_order(O):
+    """qkv's 3C outputs are q, then k, then v: with the blocks 2I, 3I, 5I
+    and wo = I the block equals the operator on (2x, 3x, 5x)."""
+    x, lw, lb = _block_inputs(43)
+    C = x.shape[-1]
+    eye = np.eye(C)
+    bq = np.concatenate([np.full(C, 0.1), np.full(C, -0.2), np.full(C, 0.3)])
+    res = O.bra_block_forward(x, np.vstack([2 * eye, 3 * eye, 5 * eye]), bq, lw, lb, eye, None,
+                              heads=2, S=2, topk=1)
+    op = O.bra_forward(2 * x + 0.1, 3 * x - 0.2, 5 * x + 0.3, lw, lb, 2, 2, 1)
+    assert np.allclose(res["out"], op["out"], rtol=0, atol=1e-12)
+
+
+def pin_block_bf16_store_rounds_handoffs(O):
+    """store="bf16" rounds q, k, v and the operator's output and nothing else:
+    fed x already on the bf16 grid with identity projections, the block equals
+    wo applied to the rounded operator output."""
+    x, lw, lb = _block_inputs(44)
+    x = O.round_bf16(x)
+    C = x.shape[-1]
+    eye = np.eye(C)
+    res = O.bra_block_forward(x, np.vstack([eye, eye, eye]), None, lw, lb, eye, None,
+                              heads=2, S=2, topk=2, store="bf16")
+    op = O.bra_forward(x, x, x, lw, lb, 2, 2, 2)
+    assert np.array_equal(res["out"], O.round_bf16(op["out"]))
+    assert not np.array_equal(res["out"], op["out"])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

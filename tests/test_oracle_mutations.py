@@ -87,7 +87,43 @@ def _lce_dropped(v, w, b):
     return np.zeros_like(v)
 
 
+def _linear_weight_not_transposed(x, w, b=None):
+    y = np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64)
+    return y if b is None else y + b
+
+
+def _linear_bias_dropped(x, w, b=None):
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
+
+
+def _round_bf16_truncates(x):
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    return (f.view(np.uint32) >> 16 << 16).view(np.float32).astype(np.float64)
+
+
+def _round_bf16_ties_up(x):
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    return ((u + 0x8000) >> 16 << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _block_kv_swapped(x, wqkv, bqkv, lce_w, lce_b, wo, bo, heads, S, topk, store=None,
+                      route_override=None):
+    C = np.asarray(x).shape[-1]
+    wqkv = np.asarray(wqkv, dtype=np.float64)
+    wqkv = np.concatenate([wqkv[:C], wqkv[2 * C:], wqkv[C:2 * C]])
+    if bqkv is not None:
+        bqkv = np.concatenate([bqkv[:C], bqkv[2 * C:], bqkv[C:2 * C]])
+    return O.__dict__["_orig_block"](x, wqkv, bqkv, lce_w, lce_b, wo, bo, heads, S, topk,
+                                     store, route_override)
+
+
 MUTATIONS = {
+    "linear_weight_not_transposed": ("linear", _linear_weight_not_transposed),
+    "linear_bias_dropped": ("linear", _linear_bias_dropped),
+    "round_bf16_truncates": ("round_bf16", _round_bf16_truncates),
+    "round_bf16_ties_away": ("round_bf16", _round_bf16_ties_up),
+    "block_k_and_v_swapped": ("bra_block_forward", _block_kv_swapped),
     "partition_region_order_swapped": ("partition", _partition_swapped),
     "means_over_channels": ("region_means", _means_over_channels),
     "means_wrong_count": ("region_means", _means_wrong_count),
@@ -111,6 +147,7 @@ def test_some_pin_catches(name, monkeypatch):
     attr, bad = MUTATIONS[name]
     monkeypatch.setitem(O.__dict__, "_orig_gather", O.gather_regions)
     monkeypatch.setitem(O.__dict__, "_orig_lce", O.lce)
+    monkeypatch.setitem(O.__dict__, "_orig_block", O.bra_block_forward)
     monkeypatch.setattr(O, attr, bad)
     caught = []
     for pin in P.ALL_PINS:
