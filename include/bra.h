@@ -111,6 +111,26 @@ int bra_attend(const void* q, const void* k, const void* v,
 int bra_lce(const void* v, const void* lce_w, const void* lce_b,
             int N, int H, int W, int C, int dtype, float* out);
 
+/* The Linear layers around the operator: y = x w^T + b over the channels of
+ * every token (the walk-through TRANSFORMER.niftyadmin.cn/n/347023.html,
+ * section BRA模块: one Linear(C, 3C) gives q, k and v, split in that order,
+ * and the output Linear(C, C), wo, follows attention + LCE; section 网络结构
+ * prints them as Linear(64, 192) and Linear(64, 64)).
+ * x: [M][K] row-major (M tokens of K channels), w: [Nout][K] row-major (the
+ * Linear weight as stored), b: [Nout] or NULL (no bias); all device memory
+ * of dtype, owned by the caller. Output feature f goes to part p = f / split
+ * at column f - p*split: y0, y1, y2 are row-major [M][split] each, and
+ * Nout = split * parts with 1 <= parts <= 3 (y1 / y2 are ignored, and may be
+ * NULL, when unused). bf16 runs on the matrix cores with fp32 accumulation
+ * and rounds y to nearest even; f32 accumulates with fma in k order.
+ * Requires K % 32 == 0 and split % 4 == 0 (else BRA_ERR_UNSUPPORTED), and
+ * x and w each under 2 GiB. x and w must be 16-byte aligned, the outputs
+ * 8-byte aligned and b 4-byte aligned (BRA_ERR_ALIGN). Errors: BRA_ERR_NULL
+ * for a missing x, w or used output, BRA_ERR_SHAPE for sizes <= 0 or Nout not
+ * 1-3 times split, BRA_ERR_DTYPE, BRA_ERR_POINTER, BRA_ERR_HIP. */
+int bra_linear(const void* x, const void* w, const void* b, int M, int K, int Nout, int split,
+               int dtype, void* y0, void* y1, void* y2);
+
 /* Stream used by every later call from this host thread (a hipStream_t;
  * NULL = the null stream). Always returns BRA_OK. */
 int bra_set_stream(void* stream);
@@ -145,7 +165,8 @@ int bra_version(void);
  * bra_profile_set_mask(mask) changes which kinds are recorded from the next
  * launch on without clearing the record (to sample some launches of a run). */
 enum bra_kernel_kind {
-  BRA_K_POOL = 0, BRA_K_ROUTE = 1, BRA_K_ATTN = 2, BRA_K_LCE = 3, BRA_K_COUNT = 4
+  BRA_K_POOL = 0, BRA_K_ROUTE = 1, BRA_K_ATTN = 2, BRA_K_LCE = 3, BRA_K_LINEAR = 4,
+  BRA_K_COUNT = 5
 };
 int bra_profile_begin(int mask);
 int bra_profile_set_mask(int mask);

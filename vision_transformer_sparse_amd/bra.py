@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libbra.so")
 
 F32, BF16 = 0, 1
 K_POOL, K_ROUTE, K_ATTN, K_LCE = 0, 1, 2, 3
-KERNEL_NAMES = ("pool", "route", "attn", "lce")
+KERNEL_NAMES = ("pool", "route", "attn", "lce", "linear")
 
 _lib = None
 
@@ -29,6 +29,7 @@ _SIGS = {
     "bra_route": (_i, [_vp, _vp, _i, _i, _i, _i, _vp]),
     "bra_attend": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "bra_lce": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
+    "bra_linear": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
     "bra_set_stream": (_i, [_vp]),
     "bra_get_stream": (_vp, []),
     "bra_workspace_bytes": (_sz, [_i, _i, _i]),
@@ -199,6 +200,49 @@ def lce(v, lce_w, lce_b):
     return out
 
 
+def linear(x, w, b, split=None, outs=None):
+    """bra_linear: y = x w^T + b over the last axis of x (float32 or
+    bfloat16). w: (Nout, K); b: (Nout,) or None. The Nout features are
+    returned as Nout // split tensors of shape x.shape[:-1] + (split,)
+    (split defaults to Nout: one tensor)."""
+    _check(x, "x")
+    _check(w, "w", x.dtype, x.device)
+    if b is not None:
+        _check(b, "b", x.dtype, x.device)
+    K = x.shape[-1]
+    M = x.numel() // K if K else 0
+    Nout = w.shape[0]
+    if w.dim() != 2 or w.shape[1] != K or (b is not None and b.numel() != Nout):
+        raise ValueError("w must be (Nout, K) and b (Nout,)")
+    split = Nout if split is None else split
+    if split <= 0 or Nout % split or not 1 <= Nout // split <= 3:
+        raise ValueError("Nout must be 1, 2 or 3 times split")
+    shape = tuple(x.shape[:-1]) + (split,)
+    if outs is None:
+        outs = [torch.empty(shape, dtype=x.dtype, device=x.device) for _ in range(Nout // split)]
+    for i, o in enumerate(outs):
+        _check(o, f"outs[{i}]", x.dtype, x.device)
+        if tuple(o.shape) != shape:
+            raise ValueError("an output has the wrong shape")
+    ys = list(outs) + [None] * (3 - len(outs))
+    with torch.cuda.device(x.device):
+        _stream(x.device)
+        _call("bra_linear", _ptr(x), _ptr(w), _ptr(b), M, K, Nout, split, _dtype_code(x),
+              _ptr(ys[0]), _ptr(ys[1]), _ptr(ys[2]))
+    return tuple(outs)
+
+
+def block_forward(x, wqkv, bqkv, lce_w, lce_b, wo, bo, heads: int, S: int, topk: int):
+    """The BRA block of the walk-through: q, k, v = split(x wqkv^T + bqkv),
+    o = bra_forward(q, k, v) (attention + LCE), y = o wo^T + bo. Three library
+    calls on the current stream; returns (y, route_idx)."""
+    C = x.shape[-1]
+    q, k, v = linear(x, wqkv, bqkv, split=C)
+    o, route_idx = forward(q, k, v, lce_w, lce_b, heads, S, topk)
+    (y,) = linear(o, wo, bo)
+    return y, route_idx
+
+
 def workspace_bytes(N: int, C: int, S: int) -> int:
     return int(load().bra_workspace_bytes(N, C, S))
 
@@ -234,10 +278,11 @@ def profile_set_mask(kinds=KERNEL_NAMES) -> None:
 def profile_read() -> dict:
     """Summed event milliseconds and launch counts per kernel kind since the
     last profile_begin/profile_read (synchronises on the recorded events)."""
-    ms = (ctypes.c_double * 4)()
-    cnt = (ctypes.c_int * 4)()
-    _call("bra_profile_read", ms, cnt, 4)
-    return {KERNEL_NAMES[i]: (ms[i], cnt[i]) for i in range(4)}
+    n = len(KERNEL_NAMES)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int * n)()
+    _call("bra_profile_read", ms, cnt, n)
+    return {KERNEL_NAMES[i]: (ms[i], cnt[i]) for i in range(n)}
 
 
 def calib_copy(src: torch.Tensor, dst: torch.Tensor) -> None:

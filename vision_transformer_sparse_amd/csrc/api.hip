@@ -384,6 +384,36 @@ int bra_lce(const void* v, const void* lce_w, const void* lce_b, int N, int H, i
   return e == hipSuccess ? BRA_OK : hip_fail(e);
 }
 
+int bra_linear(const void* x, const void* w, const void* b, int M, int K, int Nout, int split,
+               int dtype, void* y0, void* y1, void* y2) {
+  if (!x || !w || !y0) return BRA_ERR_NULL;
+  if (dtype != BRA_F32 && dtype != BRA_BF16) return BRA_ERR_DTYPE;
+  if (M <= 0 || K <= 0 || Nout <= 0 || split <= 0) return BRA_ERR_SHAPE;
+  const int parts = Nout / split;
+  if (Nout % split != 0 || parts > 3) return BRA_ERR_SHAPE;
+  if ((parts > 1 && !y1) || (parts > 2 && !y2)) return BRA_ERR_NULL;
+  const long long esz = dtype == BRA_BF16 ? 2 : 4;
+  if (K % 32 != 0 || split % 4 != 0) return BRA_ERR_UNSUPPORTED;
+  if ((long long)M * K * esz >= (1ll << 31) || (long long)Nout * K * esz >= (1ll << 31) ||
+      (long long)M * split * esz >= (1ll << 40))
+    return BRA_ERR_UNSUPPORTED;
+  const void* y1c = parts > 1 ? y1 : nullptr;
+  const void* y2c = parts > 2 ? y2 : nullptr;
+  int rc = check_align({x, w}, {b, y0, y1c, y2c});
+  if (rc) return rc;
+  if (((uintptr_t)y0 | (uintptr_t)y1c | (uintptr_t)y2c) & 7u) return BRA_ERR_ALIGN;
+  rc = check_ptrs({x, w, b, y0, y1c, y2c});
+  if (rc) return rc;
+  hipStream_t st = g_stream;
+  hipError_t e;
+  {
+    ProfScope ps(BRA_K_LINEAR, st);
+    e = bra::launch_linear(x, w, b, M, K, Nout, split, dtype, y0, const_cast<void*>(y1c),
+                           const_cast<void*>(y2c), st);
+  }
+  return e == hipSuccess ? BRA_OK : hip_fail(e);
+}
+
 int bra_set_stream(void* stream) {
   g_stream = static_cast<hipStream_t>(stream);
   return BRA_OK;

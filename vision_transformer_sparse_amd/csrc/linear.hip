@@ -1,0 +1,154 @@
+// The projections around the BRA operator: y = x W^T + b, a Linear layer over
+// the channels of every token. The walk-through at
+// TRANSFORMER.niftyadmin.cn/n/347023.html, section BRA模块, projects the
+// tokens to q and kv with one Linear(C, 3C) and splits the result (q first,
+// then k, then v; the module print in section 网络结构 shows QKVLinear's
+// Linear(64, 192)), and ends the block with the output Linear(C, C) (wo).
+//
+// y's features are written in consecutive blocks of `split` features to up
+// to three outputs (y0: features [0, split), y1: [split, 2 split), y2:
+// [2 split, 3 split)), each a row-major [M][split] matrix, so the q, k and v
+// of the qkv projection come out as three NHWC tensors. The host checks
+// K % 32 == 0, split % 4 == 0, Nout = split * (1, 2 or 3) and that both
+// operands stay under 2 GiB.
+//
+// bf16: the matrix cores. A wave computes 64 tokens x 64 features as 4 x 4
+// tiles of v_mfma_f32_16x16x32_bf16 with D = W_tile . X_tile^T: the A operand
+// is 16 bytes of a weight row and the B operand 16 bytes of a token row (both
+// straight from memory, the channels contiguous), and a lane's D column is
+// four consecutive features of one token -- one 8-byte store. A workgroup of
+// four waves takes 256 tokens x 64 features; the feature blocks of one token
+// block are consecutive units on one XCD, so its L2 serves the token rows to
+// all of them and they come from HBM once.
+// fp32: a lane computes four features of one token with fma chains.
+#include "bra_internal.h"
+
+namespace bra {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLinTok = 256;  // tokens per workgroup (64 per wave)
+constexpr int kLinFeat = 64;  // features per workgroup
+
+struct LinArgs {
+  const uint16_t* x;
+  const uint16_t* w;
+  const uint16_t* b;  // or null
+  uint16_t* y[3];
+  int M, K, Nout, split;
+};
+
+__global__ __launch_bounds__(256) void linear_bf16_kernel(LinArgs a) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int nfb = (a.Nout + kLinFeat - 1) / kLinFeat;
+  const int u = xcd_unit((int)blockIdx.x, (int)gridDim.x);
+  const int tb = u / nfb, fb = u - tb * nfb;
+  const int t0 = tb * kLinTok + wave * 64, f0 = fb * kLinFeat;
+  const uint32_t xbytes = (uint32_t)a.M * a.K * 2, wbytes = (uint32_t)a.Nout * a.K * 2;
+  const Rsrc xr = rsrc(a.x, xbytes), wr = rsrc(a.w, wbytes);
+  // operand rows of this lane: tokens t0 + 16 i + col, features f0 + 16 j + col
+  uint32_t xo[4], wo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 16 * i + col, f = f0 + 16 * i + col;
+    // rows past the end read zeros: kOut plus any k offset stays past both buffers
+    xo[i] = t < a.M ? (uint32_t)t * a.K * 2 + (uint32_t)grp * 16 : kOut;
+    wo[i] = f < a.Nout ? (uint32_t)f * a.K * 2 + (uint32_t)grp * 16 : kOut;
+  }
+  f32x4 acc[4][4];  // [feature tile j][token tile i]
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < a.K; k0 += 32) {
+    bf16x8 xb[4], wb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xb[i] = __builtin_bit_cast(bf16x8, ld16(xr, xo[i] + (uint32_t)k0 * 2));
+      wb[i] = __builtin_bit_cast(bf16x8, ld16(wr, wo[i] + (uint32_t)k0 * 2));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[j], xb[i], acc[j][i], 0, 0, 0);
+  }
+  // lane (col, grp) of tile (j, i): features f0 + 16 j + 4 grp .. + 3 of
+  // token t0 + 16 i + col
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // f is a multiple of 4 and so are Nout and split: the four features
+    // exist and share one output
+    const int f = f0 + 16 * j + 4 * grp;
+    if (f >= a.Nout) continue;
+    float bias[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bias[e] = a.b ? __uint_as_float((uint32_t)a.b[f + e] << 16) : 0.f;
+    const int part = f / a.split, fl = f - part * a.split;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 16 * i + col;
+      if (t >= a.M) continue;
+      uint16_t* yrow = a.y[part] + (size_t)t * a.split + fl;
+      uint32_t v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = float_to_bf16_bits(acc[j][i][e] + bias[e]);
+      *reinterpret_cast<uint2*>(yrow) = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+    }
+  }
+}
+
+struct LinArgsF {
+  const float* x;
+  const float* w;
+  const float* b;
+  float* y[3];
+  int M, K, Nout, split;
+};
+
+// fp32: a thread computes features f .. f+3 of one token
+__global__ __launch_bounds__(256) void linear_f32_kernel(LinArgsF a) {
+  const int nq = a.Nout / 4;
+  const long long g = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= (long long)a.M * nq) return;
+  const int t = (int)(g / nq), f = (int)(g - (long long)t * nq) * 4;
+  const float* xr = a.x + (size_t)t * a.K;
+  float acc[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] = 0.f;
+  for (int k = 0; k < a.K; ++k) {
+    const float xv = xr[k];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(xv, a.w[(size_t)(f + e) * a.K + k], acc[e]);
+  }
+  const int part = f / a.split;
+  float* yrow = a.y[part] + (size_t)t * a.split + (f - part * a.split);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) yrow[e] = acc[e] + (a.b ? a.b[f + e] : 0.f);
+}
+
+}  // namespace
+
+hipError_t launch_linear(const void* x, const void* w, const void* b, int M, int K, int Nout,
+                         int split, int dtype, void* y0, void* y1, void* y2, hipStream_t st) {
+  if (dtype == 1) {
+    LinArgs a;
+    a.x = (const uint16_t*)x; a.w = (const uint16_t*)w; a.b = (const uint16_t*)b;
+    a.y[0] = (uint16_t*)y0; a.y[1] = (uint16_t*)y1; a.y[2] = (uint16_t*)y2;
+    a.M = M; a.K = K; a.Nout = Nout; a.split = split;
+    const unsigned blocks = (unsigned)((M + kLinTok - 1) / kLinTok) * (unsigned)((Nout + kLinFeat - 1) / kLinFeat);
+    launch(linear_bf16_kernel, dim3(blocks), dim3(256), 0, st, a);
+  } else {
+    LinArgsF a;
+    a.x = (const float*)x; a.w = (const float*)w; a.b = (const float*)b;
+    a.y[0] = (float*)y0; a.y[1] = (float*)y1; a.y[2] = (float*)y2;
+    a.M = M; a.K = K; a.Nout = Nout; a.split = split;
+    const long long n = (long long)M * (Nout / 4);
+    launch(linear_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bra
