@@ -17,6 +17,9 @@ One JSON line is printed. It carries:
   cpu_baseline  the fp64 CPU oracle timed on whole-batch passes of the same
              workload (about 10 s of CPU work)
 Other workloads: --config c0..c4 (c1 is the default).
+--op block times the block around the operator instead: the qkv projection
+(Linear C -> 3C, bra_linear), bra_forward, and the output projection (Linear
+C -> C); "kernels" then also holds the projection kernel's roofline.
 """
 from __future__ import annotations
 
@@ -51,12 +54,23 @@ def algorithmic(cfg):
         "pool": {"bytes": 2 * E * b + means},
         "route": {"bytes": means + routes, "flops": 2 * cfg.N * cfg.R * cfg.R * cfg.C},
         "attn": {"bytes": 4 * E * b + routes + lce_params, "flops": 4 * E * cfg.L + 50 * E},
+        # the block's two projections, averaged per launch: qkv reads x and
+        # writes q, k, v; wo reads o and writes y (weights and biases once)
+        "linear": {"bytes": (4 * E + 4 * cfg.C * (cfg.C + 1) + 2 * E) * b / 2,
+                   "flops": 2 * E * 4 * cfg.C / 2},
     }
 
 
 def roofline_for(kind, cfg, ms_per_launch, traffic):
     alg = algorithmic(cfg)[kind]
     t = ms_per_launch * 1e-3
+    if kind == "linear" and cfg.dtype == "bf16":
+        ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        if alg["flops"] / alg["bytes"] > ridge:
+            achieved = alg["flops"] / t / 1e12
+            return {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                    "traffic": traffic, "kernel": kind}
     if kind == "attn":
         mfma_flops = 4 * cfg.N * cfg.H * cfg.W * cfg.C * cfg.L
         if cfg.dtype == "bf16":
@@ -99,7 +113,7 @@ def measured_traffic(cfg_name: str):
         return None
 
 
-def cpu_baseline(inp, cfg, budget_s: float):
+def cpu_baseline(inp, cfg, budget_s: float, op: str = "forward"):
     import numpy as np
     import oracle
     try:
@@ -112,8 +126,13 @@ def cpu_baseline(inp, cfg, budget_s: float):
     passes, t0 = 0, time.perf_counter()
     try:
         while True:
-            oracle.bra_forward(inp["q"], inp["k"], inp["v"], inp["lce_w"], inp["lce_b"],
-                               cfg.heads, cfg.S, cfg.topk)
+            if op == "block":
+                oracle.bra_block_forward(inp["x"], inp["wqkv"], inp["bqkv"], inp["lce_w"],
+                                         inp["lce_b"], inp["wo"], inp["bo"], cfg.heads, cfg.S,
+                                         cfg.topk)
+            else:
+                oracle.bra_forward(inp["q"], inp["k"], inp["v"], inp["lce_w"], inp["lce_b"],
+                                   cfg.heads, cfg.S, cfg.topk)
             passes += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
@@ -123,7 +142,7 @@ def cpu_baseline(inp, cfg, budget_s: float):
     dt = time.perf_counter() - t0
     return {"value": passes * cfg.queries / dt, "unit": "queries/s", "cores": ncores,
             "kind": "oracle",
-            "sample": f"{passes} full pass(es) of the {cfg.name} batch (N={cfg.N}, "
+            "sample": f"{passes} full {op} pass(es) of the {cfg.name} batch (N={cfg.N}, "
                       f"{cfg.queries} queries each), fp64 numpy, {dt:.1f} s"}
 
 
@@ -135,6 +154,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--config", default="c1")
+    ap.add_argument("--op", choices=("forward", "block"), default="forward",
+                    help="forward: bra_forward alone; block: qkv projection, bra_forward, wo")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -149,7 +170,7 @@ def main(argv=None) -> int:
     import numpy as np
     import torch
 
-    from synth import CONFIGS, draw_config
+    from synth import CONFIGS, draw_block, draw_config
     from vision_transformer_sparse_amd import bra
 
     cfg = {c.name: c for c in CONFIGS}[a.config]
@@ -159,15 +180,29 @@ def main(argv=None) -> int:
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    inp = draw_config(cfg)
+    if a.op == "block":
+        inp = draw_block(cfg.N, cfg.H, cfg.W, cfg.C, cfg.S, cfg.dtype, 2000 + CONFIGS.index(cfg),
+                         cfg.offset_std, cfg.w_std, cfg.b_std)
+    else:
+        inp = draw_config(cfg)
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     t = {k: torch.from_numpy(v.astype(np.float32)).to(dev, tdt) for k, v in inp.items()}
-    out = torch.empty_like(t["q"])
+    shape = (cfg.N, cfg.H, cfg.W, cfg.C)
+    out = torch.empty(shape, dtype=tdt, device=dev)
     route = torch.empty((cfg.N, cfg.R, cfg.topk), dtype=torch.int32, device=dev)
+    if a.op == "block":
+        qkv = [torch.empty(shape, dtype=tdt, device=dev) for _ in range(3)]
+        y = torch.empty(shape, dtype=tdt, device=dev)
 
-    def step():
-        bra.forward(t["q"], t["k"], t["v"], t["lce_w"], t["lce_b"], cfg.heads, cfg.S, cfg.topk,
-                    out=out, route_idx=route)
+        def step():
+            bra.linear(t["x"], t["wqkv"], t["bqkv"], split=cfg.C, outs=qkv)
+            bra.forward(*qkv, t["lce_w"], t["lce_b"], cfg.heads, cfg.S, cfg.topk,
+                        out=out, route_idx=route)
+            bra.linear(out, t["wo"], t["bo"], outs=[y])
+    else:
+        def step():
+            bra.forward(t["q"], t["k"], t["v"], t["lce_w"], t["lce_b"], cfg.heads, cfg.S,
+                        cfg.topk, out=out, route_idx=route)
 
     for _ in range(a.warmup):
         step()
@@ -221,7 +256,7 @@ def main(argv=None) -> int:
         kernels[kind].update(bound=r["bound"], achieved=round(r["achieved"], 2), unit=r["unit"],
                              frac=round(r["frac"], 4))
 
-    cpu = cpu_baseline(inp, cfg, a.cpu_budget) if a.cpu_budget > 0 else None
+    cpu = cpu_baseline(inp, cfg, a.cpu_budget, a.op) if a.cpu_budget > 0 else None
     value = cfg.queries * a.steps / elapsed
     line = {
         "metric": METRIC,
@@ -236,7 +271,9 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) q/k/v; see synth/)",
-        "config": {"workload": f"{cfg.name}: {cfg.what}", "N": cfg.N, "H": cfg.H, "W": cfg.W,
+        "config": {"workload": f"{cfg.name}: {cfg.what}"
+                               + (" -- block: qkv Linear, BRA, wo Linear" if a.op == "block" else ""),
+                   "N": cfg.N, "H": cfg.H, "W": cfg.W,
                    "C": cfg.C, "heads": cfg.heads, "S": cfg.S, "topk": cfg.topk,
                    "queries_per_step": cfg.queries, "parallelism": "single GPU"},
         "roofline": roof,

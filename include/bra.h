@@ -123,9 +123,9 @@ int bra_lce(const void* v, const void* lce_w, const void* lce_b,
  * Nout = split * parts with 1 <= parts <= 3 (y1 / y2 are ignored, and may be
  * NULL, when unused). bf16 runs on the matrix cores with fp32 accumulation
  * and rounds y to nearest even; f32 accumulates with fma in k order.
- * Requires K % 32 == 0 and split % 4 == 0 (else BRA_ERR_UNSUPPORTED), and
- * x and w each under 2 GiB. x and w must be 16-byte aligned, the outputs
- * 8-byte aligned and b 4-byte aligned (BRA_ERR_ALIGN). Errors: BRA_ERR_NULL
+ * Requires K % 32 == 0 and split % 8 == 0 (else BRA_ERR_UNSUPPORTED), and
+ * x and w each under 2 GiB. x, w and the outputs must be 16-byte aligned and
+ * b 4-byte aligned (BRA_ERR_ALIGN). Errors: BRA_ERR_NULL
  * for a missing x, w or used output, BRA_ERR_SHAPE for sizes <= 0 or Nout not
  * 1-3 times split, BRA_ERR_DTYPE, BRA_ERR_POINTER, BRA_ERR_HIP. */
 int bra_linear(const void* x, const void* w, const void* b, int M, int K, int Nout, int split,

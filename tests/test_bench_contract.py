@@ -35,3 +35,19 @@ def test_roofline_arithmetic():
     assert r4["bound"] == "mfma" and r4["unit"] == "TFLOP/s" and r4["peak"] == 2500.0
     flops = 4 * c4.N * c4.H * c4.W * c4.C * c4.L
     assert abs(r4["achieved"] - flops / 70e-6 / 1e12) < 1e-6
+
+
+def test_projection_roofline_arithmetic():
+    """The block's two projections per step: qkv reads x (E elements) and
+    writes q, k, v (3E), wo reads o and writes y (2E), plus 4C^2 weights and 4C
+    biases; 8EC flops. Reported per launch (half of that) against HBM: at
+    C = 128 the intensity (about 2C/3 flop per byte) is far below the ridge."""
+    import bench
+    from synth import CONFIGS
+    c1 = CONFIGS[1]
+    E = c1.N * c1.H * c1.W * c1.C
+    alg = bench.algorithmic(c1)["linear"]
+    assert alg["bytes"] == (6 * E + 4 * c1.C * c1.C + 4 * c1.C) * 2 / 2
+    assert alg["flops"] == 8 * E * c1.C / 2
+    r = bench.roofline_for("linear", c1, 0.01, None)
+    assert r["bound"] == "hbm" and abs(r["achieved"] - alg["bytes"] / 10e-6 / 1e9) < 1e-6

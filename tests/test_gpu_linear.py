@@ -64,10 +64,10 @@ LINEAR_CASES = [
     ("one_token", 1, 32, 96, 32, "bf16"),
     ("wo_c64_partial_wave", 77, 64, 64, 64, "bf16"),
     ("nout_72_one_part", 257, 96, 72, 72, "bf16"),
-    ("two_parts", 130, 160, 40, 20, "bf16"),
+    ("two_parts", 130, 160, 48, 24, "bf16"),
     ("qkv_c64_f32", 300, 64, 192, 64, "f32"),
     ("nout_72_f32", 257, 96, 72, 72, "f32"),
-    ("one_token_f32", 1, 32, 12, 4, "f32"),
+    ("one_token_f32", 1, 32, 24, 8, "f32"),
 ]
 
 
@@ -112,6 +112,9 @@ def test_linear_rejects_bad_shapes(gpu_lib):
     w = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError):
         gpu_lib.linear(x, w, None, split=16)            # four parts
+    w = torch.zeros((12, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(gpu_lib.BraError):
+        gpu_lib.linear(x, w, None, split=4)             # split % 8 != 0
 
 
 def run_block(bra, d, heads, S, topk, dtype, images=None, name=""):
@@ -151,8 +154,8 @@ def test_block_small(gpu_lib, case):
 
 def test_block_full_size_sampled(gpu_lib):
     """The block at the 28x28 classification stage's full batch (128 images);
-    the oracle checks three of them (first, middle, last) and the routes of
-    all."""
+    the oracle checks three of them (first, middle, last), routes and
+    outputs."""
     cfg = CONFIGS[1]
     d = draw_block(cfg.N, cfg.H, cfg.W, cfg.C, cfg.S, "bf16", seed=3400, w_std=cfg.w_std,
                    b_std=cfg.b_std)

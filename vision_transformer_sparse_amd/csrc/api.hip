@@ -36,6 +36,10 @@ hipError_t launch_attend_image(const void* q, const void* k, const void* v, cons
 hipError_t launch_forward_image(const void* q, const void* k, const void* v, const void* lce_w,
                                 const void* b, const Shape& s, void* out, int32_t* route_out,
                                 hipStream_t st);
+// y = x w^T + b, output features split over y0..y2 in blocks of split
+// (linear.hip)
+hipError_t launch_linear(const void* x, const void* w, const void* b, int M, int K, int Nout,
+                         int split, int dtype, void* y0, void* y1, void* y2, hipStream_t st);
 bool tile_kernel_supports(const Shape& s);
 bool f32_kernel_supports(const Shape& s);
 hipError_t launch_attend_f32(const void* q, const void* k, const void* v, const void* w,
@@ -393,7 +397,7 @@ int bra_linear(const void* x, const void* w, const void* b, int M, int K, int No
   if (Nout % split != 0 || parts > 3) return BRA_ERR_SHAPE;
   if ((parts > 1 && !y1) || (parts > 2 && !y2)) return BRA_ERR_NULL;
   const long long esz = dtype == BRA_BF16 ? 2 : 4;
-  if (K % 32 != 0 || split % 4 != 0) return BRA_ERR_UNSUPPORTED;
+  if (K % 32 != 0 || split % 8 != 0) return BRA_ERR_UNSUPPORTED;
   if ((long long)M * K * esz >= (1ll << 31) || (long long)Nout * K * esz >= (1ll << 31) ||
       (long long)M * split * esz >= (1ll << 40))
     return BRA_ERR_UNSUPPORTED;
@@ -401,7 +405,7 @@ int bra_linear(const void* x, const void* w, const void* b, int M, int K, int No
   const void* y2c = parts > 2 ? y2 : nullptr;
   int rc = check_align({x, w}, {b, y0, y1c, y2c});
   if (rc) return rc;
-  if (((uintptr_t)y0 | (uintptr_t)y1c | (uintptr_t)y2c) & 7u) return BRA_ERR_ALIGN;
+  if (((uintptr_t)y0 | (uintptr_t)y1c | (uintptr_t)y2c) & 15u) return BRA_ERR_ALIGN;
   rc = check_ptrs({x, w, b, y0, y1c, y2c});
   if (rc) return rc;
   hipStream_t st = g_stream;

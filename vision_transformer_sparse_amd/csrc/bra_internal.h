@@ -61,8 +61,6 @@ hipError_t launch_attend(const void* q, const void* k, const void* v,
 hipError_t launch_lce(const void* v, const void* w, const void* b,
                       const Shape& s, int dtype, float* out, hipStream_t st);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
-hipError_t launch_linear(const void* x, const void* w, const void* b, int M, int K, int Nout,
-                         int split, int dtype, void* y0, void* y1, void* y2, hipStream_t st);
 
 // Device helpers ------------------------------------------------------------
 #if defined(__HIPCC__)

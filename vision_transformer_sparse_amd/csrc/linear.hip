@@ -9,14 +9,17 @@
 // to three outputs (y0: features [0, split), y1: [split, 2 split), y2:
 // [2 split, 3 split)), each a row-major [M][split] matrix, so the q, k and v
 // of the qkv projection come out as three NHWC tensors. The host checks
-// K % 32 == 0, split % 4 == 0, Nout = split * (1, 2 or 3) and that both
-// operands stay under 2 GiB.
+// K % 32 == 0, split % 8 == 0, Nout = split * (1, 2 or 3), that both
+// operands stay under 2 GiB, and 16-byte aligned outputs.
 //
 // bf16: the matrix cores. A wave computes 64 tokens x 64 features as 4 x 4
 // tiles of v_mfma_f32_16x16x32_bf16 with D = W_tile . X_tile^T: the A operand
 // is 16 bytes of a weight row and the B operand 16 bytes of a token row (both
 // straight from memory, the channels contiguous), and a lane's D column is
-// four consecutive features of one token -- one 8-byte store. A workgroup of
+// four consecutive features of one token. The wave stages its tile in LDS
+// and stores it back as 16-byte pieces of whole 128-byte rows (a row's 64
+// features), so every store fills whole cache lines. The next k step's
+// operands load while the current step's products run. A workgroup of
 // four waves takes 256 tokens x 64 features; the feature blocks of one token
 // block are consecutive units on one XCD, so its L2 serves the token rows to
 // all of them and they come from HBM once.
@@ -41,6 +44,11 @@ struct LinArgs {
 };
 
 __global__ __launch_bounds__(256) void linear_bf16_kernel(LinArgs a) {
+  // this wave's 64 x 64 output tile, staged for row-contiguous stores; the
+  // row pitch of 72 elements (144 bytes) keeps rows 16-byte aligned and
+  // spreads a tile column's 16 tokens over 16 bank groups
+  constexpr int kPitch = 72;
+  __shared__ __align__(16) uint16_t tile[4][64 * kPitch];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
   const int nfb = (a.Nout + kLinFeat - 1) / kLinFeat;
@@ -58,44 +66,85 @@ __global__ __launch_bounds__(256) void linear_bf16_kernel(LinArgs a) {
     xo[i] = t < a.M ? (uint32_t)t * a.K * 2 + (uint32_t)grp * 16 : kOut;
     wo[i] = f < a.Nout ? (uint32_t)f * a.K * 2 + (uint32_t)grp * 16 : kOut;
   }
+  // this lane's bias words (features f0 + 16 j + 4 grp .. + 3), loaded before
+  // the products so their latency hides behind them; Nout % 8 == 0, so the
+  // four features are all in range or all out
+  uint32_t bw[4][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int f = f0 + 16 * j + 4 * grp;
+    const bool has = a.b && f < a.Nout;
+    const uint32_t* bp = reinterpret_cast<const uint32_t*>(a.b + (has ? f : 0));
+    bw[j][0] = has ? bp[0] : 0u;
+    bw[j][1] = has ? bp[1] : 0u;
+  }
   f32x4 acc[4][4];  // [feature tile j][token tile i]
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < a.K; k0 += 32) {
-    bf16x8 xb[4], wb[4];
+  // two operand sets: one k step's products run while the next step's
+  // operands load. A step at or past K loads zeros (its offsets moved past
+  // the buffers), so it adds nothing and needs no branch.
+  bf16x8 xa[4], wa[4], xb[4], wb[4];
+  auto load = [&](bf16x8* xs, bf16x8* ws, int k) {
+    const uint32_t kb = k < a.K ? (uint32_t)k * 2 : kOut;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      xb[i] = __builtin_bit_cast(bf16x8, ld16(xr, xo[i] + (uint32_t)k0 * 2));
-      wb[i] = __builtin_bit_cast(bf16x8, ld16(wr, wo[i] + (uint32_t)k0 * 2));
+      xs[i] = __builtin_bit_cast(bf16x8, ld16(xr, xo[i] + kb));
+      ws[i] = __builtin_bit_cast(bf16x8, ld16(wr, wo[i] + kb));
     }
+  };
+  auto mma = [&](const bf16x8* xs, const bf16x8* ws) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[j], xb[i], acc[j][i], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ws[j], xs[i], acc[j][i], 0, 0, 0);
+  };
+  // (the scheduling barriers keep each load batch ahead of the products
+  // that overlap it)
+  load(xa, wa, 0);
+  for (int k0 = 0; k0 < a.K; k0 += 64) {
+    load(xb, wb, k0 + 32);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(xa, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    load(xa, wa, k0 + 64);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(xb, wb);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // lane (col, grp) of tile (j, i): features f0 + 16 j + 4 grp .. + 3 of
-  // token t0 + 16 i + col
+  // lane (col, grp) of tile (j, i) holds features 16 j + 4 grp .. + 3 (of
+  // the block) of token 16 i + col: bias, round, and stage 8 bytes
+  uint16_t* tw = tile[wave];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    // f is a multiple of 4 and so are Nout and split: the four features
-    // exist and share one output
-    const int f = f0 + 16 * j + 4 * grp;
-    if (f >= a.Nout) continue;
-    float bias[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) bias[e] = a.b ? __uint_as_float((uint32_t)a.b[f + e] << 16) : 0.f;
-    const int part = f / a.split, fl = f - part * a.split;
+    const int fl = 16 * j + 4 * grp;
+    const float bias[4] = {bf16_lo(bw[j][0]), bf16_hi(bw[j][0]), bf16_lo(bw[j][1]), bf16_hi(bw[j][1])};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 16 * i + col;
-      if (t >= a.M) continue;
-      uint16_t* yrow = a.y[part] + (size_t)t * a.split + fl;
       uint32_t v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = float_to_bf16_bits(acc[j][i][e] + bias[e]);
-      *reinterpret_cast<uint2*>(yrow) = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+      *reinterpret_cast<uint2*>(tw + (16 * i + col) * kPitch + fl) =
+          make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // 16-byte chunks: lane -> row 8 p + lane / 8, features 8 (lane % 8) .. + 7;
+  // split % 8 == 0 keeps a chunk inside one output
+  const int c8 = (lane & 7) * 8, f = f0 + c8;
+  if (f < a.Nout) {
+    const int part = f / a.split, fo = f - part * a.split;
+    uint16_t* ybase = a.y[part] + fo;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int r = 8 * p + (lane >> 3), t = t0 + r;
+      const uint4 v = *reinterpret_cast<const uint4*>(tw + r * kPitch + c8);
+      if (t < a.M) *reinterpret_cast<uint4*>(ybase + (size_t)t * a.split) = v;
     }
   }
 }
