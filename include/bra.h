@@ -123,7 +123,8 @@ int bra_lce(const void* v, const void* lce_w, const void* lce_b,
  * Nout = split * parts with 1 <= parts <= 3 (y1 / y2 are ignored, and may be
  * NULL, when unused). bf16 runs on the matrix cores with fp32 accumulation
  * and rounds y to nearest even; f32 accumulates with fma in k order.
- * Requires K % 32 == 0 and split % 8 == 0 (else BRA_ERR_UNSUPPORTED), and
+ * Requires K % 32 == 0, split % 8 == 0 and, for bf16, K <= 256 (else
+ * BRA_ERR_UNSUPPORTED), and
  * x and w each under 2 GiB. x, w and the outputs must be 16-byte aligned and
  * b 4-byte aligned (BRA_ERR_ALIGN). Errors: BRA_ERR_NULL
  * for a missing x, w or used output, BRA_ERR_SHAPE for sizes <= 0 or Nout not

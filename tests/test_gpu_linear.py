@@ -65,6 +65,7 @@ LINEAR_CASES = [
     ("wo_c64_partial_wave", 77, 64, 64, 64, "bf16"),
     ("nout_72_one_part", 257, 96, 72, 72, "bf16"),
     ("two_parts", 130, 160, 48, 24, "bf16"),
+    ("k_256_max", 200, 256, 128, 128, "bf16"),
     ("qkv_c64_f32", 300, 64, 192, 64, "f32"),
     ("nout_72_f32", 257, 96, 72, 72, "f32"),
     ("one_token_f32", 1, 32, 24, 8, "f32"),
@@ -115,6 +116,10 @@ def test_linear_rejects_bad_shapes(gpu_lib):
     w = torch.zeros((12, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(gpu_lib.BraError):
         gpu_lib.linear(x, w, None, split=4)             # split % 8 != 0
+    x = torch.zeros((10, 288), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((64, 288), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(gpu_lib.BraError):
+        gpu_lib.linear(x, w, None)                      # bf16 K > 256
 
 
 def run_block(bra, d, heads, S, topk, dtype, images=None, name=""):

@@ -398,6 +398,7 @@ int bra_linear(const void* x, const void* w, const void* b, int M, int K, int No
   if ((parts > 1 && !y1) || (parts > 2 && !y2)) return BRA_ERR_NULL;
   const long long esz = dtype == BRA_BF16 ? 2 : 4;
   if (K % 32 != 0 || split % 8 != 0) return BRA_ERR_UNSUPPORTED;
+  if (dtype == BRA_BF16 && K > 256) return BRA_ERR_UNSUPPORTED;
   if ((long long)M * K * esz >= (1ll << 31) || (long long)Nout * K * esz >= (1ll << 31) ||
       (long long)M * split * esz >= (1ll << 40))
     return BRA_ERR_UNSUPPORTED;

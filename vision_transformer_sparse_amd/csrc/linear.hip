@@ -14,15 +14,16 @@
 //
 // bf16: the matrix cores. A wave computes 64 tokens x 64 features as 4 x 4
 // tiles of v_mfma_f32_16x16x32_bf16 with D = W_tile . X_tile^T: the A operand
-// is 16 bytes of a weight row and the B operand 16 bytes of a token row (both
-// straight from memory, the channels contiguous), and a lane's D column is
-// four consecutive features of one token. The wave stages its tile in LDS
-// and stores it back as 16-byte pieces of whole 128-byte rows (a row's 64
+// is 16 bytes of a weight row (from LDS, where the workgroup puts its 64
+// weight rows once for its four waves) and the B operand 16 bytes of a token
+// row (straight from memory, channels contiguous); a lane's D column is four
+// consecutive features of one token. The wave stages its tile in LDS and
+// stores it back as 16-byte pieces of whole 128-byte rows (a row's 64
 // features), so every store fills whole cache lines. The next k step's
 // operands load while the current step's products run. A workgroup of
 // four waves takes 256 tokens x 64 features; the feature blocks of one token
 // block are consecutive units on one XCD, so its L2 serves the token rows to
-// all of them and they come from HBM once.
+// all of them and they come from HBM once. K is at most 256.
 // fp32: a lane computes four features of one token with fma chains.
 #include "bra_internal.h"
 
@@ -44,11 +45,14 @@ struct LinArgs {
 };
 
 __global__ __launch_bounds__(256) void linear_bf16_kernel(LinArgs a) {
-  // this wave's 64 x 64 output tile, staged for row-contiguous stores; the
-  // row pitch of 72 elements (144 bytes) keeps rows 16-byte aligned and
-  // spreads a tile column's 16 tokens over 16 bank groups
+  // LDS: first the workgroup's 64 weight rows (row pitch 2K + 16 bytes, so a
+  // tile column's 16 rows fall in distinct bank groups), shared by its four
+  // waves; after the products, each wave's 64 x 64 output tile, staged for
+  // row-contiguous stores (row pitch 72 elements = 144 bytes: rows stay
+  // 16-byte aligned and a tile column's 16 tokens spread over the banks).
+  // K <= 256 keeps the weight rows inside the same 36 KiB.
   constexpr int kPitch = 72;
-  __shared__ __align__(16) uint16_t tile[4][64 * kPitch];
+  __shared__ __align__(16) uint8_t lds[4 * 64 * kPitch * 2];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
   const int nfb = (a.Nout + kLinFeat - 1) / kLinFeat;
@@ -57,14 +61,33 @@ __global__ __launch_bounds__(256) void linear_bf16_kernel(LinArgs a) {
   const int t0 = tb * kLinTok + wave * 64, f0 = fb * kLinFeat;
   const uint32_t xbytes = (uint32_t)a.M * a.K * 2, wbytes = (uint32_t)a.Nout * a.K * 2;
   const Rsrc xr = rsrc(a.x, xbytes), wr = rsrc(a.w, wbytes);
-  // operand rows of this lane: tokens t0 + 16 i + col, features f0 + 16 j + col
-  uint32_t xo[4], wo[4];
+  const int wpitch = 2 * a.K + 16;
+  {
+    // the weight rows f0 .. f0 + 63 in 16-byte chunks (at most 8 a thread for
+    // K <= 256), all loads issued before the first LDS write; rows past Nout
+    // and chunks past the tile read zeros
+    const int cpr = a.K / 8, chunks = 64 * cpr;
+    uint4 v[8];
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int c = tid + 256 * n, r = c / cpr, q = c - r * cpr, f = f0 + r;
+      v[n] = ld16(wr, c < chunks && f < a.Nout ? (uint32_t)f * a.K * 2 + (uint32_t)q * 16 : kOut);
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int c = tid + 256 * n, r = c / cpr, q = c - r * cpr;
+      if (c < chunks) *reinterpret_cast<uint4*>(lds + r * wpitch + q * 16) = v[n];
+    }
+  }
+  // operand rows of this lane: tokens t0 + 16 i + col (HBM), features
+  // f0 + 16 j + col (LDS)
+  uint32_t xo[4], wl[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int t = t0 + 16 * i + col, f = f0 + 16 * i + col;
-    // rows past the end read zeros: kOut plus any k offset stays past both buffers
+    const int t = t0 + 16 * i + col;
+    // rows past the end read zeros: kOut plus any k offset stays past the buffer
     xo[i] = t < a.M ? (uint32_t)t * a.K * 2 + (uint32_t)grp * 16 : kOut;
-    wo[i] = f < a.Nout ? (uint32_t)f * a.K * 2 + (uint32_t)grp * 16 : kOut;
+    wl[i] = (uint32_t)((16 * i + col) * wpitch + grp * 16);
   }
   // this lane's bias words (features f0 + 16 j + 4 grp .. + 3), loaded before
   // the products so their latency hides behind them; Nout % 8 == 0, so the
@@ -83,16 +106,19 @@ __global__ __launch_bounds__(256) void linear_bf16_kernel(LinArgs a) {
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
   // two operand sets: one k step's products run while the next step's
-  // operands load. A step at or past K loads zeros (its offsets moved past
-  // the buffers), so it adds nothing and needs no branch.
+  // operands load. A step at or past K loads zero token rows (their offsets
+  // moved past the buffer) against weights of step 0 (finite), so it adds
+  // nothing and needs no branch.
   bf16x8 xa[4], wa[4], xb[4], wb[4];
   auto load = [&](bf16x8* xs, bf16x8* ws, int k) {
-    const uint32_t kb = k < a.K ? (uint32_t)k * 2 : kOut;
+    const bool in = k < a.K;
+    const uint32_t kb = in ? (uint32_t)k * 2 : kOut, kw = in ? (uint32_t)k * 2 : 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       xs[i] = __builtin_bit_cast(bf16x8, ld16(xr, xo[i] + kb));
-      ws[i] = __builtin_bit_cast(bf16x8, ld16(wr, wo[i] + kb));
+      ws[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(lds + wl[i] + kw));
     }
   };
   auto mma = [&](const bf16x8* xs, const bf16x8* ws) {
@@ -114,9 +140,10 @@ __global__ __launch_bounds__(256) void linear_bf16_kernel(LinArgs a) {
     mma(xb, wb);
     __builtin_amdgcn_sched_barrier(0);
   }
+  __syncthreads();  // every wave is done with the weight rows
   // lane (col, grp) of tile (j, i) holds features 16 j + 4 grp .. + 3 (of
   // the block) of token 16 i + col: bias, round, and stage 8 bytes
-  uint16_t* tw = tile[wave];
+  uint16_t* tw = reinterpret_cast<uint16_t*>(lds) + wave * 64 * kPitch;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int fl = 16 * j + 4 * grp;
