@@ -18,8 +18,9 @@
 // weight rows once for its four waves) and the B operand 16 bytes of a token
 // row (straight from memory, channels contiguous); a lane's D column is four
 // consecutive features of one token. The wave stages its tile in LDS and
-// stores it back as 16-byte pieces of whole 128-byte rows (a row's 64
-// features), so every store fills whole cache lines. The next k step's
+// stores it back as 16-byte pieces of the tile's 128-byte rows (64 features
+// of a token), so the stores fill whole cache lines (when split is a multiple
+// of 64 and the outputs 128-byte aligned, as torch allocates them). The next k step's
 // operands load while the current step's products run. A workgroup of
 // four waves takes 256 tokens x 64 features; the feature blocks of one token
 // block are consecutive units on one XCD, so its L2 serves the token rows to
