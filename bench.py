@@ -1,22 +1,35 @@
 """Throughput of the BRA forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c4]
 
 A step is one bra_forward call -- region pooling, routing, gathered attention
 and LCE -- over one batch of seeded synthetic input already resident in HBM.
-W untimed steps, then K steps timed between two device synchronisations.
+The headline workload is c4 (segmentation stage 1: 8 images of 128x128, 64
+channels, 2 heads, 8x8 regions of 256 tokens, topk 4): the largest single-GPU
+workload, and the one whose attention is bound by the matrix cores.
+
+Order of the run:
+  1. per_config: every workload c0..c4 is measured in turn -- warm steps
+     timed back to back, every kernel kind timed with HIP events, and cold
+     steps (each after a 1 GiB write that flushes L2 and the memory-side
+     cache) timed with events around the whole step and around the
+     attention kernel. This also brings the GPU's clocks to steady state.
+  2. headline: W untimed warm-up steps of the headline workload, then K
+     steps timed between two device synchronisations.
 One JSON line is printed. It carries:
-  value      whole-job queries/s (a query is one token position, N*H*W per step)
-  roofline   the attention kernel's (the dominant kernel's) algorithmic bytes
-             (or flops) per launch over its mean launch time, measured with HIP
-             events on the launch stream on every PROFILE_EVERY-th step of the
-             timed region (the library launches a timed kernel with
-             hipExtLaunchKernelGGL, which ties the event pair to that dispatch);
-             the other kernels are timed the same way in a separate pass after
-             it (the "kernels" object)
-  cpu_baseline  the fp64 CPU oracle timed on whole-batch passes of the same
-             workload (about 10 s of CPU work)
-Other workloads: --config c0..c4 (c1 is the default).
+  value      whole-job queries/s of the K timed steps (a query is one token
+             position, N*H*W per step)
+  roofline   the attention kernel's (the dominant kernel's) algorithmic flops
+             (c4; bytes for the HBM-bound workloads) per launch over its mean
+             launch time, measured with HIP events on the launch stream on
+             every PROFILE_EVERY-th step of the timed region (the library
+             launches a timed kernel with hipExtLaunchKernelGGL, which ties
+             the event pair to that dispatch)
+  per_config per workload: warm ms/step and queries/s, cold step and
+             attention medians (p10, p90), and each kernel kind's us per
+             launch and fraction of the roofline that bounds it
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the headline
+             workload (about 10 s of CPU work), threads and CPU model stated
 --op block times the block around the operator instead: the qkv projection
 (Linear C -> 3C, bra_linear), bra_forward, and the output projection (Linear
 C -> C); "kernels" then also holds the projection kernel's roofline.
@@ -38,6 +51,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
 PROFILE_EVERY = 4
+FLUSH_BYTES = 1 << 30
 ATTN_SOURCES = ("attn_image.hip", "attn_region.hip", "attn_tile.hip", "attn_mfma.hip", "attn_valu.hip",
                 "attn_f32.hip", "bra_internal.h", "route_common.h")
 
@@ -113,15 +127,35 @@ def measured_traffic(cfg_name: str):
         return None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads() -> int:
+    """Threads for the oracle's BLAS pool: every core of the process's
+    affinity set, capped by OMP_NUM_THREADS where the host sets it (a shared
+    host states the share of its cores a job may use that way)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return n
+
+
 def cpu_baseline(inp, cfg, budget_s: float, op: str = "forward"):
-    import numpy as np
     import oracle
     try:
-        from threadpoolctl import threadpool_info, threadpool_limits
+        from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_limits = None
-    ncores = len(os.sched_getaffinity(0))
-    ncores = min(ncores, 16)
+    ncores = cpu_threads()
     ctx = threadpool_limits(limits=ncores) if threadpool_limits else None
     passes, t0 = 0, time.perf_counter()
     try:
@@ -141,21 +175,132 @@ def cpu_baseline(inp, cfg, budget_s: float, op: str = "forward"):
             ctx.__exit__(None, None, None)
     dt = time.perf_counter() - t0
     return {"value": passes * cfg.queries / dt, "unit": "queries/s", "cores": ncores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "affinity_cores": len(os.sched_getaffinity(0)),
             "sample": f"{passes} full {op} pass(es) of the {cfg.name} batch (N={cfg.N}, "
                       f"{cfg.queries} queries each), fp64 numpy, {dt:.1f} s"}
+
+
+def pctl(xs, p):
+    xs = sorted(xs)
+    if not xs:
+        return None
+    i = min(len(xs) - 1, max(0, int(round(p / 100.0 * (len(xs) - 1)))))
+    return xs[i]
+
+
+class Workload:
+    """Device tensors and the step function of one workload."""
+
+    def __init__(self, cfg, op, dev, inputs=None):
+        import numpy as np
+        import torch
+
+        from synth import CONFIGS, draw_block, draw_config
+        from vision_transformer_sparse_amd import bra
+
+        self.cfg = cfg
+        if inputs is None:
+            if op == "block":
+                inputs = draw_block(cfg.N, cfg.H, cfg.W, cfg.C, cfg.S, cfg.dtype,
+                                    2000 + CONFIGS.index(cfg), cfg.offset_std, cfg.w_std, cfg.b_std)
+            else:
+                inputs = draw_config(cfg)
+        self.inputs = inputs
+        tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        t = {k: torch.from_numpy(v.astype(np.float32)).to(dev, tdt) for k, v in inputs.items()}
+        shape = (cfg.N, cfg.H, cfg.W, cfg.C)
+        out = torch.empty(shape, dtype=tdt, device=dev)
+        route = torch.empty((cfg.N, cfg.R, cfg.topk), dtype=torch.int32, device=dev)
+        if op == "block":
+            qkv = [torch.empty(shape, dtype=tdt, device=dev) for _ in range(3)]
+            y = torch.empty(shape, dtype=tdt, device=dev)
+
+            def step():
+                bra.linear(t["x"], t["wqkv"], t["bqkv"], split=cfg.C, outs=qkv)
+                bra.forward(*qkv, t["lce_w"], t["lce_b"], cfg.heads, cfg.S, cfg.topk,
+                            out=out, route_idx=route)
+                bra.linear(out, t["wo"], t["bo"], outs=[y])
+        else:
+            def step():
+                bra.forward(t["q"], t["k"], t["v"], t["lce_w"], t["lce_b"], cfg.heads, cfg.S,
+                            cfg.topk, out=out, route_idx=route)
+        self.step = step
+
+
+def kernel_rooflines(prof, cfg):
+    kernels = {}
+    for kind, (ms, cnt) in prof.items():
+        if cnt:
+            us = ms * 1e3 / cnt
+            r = roofline_for(kind, cfg, us * 1e-3, None)
+            kernels[kind] = {"us_per_launch": round(us, 3), "launches": cnt, "bound": r["bound"],
+                             "achieved": round(r["achieved"], 2), "unit": r["unit"],
+                             "frac": round(r["frac"], 4)}
+    return kernels
+
+
+def measure_config(w, flush, n_warm, n_cold):
+    """Warm and cold timings of one workload (see the module docstring)."""
+    import torch
+
+    from vision_transformer_sparse_amd import bra
+
+    cfg = w.cfg
+    for _ in range(n_warm // 2):
+        w.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_warm):
+        w.step()
+    torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - t0) * 1e3 / n_warm
+    bra.profile_begin(bra.KERNEL_NAMES)
+    for _ in range(max(20, n_warm // 4)):
+        w.step()
+    kernels = kernel_rooflines(bra.profile_read(), cfg)
+    bra.profile_begin(())
+    # cold: a 1 GiB write before each step; events around the step (torch's
+    # current stream, which the binding hands to the library) and around the
+    # attention kernel (the library's event pair on its dispatch)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_cold)]
+    attn_us = []
+    for a, b in ev:
+        flush.zero_()
+        bra.profile_begin(["attn"])
+        a.record()
+        w.step()
+        b.record()
+        ms, cnt = bra.profile_read()["attn"]
+        if cnt:
+            attn_us.append(ms * 1e3 / cnt)
+    bra.profile_begin(())
+    torch.cuda.synchronize()
+    cold_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    cold = {"step_us_median": round(pctl(cold_us, 50), 3), "step_us_p10": round(pctl(cold_us, 10), 3),
+            "step_us_p90": round(pctl(cold_us, 90), 3), "calls": n_cold,
+            "queries_per_s": cfg.queries / (pctl(cold_us, 50) * 1e-6)}
+    if attn_us:
+        med = pctl(attn_us, 50)
+        r = roofline_for("attn", cfg, med * 1e-3, None)
+        cold.update(attn_us_median=round(med, 3), attn_us_p10=round(pctl(attn_us, 10), 3),
+                    attn_us_p90=round(pctl(attn_us, 90), 3), attn_frac=round(r["frac"], 4))
+    return {"ms_per_step": round(warm_ms, 5), "queries_per_s": cfg.queries / (warm_ms * 1e-3),
+            "queries_per_step": cfg.queries, "kernels": kernels, "cold": cold}
 
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the GPU's clocks settle over tens of milliseconds of load: the defaults
-    # warm up for ~50 ms and time ~100 ms
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--config", default="c1")
+    ap.add_argument("--warmup", type=int, default=500)
+    ap.add_argument("--config", default="c4", help="headline workload (c0..c4)")
     ap.add_argument("--op", choices=("forward", "block"), default="forward",
                     help="forward: bra_forward alone; block: qkv projection, bra_forward, wo")
+    ap.add_argument("--per-config", choices=("all", "none"), default="all",
+                    help="all: measure every workload first (per_config); none: the headline only")
+    ap.add_argument("--cold", type=int, default=100, help="cold calls per workload in per_config")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -167,43 +312,39 @@ def main(argv=None) -> int:
               "but this build runs on one device)", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
-    from synth import CONFIGS, draw_block, draw_config
+    from synth import CONFIGS
     from vision_transformer_sparse_amd import bra
 
-    cfg = {c.name: c for c in CONFIGS}[a.config]
+    by_name = {c.name: c for c in CONFIGS}
+    cfg = by_name[a.config]
     bra.load()
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if a.op == "block":
-        inp = draw_block(cfg.N, cfg.H, cfg.W, cfg.C, cfg.S, cfg.dtype, 2000 + CONFIGS.index(cfg),
-                         cfg.offset_std, cfg.w_std, cfg.b_std)
-    else:
-        inp = draw_config(cfg)
-    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-    t = {k: torch.from_numpy(v.astype(np.float32)).to(dev, tdt) for k, v in inp.items()}
-    shape = (cfg.N, cfg.H, cfg.W, cfg.C)
-    out = torch.empty(shape, dtype=tdt, device=dev)
-    route = torch.empty((cfg.N, cfg.R, cfg.topk), dtype=torch.int32, device=dev)
-    if a.op == "block":
-        qkv = [torch.empty(shape, dtype=tdt, device=dev) for _ in range(3)]
-        y = torch.empty(shape, dtype=tdt, device=dev)
 
-        def step():
-            bra.linear(t["x"], t["wqkv"], t["bqkv"], split=cfg.C, outs=qkv)
-            bra.forward(*qkv, t["lce_w"], t["lce_b"], cfg.heads, cfg.S, cfg.topk,
-                        out=out, route_idx=route)
-            bra.linear(out, t["wo"], t["bo"], outs=[y])
-    else:
-        def step():
-            bra.forward(t["q"], t["k"], t["v"], t["lce_w"], t["lce_b"], cfg.heads, cfg.S,
-                        cfg.topk, out=out, route_idx=route)
+    per_config = {}
+    head = None
+    if a.per_config == "all":
+        flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        for c in CONFIGS:
+            w = Workload(c, a.op, dev)
+            per_config[c.name] = measure_config(w, flush, n_warm=1000, n_cold=a.cold)
+            print(f"[bench] per_config {c.name}: {per_config[c.name]['ms_per_step'] * 1e3:.2f} us/step warm, "
+                  f"{per_config[c.name]['cold']['step_us_median']:.2f} us cold", file=sys.stderr, flush=True)
+            if c is cfg:
+                head = w
+            else:
+                del w
+        del flush
+        torch.cuda.synchronize()
+    if head is None:
+        head = Workload(cfg, a.op, dev)
 
+    step = head.step
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -224,13 +365,13 @@ def main(argv=None) -> int:
     elapsed = time.perf_counter() - t0
     prof_timed = bra.profile_read()
     bra.profile_begin(())
-    print(f"[bench] {cfg.name} timed {a.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+    print(f"[bench] {cfg.name} timed {a.steps} steps in {elapsed:.4f} s", file=sys.stderr, flush=True)
 
     # every kernel kind, in a separate (untimed) pass
     bra.profile_begin(bra.KERNEL_NAMES)
     for _ in range(max(10, a.steps // 4)):
         step()
-    prof_all = bra.profile_read()
+    kernels = kernel_rooflines(bra.profile_read(), cfg)
     bra.profile_begin(())
 
     if a.calib_copy_mb > 0:
@@ -242,21 +383,13 @@ def main(argv=None) -> int:
         del src, dst
 
     ms_step = elapsed * 1e3 / a.steps
-    kernels = {}
-    for kind, (ms, cnt) in prof_all.items():
-        if cnt:
-            kernels[kind] = {"us_per_launch": ms * 1e3 / cnt, "launches": cnt}
     attn_ms, attn_cnt = prof_timed["attn"]
     attn_ms_per_launch = attn_ms / attn_cnt
     roof = roofline_for("attn", cfg, attn_ms_per_launch, measured_traffic(cfg.name))
     roof["us_per_launch"] = attn_ms_per_launch * 1e3
     roof["launches"] = attn_cnt
-    for kind in kernels:
-        r = roofline_for(kind, cfg, kernels[kind]["us_per_launch"] * 1e-3, None)
-        kernels[kind].update(bound=r["bound"], achieved=round(r["achieved"], 2), unit=r["unit"],
-                             frac=round(r["frac"], 4))
 
-    cpu = cpu_baseline(inp, cfg, a.cpu_budget, a.op) if a.cpu_budget > 0 else None
+    cpu = cpu_baseline(head.inputs, cfg, a.cpu_budget, a.op) if a.cpu_budget > 0 else None
     value = cfg.queries * a.steps / elapsed
     line = {
         "metric": METRIC,
@@ -279,6 +412,7 @@ def main(argv=None) -> int:
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "per_config": per_config,
         "attention_source_sha256_16": source_digest(),
     }
     print(json.dumps(line), flush=True)

@@ -123,6 +123,8 @@ int bra_lce(const void* v, const void* lce_w, const void* lce_b,
  * Nout = split * parts with 1 <= parts <= 3 (y1 / y2 are ignored, and may be
  * NULL, when unused). bf16 runs on the matrix cores with fp32 accumulation
  * and rounds y to nearest even; f32 accumulates with fma in k order.
+ * The outputs must not alias x, w or b (they are written while x is still
+ * being read by other workgroups).
  * Requires K % 32 == 0, split % 8 == 0 and, for bf16, K <= 256 (else
  * BRA_ERR_UNSUPPORTED), and
  * x and w each under 2 GiB. x, w and the outputs must be 16-byte aligned and
@@ -138,9 +140,9 @@ int bra_set_stream(void* stream);
 void* bra_get_stream(void);
 
 /* Bytes of library workspace bra_forward needs: two fp32 [N][S*S][C]
- * arrays (region means), 256-byte aligned, then 170*C bytes of LCE weights
- * repacked for the attention kernels (pixel-pair and tap-major layouts).
- * Returns 0 for invalid sizes. */
+ * arrays (region means), 256-byte aligned, then 490*C bytes of LCE weights
+ * repacked for the attention kernels (pixel-pair, tap-major and Toeplitz
+ * layouts). Returns 0 for invalid sizes. */
 size_t bra_workspace_bytes(int N, int C, int S);
 
 /* Frees the library workspace of every device (synchronises each device

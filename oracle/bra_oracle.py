@@ -37,7 +37,8 @@ design notes of the repository):
 * H and W must be divisible by S (no padding branch);
 * the key/value downsampling hook is the identity and qk_dim = C.
 
-Parity pins for every function live in tests/test_oracle.py.
+Parity pins for every function live in tests/oracle_pins.py (run by
+tests/test_oracle.py).
 """
 from __future__ import annotations
 
@@ -89,9 +90,9 @@ def unpartition(xp: np.ndarray, S: int, H: int, W: int) -> np.ndarray:
 
 
 def region_means(xp: np.ndarray) -> np.ndarray:
-    """Q^r or K^r: the mean over each region's tokens, per channel -- "not an
-    average over channels but over the region's vectors" (section BRA模块,
-    q_win / k_win). (N, R, T, C) -> (N, R, C)."""
+    """Q^r or K^r: for each channel separately, the mean over the T tokens of
+    the region; the channels are never averaged together (walk-through,
+    section BRA模块, q_win / k_win). (N, R, T, C) -> (N, R, C)."""
     return xp.sum(axis=2) / xp.shape[2]
 
 

@@ -4,7 +4,9 @@
 
 Every .hip file under csrc/ is compiled to an object in _build/ and the
 objects are linked into vision_transformer_sparse_amd/libbra.so (in-tree, so
-the library travels with the source tree). The build always recompiles.
+the library travels with the source tree). The hardware probes in micro/ are
+built, with the same flags, into micro/libbra_micro.so. The build always
+recompiles.
 """
 from __future__ import annotations
 
@@ -20,6 +22,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbra.so")
+MICRO_SRC = os.path.join(PKG, "micro", "probes.hip")
+MICRO_LIB = os.path.join(PKG, "micro", "libbra_micro.so")
 ARCH = "gfx950"
 
 CFLAGS = [
@@ -70,6 +74,10 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    # the hardware probes: a library of their own, built with the same flags
+    tmp = MICRO_LIB + ".tmp"
+    _run([cc, *CFLAGS, "-shared", MICRO_SRC, "-o", tmp], verbose)
+    os.replace(tmp, MICRO_LIB)
     return LIB
 
 

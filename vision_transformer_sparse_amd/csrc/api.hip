@@ -5,6 +5,7 @@
 
 #include <math.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -195,7 +196,16 @@ int check_align(std::initializer_list<const void*> p16, std::initializer_list<co
   return BRA_OK;
 }
 
+// Test hook: with BRA_TEST_FAIL_ALLOC=1 in the environment the workspace
+// request fails as an out-of-memory allocation would (BRA_ERR_HIP), before
+// anything is allocated or launched, so the error path can be exercised.
+bool fail_alloc_for_test() {
+  const char* v = getenv("BRA_TEST_FAIL_ALLOC");
+  return v && v[0] == '1' && v[1] == '\0';
+}
+
 int workspace(size_t bytes, void** ptr) {
+  if (fail_alloc_for_test()) return hip_fail(hipErrorOutOfMemory);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e);
@@ -258,37 +268,43 @@ int attend(const void* q, const void* k, const void* v, const void* w, const voi
   return e == hipSuccess ? BRA_OK : hip_fail(e);
 }
 
-}  // namespace
-
-extern "C" {
-
-int bra_forward(const void* q, const void* k, const void* v, const void* lce_w,
-                const void* lce_b, int N, int H, int W, int C, int heads, int S,
-                int topk, int dtype, void* out, int32_t* route_idx) {
+// Argument checks of bra_forward (and of its allocation-free variant).
+int check_forward(const void* q, const void* k, const void* v, const void* lce_w,
+                  const void* lce_b, int N, int H, int W, int C, int heads, int S, int topk,
+                  int dtype, const void* out, const int32_t* route_idx, bra::Shape* s) {
   if (!q || !k || !v || !lce_w || !out || !route_idx) return BRA_ERR_NULL;
-  bra::Shape s;
-  int rc = check_dims(N, H, W, C, heads, S, topk, dtype, true, true, &s);
+  int rc = check_dims(N, H, W, C, heads, S, topk, dtype, true, true, s);
   if (rc) return rc;
   rc = check_align({q, k, v, lce_w, out}, {lce_b, route_idx});
   if (rc) return rc;
-  rc = check_ptrs({q, k, v, lce_w, lce_b, out, route_idx});
-  if (rc) return rc;
-  hipStream_t st = g_stream;
+  return check_ptrs({q, k, v, lce_w, lce_b, out, route_idx});
+}
+
+// Does this shape run as the one kernel that needs no workspace?
+bool forward_one_kernel(const bra::Shape& s, int dtype) {
+  return dtype == BRA_BF16 && bra::image_kernel_routes(s);
+}
+
+// The one-kernel forward: it pools and routes its own images (the route
+// kernel's logit and selection code) and reports the routes to route_idx.
+int forward_one(const void* q, const void* k, const void* v, const void* lce_w, const void* lce_b,
+                const bra::Shape& s, void* out, int32_t* route_idx, hipStream_t st) {
   hipError_t e;
-  if (dtype == BRA_BF16 && bra::image_kernel_routes(s)) {
-    // one kernel: it pools and routes its own images (the route kernel's
-    // logit and selection code) and reports the routes to route_idx
-    {
-      ProfScope ps(BRA_K_ATTN, st);
-      e = bra::launch_forward_image(q, k, v, lce_w, lce_b, s, out, route_idx, st);
-    }
-    return e == hipSuccess ? BRA_OK : hip_fail(e);
+  {
+    ProfScope ps(BRA_K_ATTN, st);
+    e = bra::launch_forward_image(q, k, v, lce_w, lce_b, s, out, route_idx, st);
   }
-  std::lock_guard<std::mutex> lk(g_ws_mutex);
+  return e == hipSuccess ? BRA_OK : hip_fail(e);
+}
+
+// Pool, route and attend with a workspace of ws_layout(N, C, S).total bytes
+// at ws (256-byte aligned).
+int forward_staged(const void* q, const void* k, const void* v, const void* lce_w,
+                   const void* lce_b, const bra::Shape& s, int dtype, void* out,
+                   int32_t* route_idx, void* ws, hipStream_t st) {
+  const int N = s.N, C = s.C, S = s.S, topk = s.topk;
   const WsLayout wl = ws_layout(N, C, S);
-  void* ws = nullptr;
-  rc = workspace(wl.total, &ws);
-  if (rc) return rc;
+  hipError_t e;
   float* qr = static_cast<float*>(ws);
   float* kr = qr + (size_t)N * s.R * C;
   uint32_t* wpk = dtype == BRA_BF16 ? reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + wl.wpk) : nullptr;
@@ -303,6 +319,26 @@ int bra_forward(const void* q, const void* k, const void* v, const void* lce_w,
   }
   if (e != hipSuccess) return hip_fail(e);
   return attend(q, k, v, lce_w, lce_b, route_idx, s, dtype, out, wpk, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int bra_forward(const void* q, const void* k, const void* v, const void* lce_w,
+                const void* lce_b, int N, int H, int W, int C, int heads, int S,
+                int topk, int dtype, void* out, int32_t* route_idx) {
+  bra::Shape s;
+  int rc = check_forward(q, k, v, lce_w, lce_b, N, H, W, C, heads, S, topk, dtype, out,
+                         route_idx, &s);
+  if (rc) return rc;
+  hipStream_t st = g_stream;
+  if (forward_one_kernel(s, dtype)) return forward_one(q, k, v, lce_w, lce_b, s, out, route_idx, st);
+  std::lock_guard<std::mutex> lk(g_ws_mutex);
+  void* ws = nullptr;
+  rc = workspace(ws_layout(N, C, S).total, &ws);
+  if (rc) return rc;
+  return forward_staged(q, k, v, lce_w, lce_b, s, dtype, out, route_idx, ws, st);
 }
 
 int bra_region_means(const void* q, const void* k, int N, int H, int W, int C, int S,

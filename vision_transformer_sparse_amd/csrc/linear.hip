@@ -86,7 +86,8 @@ __global__ __launch_bounds__(256) void linear_bf16_kernel(LinArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = t0 + 16 * i + col;
-    // rows past the end read zeros: kOut plus any k offset stays past the buffer
+    // rows past the end read zeros: kOut plus an in-range k offset (< 2^31)
+    // stays past the buffer
     xo[i] = t < a.M ? (uint32_t)t * a.K * 2 + (uint32_t)grp * 16 : kOut;
     wl[i] = (uint32_t)((16 * i + col) * wpitch + grp * 16);
   }
@@ -109,9 +110,10 @@ __global__ __launch_bounds__(256) void linear_bf16_kernel(LinArgs a) {
     for (int i = 0; i < 4; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
   // two operand sets: one k step's products run while the next step's
-  // operands load. A step at or past K loads zero token rows (their offsets
-  // moved past the buffer) against weights of step 0 (finite), so it adds
-  // nothing and needs no branch.
+  // operands load. A load at or past K reads zero token rows (their offsets
+  // moved past the buffer) and is never multiplied: when K % 64 == 32 the
+  // loop's second half-step is skipped (a wave-uniform branch), so weights
+  // are only ever multiplied by real token values.
   bf16x8 xa[4], wa[4], xb[4], wb[4];
   auto load = [&](bf16x8* xs, bf16x8* ws, int k) {
     const bool in = k < a.K;
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(256) void linear_bf16_kernel(LinArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     load(xa, wa, k0 + 64);
     __builtin_amdgcn_sched_barrier(0);
-    mma(xb, wb);
+    if (k0 + 32 < a.K) mma(xb, wb);
     __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();  // every wave is done with the weight rows
