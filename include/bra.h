@@ -71,7 +71,8 @@ enum bra_status {
   BRA_ERR_UNSUPPORTED = -5, /* outside the compiled envelope (see above) */
   BRA_ERR_HIP = -6,         /* a HIP launch or allocation failed */
   BRA_ERR_POINTER = -7,     /* a tensor pointer is not device memory */
-  BRA_ERR_ALIGN = -8        /* a tensor pointer is misaligned (see above) */
+  BRA_ERR_ALIGN = -8,       /* a tensor pointer is misaligned (see above) */
+  BRA_ERR_SCRATCH = -9      /* bra_forward_noalloc: workspace beyond its static array */
 };
 
 /* The whole forward pass, steps 1-8 above.
@@ -84,6 +85,25 @@ int bra_forward(const void* q, const void* k, const void* v,
                 const void* lce_w, const void* lce_b,
                 int N, int H, int W, int C, int heads, int S, int topk,
                 int dtype, void* out, int32_t* route_idx);
+
+/* bra_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, hosts that forbid allocation):
+ * same arguments, checks, results and routes as bra_forward, but the
+ * workspace is a static device array of BRA_NOALLOC_SCRATCH_BYTES (16 MiB)
+ * that each device the library runs on holds until the process ends. The
+ * call never allocates or frees memory (no hipMalloc, hipFree or allocating
+ * library routine) and records no profiling events. Shapes whose workspace
+ * (bra_workspace_bytes) exceeds the array return BRA_ERR_SCRATCH before any
+ * launch; shapes that run as one kernel need no workspace at all. All calls
+ * on one device share that device's array and nothing serialises them on
+ * the device: calls that overlap on one GPU (two streams, or two host
+ * threads) race on it and give undefined results. Every kernel writes the
+ * scratch it later reads, so nothing needs clearing between calls. */
+#define BRA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int bra_forward_noalloc(const void* q, const void* k, const void* v,
+                        const void* lce_w, const void* lce_b,
+                        int N, int H, int W, int C, int heads, int S, int topk,
+                        int dtype, void* out, int32_t* route_idx);
 
 /* Step 2 alone: qr, kr = region means of q and k, fp32 [N][S*S][C] each
  * (caller-owned device buffers). Same checks as bra_forward (heads and topk

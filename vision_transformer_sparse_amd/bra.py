@@ -25,6 +25,7 @@ _lib = None
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 _SIGS = {
     "bra_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
+    "bra_forward_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "bra_region_means": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "bra_route": (_i, [_vp, _vp, _i, _i, _i, _i, _vp]),
     "bra_attend": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),

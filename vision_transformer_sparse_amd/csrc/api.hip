@@ -93,6 +93,9 @@ struct KindRecord {
 };
 std::mutex g_prof_mutex;
 int g_prof_mask = 0;  // bit k: record events around kernels of kind k
+// set on this thread during bra_forward_noalloc: no event is created or
+// recorded inside it
+thread_local bool g_no_prof = false;
 KindRecord g_prof[BRA_K_COUNT];
 
 // Arms the event pair of one record slot for the next kernel this thread
@@ -103,7 +106,7 @@ struct ProfScope {
   hipStream_t st;
   int slot = -1;
   ProfScope(int kind_, hipStream_t st_) : kind(kind_), st(st_) {
-    if (!(g_prof_mask & (1 << kind))) return;
+    if (g_no_prof || !(g_prof_mask & (1 << kind))) return;
     std::lock_guard<std::mutex> lk(g_prof_mutex);
     KindRecord& rec = g_prof[kind];
     if (rec.used >= kMaxEvents) return;
@@ -321,6 +324,34 @@ int forward_staged(const void* q, const void* k, const void* v, const void* lce_
   return attend(q, k, v, lce_w, lce_b, route_idx, s, dtype, out, wpk, st);
 }
 
+// ---- the allocation-free forward ------------------------------------------
+// Its workspace is this file-scope device array: every device the library
+// runs on holds one copy, at its own address, until the process ends. In
+// host code the name is only a host-side handle; the device address is
+// looked up once per device (hipGetSymbolAddress, with that device current)
+// and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[BRA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return hip_fail(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lk(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return BRA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -337,6 +368,26 @@ int bra_forward(const void* q, const void* k, const void* v, const void* lce_w,
   std::lock_guard<std::mutex> lk(g_ws_mutex);
   void* ws = nullptr;
   rc = workspace(ws_layout(N, C, S).total, &ws);
+  if (rc) return rc;
+  return forward_staged(q, k, v, lce_w, lce_b, s, dtype, out, route_idx, ws, st);
+}
+
+int bra_forward_noalloc(const void* q, const void* k, const void* v, const void* lce_w,
+                        const void* lce_b, int N, int H, int W, int C, int heads, int S,
+                        int topk, int dtype, void* out, int32_t* route_idx) {
+  bra::Shape s;
+  int rc = check_forward(q, k, v, lce_w, lce_b, N, H, W, C, heads, S, topk, dtype, out,
+                         route_idx, &s);
+  if (rc) return rc;
+  hipStream_t st = g_stream;
+  struct NoProf {
+    NoProf() { g_no_prof = true; }
+    ~NoProf() { g_no_prof = false; }
+  } np;
+  if (forward_one_kernel(s, dtype)) return forward_one(q, k, v, lce_w, lce_b, s, out, route_idx, st);
+  if (ws_layout(N, C, S).total > (size_t)BRA_NOALLOC_SCRATCH_BYTES) return BRA_ERR_SCRATCH;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
   if (rc) return rc;
   return forward_staged(q, k, v, lce_w, lce_b, s, dtype, out, route_idx, ws, st);
 }
@@ -492,6 +543,7 @@ const char* bra_error_string(int code) {
     case BRA_ERR_DTYPE: return "unknown dtype (0 = f32, 1 = bf16)";
     case BRA_ERR_UNSUPPORTED: return "outside the compiled envelope (head_dim 32, C <= 1024, S*S <= 1024, topk*T <= 65536)";
     case BRA_ERR_POINTER: return "a tensor pointer is not device memory";
+    case BRA_ERR_SCRATCH: return "the call needs more workspace than the static scratch array holds (BRA_NOALLOC_SCRATCH_BYTES)";
     case BRA_ERR_ALIGN: return "a tensor pointer is misaligned (16 bytes for q, k, v, out, lce_w and region means; 4 for lce_b and route_idx)";
     case BRA_ERR_HIP:
       snprintf(g_msg, sizeof g_msg, "HIP failure: %s", hipGetErrorString(g_last_hip));
