@@ -160,9 +160,11 @@ int bra_set_stream(void* stream);
 void* bra_get_stream(void);
 
 /* Bytes of library workspace bra_forward needs: two fp32 [N][S*S][C]
- * arrays (region means), 256-byte aligned, then 490*C bytes of LCE weights
- * repacked for the attention kernels (pixel-pair, tap-major and Toeplitz
- * layouts). Returns 0 for invalid sizes. */
+ * arrays (region means), the largest squared key norm per (image, region,
+ * head of 32 channels) (fp32 [N][S*S][C/32]), then 490*C bytes of LCE
+ * weights repacked for the attention kernels (pixel-pair, tap-major and
+ * Toeplitz layouts); each part starts 256-byte aligned. Returns 0 for
+ * invalid sizes. */
 size_t bra_workspace_bytes(int N, int C, int S);
 
 /* Frees the library workspace of every device (synchronises each device

@@ -50,9 +50,11 @@ def test_version_and_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    # region means of q and k, then the packed LCE weights (30*C + 25*C/2 +
-    # 80*C dwords)
-    assert lib.bra_workspace_bytes(128, 128, 7) == 2 * 128 * 49 * 128 * 4 + 490 * 128
+    # region means of q and k, the per-(image, region, head) key norms, then
+    # the packed LCE weights (30*C + 25*C/2 + 80*C dwords); parts 256-aligned
+    assert lib.bra_workspace_bytes(128, 128, 7) == 2 * 128 * 49 * 128 * 4 + 128 * 49 * 4 * 4 + 490 * 128
+    # 2*1*4*64*4 = 2048 bytes of means, 1*4*2*4 = 32 bytes of norms padded to 256
+    assert lib.bra_workspace_bytes(1, 64, 2) == 2048 + 256 + 490 * 64
     assert lib.bra_workspace_bytes(0, 128, 7) == 0
 
 

@@ -349,3 +349,21 @@ def test_failed_workspace_allocation_leaves_outputs_untouched(gpu_lib, monkeypat
     ref = oracle.bra_forward(inp["q"], inp["k"], inp["v"], inp["lce_w"], inp["lce_b"], heads, S,
                              topk, route_override=r)
     check_output(got, ref["out"], "bf16")
+
+
+@pytest.mark.parametrize("H,S", [(64, 4), (32, 4)], ids=["16x16_regions", "8x8_regions"])
+def test_forward_bound_far_above_scores(gpu_lib, H, S):
+    """Queries long along one channel of each head, keys long along another:
+    |q| |k| (the bound the large-region kernel takes as its softmax maximum)
+    lies hundreds of base-2 units above every real score, so the P of the
+    first pass underflow and the kernel must take its exact two-pass way
+    (each query's maximum score first). Routes and outputs against the
+    oracle."""
+    N, C, heads, topk = 2, 64, 2, 2
+    inp = draw(N, H, H, C, S, "bf16", seed=5151)
+    q, k = inp["q"].copy(), inp["k"].copy()
+    for hh in range(heads):
+        q[..., 32 * hh] = 40.0
+        k[..., 32 * hh + 1] = 40.0
+    inp = dict(inp, q=q, k=k)
+    run_forward(gpu_lib, inp, heads, S, topk, "bf16", name=f"bound_far_{H}")

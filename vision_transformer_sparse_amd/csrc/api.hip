@@ -46,9 +46,10 @@ bool f32_kernel_supports(const Shape& s);
 hipError_t launch_attend_f32(const void* q, const void* k, const void* v, const void* w,
                              const void* b, const int32_t* route, const Shape& s, void* out,
                              hipStream_t st);
+// kn: max |k|^2 per (image, region, head) from the pool kernel, or null
 hipError_t launch_attend_tile(const void* q, const void* k, const void* v, const uint32_t* wpk,
-                              const void* b, const int32_t* route, const Shape& s, void* out,
-                              hipStream_t st);
+                              const void* b, const int32_t* route, const float* kn, const Shape& s,
+                              void* out, hipStream_t st);
 size_t lce_pack_bytes(int C);
 hipError_t launch_lce_pack(const void* w, int C, uint32_t* wpk, hipStream_t st);
 
@@ -234,24 +235,29 @@ int workspace(size_t bytes, void** ptr) {
   return BRA_OK;
 }
 
-// Workspace layout: fp32 region means of q and k ([N][S*S][C] each), then the
-// LCE weights packed for the small-region kernel (30*C dwords).
+// Workspace layout: fp32 region means of q and k ([N][S*S][C] each), the
+// largest squared key norm per (image, region, head of 32 channels)
+// ([N][S*S][C/32] fp32), then the LCE weights packed for the attention
+// kernels; each part 256-byte aligned.
 struct WsLayout {
-  size_t means, wpk, total;
+  size_t means, kn, wpk, total;
 };
 WsLayout ws_layout(int N, int C, int S) {
   WsLayout l;
   l.means = (size_t)2 * N * S * S * C * sizeof(float);
-  l.wpk = (l.means + 255) & ~(size_t)255;
+  l.kn = (l.means + 255) & ~(size_t)255;
+  const size_t kn_end = l.kn + (size_t)N * S * S * (C / 32) * sizeof(float);
+  l.wpk = (kn_end + 255) & ~(size_t)255;
   l.total = l.wpk + bra::lce_pack_bytes(C);
   return l;
 }
 
 // Attention + LCE over given routes (wpk: packed LCE weights, required by the
-// small-region kernel).
+// small-region kernels; kn: per-region key norms for the large-region
+// kernel's fixed softmax maximum, or null).
 int attend(const void* q, const void* k, const void* v, const void* w, const void* b,
            const int32_t* route, const bra::Shape& s, int dtype, void* out, const uint32_t* wpk,
-           hipStream_t st) {
+           const float* kn, hipStream_t st) {
   hipError_t e;
   {
     ProfScope ps(BRA_K_ATTN, st);
@@ -260,7 +266,7 @@ int attend(const void* q, const void* k, const void* v, const void* w, const voi
     else if (dtype == BRA_BF16 && wpk && bra::region_kernel_supports(s))
       e = bra::launch_attend_region(q, k, v, wpk, b, route, s, out, st);
     else if (dtype == BRA_BF16 && wpk && bra::tile_kernel_supports(s))
-      e = bra::launch_attend_tile(q, k, v, wpk, b, route, s, out, st);
+      e = bra::launch_attend_tile(q, k, v, wpk, b, route, kn, s, out, st);
     else if (dtype == BRA_BF16 && bra::mfma_supports(s))
       e = bra::launch_attend_mfma(q, k, v, w, b, route, s, out, st);
     else if (dtype == BRA_F32 && bra::f32_kernel_supports(s))
@@ -311,9 +317,13 @@ int forward_staged(const void* q, const void* k, const void* v, const void* lce_
   float* qr = static_cast<float*>(ws);
   float* kr = qr + (size_t)N * s.R * C;
   uint32_t* wpk = dtype == BRA_BF16 ? reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + wl.wpk) : nullptr;
+  // key norms only where the large-region kernel will run
+  const bool tile = dtype == BRA_BF16 && !bra::image_kernel_supports(s) && !bra::region_kernel_supports(s) &&
+                    bra::tile_kernel_supports(s);
+  float* kn = tile ? reinterpret_cast<float*>(static_cast<char*>(ws) + wl.kn) : nullptr;
   {
     ProfScope ps(BRA_K_POOL, st);
-    e = bra::launch_region_pool(q, k, s, dtype, qr, kr, lce_w, wpk, st);
+    e = bra::launch_region_pool(q, k, s, dtype, qr, kr, lce_w, wpk, kn, st);
   }
   if (e != hipSuccess) return hip_fail(e);
   {
@@ -321,7 +331,7 @@ int forward_staged(const void* q, const void* k, const void* v, const void* lce_
     e = bra::launch_route(qr, kr, N, s.R, C, topk, route_idx, st);
   }
   if (e != hipSuccess) return hip_fail(e);
-  return attend(q, k, v, lce_w, lce_b, route_idx, s, dtype, out, wpk, st);
+  return attend(q, k, v, lce_w, lce_b, route_idx, s, dtype, out, wpk, kn, st);
 }
 
 // ---- the allocation-free forward ------------------------------------------
@@ -406,7 +416,7 @@ int bra_region_means(const void* q, const void* k, int N, int H, int W, int C, i
   hipError_t e;
   {
     ProfScope ps(BRA_K_POOL, st);
-    e = bra::launch_region_pool(q, k, s, dtype, qr, kr, nullptr, nullptr, st);
+    e = bra::launch_region_pool(q, k, s, dtype, qr, kr, nullptr, nullptr, nullptr, st);
   }
   return e == hipSuccess ? BRA_OK : hip_fail(e);
 }
@@ -451,9 +461,9 @@ int bra_attend(const void* q, const void* k, const void* v, const void* lce_w,
     uint32_t* wpk = static_cast<uint32_t*>(ws);
     hipError_t e = bra::launch_lce_pack(lce_w, C, wpk, st);
     if (e != hipSuccess) return hip_fail(e);
-    return attend(q, k, v, lce_w, lce_b, route_idx, s, dtype, out, wpk, st);
+    return attend(q, k, v, lce_w, lce_b, route_idx, s, dtype, out, wpk, nullptr, st);
   }
-  return attend(q, k, v, lce_w, lce_b, route_idx, s, dtype, out, nullptr, st);
+  return attend(q, k, v, lce_w, lce_b, route_idx, s, dtype, out, nullptr, nullptr, st);
 }
 
 int bra_lce(const void* v, const void* lce_w, const void* lce_b, int N, int H, int W,

@@ -5,16 +5,29 @@
 // BRA模块: each query region attends, per head, to the tokens of its topk
 // routed regions (topk*T keys, one joint softmax), plus LCE(V).
 //
-// One workgroup per (image, region, head): 8 waves for regions of 128 or
-// more tokens (so that a wave keeps at most two 16-query blocks in registers
-// and four waves share a SIMD), else 4. The gathered keys are walked in
-// 64-key tiles: 256 threads fetch a tile's K and V rows by route index (16
-// bytes each) one tile ahead into registers, then park them in LDS
-// row-major. A K operand is one 16-byte LDS read; a V^T operand (eight
-// consecutive keys of one channel per lane) is two transposing LDS reads
-// (ds_read_b64_tr_b16: the 16 lanes of a group read a 4-key x 16-channel
-// block and each gets one channel's 4 keys). Each wave owns T/64 blocks of
-// 16 queries and reuses every K / V^T operand read for all of them:
+// One workgroup of four waves per (image, region, head, query slab): a wave
+// owns one 16-query block, or two when region rows are 16 tokens long (then
+// its two blocks are two rows of one column band), so a workgroup covers 64
+// or 128 queries and a larger region is cut into slabs of whole rows. Small
+// workgroups keep four independent ones on each CU, in different phases of
+// their tile loops, so one's matrix-core work overlaps another's softmax.
+// The gathered keys are walked in 64-key tiles, loaded straight into LDS
+// (buffer loads with the LDS as destination: no registers hold them) one
+// tile ahead of the one being computed, in two tile buffers, one workgroup
+// barrier a tile. (The compiler makes every LDS read wait for all loads into
+// LDS issued before it, so a step reads its operands first and then starts
+// the next tile's loads.)
+// The K tile is stored in the matrix cores' operand order: the 16-byte
+// slot (x, c, col) at x*1024 + c*256 + col*16 holds chunk c (dims 8c..8c+7)
+// of the key that row col of score tile x takes, so an A-operand read is
+// one contiguous KiB per wave -- the pattern gfx950's LDS serves at its full
+// 256 bytes per clock (16 rows x one chunk per 16 lanes runs at half that).
+// The V tile is row-major, one key's 64 bytes a row with its four 16-byte
+// chunks XOR-swizzled by the row (chunk c of row r at c ^ swz(r)), for the
+// transposing V^T reads (ds_read_b64_tr_b16: 4 rows x 16 channels per 16
+// lanes; these run at 128 bytes per clock whatever the layout). The loads
+// into LDS place every chunk where it belongs. Each wave reuses every K /
+// V^T operand read for its query blocks:
 //
 //   S^T(16 keys x 16 queries) = K (A: lane = key row) x Q^T (B: lane = query)
 //   O^T(16 dims x 16 queries) += V^T (A) x P^T (B),   sum(P) via ones x P^T
@@ -22,20 +35,28 @@
 // Inside each 32-key block the K rows fed to the two score tiles are
 // permuted (tile 0 row 4g+e <- key 8g+e, tile 1 row 4g+e <- key 8g+4+e) so
 // that a lane's eight scores are eight CONSECUTIVE keys: P^T needs no
-// shuffle. Softmax in fp32, base 2, online across tiles; P is rounded to
-// bf16 for the products and the row sums are taken over that same bf16 P on
-// the matrix cores. The running maximum m is raised only when a score may
-// exceed it by more than kTau (then P may reach 2^kTau, which bf16 and the
-// fp32 sums hold). Whether one may is first decided from norms: a scaled
-// score is at most qscale*|q|*max|k| (Cauchy-Schwarz), with |q| computed
-// once and max|k| per tile by the waves that load it; only when that bound
-// exceeds m + kTau somewhere in the wave (always on the first tile) is the
-// tile's exact maximum taken (a maximum3 tree and two cross-half lane
-// swaps) and the accumulators rescaled.
+// shuffle.
+//
+// Softmax with a fixed maximum per query. Every scaled score is at most
+// qscale * |q| * max |k| over the routed keys (Cauchy-Schwarz); the pool
+// kernel reports max |k|^2 per (image, region, head), so a query's bound m
+// is known before its first key, and P = 2^(s*qscale - m) <= 1 needs no
+// running maximum, no rescaling and no per-tile check: per score one fma,
+// one v_exp_f32 and half a packed bf16 conversion. P is rounded to bf16 for
+// the products and the row sums are taken over that same bf16 P on the
+// matrix cores. The bound can sit far above the true maximum (a query
+// nearly orthogonal to long keys); then the P of that query underflow.
+// Whenever some query's row sum ends below 2^-64 -- i.e. its largest score
+// lies more than 64 (base 2) under the bound -- the workgroup runs the exact
+// way instead: one pass over the keys for each query's maximum score, then
+// the softmax pass again with m = that maximum. Without reported norms (the
+// stage entry point that takes given routes) it starts that way.
 //
 // LCE (5x5 depthwise, zero padding 2, bias): the head's 32 channels of the
-// V halo (RH+4 x RW+4 pixels) are staged as horizontal pixel pairs and the
-// weights as matching pairs, so each lane's output takes 15 packed-bf16 dot
+// slab's V halo (its rows +- 2, RW+4 pixels wide) are loaded into LDS in the
+// first tile step, behind the keys; after the last tile they are repacked
+// into the freed tile buffers as horizontal pixel pairs, and with the
+// weights as matching pairs each lane's output takes 15 packed-bf16 dot
 // products per channel. Workgroups of one image are numbered onto one XCD.
 #include "bra_internal.h"
 
@@ -47,8 +68,20 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kKStr = 40;   // K and V tile row stride (bf16): 32 dims + 8 pad
-constexpr float kTau = 64.f;  // slack of the running maximum (log2 units); 2^64 * keys << FLT_MAX
+constexpr int kTileBytes = 64 * 64;  // one 64-key tile of K (or V): 64 rows of 64 bytes
+constexpr float kUnderflow = 5.421010862427522e-20f;  // 2^-64
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8): no vector memory and no LDS operation outstanding
+constexpr int kVmcnt0 = 0x0070;
+
+// The workgroup barrier of the tile loop: the caller's s_waitcnt has already
+// drained this wave's loads into LDS and its LDS reads, and the empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
@@ -61,17 +94,6 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
 }
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-// maximum over the 64 lanes, wave-uniform: quad swaps, half-row and row
-// mirrors, then row broadcasts 15 and 31 carry it into lane 63
-__device__ __forceinline__ float wave_max(float x) {
-  x = dpp_max<0xb1, 0xf>(x);   // quad_perm [1,0,3,2]
-  x = dpp_max<0x4e, 0xf>(x);   // quad_perm [2,3,0,1]
-  x = dpp_max<0x141, 0xf>(x);  // row_half_mirror
-  x = dpp_max<0x140, 0xf>(x);  // row_mirror
-  x = dpp_max<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
-  x = dpp_max<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 // squared norm of eight bf16 (a 16-byte piece)
 __device__ __forceinline__ float sq8(uint4 v) {
@@ -86,14 +108,26 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // Transposing LDS read: within each group of 16 lanes, lanes 4r..4r+3 give
 // the address of row r's 16 consecutive bf16 (4 each); lane i gets element i
 // of rows 0..3.
-__device__ __forceinline__ bf16x4 ld_tr(const uint16_t* p) {
+__device__ __forceinline__ bf16x4 ld_tr(const char* p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(const_cast<uint16_t*>(p)));
+      (__attribute__((address_space(3))) s16x4*)(const_cast<char*>(p)));
   return __builtin_bit_cast(bf16x4, v);
 }
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
                                          __builtin_bit_cast(bf16x2, b), c, false);
+}
+// Chunk swizzle of tile row r: rows 8g..8g+7 take XOR mask 0, 2, 1, 3 for
+// g % 4 = 0, 1, 2, 3. Bytes of (row r, chunk c): r * 64 + ((c ^ swz(r)) << 4).
+__device__ __forceinline__ int swz(int r) {
+  const int g = (r >> 3) & 3;
+  return ((g & 1) << 1) | (g >> 1);
+}
+__device__ __forceinline__ int tile_off(int r, int c) { return r * 64 + ((c ^ swz(r)) << 4); }
+// The key (0..63 within a tile) that row `row` of score tile x (0..3) takes:
+// tile 2b+o, row 4g+e <- key 32b + 8g + 4o + e (see the permutation above)
+__device__ __forceinline__ int score_key(int x, int row) {
+  return 32 * (x >> 1) + 8 * (row >> 2) + 4 * (x & 1) + (row & 3);
 }
 
 struct TileArgs {
@@ -103,6 +137,7 @@ struct TileArgs {
   const uint32_t* wpk;  // LCE weights as dot2 pairs: [2 parity][15 (row, pair)][C]
   const uint16_t* b;
   const int32_t* route;  // [N][S*S][topk]
+  const float* kn;       // [N][S*S][heads] max |k|^2 of each region's head slice, or null
   uint16_t* out;
   int N, H, W, C, heads, S, topk;
   float qscale;  // head_dim^-1/2 * log2(e)
@@ -110,52 +145,83 @@ struct TileArgs {
 
 __host__ __device__ constexpr size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
+// which pass over the keys: each query's maximum score, or the softmax
+struct MaxTag { static constexpr bool value = true; };
+struct SoftTag { static constexpr bool value = false; };
+
+constexpr int kTileWaves = 4;
+constexpr int kBufs = 2;                     // tile buffers: one computed, one landing
+constexpr int kBufBytes = 2 * kTileBytes;    // K rows, then V rows of one 64-key tile
+// query blocks of 16 per wave, and query slabs per region
+template <int RH, int RW>
+constexpr int tile_qbw() { return RW == 16 ? 2 : 1; }
+template <int RH, int RW>
+constexpr int tile_slabs() { return RH * RW / (16 * kTileWaves * tile_qbw<RH, RW>()); }
+// LCE halo of a slab of SR query rows, (SR + 4) x (RW + 4) pixels of the
+// head's 32 channels: as loaded (64 bytes a pixel) and as pixel pairs
+__host__ __device__ constexpr size_t halo_raw_bytes(int SR, int RW) { return (size_t)(SR + 4) * (RW + 4) * 64; }
+__host__ __device__ constexpr size_t halo_bytes(int SR, int RW) {
+  return (size_t)(SR + 4) * ((RW + 5) / 2) * 32 * 4;
+}
+
 struct TileLds {
-  size_t ks, vs, knorm, halo, wts, total;
+  size_t tiles, halo, raw, wts, flag, rbase, total;
 };
-__host__ __device__ inline TileLds tile_lds(int RH, int RW) {
+// The halo is loaded into `raw` at the start and repacked into pixel pairs
+// in the tile buffers after the last tile. The route table (topk entries)
+// goes last, so the other offsets stay constant.
+__host__ __device__ inline TileLds tile_lds(int SR, int RW, int topk) {
   TileLds l;
   size_t o = 0;
-  l.ks = o; o += align16((size_t)2 * 64 * kKStr * 2);
-  l.vs = o; o += align16((size_t)2 * 64 * kKStr * 2);
-  l.knorm = o; o += align16((size_t)2 * 4 * 4);
-  l.halo = o; o += align16((size_t)(RH + 4) * ((RW + 5) / 2) * 32 * 4);
+  l.tiles = o; l.halo = o; o += (size_t)kBufs * kBufBytes;
+  l.raw = o; o += halo_raw_bytes(SR, RW);
   l.wts = o; o += align16((size_t)2 * 15 * 32 * 4);
+  l.flag = o; o += 16;
+  l.rbase = o; o += (size_t)4 * topk;
   l.total = o;
   return l;
 }
 
 template <int RH, int RW>
-constexpr int tile_waves() { return RH * RW >= 128 ? 8 : 4; }
-
-template <int RH, int RW>
-__global__ __launch_bounds__((64 * tile_waves<RH, RW>()), 4) void attn_tile_kernel(TileArgs a) {
+__global__ __launch_bounds__(64 * kTileWaves, 4) void attn_tile_kernel(TileArgs a) {
   constexpr int T = RH * RW;
-  constexpr int WAVES = tile_waves<RH, RW>();
-  constexpr int QBW = T / (16 * WAVES);  // query blocks of 16 per wave
-  constexpr int HP = RH + 4, WP = RW + 4, NPAIR = (WP + 1) / 2;
+  constexpr int WAVES = kTileWaves;
+  constexpr int NT = 64 * WAVES;
+  constexpr int QBW = tile_qbw<RH, RW>();
+  constexpr int SLABS = tile_slabs<RH, RW>();
+  constexpr int SR = RH / SLABS;  // region rows per slab
+  constexpr int HP = SR + 4, WP = RW + 4, NPAIR = (WP + 1) / 2;
+  static_assert(SLABS * SR == RH && SR * RW == 16 * WAVES * QBW, "slabs of whole rows");
+  static_assert(halo_bytes(SR, RW) <= (size_t)kBufs * kBufBytes, "the halo fits the tile buffers");
+  static_assert(halo_raw_bytes(SR, RW) % 1024 == 0 && WP % 2 == 0, "whole 1 KiB loads, whole pixel pairs");
+  static_assert(64 % RW == 0, "a tile starts on a region row");
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const TileLds lay = tile_lds(RH, RW);
-  uint16_t* ks = reinterpret_cast<uint16_t*>(smem + lay.ks);    // [2][64][kKStr]
-  uint16_t* vs = reinterpret_cast<uint16_t*>(smem + lay.vs);    // [2][64][kKStr]
-  float* knorm = reinterpret_cast<float*>(smem + lay.knorm);     // [2][4] max |k|^2 per loader wave
-  uint32_t* halo = reinterpret_cast<uint32_t*>(smem + lay.halo);  // [HP][NPAIR][32]
+  const TileLds lay = tile_lds(SR, RW, a.topk);
+  char* tiles = smem + lay.tiles;  // [kBufs][K: 64 rows x 64 bytes | V: the same], swizzled chunks
+  uint32_t* halo = reinterpret_cast<uint32_t*>(smem + lay.halo);  // [HP][NPAIR][32] after the loop
+  char* raw = smem + lay.raw;                                      // [HP][WP][64 bytes]
   uint32_t* wts = reinterpret_cast<uint32_t*>(smem + lay.wts);    // [2][15][32]
+  int* flag = reinterpret_cast<int*>(smem + lay.flag);
+  uint32_t* rbase = reinterpret_cast<uint32_t*>(smem + lay.rbase);  // [topk] byte offset of each routed region
 
   const int W = a.W, H = a.H, C = a.C, S = a.S, R = S * S, topk = a.topk;
   const int L = topk * T;  // a multiple of 64
+  const int ntiles = L / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
 
-  // XCD-aware numbering: consecutive units (n, r, h) share blockIdx % 8.
-  const int units = a.N * R * a.heads;
+  // XCD-aware numbering: consecutive units (n, r, h, slab) share blockIdx %
+  // 8, so the slabs and heads of a region -- the same K/V cache lines -- are
+  // read through one XCD's L2.
+  const int units = a.N * R * a.heads * SLABS;
   const int per = (units + 7) / 8;
   const int u = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   if (u >= units) return;  // the whole workgroup leaves together
-  const int h = u % a.heads, nr = u / a.heads;
+  const int slab = u % SLABS, hu = u / SLABS;
+  const int h = hu % a.heads, nr = hu / a.heads;
   const int n = nr / R, r = nr - n * R;
   const int jr = r / S, ir = r - jr * S;
-  const int y0 = jr * RH, x0 = ir * RW;
+  const int y0 = jr * RH + slab * SR, x0 = ir * RW;  // the slab's first query row and column
   const size_t img = (size_t)n * H * W * C;
   const uint32_t img_bytes = (uint32_t)H * W * C * 2;
   const Rsrc qb = rsrc(a.q + img, img_bytes), kb = rsrc(a.k + img, img_bytes);
@@ -164,167 +230,239 @@ __global__ __launch_bounds__((64 * tile_waves<RH, RW>()), 4) void attn_tile_kern
   const uint32_t hb = (uint32_t)h * 64;  // byte offset of this head's channels
   const int32_t* rrow = a.route + (size_t)nr * topk;
 
-  // ---- tile loader: thread -> (key ld_key of the tile, 8-dim chunk ld_g)
-  const int ld_key = tid >> 2, ld_g = tid & 3;
-  uint4 kreg, vreg;  // the next tile, in flight during this one
-  auto fetch = [&](int tile) {
-    const int key = tile * 64 + ld_key;
-    const int p = key / T, tt = key - p * T;   // T is compile-time
-    const int s = rrow[p];                     // uniform per 4-row group; a cached load
-    const int js = s / S, is = s - js * S;
-    const uint32_t off = (uint32_t)(js * RH + tt / RW) * rowb + (uint32_t)(is * RW + tt % RW) * pixb +
-                         hb + ld_g * 16;
-    kreg = ld16(kb, off);
-    vreg = ld16(vb, off);
-  };
-  const bool loader = tid < 256;  // waves 0-3 move the tiles
-  auto park = [&](int buf) {
-    *reinterpret_cast<uint4*>(ks + (buf * 64 + ld_key) * kKStr + ld_g * 8) = kreg;
-    *reinterpret_cast<uint4*>(vs + (buf * 64 + ld_key) * kKStr + ld_g * 8) = vreg;
-    // |k|^2 of the key (its four 8-dim pieces sit in one quad of lanes),
-    // then the largest of this wave's 16 keys
-    float n2 = sq8(kreg);
-    n2 += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(n2), 0xb1, 0xf, 0xf, false));
-    n2 += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(n2), 0x4e, 0xf, 0xf, false));
-    const float wmax = wave_max(n2);
-    if (lane == 0) knorm[buf * 4 + wave] = wmax;
-  };
-
-  if (loader) fetch(0);
-
-  // ---- halo (the head's 32 channels) and LCE weights -> LDS
+  // ---- tile loader. A 64-key tile lies inside one routed region (T is a
+  // multiple of 64) and starts on a region row: region p = tile * 64 / T,
+  // first token tt0 = (tile * 64) % T. Wave w fills the w-th KiB of the K
+  // tile and of the V tile with one direct-to-LDS 16-byte load each: lane i
+  // lands at byte 16i of the wave's KiB. K: that is slot (x = w, c = i/16,
+  // col = i%16), the chunk c of key krow(w, col). V: row 16w + i/4, chunk
+  // position i%4, i.e. logical chunk (i%4) ^ swz(row) of that key. The
+  // lane's offsets within the region are constant; the region's offset (LDS
+  // route table) and the tile's first row are a uniform add.
+  uint32_t ld_off_k, ld_off_v;
   {
-    // 4 chunks of 8 channels per pixel pair; 16 pair slots per wave and pass
-    constexpr int NSLOT = HP * NPAIR, SLOTS = 16 * WAVES;
-    const int ch = tid & 3, slot0 = tid >> 2;
-    for (int pp0 = 0; pp0 < NSLOT; pp0 += 2 * SLOTS) {
-      uint4 va[2], vb2[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int pp = pp0 + slot0 + SLOTS * i;
-        const int pr = pp % NPAIR, py = pp / NPAIR;
-        const int y = y0 - 2 + py, x = x0 - 2 + 2 * pr;
-        const bool rowok = pp < NSLOT && y >= 0 && y < H;
-        const uint32_t base = (uint32_t)y * rowb + hb + ch * 16;
-        va[i] = ld16(vb, rowok && x >= 0 && x < W ? base + (uint32_t)x * pixb : kOut);
-        vb2[i] = ld16(vb, rowok && x + 1 >= 0 && x + 1 < W && 2 * pr + 1 < WP ? base + (uint32_t)(x + 1) * pixb : kOut);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int pp = pp0 + slot0 + SLOTS * i;
-        if (pp < NSLOT) {
-          uint4 lo, hi;
-          lo.x = (va[i].x & 0xffffu) | (vb2[i].x << 16); lo.y = (va[i].x >> 16) | (vb2[i].x & 0xffff0000u);
-          lo.z = (va[i].y & 0xffffu) | (vb2[i].y << 16); lo.w = (va[i].y >> 16) | (vb2[i].y & 0xffff0000u);
-          hi.x = (va[i].z & 0xffffu) | (vb2[i].z << 16); hi.y = (va[i].z >> 16) | (vb2[i].z & 0xffff0000u);
-          hi.z = (va[i].w & 0xffffu) | (vb2[i].w << 16); hi.w = (va[i].w >> 16) | (vb2[i].w & 0xffff0000u);
-          uint32_t* dst = halo + (size_t)pp * 32 + 8 * ch;
-          *reinterpret_cast<uint4*>(dst) = lo;
-          *reinterpret_cast<uint4*>(dst + 4) = hi;
-        }
-      }
-    }
-    // weights: [2][15][C] -> this head's [2][15][32]; 240 pieces of 16 bytes
-    if (tid < 240) {
-      const int row = tid >> 3, piece = tid & 7;  // row = parity * 15 + (ay * 3 + j)
-      const uint4 w = *reinterpret_cast<const uint4*>(a.wpk + (size_t)row * C + h * 32 + piece * 4);
-      *reinterpret_cast<uint4*>(wts + row * 32 + piece * 4) = w;
-    }
+    const int kk = score_key(wave, lane & 15), kc = lane >> 4;
+    ld_off_k = (uint32_t)(kk / RW) * rowb + (uint32_t)(kk % RW) * pixb + hb + (uint32_t)kc * 16;
+    const int kr = 16 * wave + (lane >> 2), c = (lane & 3) ^ swz(kr);
+    ld_off_v = (uint32_t)(kr / RW) * rowb + (uint32_t)(kr % RW) * pixb + hb + (uint32_t)c * 16;
   }
+  auto issue = [&](int tile, int buf) {
+    const int p = tile * 64 / T, tt0 = tile * 64 - p * T;
+    const uint32_t soff = __builtin_amdgcn_readfirstlane(rbase[p]) + (uint32_t)(tt0 / RW) * rowb;
+    char* dst = tiles + buf * kBufBytes + wave * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kb, (__attribute__((address_space(3))) void*)dst, 16, ld_off_k,
+                                             soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vb, (__attribute__((address_space(3))) void*)(dst + kTileBytes),
+                                             16, ld_off_v, soff, 0, 0);
+  };
 
-  // ---- queries: this wave's blocks, B operands
+  // ---- the slab's V halo (rows y0-2 .. y0+SR+1, columns x0-2 .. x0+RW+1,
+  // the head's 32 channels) straight into LDS, 64 bytes a pixel: piece
+  // j*64 + i (instruction j, lane i) is chunk i%4 of pixel (j*64 + i)/4;
+  // pixels outside the image read as zero (the LCE padding). It is issued
+  // in the first tile step, behind that step's key loads (a wait for an
+  // earlier-issued load would wait for it too), and lands while the keys
+  // are walked.
+  auto issue_halo = [&]() {
+    constexpr int NLOAD = (int)(halo_raw_bytes(SR, RW) / 1024);
+    for (int j = wave; j < NLOAD; j += WAVES) {
+      const int piece = j * 64 + lane, pix = piece >> 2, ch = piece & 3;
+      const int y = y0 - 2 + pix / WP, x = x0 - 2 + pix % WP;
+      const uint32_t off = y >= 0 && y < H && x >= 0 && x < W
+                               ? (uint32_t)y * rowb + (uint32_t)x * pixb + hb + (uint32_t)ch * 16 : kOut;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vb, (__attribute__((address_space(3))) void*)(raw + j * 1024), 16,
+                                               off, 0, 0, 0);
+    }
+  };
+  bool halo_issued = false;
+
+  // ---- queries: this wave's blocks (B operands) -- issued first, they are
+  // on the path to the first product
   bf16x8 bq[QBW];
 #pragma unroll
   for (int i = 0; i < QBW; ++i) {
     const int t = (wave * QBW + i) * 16 + col;
     bq[i] = as_bf16x8(ld16(qb, (uint32_t)(y0 + t / RW) * rowb + (uint32_t)(x0 + t % RW) * pixb + hb + grp * 16));
   }
-
-  float m[QBW], qn[QBW];  // running maximum; qscale * |q| of the lane's query
-  f32x4 o0[QBW], o1[QBW], ls[QBW];
-#pragma unroll
-  for (int i = 0; i < QBW; ++i) {
-    qn[i] = a.qscale * __builtin_sqrtf(group_sum(sq8(__builtin_bit_cast(uint4, bq[i]))));
-    m[i] = -INFINITY;
-    o0[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    o1[i] = o0[i];
-    ls[i] = o0[i];
+  // ---- route table -> LDS, and the largest squared key norm over the
+  // routed regions: each wave reads the route row and the norms with one
+  // load per lane (two dependent loads in all, not two per route)
+  const bool bounded = a.kn != nullptr;
+  float k2 = 0.f;
+  for (int p0 = 0; p0 < topk; p0 += 64) {
+    const int p = p0 + lane;
+    if (p < topk) {
+      const int s = rrow[p];
+      if (wave == 0) {
+        const int js = s / S, is = s - js * S;
+        rbase[p] = (uint32_t)(js * RH) * rowb + (uint32_t)(is * RW) * pixb;
+      }
+      if (bounded) k2 = fmaxf(k2, a.kn[((size_t)n * R + s) * a.heads + h]);
+    }
   }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) k2 = fmaxf(k2, __shfl_xor(k2, d));
+  // weights: [2][15][C] -> this head's [2][15][32]; 240 pieces of 16 bytes
+  if (tid < 240) {
+    const int row = tid >> 3, piece = tid & 7;  // row = parity * 15 + (ay * 3 + j)
+    const uint4 w = *reinterpret_cast<const uint4*>(a.wpk + (size_t)row * C + h * 32 + piece * 4);
+    *reinterpret_cast<uint4*>(wts + row * 32 + piece * 4) = w;
+  }
+  // the softmax's fixed maximum of the lane's query (scaled, base 2):
+  // qscale * |q| * max |k| (replaced by the exact maximum on the exact way)
+  float m[QBW];
+  {
+    const float kmax = __builtin_sqrtf(k2);
+#pragma unroll
+    for (int i = 0; i < QBW; ++i)
+      m[i] = bounded ? a.qscale * __builtin_sqrtf(group_sum(sq8(__builtin_bit_cast(uint4, bq[i])))) * kmax : 0.f;
+  }
+
+  f32x4 o0[QBW], o1[QBW], ls[QBW];
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
-  // A-operand rows of the two score tiles of a 32-key block (see header)
-  const int krow0 = 8 * (col >> 2) + (col & 3), krow1 = krow0 + 4;
-  // V^T operand addresses: this lane gives row 8grp + col/4 (+4), channels
-  // 4*(col%4) .. +3 of each 16-channel half
-  const int vrow = 8 * grp + (col >> 2), vch = 4 * (col & 3);
-
-  const int ntiles = L / 64;
-  if (loader) park(0);
-  // one 64-key tile, from LDS buffer buf = tile & 1
-  auto step = [&](int tile, int buf) {
-    __syncthreads();  // tile `buf` parked; the other buffer is free
-    if (loader && tile + 1 < ntiles) fetch(tile + 1);
-    const uint16_t* kt = ks + buf * 64 * kKStr;
-    const uint16_t* vtl = vs + buf * 64 * kKStr;
-    const float kmax = __builtin_sqrtf(__builtin_elementwise_maximum(
-        __builtin_elementwise_maximum(knorm[buf * 4 + 0], knorm[buf * 4 + 1]),
-        __builtin_elementwise_maximum(knorm[buf * 4 + 2], knorm[buf * 4 + 3])));
-    bf16x8 ka[4], va0[2], va1[2];
+  // K operand of score tile x: slot (x, grp, col), i.e. byte x*1024 + 16*lane
+  // V^T operands: this lane gives row 8grp + col/4 (+4) of each 32-key block,
+  // channels 4*(col%4) .. +3 of each 16-channel half
+  int voff[2][2][2];  // [block b][row +0 / +4][channel half]
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      ka[2 * b] = as_bf16x8(*reinterpret_cast<const uint4*>(kt + (32 * b + krow0) * kKStr + grp * 8));
-      ka[2 * b + 1] = as_bf16x8(*reinterpret_cast<const uint4*>(kt + (32 * b + krow1) * kKStr + grp * 8));
-      // keys 32b + 8grp .. +7 of channel col (va0) and 16 + col (va1)
-      const uint16_t* vr = vtl + (32 * b + vrow) * kKStr + vch;
-      va0[b] = cat(ld_tr(vr), ld_tr(vr + 4 * kKStr));
-      va1[b] = cat(ld_tr(vr + 16), ld_tr(vr + 4 * kKStr + 16));
-    }
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int row = 32 * b + 8 * grp + (col >> 2) + 4 * rr;
+        const int chn = 16 * hh + 4 * (col & 3);  // first of the 4 channels
+        voff[b][rr][hh] = tile_off(row, chn >> 3) + (chn & 7) * 2;
+      }
+
+  // One pass over all tiles. MAXPASS: each lane's largest raw score into
+  // smax (no exponentials); otherwise the softmax pass with maximum m.
+  float smax[QBW];
+  auto pass = [&](auto maxpass_tag) {
+    constexpr bool MAXPASS = decltype(maxpass_tag)::value;
 #pragma unroll
     for (int i = 0; i < QBW; ++i) {
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      f32x4 s[4];
+      o0[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      o1[i] = o0[i];
+      ls[i] = o0[i];
+      smax[i] = -INFINITY;
+    }
+    __syncthreads();  // nobody reads the tile buffers any more
+    issue(0, 0);
+    for (int t = 0; t < ntiles; ++t) {
+      // this wave's share of tile t has landed and every LDS read of this
+      // wave has returned (so tile t - 1's buffer may be refilled once all
+      // waves pass the barrier)
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      tile_barrier();
+      const char* kt = tiles + (t & 1) * kBufBytes;
+      const char* vt = kt + kTileBytes;
+      bf16x8 ka[4], va0[2], va1[2];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) s[t] = mfma(ka[t], bq[i], z);
-      // Can a score of this tile exceed m + kTau? Not if the norm bound says
-      // so for every query of the wave (the common case after the first tile).
-      if (__builtin_amdgcn_ballot_w64(qn[i] * kmax > m[i] + kTau) != 0) {
-        // this tile's exact maximum for the lane's query (16 scores here, 64 in all)
-        const float c0 = max3(s[0][0], s[0][1], s[0][2]), c1 = max3(s[0][3], s[1][0], s[1][1]);
-        const float c2 = max3(s[1][2], s[1][3], s[2][0]), c3 = max3(s[2][1], s[2][2], s[2][3]);
-        const float c4 = max3(s[3][0], s[3][1], s[3][2]);
-        const float cm = group_max(max3(max3(c0, c1, c2), max3(c3, c4, s[3][3]), c4)) * a.qscale;
-        // raise the running maximum (and rescale) only where the tile's exceeds
-        // it by more than kTau (first tile: everywhere)
-        if (cm > m[i] + kTau) {
-          const float corr = __builtin_amdgcn_exp2f(m[i] - cm);  // 0 on the first tile
-          o0[i] *= corr;
-          o1[i] *= corr;
-          ls[i] *= corr;
-          m[i] = cm;
+      for (int x = 0; x < 4; ++x) ka[x] = as_bf16x8(*reinterpret_cast<const uint4*>(kt + x * 1024 + lane * 16));
+      if constexpr (!MAXPASS) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          // keys 32b + 8grp .. +7 of channel col (va0) and 16 + col (va1)
+          va0[b] = cat(ld_tr(vt + voff[b][0][0]), ld_tr(vt + voff[b][1][0]));
+          va1[b] = cat(ld_tr(vt + voff[b][0][1]), ld_tr(vt + voff[b][1][1]));
         }
       }
-      bf16x4 pb[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        f32x4 pv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(s[t][e], a.qscale, -m[i]));
-        pb[t] = to_bf16x4(pv);
+      // the next tile goes into the other buffer (tile t - 1's) only after
+      // this tile's operands are read: the compiler makes an LDS read wait
+      // for every load into LDS issued before it
+      if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
+      if (!halo_issued) {
+        issue_halo();
+        halo_issued = true;
       }
+      if constexpr (MAXPASS) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const bf16x8 pt = cat(pb[2 * b], pb[2 * b + 1]);  // keys 32b + 8g .. 32b + 8g + 7
-        o0[i] = mfma(va0[b], pt, o0[i]);
-        o1[i] = mfma(va1[b], pt, o1[i]);
-        ls[i] = mfma(ones, pt, ls[i]);
+        for (int i = 0; i < QBW; ++i) {
+          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          f32x4 s[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) s[x] = mfma(ka[x], bq[i], z);
+          const float c0 = max3(s[0][0], s[0][1], s[0][2]), c1 = max3(s[0][3], s[1][0], s[1][1]);
+          const float c2 = max3(s[1][2], s[1][3], s[2][0]), c3 = max3(s[2][1], s[2][2], s[2][3]);
+          const float c4 = max3(s[3][0], s[3][1], s[3][2]);
+          smax[i] = max3(smax[i], max3(c0, c1, c2), max3(c3, c4, s[3][3]));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < QBW; ++i) {
+          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          f32x4 s[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) s[x] = mfma(ka[x], bq[i], z);
+          bf16x4 pb[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            f32x4 pv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(s[x][e], a.qscale, -m[i]));
+            pb[x] = to_bf16x4(pv);
+          }
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            const bf16x8 pt = cat(pb[2 * b], pb[2 * b + 1]);  // keys 32b + 8g .. 32b + 8g + 7
+            o0[i] = mfma(va0[b], pt, o0[i]);
+            o1[i] = mfma(va1[b], pt, o1[i]);
+            ls[i] = mfma(ones, pt, ls[i]);
+          }
+        }
       }
     }
-    if (loader && tile + 1 < ntiles) park(buf ^ 1);
-    };
-  for (int tile = 0; tile < ntiles; ++tile) step(tile, tile & 1);
-  __syncthreads();  // halo and weights were parked before the first barrier; all reads below
+  };
+
+  bool exact = !bounded;
+  if (bounded) {
+    pass(SoftTag{});
+    // did some query's largest P underflow (its maximum far under the bound)?
+    bool low = false;
+#pragma unroll
+    for (int i = 0; i < QBW; ++i) low |= !(ls[i][0] >= kUnderflow);
+    if (tid == 0) *flag = 0;
+    __syncthreads();
+    if (__builtin_amdgcn_ballot_w64(low) != 0 && lane == 0) *flag = 1;
+    __syncthreads();
+    exact = *flag != 0;
+  }
+  if (exact) {
+    pass(MaxTag{});
+#pragma unroll
+    for (int i = 0; i < QBW; ++i) m[i] = group_max(smax[i]) * a.qscale;
+    pass(SoftTag{});
+  }
+  __syncthreads();  // every wave is done with the tile buffers: the halo goes there
+
+  // ---- the halo as horizontal pixel pairs of the head's 32 channels (the
+  // raw halo landed before the second tile's barrier, or before the
+  // barrier above when there is one tile)
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  __syncthreads();
+  {
+    constexpr int NSLOT = HP * NPAIR;
+    for (int e = tid; e < NSLOT * 4; e += NT) {
+      const int pp = e >> 2, ch = e & 3;
+      const int pr = pp % NPAIR, py = pp / NPAIR;
+      const char* src = raw + (py * WP + 2 * pr) * 64 + ch * 16;
+      const uint4 va = *reinterpret_cast<const uint4*>(src);
+      const uint4 vb2 = *reinterpret_cast<const uint4*>(src + 64);
+      uint4 lo, hi;
+      lo.x = (va.x & 0xffffu) | (vb2.x << 16); lo.y = (va.x >> 16) | (vb2.x & 0xffff0000u);
+      lo.z = (va.y & 0xffffu) | (vb2.y << 16); lo.w = (va.y >> 16) | (vb2.y & 0xffff0000u);
+      hi.x = (va.z & 0xffffu) | (vb2.z << 16); hi.y = (va.z >> 16) | (vb2.z & 0xffff0000u);
+      hi.z = (va.w & 0xffffu) | (vb2.w << 16); hi.w = (va.w >> 16) | (vb2.w & 0xffff0000u);
+      uint32_t* dst = halo + (size_t)pp * 32 + 8 * ch;
+      *reinterpret_cast<uint4*>(dst) = lo;
+      *reinterpret_cast<uint4*>(dst + 4) = hi;
+    }
+  }
+  __syncthreads();
 
   // ---- LCE + merge + store: lane = (query col, channel group grp); the
   // lane's query rows i = 0..QBW-1 are stacked in one column when RW == 16
@@ -390,11 +528,11 @@ __global__ __launch_bounds__((64 * tile_waves<RH, RW>()), 4) void attn_tile_kern
 
 template <int RH, int RW>
 hipError_t launch_t(const TileArgs& a, hipStream_t st) {
-  const int units = a.N * a.S * a.S * a.heads;
+  const int units = a.N * a.S * a.S * a.heads * tile_slabs<RH, RW>();
   const unsigned blocks = (unsigned)(((units + 7) / 8) * 8);
-  constexpr int threads = 64 * tile_waves<RH, RW>();
+  constexpr int threads = 64 * kTileWaves;
   launch((attn_tile_kernel<RH, RW>), dim3(blocks), dim3(threads),
-                     tile_lds(RH, RW).total, st, a);
+                     tile_lds(RH / tile_slabs<RH, RW>(), RW, a.topk).total, st, a);
   return hipGetLastError();
 }
 
@@ -407,15 +545,16 @@ bool tile_kernel_supports(const Shape& s) {
                         code == 16 * 64 + 8;
   if (!compiled) return false;
   if ((long long)s.H * s.W * s.C >= (1ll << 30)) return false;  // 32-bit byte offsets in an image
-  return tile_lds(s.rh, s.rw).total <= 65536;
+  const int qbw = s.rw == 16 ? 2 : 1, slabs = s.rh * s.rw / (16 * kTileWaves * qbw);
+  return tile_lds(s.rh / slabs, s.rw, s.topk).total <= 65536;
 }
 
 hipError_t launch_attend_tile(const void* q, const void* k, const void* v, const uint32_t* wpk,
-                              const void* b, const int32_t* route, const Shape& s, void* out,
-                              hipStream_t st) {
+                              const void* b, const int32_t* route, const float* kn, const Shape& s,
+                              void* out, hipStream_t st) {
   TileArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
-  a.wpk = wpk; a.b = (const uint16_t*)b; a.route = route; a.out = (uint16_t*)out;
+  a.wpk = wpk; a.b = (const uint16_t*)b; a.route = route; a.kn = kn; a.out = (uint16_t*)out;
   a.N = s.N; a.H = s.H; a.W = s.W; a.C = s.C; a.heads = s.heads; a.S = s.S; a.topk = s.topk;
   a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
   switch (s.rh * 64 + s.rw) {

@@ -49,10 +49,11 @@ constexpr int kHeadDim = 32;     // compiled head dimension
 constexpr int kMaxRegions = 1024;
 
 // Region means; for bf16 (wpk non-null) also repacks the LCE weights for the
-// small-region attention kernel.
+// attention kernels, and (kn non-null) writes the largest squared key norm
+// per (image, region, head) to kn [N][S*S][C/32].
 hipError_t launch_region_pool(const void* q, const void* k, const Shape& s,
                               int dtype, float* qr, float* kr, const void* lce_w,
-                              uint32_t* wpk, hipStream_t st);
+                              uint32_t* wpk, float* kn, hipStream_t st);
 hipError_t launch_route(const float* qr, const float* kr, int N, int R, int C,
                         int topk, int32_t* route, hipStream_t st);
 hipError_t launch_attend(const void* q, const void* k, const void* v,

@@ -9,6 +9,14 @@
 // latency x bytes in flight, not by arithmetic). Per-thread partial sums are
 // combined in LDS in a fixed order, so the means are reproducible bit for bit
 // (the routing that follows breaks ties exactly).
+//
+// On request (kn non-null, bf16) the kernel also reports, per (image,
+// region, head of 32 channels), the largest squared norm |k_t|^2 of the
+// head's slice over the region's tokens. The large-region attention kernel
+// bounds every score of a query by |q| * max |k| over its routed regions
+// (Cauchy-Schwarz) and uses that bound as the softmax's fixed maximum. The
+// four 16-byte chunks of one head are consecutive threads (one lane quad),
+// so a token's head norm is a quad sum.
 #include "bra_internal.h"
 
 namespace bra {
@@ -39,7 +47,7 @@ template <typename T, int TPT>
 __global__ __launch_bounds__(256) void region_pool_kernel(
     const T* __restrict__ q, const T* __restrict__ k, int H, int W, int C, int S,
     float* __restrict__ qr, float* __restrict__ kr, const uint16_t* __restrict__ lw,
-    uint32_t* __restrict__ wpk) {
+    uint32_t* __restrict__ wpk, float* __restrict__ kn) {
   constexpr int V = Vec16<T>::n;
   extern __shared__ float part[];  // [2][lanes][C]
   const int R = S * S;
@@ -61,6 +69,8 @@ __global__ __launch_bounds__(256) void region_pool_kernel(
   float aq[V], ak[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) { aq[e] = 0.f; ak[e] = 0.f; }
+  float kmax2 = 0.f;  // largest |k|^2 of this thread's head over its tokens (kn only)
+  const bool norms = V == 8 && kn != nullptr;
   if (tl < lanes) {
     for (int t0 = tl; t0 < T_; t0 += TPT * lanes) {
       uint4 bq[TPT], bk[TPT];
@@ -79,6 +89,15 @@ __global__ __launch_bounds__(256) void region_pool_kernel(
         if (t0 + u * lanes < T_) {
           Vec16<T>::add(bq[u], aq);
           Vec16<T>::add(bk[u], ak);
+          if (norms) {
+            // the quad (one token's four chunks of a head) shares the branch
+            float n2 = 0.f;
+            n2 = fmaf(bf16_lo(bk[u].x), bf16_lo(bk[u].x), n2); n2 = fmaf(bf16_hi(bk[u].x), bf16_hi(bk[u].x), n2);
+            n2 = fmaf(bf16_lo(bk[u].y), bf16_lo(bk[u].y), n2); n2 = fmaf(bf16_hi(bk[u].y), bf16_hi(bk[u].y), n2);
+            n2 = fmaf(bf16_lo(bk[u].z), bf16_lo(bk[u].z), n2); n2 = fmaf(bf16_hi(bk[u].z), bf16_hi(bk[u].z), n2);
+            n2 = fmaf(bf16_lo(bk[u].w), bf16_lo(bk[u].w), n2); n2 = fmaf(bf16_hi(bk[u].w), bf16_hi(bk[u].w), n2);
+            kmax2 = fmaxf(kmax2, quad_sum(n2));
+          }
         }
       }
     }
@@ -86,8 +105,17 @@ __global__ __launch_bounds__(256) void region_pool_kernel(
     float* pk = part + (size_t)(lanes + tl) * C + chunk * V;
 #pragma unroll
     for (int e = 0; e < V; ++e) { pq[e] = aq[e]; pk[e] = ak[e]; }
+    if (norms && (chunk & 3) == 0) part[(size_t)2 * lanes * C + (size_t)tl * (C / 32) + chunk / 4] = kmax2;
   }
   __syncthreads();
+  if (norms) {
+    const int heads = C / 32;
+    for (int h = tid; h < heads; h += blockDim.x) {
+      float mx = 0.f;
+      for (int l = 0; l < lanes; ++l) mx = fmaxf(mx, part[(size_t)2 * lanes * C + (size_t)l * heads + h]);
+      kn[(size_t)nr * heads + h] = mx;
+    }
+  }
   const float count = (float)T_;
   for (int c = tid; c < C; c += blockDim.x) {
     float sq = 0.f, sk = 0.f;
@@ -102,7 +130,7 @@ __global__ __launch_bounds__(256) void region_pool_kernel(
 
 template <typename T>
 hipError_t launch_t(const void* q, const void* k, const Shape& s, float* qr, float* kr,
-                    const void* lw, uint32_t* wpk, hipStream_t st) {
+                    const void* lw, uint32_t* wpk, float* kn, hipStream_t st) {
   constexpr int V = Vec16<T>::n;
   const int nchunk = s.C / V;                 // <= 256 (C <= 1024)
   int threads, lanes;
@@ -123,11 +151,11 @@ hipError_t launch_t(const void* q, const void* k, const Shape& s, float* qr, flo
     if (lanes < 1) lanes = 1;
   }
   const int tpt = (s.T + lanes - 1) / lanes;  // tokens per thread (looped in batches of <= 8)
-  const size_t lds = (size_t)2 * lanes * s.C * sizeof(float);
+  const size_t lds = ((size_t)2 * lanes * s.C + (kn ? (size_t)lanes * (s.C / 32) : 0)) * sizeof(float);
   dim3 grid((unsigned)(s.N * s.R)), block(threads);
 #define BRA_POOL(TP)                                                                    \
   launch((region_pool_kernel<T, TP>), grid, block, lds, st, (const T*)q,    \
-                     (const T*)k, s.H, s.W, s.C, s.S, qr, kr, (const uint16_t*)lw, wpk)
+                     (const T*)k, s.H, s.W, s.C, s.S, qr, kr, (const uint16_t*)lw, wpk, kn)
   if (tpt <= 1) BRA_POOL(1);
   else if (tpt <= 2) BRA_POOL(2);
   else if (tpt <= 4) BRA_POOL(4);
@@ -140,9 +168,9 @@ hipError_t launch_t(const void* q, const void* k, const Shape& s, float* qr, flo
 
 hipError_t launch_region_pool(const void* q, const void* k, const Shape& s, int dtype,
                               float* qr, float* kr, const void* lce_w, uint32_t* wpk,
-                              hipStream_t st) {
-  return dtype == 1 ? launch_t<uint16_t>(q, k, s, qr, kr, lce_w, wpk, st)
-                    : launch_t<float>(q, k, s, qr, kr, nullptr, nullptr, st);
+                              float* kn, hipStream_t st) {
+  return dtype == 1 ? launch_t<uint16_t>(q, k, s, qr, kr, lce_w, wpk, kn, st)
+                    : launch_t<float>(q, k, s, qr, kr, nullptr, nullptr, nullptr, st);
 }
 
 }  // namespace bra

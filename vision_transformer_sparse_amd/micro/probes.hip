@@ -26,7 +26,11 @@ __device__ __forceinline__ void stamp(uint64_t* st, int which) {
   }
 }
 
-// kind bits: 1 = exp chains, 2 = fma chains, 4 = mfma chains
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// kind bits: 1 = exp chains, 2 = fma chains, 4 = mfma chains, 8 = the
+// mfma chains use v_mfma_f32_32x32x16_bf16 (twice the flops of one
+// 16x16x32 instruction)
 template <int KIND, int NEXP, int NFMA, int NMFMA>
 __global__ __launch_bounds__(256) void unit_kernel(float* out, int iters, uint64_t* st) {
   const int gid = blockIdx.x * blockDim.x + threadIdx.x;
@@ -45,14 +49,23 @@ __global__ __launch_bounds__(256) void unit_kernel(float* out, int iters, uint64
   f32x4 acc[NMFMA > 0 ? NMFMA : 1];
 #pragma unroll
   for (int i = 0; i < NMFMA; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x16 acc32[NMFMA > 0 ? NMFMA : 1];
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc32[i][e] = 0.f;
   __syncthreads();
   stamp(st, 0);
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      if constexpr ((KIND & 4) != 0) {
+      if constexpr ((KIND & 12) == 4) {
 #pragma unroll
         for (int i = 0; i < NMFMA; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
+      }
+      if constexpr ((KIND & 12) == 12) {
+#pragma unroll
+        for (int i = 0; i < NMFMA; ++i) acc32[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc32[i], 0, 0, 0);
       }
       if constexpr ((KIND & 1) != 0) {
         // x <- 2^-x converges to about 0.64: the inputs stay ordinary numbers
@@ -73,6 +86,8 @@ __global__ __launch_bounds__(256) void unit_kernel(float* out, int iters, uint64
   for (int i = 0; i < NFMA; ++i) s += f[i];
 #pragma unroll
   for (int i = 0; i < NMFMA; ++i) s += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) s += acc32[i][0] + acc32[i][15];
   out[gid] = s;
 }
 
@@ -96,6 +111,64 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
     __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+// LDS read patterns of the attention kernels' operand loads, 64 lanes per
+// instruction, eight independent reads per step:
+//  0  ds_read_b128, lanes read 1 KiB contiguously (the reference)
+//  1  ds_read_b128, 16 rows x one 16-byte chunk per 16 lanes, rows of 64
+//     bytes with the chunk XOR-swizzled by the row (the K-operand read)
+//  2  the same rows without the swizzle
+//  3  the same rows at an 80-byte pitch (padding instead of a swizzle)
+//  4  ds_read_b64_tr_b16, 4 rows x 16 channels per 16 lanes, swizzled rows
+//     (the V^T-operand read)
+//  5  the same without the swizzle
+//  6  the same at an 80-byte pitch
+//  7  ds_read_b64_tr_b16, the 16 lanes of a group read one contiguous 128
+//     bytes (4 rows x 32 bytes) and the four groups contiguous blocks
+template <int PAT>
+__global__ __launch_bounds__(256) void lds_kernel(float* out, int iters, uint64_t* st) {
+  __shared__ __attribute__((aligned(16))) unsigned char buf[16384];
+  for (int i = threadIdx.x; i < 16384 / 4; i += blockDim.x) reinterpret_cast<unsigned*>(buf)[i] = i * 2654435761u;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+  auto swz = [](int r) { const int g = (r >> 3) & 3; return ((g & 1) << 1) | (g >> 1); };
+  int off;
+  if (PAT == 0) {
+    off = lane * 16;
+  } else if (PAT <= 3) {
+    const int row = 8 * (col >> 2) + (col & 3);
+    off = PAT == 1 ? row * 64 + ((grp ^ swz(row)) << 4) : PAT == 2 ? row * 64 + grp * 16 : row * 80 + grp * 16;
+  } else {
+    const int row = 8 * grp + (col >> 2), chn = 4 * (col & 3);
+    off = PAT == 4 ? row * 64 + (((chn >> 3) ^ swz(row)) << 4) + (chn & 7) * 2
+        : PAT == 5 ? row * 64 + chn * 2 : PAT == 6 ? row * 80 + chn * 2
+        : grp * 128 + (col >> 2) * 32 + (col & 3) * 8;
+  }
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  __syncthreads();
+  stamp(st, 0);
+  for (int it = 0; it < iters; ++it) {
+    // the LDS may have changed for all the compiler knows: every read is
+    // issued again in every iteration
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      // eight distinct places 1280 bytes (5 x 256) apart, shifted by 32
+      // bytes every other step: the same banks for every read
+      const int o = off + j * 1280 + (it & 1) * 32;
+      if constexpr (PAT <= 3) {
+        acc += *reinterpret_cast<const u32x4*>(buf + o);
+      } else {
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(buf + o));
+        acc[j & 3] += (unsigned)v[0] + ((unsigned)v[3] << 16);
+      }
+    }
+  }
+  stamp(st, 1);
+  out[blockIdx.x * blockDim.x + threadIdx.x] = (float)(acc[0] + acc[1] + acc[2] + acc[3]);
 }
 
 thread_local char g_err[256];
@@ -123,6 +196,18 @@ UnitFn unit_fn(int probe) {
     case 5: return unit_kernel<5, 8, 0, 4>;    // mfma + exp (4 + 8)
     case 6: return unit_kernel<7, 8, 8, 4>;    // mfma + exp + fma (4 + 8 + 8)
     case 7: return unit_kernel<6, 0, 8, 4>;    // mfma + fma (4 + 8)
+    case 8: return unit_kernel<12, 0, 0, 2>;   // mfma 32x32x16, 2 chains
+    case 9: return unit_kernel<13, 8, 0, 2>;   // mfma 32x32x16 + exp (2 + 8)
+    case 18: return unit_kernel<15, 8, 8, 2>;  // mfma 32x32x16 + exp + fma (2 + 8 + 8)
+    case 19: return unit_kernel<13, 16, 0, 4>; // mfma 32x32x16 + exp (4 + 16)
+    case 10: return lds_kernel<0>;
+    case 11: return lds_kernel<1>;
+    case 12: return lds_kernel<2>;
+    case 13: return lds_kernel<3>;
+    case 14: return lds_kernel<4>;
+    case 15: return lds_kernel<5>;
+    case 16: return lds_kernel<6>;
+    case 17: return lds_kernel<7>;
     default: return nullptr;
   }
 }
