@@ -240,5 +240,44 @@ __device__ __forceinline__ void rank_rows(const float* logit, int RP, int R, int
   }
 }
 
+// ---- one 16-row block of an image's routes (R <= 64) ----------------------
+__host__ __device__ inline int col_tiles(int R) { return (R + 15) / 16; }
+// LDS of route_block: the logit block [16][16 col_tiles], then a [4][64]
+// key buffer per wave
+__host__ __device__ inline size_t route_block_lds(int R, int waves) {
+  return (size_t)16 * 16 * col_tiles(R) * sizeof(float) + (size_t)waves * 4 * 64 * sizeof(uint64_t);
+}
+// Routes of query rows r0 .. r0+15 (those below R) of image n, from the
+// image's fp32 region means qr_img, kr_img ([R][C]), written to
+// route_img[row][topk]. Wave w of `waves` computes column tiles w, w +
+// waves, ... (split-bf16 matrix-core logits), the logits go to LDS, and the
+// waves rank rows w, w + waves, ... Starts and ends with a workgroup
+// barrier (the caller may reuse smem before and after).
+__device__ __forceinline__ void route_block(const float* qr_img, const float* kr_img, int R, int C, int topk,
+                                            float scale, int32_t* route_img, int r0, char* smem, int wave,
+                                            int waves, int lane) {
+  const int CT = col_tiles(R), RP = 16 * CT;  // padded logit row
+  float* logit = reinterpret_cast<float*>(smem);                   // [16][RP]
+  uint64_t* keys = reinterpret_cast<uint64_t*>(logit + 16 * RP);   // [waves][4][64]
+  const int col = lane & 15, grp = lane >> 4;
+  const uint32_t img_bytes = (uint32_t)R * C * 4;
+  const Rsrc qb = rsrc(qr_img, img_bytes), kb = rsrc(kr_img, img_bytes);
+  const uint32_t qrow = (uint32_t)min(r0 + col, R - 1) * C * 4;
+  __syncthreads();
+  for (int ct = wave; ct < CT; ct += waves) {
+    const uint32_t krow = (uint32_t)min(16 * ct + col, R - 1) * C * 4;
+    const f32x4 acc = logit_tile_x3(
+        grp, C, [&](int c) { return ld16(qb, c < C ? qrow + 4 * c : kOut); },
+        [&](int c) { return ld16(kb, c < C ? krow + 4 * c : kOut); });
+    // lane (col, grp) holds rows 4grp..4grp+3 of the tile at column col
+#pragma unroll
+    for (int e = 0; e < 4; ++e) logit[(4 * grp + e) * RP + 16 * ct + col] = acc[e] * scale;
+  }
+  __syncthreads();
+  rank_rows(logit, RP, R, min(16, R - r0), wave, waves, topk, keys + (size_t)wave * 4 * 64, lane,
+            [&](int i, int k, int s) { route_img[(size_t)(r0 + i) * topk + k] = s; });
+  __syncthreads();
+}
+
 }  // namespace route
 }  // namespace bra

@@ -66,53 +66,26 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
 }
 
 // ---------------------------------------------------------------- R <= 64
-__host__ __device__ inline int col_tiles(int R) { return (R + 15) / 16; }  // also waves
-__host__ __device__ inline size_t route_lds(int R) {
-  return (size_t)16 * 16 * col_tiles(R) * sizeof(float) +
-         (size_t)col_tiles(R) * 4 * 64 * sizeof(uint64_t);
-}
-
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ qr,
                                                     const float* __restrict__ kr, int R, int C,
                                                     int topk, float scale,
                                                     int32_t* __restrict__ route) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int CT = col_tiles(R), RP = 16 * CT;  // padded logit row
-  const int waves = blockDim.x >> 6;
-  float* logit = reinterpret_cast<float*>(smem);                    // [16][RP]
-  uint64_t* keys = reinterpret_cast<uint64_t*>(logit + 16 * RP);    // [waves][4][64]
+  const int CT = col_tiles(R);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int col = lane & 15, grp = lane >> 4;
   const int u = xcd_unit(blockIdx.x, gridDim.x);
   const int n = u / CT;
   const int r0 = (u - n * CT) * 16;
-  const uint32_t img_bytes = (uint32_t)R * C * 4;
-  const Rsrc qb = rsrc(qr + (size_t)n * R * C, img_bytes);
-  const Rsrc kb = rsrc(kr + (size_t)n * R * C, img_bytes);
-  const uint32_t qrow = (uint32_t)min(r0 + col, R - 1) * C * 4;
-
-  // ---- affinities: wave ct computes column tile ct
-  for (int ct = wave; ct < CT; ct += waves) {
-    const uint32_t krow = (uint32_t)min(16 * ct + col, R - 1) * C * 4;
-    const f32x4 acc = logit_tile_x3(
-        grp, C, [&](int c) { return ld16(qb, c < C ? qrow + 4 * c : kOut); },
-        [&](int c) { return ld16(kb, c < C ? krow + 4 * c : kOut); });
-    // lane (col, grp) holds rows 4grp..4grp+3 of the tile at column col
-#pragma unroll
-    for (int e = 0; e < 4; ++e) logit[(4 * grp + e) * RP + 16 * ct + col] = acc[e] * scale;
-  }
-  __syncthreads();
-
-  // ---- rank selection, rows wave, wave + waves, ... in groups of four
-  rank_rows(logit, RP, R, min(16, R - r0), wave, waves, topk, keys + (size_t)wave * 4 * 64, lane,
-            [&](int i, int k, int s) { route[((size_t)n * R + r0 + i) * topk + k] = s; });
+  route_block(qr + (size_t)n * R * C, kr + (size_t)n * R * C, R, C, topk, scale, route + (size_t)n * R * topk,
+              r0, smem, wave, blockDim.x >> 6, lane);
 }
 
 hipError_t launch_small(const float* qr, const float* kr, int N, int R, int C, int topk,
                         int32_t* route, hipStream_t st) {
   const float scale = (float)(1.0 / __builtin_sqrt((double)C));
   const unsigned blocks = (unsigned)(N * col_tiles(R));
-  launch(route_kernel, dim3(blocks), dim3(64 * col_tiles(R)), route_lds(R), st, qr, kr, R, C, topk, scale, route);
+  launch(route_kernel, dim3(blocks), dim3(64 * col_tiles(R)), route_block_lds(R, col_tiles(R)), st, qr, kr, R, C,
+         topk, scale, route);
   return hipGetLastError();
 }
 
