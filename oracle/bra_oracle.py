@@ -48,6 +48,7 @@ __all__ = [
     "check_shapes", "partition", "unpartition", "region_means",
     "region_affinity", "topk_routes", "gather_regions", "token_attention",
     "lce", "bra_forward", "linear", "round_bf16", "bra_block_forward",
+    "dense_attention",
 ]
 
 
@@ -263,3 +264,38 @@ def bra_block_forward(x, wqkv, bqkv, lce_w, lce_b, wo, bo, heads: int, S: int, t
     res["attn_out"] = o
     res["out"] = linear(o, wo, bo)
     return res
+
+
+def dense_attention(q, k, v, lce_w, lce_b, heads: int) -> np.ndarray:
+    """The router-free attention of the last stage: every query attends to
+    every token of its own image, plus the same 5x5 depthwise term on V.
+
+    The walk-through's module print (section "网络结构") shows the last stage
+    built from AttentionLePE blocks (a bias-free qkv Linear(C, 3C), a lepe
+    Conv2d(C, C, 5, padding=2, groups=C) and a proj Linear), and page
+    bernice.tw/posts/biformer, section "Biformer", gives that stage k = S^2:
+    all regions routed, i.e. plain attention over the whole map. Per image n
+    and head m (channels [m*hd, (m+1)*hd)), with the H*W tokens in raster
+    order: o = softmax_u((q_t . k_u) * hd^-1/2) v_u over all u; out = o +
+    lce(v). q, k, v: (N, H, W, C); lce_w: (C, 5, 5); lce_b: (C,) or None."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    N, H, W, C = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    if heads < 1 or C % heads:
+        raise ValueError("heads must divide C")
+    hd = C // heads
+    w = np.asarray(lce_w, dtype=np.float64).reshape(C, 5, 5)
+    b = None if lce_b is None else np.asarray(lce_b, dtype=np.float64).reshape(C)
+    att = np.empty((N, H * W, C))
+    for n in range(N):
+        qn, kn, vn = (x[n].reshape(H * W, C) for x in (q, k, v))
+        for m in range(heads):
+            sl = slice(m * hd, (m + 1) * hd)
+            s = (qn[:, sl] @ kn[:, sl].T) / np.sqrt(hd)      # (queries, keys)
+            s = s - s.max(axis=1, keepdims=True)
+            e = np.exp(s)
+            att[n][:, sl] = (e / e.sum(axis=1, keepdims=True)) @ vn[:, sl]
+    return att.reshape(N, H, W, C) + lce(v, w, b)

@@ -288,6 +288,60 @@ def pin_single_token_regions(O):
         assert s == int(np.argmax(dots))
 
 
+def pin_dense_attention_matches_library(O):
+    """The router-free path against torch's scaled_dot_product_attention and
+    grouped conv2d in fp64 (a library routine computing the same thing)."""
+    cases = [(2, 7, 7, 8, 2), (1, 3, 5, 12, 3), (1, 4, 4, 4, 1)]
+    for seed, (N, H, W, C, heads) in enumerate(cases):
+        rng = _rng(600 + seed)
+        q, k, v = (rng.standard_normal((N, H, W, C)) for _ in range(3))
+        w = rng.standard_normal((C, 5, 5)) * 0.2
+        b = rng.standard_normal(C) * 0.1
+        got = O.dense_attention(q, k, v, w, b, heads)
+        want = _dense_reference(q, k, v, w, b, heads)
+        assert np.allclose(got, want, rtol=1e-11, atol=1e-11), np.abs(got - want).max()
+
+
+def pin_dense_attention_equals_full_routing(O):
+    """North-star check (a) from the other side: BRA with every region routed
+    (topk = S^2, S > 1, so the keys arrive in routing order, region by region)
+    equals the dense path."""
+    for seed, (N, H, W, C, heads, S) in enumerate([(1, 6, 6, 8, 2, 3), (2, 4, 8, 4, 2, 2)]):
+        rng = _rng(610 + seed)
+        q, k, v = (rng.standard_normal((N, H, W, C)) for _ in range(3))
+        w = rng.standard_normal((C, 5, 5)) * 0.2
+        b = rng.standard_normal(C) * 0.1
+        got = O.dense_attention(q, k, v, w, b, heads)
+        want = O.bra_forward(q, k, v, w, b, heads, S, S * S)["out"]
+        assert np.allclose(got, want, rtol=1e-11, atol=1e-11), np.abs(got - want).max()
+
+
+def pin_dense_attention_single_token(O):
+    """A 1x1 map: the one key gets probability 1 and only the centre tap of
+    the 5x5 window sees the image, so out = v + w[:, 2, 2] * v + b."""
+    rng = _rng(620)
+    C = 6
+    q, k, v = (rng.standard_normal((3, 1, 1, C)) for _ in range(3))
+    w = rng.standard_normal((C, 5, 5))
+    b = rng.standard_normal(C)
+    got = O.dense_attention(q, k, v, w, b, 2)
+    assert np.allclose(got, v + w[:, 2, 2] * v + b, rtol=0, atol=1e-13)
+
+
+def pin_dense_attention_uniform_keys(O):
+    """All keys equal: the softmax is uniform over the image, so with the
+    LCE weights zero each output is the mean of V over all tokens (per
+    channel) plus the bias; queries do not matter."""
+    rng = _rng(621)
+    N, H, W, C = 2, 3, 4, 4
+    q = rng.standard_normal((N, H, W, C))
+    v = rng.standard_normal((N, H, W, C))
+    b = rng.standard_normal(C)
+    got = O.dense_attention(q, np.ones((N, H, W, C)), v, np.zeros((C, 5, 5)), b, 2)
+    want = v.mean(axis=(1, 2), keepdims=True) + b
+    assert np.allclose(got, np.broadcast_to(want, got.shape), rtol=0, atol=1e-13)
+
+
 # ---------------------------------------------------------------- LCE
 def pin_lce_delta_kernel(O):
     rng = _rng(13)

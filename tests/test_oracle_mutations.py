@@ -118,7 +118,39 @@ def _block_kv_swapped(x, wqkv, bqkv, lce_w, lce_b, wo, bo, heads, S, topk, store
                                      store, route_override)
 
 
+def _dense_variant(mode):
+    def f(q, k, v, lce_w, lce_b, heads):
+        q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+        N, H, W, C = q.shape
+        hd = C // heads
+        scale = 1.0 / np.sqrt(C if mode == "scale_C" else hd)
+        axis = 0 if mode == "softmax_over_queries" else 1
+        att = np.empty((N, H * W, C))
+        for n in range(N):
+            qn, kn, vn = (x[n].reshape(H * W, C) for x in (q, k, v))
+            if mode == "k_v_swapped":
+                kn, vn = vn, kn
+            for m in range(heads):
+                sl = slice(m * hd, (m + 1) * hd)
+                s = (qn[:, sl] @ kn[:, sl].T) * scale
+                e = np.exp(s - s.max(axis=axis, keepdims=True))
+                att[n][:, sl] = (e / e.sum(axis=axis, keepdims=True)) @ vn[:, sl]
+        att = att.reshape(N, H, W, C)
+        if mode == "lepe_dropped":
+            return att
+        lw = np.asarray(lce_w, dtype=np.float64).reshape(C, 5, 5)
+        if mode == "lepe_on_q":
+            return att + O.lce(q, lw, lce_b)
+        return att + O.lce(v, lw, lce_b)
+    return f
+
+
 MUTATIONS = {
+    "dense_scale_uses_C": ("dense_attention", _dense_variant("scale_C")),
+    "dense_softmax_over_queries": ("dense_attention", _dense_variant("softmax_over_queries")),
+    "dense_k_and_v_swapped": ("dense_attention", _dense_variant("k_v_swapped")),
+    "dense_lepe_dropped": ("dense_attention", _dense_variant("lepe_dropped")),
+    "dense_lepe_on_q": ("dense_attention", _dense_variant("lepe_on_q")),
     "linear_weight_not_transposed": ("linear", _linear_weight_not_transposed),
     "linear_bias_dropped": ("linear", _linear_bias_dropped),
     "round_bf16_truncates": ("round_bf16", _round_bf16_truncates),
