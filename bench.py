@@ -33,6 +33,9 @@ One JSON line is printed. It carries:
 --op block times the block around the operator instead: the qkv projection
 (Linear C -> 3C, bra_linear), bra_forward, and the output projection (Linear
 C -> C); "kernels" then also holds the projection kernel's roofline.
+The router-free last stage (s4: 128 images of 7x7 tokens, C = 512, 16 heads)
+is measured in per_config as its own workload: a step is one
+bra_attention_dense call. `--config s4` makes it the headline.
 """
 from __future__ import annotations
 
@@ -56,13 +59,18 @@ ATTN_SOURCES = ("attn_image.hip", "attn_region.hip", "attn_tile.hip", "attn_mfma
                 "attn_f32.hip", "bra_internal.h", "route_common.h")
 
 
+def dense(cfg) -> bool:
+    """The router-free workload: its step is bra_attention_dense."""
+    return cfg.name == "s4"
+
+
 def algorithmic(cfg):
     """Per-launch algorithmic traffic / work of each kernel (what the method
     must move or compute, not what a dense method would)."""
     b = 2 if cfg.dtype == "bf16" else 4
     E = cfg.N * cfg.H * cfg.W * cfg.C
     means = 2 * cfg.N * cfg.R * cfg.C * 4
-    routes = cfg.N * cfg.R * cfg.topk * 4
+    routes = 0 if dense(cfg) else cfg.N * cfg.R * cfg.topk * 4
     lce_params = cfg.C * 26 * b
     return {
         "pool": {"bytes": 2 * E * b + means},
@@ -164,6 +172,9 @@ def cpu_baseline(inp, cfg, budget_s: float, op: str = "forward"):
                 oracle.bra_block_forward(inp["x"], inp["wqkv"], inp["bqkv"], inp["lce_w"],
                                          inp["lce_b"], inp["wo"], inp["bo"], cfg.heads, cfg.S,
                                          cfg.topk)
+            elif op == "dense":
+                oracle.dense_attention(inp["q"], inp["k"], inp["v"], inp["lce_w"], inp["lce_b"],
+                                       cfg.heads)
             else:
                 oracle.bra_forward(inp["q"], inp["k"], inp["v"], inp["lce_w"], inp["lce_b"],
                                    cfg.heads, cfg.S, cfg.topk)
@@ -200,6 +211,9 @@ class Workload:
         from vision_transformer_sparse_amd import bra
 
         self.cfg = cfg
+        if dense(cfg) and op == "forward":
+            op = "dense"
+        self.op = op
         if inputs is None:
             if op == "block":
                 inputs = draw_block(cfg.N, cfg.H, cfg.W, cfg.C, cfg.S, cfg.dtype,
@@ -221,6 +235,9 @@ class Workload:
                 bra.forward(*qkv, t["lce_w"], t["lce_b"], cfg.heads, cfg.S, cfg.topk,
                             out=out, route_idx=route)
                 bra.linear(out, t["wo"], t["bo"], outs=[y])
+        elif op == "dense":
+            def step():
+                bra.attention_dense(t["q"], t["k"], t["v"], t["lce_w"], t["lce_b"], cfg.heads, out=out)
         else:
             def step():
                 bra.forward(t["q"], t["k"], t["v"], t["lce_w"], t["lce_b"], cfg.heads, cfg.S,
@@ -295,7 +312,7 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--config", default="c4", help="headline workload (c0..c4)")
+    ap.add_argument("--config", default="c4", help="headline workload (c0..c4, or s4)")
     ap.add_argument("--op", choices=("forward", "block"), default="forward",
                     help="forward: bra_forward alone; block: qkv projection, bra_forward, wo")
     ap.add_argument("--per-config", choices=("all", "none"), default="all",
@@ -314,10 +331,11 @@ def main(argv=None) -> int:
 
     import torch
 
-    from synth import CONFIGS
+    from synth import CONFIGS, STAGE4
     from vision_transformer_sparse_amd import bra
 
-    by_name = {c.name: c for c in CONFIGS}
+    workloads = CONFIGS + [STAGE4] if a.op == "forward" else CONFIGS
+    by_name = {c.name: c for c in workloads}
     cfg = by_name[a.config]
     bra.load()
     if not torch.cuda.is_available():
@@ -330,7 +348,7 @@ def main(argv=None) -> int:
     head = None
     if a.per_config == "all":
         flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
-        for c in CONFIGS:
+        for c in workloads:
             w = Workload(c, a.op, dev)
             per_config[c.name] = measure_config(w, flush, n_warm=1000, n_cold=a.cold)
             print(f"[bench] per_config {c.name}: {per_config[c.name]['ms_per_step'] * 1e3:.2f} us/step warm, "
@@ -389,7 +407,7 @@ def main(argv=None) -> int:
     roof["us_per_launch"] = attn_ms_per_launch * 1e3
     roof["launches"] = attn_cnt
 
-    cpu = cpu_baseline(head.inputs, cfg, a.cpu_budget, a.op) if a.cpu_budget > 0 else None
+    cpu = cpu_baseline(head.inputs, cfg, a.cpu_budget, head.op) if a.cpu_budget > 0 else None
     value = cfg.queries * a.steps / elapsed
     line = {
         "metric": METRIC,
@@ -405,7 +423,8 @@ def main(argv=None) -> int:
         "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) q/k/v; see synth/)",
         "config": {"workload": f"{cfg.name}: {cfg.what}"
-                               + (" -- block: qkv Linear, BRA, wo Linear" if a.op == "block" else ""),
+                               + (" -- block: qkv Linear, BRA, wo Linear" if a.op == "block" else "")
+                               + (" -- bra_attention_dense" if head.op == "dense" else ""),
                    "N": cfg.N, "H": cfg.H, "W": cfg.W,
                    "C": cfg.C, "heads": cfg.heads, "S": cfg.S, "topk": cfg.topk,
                    "queries_per_step": cfg.queries, "parallelism": "single GPU"},

@@ -105,6 +105,20 @@ int bra_forward_noalloc(const void* q, const void* k, const void* v,
                         int N, int H, int W, int C, int heads, int S, int topk,
                         int dtype, void* out, int32_t* route_idx);
 
+/* The router-free attention of BiFormer's last stage (AttentionLePE; the
+ * walk-through's module print, section 网络结构, and bernice.tw/posts/biformer,
+ * section "Biformer", which gives that stage k = S^2): per image and head,
+ * softmax attention of every query over all H*W tokens of its image, scale
+ * hd^-1/2, plus LCE(V) as in step 7, rounded once. Equal to bra_forward with
+ * every region routed (topk = S*S) for any S, without the routing. Same
+ * tensor conventions and checks as bra_forward (no S, topk or route_idx).
+ * bf16 maps of at most 256 tokens (7x7 .. 16x16) run one kernel; other
+ * shapes run the routed path with a single region (S = 1), in the library
+ * workspace. */
+int bra_attention_dense(const void* q, const void* k, const void* v,
+                        const void* lce_w, const void* lce_b,
+                        int N, int H, int W, int C, int heads, int dtype, void* out);
+
 /* Step 2 alone: qr, kr = region means of q and k, fp32 [N][S*S][C] each
  * (caller-owned device buffers). Same checks as bra_forward (heads and topk
  * are not involved). The means are bit-identical to the ones bra_forward

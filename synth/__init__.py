@@ -21,7 +21,7 @@ import math
 
 import numpy as np
 
-__all__ = ["Config", "CONFIGS", "draw", "round_to_bf16", "draw_config", "draw_linear",
+__all__ = ["Config", "CONFIGS", "STAGE4", "draw", "round_to_bf16", "draw_config", "draw_linear",
            "draw_block"]
 
 
@@ -76,6 +76,15 @@ CONFIGS = [
 ]
 
 
+# The router-free last stage (every region routed, k = S^2 on page
+# bernice.tw/posts/biformer, section "Biformer"; AttentionLePE with C = 512 in
+# the walk-through's module print, section 网络结构): 7x7 tokens at 224x224
+# input /32, 16 heads of 32. S = 1 (the whole map is one region) and topk = 1
+# describe the same computation for the routed entry points.
+STAGE4 = Config("s4", "classification stage 4 (224x224 input /32), dense", "bf16",
+                128, 7, 7, 512, 16, 1, 1, 0.0, 0.2, 0.1)
+
+
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round float64 values to bf16 (via fp32, round-to-nearest-even both times)
     and return them as float64 holding exactly the bf16 values."""
@@ -126,7 +135,7 @@ def draw_config(cfg: Config | int, seed: int | None = None, N: int | None = None
     if isinstance(cfg, int):
         idx, cfg = cfg, CONFIGS[cfg]
     else:
-        idx = CONFIGS.index(cfg)
+        idx = len(CONFIGS) if cfg == STAGE4 else CONFIGS.index(cfg)
     if seed is None:
         seed = 1000 + idx
     return draw(N if N is not None else cfg.N, cfg.H, cfg.W, cfg.C, cfg.S,

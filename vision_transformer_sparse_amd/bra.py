@@ -26,6 +26,7 @@ _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 _SIGS = {
     "bra_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "bra_forward_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
+    "bra_attention_dense": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "bra_region_means": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "bra_route": (_i, [_vp, _vp, _i, _i, _i, _i, _vp]),
     "bra_attend": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
@@ -135,6 +136,32 @@ def forward(q, k, v, lce_w, lce_b, heads: int, S: int, topk: int, out=None, rout
         _call("bra_forward", _ptr(q), _ptr(k), _ptr(v), _ptr(lce_w), _ptr(lce_b),
               N, H, W, C, heads, S, topk, _dtype_code(q), _ptr(out), _ptr(route_idx))
     return out, route_idx
+
+
+def attention_dense(q, k, v, lce_w, lce_b, heads: int, out=None):
+    """bra_attention_dense: the router-free attention of the last stage (every
+    query over all H*W tokens of its image) plus LCE; returns out."""
+    _check(q, "q")
+    dev, dt = q.device, q.dtype
+    for name, t in (("k", k), ("v", v), ("lce_w", lce_w)):
+        _check(t, name, dt, dev)
+    if lce_b is not None:
+        _check(lce_b, "lce_b", dt, dev)
+    N, H, W, C = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v shapes differ")
+    if lce_w.numel() != C * 25 or (lce_b is not None and lce_b.numel() != C):
+        raise ValueError("lce_w must hold C*25 and lce_b C elements")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", dt, dev)
+    if out.shape != q.shape:
+        raise ValueError("out has the wrong size")
+    with torch.cuda.device(dev):
+        _stream(dev)
+        _call("bra_attention_dense", _ptr(q), _ptr(k), _ptr(v), _ptr(lce_w), _ptr(lce_b),
+              N, H, W, C, heads, _dtype_code(q), _ptr(out))
+    return out
 
 
 def region_means(q, k, S: int):

@@ -47,6 +47,11 @@ hipError_t launch_attend_f32(const void* q, const void* k, const void* v, const 
                              const void* b, const int32_t* route, const Shape& s, void* out,
                              hipStream_t st);
 // kn: max |k|^2 per (image, region, head) from the pool kernel, or null
+// The router-free last-stage attention (attn_dense.hip): bf16, at most 256
+// tokens a map
+bool dense_kernel_supports(const Shape& s);
+hipError_t launch_attend_dense(const void* q, const void* k, const void* v, const void* w, const void* b,
+                               const Shape& s, void* out, hipStream_t st);
 hipError_t launch_attend_tile(const void* q, const void* k, const void* v, const uint32_t* wpk,
                               const void* b, const int32_t* route, const float* kn, const Shape& s,
                               void* out, hipStream_t st);
@@ -400,6 +405,37 @@ int bra_forward_noalloc(const void* q, const void* k, const void* v, const void*
   rc = scratch_address(&ws);
   if (rc) return rc;
   return forward_staged(q, k, v, lce_w, lce_b, s, dtype, out, route_idx, ws, st);
+}
+
+int bra_attention_dense(const void* q, const void* k, const void* v, const void* lce_w,
+                        const void* lce_b, int N, int H, int W, int C, int heads, int dtype,
+                        void* out) {
+  if (!q || !k || !v || !lce_w || !out) return BRA_ERR_NULL;
+  bra::Shape s;
+  // one region holding the whole map, routed to itself: attention over all H*W tokens
+  int rc = check_dims(N, H, W, C, heads, 1, 1, dtype, true, true, &s);
+  if (rc) return rc;
+  rc = check_align({q, k, v, lce_w, out}, {lce_b});
+  if (rc) return rc;
+  rc = check_ptrs({q, k, v, lce_w, lce_b, out});
+  if (rc) return rc;
+  hipStream_t st = g_stream;
+  if (dtype == BRA_BF16 && bra::dense_kernel_supports(s)) {
+    hipError_t e;
+    {
+      ProfScope ps(BRA_K_ATTN, st);
+      e = bra::launch_attend_dense(q, k, v, lce_w, lce_b, s, out, st);
+    }
+    return e == hipSuccess ? BRA_OK : hip_fail(e);
+  }
+  // elsewhere the routed path with that one region (a single routing candidate)
+  std::lock_guard<std::mutex> lk(g_ws_mutex);
+  const size_t routes_at = (ws_layout(N, C, 1).total + 255) & ~(size_t)255;
+  void* ws = nullptr;
+  rc = workspace(routes_at + (size_t)N * sizeof(int32_t), &ws);
+  if (rc) return rc;
+  int32_t* route = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + routes_at);
+  return forward_staged(q, k, v, lce_w, lce_b, s, dtype, out, route, ws, st);
 }
 
 int bra_region_means(const void* q, const void* k, int N, int H, int W, int C, int S,

@@ -1,0 +1,241 @@
+// Router-free attention of the last stage: every query attends to all H*W
+// tokens of its image, plus the 5x5 depthwise term on V. The walk-through's
+// module print (TRANSFORMER.niftyadmin.cn/n/347023.html, section 网络结构)
+// builds BiFormer's last stage from AttentionLePE blocks (qkv Linear, a
+// depthwise 5x5 lepe Conv2d with padding 2, proj Linear), and
+// bernice.tw/posts/biformer, section "Biformer", gives that stage k = S^2,
+// i.e. every region routed: the routing step has nothing to choose, so this
+// path skips it.
+//
+// Small maps (at most 256 tokens: 7x7 at 224 input, up to 16x16), bf16,
+// head_dim 32. One workgroup owns one (image, head): it stages the head's K
+// (one 64-byte row per token) and V (the same rows inside a 2-pixel zero
+// border, which is the LePE padding) in LDS once, and its four waves walk the
+// image's 16-query blocks:
+//
+//   S^T = K Q^T   16x16x32 bf16 products; A = 16 keys x 32 dims read from
+//                 LDS, B = the block's queries straight from memory; lane
+//                 (query j, group g) holds keys 16kt + 4g + i of tile kt
+//   softmax       exact: the maximum over the lane's keys, then over the
+//                 four groups (permlane swaps); exp2 of the scaled
+//                 difference, rounded to bf16; the sum of the rounded values
+//   O^T = V^T P^T within a 32-key step the lane's own eight probabilities
+//                 (tiles 2s and 2s+1) form its B operand; the A operand is the
+//                 same eight keys' values, read transposed from LDS
+//                 (ds_read_b64_tr_b16), so both sides agree on the key order
+//   LePE          the query's 5x5 window of the bordered V, 8 channels a
+//                 lane, fp32 weights from LDS, plus the bias
+//   store         one rounding to bf16, non-temporal 8-byte stores
+#include "bra_internal.h"
+
+namespace bra {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kDenseThreads = 256;
+constexpr int kDenseWaves = kDenseThreads / 64;
+constexpr int kDenseMaxTokens = 256;
+constexpr int kDenseMaxBordered = 512;  // rows of the bordered V, (H+4)(W+4)
+constexpr int kStage = 2;               // 16-byte pieces of K and of V a thread loads at once
+
+// LDS: [16 KT][32] bf16 keys | [(H+4)(W+4)][32] bf16 bordered values |
+// [25][32] fp32 LePE weights | [32] fp32 bias | [16 KT] key -> byte offset
+// of its bordered value row
+struct DenseLds {
+  int k, v, w, b, rows, total;
+};
+__host__ __device__ inline DenseLds dense_lds(int H, int W, int KT) {
+  DenseLds l;
+  l.k = 0;
+  l.v = 16 * KT * 64;
+  l.w = l.v + (H + 4) * (W + 4) * 64;
+  l.b = l.w + 25 * 32 * 4;
+  l.rows = l.b + 32 * 4;
+  l.total = l.rows + 16 * KT * 4;
+  return l;
+}
+
+__device__ __forceinline__ bf16x4 ld_tr(const char* p) {
+  // within each 16-lane group, lanes 4r..4r+3 address row r's 16 consecutive
+  // bf16 (4 each); lane i receives element i of rows 0..3
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<char*>(p)));
+  return __builtin_bit_cast(bf16x4, x);
+}
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int KT>
+__global__ __launch_bounds__(kDenseThreads) void attn_dense_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ lw, const uint16_t* __restrict__ lb, int H, int W, int C, int heads,
+    uint16_t* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const DenseLds L = dense_lds(H, W, KT);
+  const int u = xcd_unit(blockIdx.x, gridDim.x);  // an image's heads share an XCD (and its L2 lines)
+  const int n = u / heads, h = u - n * heads;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, g = lane >> 4;
+  const int HW = H * W, WB = W + 4, VB = (H + 4) * WB;
+  const uint32_t rowb = (uint32_t)C * 2, hoff = (uint32_t)h * 64;
+  const size_t img = (size_t)n * HW * C;
+  const uint32_t img_bytes = (uint32_t)HW * rowb;
+  const Rsrc qr = rsrc(q + img, img_bytes), kr = rsrc(k + img, img_bytes), vr = rsrc(v + img, img_bytes);
+  const Rsrc orr = rsrc(out + img, img_bytes);
+  const int QB = (HW + 15) / 16;
+
+  // the first block's Q^T operand is in flight while K and V are staged
+  auto q_operand = [&](int qb) {
+    const int t = min(16 * qb + col, HW - 1);
+    return ld16(qr, (uint32_t)t * rowb + hoff + 16 * g);
+  };
+  uint4 qv = q_operand(wave < QB ? wave : 0);
+  for (int e = tid; e < 25 * 32; e += kDenseThreads) {  // weights [tap][channel] from [channel][tap]
+    const int tap = e >> 5, c = e & 31;
+    reinterpret_cast<float*>(lds + L.w)[e] = bf16_bits_to_float(lw[(size_t)(h * 32 + c) * 25 + tap]);
+  }
+  if (tid < 32) reinterpret_cast<float*>(lds + L.b)[tid] = lb ? bf16_bits_to_float(lb[h * 32 + tid]) : 0.f;
+  for (int key = tid; key < 16 * KT; key += kDenseThreads) {  // keys past HW point at a border row (zeros)
+    const int y = key / W, x = key - (key / W) * W;
+    reinterpret_cast<int*>(lds + L.rows)[key] = key < HW ? ((y + 2) * WB + x + 2) * 64 : 0;
+  }
+  // K rows (keys past HW stay unwritten: their scores are masked) and the
+  // bordered V, in batches of kStage 16-byte pieces of each per thread
+  const int kpieces = HW * 4, vpieces = VB * 4;
+  for (int e0 = tid; e0 < kpieces || e0 < vpieces; e0 += kStage * kDenseThreads) {
+    uint4 kx[kStage], vx[kStage];
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) {
+      const int e = e0 + i * kDenseThreads, t = e >> 2;
+      kx[i] = ld16(kr, e < kpieces ? (uint32_t)t * rowb + hoff + 16 * (e & 3) : kOut);
+      const int p = e >> 2, y = p / WB - 2, x = p - (p / WB) * WB - 2;
+      const bool inside = e < vpieces && y >= 0 && y < H && x >= 0 && x < W;
+      vx[i] = ld16(vr, inside ? (uint32_t)(y * W + x) * rowb + hoff + 16 * (e & 3) : kOut);  // border: zeros
+    }
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) {
+      const int e = e0 + i * kDenseThreads;
+      if (e < kpieces) *reinterpret_cast<uint4*>(lds + L.k + e * 16) = kx[i];
+      if (e < vpieces) *reinterpret_cast<uint4*>(lds + L.v + e * 16) = vx[i];
+    }
+  }
+  __syncthreads();
+
+  const float qscale = 0.17677669529663687f * 1.4426950408889634f;  // head_dim^-1/2, in log2 units
+  const float* wl = reinterpret_cast<const float*>(lds + L.w);
+  const float* bias = reinterpret_cast<const float*>(lds + L.b);
+  const int* rows = reinterpret_cast<const int*>(lds + L.rows);
+  for (int qb = wave; qb < QB; qb += kDenseWaves) {
+    if (qb != wave) qv = q_operand(qb);
+    const bf16x8 qb8 = __builtin_bit_cast(bf16x8, qv);
+    f32x4 s[KT];
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(lds + L.k + (16 * kt + col) * 64 + 16 * g);
+      s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb8, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (16 * kt + 16 > HW && 16 * kt + 4 * g + i >= HW) s[kt][i] = -__builtin_inff();
+        m = __builtin_elementwise_maximum(m, s[kt][i]);
+      }
+    }
+    const float mq = group_max(m) * qscale;
+    bf16x4 p[KT];
+    float l = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[kt][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kt][i], qscale, -mq));
+        l += (float)p[kt][i];
+      }
+    l = group_sum(l);
+    f32x4 o[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    const int r = col >> 2, c = col & 3;  // this lane's row and piece of the transposing reads
+#pragma unroll
+    for (int j = 0; j < KT / 2; ++j) {
+      const bf16x8 pb = cat(p[2 * j], p[2 * j + 1]);
+      const char* v0 = lds + L.v + rows[32 * j + 4 * g + r] + 8 * c;
+      const char* v1 = lds + L.v + rows[32 * j + 16 + 4 * g + r] + 8 * c;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cat(ld_tr(v0 + 32 * dt), ld_tr(v1 + 32 * dt)), pb, o[dt],
+                                                        0, 0, 0);
+    }
+    // lane (query col, group g) holds channels 16 dt + 4g + i of its query
+    const int t = 16 * qb + col;
+    if (t < HW) {
+      const int y = t / W, x = t - (t / W) * W;
+      const float inv = 1.f / l;
+      float acc[2][4];
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[dt][i] = fmaf(o[dt][i], inv, bias[16 * dt + 4 * g + i]);
+#pragma unroll
+      for (int a = 0; a < 5; ++a)
+#pragma unroll
+        for (int e = 0; e < 5; ++e) {
+          const char* px = lds + L.v + ((y + a) * WB + x + e) * 64;
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) {
+            const uint2 vv = *reinterpret_cast<const uint2*>(px + (16 * dt + 4 * g) * 2);
+            const f32x4 ww = *reinterpret_cast<const f32x4*>(wl + (5 * a + e) * 32 + 16 * dt + 4 * g);
+            acc[dt][0] = fmaf(ww[0], bf16_lo(vv.x), acc[dt][0]);
+            acc[dt][1] = fmaf(ww[1], bf16_hi(vv.x), acc[dt][1]);
+            acc[dt][2] = fmaf(ww[2], bf16_lo(vv.y), acc[dt][2]);
+            acc[dt][3] = fmaf(ww[3], bf16_hi(vv.y), acc[dt][3]);
+          }
+        }
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        uint2 w2;
+        w2.x = float_to_bf16_bits(acc[dt][0]) | (float_to_bf16_bits(acc[dt][1]) << 16);
+        w2.y = float_to_bf16_bits(acc[dt][2]) | (float_to_bf16_bits(acc[dt][3]) << 16);
+        st_nt(orr, (uint32_t)t * rowb + hoff + (16 * dt + 4 * g) * 2, w2);
+      }
+    }
+  }
+}
+
+int dense_key_tiles(const Shape& s) { return 2 * ((s.H * s.W + 31) / 32); }
+
+}  // namespace
+
+bool dense_kernel_supports(const Shape& s) {
+  const int HW = s.H * s.W;
+  if (s.hd != 32 || HW > kDenseMaxTokens) return false;
+  if ((s.H + 4) * (s.W + 4) > kDenseMaxBordered) return false;
+  return dense_lds(s.H, s.W, dense_key_tiles(s)).total <= 64 * 1024;
+}
+
+hipError_t launch_attend_dense(const void* q, const void* k, const void* v, const void* w, const void* b,
+                               const Shape& s, void* out, hipStream_t st) {
+  const int KT = dense_key_tiles(s);
+  const size_t lds = (size_t)dense_lds(s.H, s.W, KT).total;
+  const dim3 grid((unsigned)(s.N * s.heads)), block(kDenseThreads);
+#define BRA_DENSE(KTV)                                                                                   \
+  launch(attn_dense_kernel<KTV>, grid, block, lds, st, (const uint16_t*)q, (const uint16_t*)k,       \
+         (const uint16_t*)v, (const uint16_t*)w, (const uint16_t*)b, s.H, s.W, s.C, s.heads, (uint16_t*)out)
+  switch (KT) {
+    case 2: BRA_DENSE(2); break;
+    case 4: BRA_DENSE(4); break;
+    case 6: BRA_DENSE(6); break;
+    case 8: BRA_DENSE(8); break;
+    case 10: BRA_DENSE(10); break;
+    case 12: BRA_DENSE(12); break;
+    case 14: BRA_DENSE(14); break;
+    case 16: BRA_DENSE(16); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef BRA_DENSE
+  return hipGetLastError();
+}
+
+}  // namespace bra
