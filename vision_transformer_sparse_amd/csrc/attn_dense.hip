@@ -23,9 +23,14 @@
 //                 (tiles 2s and 2s+1) form its B operand; the A operand is the
 //                 same eight keys' values, read transposed from LDS
 //                 (ds_read_b64_tr_b16), so both sides agree on the key order
-//   LePE          the query's 5x5 window of the bordered V, 8 channels a
-//                 lane, fp32 weights from LDS, plus the bias
-//   store         one rounding to bf16, non-temporal 8-byte stores
+//   LePE          before the attention, in its own pass: a lane owns one
+//                 channel (its 25 weights and bias in registers) and a run of
+//                 7 pixels of one output row; per window row it reads the 11
+//                 values once and applies all five horizontal taps from
+//                 registers (about 8 LDS reads an output instead of 25). The
+//                 fp32 results wait in LDS for the attention epilogue.
+//   store         attention / sum + LePE, one rounding to bf16,
+//                 non-temporal 8-byte stores
 #include "bra_internal.h"
 
 namespace bra {
@@ -41,21 +46,29 @@ constexpr int kDenseWaves = kDenseThreads / 64;
 constexpr int kDenseMaxTokens = 256;
 constexpr int kDenseMaxBordered = 512;  // rows of the bordered V, (H+4)(W+4)
 constexpr int kStage = 2;               // 16-byte pieces of K and of V a thread loads at once
+constexpr int kSeg = 7;                 // output pixels of one row a lane convolves at once (one run covers a 7-wide map)
+// A run of kSeg outputs starting at x0 <= W - 1 reads columns x0 ..
+// x0 + kSeg + 3 of a bordered row of W + 4, so the last run of a row reads at
+// most kSeg - 1 columns (64 bytes each) past the row's end: into the next row
+// or, from the last row, past the bordered V, which this slack keeps inside
+// the allocation. Those values feed only outputs past W, which are never read.
+constexpr int kLceSlack = (kSeg - 1) * 64;
 
 // LDS: [16 KT][32] bf16 keys | [(H+4)(W+4)][32] bf16 bordered values |
-// [25][32] fp32 LePE weights | [32] fp32 bias | [16 KT] key -> byte offset
-// of its bordered value row
+// [H][WP][32] fp32 LePE results (bias included; WP = W rounded up to whole
+// runs of kSeg, so every run stores all its outputs) | [16 KT] key -> byte
+// offset of its bordered value row
+__host__ __device__ inline int lce_pitch(int W) { return (W + kSeg - 1) / kSeg * kSeg; }
 struct DenseLds {
-  int k, v, w, b, rows, total;
+  int k, v, lce, rows, total;
 };
 __host__ __device__ inline DenseLds dense_lds(int H, int W, int KT) {
   DenseLds l;
   l.k = 0;
   l.v = 16 * KT * 64;
-  l.w = l.v + (H + 4) * (W + 4) * 64;
-  l.b = l.w + 25 * 32 * 4;
-  l.rows = l.b + 32 * 4;
-  l.total = l.rows + 16 * KT * 4;
+  l.lce = l.v + (H + 4) * (W + 4) * 64;
+  l.rows = l.lce + H * lce_pitch(W) * 32 * 4;
+  l.total = l.rows + 16 * KT * 4 + kLceSlack;
   return l;
 }
 
@@ -70,8 +83,10 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Up to 64 tokens (the 7x7 and 8x8 maps): eight workgroups a CU, so a
+// batch of 128 images x 16 heads runs in one round.
 template <int KT>
-__global__ __launch_bounds__(kDenseThreads) void attn_dense_kernel(
+__global__ __launch_bounds__(kDenseThreads, KT <= 4 ? 8 : 1) void attn_dense_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ lw, const uint16_t* __restrict__ lb, int H, int W, int C, int heads,
     uint16_t* __restrict__ out) {
@@ -95,11 +110,16 @@ __global__ __launch_bounds__(kDenseThreads) void attn_dense_kernel(
     return ld16(qr, (uint32_t)t * rowb + hoff + 16 * g);
   };
   uint4 qv = q_operand(wave < QB ? wave : 0);
-  for (int e = tid; e < 25 * 32; e += kDenseThreads) {  // weights [tap][channel] from [channel][tap]
-    const int tap = e >> 5, c = e & 31;
-    reinterpret_cast<float*>(lds + L.w)[e] = bf16_bits_to_float(lw[(size_t)(h * 32 + c) * 25 + tap]);
-  }
-  if (tid < 32) reinterpret_cast<float*>(lds + L.b)[tid] = lb ? bf16_bits_to_float(lb[h * 32 + tid]) : 0.f;
+  // LePE weights and bias of this thread's channel (every LePE item of the
+  // thread has channel tid % 32)
+  const int lc = tid & 31;
+  float wreg[25];
+#pragma unroll
+  for (int tap = 0; tap < 25; ++tap) wreg[tap] = bf16_bits_to_float(lw[(size_t)(h * 32 + lc) * 25 + tap]);
+  // (a null bias is a zero-length buffer: its load reads 0, and no branch
+  // waits on the loads already in flight)
+  const Rsrc br = rsrc(lb, lb ? (uint32_t)C * 2 : 0u);
+  const float bias_c = bf16_bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(br, (h * 32 + lc) * 2, 0, 0));
   for (int key = tid; key < 16 * KT; key += kDenseThreads) {  // keys past HW point at a border row (zeros)
     const int y = key / W, x = key - (key / W) * W;
     reinterpret_cast<int*>(lds + L.rows)[key] = key < HW ? ((y + 2) * WB + x + 2) * 64 : 0;
@@ -126,9 +146,35 @@ __global__ __launch_bounds__(kDenseThreads) void attn_dense_kernel(
   }
   __syncthreads();
 
+  // LePE(V) + bias of every pixel: items (channel, output row, run of kSeg
+  // pixels), channel fastest
+  float* lce = reinterpret_cast<float*>(lds + L.lce);
+  const int segs = (W + kSeg - 1) / kSeg, items = 32 * H * segs, WP = segs * kSeg;
+  for (int it = tid; it < items; it += kDenseThreads) {
+    const int rs = it >> 5, y = rs / segs, x0 = (rs - y * segs) * kSeg;
+    float acc[kSeg];
+#pragma unroll
+    for (int j = 0; j < kSeg; ++j) acc[j] = bias_c;
+#pragma unroll
+    for (int a = 0; a < 5; ++a) {
+      // bordered row y + a holds image row y + a - 2; column x0 + j + e is
+      // tap e of output x0 + j
+      const char* rp = lds + L.v + ((y + a) * WB + x0) * 64 + 2 * lc;
+      float vrow[kSeg + 4];
+#pragma unroll
+      for (int j = 0; j < kSeg + 4; ++j) vrow[j] = bf16_bits_to_float(*reinterpret_cast<const uint16_t*>(rp + j * 64));
+#pragma unroll
+      for (int e = 0; e < 5; ++e)
+#pragma unroll
+        for (int j = 0; j < kSeg; ++j) acc[j] = fmaf(wreg[5 * a + e], vrow[j + e], acc[j]);
+      __builtin_amdgcn_sched_barrier(0);  // one window row's values live at a time
+    }
+#pragma unroll
+    for (int j = 0; j < kSeg; ++j) lce[(y * WP + x0 + j) * 32 + lc] = acc[j];
+  }
+  __syncthreads();
+
   const float qscale = 0.17677669529663687f * 1.4426950408889634f;  // head_dim^-1/2, in log2 units
-  const float* wl = reinterpret_cast<const float*>(lds + L.w);
-  const float* bias = reinterpret_cast<const float*>(lds + L.b);
   const int* rows = reinterpret_cast<const int*>(lds + L.rows);
   for (int qb = wave; qb < QB; qb += kDenseWaves) {
     if (qb != wave) qv = q_operand(qb);
@@ -171,28 +217,15 @@ __global__ __launch_bounds__(kDenseThreads) void attn_dense_kernel(
     // lane (query col, group g) holds channels 16 dt + 4g + i of its query
     const int t = 16 * qb + col;
     if (t < HW) {
-      const int y = t / W, x = t - (t / W) * W;
+      const int y = t / W, x = t - y * W;
       const float inv = 1.f / l;
       float acc[2][4];
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
+      for (int dt = 0; dt < 2; ++dt) {
+        const f32x4 le = *reinterpret_cast<const f32x4*>(lce + (y * WP + x) * 32 + 16 * dt + 4 * g);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[dt][i] = fmaf(o[dt][i], inv, bias[16 * dt + 4 * g + i]);
-#pragma unroll
-      for (int a = 0; a < 5; ++a)
-#pragma unroll
-        for (int e = 0; e < 5; ++e) {
-          const char* px = lds + L.v + ((y + a) * WB + x + e) * 64;
-#pragma unroll
-          for (int dt = 0; dt < 2; ++dt) {
-            const uint2 vv = *reinterpret_cast<const uint2*>(px + (16 * dt + 4 * g) * 2);
-            const f32x4 ww = *reinterpret_cast<const f32x4*>(wl + (5 * a + e) * 32 + 16 * dt + 4 * g);
-            acc[dt][0] = fmaf(ww[0], bf16_lo(vv.x), acc[dt][0]);
-            acc[dt][1] = fmaf(ww[1], bf16_hi(vv.x), acc[dt][1]);
-            acc[dt][2] = fmaf(ww[2], bf16_lo(vv.y), acc[dt][2]);
-            acc[dt][3] = fmaf(ww[3], bf16_hi(vv.y), acc[dt][3]);
-          }
-        }
+        for (int i = 0; i < 4; ++i) acc[dt][i] = fmaf(o[dt][i], inv, le[i]);
+      }
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         uint2 w2;
