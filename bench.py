@@ -56,7 +56,7 @@ FP32_PEAK_TFLOPS = 157.3
 PROFILE_EVERY = 4
 FLUSH_BYTES = 1 << 30
 ATTN_SOURCES = ("attn_image.hip", "attn_region.hip", "attn_tile.hip", "attn_mfma.hip", "attn_valu.hip",
-                "attn_f32.hip", "bra_internal.h", "route_common.h")
+                "attn_f32.hip", "attn_dense.hip", "bra_internal.h", "route_common.h")
 
 
 def dense(cfg) -> bool:
