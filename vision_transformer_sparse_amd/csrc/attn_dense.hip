@@ -29,8 +29,9 @@
 //                 values once and applies all five horizontal taps from
 //                 registers (about 8 LDS reads an output instead of 25). The
 //                 fp32 results wait in LDS for the attention epilogue.
-//   store         attention / sum + LePE, one rounding to bf16,
-//                 non-temporal 8-byte stores
+//   store         attention / sum + LePE, one rounding to bf16; two
+//                 cross-lane swaps give each lane 8 consecutive channels, so a
+//                 token's 64 bytes leave in one instruction (non-temporal)
 #include "bra_internal.h"
 
 namespace bra {
@@ -215,24 +216,36 @@ __global__ __launch_bounds__(kDenseThreads, KT <= 4 ? 8 : 1) void attn_dense_ker
                                                         0, 0, 0);
     }
     // lane (query col, group g) holds channels 16 dt + 4g + i of its query
-    const int t = 16 * qb + col;
+    const int t = 16 * qb + col, tc = min(t, HW - 1);
+    const int y = tc / W, x = tc - y * W;
+    const float inv = 1.f / l;
+    uint32_t pk[2][2];  // [dt][pair]: channels 16 dt + 4g + (0, 1) and (2, 3), bf16
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      const f32x4 le = *reinterpret_cast<const f32x4*>(lce + (y * WP + x) * 32 + 16 * dt + 4 * g);
+      float r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = fmaf(o[dt][i], inv, le[i]);
+      pk[dt][0] = float_to_bf16_bits(r[0]) | (float_to_bf16_bits(r[1]) << 16);
+      pk[dt][1] = float_to_bf16_bits(r[2]) | (float_to_bf16_bits(r[3]) << 16);
+    }
+    // Regroup so that lane group g holds channels 8g .. 8g+7 of its query (one
+    // 16-byte store; the four groups write the token's 64 bytes in one
+    // instruction): with A = the dt 0 quartets and B = the dt 1 quartets of
+    // groups 0..3, the 32-lane swap gives X = (A0, A1, B0, B1), Y = (A2, A3,
+    // B2, B3), and the 16-lane swap X = (A0, A2, B0, B2), Y = (A1, A3, B1, B3).
+    uint32_t xs[2], ys[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const auto h32 = __builtin_amdgcn_permlane32_swap(pk[0][j], pk[1][j], false, false);
+      const auto h16 = __builtin_amdgcn_permlane16_swap(h32[0], h32[1], false, false);
+      xs[j] = h16[0];
+      ys[j] = h16[1];
+    }
     if (t < HW) {
-      const int y = t / W, x = t - y * W;
-      const float inv = 1.f / l;
-      float acc[2][4];
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const f32x4 le = *reinterpret_cast<const f32x4*>(lce + (y * WP + x) * 32 + 16 * dt + 4 * g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[dt][i] = fmaf(o[dt][i], inv, le[i]);
-      }
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        uint2 w2;
-        w2.x = float_to_bf16_bits(acc[dt][0]) | (float_to_bf16_bits(acc[dt][1]) << 16);
-        w2.y = float_to_bf16_bits(acc[dt][2]) | (float_to_bf16_bits(acc[dt][3]) << 16);
-        st_nt(orr, (uint32_t)t * rowb + hoff + (16 * dt + 4 * g) * 2, w2);
-      }
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 w4 = {xs[0], xs[1], ys[0], ys[1]};
+      __builtin_amdgcn_raw_buffer_store_b128(w4, orr, (uint32_t)t * rowb + hoff + 16 * g, 0, kNt);
     }
   }
 }
