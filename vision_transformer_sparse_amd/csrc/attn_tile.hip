@@ -519,10 +519,24 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void attn_tile_kernel(TileArgs 
     lo.y = float_to_bf16_bits(fmaf(o0[i][2], inv, acc[i][2])) | (float_to_bf16_bits(fmaf(o0[i][3], inv, acc[i][3])) << 16);
     hi.x = float_to_bf16_bits(fmaf(o1[i][0], inv, acc[i][4])) | (float_to_bf16_bits(fmaf(o1[i][1], inv, acc[i][5])) << 16);
     hi.y = float_to_bf16_bits(fmaf(o1[i][2], inv, acc[i][6])) | (float_to_bf16_bits(fmaf(o1[i][3], inv, acc[i][7])) << 16);
+    // regroup: lane group g gets channels 8g .. 8g+7 (the 32-lane swap of
+    // (lo, hi) gives (lo0, lo1, hi0, hi1) / (lo2, lo3, hi2, hi3) by group,
+    // the 16-lane swap (lo0, lo2, hi0, hi2) / (lo1, lo3, hi1, hi3)), so the
+    // token's 64 bytes leave in one 16-byte-per-lane store
+    const uint32_t la[2] = {lo.x, lo.y}, hb[2] = {hi.x, hi.y};
+    uint32_t xs[2], ys[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const auto h32 = __builtin_amdgcn_permlane32_swap(la[j], hb[j], false, false);
+      const auto h16 = __builtin_amdgcn_permlane16_swap(h32[0], h32[1], false, false);
+      xs[j] = h16[0];
+      ys[j] = h16[1];
+    }
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 w4 = {xs[0], xs[1], ys[0], ys[1]};
     const Rsrc ob = rsrc(a.out + img, img_bytes);
     const uint32_t oo = (uint32_t)(((y0 + ty) * W + x0 + tx) * C + h * 32) * 2;
-    st_nt(ob, oo + 8 * grp, lo);
-    st_nt(ob, oo + 32 + 8 * grp, hi);
+    __builtin_amdgcn_raw_buffer_store_b128(w4, ob, oo + 16 * grp, 0, kNt);
   }
 }
 
