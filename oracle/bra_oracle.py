@@ -48,7 +48,7 @@ __all__ = [
     "check_shapes", "partition", "unpartition", "region_means",
     "region_affinity", "topk_routes", "gather_regions", "token_attention",
     "lce", "bra_forward", "linear", "round_bf16", "bra_block_forward",
-    "dense_attention",
+    "dense_attention", "bra_forward_head_routed",
 ]
 
 
@@ -299,3 +299,52 @@ def dense_attention(q, k, v, lce_w, lce_b, heads: int) -> np.ndarray:
             e = np.exp(s)
             att[n][:, sl] = (e / e.sum(axis=1, keepdims=True)) @ vn[:, sl]
     return att.reshape(N, H, W, C) + lce(v, w, b)
+
+
+def bra_forward_head_routed(q, k, v, lce_w, lce_b, heads: int, S: int, topk: int,
+                            route_override: np.ndarray | None = None):
+    """The per-head routing variant: every head routes on its own channels.
+
+    The hand-written BRA class of the qqiyuan.cn blog (its forward, section on
+    the region-level routing) splits q and k into heads first and then takes
+    region means, region scores (scaled by its self.scale = head_dim^-1/2) and
+    the top-k per head, so each head gathers its own regions. This function
+    keeps everything else of the operator as bra_forward computes it (joint
+    softmax over the gathered keys, LCE on V over the whole image) and changes
+    only the routing: for head m (channels [m*hd, (m+1)*hd)), steps 2-6 run
+    on that head's channel slice alone -- region_affinity scales by the last
+    axis' size^-1/2, which on a head's slice is head_dim^-1/2.
+    Returns "out" (N,H,W,C), "route_idx" (N,heads,R,topk) (the routes used),
+    "route_oracle" and "logits" (N,heads,R,R). route_override, if given, is
+    (N, heads, R, topk)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    N, H, W, C = q.shape
+    check_shapes(N, H, W, C, heads, S, topk)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape")
+    R, hd = S * S, C // heads
+    w = np.asarray(lce_w, dtype=np.float64).reshape(C, 5, 5)
+    b = None if lce_b is None else np.asarray(lce_b, dtype=np.float64).reshape(C)
+    if route_override is not None:
+        route_override = np.asarray(route_override, dtype=np.int64).reshape(N, heads, R, topk)
+        if route_override.min() < 0 or route_override.max() >= R:
+            raise ValueError("route_override holds an index outside [0, S*S)")
+    logits = np.empty((N, heads, R, R))
+    own = np.empty((N, heads, R, topk), dtype=np.int64)
+    used = np.empty_like(own)
+    att = np.empty((N, H, W, C))
+    for m in range(heads):
+        sl = slice(m * hd, (m + 1) * hd)
+        qp, kp, vp = partition(q[..., sl], S), partition(k[..., sl], S), partition(v[..., sl], S)
+        A = region_affinity(region_means(qp), region_means(kp))
+        logits[:, m], own[:, m] = A, topk_routes(A, topk)
+        route = own[:, m] if route_override is None else route_override[:, m]
+        used[:, m] = route
+        o = np.empty_like(qp)
+        for n in range(N):
+            o[n:n + 1] = token_attention(qp[n:n + 1], gather_regions(kp[n:n + 1], route[n:n + 1]),
+                                         gather_regions(vp[n:n + 1], route[n:n + 1]), 1)
+        att[..., sl] = unpartition(o, S, H, W)
+    return {"out": att + lce(v, w, b), "route_idx": used, "route_oracle": own, "logits": logits}

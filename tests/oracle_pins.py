@@ -342,6 +342,70 @@ def pin_dense_attention_uniform_keys(O):
     assert np.allclose(got, np.broadcast_to(want, got.shape), rtol=0, atol=1e-13)
 
 
+def pin_head_routed_one_head_is_the_operator(O):
+    """With one head, routing per head is routing over all channels: the
+    variant equals bra_forward (routes, logits and output)."""
+    rng = _rng(630)
+    N, H, W, C, S, topk = 2, 6, 6, 8, 3, 4
+    q, k, v = (rng.standard_normal((N, H, W, C)) for _ in range(3))
+    w = rng.standard_normal((C, 5, 5)) * 0.2
+    b = rng.standard_normal(C) * 0.1
+    got = O.bra_forward_head_routed(q, k, v, w, b, 1, S, topk)
+    want = O.bra_forward(q, k, v, w, b, 1, S, topk)
+    assert np.array_equal(got["route_idx"][:, 0], want["route_idx"])
+    assert np.allclose(got["logits"][:, 0], want["logits"], rtol=0, atol=1e-13)
+    assert np.allclose(got["out"], want["out"], rtol=0, atol=1e-12)
+
+
+def pin_head_routed_brute_force_routes(O):
+    """Per-head routes and logits from plain Python loops on a tiny input:
+    head m's region means over its own channels, logits scaled by
+    head_dim^-1/2, descending order with ties to the lower index."""
+    rng = _rng(631)
+    N, H, W, C, heads, S, topk = 1, 4, 4, 6, 3, 2, 3
+    q, k, v = (rng.standard_normal((N, H, W, C)) for _ in range(3))
+    res = O.bra_forward_head_routed(q, k, v, np.zeros((C, 5, 5)), None, heads, S, topk)
+    hd, rh, R = C // heads, H // S, S * S
+    for m in range(heads):
+        def mean(x, r):
+            j, i = divmod(r, S)
+            return [sum(x[0, j * rh + a, i * rh + e, m * hd + c] for a in range(rh) for e in range(rh)) / (rh * rh)
+                    for c in range(hd)]
+        for r in range(R):
+            qm = mean(q, r)
+            row = [sum(a * c for a, c in zip(qm, mean(k, t))) / hd ** 0.5 for t in range(R)]
+            assert np.allclose(res["logits"][0, m, r], row, rtol=0, atol=1e-12)
+            order = sorted(range(R), key=lambda t: (-row[t], t))[:topk]
+            assert list(res["route_idx"][0, m, r]) == order
+
+
+def pin_head_routed_heads_route_apart(O):
+    """A known answer where the heads must disagree: head 0's channels make
+    every region prefer region 1, head 1's prefer region 2 (k's channels of a
+    head are large only in that region). Shared routing could not give both."""
+    N, H, W, C, heads, S = 1, 4, 4, 4, 2, 2
+    q = np.ones((N, H, W, C))
+    k = np.zeros((N, H, W, C))
+    k[0, 0:2, 2:4, 0:2] = 5.0      # region 1 (j = 0, i = 1), head 0's channels
+    k[0, 2:4, 0:2, 2:4] = 3.0      # region 2 (j = 1, i = 0), head 1's channels
+    v = _rng(632).standard_normal((N, H, W, C))
+    res = O.bra_forward_head_routed(q, k, v, np.zeros((C, 5, 5)), None, heads, S, 1)
+    assert np.all(res["route_idx"][0, 0, :, 0] == 1)
+    assert np.all(res["route_idx"][0, 1, :, 0] == 2)
+
+
+def pin_head_routed_all_regions_is_dense(O):
+    """topk = S^2 routes every region for every head: the variant equals the
+    dense attention (pinned to torch's SDPA)."""
+    rng = _rng(633)
+    N, H, W, C, heads, S = 2, 6, 6, 8, 2, 3
+    q, k, v = (rng.standard_normal((N, H, W, C)) for _ in range(3))
+    w = rng.standard_normal((C, 5, 5)) * 0.2
+    b = rng.standard_normal(C) * 0.1
+    got = O.bra_forward_head_routed(q, k, v, w, b, heads, S, S * S)["out"]
+    assert np.allclose(got, _dense_reference(q, k, v, w, b, heads), rtol=1e-11, atol=1e-11)
+
+
 # ---------------------------------------------------------------- LCE
 def pin_lce_delta_kernel(O):
     rng = _rng(13)

@@ -145,7 +145,34 @@ def _dense_variant(mode):
     return f
 
 
+def _head_routed_shared(q, k, v, lce_w, lce_b, heads, S, topk, route_override=None):
+    # routes once over all channels and gives every head that choice
+    base = O.bra_forward(q, k, v, lce_w, lce_b, heads, S, topk)
+    r = np.repeat(base["route_idx"][:, None], heads, axis=1)
+    lg = np.repeat(base["logits"][:, None], heads, axis=1)
+    return {"out": base["out"], "route_idx": r, "route_oracle": r, "logits": lg}
+
+
+def _head_routed_heads_swapped(q, k, v, lce_w, lce_b, heads, S, topk, route_override=None):
+    res = O.__dict__["_orig_head_routed"](q, k, v, lce_w, lce_b, heads, S, topk)
+    perm = np.roll(np.arange(heads), 1)
+    again = O.__dict__["_orig_head_routed"](q, k, v, lce_w, lce_b, heads, S, topk,
+                                            route_override=res["route_idx"][:, perm])
+    again["logits"] = res["logits"][:, perm]
+    again["route_oracle"] = res["route_idx"][:, perm]
+    return again
+
+
+def _head_routed_scale_C(q, k, v, lce_w, lce_b, heads, S, topk, route_override=None):
+    res = O.__dict__["_orig_head_routed"](q, k, v, lce_w, lce_b, heads, S, topk, route_override)
+    res["logits"] = res["logits"] / np.sqrt(heads)   # C^-1/2 instead of head_dim^-1/2
+    return res
+
+
 MUTATIONS = {
+    "head_routed_shares_routes": ("bra_forward_head_routed", _head_routed_shared),
+    "head_routed_heads_swapped": ("bra_forward_head_routed", _head_routed_heads_swapped),
+    "head_routed_scale_uses_C": ("bra_forward_head_routed", _head_routed_scale_C),
     "dense_scale_uses_C": ("dense_attention", _dense_variant("scale_C")),
     "dense_softmax_over_queries": ("dense_attention", _dense_variant("softmax_over_queries")),
     "dense_k_and_v_swapped": ("dense_attention", _dense_variant("k_v_swapped")),
@@ -180,6 +207,7 @@ def test_some_pin_catches(name, monkeypatch):
     monkeypatch.setitem(O.__dict__, "_orig_gather", O.gather_regions)
     monkeypatch.setitem(O.__dict__, "_orig_lce", O.lce)
     monkeypatch.setitem(O.__dict__, "_orig_block", O.bra_block_forward)
+    monkeypatch.setitem(O.__dict__, "_orig_head_routed", O.bra_forward_head_routed)
     monkeypatch.setattr(O, attr, bad)
     caught = []
     for pin in P.ALL_PINS:
