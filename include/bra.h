@@ -105,6 +105,21 @@ int bra_forward_noalloc(const void* q, const void* k, const void* v,
                         int N, int H, int W, int C, int heads, int S, int topk,
                         int dtype, void* out, int32_t* route_idx);
 
+/* The per-head routing variant (the qqiyuan.cn blog's BRA class routes
+ * every head on its own channels, section on region-level routing): for
+ * head h, steps 2-4 run on channels [h*32, h*32+32) alone -- region means of
+ * that slice, A_h = (Q^r_h * 32^-1/2) K^r_h^T (the class scales by
+ * head_dim^-1/2), top-k with the same order and tie rule -- and head h
+ * gathers its own routed regions; the joint softmax, LCE and merge are as in
+ * bra_forward. route_idx is int32 [N][heads][S*S][topk]. Same tensor
+ * conventions and checks as bra_forward. Runs the operator once per head on
+ * head-major copies of q, k, v (library workspace: 4 copies of the tensor,
+ * the per-head routes and one head's bra_forward workspace). */
+int bra_forward_head_routed(const void* q, const void* k, const void* v,
+                            const void* lce_w, const void* lce_b,
+                            int N, int H, int W, int C, int heads, int S, int topk,
+                            int dtype, void* out, int32_t* route_idx);
+
 /* The router-free attention of BiFormer's last stage (AttentionLePE; the
  * walk-through's module print, section 网络结构, and bernice.tw/posts/biformer,
  * section "Biformer", which gives that stage k = S^2): per image and head,

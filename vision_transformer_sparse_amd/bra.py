@@ -27,6 +27,7 @@ _SIGS = {
     "bra_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "bra_forward_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "bra_attention_dense": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
+    "bra_forward_head_routed": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "bra_region_means": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "bra_route": (_i, [_vp, _vp, _i, _i, _i, _i, _vp]),
     "bra_attend": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
@@ -134,6 +135,37 @@ def forward(q, k, v, lce_w, lce_b, heads: int, S: int, topk: int, out=None, rout
     with torch.cuda.device(dev):
         _stream(dev)
         _call("bra_forward", _ptr(q), _ptr(k), _ptr(v), _ptr(lce_w), _ptr(lce_b),
+              N, H, W, C, heads, S, topk, _dtype_code(q), _ptr(out), _ptr(route_idx))
+    return out, route_idx
+
+
+def forward_head_routed(q, k, v, lce_w, lce_b, heads: int, S: int, topk: int, out=None,
+                        route_idx=None):
+    """bra_forward_head_routed: returns (out, route_idx) with route_idx int32
+    (N, heads, S*S, topk) -- every head routed on its own channels."""
+    _check(q, "q")
+    dev, dt = q.device, q.dtype
+    for name, t in (("k", k), ("v", v), ("lce_w", lce_w)):
+        _check(t, name, dt, dev)
+    if lce_b is not None:
+        _check(lce_b, "lce_b", dt, dev)
+    N, H, W, C = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v shapes differ")
+    if lce_w.numel() != C * 25 or (lce_b is not None and lce_b.numel() != C):
+        raise ValueError("lce_w must hold C*25 and lce_b C elements")
+    if out is None:
+        out = torch.empty_like(q)
+    if route_idx is None:
+        route_idx = torch.empty((N, max(heads, 0), S * S, topk) if S > 0 and topk > 0 else (0,),
+                                dtype=torch.int32, device=dev)
+    _check(out, "out", dt, dev)
+    _check(route_idx, "route_idx", torch.int32, dev)
+    if out.shape != q.shape or route_idx.numel() != N * heads * S * S * topk:
+        raise ValueError("out / route_idx have the wrong size")
+    with torch.cuda.device(dev):
+        _stream(dev)
+        _call("bra_forward_head_routed", _ptr(q), _ptr(k), _ptr(v), _ptr(lce_w), _ptr(lce_b),
               N, H, W, C, heads, S, topk, _dtype_code(q), _ptr(out), _ptr(route_idx))
     return out, route_idx
 

@@ -47,6 +47,10 @@ hipError_t launch_attend_f32(const void* q, const void* k, const void* v, const 
                              const void* b, const int32_t* route, const Shape& s, void* out,
                              hipStream_t st);
 // kn: max |k|^2 per (image, region, head) from the pool kernel, or null
+// Layout moves of the per-head routing variant (heads.hip)
+hipError_t launch_head_split(const void* src, void* dst, long long tokens, int heads, int esz, hipStream_t st);
+hipError_t launch_head_merge(const void* src, void* dst, long long tokens, int heads, int esz, hipStream_t st);
+hipError_t launch_route_heads(const int32_t* src, int32_t* dst, int N, int heads, int rk, hipStream_t st);
 // The router-free last-stage attention (attn_dense.hip): bf16, at most 256
 // tokens a map
 bool dense_kernel_supports(const Shape& s);
@@ -436,6 +440,50 @@ int bra_attention_dense(const void* q, const void* k, const void* v, const void*
   if (rc) return rc;
   int32_t* route = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + routes_at);
   return forward_staged(q, k, v, lce_w, lce_b, s, dtype, out, route, ws, st);
+}
+
+int bra_forward_head_routed(const void* q, const void* k, const void* v, const void* lce_w,
+                            const void* lce_b, int N, int H, int W, int C, int heads, int S, int topk,
+                            int dtype, void* out, int32_t* route_idx) {
+  bra::Shape s;
+  int rc = check_forward(q, k, v, lce_w, lce_b, N, H, W, C, heads, S, topk, dtype, out, route_idx, &s);
+  if (rc) return rc;
+  // one head of the batch: the operator on 32 channels with one head
+  bra::Shape sh;
+  rc = check_dims(N, H, W, bra::kHeadDim, 1, S, topk, dtype, true, true, &sh);
+  if (rc) return rc;
+  hipStream_t st = g_stream;
+  const size_t esz = dtype == BRA_BF16 ? 2 : 4;
+  const long long tokens = (long long)N * H * W;
+  const size_t per_head = (size_t)tokens * bra::kHeadDim * esz;  // one head's tensor, bytes
+  const size_t tensor = ((size_t)heads * per_head + 255) & ~(size_t)255;
+  const size_t rk = (size_t)s.R * topk;
+  const size_t routes_at = 4 * tensor;
+  const size_t ws_at = (routes_at + (size_t)heads * N * rk * sizeof(int32_t) + 255) & ~(size_t)255;
+  std::lock_guard<std::mutex> lk(g_ws_mutex);
+  void* ws = nullptr;
+  rc = workspace(ws_at + ws_layout(N, bra::kHeadDim, S).total, &ws);
+  if (rc) return rc;
+  char* base = static_cast<char*>(ws);
+  char* qh = base;
+  char* kh = base + tensor;
+  char* vh = base + 2 * tensor;
+  char* oh = base + 3 * tensor;
+  int32_t* rh = reinterpret_cast<int32_t*>(base + routes_at);
+  hipError_t e = bra::launch_head_split(q, qh, tokens, heads, (int)esz, st);
+  if (e == hipSuccess) e = bra::launch_head_split(k, kh, tokens, heads, (int)esz, st);
+  if (e == hipSuccess) e = bra::launch_head_split(v, vh, tokens, heads, (int)esz, st);
+  if (e != hipSuccess) return hip_fail(e);
+  for (int h = 0; h < heads; ++h) {
+    const char* wh = static_cast<const char*>(lce_w) + (size_t)h * bra::kHeadDim * 25 * esz;
+    const char* bh = lce_b ? static_cast<const char*>(lce_b) + (size_t)h * bra::kHeadDim * esz : nullptr;
+    rc = forward_staged(qh + h * per_head, kh + h * per_head, vh + h * per_head, wh, bh, sh, dtype,
+                        oh + h * per_head, rh + (size_t)h * N * rk, base + ws_at, st);
+    if (rc) return rc;
+  }
+  e = bra::launch_head_merge(oh, out, tokens, heads, (int)esz, st);
+  if (e == hipSuccess) e = bra::launch_route_heads(rh, route_idx, N, heads, (int)rk, st);
+  return e == hipSuccess ? BRA_OK : hip_fail(e);
 }
 
 int bra_region_means(const void* q, const void* k, int N, int H, int W, int C, int S,
