@@ -35,7 +35,9 @@ One JSON line is printed. It carries:
 C -> C); "kernels" then also holds the projection kernel's roofline.
 The router-free last stage (s4: 128 images of 7x7 tokens, C = 512, 16 heads)
 is measured in per_config as its own workload: a step is one
-bra_attention_dense call. `--config s4` makes it the headline.
+bra_attention_dense call. `--config s4` makes it the headline. The per-head
+routing variant on the c4 shape (c4h: one bra_forward_head_routed call a
+step) is measured there too.
 """
 from __future__ import annotations
 
@@ -83,8 +85,10 @@ def algorithmic(cfg):
     }
 
 
-def roofline_for(kind, cfg, ms_per_launch, traffic):
-    alg = algorithmic(cfg)[kind]
+def roofline_for(kind, cfg, ms_per_launch, traffic, share=1.0):
+    """share: the fraction of the workload one launch processes (1/heads
+    for the per-head routing variant, which launches each kernel per head)."""
+    alg = {k: v * share for k, v in algorithmic(cfg)[kind].items()}
     t = ms_per_launch * 1e-3
     if kind == "linear" and cfg.dtype == "bf16":
         ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -94,7 +98,7 @@ def roofline_for(kind, cfg, ms_per_launch, traffic):
                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                     "traffic": traffic, "kernel": kind}
     if kind == "attn":
-        mfma_flops = 4 * cfg.N * cfg.H * cfg.W * cfg.C * cfg.L
+        mfma_flops = 4 * cfg.N * cfg.H * cfg.W * cfg.C * cfg.L * share
         if cfg.dtype == "bf16":
             ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
             if mfma_flops / alg["bytes"] > ridge:
@@ -225,7 +229,8 @@ class Workload:
         t = {k: torch.from_numpy(v.astype(np.float32)).to(dev, tdt) for k, v in inputs.items()}
         shape = (cfg.N, cfg.H, cfg.W, cfg.C)
         out = torch.empty(shape, dtype=tdt, device=dev)
-        route = torch.empty((cfg.N, cfg.R, cfg.topk), dtype=torch.int32, device=dev)
+        route = torch.empty((cfg.N, cfg.heads, cfg.R, cfg.topk) if op == "head_routed" else (cfg.N, cfg.R, cfg.topk),
+                            dtype=torch.int32, device=dev)
         if op == "block":
             qkv = [torch.empty(shape, dtype=tdt, device=dev) for _ in range(3)]
             y = torch.empty(shape, dtype=tdt, device=dev)
@@ -238,6 +243,10 @@ class Workload:
         elif op == "dense":
             def step():
                 bra.attention_dense(t["q"], t["k"], t["v"], t["lce_w"], t["lce_b"], cfg.heads, out=out)
+        elif op == "head_routed":
+            def step():
+                bra.forward_head_routed(t["q"], t["k"], t["v"], t["lce_w"], t["lce_b"], cfg.heads, cfg.S,
+                                        cfg.topk, out=out, route_idx=route)
         else:
             def step():
                 bra.forward(t["q"], t["k"], t["v"], t["lce_w"], t["lce_b"], cfg.heads, cfg.S,
@@ -245,12 +254,12 @@ class Workload:
         self.step = step
 
 
-def kernel_rooflines(prof, cfg):
+def kernel_rooflines(prof, cfg, share=1.0):
     kernels = {}
     for kind, (ms, cnt) in prof.items():
         if cnt:
             us = ms * 1e3 / cnt
-            r = roofline_for(kind, cfg, us * 1e-3, None)
+            r = roofline_for(kind, cfg, us * 1e-3, None, share)
             kernels[kind] = {"us_per_launch": round(us, 3), "launches": cnt, "bound": r["bound"],
                              "achieved": round(r["achieved"], 2), "unit": r["unit"],
                              "frac": round(r["frac"], 4)}
@@ -264,6 +273,7 @@ def measure_config(w, flush, n_warm, n_cold):
     from vision_transformer_sparse_amd import bra
 
     cfg = w.cfg
+    share = 1.0 / cfg.heads if w.op == "head_routed" else 1.0
     for _ in range(n_warm // 2):
         w.step()
     torch.cuda.synchronize()
@@ -275,7 +285,7 @@ def measure_config(w, flush, n_warm, n_cold):
     bra.profile_begin(bra.KERNEL_NAMES)
     for _ in range(max(20, n_warm // 4)):
         w.step()
-    kernels = kernel_rooflines(bra.profile_read(), cfg)
+    kernels = kernel_rooflines(bra.profile_read(), cfg, share)
     bra.profile_begin(())
     # cold: a 1 GiB write before each step; events around the step (torch's
     # current stream, which the binding hands to the library) and around the
@@ -300,7 +310,7 @@ def measure_config(w, flush, n_warm, n_cold):
             "queries_per_s": cfg.queries / (pctl(cold_us, 50) * 1e-6)}
     if attn_us:
         med = pctl(attn_us, 50)
-        r = roofline_for("attn", cfg, med * 1e-3, None)
+        r = roofline_for("attn", cfg, med * 1e-3, None, share)
         cold.update(attn_us_median=round(med, 3), attn_us_p10=round(pctl(attn_us, 10), 3),
                     attn_us_p90=round(pctl(attn_us, 90), 3), attn_frac=round(r["frac"], 4))
     return {"ms_per_step": round(warm_ms, 5), "queries_per_s": cfg.queries / (warm_ms * 1e-3),
@@ -348,12 +358,17 @@ def main(argv=None) -> int:
     head = None
     if a.per_config == "all":
         flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
-        for c in workloads:
-            w = Workload(c, a.op, dev)
-            per_config[c.name] = measure_config(w, flush, n_warm=1000, n_cold=a.cold)
-            print(f"[bench] per_config {c.name}: {per_config[c.name]['ms_per_step'] * 1e3:.2f} us/step warm, "
-                  f"{per_config[c.name]['cold']['step_us_median']:.2f} us cold", file=sys.stderr, flush=True)
-            if c is cfg:
+        runs = [(c.name, c, a.op) for c in workloads]
+        if a.op == "forward":
+            runs.append(("c4h", by_name["c4"], "head_routed"))
+        for name, c, op in runs:
+            w = Workload(c, op, dev)
+            per_config[name] = measure_config(w, flush, n_warm=1000, n_cold=a.cold)
+            if op == "head_routed":
+                per_config[name]["op"] = "bra_forward_head_routed (every head routed on its own channels)"
+            print(f"[bench] per_config {name}: {per_config[name]['ms_per_step'] * 1e3:.2f} us/step warm, "
+                  f"{per_config[name]['cold']['step_us_median']:.2f} us cold", file=sys.stderr, flush=True)
+            if c is cfg and op == a.op:
                 head = w
             else:
                 del w
