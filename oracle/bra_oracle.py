@@ -48,7 +48,7 @@ __all__ = [
     "check_shapes", "partition", "unpartition", "region_means",
     "region_affinity", "topk_routes", "gather_regions", "token_attention",
     "lce", "bra_forward", "linear", "round_bf16", "bra_block_forward",
-    "dense_attention", "bra_forward_head_routed",
+    "dense_attention", "bra_forward_head_routed", "bra_backward",
 ]
 
 
@@ -348,3 +348,65 @@ def bra_forward_head_routed(q, k, v, lce_w, lce_b, heads: int, S: int, topk: int
                                          gather_regions(vp[n:n + 1], route[n:n + 1]), 1)
         att[..., sl] = unpartition(o, S, H, W)
     return {"out": att + lce(v, w, b), "route_idx": used, "route_oracle": own, "logits": logits}
+
+
+def bra_backward(q, k, v, lce_w, route, dout, heads: int, S: int):
+    """Gradients of bra_forward's output with respect to q, k, v and the LCE
+    weights and bias, for given routes.
+
+    The walk-through's router (section "BRA模块") detaches the region means
+    before the affinity, so no gradient flows through the routing: the
+    routes are fixed indices here, as the forward used them. For image n,
+    head m and query region r with gathered keys/values K, V (rank-major, as
+    in gather_regions), queries Q and output gradient G (the rows of dout):
+      s = hd^-1/2 Q K^T,  P = softmax over each row,  O = P V;
+      dP = G V^T,  D = rowsum(P * dP) (= rowsum(G * O)),  dS = P * (dP - D);
+      dQ = hd^-1/2 dS K,  dK = hd^-1/2 dS^T Q,  dV = P^T G,
+    and the rows of dK, dV are added back to the regions they were gathered
+    from (a region routed by several query regions collects all their
+    contributions). LCE(v) = b + sum_{a,e} w[c,a,e] v[y+a-2, x+e-2] adds
+    dv[y', x'] = sum_{a,e} w[c,a,e] dout[y'-a+2, x'-e+2] (zero outside the
+    image), dw[c,a,e] = sum over pixels of dout[y,x,c] v[y+a-2, x+e-2, c] and
+    db[c] = sum over pixels of dout[.., c].
+    q, k, v, dout: (N, H, W, C); lce_w: (C, 5, 5); route: (N, S*S, topk).
+    Returns a dict with dq, dk, dv (N,H,W,C), dlce_w (C,5,5), dlce_b (C,)."""
+    q, k, v, g = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    N, H, W, C = q.shape
+    route = np.asarray(route, dtype=np.int64)
+    topk = route.shape[-1]
+    check_shapes(N, H, W, C, heads, S, topk)
+    R, hd = S * S, C // heads
+    scale = 1.0 / np.sqrt(hd)
+    w = np.asarray(lce_w, dtype=np.float64).reshape(C, 5, 5)
+    qp, kp, vp, gp = (partition(x, S) for x in (q, k, v, g))
+    T = qp.shape[2]
+    dqp, dkp, dvp = np.zeros_like(qp), np.zeros_like(kp), np.zeros_like(vp)
+    for n in range(N):
+        for m in range(heads):
+            sl = slice(m * hd, (m + 1) * hd)
+            for r in range(R):
+                Q, G = qp[n, r, :, sl], gp[n, r, :, sl]
+                Kg = np.concatenate([kp[n, s, :, sl] for s in route[n, r]])
+                Vg = np.concatenate([vp[n, s, :, sl] for s in route[n, r]])
+                sc = (Q @ Kg.T) * scale
+                P = np.exp(sc - sc.max(axis=1, keepdims=True))
+                P /= P.sum(axis=1, keepdims=True)
+                dP = G @ Vg.T
+                dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+                dqp[n, r, :, sl] += scale * (dS @ Kg)
+                dK, dV = scale * (dS.T @ Q), P.T @ G
+                for i, s in enumerate(route[n, r]):
+                    dkp[n, s, :, sl] += dK[i * T:(i + 1) * T]
+                    dvp[n, s, :, sl] += dV[i * T:(i + 1) * T]
+    dq, dk, dv = (unpartition(x, S, H, W) for x in (dqp, dkp, dvp))
+    gpad = np.zeros((N, H + 4, W + 4, C))
+    gpad[:, 2:H + 2, 2:W + 2, :] = g
+    vpad = np.zeros((N, H + 4, W + 4, C))
+    vpad[:, 2:H + 2, 2:W + 2, :] = v
+    dw = np.zeros((C, 5, 5))
+    for a in range(5):
+        for e in range(5):
+            # output (y, x) read v[y+a-2, x+e-2]: that pixel receives w * dout[y, x]
+            dv += w[:, a, e] * gpad[:, 4 - a:4 - a + H, 4 - e:4 - e + W, :]
+            dw[:, a, e] = (g * vpad[:, a:a + H, e:e + W, :]).sum(axis=(0, 1, 2))
+    return {"dq": dq, "dk": dk, "dv": dv, "dlce_w": dw, "dlce_b": g.sum(axis=(0, 1, 2))}

@@ -406,6 +406,72 @@ def pin_head_routed_all_regions_is_dense(O):
     assert np.allclose(got, _dense_reference(q, k, v, w, b, heads), rtol=1e-11, atol=1e-11)
 
 
+def _fd_check(O, N, H, W, C, heads, S, topk, seed, h=1e-6, rtol=1e-6):
+    """Directional finite differences of sum(bra_forward(...)["out"] * dout)
+    against bra_backward, for q, k, v, the LCE weights and bias."""
+    rng = _rng(seed)
+    q, k, v, g = (rng.standard_normal((N, H, W, C)) for _ in range(4))
+    w = rng.standard_normal((C, 5, 5)) * 0.3
+    b = rng.standard_normal(C) * 0.1
+    route = O.bra_forward(q, k, v, w, b, heads, S, topk)["route_idx"]
+    res = O.bra_backward(q, k, v, w, route, g, heads, S)
+    args = {"q": q, "k": k, "v": v, "w": w, "b": b}
+    f = lambda a: (O.bra_forward(a["q"], a["k"], a["v"], a["w"], a["b"], heads, S, topk,
+                                 route_override=route)["out"] * g).sum()
+    for name, key in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("w", "dlce_w"), ("b", "dlce_b")):
+        d = rng.standard_normal(args[name].shape)
+        ap, am = dict(args), dict(args)
+        ap[name], am[name] = args[name] + h * d, args[name] - h * d
+        fd = (f(ap) - f(am)) / (2 * h)
+        an = (res[key] * d).sum()
+        assert abs(fd - an) <= rtol * max(1.0, abs(fd)), (name, fd, an)
+
+
+def pin_backward_finite_differences(O):
+    """The routed gradients against central finite differences of the
+    forward (routes held fixed, as the detached router does): regions
+    routed by several query regions, topk 1 and S^2, one and three heads."""
+    for i, case in enumerate([(1, 4, 4, 4, 2, 2, 2), (2, 6, 6, 6, 3, 3, 3), (1, 4, 6, 4, 1, 2, 4),
+                              (1, 6, 6, 4, 2, 3, 1)]):
+        _fd_check(O, *case, seed=640 + i)
+
+
+def pin_backward_one_region_is_autograd(O):
+    """One region routed to itself (S = 1) is dense attention: the gradients
+    equal torch.autograd through scaled_dot_product_attention and the grouped
+    conv2d, in fp64."""
+    import torch
+    import torch.nn.functional as F
+    from einops import rearrange
+    rng = _rng(650)
+    N, H, W, C, heads = 2, 5, 4, 6, 3
+    q, k, v, g = (rng.standard_normal((N, H, W, C)) for _ in range(4))
+    w = rng.standard_normal((C, 5, 5)) * 0.3
+    b = rng.standard_normal(C) * 0.1
+    res = O.bra_backward(q, k, v, w, np.zeros((N, 1, 1), dtype=np.int64), g, heads, 1)
+    t = {n: torch.tensor(x, requires_grad=True) for n, x in (("q", q), ("k", k), ("v", v), ("w", w), ("b", b))}
+    split = lambda x: rearrange(x, "n h w (m c) -> n m (h w) c", m=heads)
+    o = rearrange(F.scaled_dot_product_attention(split(t["q"]), split(t["k"]), split(t["v"])),
+                  "n m (h w) c -> n h w (m c)", h=H)
+    l = F.conv2d(t["v"].permute(0, 3, 1, 2), t["w"].reshape(C, 1, 5, 5), t["b"], padding=2, groups=C)
+    ((o + l.permute(0, 2, 3, 1)) * torch.tensor(g)).sum().backward()
+    for n, key in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("w", "dlce_w"), ("b", "dlce_b")):
+        assert np.allclose(res[key], t[n].grad.numpy(), rtol=1e-10, atol=1e-10), n
+
+
+def pin_backward_value_gradient_sums(O):
+    """With the LCE weights zero, every query's probabilities sum to 1, so
+    the value gradients of an image sum (over all pixels, per channel) to the
+    sum of dout; the bias gradient is the sum of dout over the batch."""
+    rng = _rng(651)
+    N, H, W, C, heads, S, topk = 2, 6, 6, 4, 2, 3, 2
+    q, k, v, g = (rng.standard_normal((N, H, W, C)) for _ in range(4))
+    route = O.bra_forward(q, k, v, np.zeros((C, 5, 5)), None, heads, S, topk)["route_idx"]
+    res = O.bra_backward(q, k, v, np.zeros((C, 5, 5)), route, g, heads, S)
+    assert np.allclose(res["dv"].sum(axis=(1, 2)), g.sum(axis=(1, 2)), rtol=0, atol=1e-11)
+    assert np.allclose(res["dlce_b"], g.sum(axis=(0, 1, 2)), rtol=0, atol=1e-11)
+
+
 # ---------------------------------------------------------------- LCE
 def pin_lce_delta_kernel(O):
     rng = _rng(13)

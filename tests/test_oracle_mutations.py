@@ -169,7 +169,61 @@ def _head_routed_scale_C(q, k, v, lce_w, lce_b, heads, S, topk, route_override=N
     return res
 
 
+def _backward_variant(mode):
+    """bra_backward with one planted mistake (the same steps otherwise)."""
+    def f(q, k, v, lce_w, route, dout, heads, S):
+        q, k, v, g = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+        N, H, W, C = q.shape
+        route = np.asarray(route, dtype=np.int64)
+        R, hd = S * S, C // heads
+        scale = 1.0 / np.sqrt(hd)
+        w = np.asarray(lce_w, dtype=np.float64).reshape(C, 5, 5)
+        qp, kp, vp, gp = (O.partition(x, S) for x in (q, k, v, g))
+        T = qp.shape[2]
+        dqp, dkp, dvp = np.zeros_like(qp), np.zeros_like(kp), np.zeros_like(vp)
+        for n in range(N):
+            for m in range(heads):
+                sl = slice(m * hd, (m + 1) * hd)
+                for r in range(R):
+                    Q, G = qp[n, r, :, sl], gp[n, r, :, sl]
+                    rr = (route[n, r] + 1) % R if mode == "scatter_wrong_region" else route[n, r]
+                    Kg = np.concatenate([kp[n, s, :, sl] for s in route[n, r]])
+                    Vg = np.concatenate([vp[n, s, :, sl] for s in route[n, r]])
+                    sc = (Q @ Kg.T) * scale
+                    P = np.exp(sc - sc.max(axis=1, keepdims=True))
+                    P /= P.sum(axis=1, keepdims=True)
+                    dP = G @ Vg.T
+                    D = 0.0 if mode == "no_D" else (P * dP).sum(axis=1, keepdims=True)
+                    dS = P * (dP - D)
+                    dqp[n, r, :, sl] += (1.0 if mode == "dq_unscaled" else scale) * (dS @ Kg)
+                    dK, dV = scale * (dS.T @ Q), P.T @ G
+                    for i, s in enumerate(rr):
+                        dkp[n, s, :, sl] += dK[i * T:(i + 1) * T]
+                        dvp[n, s, :, sl] += dV[i * T:(i + 1) * T]
+        dq, dk, dv = (O.unpartition(x, S, H, W) for x in (dqp, dkp, dvp))
+        gpad = np.zeros((N, H + 4, W + 4, C))
+        gpad[:, 2:H + 2, 2:W + 2, :] = g
+        vpad = np.zeros((N, H + 4, W + 4, C))
+        vpad[:, 2:H + 2, 2:W + 2, :] = v
+        dw = np.zeros((C, 5, 5))
+        for a in range(5):
+            for e in range(5):
+                src = gpad[:, a:a + H, e:e + W, :] if mode == "lce_dv_unflipped" else \
+                    gpad[:, 4 - a:4 - a + H, 4 - e:4 - e + W, :]
+                dv += w[:, a, e] * src
+                dw[:, a, e] = (g * vpad[:, a:a + H, e:e + W, :]).sum(axis=(0, 1, 2))
+        if mode == "lce_dw_transposed":
+            dw = np.swapaxes(dw, 1, 2)
+        return {"dq": dq, "dk": dk, "dv": dv, "dlce_w": dw, "dlce_b": g.sum(axis=(0, 1, 2))}
+    return f
+
+
 MUTATIONS = {
+    "backward_without_D": ("bra_backward", _backward_variant("no_D")),
+    "backward_dq_unscaled": ("bra_backward", _backward_variant("dq_unscaled")),
+    "backward_scatter_wrong_region": ("bra_backward", _backward_variant("scatter_wrong_region")),
+    "backward_lce_dv_unflipped": ("bra_backward", _backward_variant("lce_dv_unflipped")),
+    "backward_lce_dw_transposed": ("bra_backward", _backward_variant("lce_dw_transposed")),
     "head_routed_shares_routes": ("bra_forward_head_routed", _head_routed_shared),
     "head_routed_heads_swapped": ("bra_forward_head_routed", _head_routed_heads_swapped),
     "head_routed_scale_uses_C": ("bra_forward_head_routed", _head_routed_scale_C),
