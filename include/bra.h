@@ -105,6 +105,26 @@ int bra_forward_noalloc(const void* q, const void* k, const void* v,
                         int N, int H, int W, int C, int heads, int S, int topk,
                         int dtype, void* out, int32_t* route_idx);
 
+/* Backward of the operator for given routes (training): gradients of
+ * sum(out * dout) with respect to q, k, v (same layout and dtype as the
+ * inputs), the LCE weights (dlce_w, fp32 [C][25]) and the LCE bias (dlce_b,
+ * fp32 [C], or NULL to skip). The walk-through (section BRA模块) detaches the
+ * router, so route_idx -- the forward's routes, int32 [N][S*S][topk], every
+ * entry in [0, S*S) (not checked on the device) -- is an input and gets no
+ * gradient. For query region r with gathered keys/values K, V and rows G of
+ * dout: dS = P * (G V^T - rowsum(G * O)), dQ = hd^-1/2 dS K, and each routed
+ * region collects hd^-1/2 dS^T Q into dk and P^T G into dv; LCE adds dout
+ * correlated with the flipped 5x5 kernel to dv, dlce_w[c][a*5+e] = sum over
+ * pixels of dout * v shifted by (a-2, e-2), dlce_b[c] = sum of dout.
+ * Every gradient is a fixed-order sum (bit-reproducible). bf16 only, with
+ * regions of a multiple of 16 tokens and topk <= 16 (else
+ * BRA_ERR_UNSUPPORTED). Uses the library workspace; alignment as for
+ * bra_forward (dout, dq, dk, dv 16 bytes; dlce_w, dlce_b 4 bytes). */
+int bra_backward(const void* q, const void* k, const void* v, const void* lce_w,
+                 const int32_t* route_idx, const void* dout,
+                 int N, int H, int W, int C, int heads, int S, int topk, int dtype,
+                 void* dq, void* dk, void* dv, float* dlce_w, float* dlce_b);
+
 /* The per-head routing variant (the qqiyuan.cn blog's BRA class routes
  * every head on its own channels, section on region-level routing): for
  * head h, steps 2-4 run on channels [h*32, h*32+32) alone -- region means of

@@ -28,6 +28,8 @@ _SIGS = {
     "bra_forward_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "bra_attention_dense": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]),
     "bra_forward_head_routed": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp]),
+    "bra_backward": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
+                          _vp, _vp, _vp, _vp, _vp]),
     "bra_region_means": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "bra_route": (_i, [_vp, _vp, _i, _i, _i, _i, _vp]),
     "bra_attend": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
@@ -137,6 +139,32 @@ def forward(q, k, v, lce_w, lce_b, heads: int, S: int, topk: int, out=None, rout
         _call("bra_forward", _ptr(q), _ptr(k), _ptr(v), _ptr(lce_w), _ptr(lce_b),
               N, H, W, C, heads, S, topk, _dtype_code(q), _ptr(out), _ptr(route_idx))
     return out, route_idx
+
+
+def backward(q, k, v, lce_w, route_idx, dout, heads: int, S: int, lce_b_grad: bool = True):
+    """bra_backward: returns (dq, dk, dv, dlce_w, dlce_b) for the given routes
+    (dlce_w fp32 (C, 25), dlce_b fp32 (C,) or None)."""
+    _check(q, "q")
+    dev, dt = q.device, q.dtype
+    for name, t in (("k", k), ("v", v), ("lce_w", lce_w), ("dout", dout)):
+        _check(t, name, dt, dev)
+    _check(route_idx, "route_idx", torch.int32, dev)
+    N, H, W, C = q.shape
+    if k.shape != q.shape or v.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, k, v, dout shapes differ")
+    if lce_w.numel() != C * 25:
+        raise ValueError("lce_w must hold C*25 elements")
+    topk = route_idx.shape[-1]
+    if route_idx.numel() != N * S * S * topk:
+        raise ValueError("route_idx must be (N, S*S, topk)")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dw = torch.empty((C, 25), dtype=torch.float32, device=dev)
+    db = torch.empty((C,), dtype=torch.float32, device=dev) if lce_b_grad else None
+    with torch.cuda.device(dev):
+        _stream(dev)
+        _call("bra_backward", _ptr(q), _ptr(k), _ptr(v), _ptr(lce_w), _ptr(route_idx), _ptr(dout),
+              N, H, W, C, heads, S, topk, _dtype_code(q), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dw), _ptr(db))
+    return dq, dk, dv, dw, db
 
 
 def forward_head_routed(q, k, v, lce_w, lce_b, heads: int, S: int, topk: int, out=None,

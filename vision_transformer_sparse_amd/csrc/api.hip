@@ -47,6 +47,13 @@ hipError_t launch_attend_f32(const void* q, const void* k, const void* v, const 
                              const void* b, const int32_t* route, const Shape& s, void* out,
                              hipStream_t st);
 // kn: max |k|^2 per (image, region, head) from the pool kernel, or null
+// The backward for given routes (backward.hip): bf16, head_dim 32, regions of
+// a multiple of 16 tokens, topk <= 16
+bool backward_supports(const Shape& s, int dtype);
+size_t backward_workspace_bytes(const Shape& s);
+hipError_t launch_backward(const void* q, const void* k, const void* v, const void* w, const int32_t* route,
+                           const void* dout, const Shape& s, void* dq, void* dk, void* dv, float* dw, float* db,
+                           void* ws, hipStream_t st);
 // Layout moves of the per-head routing variant (heads.hip)
 hipError_t launch_head_split(const void* src, void* dst, long long tokens, int heads, int esz, hipStream_t st);
 hipError_t launch_head_merge(const void* src, void* dst, long long tokens, int heads, int esz, hipStream_t st);
@@ -483,6 +490,32 @@ int bra_forward_head_routed(const void* q, const void* k, const void* v, const v
   }
   e = bra::launch_head_merge(oh, out, tokens, heads, (int)esz, st);
   if (e == hipSuccess) e = bra::launch_route_heads(rh, route_idx, N, heads, (int)rk, st);
+  return e == hipSuccess ? BRA_OK : hip_fail(e);
+}
+
+int bra_backward(const void* q, const void* k, const void* v, const void* lce_w,
+                 const int32_t* route_idx, const void* dout, int N, int H, int W, int C, int heads,
+                 int S, int topk, int dtype, void* dq, void* dk, void* dv, float* dlce_w,
+                 float* dlce_b) {
+  if (!q || !k || !v || !lce_w || !route_idx || !dout || !dq || !dk || !dv || !dlce_w) return BRA_ERR_NULL;
+  bra::Shape s;
+  int rc = check_dims(N, H, W, C, heads, S, topk, dtype, true, true, &s);
+  if (rc) return rc;
+  rc = check_align({q, k, v, dout, dq, dk, dv}, {route_idx, dlce_w, dlce_b});
+  if (rc) return rc;
+  rc = check_ptrs({q, k, v, lce_w, route_idx, dout, dq, dk, dv, dlce_w, dlce_b});
+  if (rc) return rc;
+  if (!bra::backward_supports(s, dtype)) return BRA_ERR_UNSUPPORTED;
+  hipStream_t st = g_stream;
+  std::lock_guard<std::mutex> lk(g_ws_mutex);
+  void* ws = nullptr;
+  rc = workspace(bra::backward_workspace_bytes(s), &ws);
+  if (rc) return rc;
+  hipError_t e;
+  {
+    ProfScope ps(BRA_K_ATTN, st);
+    e = bra::launch_backward(q, k, v, lce_w, route_idx, dout, s, dq, dk, dv, dlce_w, dlce_b, ws, st);
+  }
   return e == hipSuccess ? BRA_OK : hip_fail(e);
 }
 
