@@ -12,8 +12,8 @@
 //   dW[c][a][e] = sum dout * v shifted, db[c] = sum dout.
 //
 // bf16 tensors, head_dim 32, regions of a multiple of 16 tokens. Kernels:
-//  * inv_route_kernel: per image, the routers of every region (CSR, routers
-//    in ascending order), so the key side gathers instead of scattering and
+//  * inv_route_kernel: per (image, region), the regions that route to it, in
+//    ascending order, so the key side gathers instead of scattering and
 //    every gradient is a fixed-order sum (no atomics).
 //  * bwd_query_kernel: one workgroup per (image, region, head, up to 64
 //    queries), a wave per 16 queries; 32-key tiles of the gathered K and V
@@ -41,7 +41,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTile = 32;                                // keys (query side) / queries (key side) a tile
+constexpr int kBwdMaxWaves = 8;  // waves of a backward workgroup, at most
 constexpr float kQs = 0.17677669529663687f * 1.4426950408889634f;  // hd^-1/2 in log2 units
 constexpr float kScale = 0.17677669529663687f;                     // hd^-1/2
 
@@ -52,10 +52,11 @@ struct BwdArgs {
   const uint16_t* g;   // dout
   const uint16_t* w;   // LCE weights [C][25]
   const int32_t* route;
-  const int32_t* inv_off;  // [N][R+1]
-  const int32_t* inv_ent;  // [N][R*topk]
+  const int32_t* inv_cnt;  // [N][R]: routers of each region
+  const int32_t* inv_ent;  // [N][R][R]: their indices, ascending
   float* lse;              // [N][H*W][heads], base 2
   float* dsum;             // [N][H*W][heads]
+  const float* dv_lce;     // [N][H][W][C]: dv's LCE term
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -102,45 +103,48 @@ __device__ __forceinline__ void store_slice(Rsrc r, uint32_t off, int g, const f
 }
 
 // ---------------------------------------------------------------- routers
-// Per image: off[s] .. off[s+1] index the routers of region s in ent, in
-// ascending order of the routing region r.
-__global__ __launch_bounds__(256) void inv_route_kernel(const int32_t* __restrict__ route, int R, int topk,
-                                                        int32_t* __restrict__ off, int32_t* __restrict__ ent) {
-  extern __shared__ int cnt[];  // [R]
-  const int n = blockIdx.x, tid = threadIdx.x;
-  const int32_t* rt = route + (size_t)n * R * topk;
-  for (int s = tid; s < R; s += blockDim.x) {
-    int c = 0;
-    for (int e = 0; e < R * topk; ++e) c += rt[e] == s;
-    cnt[s] = c;
+// One wave per (image, region s): the routers of s (the regions r whose row
+// of the route table holds s) in ascending order of r, at most R of them (a
+// row's routes are distinct), into ent[n][s][0 .. cnt-1]: the wave walks the
+// image's table 64 entries at a time and compacts the matches with a ballot.
+__global__ __launch_bounds__(64) void inv_route_kernel(const int32_t* __restrict__ route, int R, int topk,
+                                                       int32_t* __restrict__ cnt, int32_t* __restrict__ ent) {
+  const int ns = blockIdx.x, n = ns / R, s = ns - n * R, lane = threadIdx.x;
+  const int RK = R * topk;
+  const int32_t* rt = route + (size_t)n * RK;
+  int32_t* out = ent + (size_t)ns * R;
+  int c = 0;
+  for (int e0 = 0; e0 < RK; e0 += 64) {
+    const int e = e0 + lane;
+    const bool hit = e < RK && rt[e] == s;
+    const uint64_t mask = __ballot(hit);
+    if (hit) out[c + __builtin_popcountll(mask & ((1ull << lane) - 1))] = e / topk;
+    c += __builtin_popcountll(mask);
   }
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int s = 0; s < R; ++s) {
-      const int c = cnt[s];
-      cnt[s] = acc;
-      acc += c;
-    }
-    off[(size_t)n * (R + 1) + R] = acc;
-  }
-  __syncthreads();
-  for (int s = tid; s < R; s += blockDim.x) {
-    int o = cnt[s];
-    off[(size_t)n * (R + 1) + s] = o;
-    for (int e = 0; e < R * topk; ++e)
-      if (rt[e] == s) ent[(size_t)n * R * topk + o++] = e / topk;
-  }
+  if (lane == 0) cnt[ns] = c;
 }
 
 // ---------------------------------------------------------------- query side
-template <int WAVES>
+// Rows [0, TILE) of two [TILE][64-byte] LDS tiles, loaded as 16-byte pieces:
+// thread `tid` of `threads` holds pieces tid, tid + threads, ... (PPT of
+// them) in registers between the load and the store, so the next tile's loads
+// are in flight while the current tile is used.
+template <int TILE, int THREADS>
+struct TilePair {
+  static constexpr int PPT = (TILE * 4 + THREADS - 1) / THREADS;
+  uint4 a[PPT], b[PPT];
+};
+
+template <int WAVES, int TK, int QB>
 __global__ __launch_bounds__(64 * WAVES) void bwd_query_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * kTile * 64];  // K tile | V tile, [32][64 bytes]
+  // QB 16-query blocks a wave: every K / V / K^T / V^T operand read from LDS
+  // serves all of them
+  constexpr int TH = 64 * WAVES;
+  __shared__ __attribute__((aligned(16))) char lds[2 * TK * 64];  // K tile | V tile, [TK][64 bytes]
   __shared__ uint32_t rbase[16];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, g = lane >> 4;
-  const int GPR = a.T / 16 / WAVES;  // query groups of a region
+  const int GPR = a.T / 16 / (WAVES * QB);  // query groups of a region
   int u = xcd_unit(blockIdx.x, gridDim.x);
   const int qg = u % GPR;
   u /= GPR;
@@ -154,12 +158,18 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_query_kernel(BwdArgs a) {
   const Rsrc qr = rsrc(a.q + img, img_bytes), kr = rsrc(a.k + img, img_bytes), vr = rsrc(a.v + img, img_bytes);
   const Rsrc gr = rsrc(a.g + img, img_bytes), dqr = rsrc(a.dq + img, img_bytes);
 
-  // this wave's 16 queries of region r
-  const int t = 16 * (qg * WAVES + wave) + col;
-  const int qpix = ((r / a.S) * a.rh + t / a.rw) * a.W + (r % a.S) * a.rw + t % a.rw;
-  const uint32_t qoff = (uint32_t)qpix * rowb + hoff;
-  const bf16x8 bq = as8(ld16(qr, qoff + 16 * g));
-  const bf16x8 bg = as8(ld16(gr, qoff + 16 * g));
+  // this wave's QB blocks of 16 queries of region r
+  int qpix[QB];
+  uint32_t qoff[QB];
+  bf16x8 bq[QB], bg[QB];
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    const int t = 16 * ((qg * WAVES + wave) * QB + b) + col;
+    qpix[b] = ((r / a.S) * a.rh + t / a.rw) * a.W + (r % a.S) * a.rw + t % a.rw;
+    qoff[b] = (uint32_t)qpix[b] * rowb + hoff;
+    bq[b] = as8(ld16(qr, qoff[b] + 16 * g));
+    bg[b] = as8(ld16(gr, qoff[b] + 16 * g));
+  }
   if (tid < a.topk) {
     const int s = a.route[((size_t)n * a.R + r) * a.topk + tid];
     rbase[tid] = (uint32_t)(((s / a.S) * a.rh * a.W + (s % a.S) * a.rw)) * rowb + hoff;
@@ -167,128 +177,193 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_query_kernel(BwdArgs a) {
   __syncthreads();
 
   char* kt_lds = lds;
-  char* vt_lds = lds + kTile * 64;
-  // keys u0 .. u0+31 of the gathered sequence into LDS (rows past L read zero)
-  auto load_tile = [&](int u0) {
-    for (int e = tid; e < kTile * 4; e += 64 * WAVES) {
-      const int kk = e >> 2, ch = e & 3, uu = u0 + kk;
+  char* vt_lds = lds + TK * 64;
+  TilePair<TK, TH> pre;
+  auto fetch = [&](int u0) {  // keys u0 .. u0+TK-1 of the gathered sequence (past L: zeros)
+#pragma unroll
+    for (int i = 0; i < TilePair<TK, TH>::PPT; ++i) {
+      const int e = tid + i * TH, kk = e >> 2, ch = e & 3, uu = u0 + kk;
       uint32_t off = kOut;
-      if (uu < a.L) {
+      if (e < TK * 4 && uu < a.L) {
         const int p = uu / a.T, j = uu - p * a.T;
         off = rbase[p] + (uint32_t)((j / a.rw) * a.W + j % a.rw) * rowb + ch * 16;
       }
-      const uint4 kx = ld16(kr, off), vx = ld16(vr, off);
-      *reinterpret_cast<uint4*>(kt_lds + kk * 64 + ch * 16) = kx;
-      *reinterpret_cast<uint4*>(vt_lds + kk * 64 + ch * 16) = vx;
+      pre.a[i] = ld16(kr, off);
+      pre.b[i] = ld16(vr, off);
+    }
+  };
+  auto park = [&]() {
+#pragma unroll
+    for (int i = 0; i < TilePair<TK, TH>::PPT; ++i) {
+      const int e = tid + i * TH;
+      if (e < TK * 4) {
+        *reinterpret_cast<uint4*>(kt_lds + e * 16) = pre.a[i];
+        *reinterpret_cast<uint4*>(vt_lds + e * 16) = pre.b[i];
+      }
     }
   };
   const int r4 = col >> 2, c4 = col & 3;  // this lane's row and piece of the transposing reads
+  constexpr int KS = TK / 32;             // 32-key steps of a tile
 
-  // pass 1: forward with an online maximum
-  float m = -__builtin_inff(), l = 0.f;
-  f32x4 o[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  for (int u0 = 0; u0 < a.L; u0 += kTile) {
-    __syncthreads();
-    load_tile(u0);
-    __syncthreads();
-    f32x4 sc[2];
-    float mt = -__builtin_inff();
+  // pass 1: forward with an online maximum (one maximum a tile)
+  float m[QB], l[QB];
+  f32x4 o[QB][2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      sc[kt] = mfma(*reinterpret_cast<const bf16x8*>(kt_lds + (16 * kt + col) * 64 + 16 * g), bq,
-                    f32x4{0.f, 0.f, 0.f, 0.f});
+  for (int b = 0; b < QB; ++b) {
+    m[b] = -__builtin_inff();
+    l[b] = 0.f;
+    o[b][0] = o[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  fetch(0);
+  for (int u0 = 0; u0 < a.L; u0 += TK) {
+    __syncthreads();
+    park();
+    __syncthreads();
+    if (u0 + TK < a.L) fetch(u0 + TK);
+    f32x4 sc[QB][2 * KS];
+    float mt[QB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc[kt][i] = u0 + 16 * kt + 4 * g + i < a.L ? sc[kt][i] * kQs : -__builtin_inff();
-        mt = __builtin_elementwise_maximum(mt, sc[kt][i]);
+    for (int b = 0; b < QB; ++b) mt[b] = -__builtin_inff();
+#pragma unroll
+    for (int kt = 0; kt < 2 * KS; ++kt) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt_lds + (16 * kt + col) * 64 + 16 * g);
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        sc[b][kt] = mfma(ka, bq[b], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc[b][kt][i] = u0 + 16 * kt + 4 * g + i < a.L ? sc[b][kt][i] * kQs : -__builtin_inff();
+          mt[b] = __builtin_elementwise_maximum(mt[b], sc[b][kt][i]);
+        }
       }
     }
-    const float mn = __builtin_elementwise_maximum(m, group_max(mt));
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    l *= alpha;
+    float mn[QB];
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
+    for (int b = 0; b < QB; ++b) {
+      mn[b] = __builtin_elementwise_maximum(m[b], group_max(mt[b]));
+      const float alpha = __builtin_amdgcn_exp2f(m[b] - mn[b]);
+      l[b] *= alpha;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[dt][i] *= alpha;
-    bf16x4 p[2];
+      for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+        for (int i = 0; i < 4; ++i) o[b][dt][i] *= alpha;
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[kt][i] = (__bf16)__builtin_amdgcn_exp2f(sc[kt][i] - mn);
-        l += (float)p[kt][i];
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 pb[QB];
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        bf16x4 p[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[j][i] = (__bf16)__builtin_amdgcn_exp2f(sc[b][2 * ks + j][i] - mn[b]);
+            l[b] += (float)p[j][i];
+          }
+        pb[b] = cat(p[0], p[1]);
       }
-    const bf16x8 pb = cat(p[0], p[1]);
-    const char* v0 = vt_lds + (4 * g + r4) * 64 + 8 * c4;
-    const char* v1 = vt_lds + (16 + 4 * g + r4) * 64 + 8 * c4;
+      const char* v0 = vt_lds + (32 * ks + 4 * g + r4) * 64 + 8 * c4;
+      const char* v1 = vt_lds + (32 * ks + 16 + 4 * g + r4) * 64 + 8 * c4;
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) o[dt] = mfma(cat(ld_tr(v0 + 32 * dt), ld_tr(v1 + 32 * dt)), pb, o[dt]);
-    m = mn;
-  }
-  l = group_sum(l);
-  const float inv = 1.f / l;
-  // D = G . O over the head's 32 channels (the lane holds 8 of them)
-  float dpart = 0.f;
+      for (int dt = 0; dt < 2; ++dt) {
+        const bf16x8 va = cat(ld_tr(v0 + 32 * dt), ld_tr(v1 + 32 * dt));
 #pragma unroll
-  for (int dt = 0; dt < 2; ++dt) {
-    const uint32_t x0 = __builtin_amdgcn_raw_buffer_load_b32(gr, qoff + (16 * dt + 4 * g) * 2, 0, 0);
-    const uint32_t x1 = __builtin_amdgcn_raw_buffer_load_b32(gr, qoff + (16 * dt + 4 * g) * 2 + 4, 0, 0);
-    dpart = fmaf(o[dt][0], bf16_lo(x0), dpart);
-    dpart = fmaf(o[dt][1], bf16_hi(x0), dpart);
-    dpart = fmaf(o[dt][2], bf16_lo(x1), dpart);
-    dpart = fmaf(o[dt][3], bf16_hi(x1), dpart);
+        for (int b = 0; b < QB; ++b) o[b][dt] = mfma(va, pb[b], o[b][dt]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < QB; ++b) m[b] = mn[b];
   }
-  const float D = group_sum(dpart) * inv;
-  const float lse = m + __builtin_amdgcn_logf(l);  // base 2
-  if (g == 0) {
-    const size_t si = ((size_t)n * HW + qpix) * a.heads + h;
-    a.lse[si] = lse;
-    a.dsum[si] = D;
+  float lse[QB], D[QB];
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    const float lb = group_sum(l[b]);
+    // D = G . O over the head's 32 channels (the lane holds 8 of them)
+    float dpart = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      const uint32_t x0 = __builtin_amdgcn_raw_buffer_load_b32(gr, qoff[b] + (16 * dt + 4 * g) * 2, 0, 0);
+      const uint32_t x1 = __builtin_amdgcn_raw_buffer_load_b32(gr, qoff[b] + (16 * dt + 4 * g) * 2 + 4, 0, 0);
+      dpart = fmaf(o[b][dt][0], bf16_lo(x0), dpart);
+      dpart = fmaf(o[b][dt][1], bf16_hi(x0), dpart);
+      dpart = fmaf(o[b][dt][2], bf16_lo(x1), dpart);
+      dpart = fmaf(o[b][dt][3], bf16_hi(x1), dpart);
+    }
+    D[b] = group_sum(dpart) / lb;
+    lse[b] = m[b] + __builtin_amdgcn_logf(lb);  // base 2
+    if (g == 0) {
+      const size_t si = ((size_t)n * HW + qpix[b]) * a.heads + h;
+      a.lse[si] = lse[b];
+      a.dsum[si] = D[b];
+    }
   }
 
   // pass 2: dQ^T += K^T dS^T
-  f32x4 dqt[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  for (int u0 = 0; u0 < a.L; u0 += kTile) {
-    __syncthreads();
-    load_tile(u0);
-    __syncthreads();
-    bf16x4 ds[2];
+  f32x4 dqt[QB][2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const f32x4 sc = mfma(*reinterpret_cast<const bf16x8*>(kt_lds + (16 * kt + col) * 64 + 16 * g), bq,
-                            f32x4{0.f, 0.f, 0.f, 0.f});
-      const f32x4 dp = mfma(*reinterpret_cast<const bf16x8*>(vt_lds + (16 * kt + col) * 64 + 16 * g), bg,
-                            f32x4{0.f, 0.f, 0.f, 0.f});
+  for (int b = 0; b < QB; ++b) dqt[b][0] = dqt[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  fetch(0);
+  for (int u0 = 0; u0 < a.L; u0 += TK) {
+    __syncthreads();
+    park();
+    __syncthreads();
+    if (u0 + TK < a.L) fetch(u0 + TK);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = u0 + 16 * kt + 4 * g + i < a.L ? __builtin_amdgcn_exp2f(fmaf(sc[i], kQs, -lse)) : 0.f;
-        ds[kt][i] = (__bf16)(p * (dp[i] - D));
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x4 ds[QB][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = 32 * ks + 16 * j + col;
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt_lds + row * 64 + 16 * g);
+        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(vt_lds + row * 64 + 16 * g);
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+          const f32x4 sc = mfma(ka, bq[b], f32x4{0.f, 0.f, 0.f, 0.f});
+          const f32x4 dp = mfma(vb, bg[b], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool live = u0 + 32 * ks + 16 * j + 4 * g + i < a.L;
+            const float p = live ? __builtin_amdgcn_exp2f(fmaf(sc[i], kQs, -lse[b])) : 0.f;
+            ds[b][j][i] = (__bf16)(p * (dp[i] - D[b]));
+          }
+        }
+      }
+      const char* k0 = kt_lds + (32 * ks + 4 * g + r4) * 64 + 8 * c4;
+      const char* k1 = kt_lds + (32 * ks + 16 + 4 * g + r4) * 64 + 8 * c4;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const bf16x8 ka = cat(ld_tr(k0 + 32 * dt), ld_tr(k1 + 32 * dt));
+#pragma unroll
+        for (int b = 0; b < QB; ++b) dqt[b][dt] = mfma(ka, cat(ds[b][0], ds[b][1]), dqt[b][dt]);
       }
     }
-    const bf16x8 dsb = cat(ds[0], ds[1]);
-    const char* k0 = kt_lds + (4 * g + r4) * 64 + 8 * c4;
-    const char* k1 = kt_lds + (16 + 4 * g + r4) * 64 + 8 * c4;
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt) dqt[dt] = mfma(cat(ld_tr(k0 + 32 * dt), ld_tr(k1 + 32 * dt)), dsb, dqt[dt]);
   }
-  float d0[4], d1[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    d0[i] = dqt[0][i] * kScale;
-    d1[i] = dqt[1][i] * kScale;
+  for (int b = 0; b < QB; ++b) {
+    float d0[4], d1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      d0[i] = dqt[b][0][i] * kScale;
+      d1[i] = dqt[b][1][i] * kScale;
+    }
+    store_slice(dqr, qoff[b], g, d0, d1, true);
   }
-  store_slice(dqr, qoff, g, d0, d1, true);
 }
 
 // ---------------------------------------------------------------- key side
-template <int WAVES>
+template <int WAVES, int TQ, int KB>
 __global__ __launch_bounds__(64 * WAVES) void bwd_key_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * kTile * 64];  // Q tile | G tile
-  __shared__ float st_lse[kTile], st_d[kTile];
-  __shared__ float wl[25 * 32];  // the head's LCE weights, [tap][channel]
+  // KB 16-key blocks a wave: every Q / G / Q^T / G^T operand read from LDS
+  // serves all of them
+  constexpr int TH = 64 * WAVES;
+  __shared__ __attribute__((aligned(16))) char lds[2 * TQ * 64];  // Q tile | G tile
+  __shared__ __attribute__((aligned(16))) float st_lse[TQ];
+  __shared__ __attribute__((aligned(16))) float st_d[TQ];
+  __shared__ int routers[1024];  // the regions routing to s, ascending
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, g = lane >> 4;
-  const int GPR = a.T / 16 / WAVES;
+  const int GPR = a.T / 16 / (WAVES * KB);
   int u = xcd_unit(blockIdx.x, gridDim.x);
   const int kg = u % GPR;
   u /= GPR;
@@ -303,177 +378,292 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_key_kernel(BwdArgs a) {
   const Rsrc gr = rsrc(a.g + img, img_bytes);
   const Rsrc dkr = rsrc(a.dk + img, img_bytes), dvr = rsrc(a.dv + img, img_bytes);
 
-  // this wave's 16 keys of region s: K and V rows as B operands
-  const int j = 16 * (kg * WAVES + wave) + col;
-  const int ky = (s / a.S) * a.rh + j / a.rw, kx = (s % a.S) * a.rw + j % a.rw;
-  const uint32_t koff = (uint32_t)(ky * a.W + kx) * rowb + hoff;
-  const bf16x8 bk = as8(ld16(kr, koff + 16 * g));
-  const bf16x8 bv = as8(ld16(vr, koff + 16 * g));
-  for (int e = tid; e < 25 * 32; e += 64 * WAVES) {
-    const int tap = e >> 5, c = e & 31;
-    wl[e] = bf16_bits_to_float(a.w[(size_t)(h * 32 + c) * 25 + tap]);
+  // this wave's KB blocks of 16 keys of region s: K and V rows as B operands
+  int ky[KB], kx[KB];
+  uint32_t koff[KB];
+  bf16x8 bk[KB], bv[KB];
+#pragma unroll
+  for (int b = 0; b < KB; ++b) {
+    const int j = 16 * ((kg * WAVES + wave) * KB + b) + col;
+    ky[b] = (s / a.S) * a.rh + j / a.rw;
+    kx[b] = (s % a.S) * a.rw + j % a.rw;
+    koff[b] = (uint32_t)(ky[b] * a.W + kx[b]) * rowb + hoff;
+    bk[b] = as8(ld16(kr, koff[b] + 16 * g));
+    bv[b] = as8(ld16(vr, koff[b] + 16 * g));
   }
+  const int nrout = a.inv_cnt[(size_t)n * a.R + s];
+  for (int e = tid; e < nrout; e += TH) routers[e] = a.inv_ent[((size_t)n * a.R + s) * a.R + e];
+  __syncthreads();
 
   char* qt_lds = lds;
-  char* gt_lds = lds + kTile * 64;
+  char* gt_lds = lds + TQ * 64;
   const int r4 = col >> 2, c4 = col & 3;
-  f32x4 dkt[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  f32x4 dvt[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  const int beg = a.inv_off[(size_t)n * (a.R + 1) + s], end = a.inv_off[(size_t)n * (a.R + 1) + s + 1];
-  for (int ei = beg; ei < end; ++ei) {
-    const int r = a.inv_ent[(size_t)n * a.R * a.topk + ei];
+  constexpr int QS = TQ / 32;
+  f32x4 dkt[KB][2], dvt[KB][2];
+#pragma unroll
+  for (int b = 0; b < KB; ++b) dkt[b][0] = dkt[b][1] = dvt[b][0] = dvt[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int tiles_per_router = (a.T + TQ - 1) / TQ, ntiles = nrout * tiles_per_router;
+  TilePair<TQ, TH> pre;
+  float pl = 0.f, pd = 0.f;  // the statistics of query tid of the prefetched tile
+  auto fetch = [&](int it) {  // tile it: router it / tiles_per_router, its queries t0 .. t0+TQ-1
+    const int r = routers[it / tiles_per_router];
+    const int t0 = (it % tiles_per_router) * TQ;
     const int ry = (r / a.S) * a.rh, rx = (r % a.S) * a.rw;
-    for (int t0 = 0; t0 < a.T; t0 += kTile) {
-      __syncthreads();
-      for (int e = tid; e < kTile * 4; e += 64 * WAVES) {  // query rows t0 .. t0+31 of region r
-        const int kk = e >> 2, ch = e & 3, tq = t0 + kk;
-        const uint32_t off = tq < a.T ? (uint32_t)((ry + tq / a.rw) * a.W + rx + tq % a.rw) * rowb + hoff + ch * 16
-                                      : kOut;
-        const uint4 qx = ld16(qr, off), gx = ld16(gr, off);
-        *reinterpret_cast<uint4*>(qt_lds + kk * 64 + ch * 16) = qx;
-        *reinterpret_cast<uint4*>(gt_lds + kk * 64 + ch * 16) = gx;
+#pragma unroll
+    for (int i = 0; i < TilePair<TQ, TH>::PPT; ++i) {
+      const int e = tid + i * TH, kk = e >> 2, ch = e & 3, tq = t0 + kk;
+      const uint32_t off = e < TQ * 4 && tq < a.T
+                               ? (uint32_t)((ry + tq / a.rw) * a.W + rx + tq % a.rw) * rowb + hoff + ch * 16
+                               : kOut;
+      pre.a[i] = ld16(qr, off);
+      pre.b[i] = ld16(gr, off);
+    }
+    pl = pd = 0.f;
+    if (tid < TQ && t0 + tid < a.T) {
+      const int tq = t0 + tid;
+      const size_t si = ((size_t)n * HW + (ry + tq / a.rw) * a.W + rx + tq % a.rw) * a.heads + h;
+      pl = a.lse[si];
+      pd = a.dsum[si];
+    }
+  };
+  if (ntiles > 0) fetch(0);
+  for (int it = 0; it < ntiles; ++it) {
+    const int t0 = (it % tiles_per_router) * TQ;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TilePair<TQ, TH>::PPT; ++i) {
+      const int e = tid + i * TH;
+      if (e < TQ * 4) {
+        *reinterpret_cast<uint4*>(qt_lds + e * 16) = pre.a[i];
+        *reinterpret_cast<uint4*>(gt_lds + e * 16) = pre.b[i];
       }
-      if (tid < kTile) {
-        const int tq = t0 + tid;
-        float lv = 0.f, dv_ = 0.f;
-        if (tq < a.T) {
-          const size_t si = ((size_t)n * HW + (ry + tq / a.rw) * a.W + rx + tq % a.rw) * a.heads + h;
-          lv = a.lse[si];
-          dv_ = a.dsum[si];
-        }
-        st_lse[tid] = lv;
-        st_d[tid] = dv_;
-      }
-      __syncthreads();
-      bf16x4 pb[2], dsb[2];
+    }
+    if (tid < TQ) {
+      st_lse[tid] = pl;
+      st_d[tid] = pd;
+    }
+    __syncthreads();
+    if (it + 1 < ntiles) fetch(it + 1);
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) {
+      bf16x4 pb[KB][2], dsb[KB][2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
-        const f32x4 sc = mfma(*reinterpret_cast<const bf16x8*>(qt_lds + (16 * qt + col) * 64 + 16 * g), bk,
-                              f32x4{0.f, 0.f, 0.f, 0.f});
-        const f32x4 dp = mfma(*reinterpret_cast<const bf16x8*>(gt_lds + (16 * qt + col) * 64 + 16 * g), bv,
-                              f32x4{0.f, 0.f, 0.f, 0.f});
+        const int row = 32 * qs + 16 * qt + col;
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt_lds + row * 64 + 16 * g);
+        const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gt_lds + row * 64 + 16 * g);
+        const int q4 = 32 * qs + 16 * qt + 4 * g;  // this lane's four query rows
+        const f32x4 lq = *reinterpret_cast<const f32x4*>(st_lse + q4);
+        const f32x4 dq4 = *reinterpret_cast<const f32x4*>(st_d + q4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int qi = 16 * qt + 4 * g + i;
-          const float p = t0 + qi < a.T ? __builtin_amdgcn_exp2f(fmaf(sc[i], kQs, -st_lse[qi])) : 0.f;
-          pb[qt][i] = (__bf16)p;
-          dsb[qt][i] = (__bf16)(p * (dp[i] - st_d[qi]));
+        for (int b = 0; b < KB; ++b) {
+          const f32x4 sc = mfma(qa, bk[b], f32x4{0.f, 0.f, 0.f, 0.f});
+          const f32x4 dp = mfma(ga, bv[b], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = t0 + q4 + i < a.T ? __builtin_amdgcn_exp2f(fmaf(sc[i], kQs, -lq[i])) : 0.f;
+            pb[b][qt][i] = (__bf16)p;
+            dsb[b][qt][i] = (__bf16)(p * (dp[i] - dq4[i]));
+          }
         }
       }
-      const bf16x8 pB = cat(pb[0], pb[1]), dsB = cat(dsb[0], dsb[1]);
-      const int q0 = (4 * g + r4) * 64 + 8 * c4, q1 = (16 + 4 * g + r4) * 64 + 8 * c4;
+      const int q0 = (32 * qs + 4 * g + r4) * 64 + 8 * c4, q1 = (32 * qs + 16 + 4 * g + r4) * 64 + 8 * c4;
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
-        dvt[dt] = mfma(cat(ld_tr(gt_lds + q0 + 32 * dt), ld_tr(gt_lds + q1 + 32 * dt)), pB, dvt[dt]);
-        dkt[dt] = mfma(cat(ld_tr(qt_lds + q0 + 32 * dt), ld_tr(qt_lds + q1 + 32 * dt)), dsB, dkt[dt]);
-      }
-    }
-  }
-  __syncthreads();  // the weights are in LDS
-  // dV's LCE term: the key pixel feeds outputs (ky + 2 - a, kx + 2 - e) through tap (a, e)
-  float lv0[4] = {0.f, 0.f, 0.f, 0.f}, lv1[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-  for (int ta = 0; ta < 5; ++ta) {  // one window row's loads in flight at a time
-    const int yy = ky + 2 - ta;
+        const bf16x8 gta = cat(ld_tr(gt_lds + q0 + 32 * dt), ld_tr(gt_lds + q1 + 32 * dt));
+        const bf16x8 qta = cat(ld_tr(qt_lds + q0 + 32 * dt), ld_tr(qt_lds + q1 + 32 * dt));
 #pragma unroll
-    for (int te = 0; te < 5; ++te) {
-      const int xx = kx + 2 - te;
-      const bool in = yy >= 0 && yy < a.H && xx >= 0 && xx < a.W;
-      const uint32_t go = in ? (uint32_t)(yy * a.W + xx) * rowb + hoff : kOut;
-      const float* wt = wl + (5 * ta + te) * 32;
-      const uint32_t g0a = __builtin_amdgcn_raw_buffer_load_b32(gr, go + 8 * g, 0, 0);
-      const uint32_t g0b = __builtin_amdgcn_raw_buffer_load_b32(gr, go + 8 * g + 4, 0, 0);
-      const uint32_t g1a = __builtin_amdgcn_raw_buffer_load_b32(gr, go + 32 + 8 * g, 0, 0);
-      const uint32_t g1b = __builtin_amdgcn_raw_buffer_load_b32(gr, go + 32 + 8 * g + 4, 0, 0);
-      lv0[0] = fmaf(wt[4 * g + 0], bf16_lo(g0a), lv0[0]);
-      lv0[1] = fmaf(wt[4 * g + 1], bf16_hi(g0a), lv0[1]);
-      lv0[2] = fmaf(wt[4 * g + 2], bf16_lo(g0b), lv0[2]);
-      lv0[3] = fmaf(wt[4 * g + 3], bf16_hi(g0b), lv0[3]);
-      lv1[0] = fmaf(wt[16 + 4 * g + 0], bf16_lo(g1a), lv1[0]);
-      lv1[1] = fmaf(wt[16 + 4 * g + 1], bf16_hi(g1a), lv1[1]);
-      lv1[2] = fmaf(wt[16 + 4 * g + 2], bf16_lo(g1b), lv1[2]);
-      lv1[3] = fmaf(wt[16 + 4 * g + 3], bf16_hi(g1b), lv1[3]);
-    }
-  }
-  float k0[4], k1[4], v0[4], v1[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    k0[i] = dkt[0][i] * kScale;
-    k1[i] = dkt[1][i] * kScale;
-    v0[i] = dvt[0][i] + lv0[i];
-    v1[i] = dvt[1][i] + lv1[i];
-  }
-  store_slice(dkr, koff, g, k0, k1, true);
-  store_slice(dvr, koff, g, v0, v1, true);
-}
-
-// ---------------------------------------------------------------- LCE weights
-// Row (n, y), channel c: the 25 tap sums sum_x dout[y][x][c] * v[y+a-2][x+e-2][c]
-// and the bias sum, into part[(n*H + y)][c][26].
-__global__ __launch_bounds__(256) void lce_grad_rows_kernel(const uint16_t* __restrict__ v,
-                                                            const uint16_t* __restrict__ g, int H, int W, int C,
-                                                            float* __restrict__ part) {
-  const int ny = blockIdx.x, n = ny / H, y = ny - n * H;
-  const size_t img = (size_t)n * H * W * C;
-  for (int c = threadIdx.x; c < C; c += blockDim.x) {
-    float acc[25], accb = 0.f;
-#pragma unroll
-    for (int i = 0; i < 25; ++i) acc[i] = 0.f;
-    for (int x = 0; x < W; ++x) {
-      const float gv = bf16_bits_to_float(g[img + ((size_t)y * W + x) * C + c]);
-      accb += gv;
-#pragma unroll
-      for (int ta = 0; ta < 5; ++ta) {
-        const int yy = y + ta - 2;
-        if (yy < 0 || yy >= H) continue;
-#pragma unroll
-        for (int te = 0; te < 5; ++te) {
-          const int xx = x + te - 2;
-          if (xx < 0 || xx >= W) continue;
-          acc[5 * ta + te] = fmaf(gv, bf16_bits_to_float(v[img + ((size_t)yy * W + xx) * C + c]), acc[5 * ta + te]);
+        for (int b = 0; b < KB; ++b) {
+          dvt[b][dt] = mfma(gta, cat(pb[b][0], pb[b][1]), dvt[b][dt]);
+          dkt[b][dt] = mfma(qta, cat(dsb[b][0], dsb[b][1]), dkt[b][dt]);
         }
       }
     }
-    float* o = part + ((size_t)ny * C + c) * 26;
+  }
+  // dV's LCE term, computed beforehand in fp32
 #pragma unroll
-    for (int i = 0; i < 25; ++i) o[i] = acc[i];
-    o[25] = accb;
+  for (int b = 0; b < KB; ++b) {
+    const float* lp = a.dv_lce + img + (size_t)(ky[b] * a.W + kx[b]) * a.C + h * 32;
+    const f32x4 lv0 = *reinterpret_cast<const f32x4*>(lp + 4 * g);
+    const f32x4 lv1 = *reinterpret_cast<const f32x4*>(lp + 16 + 4 * g);
+    float k0[4], k1[4], v0[4], v1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      k0[i] = dkt[b][0][i] * kScale;
+      k1[i] = dkt[b][1][i] * kScale;
+      v0[i] = dvt[b][0][i] + lv0[i];
+      v1[i] = dvt[b][1][i] + lv1[i];
+    }
+    store_slice(dkr, koff[b], g, k0, k1, true);
+    store_slice(dvr, koff[b], g, v0, v1, true);
   }
 }
 
-// dw[c][tap] and db[c]: the row partials summed in row order
-__global__ __launch_bounds__(256) void lce_grad_sum_kernel(const float* __restrict__ part, int rows, int C,
+// ---------------------------------------------------------------- LCE terms
+// One workgroup per (image, block of kLceRows rows, block of 16 channels):
+// the V rows and the dout rows of the block and two more on each side
+// (columns -2 .. W+1, zero outside the image) are staged in LDS as 16-byte
+// pieces. Thread (channel c, column group xg) takes columns x = xg, xg + 16,
+// ...: it sums the 25 tap terms dout[y][x] * v[y+a-2][x+e-2] and the bias
+// term (the 16 column groups are then added in a fixed order into
+// part[block][c][26]) and writes dv's LCE term sum_{a,e} w[a][e] *
+// dout[y-a+2][x-e+2] (fp32, the key side adds it to the attention part).
+constexpr int kLceRows = 4;
+constexpr int kLceCh = 16;
+__host__ __device__ inline size_t lce_grad_lds(int W) {
+  const size_t stage = (size_t)2 * (kLceRows + 4) * (W + 4) * kLceCh * 2 + (size_t)25 * kLceCh * sizeof(float);
+  const size_t red = (size_t)16 * kLceCh * 26 * sizeof(float) + (size_t)25 * kLceCh * sizeof(float);
+  return stage > red ? stage : red;
+}
+
+__global__ __launch_bounds__(256) void lce_grad_rows_kernel(const uint16_t* __restrict__ v,
+                                                            const uint16_t* __restrict__ g,
+                                                            const uint16_t* __restrict__ lw, int N, int H, int W,
+                                                            int C, float* __restrict__ part,
+                                                            float* __restrict__ dv_lce) {
+  extern __shared__ __attribute__((aligned(16))) char sm[];
+  const int YB = (H + kLceRows - 1) / kLceRows, CB = C / kLceCh;
+  int u = blockIdx.x;
+  const int cb = u % CB;
+  u /= CB;
+  const int yb = u % YB, n = u / YB;
+  const int y0 = yb * kLceRows, tid = threadIdx.x;
+  const int WB = W + 4, RB = kLceRows + 4;
+  float* wsm = reinterpret_cast<float*>(sm);                        // [25][16] weights of the block's channels
+  uint16_t* vs = reinterpret_cast<uint16_t*>(sm + 25 * kLceCh * 4);  // [RB][W+4][16]
+  uint16_t* gs = vs + (size_t)RB * WB * kLceCh;                      // [RB][W+4][16]
+  const size_t img = (size_t)n * H * W * C;
+  const uint32_t img_bytes = (uint32_t)((size_t)H * W * C * 2);
+  const Rsrc vr = rsrc(v + img, img_bytes), gr = rsrc(g + img, img_bytes);
+  const uint32_t cofs = (uint32_t)cb * kLceCh * 2;
+  for (int e = tid; e < 25 * kLceCh; e += 256) {
+    const int tap = e / kLceCh, c = e - tap * kLceCh;
+    wsm[e] = bf16_bits_to_float(lw[(size_t)(cb * kLceCh + c) * 25 + tap]);
+  }
+  // staging: two 16-byte pieces (8 channels each) per pixel, rows y0-2 .. y0+RB-3
+  // (four pieces of each a thread in flight before any is stored)
+  const int pieces = RB * WB * 2;
+  constexpr int kBatch = 4;
+  for (int e0 = tid; e0 < pieces; e0 += 256 * kBatch) {
+    uint4 vx[kBatch], gx[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int e = e0 + 256 * i, pix = e >> 1, half = e & 1, ry = pix / WB, rx = pix - ry * WB;
+      const int y = y0 + ry - 2, x = rx - 2;
+      const uint32_t off = e < pieces && y >= 0 && y < H && x >= 0 && x < W
+                               ? (uint32_t)((y * W + x) * C * 2) + cofs + 16 * half
+                               : kOut;
+      vx[i] = ld16(vr, off);
+      gx[i] = ld16(gr, off);
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int e = e0 + 256 * i;
+      if (e < pieces) {
+        reinterpret_cast<uint4*>(vs)[e] = vx[i];
+        reinterpret_cast<uint4*>(gs)[e] = gx[i];
+      }
+    }
+  }
+  __syncthreads();
+  const int c = tid & 15, xg = tid >> 4;
+  float acc[26];
+#pragma unroll
+  for (int i = 0; i < 26; ++i) acc[i] = 0.f;
+  for (int ry = 0; ry < kLceRows; ++ry) {
+    const int y = y0 + ry;
+    for (int x = xg; x < W; x += 16) {
+      const float gv = bf16_bits_to_float(gs[((size_t)(ry + 2) * WB + x + 2) * kLceCh + c]);
+      acc[25] += gv;
+      float dl = 0.f;
+#pragma unroll
+      for (int ta = 0; ta < 5; ++ta)
+#pragma unroll
+        for (int te = 0; te < 5; ++te) {
+          acc[5 * ta + te] = fmaf(gv, bf16_bits_to_float(vs[((size_t)(ry + ta) * WB + x + te) * kLceCh + c]),
+                                  acc[5 * ta + te]);
+          // v[y][x] feeds output (y + 2 - ta, x + 2 - te) through tap (ta, te)
+          dl = fmaf(wsm[(5 * ta + te) * kLceCh + c],
+                    bf16_bits_to_float(gs[((size_t)(ry + 4 - ta) * WB + x + 4 - te) * kLceCh + c]), dl);
+        }
+      if (y < H) dv_lce[img + ((size_t)y * W + x) * C + cb * kLceCh + c] = dl;
+    }
+  }
+  __syncthreads();  // the staging area becomes the reduction area
+  float* red = reinterpret_cast<float*>(sm + 25 * kLceCh * 4);  // [16 xg][16 c][26]
+#pragma unroll
+  for (int i = 0; i < 26; ++i) red[((size_t)xg * kLceCh + c) * 26 + i] = acc[i];
+  __syncthreads();
+  for (int e = tid; e < kLceCh * 26; e += 256) {
+    float sum = 0.f;
+    for (int j = 0; j < 16; ++j) sum += red[(size_t)j * kLceCh * 26 + e];
+    part[((size_t)(n * YB + yb) * C + cb * kLceCh) * 26 + e] = sum;
+  }
+}
+
+// dw[c][tap] and db[c]: 32 threads per (c, tap) element add the blocks j,
+// j + 32, ... in order, then a fixed butterfly adds the 32 partial sums
+__global__ __launch_bounds__(256) void lce_grad_sum_kernel(const float* __restrict__ part, int blocks, int C,
                                                            float* __restrict__ dw, float* __restrict__ db) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;  // c * 26 + tap
-  if (e >= C * 26) return;
+  const int e = blockIdx.x * 8 + (threadIdx.x >> 5), j = threadIdx.x & 31;
+  const bool live = e < C * 26;
   float acc = 0.f;
-  for (int r = 0; r < rows; ++r) acc += part[(size_t)r * C * 26 + e];
+  if (live)
+    for (int b = j; b < blocks; b += 32) acc += part[(size_t)b * C * 26 + e];
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 32);
+  if (!live || j != 0) return;
   const int c = e / 26, tap = e - c * 26;
   if (tap < 25) dw[(size_t)c * 25 + tap] = acc;
   else if (db) db[c] = acc;
 }
 
-template <int WAVES>
+template <int WAVES, int TK, int TQ, int BPW>
 hipError_t launch_sides(const BwdArgs& a, hipStream_t st) {
-  const unsigned units = (unsigned)(a.N * a.R * a.heads * (a.T / 16 / WAVES));
-  launch(bwd_query_kernel<WAVES>, dim3(units), dim3(64 * WAVES), 0, st, a);
+  const unsigned units = (unsigned)(a.N * a.R * a.heads * (a.T / 16 / (WAVES * BPW)));
+  launch(bwd_query_kernel<WAVES, TK, BPW>, dim3(units), dim3(64 * WAVES), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  launch(bwd_key_kernel<WAVES>, dim3(units), dim3(64 * WAVES), 0, st, a);
+  launch(bwd_key_kernel<WAVES, TQ, BPW>, dim3(units), dim3(64 * WAVES), 0, st, a);
   return hipGetLastError();
+}
+
+// A region's 16-token blocks two to a wave when there are at least two, the
+// waves of one workgroup covering up to 256 tokens; key tiles of 64 keys for
+// workgroups of 4 or 8 waves (so the query side stays within 128 registers
+// and two workgroups share a CU), else 128 (64, 32 for short gathered
+// sequences); query tiles of up to 128 by T.
+hipError_t launch_sides_for(const BwdArgs& a, hipStream_t st) {
+  const int blocks = a.T / 16;
+  const bool big = a.L >= 128;
+  if (blocks % 2) {  // odd block counts: one block a wave, one wave a workgroup
+    return big ? launch_sides<1, 128, 32, 1>(a, st)
+               : a.L >= 64 ? launch_sides<1, 64, 32, 1>(a, st) : launch_sides<1, 32, 32, 1>(a, st);
+  }
+  const int pairs = blocks / 2;
+  int waves = pairs % 8 == 0 ? 8 : pairs % 4 == 0 ? 4 : pairs % 2 == 0 ? 2 : 1;
+  if (waves > kBwdMaxWaves) waves = kBwdMaxWaves;
+  switch (waves) {
+    case 8: return launch_sides<8, 64, 128, 2>(a, st);  // <= 128 VGPRs: two workgroups a CU
+    case 4: return launch_sides<4, 64, 128, 2>(a, st);
+    case 2: return big ? launch_sides<2, 128, 64, 2>(a, st) : launch_sides<2, 64, 64, 2>(a, st);
+    default: return big ? launch_sides<1, 128, 32, 2>(a, st) : launch_sides<1, 64, 32, 2>(a, st);
+  }
 }
 
 }  // namespace
 
 bool backward_supports(const Shape& s, int dtype) {
-  return dtype == 1 && s.hd == 32 && s.T % 16 == 0 && s.topk <= 16 && s.R <= 1024;
+  return dtype == 1 && s.hd == 32 && s.T % 16 == 0 && s.topk <= 16 && s.R <= 1024 &&
+         lce_grad_lds(s.W) <= 96 * 1024 && (size_t)s.H * s.W * s.C * 2 < (1ull << 31);
 }
 
 size_t backward_workspace_bytes(const Shape& s) {
   const size_t stats = (size_t)s.N * s.H * s.W * s.heads * sizeof(float);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  return 2 * al(stats) + al((size_t)s.N * (s.R + 1) * 4) + al((size_t)s.N * s.R * s.topk * 4) +
-         al((size_t)s.N * s.H * s.C * 26 * sizeof(float));
+  return 2 * al(stats) + al((size_t)s.N * s.R * 4) + al((size_t)s.N * s.R * s.R * 4) +
+         al((size_t)s.N * ((s.H + kLceRows - 1) / kLceRows) * s.C * 26 * sizeof(float)) +
+         al((size_t)s.N * s.H * s.W * s.C * sizeof(float));
 }
 
 hipError_t launch_backward(const void* q, const void* k, const void* v, const void* w, const int32_t* route,
@@ -493,12 +683,15 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const vo
   p += al(stats);
   a.dsum = reinterpret_cast<float*>(p);
   p += al(stats);
-  int32_t* off = reinterpret_cast<int32_t*>(p);
-  p += al((size_t)s.N * (s.R + 1) * 4);
+  int32_t* cnt = reinterpret_cast<int32_t*>(p);
+  p += al((size_t)s.N * s.R * 4);
   int32_t* ent = reinterpret_cast<int32_t*>(p);
-  p += al((size_t)s.N * s.R * s.topk * 4);
+  p += al((size_t)s.N * s.R * s.R * 4);
   float* part = reinterpret_cast<float*>(p);
-  a.inv_off = off;
+  p += al((size_t)s.N * ((s.H + kLceRows - 1) / kLceRows) * s.C * 26 * sizeof(float));
+  float* dvl = reinterpret_cast<float*>(p);
+  a.dv_lce = dvl;
+  a.inv_cnt = cnt;
   a.inv_ent = ent;
   a.dq = (uint16_t*)dq;
   a.dk = (uint16_t*)dk;
@@ -506,19 +699,20 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const vo
   a.N = s.N; a.H = s.H; a.W = s.W; a.C = s.C; a.heads = s.heads; a.S = s.S; a.topk = s.topk;
   a.R = s.R; a.rh = s.rh; a.rw = s.rw; a.T = s.T; a.L = s.L;
 
-  launch(inv_route_kernel, dim3((unsigned)s.N), dim3(256), (size_t)s.R * sizeof(int), st, route, s.R, s.topk, off,
-         ent);
+  launch(inv_route_kernel, dim3((unsigned)(s.N * s.R)), dim3(64), 0, st, route, s.R, s.topk, cnt, ent);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int qgroups = s.T / 16;
-  e = qgroups % 4 == 0 ? launch_sides<4>(a, st) : qgroups % 2 == 0 ? launch_sides<2>(a, st) : launch_sides<1>(a, st);
-  if (e != hipSuccess) return e;
-  launch(lce_grad_rows_kernel, dim3((unsigned)(s.N * s.H)), dim3(s.C < 256 ? ((s.C + 63) / 64) * 64 : 256), 0, st,
-         (const uint16_t*)v, (const uint16_t*)dout, s.H, s.W, s.C, part);
+  const int lblocks = s.N * ((s.H + kLceRows - 1) / kLceRows);
+  launch(lce_grad_rows_kernel, dim3((unsigned)(lblocks * (s.C / kLceCh))), dim3(256), lce_grad_lds(s.W), st,
+         (const uint16_t*)v, (const uint16_t*)dout, (const uint16_t*)w, s.N, s.H, s.W, s.C, part, dvl);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  launch(lce_grad_sum_kernel, dim3((unsigned)((s.C * 26 + 255) / 256)), dim3(256), 0, st, (const float*)part,
-         s.N * s.H, s.C, dw, db);
+  launch(lce_grad_sum_kernel, dim3((unsigned)((s.C * 26 + 7) / 8)), dim3(256), 0, st, (const float*)part, lblocks,
+         s.C, dw, db);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_sides_for(a, st);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 
