@@ -56,7 +56,7 @@ struct BwdArgs {
   const int32_t* inv_ent;  // [N][R][R]: their indices, ascending
   float* lse;              // [N][H*W][heads], base 2
   float* dsum;             // [N][H*W][heads]
-  const float* dv_lce;     // [N][H][W][C]: dv's LCE term
+  const float* dv_lce;     // [N][C/8][H][W][8]: dv's LCE term, channel blocks of 8
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -135,8 +135,9 @@ struct TilePair {
   uint4 a[PPT], b[PPT];
 };
 
-template <int WAVES, int TK, int QB>
+template <int WAVES, int TK, int QB, bool FULL>
 __global__ __launch_bounds__(64 * WAVES) void bwd_query_kernel(BwdArgs a) {
+  // FULL: every key tile is whole (L a multiple of TK), so no key is masked
   // QB 16-query blocks a wave: every K / V / K^T / V^T operand read from LDS
   // serves all of them
   constexpr int TH = 64 * WAVES;
@@ -205,21 +206,19 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_query_kernel(BwdArgs a) {
   const int r4 = col >> 2, c4 = col & 3;  // this lane's row and piece of the transposing reads
   constexpr int KS = TK / 32;             // 32-key steps of a tile
 
-  // pass 1: forward with an online maximum (one maximum a tile)
-  float m[QB], l[QB];
-  f32x4 o[QB][2];
+  // pass 1: forward with an online maximum (one maximum a tile); the row
+  // sums of the bf16 P on the matrix cores (ones x P^T). Only the last tile
+  // can hold keys past L; the others skip the masks.
+  const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                       (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+  float m[QB];
+  f32x4 o[QB][2], lsum[QB];
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     m[b] = -__builtin_inff();
-    l[b] = 0.f;
-    o[b][0] = o[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    o[b][0] = o[b][1] = lsum[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  fetch(0);
-  for (int u0 = 0; u0 < a.L; u0 += TK) {
-    __syncthreads();
-    park();
-    __syncthreads();
-    if (u0 + TK < a.L) fetch(u0 + TK);
+  auto tile1 = [&](int u0) {
     f32x4 sc[QB][2 * KS];
     float mt[QB];
 #pragma unroll
@@ -232,7 +231,8 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_query_kernel(BwdArgs a) {
         sc[b][kt] = mfma(ka, bq[b], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          sc[b][kt][i] = u0 + 16 * kt + 4 * g + i < a.L ? sc[b][kt][i] * kQs : -__builtin_inff();
+          if constexpr (!FULL)
+            if (u0 + 16 * kt + 4 * g + i >= a.L) sc[b][kt][i] = -__builtin_inff();
           mt[b] = __builtin_elementwise_maximum(mt[b], sc[b][kt][i]);
         }
       }
@@ -240,13 +240,15 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_query_kernel(BwdArgs a) {
     float mn[QB];
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
-      mn[b] = __builtin_elementwise_maximum(m[b], group_max(mt[b]));
+      mn[b] = __builtin_elementwise_maximum(m[b], group_max(mt[b]) * kQs);  // the scale is positive
       const float alpha = __builtin_amdgcn_exp2f(m[b] - mn[b]);
-      l[b] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[b][dt][i] *= alpha;
+      for (int i = 0; i < 4; ++i) {
+        o[b][0][i] *= alpha;
+        o[b][1][i] *= alpha;
+        lsum[b][i] *= alpha;
+      }
+      m[b] = mn[b];
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -257,11 +259,10 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_query_kernel(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[j][i] = (__bf16)__builtin_amdgcn_exp2f(sc[b][2 * ks + j][i] - mn[b]);
-            l[b] += (float)p[j][i];
-          }
+          for (int i = 0; i < 4; ++i)
+            p[j][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[b][2 * ks + j][i], kQs, -mn[b]));
         pb[b] = cat(p[0], p[1]);
+        lsum[b] = mfma(ones, pb[b], lsum[b]);
       }
       const char* v0 = vt_lds + (32 * ks + 4 * g + r4) * 64 + 8 * c4;
       const char* v1 = vt_lds + (32 * ks + 16 + 4 * g + r4) * 64 + 8 * c4;
@@ -272,13 +273,19 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_query_kernel(BwdArgs a) {
         for (int b = 0; b < QB; ++b) o[b][dt] = mfma(va, pb[b], o[b][dt]);
       }
     }
-#pragma unroll
-    for (int b = 0; b < QB; ++b) m[b] = mn[b];
+  };
+  fetch(0);
+  for (int u0 = 0; u0 < a.L; u0 += TK) {
+    __syncthreads();
+    park();
+    __syncthreads();
+    if (u0 + TK < a.L) fetch(u0 + TK);
+    tile1(u0);
   }
   float lse[QB], D[QB];
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
-    const float lb = group_sum(l[b]);
+    const float lb = lsum[b][0];
     // D = G . O over the head's 32 channels (the lane holds 8 of them)
     float dpart = 0.f;
 #pragma unroll
@@ -303,12 +310,7 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_query_kernel(BwdArgs a) {
   f32x4 dqt[QB][2];
 #pragma unroll
   for (int b = 0; b < QB; ++b) dqt[b][0] = dqt[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  fetch(0);
-  for (int u0 = 0; u0 < a.L; u0 += TK) {
-    __syncthreads();
-    park();
-    __syncthreads();
-    if (u0 + TK < a.L) fetch(u0 + TK);
+  auto tile2 = [&](int u0) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16x4 ds[QB][2];
@@ -323,8 +325,9 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_query_kernel(BwdArgs a) {
           const f32x4 dp = mfma(vb, bg[b], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const bool live = u0 + 32 * ks + 16 * j + 4 * g + i < a.L;
-            const float p = live ? __builtin_amdgcn_exp2f(fmaf(sc[i], kQs, -lse[b])) : 0.f;
+            float p = __builtin_amdgcn_exp2f(fmaf(sc[i], kQs, -lse[b]));
+            if constexpr (!FULL)
+              if (u0 + 32 * ks + 16 * j + 4 * g + i >= a.L) p = 0.f;
             ds[b][j][i] = (__bf16)(p * (dp[i] - D[b]));
           }
         }
@@ -338,6 +341,14 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_query_kernel(BwdArgs a) {
         for (int b = 0; b < QB; ++b) dqt[b][dt] = mfma(ka, cat(ds[b][0], ds[b][1]), dqt[b][dt]);
       }
     }
+  };
+  fetch(0);
+  for (int u0 = 0; u0 < a.L; u0 += TK) {
+    __syncthreads();
+    park();
+    __syncthreads();
+    if (u0 + TK < a.L) fetch(u0 + TK);
+    tile2(u0);
   }
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
@@ -352,8 +363,9 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_query_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- key side
-template <int WAVES, int TQ, int KB>
+template <int WAVES, int TQ, int KB, bool FULL>
 __global__ __launch_bounds__(64 * WAVES) void bwd_key_kernel(BwdArgs a) {
+  // FULL: every query tile is whole (T a multiple of TQ), so no query is masked
   // KB 16-key blocks a wave: every Q / G / Q^T / G^T operand read from LDS
   // serves all of them
   constexpr int TH = 64 * WAVES;
@@ -426,6 +438,45 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_key_kernel(BwdArgs a) {
       pd = a.dsum[si];
     }
   };
+  auto ktile = [&](int t0) {
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) {
+      bf16x4 pb[KB][2], dsb[KB][2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const int row = 32 * qs + 16 * qt + col;
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt_lds + row * 64 + 16 * g);
+        const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gt_lds + row * 64 + 16 * g);
+        const int q4 = 32 * qs + 16 * qt + 4 * g;  // this lane's four query rows
+        const f32x4 lq = *reinterpret_cast<const f32x4*>(st_lse + q4);
+        const f32x4 dq4 = *reinterpret_cast<const f32x4*>(st_d + q4);
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+          const f32x4 sc = mfma(qa, bk[b], f32x4{0.f, 0.f, 0.f, 0.f});
+          const f32x4 dp = mfma(ga, bv[b], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float p = __builtin_amdgcn_exp2f(fmaf(sc[i], kQs, -lq[i]));
+            if constexpr (!FULL)
+              if (t0 + q4 + i >= a.T) p = 0.f;
+            pb[b][qt][i] = (__bf16)p;
+            dsb[b][qt][i] = (__bf16)(p * (dp[i] - dq4[i]));
+          }
+        }
+      }
+      const int q0 = (32 * qs + 4 * g + r4) * 64 + 8 * c4, q1 = (32 * qs + 16 + 4 * g + r4) * 64 + 8 * c4;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const bf16x8 gta = cat(ld_tr(gt_lds + q0 + 32 * dt), ld_tr(gt_lds + q1 + 32 * dt));
+        const bf16x8 qta = cat(ld_tr(qt_lds + q0 + 32 * dt), ld_tr(qt_lds + q1 + 32 * dt));
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+          dvt[b][dt] = mfma(gta, cat(pb[b][0], pb[b][1]), dvt[b][dt]);
+          dkt[b][dt] = mfma(qta, cat(dsb[b][0], dsb[b][1]), dkt[b][dt]);
+        }
+      }
+    }
+  };
   if (ntiles > 0) fetch(0);
   for (int it = 0; it < ntiles; ++it) {
     const int t0 = (it % tiles_per_router) * TQ;
@@ -444,48 +495,17 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_key_kernel(BwdArgs a) {
     }
     __syncthreads();
     if (it + 1 < ntiles) fetch(it + 1);
-#pragma unroll
-    for (int qs = 0; qs < QS; ++qs) {
-      bf16x4 pb[KB][2], dsb[KB][2];
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const int row = 32 * qs + 16 * qt + col;
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt_lds + row * 64 + 16 * g);
-        const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gt_lds + row * 64 + 16 * g);
-        const int q4 = 32 * qs + 16 * qt + 4 * g;  // this lane's four query rows
-        const f32x4 lq = *reinterpret_cast<const f32x4*>(st_lse + q4);
-        const f32x4 dq4 = *reinterpret_cast<const f32x4*>(st_d + q4);
-#pragma unroll
-        for (int b = 0; b < KB; ++b) {
-          const f32x4 sc = mfma(qa, bk[b], f32x4{0.f, 0.f, 0.f, 0.f});
-          const f32x4 dp = mfma(ga, bv[b], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = t0 + q4 + i < a.T ? __builtin_amdgcn_exp2f(fmaf(sc[i], kQs, -lq[i])) : 0.f;
-            pb[b][qt][i] = (__bf16)p;
-            dsb[b][qt][i] = (__bf16)(p * (dp[i] - dq4[i]));
-          }
-        }
-      }
-      const int q0 = (32 * qs + 4 * g + r4) * 64 + 8 * c4, q1 = (32 * qs + 16 + 4 * g + r4) * 64 + 8 * c4;
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const bf16x8 gta = cat(ld_tr(gt_lds + q0 + 32 * dt), ld_tr(gt_lds + q1 + 32 * dt));
-        const bf16x8 qta = cat(ld_tr(qt_lds + q0 + 32 * dt), ld_tr(qt_lds + q1 + 32 * dt));
-#pragma unroll
-        for (int b = 0; b < KB; ++b) {
-          dvt[b][dt] = mfma(gta, cat(pb[b][0], pb[b][1]), dvt[b][dt]);
-          dkt[b][dt] = mfma(qta, cat(dsb[b][0], dsb[b][1]), dkt[b][dt]);
-        }
-      }
-    }
+    ktile(t0);
   }
-  // dV's LCE term, computed beforehand in fp32
+  // dV's LCE term, computed beforehand in fp32 ([N][C/8][H][W][8])
 #pragma unroll
   for (int b = 0; b < KB; ++b) {
-    const float* lp = a.dv_lce + img + (size_t)(ky[b] * a.W + kx[b]) * a.C + h * 32;
-    const f32x4 lv0 = *reinterpret_cast<const f32x4*>(lp + 4 * g);
-    const f32x4 lv1 = *reinterpret_cast<const f32x4*>(lp + 16 + 4 * g);
+    auto lce4 = [&](int ch) {  // channels ch .. ch+3 of the key pixel
+      return *reinterpret_cast<const f32x4*>(
+          a.dv_lce + ((((size_t)n * (a.C / 8) + ch / 8) * a.H + ky[b]) * a.W + kx[b]) * 8 + ch % 8);
+    };
+    const f32x4 lv0 = lce4(h * 32 + 4 * g);
+    const f32x4 lv1 = lce4(h * 32 + 16 + 4 * g);
     float k0[4], k1[4], v0[4], v1[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -500,19 +520,29 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_key_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- LCE terms
-// One workgroup per (image, block of kLceRows rows, block of 16 channels):
-// the V rows and the dout rows of the block and two more on each side
-// (columns -2 .. W+1, zero outside the image) are staged in LDS as 16-byte
-// pieces. Thread (channel c, column group xg) takes columns x = xg, xg + 16,
-// ...: it sums the 25 tap terms dout[y][x] * v[y+a-2][x+e-2] and the bias
-// term (the 16 column groups are then added in a fixed order into
-// part[block][c][26]) and writes dv's LCE term sum_{a,e} w[a][e] *
-// dout[y-a+2][x-e+2] (fp32, the key side adds it to the attention part).
-constexpr int kLceRows = 4;
-constexpr int kLceCh = 16;
+// One workgroup per (image, block of kLceRows rows, block of kLceCh
+// channels): the V rows and the dout rows of the block and two more on each
+// side are staged in LDS, one 16-byte piece a pixel, zero outside the image
+// (the staged rows run kLceRun columns past W + 4, also zero, so every run
+// reads inside them). Thread (channel c, group xg) walks (row, run of
+// kLceRun consecutive columns) items xg, xg + kLceXg, ..., its channel's 25
+// weights in registers; per
+// window row it reads the kLceRun + 4 values of the row once and applies all
+// five horizontal taps from registers. It sums the 25 tap terms dout[y][x] *
+// v[y+a-2][x+e-2] and the bias term (the column groups are then added in a
+// fixed order into part[block][c][26]) and writes dv's LCE term
+// sum_{a,e} w[a][e] * dout[y-a+2][x-e+2] (fp32, stored by channel block,
+// [N][C/8][H][W][8], so a block's writes are whole rows; the key side adds it
+// to the attention part).
+constexpr int kLceRows = 8;               // output rows of a block
+constexpr int kLceCh = 8;                 // channels of a block: one 16-byte piece a pixel
+constexpr int kLceXg = 256 / kLceCh;      // column groups
+constexpr int kLceRun = 4;                // consecutive columns a thread takes at once
+constexpr int kLceBatch = 8;              // staging pieces of each tensor a thread has in flight
+__host__ __device__ inline int lce_pitch(int W) { return W + 4 + kLceRun; }
 __host__ __device__ inline size_t lce_grad_lds(int W) {
-  const size_t stage = (size_t)2 * (kLceRows + 4) * (W + 4) * kLceCh * 2 + (size_t)25 * kLceCh * sizeof(float);
-  const size_t red = (size_t)16 * kLceCh * 26 * sizeof(float) + (size_t)25 * kLceCh * sizeof(float);
+  const size_t stage = (size_t)2 * (kLceRows + 4) * lce_pitch(W) * kLceCh * 2;
+  const size_t red = (size_t)kLceXg * kLceCh * 26 * sizeof(float);
   return stage > red ? stage : red;
 }
 
@@ -528,36 +558,32 @@ __global__ __launch_bounds__(256) void lce_grad_rows_kernel(const uint16_t* __re
   u /= CB;
   const int yb = u % YB, n = u / YB;
   const int y0 = yb * kLceRows, tid = threadIdx.x;
-  const int WB = W + 4, RB = kLceRows + 4;
-  float* wsm = reinterpret_cast<float*>(sm);                        // [25][16] weights of the block's channels
-  uint16_t* vs = reinterpret_cast<uint16_t*>(sm + 25 * kLceCh * 4);  // [RB][W+4][16]
-  uint16_t* gs = vs + (size_t)RB * WB * kLceCh;                      // [RB][W+4][16]
+  const int WP = lce_pitch(W), RB = kLceRows + 4;
+  uint16_t* vs = reinterpret_cast<uint16_t*>(sm);   // [RB][WP][kLceCh], column x at x + 2
+  uint16_t* gs = vs + (size_t)RB * WP * kLceCh;     // [RB][WP][kLceCh]
   const size_t img = (size_t)n * H * W * C;
   const uint32_t img_bytes = (uint32_t)((size_t)H * W * C * 2);
   const Rsrc vr = rsrc(v + img, img_bytes), gr = rsrc(g + img, img_bytes);
   const uint32_t cofs = (uint32_t)cb * kLceCh * 2;
-  for (int e = tid; e < 25 * kLceCh; e += 256) {
-    const int tap = e / kLceCh, c = e - tap * kLceCh;
-    wsm[e] = bf16_bits_to_float(lw[(size_t)(cb * kLceCh + c) * 25 + tap]);
-  }
-  // staging: two 16-byte pieces (8 channels each) per pixel, rows y0-2 .. y0+RB-3
-  // (four pieces of each a thread in flight before any is stored)
-  const int pieces = RB * WB * 2;
-  constexpr int kBatch = 4;
-  for (int e0 = tid; e0 < pieces; e0 += 256 * kBatch) {
-    uint4 vx[kBatch], gx[kBatch];
+  const int c = tid % kLceCh, xg = tid / kLceCh;
+  float wr[25];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int e = e0 + 256 * i, pix = e >> 1, half = e & 1, ry = pix / WB, rx = pix - ry * WB;
+  for (int tap = 0; tap < 25; ++tap) wr[tap] = bf16_bits_to_float(lw[(size_t)(cb * kLceCh + c) * 25 + tap]);
+  // staging: kLceBatch pieces of each tensor a thread in flight before any is stored
+  const int pieces = RB * WP;
+  for (int e0 = tid; e0 < pieces; e0 += 256 * kLceBatch) {
+    uint4 vx[kLceBatch], gx[kLceBatch];
+#pragma unroll
+    for (int i = 0; i < kLceBatch; ++i) {
+      const int e = e0 + 256 * i, ry = e / WP, rx = e - ry * WP;
       const int y = y0 + ry - 2, x = rx - 2;
-      const uint32_t off = e < pieces && y >= 0 && y < H && x >= 0 && x < W
-                               ? (uint32_t)((y * W + x) * C * 2) + cofs + 16 * half
-                               : kOut;
+      const uint32_t off =
+          e < pieces && y >= 0 && y < H && x >= 0 && x < W ? (uint32_t)((y * W + x) * C * 2) + cofs : kOut;
       vx[i] = ld16(vr, off);
       gx[i] = ld16(gr, off);
     }
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
+    for (int i = 0; i < kLceBatch; ++i) {
       const int e = e0 + 256 * i;
       if (e < pieces) {
         reinterpret_cast<uint4*>(vs)[e] = vx[i];
@@ -566,37 +592,53 @@ __global__ __launch_bounds__(256) void lce_grad_rows_kernel(const uint16_t* __re
     }
   }
   __syncthreads();
-  const int c = tid & 15, xg = tid >> 4;
+  auto V = [&](int row, int col) { return bf16_bits_to_float(vs[((size_t)row * WP + col) * kLceCh + c]); };
+  auto G = [&](int row, int col) { return bf16_bits_to_float(gs[((size_t)row * WP + col) * kLceCh + c]); };
   float acc[26];
 #pragma unroll
   for (int i = 0; i < 26; ++i) acc[i] = 0.f;
-  for (int ry = 0; ry < kLceRows; ++ry) {
-    const int y = y0 + ry;
-    for (int x = xg; x < W; x += 16) {
-      const float gv = bf16_bits_to_float(gs[((size_t)(ry + 2) * WB + x + 2) * kLceCh + c]);
-      acc[25] += gv;
-      float dl = 0.f;
+  const int runs = (W + kLceRun - 1) / kLceRun;  // runs of a row
+  for (int item = xg; item < kLceRows * runs; item += kLceXg) {  // (row, run) items over the column groups
+    const int ry = item / runs, x0 = (item - ry * runs) * kLceRun, y = y0 + ry;
+    {
+      float gv[kLceRun], dl[kLceRun];
 #pragma unroll
-      for (int ta = 0; ta < 5; ++ta)
+      for (int j = 0; j < kLceRun; ++j) {
+        gv[j] = x0 + j < W ? G(ry + 2, x0 + j + 2) : 0.f;  // dout[y][x0+j] (zero past W)
+        dl[j] = 0.f;
+        acc[25] += gv[j];
+      }
 #pragma unroll
-        for (int te = 0; te < 5; ++te) {
-          acc[5 * ta + te] = fmaf(gv, bf16_bits_to_float(vs[((size_t)(ry + ta) * WB + x + te) * kLceCh + c]),
-                                  acc[5 * ta + te]);
-          // v[y][x] feeds output (y + 2 - ta, x + 2 - te) through tap (ta, te)
-          dl = fmaf(wsm[(5 * ta + te) * kLceCh + c],
-                    bf16_bits_to_float(gs[((size_t)(ry + 4 - ta) * WB + x + 4 - te) * kLceCh + c]), dl);
+      for (int ta = 0; ta < 5; ++ta) {
+        float vw[kLceRun + 4], gw[kLceRun + 4];
+#pragma unroll
+        for (int j = 0; j < kLceRun + 4; ++j) {
+          vw[j] = V(ry + ta, x0 + j);       // v[y+ta-2][x0+j-2]
+          gw[j] = G(ry + 4 - ta, x0 + j);   // dout[y+2-ta][x0+j-2]
         }
-      if (y < H) dv_lce[img + ((size_t)y * W + x) * C + cb * kLceCh + c] = dl;
+#pragma unroll
+        for (int te = 0; te < 5; ++te)
+#pragma unroll
+          for (int j = 0; j < kLceRun; ++j) {
+            acc[5 * ta + te] = fmaf(gv[j], vw[j + te], acc[5 * ta + te]);
+            // v[y][x] feeds output (y + 2 - ta, x + 2 - te) through tap (ta, te)
+            dl[j] = fmaf(wr[5 * ta + te], gw[j + 4 - te], dl[j]);
+          }
+      }
+      if (y < H)
+#pragma unroll
+        for (int j = 0; j < kLceRun; ++j)
+          if (x0 + j < W) dv_lce[((((size_t)n * CB + cb) * H + y) * W + x0 + j) * kLceCh + c] = dl[j];
     }
   }
   __syncthreads();  // the staging area becomes the reduction area
-  float* red = reinterpret_cast<float*>(sm + 25 * kLceCh * 4);  // [16 xg][16 c][26]
+  float* red = reinterpret_cast<float*>(sm);  // [kLceXg][kLceCh][26]
 #pragma unroll
   for (int i = 0; i < 26; ++i) red[((size_t)xg * kLceCh + c) * 26 + i] = acc[i];
   __syncthreads();
   for (int e = tid; e < kLceCh * 26; e += 256) {
     float sum = 0.f;
-    for (int j = 0; j < 16; ++j) sum += red[(size_t)j * kLceCh * 26 + e];
+    for (int j = 0; j < kLceXg; ++j) sum += red[(size_t)j * kLceCh * 26 + e];
     part[((size_t)(n * YB + yb) * C + cb * kLceCh) * 26 + e] = sum;
   }
 }
@@ -621,10 +663,16 @@ __global__ __launch_bounds__(256) void lce_grad_sum_kernel(const float* __restri
 template <int WAVES, int TK, int TQ, int BPW>
 hipError_t launch_sides(const BwdArgs& a, hipStream_t st) {
   const unsigned units = (unsigned)(a.N * a.R * a.heads * (a.T / 16 / (WAVES * BPW)));
-  launch(bwd_query_kernel<WAVES, TK, BPW>, dim3(units), dim3(64 * WAVES), 0, st, a);
+  if (a.L % TK == 0)
+    launch(bwd_query_kernel<WAVES, TK, BPW, true>, dim3(units), dim3(64 * WAVES), 0, st, a);
+  else
+    launch(bwd_query_kernel<WAVES, TK, BPW, false>, dim3(units), dim3(64 * WAVES), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  launch(bwd_key_kernel<WAVES, TQ, BPW>, dim3(units), dim3(64 * WAVES), 0, st, a);
+  if (a.T % TQ == 0)
+    launch(bwd_key_kernel<WAVES, TQ, BPW, true>, dim3(units), dim3(64 * WAVES), 0, st, a);
+  else
+    launch(bwd_key_kernel<WAVES, TQ, BPW, false>, dim3(units), dim3(64 * WAVES), 0, st, a);
   return hipGetLastError();
 }
 
