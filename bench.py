@@ -37,7 +37,8 @@ The router-free last stage (s4: 128 images of 7x7 tokens, C = 512, 16 heads)
 is measured in per_config as its own workload: a step is one
 bra_attention_dense call. `--config s4` makes it the headline. The per-head
 routing variant on the c4 shape (c4h: one bra_forward_head_routed call a
-step) is measured there too.
+step) and the backward for given routes on the c4 and c1 shapes (c4b, c1b:
+one bra_backward call a step) are measured there too.
 """
 from __future__ import annotations
 
@@ -78,6 +79,10 @@ def algorithmic(cfg):
         "pool": {"bytes": 2 * E * b + means},
         "route": {"bytes": means + routes, "flops": 2 * cfg.N * cfg.R * cfg.R * cfg.C},
         "attn": {"bytes": 4 * E * b + routes + lce_params, "flops": 4 * E * cfg.L + 50 * E},
+        # backward for given routes: reads q, k, v, dout, writes dq, dk, dv; the
+        # five products S (recomputed), dP, dV, dQ, dK, and the LCE's two
+        "attn_bwd": {"bytes": 7 * E * b + routes + lce_params + cfg.C * 26 * 4,
+                     "flops": 10 * E * cfg.L + 100 * E},
         # the block's two projections, averaged per launch: qkv reads x and
         # writes q, k, v; wo reads o and writes y (weights and biases once)
         "linear": {"bytes": (4 * E + 4 * cfg.C * (cfg.C + 1) + 2 * E) * b / 2,
@@ -85,10 +90,13 @@ def algorithmic(cfg):
     }
 
 
-def roofline_for(kind, cfg, ms_per_launch, traffic, share=1.0):
+def roofline_for(kind, cfg, ms_per_launch, traffic, share=1.0, backward=False):
     """share: the fraction of the workload one launch processes (1/heads
-    for the per-head routing variant, which launches each kernel per head)."""
-    alg = {k: v * share for k, v in algorithmic(cfg)[kind].items()}
+    for the per-head routing variant, which launches each kernel per head).
+    backward: the attention kind is the backward's kernels (one bra_backward
+    call, priced by its own algorithmic work)."""
+    akind = "attn_bwd" if backward and kind == "attn" else kind
+    alg = {k: v * share for k, v in algorithmic(cfg)[akind].items()}
     t = ms_per_launch * 1e-3
     if kind == "linear" and cfg.dtype == "bf16":
         ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -98,7 +106,7 @@ def roofline_for(kind, cfg, ms_per_launch, traffic, share=1.0):
                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                     "traffic": traffic, "kernel": kind}
     if kind == "attn":
-        mfma_flops = 4 * cfg.N * cfg.H * cfg.W * cfg.C * cfg.L * share
+        mfma_flops = (10 if backward else 4) * cfg.N * cfg.H * cfg.W * cfg.C * cfg.L * share
         if cfg.dtype == "bf16":
             ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
             if mfma_flops / alg["bytes"] > ridge:
@@ -211,7 +219,7 @@ class Workload:
         import numpy as np
         import torch
 
-        from synth import CONFIGS, draw_block, draw_config
+        from synth import CONFIGS, draw, draw_block, draw_config
         from vision_transformer_sparse_amd import bra
 
         self.cfg = cfg
@@ -243,6 +251,14 @@ class Workload:
         elif op == "dense":
             def step():
                 bra.attention_dense(t["q"], t["k"], t["v"], t["lce_w"], t["lce_b"], cfg.heads, out=out)
+        elif op == "backward":
+            g = torch.from_numpy(draw(cfg.N, cfg.H, cfg.W, cfg.C, cfg.S, cfg.dtype, 3000 + CONFIGS.index(cfg))["q"]
+                                 .astype(np.float32)).to(dev, tdt)
+            bra.forward(t["q"], t["k"], t["v"], t["lce_w"], t["lce_b"], cfg.heads, cfg.S, cfg.topk,
+                        out=out, route_idx=route)
+
+            def step():
+                bra.backward(t["q"], t["k"], t["v"], t["lce_w"], route, g, cfg.heads, cfg.S)
         elif op == "head_routed":
             def step():
                 bra.forward_head_routed(t["q"], t["k"], t["v"], t["lce_w"], t["lce_b"], cfg.heads, cfg.S,
@@ -254,12 +270,12 @@ class Workload:
         self.step = step
 
 
-def kernel_rooflines(prof, cfg, share=1.0):
+def kernel_rooflines(prof, cfg, share=1.0, backward=False):
     kernels = {}
     for kind, (ms, cnt) in prof.items():
         if cnt:
             us = ms * 1e3 / cnt
-            r = roofline_for(kind, cfg, us * 1e-3, None, share)
+            r = roofline_for(kind, cfg, us * 1e-3, None, share, backward)
             kernels[kind] = {"us_per_launch": round(us, 3), "launches": cnt, "bound": r["bound"],
                              "achieved": round(r["achieved"], 2), "unit": r["unit"],
                              "frac": round(r["frac"], 4)}
@@ -274,6 +290,7 @@ def measure_config(w, flush, n_warm, n_cold):
 
     cfg = w.cfg
     share = 1.0 / cfg.heads if w.op == "head_routed" else 1.0
+    bwd = w.op == "backward"
     for _ in range(n_warm // 2):
         w.step()
     torch.cuda.synchronize()
@@ -285,7 +302,7 @@ def measure_config(w, flush, n_warm, n_cold):
     bra.profile_begin(bra.KERNEL_NAMES)
     for _ in range(max(20, n_warm // 4)):
         w.step()
-    kernels = kernel_rooflines(bra.profile_read(), cfg, share)
+    kernels = kernel_rooflines(bra.profile_read(), cfg, share, bwd)
     bra.profile_begin(())
     # cold: a 1 GiB write before each step; events around the step (torch's
     # current stream, which the binding hands to the library) and around the
@@ -310,7 +327,7 @@ def measure_config(w, flush, n_warm, n_cold):
             "queries_per_s": cfg.queries / (pctl(cold_us, 50) * 1e-6)}
     if attn_us:
         med = pctl(attn_us, 50)
-        r = roofline_for("attn", cfg, med * 1e-3, None, share)
+        r = roofline_for("attn", cfg, med * 1e-3, None, share, bwd)
         cold.update(attn_us_median=round(med, 3), attn_us_p10=round(pctl(attn_us, 10), 3),
                     attn_us_p90=round(pctl(attn_us, 90), 3), attn_frac=round(r["frac"], 4))
     return {"ms_per_step": round(warm_ms, 5), "queries_per_s": cfg.queries / (warm_ms * 1e-3),
@@ -361,11 +378,15 @@ def main(argv=None) -> int:
         runs = [(c.name, c, a.op) for c in workloads]
         if a.op == "forward":
             runs.append(("c4h", by_name["c4"], "head_routed"))
+            runs.append(("c4b", by_name["c4"], "backward"))
+            runs.append(("c1b", by_name["c1"], "backward"))
         for name, c, op in runs:
             w = Workload(c, op, dev)
             per_config[name] = measure_config(w, flush, n_warm=1000, n_cold=a.cold)
             if op == "head_routed":
                 per_config[name]["op"] = "bra_forward_head_routed (every head routed on its own channels)"
+            if op == "backward":
+                per_config[name]["op"] = "bra_backward (gradients for the forward's routes)"
             print(f"[bench] per_config {name}: {per_config[name]['ms_per_step'] * 1e3:.2f} us/step warm, "
                   f"{per_config[name]['cold']['step_us_median']:.2f} us cold", file=sys.stderr, flush=True)
             if c is cfg and op == a.op:

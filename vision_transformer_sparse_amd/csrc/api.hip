@@ -115,14 +115,18 @@ int g_prof_mask = 0;  // bit k: record events around kernels of kind k
 thread_local bool g_no_prof = false;
 KindRecord g_prof[BRA_K_COUNT];
 
-// Arms the event pair of one record slot for the next kernel this thread
-// launches (bra::launch stamps them with that dispatch's start and end). If
+// A timed region of one kernel kind. By default it arms the event pair of one
+// record slot for the next kernel this thread launches (bra::launch stamps
+// them with that dispatch's start and end through hipExtLaunchKernelGGL); if
 // no kernel took them, both are recorded on the stream when the scope ends.
+// With span = true (entry points made of several launches) the events are
+// recorded on the stream before the first and after the last launch instead.
 struct ProfScope {
   int kind;
   hipStream_t st;
   int slot = -1;
-  ProfScope(int kind_, hipStream_t st_) : kind(kind_), st(st_) {
+  bool span = false;
+  ProfScope(int kind_, hipStream_t st_, bool span_ = false) : kind(kind_), st(st_), span(span_) {
     if (g_no_prof || !(g_prof_mask & (1 << kind))) return;
     std::lock_guard<std::mutex> lk(g_prof_mutex);
     KindRecord& rec = g_prof[kind];
@@ -139,12 +143,21 @@ struct ProfScope {
       rec.stop.push_back(b);
     }
     slot = rec.used++;
+    if (span) {
+      hipEventRecord(rec.start[slot], st);
+      return;
+    }
     bra::ProfEvents& pe = bra::prof_events();
     pe.start = rec.start[slot];
     pe.stop = rec.stop[slot];
   }
   ~ProfScope() {
     if (slot < 0) return;
+    if (span) {
+      std::lock_guard<std::mutex> lk(g_prof_mutex);
+      hipEventRecord(g_prof[kind].stop[slot], st);
+      return;
+    }
     bra::ProfEvents& pe = bra::prof_events();
     if (pe.start) {
       hipEventRecord(pe.start, st);
@@ -513,7 +526,7 @@ int bra_backward(const void* q, const void* k, const void* v, const void* lce_w,
   if (rc) return rc;
   hipError_t e;
   {
-    ProfScope ps(BRA_K_ATTN, st);
+    ProfScope ps(BRA_K_ATTN, st, true);  // five launches, timed as one span
     e = bra::launch_backward(q, k, v, lce_w, route_idx, dout, s, dq, dk, dv, dlce_w, dlce_b, ws, st);
   }
   return e == hipSuccess ? BRA_OK : hip_fail(e);
