@@ -37,11 +37,12 @@
 // that a lane's eight scores are eight CONSECUTIVE keys: P^T needs no
 // shuffle.
 //
-// Softmax with a fixed maximum per query. Every scaled score is at most
-// qscale * |q| * max |k| over the routed keys (Cauchy-Schwarz); the pool
-// kernel reports max |k|^2 per (image, region, head), so a query's bound m
-// is known before its first key, and P = 2^(s*qscale - m) <= 1 needs no
-// running maximum, no rescaling and no per-tile check: per score one fma,
+// Softmax with a fixed maximum per query. The query operand is scaled
+// first, q' = bf16(qscale * q), and every score q'.k is at most |q'| *
+// max |k| over the routed keys (Cauchy-Schwarz); the pool kernel reports
+// max |k|^2 per (image, region, head), so a query's bound m is known before
+// its first key. The score products start from -m, and P = 2^(s - m) <= 1
+// needs no running maximum, no rescaling and no per-tile check: per score
 // one v_exp_f32 and half a packed bf16 conversion. P is rounded to bf16 for
 // the products and the row sums are taken over that same bf16 P on the
 // matrix cores. The bound can sit far above the true maximum (a query
@@ -308,14 +309,23 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void attn_tile_kernel(TileArgs 
     const uint4 w = *reinterpret_cast<const uint4*>(a.wpk + (size_t)row * C + h * 32 + piece * 4);
     *reinterpret_cast<uint4*>(wts + row * 32 + piece * 4) = w;
   }
-  // the softmax's fixed maximum of the lane's query (scaled, base 2):
-  // qscale * |q| * max |k| (replaced by the exact maximum on the exact way)
+  // The query enters the products already scaled, q' = bf16(qscale * q),
+  // as the walk-through's BRA code scales it before the product: a score is
+  // then q'.k in base-2 units. The softmax's fixed maximum of the lane's
+  // query is |q'| * max |k| (replaced by the exact maximum on the exact
+  // way), and it is the score accumulators' starting value (-m), so the
+  // products give s - m and P = 2^(s - m) takes no arithmetic before the
+  // exponential.
+#pragma unroll
+  for (int i = 0; i < QBW; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bq[i][e] = (__bf16)((float)bq[i][e] * a.qscale);
   float m[QBW];
   {
     const float kmax = __builtin_sqrtf(k2);
 #pragma unroll
     for (int i = 0; i < QBW; ++i)
-      m[i] = bounded ? a.qscale * __builtin_sqrtf(group_sum(sq8(__builtin_bit_cast(uint4, bq[i])))) * kmax : 0.f;
+      m[i] = bounded ? __builtin_sqrtf(group_sum(sq8(__builtin_bit_cast(uint4, bq[i])))) * kmax : 0.f;
   }
 
   f32x4 o0[QBW], o1[QBW], ls[QBW];
@@ -394,16 +404,16 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void attn_tile_kernel(TileArgs 
       } else {
 #pragma unroll
         for (int i = 0; i < QBW; ++i) {
-          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          const f32x4 mi = {-m[i], -m[i], -m[i], -m[i]};  // the lane's four scores are of one query
           f32x4 s[4];
 #pragma unroll
-          for (int x = 0; x < 4; ++x) s[x] = mfma(ka[x], bq[i], z);
+          for (int x = 0; x < 4; ++x) s[x] = mfma(ka[x], bq[i], mi);
           bf16x4 pb[4];
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
             f32x4 pv;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(s[x][e], a.qscale, -m[i]));
+            for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(s[x][e]);
             pb[x] = to_bf16x4(pv);
           }
 #pragma unroll
@@ -434,7 +444,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void attn_tile_kernel(TileArgs 
   if (exact) {
     pass(MaxTag{});
 #pragma unroll
-    for (int i = 0; i < QBW; ++i) m[i] = group_max(smax[i]) * a.qscale;
+    for (int i = 0; i < QBW; ++i) m[i] = group_max(smax[i]);
     pass(SoftTag{});
   }
   __syncthreads();  // every wave is done with the tile buffers: the halo goes there
