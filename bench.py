@@ -184,6 +184,12 @@ def cpu_baseline(inp, cfg, budget_s: float, op: str = "forward"):
                 oracle.bra_block_forward(inp["x"], inp["wqkv"], inp["bqkv"], inp["lce_w"],
                                          inp["lce_b"], inp["wo"], inp["bo"], cfg.heads, cfg.S,
                                          cfg.topk)
+            elif op == "backward":
+                oracle.bra_backward(inp["q"], inp["k"], inp["v"], inp["lce_w"], inp["route"],
+                                    inp["g"], cfg.heads, cfg.S)
+            elif op == "head_routed":
+                oracle.bra_forward_head_routed(inp["q"], inp["k"], inp["v"], inp["lce_w"], inp["lce_b"],
+                                               cfg.heads, cfg.S, cfg.topk)
             elif op == "dense":
                 oracle.dense_attention(inp["q"], inp["k"], inp["v"], inp["lce_w"], inp["lce_b"],
                                        cfg.heads)
@@ -252,10 +258,12 @@ class Workload:
             def step():
                 bra.attention_dense(t["q"], t["k"], t["v"], t["lce_w"], t["lce_b"], cfg.heads, out=out)
         elif op == "backward":
-            g = torch.from_numpy(draw(cfg.N, cfg.H, cfg.W, cfg.C, cfg.S, cfg.dtype, 3000 + CONFIGS.index(cfg))["q"]
-                                 .astype(np.float32)).to(dev, tdt)
+            g_np = draw(cfg.N, cfg.H, cfg.W, cfg.C, cfg.S, cfg.dtype, 3000 + CONFIGS.index(cfg))["q"]
+            g = torch.from_numpy(g_np.astype(np.float32)).to(dev, tdt)
             bra.forward(t["q"], t["k"], t["v"], t["lce_w"], t["lce_b"], cfg.heads, cfg.S, cfg.topk,
                         out=out, route_idx=route)
+            # the CPU baseline differentiates for the same routes and dout
+            self.inputs = dict(inputs, route=route.cpu().numpy(), g=g_np)
 
             def step():
                 bra.backward(t["q"], t["k"], t["v"], t["lce_w"], route, g, cfg.heads, cfg.S)
@@ -340,8 +348,10 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--config", default="c4", help="headline workload (c0..c4, or s4)")
-    ap.add_argument("--op", choices=("forward", "block"), default="forward",
-                    help="forward: bra_forward alone; block: qkv projection, bra_forward, wo")
+    ap.add_argument("--op", choices=("forward", "block", "backward", "head_routed"), default="forward",
+                    help="forward: bra_forward alone; block: qkv projection, bra_forward, wo; "
+                         "backward: bra_backward for the forward's routes; head_routed: "
+                         "bra_forward_head_routed")
     ap.add_argument("--per-config", choices=("all", "none"), default="all",
                     help="all: measure every workload first (per_config); none: the headline only")
     ap.add_argument("--cold", type=int, default=100, help="cold calls per workload in per_config")
@@ -362,6 +372,10 @@ def main(argv=None) -> int:
     from vision_transformer_sparse_amd import bra
 
     workloads = CONFIGS + [STAGE4] if a.op == "forward" else CONFIGS
+    if a.op in ("backward", "head_routed") and a.per_config == "all":
+        print(f"--op {a.op} is measured with --per-config none (per_config already holds it)",
+              file=sys.stderr)
+        return 2
     by_name = {c.name: c for c in workloads}
     cfg = by_name[a.config]
     bra.load()
@@ -425,7 +439,9 @@ def main(argv=None) -> int:
     bra.profile_begin(bra.KERNEL_NAMES)
     for _ in range(max(10, a.steps // 4)):
         step()
-    kernels = kernel_rooflines(bra.profile_read(), cfg)
+    share = 1.0 / cfg.heads if head.op == "head_routed" else 1.0
+    bwd = head.op == "backward"
+    kernels = kernel_rooflines(bra.profile_read(), cfg, share, bwd)
     bra.profile_begin(())
 
     if a.calib_copy_mb > 0:
@@ -439,7 +455,8 @@ def main(argv=None) -> int:
     ms_step = elapsed * 1e3 / a.steps
     attn_ms, attn_cnt = prof_timed["attn"]
     attn_ms_per_launch = attn_ms / attn_cnt
-    roof = roofline_for("attn", cfg, attn_ms_per_launch, measured_traffic(cfg.name))
+    traffic = measured_traffic(cfg.name) if head.op in ("forward", "dense") else None
+    roof = roofline_for("attn", cfg, attn_ms_per_launch, traffic, share, bwd)
     roof["us_per_launch"] = attn_ms_per_launch * 1e3
     roof["launches"] = attn_cnt
 
@@ -460,7 +477,9 @@ def main(argv=None) -> int:
         "data": "synthetic (seeded N(0,1) q/k/v; see synth/)",
         "config": {"workload": f"{cfg.name}: {cfg.what}"
                                + (" -- block: qkv Linear, BRA, wo Linear" if a.op == "block" else "")
-                               + (" -- bra_attention_dense" if head.op == "dense" else ""),
+                               + (" -- bra_attention_dense" if head.op == "dense" else "")
+                               + (" -- bra_backward for given routes" if bwd else "")
+                               + (" -- bra_forward_head_routed" if head.op == "head_routed" else ""),
                    "N": cfg.N, "H": cfg.H, "W": cfg.W,
                    "C": cfg.C, "heads": cfg.heads, "S": cfg.S, "topk": cfg.topk,
                    "queries_per_step": cfg.queries, "parallelism": "single GPU"},

@@ -15,22 +15,27 @@
 //  * inv_route_kernel: per (image, region), the regions that route to it, in
 //    ascending order, so the key side gathers instead of scattering and
 //    every gradient is a fixed-order sum (no atomics).
-//  * bwd_query_kernel: one workgroup per (image, region, head, up to 64
-//    queries), a wave per 16 queries; 32-key tiles of the gathered K and V
-//    staged in LDS and shared by the waves. Pass 1 is the forward with an
-//    online maximum (S^T = K Q^T, O^T = V^T P^T on 16x16x32 bf16 products)
-//    and leaves per query the base-2 log-sum-exp and D = G . O; pass 2
-//    recomputes P and forms dP^T = V G^T, dS^T, and dQ^T += K^T dS^T (K^T by
-//    transposing LDS reads, dS^T from the lane's own eight keys, the same
-//    key order on both operands).
-//  * bwd_key_kernel: one workgroup per (image, region, head, up to 64 keys),
-//    a wave per 16 keys; for every router region, 32-query tiles of Q and G
-//    (and their log-sum-exp and D) staged in LDS: S = Q K^T and dP = G V^T
-//    with lane = key, P and dS from the saved statistics, dV^T += G^T P and
-//    dK^T += Q^T dS (Q^T, G^T by transposing LDS reads); then the LCE term of
-//    dV from the key's 5x5 window of dout.
-//  * lce_grad_rows_kernel / lce_grad_sum_kernel: per image row and channel
-//    the 25 tap sums and the bias sum, then a fixed-order sum over rows.
+//  * bwd_query_kernel: one workgroup per (image, region, head, group of
+//    query blocks), a wave per one or two 16-query blocks (the whole 256-token
+//    region in one workgroup of 8 waves where the region allows it); tiles of
+//    64 or 128 gathered keys (K and V) staged in LDS through registers, one
+//    tile ahead, and shared by the waves. Pass 1 is the forward with an
+//    online maximum (S^T = K Q^T, O^T = V^T P^T on 16x16x32 bf16 products,
+//    row sums on the matrix cores) and leaves per query the base-2
+//    log-sum-exp and D = G . O; pass 2 recomputes P and forms dP^T = V G^T,
+//    dS^T, and dQ^T += K^T dS^T (K^T by transposing LDS reads, dS^T from the
+//    lane's own eight keys, the same key order on both operands).
+//  * bwd_key_kernel: the same decomposition over key blocks; for every
+//    router region, tiles of its queries' Q and G (and their log-sum-exp and
+//    D) staged in LDS: S = Q K^T and dP = G V^T with lane = key, P and dS
+//    from the saved statistics, dV^T += G^T P and dK^T += Q^T dS (Q^T, G^T
+//    by transposing LDS reads); then it adds dV's LCE term.
+//    Whether the last tile can be partial is a template parameter, so whole
+//    tiles run without masks.
+//  * lce_grad_rows_kernel / lce_grad_sum_kernel: per block of image rows and
+//    of 8 channels, the 25 tap sums, the bias sum and dV's LCE term (dout
+//    correlated with the flipped 5x5 kernel); then a fixed-order sum of the
+//    tap and bias sums over the row blocks.
 #include "bra_internal.h"
 
 namespace bra {
