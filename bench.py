@@ -30,15 +30,18 @@ One JSON line is printed. It carries:
              launch and fraction of the roofline that bounds it
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the headline
              workload (about 10 s of CPU work), threads and CPU model stated
---op block times the block around the operator instead: the qkv projection
-(Linear C -> 3C, bra_linear), bra_forward, and the output projection (Linear
-C -> C); "kernels" then also holds the projection kernel's roofline.
-The router-free last stage (s4: 128 images of 7x7 tokens, C = 512, 16 heads)
-is measured in per_config as its own workload: a step is one
+--op block times the block around the operator instead, one
+bra_block_forward call a step: the qkv projection (Linear C -> 3C), the
+operator and the output projection (Linear C -> C), fused on the shapes
+bra_block_fused reports (there "linear" is the qkv projection with the
+region pooling and "attn" the attention with the output projection);
+"kernels" then also holds the projection kernel's roofline. The router-free last stage (s4: 128 images of 7x7 tokens, C = 512,
+16 heads) is measured in per_config as its own workload: a step is one
 bra_attention_dense call. `--config s4` makes it the headline. The per-head
 routing variant on the c4 shape (c4h: one bra_forward_head_routed call a
-step) and the backward for given routes on the c4 and c1 shapes (c4b, c1b:
-one bra_backward call a step) are measured there too.
+step), the backward for given routes on the c4 and c1 shapes (c4b, c1b: one
+bra_backward call a step) and the block on the c4 and c1 shapes (c4blk,
+c1blk) are measured there too.
 """
 from __future__ import annotations
 
@@ -87,15 +90,28 @@ def algorithmic(cfg):
         # writes q, k, v; wo reads o and writes y (weights and biases once)
         "linear": {"bytes": (4 * E + 4 * cfg.C * (cfg.C + 1) + 2 * E) * b / 2,
                    "flops": 2 * E * 4 * cfg.C / 2},
+        # the fused block: the qkv projection that also writes the region
+        # means and key norms; the attention that applies wo before it stores
+        # (reads q, k, v, writes y)
+        "linear_qkv": {"bytes": 4 * E * b + 3 * cfg.C * (cfg.C + 1) * b + means
+                       + cfg.N * cfg.R * (cfg.C // 32) * 4,
+                       "flops": 2 * E * 3 * cfg.C},
+        "attn_block": {"bytes": 4 * E * b + routes + lce_params + cfg.C * (cfg.C + 1) * b,
+                       "flops": 4 * E * cfg.L + 50 * E + 2 * E * cfg.C},
     }
 
 
-def roofline_for(kind, cfg, ms_per_launch, traffic, share=1.0, backward=False):
+def roofline_for(kind, cfg, ms_per_launch, traffic, share=1.0, backward=False, fused_block=False):
     """share: the fraction of the workload one launch processes (1/heads
     for the per-head routing variant, which launches each kernel per head).
     backward: the attention kind is the backward's kernels (one bra_backward
-    call, priced by its own algorithmic work)."""
-    akind = "attn_bwd" if backward and kind == "attn" else kind
+    call, priced by its own algorithmic work). fused_block: the kinds are
+    the fused block's kernels (qkv + pooling, routing, attention + wo)."""
+    akind = kind
+    if backward and kind == "attn":
+        akind = "attn_bwd"
+    elif fused_block:
+        akind = {"attn": "attn_block", "linear": "linear_qkv"}.get(kind, kind)
     alg = {k: v * share for k, v in algorithmic(cfg)[akind].items()}
     t = ms_per_launch * 1e-3
     if kind == "linear" and cfg.dtype == "bf16":
@@ -106,7 +122,8 @@ def roofline_for(kind, cfg, ms_per_launch, traffic, share=1.0, backward=False):
                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                     "traffic": traffic, "kernel": kind}
     if kind == "attn":
-        mfma_flops = (10 if backward else 4) * cfg.N * cfg.H * cfg.W * cfg.C * cfg.L * share
+        E = cfg.N * cfg.H * cfg.W * cfg.C
+        mfma_flops = (10 if backward else 4) * E * cfg.L * share + (2 * E * cfg.C if fused_block else 0)
         if cfg.dtype == "bf16":
             ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
             if mfma_flops / alg["bytes"] > ridge:
@@ -245,15 +262,12 @@ class Workload:
         out = torch.empty(shape, dtype=tdt, device=dev)
         route = torch.empty((cfg.N, cfg.heads, cfg.R, cfg.topk) if op == "head_routed" else (cfg.N, cfg.R, cfg.topk),
                             dtype=torch.int32, device=dev)
+        self.fused = op == "block" and bra.block_fused(cfg.N, cfg.H, cfg.W, cfg.C, cfg.heads, cfg.S,
+                                                       cfg.topk, tdt)
         if op == "block":
-            qkv = [torch.empty(shape, dtype=tdt, device=dev) for _ in range(3)]
-            y = torch.empty(shape, dtype=tdt, device=dev)
-
             def step():
-                bra.linear(t["x"], t["wqkv"], t["bqkv"], split=cfg.C, outs=qkv)
-                bra.forward(*qkv, t["lce_w"], t["lce_b"], cfg.heads, cfg.S, cfg.topk,
-                            out=out, route_idx=route)
-                bra.linear(out, t["wo"], t["bo"], outs=[y])
+                bra.block_forward(t["x"], t["wqkv"], t["bqkv"], t["lce_w"], t["lce_b"], t["wo"], t["bo"],
+                                  cfg.heads, cfg.S, cfg.topk, out=out, route_idx=route)
         elif op == "dense":
             def step():
                 bra.attention_dense(t["q"], t["k"], t["v"], t["lce_w"], t["lce_b"], cfg.heads, out=out)
@@ -278,12 +292,12 @@ class Workload:
         self.step = step
 
 
-def kernel_rooflines(prof, cfg, share=1.0, backward=False):
+def kernel_rooflines(prof, cfg, share=1.0, backward=False, fused_block=False):
     kernels = {}
     for kind, (ms, cnt) in prof.items():
         if cnt:
             us = ms * 1e3 / cnt
-            r = roofline_for(kind, cfg, us * 1e-3, None, share, backward)
+            r = roofline_for(kind, cfg, us * 1e-3, None, share, backward, fused_block)
             kernels[kind] = {"us_per_launch": round(us, 3), "launches": cnt, "bound": r["bound"],
                              "achieved": round(r["achieved"], 2), "unit": r["unit"],
                              "frac": round(r["frac"], 4)}
@@ -299,6 +313,7 @@ def measure_config(w, flush, n_warm, n_cold):
     cfg = w.cfg
     share = 1.0 / cfg.heads if w.op == "head_routed" else 1.0
     bwd = w.op == "backward"
+    fb = w.fused
     for _ in range(n_warm // 2):
         w.step()
     torch.cuda.synchronize()
@@ -310,7 +325,7 @@ def measure_config(w, flush, n_warm, n_cold):
     bra.profile_begin(bra.KERNEL_NAMES)
     for _ in range(max(20, n_warm // 4)):
         w.step()
-    kernels = kernel_rooflines(bra.profile_read(), cfg, share, bwd)
+    kernels = kernel_rooflines(bra.profile_read(), cfg, share, bwd, fb)
     bra.profile_begin(())
     # cold: a 1 GiB write before each step; events around the step (torch's
     # current stream, which the binding hands to the library) and around the
@@ -335,7 +350,7 @@ def measure_config(w, flush, n_warm, n_cold):
             "queries_per_s": cfg.queries / (pctl(cold_us, 50) * 1e-6)}
     if attn_us:
         med = pctl(attn_us, 50)
-        r = roofline_for("attn", cfg, med * 1e-3, None, share, bwd)
+        r = roofline_for("attn", cfg, med * 1e-3, None, share, bwd, fb)
         cold.update(attn_us_median=round(med, 3), attn_us_p10=round(pctl(attn_us, 10), 3),
                     attn_us_p90=round(pctl(attn_us, 90), 3), attn_frac=round(r["frac"], 4))
     return {"ms_per_step": round(warm_ms, 5), "queries_per_s": cfg.queries / (warm_ms * 1e-3),
@@ -394,6 +409,8 @@ def main(argv=None) -> int:
             runs.append(("c4h", by_name["c4"], "head_routed"))
             runs.append(("c4b", by_name["c4"], "backward"))
             runs.append(("c1b", by_name["c1"], "backward"))
+            runs.append(("c4blk", by_name["c4"], "block"))
+            runs.append(("c1blk", by_name["c1"], "block"))
         for name, c, op in runs:
             w = Workload(c, op, dev)
             per_config[name] = measure_config(w, flush, n_warm=1000, n_cold=a.cold)
@@ -401,6 +418,9 @@ def main(argv=None) -> int:
                 per_config[name]["op"] = "bra_forward_head_routed (every head routed on its own channels)"
             if op == "backward":
                 per_config[name]["op"] = "bra_backward (gradients for the forward's routes)"
+            if op == "block":
+                per_config[name]["op"] = ("bra_block_forward (qkv Linear, BRA, wo Linear; "
+                                          + ("fused)" if w.fused else "three steps)"))
             print(f"[bench] per_config {name}: {per_config[name]['ms_per_step'] * 1e3:.2f} us/step warm, "
                   f"{per_config[name]['cold']['step_us_median']:.2f} us cold", file=sys.stderr, flush=True)
             if c is cfg and op == a.op:
@@ -441,7 +461,7 @@ def main(argv=None) -> int:
         step()
     share = 1.0 / cfg.heads if head.op == "head_routed" else 1.0
     bwd = head.op == "backward"
-    kernels = kernel_rooflines(bra.profile_read(), cfg, share, bwd)
+    kernels = kernel_rooflines(bra.profile_read(), cfg, share, bwd, head.fused)
     bra.profile_begin(())
 
     if a.calib_copy_mb > 0:
@@ -456,7 +476,7 @@ def main(argv=None) -> int:
     attn_ms, attn_cnt = prof_timed["attn"]
     attn_ms_per_launch = attn_ms / attn_cnt
     traffic = measured_traffic(cfg.name) if head.op in ("forward", "dense") else None
-    roof = roofline_for("attn", cfg, attn_ms_per_launch, traffic, share, bwd)
+    roof = roofline_for("attn", cfg, attn_ms_per_launch, traffic, share, bwd, head.fused)
     roof["us_per_launch"] = attn_ms_per_launch * 1e3
     roof["launches"] = attn_cnt
 
@@ -476,7 +496,8 @@ def main(argv=None) -> int:
         "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) q/k/v; see synth/)",
         "config": {"workload": f"{cfg.name}: {cfg.what}"
-                               + (" -- block: qkv Linear, BRA, wo Linear" if a.op == "block" else "")
+                               + ((" -- block: qkv Linear, BRA, wo Linear"
+                                   + (" (fused)" if head.fused else "")) if a.op == "block" else "")
                                + (" -- bra_attention_dense" if head.op == "dense" else "")
                                + (" -- bra_backward for given routes" if bwd else "")
                                + (" -- bra_forward_head_routed" if head.op == "head_routed" else ""),

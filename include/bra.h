@@ -203,6 +203,41 @@ int bra_lce(const void* v, const void* lce_w, const void* lce_b,
 int bra_linear(const void* x, const void* w, const void* b, int M, int K, int Nout, int split,
                int dtype, void* y0, void* y1, void* y2);
 
+/* The BRA block around the operator (the walk-through at
+ * TRANSFORMER.niftyadmin.cn/n/347023.html, section BRA模块: one Linear(C, 3C)
+ * whose output splits into q, k, v in that order along the channels, the
+ * operator, then wo = Linear(C, C); its module print in section 网络结构
+ * shows both layers):
+ *   q, k, v = split(x . w_qkv^T + b_qkv),  o = bra_forward(q, k, v, ...),
+ *   y = o . w_o^T + b_o.
+ * x, y: [N][H][W][C] in dtype; w_qkv: [3C][C] and w_o: [C][C] as a Linear
+ * layer stores them (output feature, input feature); b_qkv [3C], b_o [C],
+ * each may be NULL (no bias); lce_w, lce_b, heads, S, topk as bra_forward;
+ * route_idx [N][S*S][topk] int32 receives the routes. q, k, v and o are held
+ * in dtype between the steps (bf16: rounded to nearest even), as separate
+ * bra_linear / bra_forward calls would store them, so the result equals that
+ * chain's up to the order of fp32 sums.
+ * bf16 shapes that bra_forward runs on its large-region kernel with two heads
+ * and regions of 8x8 or 16x16 tokens run fused (bra_block_fused): the qkv
+ * projection also writes the region means and key norms that routing needs
+ * (no pass re-reads q and k), and the attention kernel, with both heads of a
+ * region in one workgroup, applies w_o and b_o before it stores. Other shapes
+ * run the three steps as bra_linear and bra_forward do.
+ * Workspace: the library's own (allocated or grown on first need, kept until
+ * bra_release), 4 * N*H*W*C * sizeof(dtype) bytes (256-byte aligned parts)
+ * plus bra_workspace_bytes(N, C, S); y and route_idx must not alias it, x,
+ * the weights or each other. Requires C <= 256 for bf16 and x under 2 GiB
+ * (else BRA_ERR_UNSUPPORTED), plus bra_forward's envelope. Alignment: x, the
+ * weights, lce_w and y 16 bytes, biases and route_idx 4 bytes (BRA_ERR_ALIGN).
+ * Errors: those of bra_forward and bra_linear. */
+int bra_block_forward(const void* x, const void* w_qkv, const void* b_qkv, const void* lce_w,
+                      const void* lce_b, const void* w_o, const void* b_o, int N, int H, int W,
+                      int C, int heads, int S, int topk, int dtype, void* y, int32_t* route_idx);
+
+/* 1 if bra_block_forward runs these sizes on its fused path, else 0 (also
+ * for invalid sizes). */
+int bra_block_fused(int N, int H, int W, int C, int heads, int S, int topk, int dtype);
+
 /* Stream used by every later call from this host thread (a hipStream_t;
  * NULL = the null stream). Always returns BRA_OK. */
 int bra_set_stream(void* stream);

@@ -161,20 +161,44 @@ def run_block(bra, d, heads, S, topk, dtype, images=None, name=""):
     return rep
 
 
-# (name, N, H, C, heads, S, topk, dtype): the one-kernel 4x4-region path
-# (S = 7 at H = 28), the general bf16 path (8x8 regions) and fp32
+# (name, N, H, C, heads, S, topk, dtype, fused): the one-kernel 4x4-region
+# path (S = 7 at H = 28) and fp32 run as three steps; two heads with 8x8 or
+# 16x16 regions run fused (qkv + pooling, routing, attention + wo): a token
+# count that leaves the last projection workgroup partly empty (24x24, 8x8
+# regions), whole-region routing (topk = S^2), 16x16 regions with two slabs
+# and a ragged topk
 BLOCK_CASES = [
-    ("block_4x4_c128_t4", 2, 28, 128, 4, 7, 4, "bf16"),
-    ("block_8x8_c64_t2", 1, 32, 64, 2, 4, 2, "bf16"),
-    ("block_f32_c64_t1", 1, 16, 64, 2, 2, 1, "f32"),
+    ("block_4x4_c128_t4", 2, 28, 128, 4, 7, 4, "bf16", False),
+    ("block_f32_c64_t1", 1, 16, 64, 2, 2, 1, "f32", False),
+    ("block_8x8_c128_t2", 1, 32, 128, 4, 4, 2, "bf16", False),
+    ("block_fused_8x8_t2", 1, 32, 64, 2, 4, 2, "bf16", True),
+    ("block_fused_8x8_ragged", 1, 24, 64, 2, 3, 4, "bf16", True),
+    ("block_fused_8x8_all", 2, 16, 64, 2, 2, 4, "bf16", True),
+    ("block_fused_16x16_t3", 2, 48, 64, 2, 3, 3, "bf16", True),
+    ("block_fused_16x16_t1", 1, 32, 64, 2, 2, 1, "bf16", True),
 ]
 
 
 @pytest.mark.parametrize("case", BLOCK_CASES, ids=[c[0] for c in BLOCK_CASES])
 def test_block_small(gpu_lib, case):
-    name, N, H, C, heads, S, topk, dtype = case
+    import torch
+    name, N, H, C, heads, S, topk, dtype, fused = case
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    assert gpu_lib.block_fused(N, H, H, C, heads, S, topk, tdt) == fused
     d = draw_block(N, H, H, C, S, dtype, seed=3300 + len(name))
     run_block(gpu_lib, d, heads, S, topk, dtype, name=name)
+
+
+def test_block_fused_full_size(gpu_lib):
+    """The fused block at the segmentation workload's shape (8 images of
+    128x128 tokens, C = 64, two heads, 16x16 regions, topk 4); the oracle
+    checks every image, routes and outputs."""
+    import torch
+    cfg = CONFIGS[4]
+    assert gpu_lib.block_fused(cfg.N, cfg.H, cfg.W, cfg.C, cfg.heads, cfg.S, cfg.topk, torch.bfloat16)
+    d = draw_block(cfg.N, cfg.H, cfg.W, cfg.C, cfg.S, "bf16", seed=3500, offset_std=cfg.offset_std,
+                   w_std=cfg.w_std, b_std=cfg.b_std)
+    run_block(gpu_lib, d, cfg.heads, cfg.S, cfg.topk, "bf16", name="block_full_c4")
 
 
 def test_block_full_size(gpu_lib):

@@ -35,6 +35,9 @@ _SIGS = {
     "bra_attend": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "bra_lce": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "bra_linear": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "bra_block_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
+                               _vp, _vp]),
+    "bra_block_fused": (_i, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "bra_set_stream": (_i, [_vp]),
     "bra_get_stream": (_vp, []),
     "bra_workspace_bytes": (_sz, [_i, _i, _i]),
@@ -320,15 +323,48 @@ def linear(x, w, b, split=None, outs=None):
     return tuple(outs)
 
 
-def block_forward(x, wqkv, bqkv, lce_w, lce_b, wo, bo, heads: int, S: int, topk: int):
-    """The BRA block of the walk-through: q, k, v = split(x wqkv^T + bqkv),
-    o = bra_forward(q, k, v) (attention + LCE), y = o wo^T + bo. Three library
-    calls on the current stream; returns (y, route_idx)."""
-    C = x.shape[-1]
-    q, k, v = linear(x, wqkv, bqkv, split=C)
-    o, route_idx = forward(q, k, v, lce_w, lce_b, heads, S, topk)
-    (y,) = linear(o, wo, bo)
-    return y, route_idx
+def block_forward(x, wqkv, bqkv, lce_w, lce_b, wo, bo, heads: int, S: int, topk: int,
+                  out=None, route_idx=None):
+    """bra_block_forward, the walk-through's BRA block: q, k, v =
+    split(x wqkv^T + bqkv), o = the operator, y = o wo^T + bo (one library
+    call; fused on the shapes bra_block_fused reports). x: (N, H, W, C);
+    wqkv: (3C, C); bqkv: (3C,) or None; wo: (C, C); bo: (C,) or None.
+    Returns (y, route_idx)."""
+    _check(x, "x")
+    dev, dt = x.device, x.dtype
+    for name, t in (("wqkv", wqkv), ("lce_w", lce_w), ("wo", wo)):
+        _check(t, name, dt, dev)
+    for name, t in (("bqkv", bqkv), ("lce_b", lce_b), ("bo", bo)):
+        if t is not None:
+            _check(t, name, dt, dev)
+    N, H, W, C = x.shape
+    if tuple(wqkv.shape) != (3 * C, C) or tuple(wo.shape) != (C, C):
+        raise ValueError("wqkv must be (3C, C) and wo (C, C)")
+    if (bqkv is not None and bqkv.numel() != 3 * C) or (bo is not None and bo.numel() != C):
+        raise ValueError("bqkv must hold 3C and bo C elements")
+    if lce_w.numel() != C * 25 or (lce_b is not None and lce_b.numel() != C):
+        raise ValueError("lce_w must hold C*25 and lce_b C elements")
+    if out is None:
+        out = torch.empty_like(x)
+    if route_idx is None:
+        route_idx = torch.empty((N, S * S, topk) if S > 0 and topk > 0 else (0,),
+                                dtype=torch.int32, device=dev)
+    _check(out, "out", dt, dev)
+    _check(route_idx, "route_idx", torch.int32, dev)
+    if out.shape != x.shape or route_idx.numel() != N * S * S * topk:
+        raise ValueError("out / route_idx have the wrong size")
+    with torch.cuda.device(dev):
+        _stream(dev)
+        _call("bra_block_forward", _ptr(x), _ptr(wqkv), _ptr(bqkv), _ptr(lce_w), _ptr(lce_b),
+              _ptr(wo), _ptr(bo), N, H, W, C, heads, S, topk, _dtype_code(x), _ptr(out),
+              _ptr(route_idx))
+    return out, route_idx
+
+
+def block_fused(N: int, H: int, W: int, C: int, heads: int, S: int, topk: int, dtype) -> bool:
+    """Does bra_block_forward run these sizes fused? dtype: torch dtype."""
+    code = BF16 if dtype == torch.bfloat16 else F32
+    return bool(load().bra_block_fused(N, H, W, C, heads, S, topk, code))
 
 
 def workspace_bytes(N: int, C: int, S: int) -> int:

@@ -68,6 +68,17 @@ hipError_t launch_attend_tile(const void* q, const void* k, const void* v, const
                               void* out, hipStream_t st);
 size_t lce_pack_bytes(int C);
 hipError_t launch_lce_pack(const void* w, int C, uint32_t* wpk, hipStream_t st);
+// The block's fused path: the qkv projection with the region pooling
+// (linear.hip), the large-region attention with every head of a region in
+// one workgroup and the output projection in its epilogue (attn_tile.hip)
+bool qkv_pool_supports(const Shape& s);
+hipError_t launch_qkv_pool(const void* x, const void* w, const void* b, const void* lw, const Shape& s,
+                           void* q, void* k, void* v, float* qr, float* kr, float* kn, uint32_t* wpk,
+                           hipStream_t st);
+bool tile_block_supports(const Shape& s);
+hipError_t launch_attend_tile_block(const void* q, const void* k, const void* v, const uint32_t* wpk,
+                                    const void* b, const int32_t* route, const float* kn, const void* wo,
+                                    const void* bo, const Shape& s, void* y, hipStream_t st);
 
 ProfEvents& prof_events() {
   thread_local ProfEvents pe;
@@ -394,6 +405,88 @@ int scratch_address(void** ptr) {
 }  // namespace
 
 extern "C" {
+
+// Does the block run fused (qkv + pooling, routing, attention + output
+// projection): bf16 shapes whose operator runs the large-region kernel, with
+// two heads and regions of 8x8 or 16x16 tokens.
+bool block_fused(const bra::Shape& s, int dtype) {
+  return dtype == BRA_BF16 && !bra::image_kernel_supports(s) && !bra::region_kernel_supports(s) &&
+         bra::tile_kernel_supports(s) && bra::tile_block_supports(s) && bra::qkv_pool_supports(s);
+}
+
+int bra_block_forward(const void* x, const void* w_qkv, const void* b_qkv, const void* lce_w,
+                      const void* lce_b, const void* w_o, const void* b_o, int N, int H, int W, int C,
+                      int heads, int S, int topk, int dtype, void* y, int32_t* route_idx) {
+  if (!x || !w_qkv || !lce_w || !w_o || !y || !route_idx) return BRA_ERR_NULL;
+  bra::Shape s;
+  int rc = check_dims(N, H, W, C, heads, S, topk, dtype, true, true, &s);
+  if (rc) return rc;
+  const long long esz = dtype == BRA_BF16 ? 2 : 4;
+  // the projections' envelope (bra_linear's)
+  if ((dtype == BRA_BF16 && C > 256) || (long long)N * H * W * C * esz >= (1ll << 31) ||
+      3ll * C * C * esz >= (1ll << 31))
+    return BRA_ERR_UNSUPPORTED;
+  rc = check_align({x, w_qkv, lce_w, w_o, y}, {b_qkv, lce_b, b_o, route_idx});
+  if (rc) return rc;
+  if ((uintptr_t)y & 15u) return BRA_ERR_ALIGN;
+  rc = check_ptrs({x, w_qkv, b_qkv, lce_w, lce_b, w_o, b_o, y, route_idx});
+  if (rc) return rc;
+  // workspace: q, k, v and the operator's output (the hand-offs), then the
+  // operator's own workspace
+  const size_t M = (size_t)N * H * W;
+  const size_t tb = (M * C * esz + 255) & ~(size_t)255;
+  const WsLayout wl = ws_layout(N, C, S);
+  hipStream_t st = g_stream;
+  std::lock_guard<std::mutex> lk(g_ws_mutex);
+  void* ws = nullptr;
+  rc = workspace(4 * tb + wl.total, &ws);
+  if (rc) return rc;
+  char* base = static_cast<char*>(ws);
+  void *q = base, *k = base + tb, *v = base + 2 * tb, *o = base + 3 * tb;
+  char* fws = base + 4 * tb;
+  hipError_t e;
+  if (block_fused(s, dtype)) {
+    float* qr = reinterpret_cast<float*>(fws);
+    float* kr = qr + (size_t)N * s.R * C;
+    float* kn = reinterpret_cast<float*>(fws + wl.kn);
+    uint32_t* wpk = reinterpret_cast<uint32_t*>(fws + wl.wpk);
+    {
+      ProfScope ps(BRA_K_LINEAR, st);  // also repacks the LCE weights, as the pooling kernel does
+      e = bra::launch_qkv_pool(x, w_qkv, b_qkv, lce_w, s, q, k, v, qr, kr, kn, wpk, st);
+    }
+    if (e != hipSuccess) return hip_fail(e);
+    {
+      ProfScope ps(BRA_K_ROUTE, st);
+      e = bra::launch_route(qr, kr, N, s.R, C, topk, route_idx, st);
+    }
+    if (e != hipSuccess) return hip_fail(e);
+    {
+      ProfScope ps(BRA_K_ATTN, st);
+      e = bra::launch_attend_tile_block(q, k, v, wpk, lce_b, route_idx, kn, w_o, b_o, s, y, st);
+    }
+    return e == hipSuccess ? BRA_OK : hip_fail(e);
+  }
+  // otherwise the three steps as bra_linear and bra_forward run them
+  {
+    ProfScope ps(BRA_K_LINEAR, st);
+    e = bra::launch_linear(x, w_qkv, b_qkv, (int)M, C, 3 * C, C, dtype, q, k, v, st);
+  }
+  if (e != hipSuccess) return hip_fail(e);
+  rc = forward_one_kernel(s, dtype) ? forward_one(q, k, v, lce_w, lce_b, s, o, route_idx, st)
+                                    : forward_staged(q, k, v, lce_w, lce_b, s, dtype, o, route_idx, fws, st);
+  if (rc) return rc;
+  {
+    ProfScope ps(BRA_K_LINEAR, st);
+    e = bra::launch_linear(o, w_o, b_o, (int)M, C, C, C, dtype, y, nullptr, nullptr, st);
+  }
+  return e == hipSuccess ? BRA_OK : hip_fail(e);
+}
+
+int bra_block_fused(int N, int H, int W, int C, int heads, int S, int topk, int dtype) {
+  bra::Shape s;
+  if (check_dims(N, H, W, C, heads, S, topk, dtype, true, true, &s) != BRA_OK) return 0;
+  return block_fused(s, dtype) ? 1 : 0;
+}
 
 int bra_forward(const void* q, const void* k, const void* v, const void* lce_w,
                 const void* lce_b, int N, int H, int W, int C, int heads, int S,

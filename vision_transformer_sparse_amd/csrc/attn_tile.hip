@@ -59,6 +59,19 @@
 // into the freed tile buffers as horizontal pixel pairs, and with the
 // weights as matching pairs each lane's output takes 15 packed-bf16 dot
 // products per channel. Workgroups of one image are numbered onto one XCD.
+//
+// With HG > 1 (the block's path: HG = heads) one workgroup covers every head
+// of its (image, region, slab): four waves per head, each head with its own
+// tile buffers and halo (the LCE weights are loaded after the key loop into
+// the head's freed halo staging, so two heads fit 64 KiB of LDS), and the
+// output projection of the walk-through's BRA block (wo = Linear(C, C),
+// section BRA模块) runs in the epilogue: the attention + LCE output is
+// rounded to bf16 (the block's hand-off precision) in the channel order
+// {4g..4g+3, 16+4g..16+4g+3} of lane group g, which is a B operand of the
+// 16x16x32 products as it stands; the waves of the same queries exchange
+// theirs through LDS and wave (head h) computes output channels 32h..32h+31
+// of its queries as y^T = Wo . o^T (the weight rows read in the same channel
+// order), adds the bias and stores them.
 #include "bra_internal.h"
 
 namespace bra {
@@ -139,6 +152,8 @@ struct TileArgs {
   const uint16_t* b;
   const int32_t* route;  // [N][S*S][topk]
   const float* kn;       // [N][S*S][heads] max |k|^2 of each region's head slice, or null
+  const uint16_t* wo;    // HG > 1: the output projection's weight [C][C] (out, in) and bias [C] or null
+  const uint16_t* bo;
   uint16_t* out;
   int N, H, W, C, heads, S, topk;
   float qscale;  // head_dim^-1/2 * log2(e)
@@ -165,29 +180,44 @@ __host__ __device__ constexpr size_t halo_bytes(int SR, int RW) {
   return (size_t)(SR + 4) * ((RW + 5) / 2) * 32 * 4;
 }
 
+constexpr size_t kWtsBytes = align16((size_t)2 * 15 * 32 * 4);  // a head's LCE weight pairs
+// the output exchange of one head's waves (HG > 1): [waves][QBW][64 lanes] x 16 bytes
+__host__ __device__ constexpr size_t xch_bytes(int qbw) { return (size_t)kTileWaves * qbw * 64 * 16; }
+
 struct TileLds {
-  size_t tiles, halo, raw, wts, flag, rbase, total;
+  size_t tiles, halo, raw, wts, xch, head, flag, rbase, total;
 };
 // The halo is loaded into `raw` at the start and repacked into pixel pairs
 // in the tile buffers after the last tile. The route table (topk entries)
-// goes last, so the other offsets stay constant.
-__host__ __device__ inline TileLds tile_lds(int SR, int RW, int topk) {
+// goes last, so the other offsets stay constant. With HG > 1 heads a
+// workgroup, each head has its own [tiles | raw] block (stride `head`), and
+// its LCE weights and output exchange go into its raw area after the repack.
+__host__ __device__ inline TileLds tile_lds(int SR, int RW, int topk, int HG, int qbw) {
   TileLds l;
   size_t o = 0;
   l.tiles = o; l.halo = o; o += (size_t)kBufs * kBufBytes;
   l.raw = o; o += halo_raw_bytes(SR, RW);
-  l.wts = o; o += align16((size_t)2 * 15 * 32 * 4);
+  if (HG == 1) {
+    l.head = 0;
+    l.xch = 0;
+    l.wts = o; o += kWtsBytes;
+  } else {
+    l.head = o;
+    l.wts = l.raw;
+    l.xch = l.raw + kWtsBytes;
+    o *= (size_t)HG;
+  }
   l.flag = o; o += 16;
   l.rbase = o; o += (size_t)4 * topk;
   l.total = o;
   return l;
 }
 
-template <int RH, int RW>
-__global__ __launch_bounds__(64 * kTileWaves, 4) void attn_tile_kernel(TileArgs a) {
+template <int RH, int RW, int HG>
+__global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(TileArgs a) {
   constexpr int T = RH * RW;
-  constexpr int WAVES = kTileWaves;
-  constexpr int NT = 64 * WAVES;
+  constexpr int WAVES = kTileWaves;  // waves of one head
+  constexpr int NT = 64 * WAVES;     // threads of one head
   constexpr int QBW = tile_qbw<RH, RW>();
   constexpr int SLABS = tile_slabs<RH, RW>();
   constexpr int SR = RH / SLABS;  // region rows per slab
@@ -196,30 +226,36 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void attn_tile_kernel(TileArgs 
   static_assert(halo_bytes(SR, RW) <= (size_t)kBufs * kBufBytes, "the halo fits the tile buffers");
   static_assert(halo_raw_bytes(SR, RW) % 1024 == 0 && WP % 2 == 0, "whole 1 KiB loads, whole pixel pairs");
   static_assert(64 % RW == 0, "a tile starts on a region row");
+  static_assert(HG == 1 || kWtsBytes + xch_bytes(QBW) <= halo_raw_bytes(SR, RW),
+                "weights and output exchange fit a head's halo staging");
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const TileLds lay = tile_lds(SR, RW, a.topk);
-  char* tiles = smem + lay.tiles;  // [kBufs][K: 64 rows x 64 bytes | V: the same], swizzled chunks
-  uint32_t* halo = reinterpret_cast<uint32_t*>(smem + lay.halo);  // [HP][NPAIR][32] after the loop
-  char* raw = smem + lay.raw;                                      // [HP][WP][64 bytes]
-  uint32_t* wts = reinterpret_cast<uint32_t*>(smem + lay.wts);    // [2][15][32]
+  const TileLds lay = tile_lds(SR, RW, a.topk, HG, QBW);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  // the wave's head within the workgroup, its wave and thread index there
+  const int hw = wave / WAVES, wv = wave % WAVES, htid = tid % NT;
+  char* hsm = smem + hw * lay.head;  // this head's block (HG > 1)
+  char* tiles = hsm + lay.tiles;  // [kBufs][K: 64 rows x 64 bytes | V: the same], swizzled chunks
+  uint32_t* halo = reinterpret_cast<uint32_t*>(hsm + lay.halo);  // [HP][NPAIR][32] after the loop
+  char* raw = hsm + lay.raw;                                      // [HP][WP][64 bytes]
+  uint32_t* wts = reinterpret_cast<uint32_t*>(hsm + lay.wts);    // [2][15][32]
   int* flag = reinterpret_cast<int*>(smem + lay.flag);
   uint32_t* rbase = reinterpret_cast<uint32_t*>(smem + lay.rbase);  // [topk] byte offset of each routed region
 
   const int W = a.W, H = a.H, C = a.C, S = a.S, R = S * S, topk = a.topk;
   const int L = topk * T;  // a multiple of 64
   const int ntiles = L / 64;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int col = lane & 15, grp = lane >> 4;
 
   // XCD-aware numbering: consecutive units (n, r, h, slab) share blockIdx %
   // 8, so the slabs and heads of a region -- the same K/V cache lines -- are
-  // read through one XCD's L2.
-  const int units = a.N * R * a.heads * SLABS;
+  // read through one XCD's L2. (HG > 1: units (n, r, slab), the head from
+  // the wave.)
+  const int units = a.N * R * (HG == 1 ? a.heads : 1) * SLABS;
   const int per = (units + 7) / 8;
   const int u = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   if (u >= units) return;  // the whole workgroup leaves together
   const int slab = u % SLABS, hu = u / SLABS;
-  const int h = hu % a.heads, nr = hu / a.heads;
+  const int h = HG == 1 ? hu % a.heads : hw, nr = HG == 1 ? hu / a.heads : hu;
   const int n = nr / R, r = nr - n * R;
   const int jr = r / S, ir = r - jr * S;
   const int y0 = jr * RH + slab * SR, x0 = ir * RW;  // the slab's first query row and column
@@ -242,15 +278,15 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void attn_tile_kernel(TileArgs 
   // route table) and the tile's first row are a uniform add.
   uint32_t ld_off_k, ld_off_v;
   {
-    const int kk = score_key(wave, lane & 15), kc = lane >> 4;
+    const int kk = score_key(wv, lane & 15), kc = lane >> 4;
     ld_off_k = (uint32_t)(kk / RW) * rowb + (uint32_t)(kk % RW) * pixb + hb + (uint32_t)kc * 16;
-    const int kr = 16 * wave + (lane >> 2), c = (lane & 3) ^ swz(kr);
+    const int kr = 16 * wv + (lane >> 2), c = (lane & 3) ^ swz(kr);
     ld_off_v = (uint32_t)(kr / RW) * rowb + (uint32_t)(kr % RW) * pixb + hb + (uint32_t)c * 16;
   }
   auto issue = [&](int tile, int buf) {
     const int p = tile * 64 / T, tt0 = tile * 64 - p * T;
     const uint32_t soff = __builtin_amdgcn_readfirstlane(rbase[p]) + (uint32_t)(tt0 / RW) * rowb;
-    char* dst = tiles + buf * kBufBytes + wave * 1024;
+    char* dst = tiles + buf * kBufBytes + wv * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(kb, (__attribute__((address_space(3))) void*)dst, 16, ld_off_k,
                                              soff, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vb, (__attribute__((address_space(3))) void*)(dst + kTileBytes),
@@ -266,7 +302,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void attn_tile_kernel(TileArgs 
   // are walked.
   auto issue_halo = [&]() {
     constexpr int NLOAD = (int)(halo_raw_bytes(SR, RW) / 1024);
-    for (int j = wave; j < NLOAD; j += WAVES) {
+    for (int j = wv; j < NLOAD; j += WAVES) {
       const int piece = j * 64 + lane, pix = piece >> 2, ch = piece & 3;
       const int y = y0 - 2 + pix / WP, x = x0 - 2 + pix % WP;
       const uint32_t off = y >= 0 && y < H && x >= 0 && x < W
@@ -282,7 +318,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void attn_tile_kernel(TileArgs 
   bf16x8 bq[QBW];
 #pragma unroll
   for (int i = 0; i < QBW; ++i) {
-    const int t = (wave * QBW + i) * 16 + col;
+    const int t = (wv * QBW + i) * 16 + col;
     bq[i] = as_bf16x8(ld16(qb, (uint32_t)(y0 + t / RW) * rowb + (uint32_t)(x0 + t % RW) * pixb + hb + grp * 16));
   }
   // ---- route table -> LDS, and the largest squared key norm over the
@@ -304,7 +340,8 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void attn_tile_kernel(TileArgs 
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) k2 = fmaxf(k2, __shfl_xor(k2, d));
   // weights: [2][15][C] -> this head's [2][15][32]; 240 pieces of 16 bytes
-  if (tid < 240) {
+  // (HG > 1: after the key loop, into the freed halo staging)
+  if (HG == 1 && tid < 240) {
     const int row = tid >> 3, piece = tid & 7;  // row = parity * 15 + (ay * 3 + j)
     const uint4 w = *reinterpret_cast<const uint4*>(a.wpk + (size_t)row * C + h * 32 + piece * 4);
     *reinterpret_cast<uint4*>(wts + row * 32 + piece * 4) = w;
@@ -448,6 +485,9 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void attn_tile_kernel(TileArgs 
     pass(SoftTag{});
   }
   __syncthreads();  // every wave is done with the tile buffers: the halo goes there
+  uint4 wreg = {0u, 0u, 0u, 0u};
+  if (HG > 1 && htid < 240)
+    wreg = *reinterpret_cast<const uint4*>(a.wpk + (size_t)(htid >> 3) * C + h * 32 + (htid & 7) * 4);
 
   // ---- the halo as horizontal pixel pairs of the head's 32 channels (the
   // raw halo landed before the second tile's barrier, or before the
@@ -456,7 +496,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void attn_tile_kernel(TileArgs 
   __syncthreads();
   {
     constexpr int NSLOT = HP * NPAIR;
-    for (int e = tid; e < NSLOT * 4; e += NT) {
+    for (int e = htid; e < NSLOT * 4; e += NT) {
       const int pp = e >> 2, ch = e & 3;
       const int pr = pp % NPAIR, py = pp / NPAIR;
       const char* src = raw + (py * WP + 2 * pr) * 64 + ch * 16;
@@ -473,13 +513,31 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void attn_tile_kernel(TileArgs 
     }
   }
   __syncthreads();
+  if constexpr (HG > 1) {  // the weights into the head's freed halo staging
+    if (htid < 240) *reinterpret_cast<uint4*>(wts + (htid >> 3) * 32 + (htid & 7) * 4) = wreg;
+    __syncthreads();
+  }
+  // HG > 1: the output projection's A operands, loaded now so that they land
+  // during the LCE: rows 32h + 16 ot + col of wo, input channels of head g in
+  // the B operand's order (4 grp .. +3, then 16 + 4 grp .. +3)
+  uint2 wa[HG > 1 ? 2 : 1][HG][2];
+  if constexpr (HG > 1) {
+#pragma unroll
+    for (int ot = 0; ot < 2; ++ot)
+#pragma unroll
+      for (int g = 0; g < HG; ++g) {
+        const uint16_t* wrow = a.wo + (size_t)(32 * h + 16 * ot + col) * C + 32 * g + 4 * grp;
+        wa[ot][g][0] = *reinterpret_cast<const uint2*>(wrow);
+        wa[ot][g][1] = *reinterpret_cast<const uint2*>(wrow + 16);
+      }
+  }
 
   // ---- LCE + merge + store: lane = (query col, channel group grp); the
   // lane's query rows i = 0..QBW-1 are stacked in one column when RW == 16
   // (one query otherwise), so each halo row is read once for all of them
   const uint32_t* w32 = wts;
   static_assert(QBW == 1 || RW == 16, "stacked queries need 16-token rows");
-  const int t0 = wave * QBW * 16 + col;
+  const int t0 = wv * QBW * 16 + col;
   const int ty0 = t0 / RW, tx = t0 % RW;
   const int par = tx & 1, p0 = tx >> 1;
   float acc[QBW][8];
@@ -520,19 +578,13 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void attn_tile_kernel(TileArgs 
       }
     }
   }
-#pragma unroll
-  for (int i = 0; i < QBW; ++i) {
-    const int ty = ty0 + i;
-    const float inv = 1.0f / ls[i][0];
-    uint2 lo, hi;
-    lo.x = float_to_bf16_bits(fmaf(o0[i][0], inv, acc[i][0])) | (float_to_bf16_bits(fmaf(o0[i][1], inv, acc[i][1])) << 16);
-    lo.y = float_to_bf16_bits(fmaf(o0[i][2], inv, acc[i][2])) | (float_to_bf16_bits(fmaf(o0[i][3], inv, acc[i][3])) << 16);
-    hi.x = float_to_bf16_bits(fmaf(o1[i][0], inv, acc[i][4])) | (float_to_bf16_bits(fmaf(o1[i][1], inv, acc[i][5])) << 16);
-    hi.y = float_to_bf16_bits(fmaf(o1[i][2], inv, acc[i][6])) | (float_to_bf16_bits(fmaf(o1[i][3], inv, acc[i][7])) << 16);
-    // regroup: lane group g gets channels 8g .. 8g+7 (the 32-lane swap of
-    // (lo, hi) gives (lo0, lo1, hi0, hi1) / (lo2, lo3, hi2, hi3) by group,
-    // the 16-lane swap (lo0, lo2, hi0, hi2) / (lo1, lo3, hi1, hi3)), so the
-    // token's 64 bytes leave in one 16-byte-per-lane store
+  // regroup (lo: channels 4grp..+3, hi: 16+4grp..+3 of the head slice) so
+  // lane group g holds channels 8g .. 8g+7 (the 32-lane swap of (lo, hi)
+  // gives (lo0, lo1, hi0, hi1) / (lo2, lo3, hi2, hi3) by group, the 16-lane
+  // swap (lo0, lo2, hi0, hi2) / (lo1, lo3, hi1, hi3)), so the token's 64
+  // bytes of the slice leave in one 16-byte-per-lane store
+  const Rsrc ob = rsrc(a.out + img, img_bytes);
+  auto store_slice = [&](uint2 lo, uint2 hi, int ty) {
     const uint32_t la[2] = {lo.x, lo.y}, hb[2] = {hi.x, hi.y};
     uint32_t xs[2], ys[2];
 #pragma unroll
@@ -544,19 +596,79 @@ __global__ __launch_bounds__(64 * kTileWaves, 4) void attn_tile_kernel(TileArgs 
     }
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 w4 = {xs[0], xs[1], ys[0], ys[1]};
-    const Rsrc ob = rsrc(a.out + img, img_bytes);
     const uint32_t oo = (uint32_t)(((y0 + ty) * W + x0 + tx) * C + h * 32) * 2;
     __builtin_amdgcn_raw_buffer_store_b128(w4, ob, oo + 16 * grp, 0, kNt);
+  };
+  uint4 oq[QBW];  // HG > 1: the rounded output, a B operand of the projection
+#pragma unroll
+  for (int i = 0; i < QBW; ++i) {
+    const float inv = 1.0f / ls[i][0];
+    uint2 lo, hi;
+    lo.x = float_to_bf16_bits(fmaf(o0[i][0], inv, acc[i][0])) | (float_to_bf16_bits(fmaf(o0[i][1], inv, acc[i][1])) << 16);
+    lo.y = float_to_bf16_bits(fmaf(o0[i][2], inv, acc[i][2])) | (float_to_bf16_bits(fmaf(o0[i][3], inv, acc[i][3])) << 16);
+    hi.x = float_to_bf16_bits(fmaf(o1[i][0], inv, acc[i][4])) | (float_to_bf16_bits(fmaf(o1[i][1], inv, acc[i][5])) << 16);
+    hi.y = float_to_bf16_bits(fmaf(o1[i][2], inv, acc[i][6])) | (float_to_bf16_bits(fmaf(o1[i][3], inv, acc[i][7])) << 16);
+    if constexpr (HG == 1)
+      store_slice(lo, hi, ty0 + i);
+    else
+      oq[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+  if constexpr (HG > 1) {
+    // ---- output projection: y^T (32 output channels of head h's slice x
+    // 16 queries) = sum over heads g of Wo[:, head g] . o_g^T, the o_g of
+    // the same queries from the exchange (wave wv of every head holds the
+    // same queries)
+    auto xch = [&](int g, int i) {
+      return reinterpret_cast<uint4*>(smem + g * lay.head + lay.xch) + (wv * QBW + i) * 64 + lane;
+    };
+#pragma unroll
+    for (int i = 0; i < QBW; ++i) *xch(hw, i) = oq[i];
+    __syncthreads();
+    f32x4 ya[2][QBW];
+#pragma unroll
+    for (int ot = 0; ot < 2; ++ot)
+#pragma unroll
+      for (int i = 0; i < QBW; ++i) ya[ot][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < HG; ++g) {
+      bf16x8 ob8[QBW];
+#pragma unroll
+      for (int i = 0; i < QBW; ++i) ob8[i] = as_bf16x8(*xch(g, i));
+#pragma unroll
+      for (int ot = 0; ot < 2; ++ot) {
+        const bf16x8 av = as_bf16x8(make_uint4(wa[ot][g][0].x, wa[ot][g][0].y, wa[ot][g][1].x, wa[ot][g][1].y));
+#pragma unroll
+        for (int i = 0; i < QBW; ++i) ya[ot][i] = mfma(av, ob8[i], ya[ot][i]);
+      }
+    }
+    // bias of the lane's output channels (no bias: zeros), round, store
+    const Rsrc bb = rsrc(a.bo, a.bo ? (uint32_t)C * 2 : 0u);
+    const uint32_t boff = (uint32_t)(h * 32 + 4 * grp) * 2;
+    const uint32_t bw[4] = {__builtin_amdgcn_raw_buffer_load_b32(bb, boff, 0, 0),
+                            __builtin_amdgcn_raw_buffer_load_b32(bb, boff + 4, 0, 0),
+                            __builtin_amdgcn_raw_buffer_load_b32(bb, boff + 32, 0, 0),
+                            __builtin_amdgcn_raw_buffer_load_b32(bb, boff + 36, 0, 0)};
+    const float bias[8] = {bf16_lo(bw[0]), bf16_hi(bw[0]), bf16_lo(bw[1]), bf16_hi(bw[1]),
+                           bf16_lo(bw[2]), bf16_hi(bw[2]), bf16_lo(bw[3]), bf16_hi(bw[3])};
+#pragma unroll
+    for (int i = 0; i < QBW; ++i) {
+      uint2 lo, hi;
+      lo.x = float_to_bf16_bits(ya[0][i][0] + bias[0]) | (float_to_bf16_bits(ya[0][i][1] + bias[1]) << 16);
+      lo.y = float_to_bf16_bits(ya[0][i][2] + bias[2]) | (float_to_bf16_bits(ya[0][i][3] + bias[3]) << 16);
+      hi.x = float_to_bf16_bits(ya[1][i][0] + bias[4]) | (float_to_bf16_bits(ya[1][i][1] + bias[5]) << 16);
+      hi.y = float_to_bf16_bits(ya[1][i][2] + bias[6]) | (float_to_bf16_bits(ya[1][i][3] + bias[7]) << 16);
+      store_slice(lo, hi, ty0 + i);
+    }
   }
 }
 
-template <int RH, int RW>
+template <int RH, int RW, int HG>
 hipError_t launch_t(const TileArgs& a, hipStream_t st) {
-  const int units = a.N * a.S * a.S * a.heads * tile_slabs<RH, RW>();
+  const int units = a.N * a.S * a.S * (HG == 1 ? a.heads : 1) * tile_slabs<RH, RW>();
   const unsigned blocks = (unsigned)(((units + 7) / 8) * 8);
-  constexpr int threads = 64 * kTileWaves;
-  launch((attn_tile_kernel<RH, RW>), dim3(blocks), dim3(threads),
-                     tile_lds(RH / tile_slabs<RH, RW>(), RW, a.topk).total, st, a);
+  constexpr int threads = 64 * kTileWaves * HG;
+  launch((attn_tile_kernel<RH, RW, HG>), dim3(blocks), dim3(threads),
+         tile_lds(RH / tile_slabs<RH, RW>(), RW, a.topk, HG, tile_qbw<RH, RW>()).total, st, a);
   return hipGetLastError();
 }
 
@@ -570,7 +682,34 @@ bool tile_kernel_supports(const Shape& s) {
   if (!compiled) return false;
   if ((long long)s.H * s.W * s.C >= (1ll << 30)) return false;  // 32-bit byte offsets in an image
   const int qbw = s.rw == 16 ? 2 : 1, slabs = s.rh * s.rw / (16 * kTileWaves * qbw);
-  return tile_lds(s.rh / slabs, s.rw, s.topk).total <= 65536;
+  return tile_lds(s.rh / slabs, s.rw, s.topk, 1, qbw).total <= 65536;
+}
+
+// The block's attention + output projection: every head of a region in one
+// workgroup (two heads of 32 channels; 8x8 or 16x16 regions).
+bool tile_block_supports(const Shape& s) {
+  if (s.hd != 32 || s.heads != 2) return false;
+  const int code = s.rh * 64 + s.rw;
+  if (code != 8 * 64 + 8 && code != 16 * 64 + 16) return false;
+  if ((long long)s.H * s.W * s.C >= (1ll << 30)) return false;
+  const int qbw = s.rw == 16 ? 2 : 1, slabs = s.rh * s.rw / (16 * kTileWaves * qbw);
+  return tile_lds(s.rh / slabs, s.rw, s.topk, 2, qbw).total <= 65536;
+}
+
+hipError_t launch_attend_tile_block(const void* q, const void* k, const void* v, const uint32_t* wpk,
+                                    const void* b, const int32_t* route, const float* kn, const void* wo,
+                                    const void* bo, const Shape& s, void* y, hipStream_t st) {
+  TileArgs a;
+  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
+  a.wpk = wpk; a.b = (const uint16_t*)b; a.route = route; a.kn = kn; a.out = (uint16_t*)y;
+  a.wo = (const uint16_t*)wo; a.bo = (const uint16_t*)bo;
+  a.N = s.N; a.H = s.H; a.W = s.W; a.C = s.C; a.heads = s.heads; a.S = s.S; a.topk = s.topk;
+  a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
+  switch (s.rh * 64 + s.rw) {
+    case 8 * 64 + 8: return launch_t<8, 8, 2>(a, st);
+    case 16 * 64 + 16: return launch_t<16, 16, 2>(a, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_attend_tile(const void* q, const void* k, const void* v, const uint32_t* wpk,
@@ -579,13 +718,14 @@ hipError_t launch_attend_tile(const void* q, const void* k, const void* v, const
   TileArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.wpk = wpk; a.b = (const uint16_t*)b; a.route = route; a.kn = kn; a.out = (uint16_t*)out;
+  a.wo = nullptr; a.bo = nullptr;
   a.N = s.N; a.H = s.H; a.W = s.W; a.C = s.C; a.heads = s.heads; a.S = s.S; a.topk = s.topk;
   a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
   switch (s.rh * 64 + s.rw) {
-    case 8 * 64 + 8: return launch_t<8, 8>(a, st);
-    case 16 * 64 + 16: return launch_t<16, 16>(a, st);
-    case 8 * 64 + 16: return launch_t<8, 16>(a, st);
-    case 16 * 64 + 8: return launch_t<16, 8>(a, st);
+    case 8 * 64 + 8: return launch_t<8, 8, 1>(a, st);
+    case 16 * 64 + 16: return launch_t<16, 16, 1>(a, st);
+    case 8 * 64 + 16: return launch_t<8, 16, 1>(a, st);
+    case 16 * 64 + 8: return launch_t<16, 8, 1>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
