@@ -63,9 +63,13 @@ hipError_t launch_route_heads(const int32_t* src, int32_t* dst, int N, int heads
 bool dense_kernel_supports(const Shape& s);
 hipError_t launch_attend_dense(const void* q, const void* k, const void* v, const void* w, const void* b,
                                const Shape& s, void* out, hipStream_t st);
+// Routes given (route), or chosen in the kernel from the region means qr, kr
+// (tile_kernel_routes) and written to route_out
 hipError_t launch_attend_tile(const void* q, const void* k, const void* v, const uint32_t* wpk,
                               const void* b, const int32_t* route, const float* kn, const Shape& s,
-                              void* out, hipStream_t st);
+                              void* out, hipStream_t st, const float* qr = nullptr, const float* kr = nullptr,
+                              int32_t* route_out = nullptr);
+bool tile_kernel_routes(const Shape& s);
 size_t lce_pack_bytes(int C);
 hipError_t launch_lce_pack(const void* w, int C, uint32_t* wpk, hipStream_t st);
 // The block's fused path: the qkv projection with the region pooling
@@ -77,8 +81,9 @@ hipError_t launch_qkv_pool(const void* x, const void* w, const void* b, const vo
                            hipStream_t st);
 bool tile_block_supports(const Shape& s);
 hipError_t launch_attend_tile_block(const void* q, const void* k, const void* v, const uint32_t* wpk,
-                                    const void* b, const int32_t* route, const float* kn, const void* wo,
-                                    const void* bo, const Shape& s, void* y, hipStream_t st);
+                                    const void* b, const float* qr, const float* kr, int32_t* route_out,
+                                    const float* kn, const void* wo, const void* bo, const Shape& s, void* y,
+                                    hipStream_t st);
 
 ProfEvents& prof_events() {
   thread_local ProfEvents pe;
@@ -366,6 +371,13 @@ int forward_staged(const void* q, const void* k, const void* v, const void* lce_
     e = bra::launch_region_pool(q, k, s, dtype, qr, kr, lce_w, wpk, kn, st);
   }
   if (e != hipSuccess) return hip_fail(e);
+  if (tile && bra::tile_kernel_routes(s)) {
+    // the large-region kernel routes its own region from the means (the
+    // route kernel's logits, bit for bit) and reports the routes
+    ProfScope ps(BRA_K_ATTN, st);
+    e = bra::launch_attend_tile(q, k, v, wpk, lce_b, route_idx, kn, s, out, st, qr, kr, route_idx);
+    return e == hipSuccess ? BRA_OK : hip_fail(e);
+  }
   {
     ProfScope ps(BRA_K_ROUTE, st);
     e = bra::launch_route(qr, kr, N, s.R, C, topk, route_idx, st);
@@ -456,13 +468,8 @@ int bra_block_forward(const void* x, const void* w_qkv, const void* b_qkv, const
     }
     if (e != hipSuccess) return hip_fail(e);
     {
-      ProfScope ps(BRA_K_ROUTE, st);
-      e = bra::launch_route(qr, kr, N, s.R, C, topk, route_idx, st);
-    }
-    if (e != hipSuccess) return hip_fail(e);
-    {
-      ProfScope ps(BRA_K_ATTN, st);
-      e = bra::launch_attend_tile_block(q, k, v, wpk, lce_b, route_idx, kn, w_o, b_o, s, y, st);
+      ProfScope ps(BRA_K_ATTN, st);  // routes chosen in the kernel
+      e = bra::launch_attend_tile_block(q, k, v, wpk, lce_b, qr, kr, route_idx, kn, w_o, b_o, s, y, st);
     }
     return e == hipSuccess ? BRA_OK : hip_fail(e);
   }

@@ -73,6 +73,7 @@
 // of its queries as y^T = Wo . o^T (the weight rows read in the same channel
 // order), adds the bias and stores them.
 #include "bra_internal.h"
+#include "route_common.h"
 
 namespace bra {
 namespace {
@@ -154,6 +155,13 @@ struct TileArgs {
   const float* kn;       // [N][S*S][heads] max |k|^2 of each region's head slice, or null
   const uint16_t* wo;    // HG > 1: the output projection's weight [C][C] (out, in) and bias [C] or null
   const uint16_t* bo;
+  // routing in the kernel (S*S <= 64): the region means [N][S*S][C] (fp32),
+  // or null when the routes are given; the chosen routes are written to
+  // route_out ([N][S*S][topk])
+  const float* qr;
+  const float* kr;
+  int32_t* route_out;
+  float rscale;  // C^-1/2, the affinity's scale
   uint16_t* out;
   int N, H, W, C, heads, S, topk;
   float qscale;  // head_dim^-1/2 * log2(e)
@@ -321,6 +329,67 @@ __global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(Tile
     const int t = (wv * QBW + i) * 16 + col;
     bq[i] = as_bf16x8(ld16(qb, (uint32_t)(y0 + t / RW) * rowb + (uint32_t)(x0 + t % RW) * pixb + hb + grp * 16));
   }
+  // ---- routes chosen here (region means given, S*S <= 64): region r's
+  // logits against every region of its image with the router's split-bf16
+  // matrix-core tile (route_common.h: the operands, products and scale of
+  // route_kernel, so the same logits bit for bit; wave w takes regions
+  // 16w .. 16w+15, its tile's row 0 is region r), then wave 0 ranks the R
+  // keys (larger logit first, ties to the lower index) and region r's top-k
+  // go to LDS and, from one workgroup of the region, to route_out. The
+  // scratch is the halo staging, unused until the first tile step.
+  int32_t* sel = reinterpret_cast<int32_t*>(smem + lay.raw + 256);  // [topk] chosen regions
+  if (a.qr) {
+    float* lrow = reinterpret_cast<float*>(smem + lay.raw);            // [64] logits of region r
+    uint64_t* kw = reinterpret_cast<uint64_t*>(smem + lay.raw + 512);  // [64] their keys
+    if (wave < (R + 15) / 16) {
+      const uint32_t mbytes = (uint32_t)R * C * 4;
+      const Rsrc qm = rsrc(a.qr + (size_t)n * R * C, mbytes), km = rsrc(a.kr + (size_t)n * R * C, mbytes);
+      const uint32_t qrow = (uint32_t)r * C * 4, krow = (uint32_t)min(16 * wave + col, R - 1) * C * 4;
+      // route::logit_tile_x3's steps in its order (hi.lo + lo.hi + hi.hi per
+      // 32 channels), two steps' operands in flight at once
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      auto step = [&](const uint4& a0, const uint4& a1, const uint4& b0, const uint4& b1) {
+        const float fa[8] = {__uint_as_float(a0.x), __uint_as_float(a0.y), __uint_as_float(a0.z), __uint_as_float(a0.w),
+                             __uint_as_float(a1.x), __uint_as_float(a1.y), __uint_as_float(a1.z), __uint_as_float(a1.w)};
+        const float fb[8] = {__uint_as_float(b0.x), __uint_as_float(b0.y), __uint_as_float(b0.z), __uint_as_float(b0.w),
+                             __uint_as_float(b1.x), __uint_as_float(b1.y), __uint_as_float(b1.z), __uint_as_float(b1.w)};
+        route::rbf16x8 ah, al, bh, bl;
+        route::split_bf16(fa, ah, al);
+        route::split_bf16(fb, bh, bl);
+        acc = route::logit_step_x3(acc, ah, al, bh, bl);
+      };
+      for (int k0 = 0; k0 < C; k0 += 64) {
+        const uint32_t c = (uint32_t)(k0 + 8 * grp) * 4;
+        const bool two = k0 + 32 < C;  // C % 32 == 0
+        const uint4 a0 = ld16(qm, qrow + c), a1 = ld16(qm, qrow + c + 16);
+        const uint4 b0 = ld16(km, krow + c), b1 = ld16(km, krow + c + 16);
+        const uint4 a2 = ld16(qm, two ? qrow + c + 128 : kOut), a3 = ld16(qm, two ? qrow + c + 144 : kOut);
+        const uint4 b2 = ld16(km, two ? krow + c + 128 : kOut), b3 = ld16(km, two ? krow + c + 144 : kOut);
+        step(a0, a1, b0, b1);
+        if (two) step(a2, a3, b2, b3);
+      }
+      if (grp == 0) lrow[16 * wave + col] = acc[0] * a.rscale;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const uint64_t key = lane < R ? route::route_key(lrow[lane], lane) : 0ull;
+      kw[lane] = key;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      int rank = 0;  // keys are distinct; the 64 - R past R are 0
+#pragma unroll
+      for (int s2 = 0; s2 < 64; s2 += 2) {
+        const uint4 two = *reinterpret_cast<const uint4*>(kw + s2);
+        rank += (((uint64_t)two.y << 32 | two.x) > key) + (((uint64_t)two.w << 32 | two.z) > key);
+      }
+      if (lane < R && rank < topk) {
+        sel[rank] = lane;
+        if (slab == 0 && (HG > 1 || h == 0)) a.route_out[(size_t)nr * topk + rank] = lane;
+      }
+    }
+    __syncthreads();
+  }
   // ---- route table -> LDS, and the largest squared key norm over the
   // routed regions: each wave reads the route row and the norms with one
   // load per lane (two dependent loads in all, not two per route)
@@ -329,7 +398,7 @@ __global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(Tile
   for (int p0 = 0; p0 < topk; p0 += 64) {
     const int p = p0 + lane;
     if (p < topk) {
-      const int s = rrow[p];
+      const int s = a.qr ? sel[p] : rrow[p];
       if (wave == 0) {
         const int js = s / S, is = s - js * S;
         rbase[p] = (uint32_t)(js * RH) * rowb + (uint32_t)(is * RW) * pixb;
@@ -685,10 +754,14 @@ bool tile_kernel_supports(const Shape& s) {
   return tile_lds(s.rh / slabs, s.rw, s.topk, 1, qbw).total <= 65536;
 }
 
+// Can the kernel choose the routes itself (from the region means)?
+bool tile_kernel_routes(const Shape& s) { return s.R <= 64; }
+
 // The block's attention + output projection: every head of a region in one
-// workgroup (two heads of 32 channels; 8x8 or 16x16 regions).
+// workgroup (two heads of 32 channels; 8x8 or 16x16 regions), routes chosen
+// in the kernel (S*S <= 64).
 bool tile_block_supports(const Shape& s) {
-  if (s.hd != 32 || s.heads != 2) return false;
+  if (s.hd != 32 || s.heads != 2 || !tile_kernel_routes(s)) return false;
   const int code = s.rh * 64 + s.rw;
   if (code != 8 * 64 + 8 && code != 16 * 64 + 16) return false;
   if ((long long)s.H * s.W * s.C >= (1ll << 30)) return false;
@@ -697,12 +770,15 @@ bool tile_block_supports(const Shape& s) {
 }
 
 hipError_t launch_attend_tile_block(const void* q, const void* k, const void* v, const uint32_t* wpk,
-                                    const void* b, const int32_t* route, const float* kn, const void* wo,
-                                    const void* bo, const Shape& s, void* y, hipStream_t st) {
+                                    const void* b, const float* qr, const float* kr, int32_t* route_out,
+                                    const float* kn, const void* wo, const void* bo, const Shape& s, void* y,
+                                    hipStream_t st) {
   TileArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
-  a.wpk = wpk; a.b = (const uint16_t*)b; a.route = route; a.kn = kn; a.out = (uint16_t*)y;
+  a.wpk = wpk; a.b = (const uint16_t*)b; a.route = route_out; a.kn = kn; a.out = (uint16_t*)y;
   a.wo = (const uint16_t*)wo; a.bo = (const uint16_t*)bo;
+  a.qr = qr; a.kr = kr; a.route_out = route_out;
+  a.rscale = (float)(1.0 / __builtin_sqrt((double)s.C));
   a.N = s.N; a.H = s.H; a.W = s.W; a.C = s.C; a.heads = s.heads; a.S = s.S; a.topk = s.topk;
   a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
   switch (s.rh * 64 + s.rw) {
@@ -712,13 +788,18 @@ hipError_t launch_attend_tile_block(const void* q, const void* k, const void* v,
   }
 }
 
+// Routes: given (route), or, with qr and kr (the region means; S*S <= 64),
+// chosen in the kernel and written to route_out.
 hipError_t launch_attend_tile(const void* q, const void* k, const void* v, const uint32_t* wpk,
                               const void* b, const int32_t* route, const float* kn, const Shape& s,
-                              void* out, hipStream_t st) {
+                              void* out, hipStream_t st, const float* qr, const float* kr,
+                              int32_t* route_out) {
   TileArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.wpk = wpk; a.b = (const uint16_t*)b; a.route = route; a.kn = kn; a.out = (uint16_t*)out;
   a.wo = nullptr; a.bo = nullptr;
+  a.qr = qr; a.kr = kr; a.route_out = route_out;
+  a.rscale = (float)(1.0 / __builtin_sqrt((double)s.C));
   a.N = s.N; a.H = s.H; a.W = s.W; a.C = s.C; a.heads = s.heads; a.S = s.S; a.topk = s.topk;
   a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
   switch (s.rh * 64 + s.rw) {
