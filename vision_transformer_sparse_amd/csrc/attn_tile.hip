@@ -221,8 +221,9 @@ __host__ __device__ inline TileLds tile_lds(int SR, int RW, int topk, int HG, in
   return l;
 }
 
-template <int RH, int RW, int HG>
+template <int RH, int RW, int HG, bool WO>
 __global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(TileArgs a) {
+  static_assert(!WO || HG > 1, "the output projection needs every head of the region in the workgroup");
   constexpr int T = RH * RW;
   constexpr int WAVES = kTileWaves;  // waves of one head
   constexpr int NT = 64 * WAVES;     // threads of one head
@@ -256,14 +257,15 @@ __global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(Tile
 
   // XCD-aware numbering: consecutive units (n, r, h, slab) share blockIdx %
   // 8, so the slabs and heads of a region -- the same K/V cache lines -- are
-  // read through one XCD's L2. (HG > 1: units (n, r, slab), the head from
-  // the wave.)
-  const int units = a.N * R * (HG == 1 ? a.heads : 1) * SLABS;
+  // read through one XCD's L2. (HG > 1: units (n, r, group of HG heads,
+  // slab), the head within the group from the wave.)
+  const int groups = a.heads / HG;
+  const int units = a.N * R * groups * SLABS;
   const int per = (units + 7) / 8;
   const int u = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
   if (u >= units) return;  // the whole workgroup leaves together
   const int slab = u % SLABS, hu = u / SLABS;
-  const int h = HG == 1 ? hu % a.heads : hw, nr = HG == 1 ? hu / a.heads : hu;
+  const int h = (hu % groups) * HG + hw, nr = hu / groups;
   const int n = nr / R, r = nr - n * R;
   const int jr = r / S, ir = r - jr * S;
   const int y0 = jr * RH + slab * SR, x0 = ir * RW;  // the slab's first query row and column
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(Tile
       }
       if (lane < R && rank < topk) {
         sel[rank] = lane;
-        if (slab == 0 && (HG > 1 || h == 0)) a.route_out[(size_t)nr * topk + rank] = lane;
+        if (slab == 0 && h == 0) a.route_out[(size_t)nr * topk + rank] = lane;
       }
     }
     __syncthreads();
@@ -586,11 +588,11 @@ __global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(Tile
     if (htid < 240) *reinterpret_cast<uint4*>(wts + (htid >> 3) * 32 + (htid & 7) * 4) = wreg;
     __syncthreads();
   }
-  // HG > 1: the output projection's A operands, loaded now so that they land
+  // WO: the output projection's A operands, loaded now so that they land
   // during the LCE: rows 32h + 16 ot + col of wo, input channels of head g in
   // the B operand's order (4 grp .. +3, then 16 + 4 grp .. +3)
-  uint2 wa[HG > 1 ? 2 : 1][HG][2];
-  if constexpr (HG > 1) {
+  uint2 wa[WO ? 2 : 1][HG][2];
+  if constexpr (WO) {
 #pragma unroll
     for (int ot = 0; ot < 2; ++ot)
 #pragma unroll
@@ -668,7 +670,7 @@ __global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(Tile
     const uint32_t oo = (uint32_t)(((y0 + ty) * W + x0 + tx) * C + h * 32) * 2;
     __builtin_amdgcn_raw_buffer_store_b128(w4, ob, oo + 16 * grp, 0, kNt);
   };
-  uint4 oq[QBW];  // HG > 1: the rounded output, a B operand of the projection
+  uint4 oq[QBW];  // WO: the rounded output, a B operand of the projection
 #pragma unroll
   for (int i = 0; i < QBW; ++i) {
     const float inv = 1.0f / ls[i][0];
@@ -677,12 +679,12 @@ __global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(Tile
     lo.y = float_to_bf16_bits(fmaf(o0[i][2], inv, acc[i][2])) | (float_to_bf16_bits(fmaf(o0[i][3], inv, acc[i][3])) << 16);
     hi.x = float_to_bf16_bits(fmaf(o1[i][0], inv, acc[i][4])) | (float_to_bf16_bits(fmaf(o1[i][1], inv, acc[i][5])) << 16);
     hi.y = float_to_bf16_bits(fmaf(o1[i][2], inv, acc[i][6])) | (float_to_bf16_bits(fmaf(o1[i][3], inv, acc[i][7])) << 16);
-    if constexpr (HG == 1)
+    if constexpr (!WO)
       store_slice(lo, hi, ty0 + i);
     else
       oq[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
-  if constexpr (HG > 1) {
+  if constexpr (WO) {
     // ---- output projection: y^T (32 output channels of head h's slice x
     // 16 queries) = sum over heads g of Wo[:, head g] . o_g^T, the o_g of
     // the same queries from the exchange (wave wv of every head holds the
@@ -731,12 +733,12 @@ __global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(Tile
   }
 }
 
-template <int RH, int RW, int HG>
+template <int RH, int RW, int HG, bool WO>
 hipError_t launch_t(const TileArgs& a, hipStream_t st) {
-  const int units = a.N * a.S * a.S * (HG == 1 ? a.heads : 1) * tile_slabs<RH, RW>();
+  const int units = a.N * a.S * a.S * (a.heads / HG) * tile_slabs<RH, RW>();
   const unsigned blocks = (unsigned)(((units + 7) / 8) * 8);
   constexpr int threads = 64 * kTileWaves * HG;
-  launch((attn_tile_kernel<RH, RW, HG>), dim3(blocks), dim3(threads),
+  launch((attn_tile_kernel<RH, RW, HG, WO>), dim3(blocks), dim3(threads),
          tile_lds(RH / tile_slabs<RH, RW>(), RW, a.topk, HG, tile_qbw<RH, RW>()).total, st, a);
   return hipGetLastError();
 }
@@ -782,8 +784,8 @@ hipError_t launch_attend_tile_block(const void* q, const void* k, const void* v,
   a.N = s.N; a.H = s.H; a.W = s.W; a.C = s.C; a.heads = s.heads; a.S = s.S; a.topk = s.topk;
   a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
   switch (s.rh * 64 + s.rw) {
-    case 8 * 64 + 8: return launch_t<8, 8, 2>(a, st);
-    case 16 * 64 + 16: return launch_t<16, 16, 2>(a, st);
+    case 8 * 64 + 8: return launch_t<8, 8, 2, true>(a, st);
+    case 16 * 64 + 16: return launch_t<16, 16, 2, true>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -803,10 +805,10 @@ hipError_t launch_attend_tile(const void* q, const void* k, const void* v, const
   a.N = s.N; a.H = s.H; a.W = s.W; a.C = s.C; a.heads = s.heads; a.S = s.S; a.topk = s.topk;
   a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
   switch (s.rh * 64 + s.rw) {
-    case 8 * 64 + 8: return launch_t<8, 8, 1>(a, st);
-    case 16 * 64 + 16: return launch_t<16, 16, 1>(a, st);
-    case 8 * 64 + 16: return launch_t<8, 16, 1>(a, st);
-    case 16 * 64 + 8: return launch_t<16, 8, 1>(a, st);
+    case 8 * 64 + 8: return launch_t<8, 8, 1, false>(a, st);
+    case 16 * 64 + 16: return launch_t<16, 16, 1, false>(a, st);
+    case 8 * 64 + 16: return launch_t<8, 16, 1, false>(a, st);
+    case 16 * 64 + 8: return launch_t<16, 8, 1, false>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
