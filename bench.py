@@ -292,6 +292,15 @@ class Workload:
         self.step = step
 
 
+def attn_share(prof, steps: int) -> float:
+    """The fraction of a step's work one attention launch does: a step of
+    the per-head routing variant launches the attention kernel once per head
+    where it runs the operator per head, once where one kernel routes every
+    head."""
+    cnt = prof.get("attn", (0.0, 0))[1]
+    return steps / cnt if cnt else 1.0
+
+
 def kernel_rooflines(prof, cfg, share=1.0, backward=False, fused_block=False):
     kernels = {}
     for kind, (ms, cnt) in prof.items():
@@ -311,7 +320,6 @@ def measure_config(w, flush, n_warm, n_cold):
     from vision_transformer_sparse_amd import bra
 
     cfg = w.cfg
-    share = 1.0 / cfg.heads if w.op == "head_routed" else 1.0
     bwd = w.op == "backward"
     fb = w.fused
     for _ in range(n_warm // 2):
@@ -323,9 +331,12 @@ def measure_config(w, flush, n_warm, n_cold):
     torch.cuda.synchronize()
     warm_ms = (time.perf_counter() - t0) * 1e3 / n_warm
     bra.profile_begin(bra.KERNEL_NAMES)
-    for _ in range(max(20, n_warm // 4)):
+    nprof = max(20, n_warm // 4)
+    for _ in range(nprof):
         w.step()
-    kernels = kernel_rooflines(bra.profile_read(), cfg, share, bwd, fb)
+    prof = bra.profile_read()
+    share = attn_share(prof, nprof)
+    kernels = kernel_rooflines(prof, cfg, share, bwd, fb)
     bra.profile_begin(())
     # cold: a 1 GiB write before each step; events around the step (torch's
     # current stream, which the binding hands to the library) and around the
@@ -457,11 +468,13 @@ def main(argv=None) -> int:
 
     # every kernel kind, in a separate (untimed) pass
     bra.profile_begin(bra.KERNEL_NAMES)
-    for _ in range(max(10, a.steps // 4)):
+    nprof = max(10, a.steps // 4)
+    for _ in range(nprof):
         step()
-    share = 1.0 / cfg.heads if head.op == "head_routed" else 1.0
+    prof = bra.profile_read()
+    share = attn_share(prof, nprof)
     bwd = head.op == "backward"
-    kernels = kernel_rooflines(bra.profile_read(), cfg, share, bwd, head.fused)
+    kernels = kernel_rooflines(prof, cfg, share, bwd, head.fused)
     bra.profile_begin(())
 
     if a.calib_copy_mb > 0:

@@ -57,7 +57,8 @@ def run_head_routed(bra, inp, heads, S, topk, dtype, name):
 
 
 # (N, H, W, C, heads, S, topk, dtype): ragged region counts, topk = 1 and S^2,
-# 4x4, 8x8 and 16x16 regions, fp32 and bf16
+# 4x4, 8x8 and 16x16 regions, fp32 and bf16; the bf16 8x8 / 16x16 cases with
+# S*S <= 64 run the one-pass path (the attention kernel routes each head)
 CASES = [
     (2, 16, 16, 64, 2, 4, 3, "bf16"),
     (1, 12, 12, 96, 3, 3, 9, "f32"),
@@ -65,6 +66,8 @@ CASES = [
     (1, 32, 32, 64, 2, 2, 1, "f32"),
     (1, 40, 40, 64, 2, 5, 2, "bf16"),
     (2, 14, 14, 96, 3, 7, 16, "bf16"),
+    (1, 32, 32, 96, 3, 2, 2, "bf16"),
+    (1, 24, 24, 64, 2, 3, 9, "bf16"),
 ]
 
 
@@ -96,3 +99,17 @@ def test_head_routed_one_head_equals_forward(gpu_lib):
     o2, r2 = gpu_lib.forward(*args, 1, S, topk)
     torch.cuda.synchronize()
     assert torch.equal(r1[:, 0], r2) and torch.equal(o1, o2)
+
+
+def test_head_routed_one_pass_launches(gpu_lib):
+    """On the large-region shapes with S*S <= 64 the variant is one pooling
+    and one attention launch (no per-head copies or launches)."""
+    cfg = CONFIGS[4]
+    inp = draw_config(cfg, N=2)
+    args = [dev(inp[x], "bf16") for x in ("q", "k", "v", "lce_w", "lce_b")]
+    say("head-routed launches")
+    gpu_lib.profile_begin()
+    gpu_lib.forward_head_routed(*args, cfg.heads, cfg.S, cfg.topk)
+    rec = gpu_lib.profile_read()
+    gpu_lib.profile_begin(())
+    assert rec["pool"][1] == 1 and rec["attn"][1] == 1 and rec["route"][1] == 0

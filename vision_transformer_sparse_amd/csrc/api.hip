@@ -68,7 +68,7 @@ hipError_t launch_attend_dense(const void* q, const void* k, const void* v, cons
 hipError_t launch_attend_tile(const void* q, const void* k, const void* v, const uint32_t* wpk,
                               const void* b, const int32_t* route, const float* kn, const Shape& s,
                               void* out, hipStream_t st, const float* qr = nullptr, const float* kr = nullptr,
-                              int32_t* route_out = nullptr);
+                              int32_t* route_out = nullptr, bool head_routes = false);
 bool tile_kernel_routes(const Shape& s);
 size_t lce_pack_bytes(int C);
 hipError_t launch_lce_pack(const void* w, int C, uint32_t* wpk, hipStream_t st);
@@ -568,11 +568,38 @@ int bra_forward_head_routed(const void* q, const void* k, const void* v, const v
   bra::Shape s;
   int rc = check_forward(q, k, v, lce_w, lce_b, N, H, W, C, heads, S, topk, dtype, out, route_idx, &s);
   if (rc) return rc;
-  // one head of the batch: the operator on 32 channels with one head
+  hipStream_t st = g_stream;
+  // bf16 shapes of the large-region kernel with S*S <= 64: one pooling pass
+  // over all channels, then the attention kernel routes every (region, head)
+  // on the head's slice of the means
+  if (dtype == BRA_BF16 && !bra::image_kernel_supports(s) && !bra::region_kernel_supports(s) &&
+      bra::tile_kernel_supports(s) && bra::tile_kernel_routes(s)) {
+    const WsLayout wl = ws_layout(N, C, S);
+    std::lock_guard<std::mutex> lk(g_ws_mutex);
+    void* ws = nullptr;
+    rc = workspace(wl.total, &ws);
+    if (rc) return rc;
+    float* qr = static_cast<float*>(ws);
+    float* kr = qr + (size_t)N * s.R * C;
+    float* kn = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.kn);
+    uint32_t* wpk = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + wl.wpk);
+    hipError_t e;
+    {
+      ProfScope ps(BRA_K_POOL, st);
+      e = bra::launch_region_pool(q, k, s, dtype, qr, kr, lce_w, wpk, kn, st);
+    }
+    if (e != hipSuccess) return hip_fail(e);
+    {
+      ProfScope ps(BRA_K_ATTN, st);
+      e = bra::launch_attend_tile(q, k, v, wpk, lce_b, route_idx, kn, s, out, st, qr, kr, route_idx, true);
+    }
+    return e == hipSuccess ? BRA_OK : hip_fail(e);
+  }
+  // otherwise each head of the batch as the operator on 32 channels with
+  // one head
   bra::Shape sh;
   rc = check_dims(N, H, W, bra::kHeadDim, 1, S, topk, dtype, true, true, &sh);
   if (rc) return rc;
-  hipStream_t st = g_stream;
   const size_t esz = dtype == BRA_BF16 ? 2 : 4;
   const long long tokens = (long long)N * H * W;
   const size_t per_head = (size_t)tokens * bra::kHeadDim * esz;  // one head's tensor, bytes

@@ -161,7 +161,10 @@ struct TileArgs {
   const float* qr;
   const float* kr;
   int32_t* route_out;
-  float rscale;  // C^-1/2, the affinity's scale
+  float rscale;    // the affinity's scale: C^-1/2, or head_dim^-1/2 with head_routes
+  int head_routes;  // each head routes on its own channels: logits over the
+                    // head's 32-channel slice of the means, route_out
+                    // [N][heads][S*S][topk]
   uint16_t* out;
   int N, H, W, C, heads, S, topk;
   float qscale;  // head_dim^-1/2 * log2(e)
@@ -337,8 +340,11 @@ __global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(Tile
   // route_kernel, so the same logits bit for bit; wave w takes regions
   // 16w .. 16w+15, its tile's row 0 is region r), then wave 0 ranks the R
   // keys (larger logit first, ties to the lower index) and region r's top-k
-  // go to LDS and, from one workgroup of the region, to route_out. The
-  // scratch is the halo staging, unused until the first tile step.
+  // go to LDS and, from one workgroup of the region, to route_out. With
+  // head_routes the logits run over the head's own 32 channels (the same
+  // steps as the route kernel over a one-head, 32-channel input) and every
+  // head reports its routes. The scratch is the halo staging, unused until
+  // the first tile step.
   int32_t* sel = reinterpret_cast<int32_t*>(smem + lay.raw + 256);  // [topk] chosen regions
   if (a.qr) {
     float* lrow = reinterpret_cast<float*>(smem + lay.raw);            // [64] logits of region r
@@ -346,7 +352,10 @@ __global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(Tile
     if (wave < (R + 15) / 16) {
       const uint32_t mbytes = (uint32_t)R * C * 4;
       const Rsrc qm = rsrc(a.qr + (size_t)n * R * C, mbytes), km = rsrc(a.kr + (size_t)n * R * C, mbytes);
-      const uint32_t qrow = (uint32_t)r * C * 4, krow = (uint32_t)min(16 * wave + col, R - 1) * C * 4;
+      const uint32_t cbase = a.head_routes ? (uint32_t)h * 128 : 0u;  // the head's first channel, bytes
+      const int CR = a.head_routes ? 32 : C;                           // channels of the logits
+      const uint32_t qrow = (uint32_t)r * C * 4 + cbase;
+      const uint32_t krow = (uint32_t)min(16 * wave + col, R - 1) * C * 4 + cbase;
       // route::logit_tile_x3's steps in its order (hi.lo + lo.hi + hi.hi per
       // 32 channels), two steps' operands in flight at once
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -360,9 +369,9 @@ __global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(Tile
         route::split_bf16(fb, bh, bl);
         acc = route::logit_step_x3(acc, ah, al, bh, bl);
       };
-      for (int k0 = 0; k0 < C; k0 += 64) {
+      for (int k0 = 0; k0 < CR; k0 += 64) {
         const uint32_t c = (uint32_t)(k0 + 8 * grp) * 4;
-        const bool two = k0 + 32 < C;  // C % 32 == 0
+        const bool two = k0 + 32 < CR;  // CR % 32 == 0
         const uint4 a0 = ld16(qm, qrow + c), a1 = ld16(qm, qrow + c + 16);
         const uint4 b0 = ld16(km, krow + c), b1 = ld16(km, krow + c + 16);
         const uint4 a2 = ld16(qm, two ? qrow + c + 128 : kOut), a3 = ld16(qm, two ? qrow + c + 144 : kOut);
@@ -387,7 +396,10 @@ __global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(Tile
       }
       if (lane < R && rank < topk) {
         sel[rank] = lane;
-        if (slab == 0 && h == 0) a.route_out[(size_t)nr * topk + rank] = lane;
+        if (slab == 0 && (a.head_routes || h == 0)) {
+          const size_t row = a.head_routes ? ((size_t)n * a.heads + h) * R + r : (size_t)nr;
+          a.route_out[row * topk + rank] = lane;
+        }
       }
     }
     __syncthreads();
@@ -780,6 +792,7 @@ hipError_t launch_attend_tile_block(const void* q, const void* k, const void* v,
   a.wpk = wpk; a.b = (const uint16_t*)b; a.route = route_out; a.kn = kn; a.out = (uint16_t*)y;
   a.wo = (const uint16_t*)wo; a.bo = (const uint16_t*)bo;
   a.qr = qr; a.kr = kr; a.route_out = route_out;
+  a.head_routes = 0;
   a.rscale = (float)(1.0 / __builtin_sqrt((double)s.C));
   a.N = s.N; a.H = s.H; a.W = s.W; a.C = s.C; a.heads = s.heads; a.S = s.S; a.topk = s.topk;
   a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
@@ -791,17 +804,19 @@ hipError_t launch_attend_tile_block(const void* q, const void* k, const void* v,
 }
 
 // Routes: given (route), or, with qr and kr (the region means; S*S <= 64),
-// chosen in the kernel and written to route_out.
+// chosen in the kernel and written to route_out -- per head with
+// head_routes (route_out [N][heads][S*S][topk]).
 hipError_t launch_attend_tile(const void* q, const void* k, const void* v, const uint32_t* wpk,
                               const void* b, const int32_t* route, const float* kn, const Shape& s,
                               void* out, hipStream_t st, const float* qr, const float* kr,
-                              int32_t* route_out) {
+                              int32_t* route_out, bool head_routes) {
   TileArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.wpk = wpk; a.b = (const uint16_t*)b; a.route = route; a.kn = kn; a.out = (uint16_t*)out;
   a.wo = nullptr; a.bo = nullptr;
   a.qr = qr; a.kr = kr; a.route_out = route_out;
-  a.rscale = (float)(1.0 / __builtin_sqrt((double)s.C));
+  a.head_routes = head_routes ? 1 : 0;
+  a.rscale = (float)(1.0 / __builtin_sqrt((double)(head_routes ? s.hd : s.C)));
   a.N = s.N; a.H = s.H; a.W = s.W; a.C = s.C; a.heads = s.heads; a.S = s.S; a.topk = s.topk;
   a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
   switch (s.rh * 64 + s.rw) {
