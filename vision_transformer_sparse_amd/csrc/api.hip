@@ -152,15 +152,17 @@ struct ProfScope {
       // device-scope release: no L2 write-back to memory is timed with the kernel
       if (hipEventCreateWithFlags(&a, hipEventReleaseToDevice) != hipSuccess) return;
       if (hipEventCreateWithFlags(&b, hipEventReleaseToDevice) != hipSuccess) {
-        hipEventDestroy(a);
+        (void)hipEventDestroy(a);
         return;
       }
       rec.start.push_back(a);
       rec.stop.push_back(b);
     }
     slot = rec.used++;
+    // (a record that fails leaves its pair unrecorded: bra_profile_read then
+    // returns that HIP error instead of a time)
     if (span) {
-      hipEventRecord(rec.start[slot], st);
+      (void)hipEventRecord(rec.start[slot], st);
       return;
     }
     bra::ProfEvents& pe = bra::prof_events();
@@ -171,13 +173,13 @@ struct ProfScope {
     if (slot < 0) return;
     if (span) {
       std::lock_guard<std::mutex> lk(g_prof_mutex);
-      hipEventRecord(g_prof[kind].stop[slot], st);
+      (void)hipEventRecord(g_prof[kind].stop[slot], st);
       return;
     }
     bra::ProfEvents& pe = bra::prof_events();
     if (pe.start) {
-      hipEventRecord(pe.start, st);
-      hipEventRecord(pe.stop, st);
+      (void)hipEventRecord(pe.start, st);
+      (void)hipEventRecord(pe.stop, st);
       pe.start = pe.stop = nullptr;
     }
   }
