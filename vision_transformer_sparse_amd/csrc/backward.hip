@@ -558,7 +558,9 @@ __global__ __launch_bounds__(256) void lce_grad_rows_kernel(const uint16_t* __re
                                                             float* __restrict__ dv_lce) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   const int YB = (H + kLceRows - 1) / kLceRows, CB = C / kLceCh;
-  int u = blockIdx.x;
+  // consecutive units -- the CB channel blocks of one row block, which read
+  // the same 128-byte pixel lines 16 bytes each -- share an XCD and its L2
+  int u = xcd_unit((int)blockIdx.x, (int)gridDim.x);
   const int cb = u % CB;
   u /= CB;
   const int yb = u % YB, n = u / YB;
