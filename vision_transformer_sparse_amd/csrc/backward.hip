@@ -311,7 +311,11 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_query_kernel(BwdArgs a) {
     }
   }
 
-  // pass 2: dQ^T += K^T dS^T
+  // pass 2: dQ^T += K^T dS^T. The dP products start from -D, so
+  // dS = P * dP' takes no subtraction. (The scores are scaled in fp32: a
+  // query rounded to bf16 after scaling, as the forward's large-region
+  // kernel takes it, moves P by up to ~2^-9 |score| relative, which dS
+  // passes on to the gradients undamped.)
   f32x4 dqt[QB][2];
 #pragma unroll
   for (int b = 0; b < QB; ++b) dqt[b][0] = dqt[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -327,13 +331,13 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_query_kernel(BwdArgs a) {
 #pragma unroll
         for (int b = 0; b < QB; ++b) {
           const f32x4 sc = mfma(ka, bq[b], f32x4{0.f, 0.f, 0.f, 0.f});
-          const f32x4 dp = mfma(vb, bg[b], f32x4{0.f, 0.f, 0.f, 0.f});
+          const f32x4 dp = mfma(vb, bg[b], f32x4{-D[b], -D[b], -D[b], -D[b]});
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float p = __builtin_amdgcn_exp2f(fmaf(sc[i], kQs, -lse[b]));
             if constexpr (!FULL)
               if (u0 + 32 * ks + 16 * j + 4 * g + i >= a.L) p = 0.f;
-            ds[b][j][i] = (__bf16)(p * (dp[i] - D[b]));
+            ds[b][j][i] = (__bf16)(p * dp[i]);
           }
         }
       }
@@ -368,15 +372,17 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_query_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- key side
+// (8 waves: at most 128 VGPRs, so two workgroups share a CU; the few values
+// this spills are the epilogue's and the tile loader's, not the products')
 template <int WAVES, int TQ, int KB, bool FULL>
-__global__ __launch_bounds__(64 * WAVES) void bwd_key_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 4 : 1) void bwd_key_kernel(BwdArgs a) {
   // FULL: every query tile is whole (T a multiple of TQ), so no query is masked
   // KB 16-key blocks a wave: every Q / G / Q^T / G^T operand read from LDS
   // serves all of them
   constexpr int TH = 64 * WAVES;
   __shared__ __attribute__((aligned(16))) char lds[2 * TQ * 64];  // Q tile | G tile
-  __shared__ __attribute__((aligned(16))) float st_lse[TQ];
-  __shared__ __attribute__((aligned(16))) float st_d[TQ];
+  __shared__ __attribute__((aligned(16))) float st_lse[TQ];  // LSE of the staged queries
+  __shared__ __attribute__((aligned(16))) float st_d[TQ];    // D of the staged queries
   __shared__ int routers[1024];  // the regions routing to s, ascending
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, g = lane >> 4;
