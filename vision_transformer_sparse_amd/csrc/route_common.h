@@ -242,10 +242,16 @@ __device__ __forceinline__ void rank_rows(const float* logit, int RP, int R, int
 
 // ---- one 16-row block of an image's routes (R <= 64) ----------------------
 __host__ __device__ inline int col_tiles(int R) { return (R + 15) / 16; }
-// LDS of route_block: the logit block [16][16 col_tiles], then a [4][64]
-// key buffer per wave
-__host__ __device__ inline size_t route_block_lds(int R, int waves) {
-  return (size_t)16 * 16 * col_tiles(R) * sizeof(float) + (size_t)waves * 4 * 64 * sizeof(uint64_t);
+// The block's 16 query rows are staged in LDS once (row pitch C + 4 floats,
+// so the 16 rows a tile column reads fall on different banks) where they fit:
+// otherwise every wave would fetch all of them again from L2 for its column
+// tile. The operand values, and so the logits, are the same either way.
+constexpr int kRouteStageC = 512;
+// LDS of route_block: the logit block [16][16 col_tiles], a [4][64] key
+// buffer per wave, then (C <= kRouteStageC) the query rows [16][C + 4]
+__host__ __device__ inline size_t route_block_lds(int R, int C, int waves) {
+  return (size_t)16 * 16 * col_tiles(R) * sizeof(float) + (size_t)waves * 4 * 64 * sizeof(uint64_t) +
+         (C <= kRouteStageC ? (size_t)16 * (C + 4) * sizeof(float) : 0);
 }
 // Routes of query rows r0 .. r0+15 (those below R) of image n, from the
 // image's fp32 region means qr_img, kr_img ([R][C]), written to
@@ -259,15 +265,40 @@ __device__ __forceinline__ void route_block(const float* qr_img, const float* kr
   const int CT = col_tiles(R), RP = 16 * CT;  // padded logit row
   float* logit = reinterpret_cast<float*>(smem);                   // [16][RP]
   uint64_t* keys = reinterpret_cast<uint64_t*>(logit + 16 * RP);   // [waves][4][64]
+  float* qrows = reinterpret_cast<float*>(keys + (size_t)waves * 4 * 64);  // [16][C + 4]
+  const bool staged = C <= kRouteStageC;
   const int col = lane & 15, grp = lane >> 4;
   const uint32_t img_bytes = (uint32_t)R * C * 4;
   const Rsrc qb = rsrc(qr_img, img_bytes), kb = rsrc(kr_img, img_bytes);
   const uint32_t qrow = (uint32_t)min(r0 + col, R - 1) * C * 4;
   __syncthreads();
+  if (staged) {
+    const int cp = C / 4, pieces = 16 * cp;  // 16-byte pieces of the rows
+    const int tid = wave * 64 + lane, nt = waves * 64;
+    for (int e0 = tid; e0 < pieces; e0 += 4 * nt) {
+      uint4 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = e0 + i * nt, row = e / cp, c4 = e - row * cp;
+        v[i] = ld16(qb, e < pieces ? (uint32_t)min(r0 + row, R - 1) * C * 4 + (uint32_t)c4 * 16 : kOut);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = e0 + i * nt, row = e / cp, c4 = e - row * cp;
+        if (e < pieces) *reinterpret_cast<uint4*>(qrows + (size_t)row * (C + 4) + 4 * c4) = v[i];
+      }
+    }
+    __syncthreads();
+  }
+  const float* qlds = qrows + (size_t)col * (C + 4);
   for (int ct = wave; ct < CT; ct += waves) {
     const uint32_t krow = (uint32_t)min(16 * ct + col, R - 1) * C * 4;
     const f32x4 acc = logit_tile_x3(
-        grp, C, [&](int c) { return ld16(qb, c < C ? qrow + 4 * c : kOut); },
+        grp, C,
+        [&](int c) {
+          if (staged) return c < C ? *reinterpret_cast<const uint4*>(qlds + c) : uint4{0u, 0u, 0u, 0u};
+          return ld16(qb, c < C ? qrow + 4 * c : kOut);
+        },
         [&](int c) { return ld16(kb, c < C ? krow + 4 * c : kOut); });
     // lane (col, grp) holds rows 4grp..4grp+3 of the tile at column col
 #pragma unroll

@@ -84,7 +84,7 @@ hipError_t launch_small(const float* qr, const float* kr, int N, int R, int C, i
                         int32_t* route, hipStream_t st) {
   const float scale = (float)(1.0 / __builtin_sqrt((double)C));
   const unsigned blocks = (unsigned)(N * col_tiles(R));
-  launch(route_kernel, dim3(blocks), dim3(64 * col_tiles(R)), route_block_lds(R, col_tiles(R)), st, qr, kr, R, C,
+  launch(route_kernel, dim3(blocks), dim3(64 * col_tiles(R)), route_block_lds(R, C, col_tiles(R)), st, qr, kr, R, C,
          topk, scale, route);
   return hipGetLastError();
 }
