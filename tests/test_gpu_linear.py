@@ -142,6 +142,36 @@ def test_linear_rejects_bad_shapes(gpu_lib):
         gpu_lib.linear(x, w, None)                      # bf16 K > 256
 
 
+def test_block_rejects_bad_arguments(gpu_lib):
+    """bra_block_forward's checks return their codes before any launch and
+    leave the outputs untouched: a missing weight, an unsupported width, a
+    misaligned output, topk above S^2."""
+    import ctypes
+    import torch
+    lib = gpu_lib.load()
+    N, H, C, heads, S, topk = 1, 16, 64, 2, 2, 2
+    dt = torch.bfloat16
+    x = torch.zeros((N, H, H, C), dtype=dt, device="cuda")
+    wqkv = torch.zeros((3 * C, C), dtype=dt, device="cuda")
+    wo = torch.zeros((C, C), dtype=dt, device="cuda")
+    lw = torch.zeros((C, 5, 5), dtype=dt, device="cuda")
+    y = torch.full((N, H, H, C + 8), 3.0, dtype=dt, device="cuda")
+    route = torch.full((N, S * S, topk), -9, dtype=torch.int32, device="cuda")
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    say("block argument checks")
+
+    def call(xp, wq, wop, yp, c=C, h=heads, k=topk):
+        return lib.bra_block_forward(xp, wq, None, p(lw), None, wop, None, N, H, H, c, h, S, k, 1, yp,
+                                     p(route))
+    # codes of include/bra.h: -1 NULL, -3 TOPK, -5 UNSUPPORTED, -8 ALIGN
+    assert call(p(x), None, p(wo), p(y)) == -1                               # no qkv weight
+    assert call(p(x), p(wqkv), p(wo), ctypes.c_void_p(y.data_ptr() + 8)) == -8  # y not 16-byte aligned
+    assert call(p(x), p(wqkv), p(wo), p(y), k=S * S + 1) == -3              # topk > S^2
+    assert call(p(x), p(wqkv), p(wo), p(y), c=288, h=9) == -5               # bf16 C > 256
+    torch.cuda.synchronize()
+    assert bool((y == 3.0).all()) and bool((route == -9).all())
+
+
 def run_block(bra, d, heads, S, topk, dtype, images=None, name=""):
     x = d["x"]
     say(name, "block", x.shape, f"heads={heads} S={S} topk={topk} {dtype}")

@@ -274,13 +274,14 @@ def test_host_pointer_rejected(gpu_lib):
     assert lib.bra_lce(hp, hp, None, 1, 8, 8, 32, 0, hp) == -7
 
 
-@pytest.mark.parametrize("ci,pools,routes", [(3, 3, 3), (2, 3, 3), (4, 3, 0), (1, 0, 0)])
+@pytest.mark.parametrize("ci,pools,routes", [(3, 3, 3), (2, 3, 3), (4, 3, 0), (0, 3, 0), (1, 0, 0)])
 def test_profile_counts(gpu_lib, ci, pools, routes):
     """Launches per forward: pool, route and attention for 8x8 regions with
     S*S = 256 (the detection shape) and for 2x2 regions (the 14x14 stage);
-    with 16x16 regions and S*S <= 64 (the segmentation shape) the attention
-    kernel chooses its region's routes itself, so no route kernel runs; with
-    4x4 regions (the 28x28 stage) one kernel pools, routes and attends."""
+    with S*S <= 64 the attention kernels of 16x16 regions (the segmentation
+    shape) and of fp32 8x8 regions (the 56x56 stage) choose their regions'
+    routes themselves, so no route kernel runs; with 4x4 regions (the 28x28
+    stage) one kernel pools, routes and attends."""
     cfg = CONFIGS[ci]
     inp = draw_config(cfg, N=4)
     args = [dev(inp[x], cfg.dtype) for x in ("q", "k", "v", "lce_w", "lce_b")]

@@ -43,9 +43,13 @@ hipError_t launch_linear(const void* x, const void* w, const void* b, int M, int
                          int split, int dtype, void* y0, void* y1, void* y2, hipStream_t st);
 bool tile_kernel_supports(const Shape& s);
 bool f32_kernel_supports(const Shape& s);
+// Routes given (route), or chosen in the kernel from the region means qr, kr
+// (f32_kernel_routes) and written to route_out
 hipError_t launch_attend_f32(const void* q, const void* k, const void* v, const void* w,
                              const void* b, const int32_t* route, const Shape& s, void* out,
-                             hipStream_t st);
+                             hipStream_t st, const float* qr = nullptr, const float* kr = nullptr,
+                             int32_t* route_out = nullptr);
+bool f32_kernel_routes(const Shape& s);
 // kn: max |k|^2 per (image, region, head) from the pool kernel, or null
 // The backward for given routes (backward.hip): bf16, head_dim 32, regions of
 // a multiple of 16 tokens, topk <= 16
@@ -378,6 +382,12 @@ int forward_staged(const void* q, const void* k, const void* v, const void* lce_
     // route kernel's logits, bit for bit) and reports the routes
     ProfScope ps(BRA_K_ATTN, st);
     e = bra::launch_attend_tile(q, k, v, wpk, lce_b, route_idx, kn, s, out, st, qr, kr, route_idx);
+    return e == hipSuccess ? BRA_OK : hip_fail(e);
+  }
+  if (dtype == BRA_F32 && bra::f32_kernel_routes(s)) {
+    // so does the fp32 kernel
+    ProfScope ps(BRA_K_ATTN, st);
+    e = bra::launch_attend_f32(q, k, v, lce_w, lce_b, route_idx, s, out, st, qr, kr, route_idx);
     return e == hipSuccess ? BRA_OK : hip_fail(e);
   }
   {

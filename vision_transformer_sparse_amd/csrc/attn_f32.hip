@@ -19,6 +19,7 @@
 // in LDS ((RH+4) x (RW+4) pixels x the head's 32 channels, zero outside the
 // image) with the head's weights staged tap-major.
 #include "bra_internal.h"
+#include "route_common.h"
 
 namespace bra {
 namespace {
@@ -39,6 +40,12 @@ struct F32Args {
   float* out;
   int N, H, W, C, heads, S, topk, rh, rw;
   float qscale;         // head_dim^-1/2 * log2(e)
+  // routes chosen in the kernel (f32_kernel_routes): the region means
+  // [N][S*S][C], where the first head's workgroups report the routes, C^-1/2
+  const float* qr;
+  const float* kr;
+  int32_t* route_out;
+  float rscale;
 };
 
 constexpr int kHaloStride = 36;  // floats per halo pixel: 32 channels + 4 (banks)
@@ -46,14 +53,17 @@ constexpr int kVStride = 33;     // floats per staged V row: 32 dims + 1 (banks)
 
 __host__ __device__ constexpr size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 struct F32Lds {
-  size_t halo, vs, wt, total;
+  size_t halo, vs, wt, rt, total;
 };
+// (the in-kernel routing borrows the V staging area for its logits and keys
+// before the key loop; the chosen routes keep rt, up to 64 of them)
 __host__ __device__ inline F32Lds f32_lds(int rh, int rw) {
   F32Lds l;
   size_t o = 0;
   l.halo = o; o += align16((size_t)(rh + 4) * (rw + 4) * kHaloStride * 4);
   l.vs = o; o += align16((size_t)64 * kVStride * 4);
   l.wt = o; o += (size_t)25 * 32 * 4;
+  l.rt = o; o += (size_t)64 * 4;
   l.total = o;
   return l;
 }
@@ -82,6 +92,15 @@ __global__ __launch_bounds__(1024) void attn_f32_kernel(F32Args a) {
   const float* ki = a.k + (size_t)n * H * W * C;
   const float* vi = a.v + (size_t)n * H * W * C;
   const int32_t* rt = a.route + ((size_t)n * R + r) * topk;
+  if (a.qr) {
+    // routes chosen here from the region means (the route kernel's logits
+    // and ranking, route_common.h), kept in LDS for the key loop
+    int32_t* sel = reinterpret_cast<int32_t*>(smem + lay.rt);
+    route::route_region(a.qr + (size_t)n * R * C, a.kr + (size_t)n * R * C, R, C, 0, C, a.rscale, r, topk,
+                        wave, lane, vs, reinterpret_cast<uint64_t*>(smem + lay.vs + 256), sel, h == 0,
+                        a.route_out + ((size_t)n * R + r) * topk);
+    rt = sel;
+  }
 
   // ---- stage the V halo and the head's LCE weights
   for (int e = tid; e < HP * WP * 8; e += nthreads) {
@@ -221,12 +240,22 @@ bool f32_kernel_supports(const Shape& s) {
   return f32_lds(s.rh, s.rw).total <= 160 * 1024;
 }
 
+// Can the kernel choose the routes itself: S*S <= 64 candidates, and at
+// least one wave per 16 of them (a wave per 16 queries)?
+bool f32_kernel_routes(const Shape& s) {
+  return f32_kernel_supports(s) && s.R <= 64 && s.T / 16 >= (s.R + 15) / 16 && s.C % 32 == 0;
+}
+
+// Routes given (route), or with qr and kr (the region means;
+// f32_kernel_routes) chosen in the kernel and written to route_out.
 hipError_t launch_attend_f32(const void* q, const void* k, const void* v, const void* w,
                              const void* b, const int32_t* route, const Shape& s, void* out,
-                             hipStream_t st) {
+                             hipStream_t st, const float* qr, const float* kr, int32_t* route_out) {
   F32Args a;
   a.q = (const float*)q; a.k = (const float*)k; a.v = (const float*)v;
   a.w = (const float*)w; a.b = (const float*)b; a.route = route; a.out = (float*)out;
+  a.qr = qr; a.kr = kr; a.route_out = route_out;
+  a.rscale = (float)(1.0 / __builtin_sqrt((double)s.C));
   a.N = s.N; a.H = s.H; a.W = s.W; a.C = s.C; a.heads = s.heads; a.S = s.S; a.topk = s.topk;
   a.rh = s.rh; a.rw = s.rw;
   a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));

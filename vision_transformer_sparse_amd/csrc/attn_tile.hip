@@ -347,62 +347,11 @@ __global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(Tile
   // the first tile step.
   int32_t* sel = reinterpret_cast<int32_t*>(smem + lay.raw + 256);  // [topk] chosen regions
   if (a.qr) {
-    float* lrow = reinterpret_cast<float*>(smem + lay.raw);            // [64] logits of region r
-    uint64_t* kw = reinterpret_cast<uint64_t*>(smem + lay.raw + 512);  // [64] their keys
-    if (wave < (R + 15) / 16) {
-      const uint32_t mbytes = (uint32_t)R * C * 4;
-      const Rsrc qm = rsrc(a.qr + (size_t)n * R * C, mbytes), km = rsrc(a.kr + (size_t)n * R * C, mbytes);
-      const uint32_t cbase = a.head_routes ? (uint32_t)h * 128 : 0u;  // the head's first channel, bytes
-      const int CR = a.head_routes ? 32 : C;                           // channels of the logits
-      const uint32_t qrow = (uint32_t)r * C * 4 + cbase;
-      const uint32_t krow = (uint32_t)min(16 * wave + col, R - 1) * C * 4 + cbase;
-      // route::logit_tile_x3's steps in its order (hi.lo + lo.hi + hi.hi per
-      // 32 channels), two steps' operands in flight at once
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      auto step = [&](const uint4& a0, const uint4& a1, const uint4& b0, const uint4& b1) {
-        const float fa[8] = {__uint_as_float(a0.x), __uint_as_float(a0.y), __uint_as_float(a0.z), __uint_as_float(a0.w),
-                             __uint_as_float(a1.x), __uint_as_float(a1.y), __uint_as_float(a1.z), __uint_as_float(a1.w)};
-        const float fb[8] = {__uint_as_float(b0.x), __uint_as_float(b0.y), __uint_as_float(b0.z), __uint_as_float(b0.w),
-                             __uint_as_float(b1.x), __uint_as_float(b1.y), __uint_as_float(b1.z), __uint_as_float(b1.w)};
-        route::rbf16x8 ah, al, bh, bl;
-        route::split_bf16(fa, ah, al);
-        route::split_bf16(fb, bh, bl);
-        acc = route::logit_step_x3(acc, ah, al, bh, bl);
-      };
-      for (int k0 = 0; k0 < CR; k0 += 64) {
-        const uint32_t c = (uint32_t)(k0 + 8 * grp) * 4;
-        const bool two = k0 + 32 < CR;  // CR % 32 == 0
-        const uint4 a0 = ld16(qm, qrow + c), a1 = ld16(qm, qrow + c + 16);
-        const uint4 b0 = ld16(km, krow + c), b1 = ld16(km, krow + c + 16);
-        const uint4 a2 = ld16(qm, two ? qrow + c + 128 : kOut), a3 = ld16(qm, two ? qrow + c + 144 : kOut);
-        const uint4 b2 = ld16(km, two ? krow + c + 128 : kOut), b3 = ld16(km, two ? krow + c + 144 : kOut);
-        step(a0, a1, b0, b1);
-        if (two) step(a2, a3, b2, b3);
-      }
-      if (grp == 0) lrow[16 * wave + col] = acc[0] * a.rscale;
-    }
-    __syncthreads();
-    if (wave == 0) {
-      const uint64_t key = lane < R ? route::route_key(lrow[lane], lane) : 0ull;
-      kw[lane] = key;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      int rank = 0;  // keys are distinct; the 64 - R past R are 0
-#pragma unroll
-      for (int s2 = 0; s2 < 64; s2 += 2) {
-        const uint4 two = *reinterpret_cast<const uint4*>(kw + s2);
-        rank += (((uint64_t)two.y << 32 | two.x) > key) + (((uint64_t)two.w << 32 | two.z) > key);
-      }
-      if (lane < R && rank < topk) {
-        sel[rank] = lane;
-        if (slab == 0 && (a.head_routes || h == 0)) {
-          const size_t row = a.head_routes ? ((size_t)n * a.heads + h) * R + r : (size_t)nr;
-          a.route_out[row * topk + rank] = lane;
-        }
-      }
-    }
-    __syncthreads();
+    const size_t row = a.head_routes ? ((size_t)n * a.heads + h) * R + r : (size_t)nr;
+    route::route_region(a.qr + (size_t)n * R * C, a.kr + (size_t)n * R * C, R, C,
+                        a.head_routes ? h * 32 : 0, a.head_routes ? 32 : C, a.rscale, r, topk, wave, lane,
+                        reinterpret_cast<float*>(smem + lay.raw), reinterpret_cast<uint64_t*>(smem + lay.raw + 512),
+                        sel, slab == 0 && (a.head_routes || h == 0), a.route_out + row * topk);
   }
   // ---- route table -> LDS, and the largest squared key norm over the
   // routed regions: each wave reads the route row and the norms with one

@@ -310,5 +310,72 @@ __device__ __forceinline__ void route_block(const float* qr_img, const float* kr
   __syncthreads();
 }
 
+// ---- one query region's routes inside an attention kernel (R <= 64) ------
+// Region r's logits against every region of its image with route_kernel's
+// split-bf16 steps in their order (an MFMA output element depends only on
+// its row and column, so the logits equal route_kernel's bit for bit): wave
+// w < col_tiles(R) computes candidates 16w .. 16w+15 (its tile's row 0 is
+// region r) over channels cbase .. cbase + CR - 1 of the fp32 means [R][C]
+// (CR % 32 == 0; the whole C, or one head's slice for per-head routing);
+// then wave 0 ranks the R keys (larger logit first, ties to the lower
+// index), and the region's top-k go to sel[rank] (LDS) and, when emit is
+// true, to route_row[rank]. lrow (64 floats) and kw (64 keys, 16-byte
+// aligned) are LDS scratch. Every wave of the workgroup calls it; it ends
+// with a workgroup barrier (sel is then visible to all).
+__device__ __forceinline__ void route_region(const float* qr_img, const float* kr_img, int R, int C, int cbase,
+                                             int CR, float scale, int r, int topk, int wave, int lane,
+                                             float* lrow, uint64_t* kw, int32_t* sel, bool emit,
+                                             int32_t* route_row) {
+  const int col = lane & 15, grp = lane >> 4;
+  if (wave < col_tiles(R)) {
+    const uint32_t mbytes = (uint32_t)R * C * 4;
+    const Rsrc qm = rsrc(qr_img, mbytes), km = rsrc(kr_img, mbytes);
+    const uint32_t qrow = (uint32_t)(r * C + cbase) * 4;
+    const uint32_t krow = (uint32_t)(min(16 * wave + col, R - 1) * C + cbase) * 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto step = [&](const uint4& a0, const uint4& a1, const uint4& b0, const uint4& b1) {
+      const float fa[8] = {__uint_as_float(a0.x), __uint_as_float(a0.y), __uint_as_float(a0.z), __uint_as_float(a0.w),
+                           __uint_as_float(a1.x), __uint_as_float(a1.y), __uint_as_float(a1.z), __uint_as_float(a1.w)};
+      const float fb[8] = {__uint_as_float(b0.x), __uint_as_float(b0.y), __uint_as_float(b0.z), __uint_as_float(b0.w),
+                           __uint_as_float(b1.x), __uint_as_float(b1.y), __uint_as_float(b1.z), __uint_as_float(b1.w)};
+      rbf16x8 ah, al, bh, bl;
+      split_bf16(fa, ah, al);
+      split_bf16(fb, bh, bl);
+      acc = logit_step_x3(acc, ah, al, bh, bl);
+    };
+    // two steps' operands in flight at once
+    for (int k0 = 0; k0 < CR; k0 += 64) {
+      const uint32_t c = (uint32_t)(k0 + 8 * grp) * 4;
+      const bool two = k0 + 32 < CR;
+      const uint4 a0 = ld16(qm, qrow + c), a1 = ld16(qm, qrow + c + 16);
+      const uint4 b0 = ld16(km, krow + c), b1 = ld16(km, krow + c + 16);
+      const uint4 a2 = ld16(qm, two ? qrow + c + 128 : kOut), a3 = ld16(qm, two ? qrow + c + 144 : kOut);
+      const uint4 b2 = ld16(km, two ? krow + c + 128 : kOut), b3 = ld16(km, two ? krow + c + 144 : kOut);
+      step(a0, a1, b0, b1);
+      if (two) step(a2, a3, b2, b3);
+    }
+    if (grp == 0) lrow[16 * wave + col] = acc[0] * scale;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const uint64_t key = lane < R ? route_key(lrow[lane], lane) : 0ull;
+    kw[lane] = key;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int rank = 0;  // keys are distinct; the 64 - R past R are 0
+#pragma unroll
+    for (int s2 = 0; s2 < 64; s2 += 2) {
+      const uint4 two = *reinterpret_cast<const uint4*>(kw + s2);
+      rank += (((uint64_t)two.y << 32 | two.x) > key) + (((uint64_t)two.w << 32 | two.z) > key);
+    }
+    if (lane < R && rank < topk) {
+      sel[rank] = lane;
+      if (emit) route_row[rank] = lane;
+    }
+  }
+  __syncthreads();
+}
+
 }  // namespace route
 }  // namespace bra
