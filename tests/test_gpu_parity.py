@@ -327,6 +327,37 @@ def test_stage_routes_equal_forward_routes(gpu_lib, cfg):
     assert torch.equal(r_fwd, r_stage)
 
 
+STAGE_ROUTE_CASES = [
+    # name, N, H, W, C, heads, S, topk, dtype: attention kernels that route
+    # their own regions, with C over several 128-channel phases of the route
+    # kernel (and a partial last phase)
+    ("tile16_c256", 2, 64, 64, 256, 8, 4, 2, "bf16"),
+    ("tile8_c160_r64", 1, 64, 64, 160, 5, 8, 3, "bf16"),
+    ("f32_c192", 2, 32, 32, 192, 6, 4, 2, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", STAGE_ROUTE_CASES, ids=[c[0] for c in STAGE_ROUTE_CASES])
+def test_stage_routes_equal_forward_routes_wide_c(gpu_lib, case):
+    """The route kernel's logits (channels split into LDS a phase at a time)
+    equal those of the routing inside the attention kernels bit for bit, at
+    channel counts past one phase: the same route bits either way."""
+    import torch
+    name, N, H, W, C, heads, S, topk, dtype = case
+    inp = draw(N, H, W, C, S, dtype, seed=zlib.crc32(name.encode()) % 10000, offset_std=0.7)
+    args = [dev(inp[x], dtype) for x in ("q", "k", "v", "lce_w", "lce_b")]
+    say(name, "stage routes")
+    gpu_lib.profile_begin()
+    _, r_fwd = gpu_lib.forward(*args, heads, S, topk)
+    rec = gpu_lib.profile_read()
+    gpu_lib.profile_begin(())
+    assert rec["route"][1] == 0 and rec["attn"][1] == 1  # routed inside the attention kernel
+    qr, kr = gpu_lib.region_means(args[0], args[1], S)
+    r_stage = gpu_lib.route(qr, kr, topk)
+    torch.cuda.synchronize()
+    assert torch.equal(r_fwd, r_stage)
+
+
 def test_failed_workspace_allocation_leaves_outputs_untouched(gpu_lib, monkeypatch):
     """With BRA_TEST_FAIL_ALLOC=1 the library's workspace request fails as an
     out-of-memory allocation would: bra_forward returns BRA_ERR_HIP, its

@@ -226,8 +226,8 @@ __global__ __launch_bounds__(kDenseThreads, KT <= 4 ? 8 : 1) void attn_dense_ker
       float r[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) r[i] = fmaf(o[dt][i], inv, le[i]);
-      pk[dt][0] = float_to_bf16_bits(r[0]) | (float_to_bf16_bits(r[1]) << 16);
-      pk[dt][1] = float_to_bf16_bits(r[2]) | (float_to_bf16_bits(r[3]) << 16);
+      pk[dt][0] = pack_bf16x2(r[0], r[1]);
+      pk[dt][1] = pack_bf16x2(r[2], r[3]);
     }
     // Regroup so that lane group g holds channels 8g .. 8g+7 of its query (one
     // 16-byte store; the four groups write the token's 64 bytes in one

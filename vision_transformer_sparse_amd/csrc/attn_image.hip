@@ -368,7 +368,7 @@ __global__ __launch_bounds__(64 * NW) void attn_image2_kernel(ImageArgs a) {
       acc0 = dot2(p4, w1.x, acc0);
       acc1 = dot2(p4, w1.y, acc1);
     }
-    const uint32_t packed = float_to_bf16_bits(at0 + (acc0 + acc2)) | (float_to_bf16_bits(at1 + (acc1 + acc3)) << 16);
+    const uint32_t packed = pack_bf16x2(at0 + (acc0 + acc2), at1 + (acc1 + acc3));
     st_nt(ob, (uint32_t)((y * W + x) * C + 32 * h + 2 * cp) * 2, packed);
   }
 }

@@ -214,10 +214,10 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     }
     uint16_t* po = out + (((size_t)n * g.H + y) * g.W + x) * g.C + c0;
     uint2 wlo, whi;
-    wlo.x = float_to_bf16_bits(fmaf(o0[0], inv, acc[0])) | (float_to_bf16_bits(fmaf(o0[1], inv, acc[1])) << 16);
-    wlo.y = float_to_bf16_bits(fmaf(o0[2], inv, acc[2])) | (float_to_bf16_bits(fmaf(o0[3], inv, acc[3])) << 16);
-    whi.x = float_to_bf16_bits(fmaf(o1[0], inv, acc[4])) | (float_to_bf16_bits(fmaf(o1[1], inv, acc[5])) << 16);
-    whi.y = float_to_bf16_bits(fmaf(o1[2], inv, acc[6])) | (float_to_bf16_bits(fmaf(o1[3], inv, acc[7])) << 16);
+    wlo.x = pack_bf16x2(fmaf(o0[0], inv, acc[0]), fmaf(o0[1], inv, acc[1]));
+    wlo.y = pack_bf16x2(fmaf(o0[2], inv, acc[2]), fmaf(o0[3], inv, acc[3]));
+    whi.x = pack_bf16x2(fmaf(o1[0], inv, acc[4]), fmaf(o1[1], inv, acc[5]));
+    whi.y = pack_bf16x2(fmaf(o1[2], inv, acc[6]), fmaf(o1[3], inv, acc[7]));
     *reinterpret_cast<uint2*>(po + 4 * grp) = wlo;
     *reinterpret_cast<uint2*>(po + 16 + 4 * grp) = whi;
   }

@@ -383,10 +383,10 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
         const float4 l0 = *reinterpret_cast<const float4*>(lp);
         const float4 l1 = *reinterpret_cast<const float4*>(lp + 16);
         uint2 p0, p1;
-        p0.x = float_to_bf16_bits(fmaf(o0[0], inv, l0.x)) | (float_to_bf16_bits(fmaf(o0[1], inv, l0.y)) << 16);
-        p0.y = float_to_bf16_bits(fmaf(o0[2], inv, l0.z)) | (float_to_bf16_bits(fmaf(o0[3], inv, l0.w)) << 16);
-        p1.x = float_to_bf16_bits(fmaf(o1[0], inv, l1.x)) | (float_to_bf16_bits(fmaf(o1[1], inv, l1.y)) << 16);
-        p1.y = float_to_bf16_bits(fmaf(o1[2], inv, l1.z)) | (float_to_bf16_bits(fmaf(o1[3], inv, l1.w)) << 16);
+        p0.x = pack_bf16x2(fmaf(o0[0], inv, l0.x), fmaf(o0[1], inv, l0.y));
+        p0.y = pack_bf16x2(fmaf(o0[2], inv, l0.z), fmaf(o0[3], inv, l0.w));
+        p1.x = pack_bf16x2(fmaf(o1[0], inv, l1.x), fmaf(o1[1], inv, l1.y));
+        p1.y = pack_bf16x2(fmaf(o1[2], inv, l1.z), fmaf(o1[3], inv, l1.w));
         const uint32_t oo = (uint32_t)(((y0 + col / RW) * W + x0 + col % RW) * C + c0 + 4 * grp) * 2;
         st_nt(ob, oo, p0);
         st_nt(ob, oo + 32, p1);
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(64 * HEADS, 4) void attn_region_kernel(RegionArgs a
 #pragma unroll
       for (int yo = 0; yo < RH; ++yo) {
         const float2 at = *reinterpret_cast<const float2*>(lce + (yo * RW + xcol) * C + c);
-        const uint32_t packed = float_to_bf16_bits(at.x + acc0[yo]) | (float_to_bf16_bits(at.y + acc1[yo]) << 16);
+        const uint32_t packed = pack_bf16x2(at.x + acc0[yo], at.y + acc1[yo]);
         st_nt(ob, (uint32_t)(((y0 + yo) * W + x0 + xcol) * C + c) * 2, packed);
       }
     }

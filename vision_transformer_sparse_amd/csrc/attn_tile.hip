@@ -334,6 +334,14 @@ __global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(Tile
     const int t = (wv * QBW + i) * 16 + col;
     bq[i] = as_bf16x8(ld16(qb, (uint32_t)(y0 + t / RW) * rowb + (uint32_t)(x0 + t % RW) * pixb + hb + grp * 16));
   }
+  // ---- the key norms of the image's regions for this head (R <= 64:
+  // region lane in lane lane), loaded before the routes are known: the bound
+  // over the routed regions is then a lane shuffle, not a load that waits
+  // for the routes (larger images load the routed regions' norms after
+  // the route row: measured faster there)
+  const bool bounded = a.kn != nullptr;
+  const bool kn_pre = bounded && R <= 64;
+  const float knv = kn_pre && lane < R ? a.kn[((size_t)n * R + lane) * a.heads + h] : 0.f;
   // ---- routes chosen here (region means given, S*S <= 64): region r's
   // logits against every region of its image with the router's split-bf16
   // matrix-core tile (route_common.h: the operands, products and scale of
@@ -356,17 +364,19 @@ __global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(Tile
   // ---- route table -> LDS, and the largest squared key norm over the
   // routed regions: each wave reads the route row and the norms with one
   // load per lane (two dependent loads in all, not two per route)
-  const bool bounded = a.kn != nullptr;
   float k2 = 0.f;
   for (int p0 = 0; p0 < topk; p0 += 64) {
     const int p = p0 + lane;
-    if (p < topk) {
-      const int s = a.qr ? sel[p] : rrow[p];
-      if (wave == 0) {
-        const int js = s / S, is = s - js * S;
-        rbase[p] = (uint32_t)(js * RH) * rowb + (uint32_t)(is * RW) * pixb;
-      }
-      if (bounded) k2 = fmaxf(k2, a.kn[((size_t)n * R + s) * a.heads + h]);
+    const int s = p < topk ? (a.qr ? sel[p] : rrow[p]) : 0;
+    if (p < topk && wave == 0) {
+      const int js = s / S, is = s - js * S;
+      rbase[p] = (uint32_t)(js * RH) * rowb + (uint32_t)(is * RW) * pixb;
+    }
+    if (kn_pre) {  // every lane takes part in the shuffle
+      const float v = __shfl(knv, s);
+      if (p < topk) k2 = fmaxf(k2, v);
+    } else if (bounded && p < topk) {
+      k2 = fmaxf(k2, a.kn[((size_t)n * R + s) * a.heads + h]);
     }
   }
 #pragma unroll
@@ -636,10 +646,10 @@ __global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(Tile
   for (int i = 0; i < QBW; ++i) {
     const float inv = 1.0f / ls[i][0];
     uint2 lo, hi;
-    lo.x = float_to_bf16_bits(fmaf(o0[i][0], inv, acc[i][0])) | (float_to_bf16_bits(fmaf(o0[i][1], inv, acc[i][1])) << 16);
-    lo.y = float_to_bf16_bits(fmaf(o0[i][2], inv, acc[i][2])) | (float_to_bf16_bits(fmaf(o0[i][3], inv, acc[i][3])) << 16);
-    hi.x = float_to_bf16_bits(fmaf(o1[i][0], inv, acc[i][4])) | (float_to_bf16_bits(fmaf(o1[i][1], inv, acc[i][5])) << 16);
-    hi.y = float_to_bf16_bits(fmaf(o1[i][2], inv, acc[i][6])) | (float_to_bf16_bits(fmaf(o1[i][3], inv, acc[i][7])) << 16);
+    lo.x = pack_bf16x2(fmaf(o0[i][0], inv, acc[i][0]), fmaf(o0[i][1], inv, acc[i][1]));
+    lo.y = pack_bf16x2(fmaf(o0[i][2], inv, acc[i][2]), fmaf(o0[i][3], inv, acc[i][3]));
+    hi.x = pack_bf16x2(fmaf(o1[i][0], inv, acc[i][4]), fmaf(o1[i][1], inv, acc[i][5]));
+    hi.y = pack_bf16x2(fmaf(o1[i][2], inv, acc[i][6]), fmaf(o1[i][3], inv, acc[i][7]));
     if constexpr (!WO)
       store_slice(lo, hi, ty0 + i);
     else
@@ -685,10 +695,10 @@ __global__ __launch_bounds__(64 * kTileWaves * HG, 4) void attn_tile_kernel(Tile
 #pragma unroll
     for (int i = 0; i < QBW; ++i) {
       uint2 lo, hi;
-      lo.x = float_to_bf16_bits(ya[0][i][0] + bias[0]) | (float_to_bf16_bits(ya[0][i][1] + bias[1]) << 16);
-      lo.y = float_to_bf16_bits(ya[0][i][2] + bias[2]) | (float_to_bf16_bits(ya[0][i][3] + bias[3]) << 16);
-      hi.x = float_to_bf16_bits(ya[1][i][0] + bias[4]) | (float_to_bf16_bits(ya[1][i][1] + bias[5]) << 16);
-      hi.y = float_to_bf16_bits(ya[1][i][2] + bias[6]) | (float_to_bf16_bits(ya[1][i][3] + bias[7]) << 16);
+      lo.x = pack_bf16x2(ya[0][i][0] + bias[0], ya[0][i][1] + bias[1]);
+      lo.y = pack_bf16x2(ya[0][i][2] + bias[2], ya[0][i][3] + bias[3]);
+      hi.x = pack_bf16x2(ya[1][i][0] + bias[4], ya[1][i][1] + bias[5]);
+      hi.y = pack_bf16x2(ya[1][i][2] + bias[6], ya[1][i][3] + bias[7]);
       store_slice(lo, hi, ty0 + i);
     }
   }

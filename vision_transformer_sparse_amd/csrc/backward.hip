@@ -88,10 +88,10 @@ __device__ __forceinline__ bf16x8 as8(uint4 x) { return __builtin_bit_cast(bf16x
 // channels 8g..8g+7, one 16-byte store a lane at byte offset off + 16g.
 __device__ __forceinline__ void store_slice(Rsrc r, uint32_t off, int g, const float* a, const float* b,
                                             bool live) {
-  const uint32_t la[2] = {float_to_bf16_bits(a[0]) | (float_to_bf16_bits(a[1]) << 16),
-                          float_to_bf16_bits(a[2]) | (float_to_bf16_bits(a[3]) << 16)};
-  const uint32_t hb[2] = {float_to_bf16_bits(b[0]) | (float_to_bf16_bits(b[1]) << 16),
-                          float_to_bf16_bits(b[2]) | (float_to_bf16_bits(b[3]) << 16)};
+  const uint32_t la[2] = {pack_bf16x2(a[0], a[1]),
+                          pack_bf16x2(a[2], a[3])};
+  const uint32_t hb[2] = {pack_bf16x2(b[0], b[1]),
+                          pack_bf16x2(b[2], b[3])};
   uint32_t xs[2], ys[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {

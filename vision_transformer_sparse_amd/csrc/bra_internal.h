@@ -121,6 +121,14 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
 }
+// Two floats rounded to nearest even into one packed bf16 pair (lo in bits
+// 0..15) by the hardware conversion (one v_cvt_pk_bf16_f32); for finite
+// values the same bits as float_to_bf16_bits, a NaN stays a NaN.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 __device__ __forceinline__ float max3(float a, float b, float c) {
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
