@@ -730,6 +730,17 @@ bool tile_kernel_supports(const Shape& s) {
 // Can the kernel choose the routes itself (from the region means)?
 bool tile_kernel_routes(const Shape& s) { return s.R <= 64; }
 
+namespace {
+// 16x16 regions routed in the kernel (one set of routes for all heads): the
+// two heads of a pair in one workgroup, which routes the region once for
+// both (measured faster than a workgroup per head)
+bool tile_head_pairs(const Shape& s, bool routed_here, bool head_routes) {
+  return s.rh == 16 && s.rw == 16 && routed_here && !head_routes && s.heads % 2 == 0 &&
+         tile_lds(8, 16, s.topk, 2, 2).total <= 65536;
+}
+}  // namespace
+
+
 // The block's attention + output projection: every head of a region in one
 // workgroup (two heads of 32 channels; 8x8 or 16x16 regions), routes chosen
 // in the kernel (S*S <= 64).
@@ -778,6 +789,7 @@ hipError_t launch_attend_tile(const void* q, const void* k, const void* v, const
   a.rscale = (float)(1.0 / __builtin_sqrt((double)(head_routes ? s.hd : s.C)));
   a.N = s.N; a.H = s.H; a.W = s.W; a.C = s.C; a.heads = s.heads; a.S = s.S; a.topk = s.topk;
   a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
+  if (tile_head_pairs(s, qr != nullptr, head_routes)) return launch_t<16, 16, 2, false>(a, st);
   switch (s.rh * 64 + s.rw) {
     case 8 * 64 + 8: return launch_t<8, 8, 1, false>(a, st);
     case 16 * 64 + 16: return launch_t<16, 16, 1, false>(a, st);
