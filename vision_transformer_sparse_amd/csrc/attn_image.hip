@@ -103,6 +103,9 @@ struct ImageArgs {
   const uint16_t* lw;
   int32_t* route_out;
   float rscale;
+  // divisions of staging indices (all below 2^16) by W, W + 4, S and the
+  // route stride, as multiply-highs
+  FastDiv dw, dwp, ds, drs;
 };
 
 __host__ __device__ constexpr size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
@@ -140,7 +143,9 @@ __host__ __device__ inline ImgLds img_lds(int RS, int NW, int H, int W, int R, i
   return l;
 }
 
-template <int NW>
+// FULL: every 64-key chunk is whole (topk * 4 a multiple of 64), so no key
+// is masked
+template <int NW, bool FULL>
 __global__ __launch_bounds__(64 * NW) void attn_image2_kernel(ImageArgs a) {
   constexpr int RS = 2, RH = RS, RW = RS, T = RS * RS;  // 2x2 regions
   constexpr int nthreads = 64 * NW;
@@ -183,22 +188,22 @@ __global__ __launch_bounds__(64 * NW) void attn_image2_kernel(ImageArgs a) {
 #pragma unroll
       for (int j = 0; j < 6; ++j) {
         const int i = j0 + j * nthreads + tid;
-        const int pix = i >> 2;
-        const int y = pix / WP - 2, x = pix % WP - 2;
+        const int pix = i >> 2, py = (int)fdiv(a.dwp, (uint32_t)pix);
+        const int y = py - 2, x = pix - py * WP - 2;
         const bool in = i < vp && y >= 0 && y < H && x >= 0 && x < W;  // border: zero
         vbuf[j] = ld16(vb, in ? (uint32_t)(y * W + x) * pixb + hoff + (uint32_t)(i & 3) * 16 : kOut);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = i0 + j * nthreads + tid;
-        const int tok = i >> 2, y = tok / W, x = tok - y * W;
+        const int tok = i >> 2, y = (int)fdiv(a.dw, (uint32_t)tok), x = tok - y * W;
         const int pc = (i & 3) ^ kswz(y, x);
         *reinterpret_cast<uint4*>(i < kp ? kh + (size_t)(4 * tok + pc) * 8 : sink) = kbuf[j];
       }
 #pragma unroll
       for (int j = 0; j < 6; ++j) {
         const int i = j0 + j * nthreads + tid;
-        const int pix = i >> 2, py = pix / WP;
+        const int pix = i >> 2, py = (int)fdiv(a.dwp, (uint32_t)pix);
         const int pc = (i & 3) ^ vswz(py);
         *reinterpret_cast<uint4*>(i < vp ? vh + (size_t)(4 * pix + pc) * 8 : sink) = vbuf[j];
       }
@@ -207,9 +212,9 @@ __global__ __launch_bounds__(64 * NW) void attn_image2_kernel(ImageArgs a) {
     // bordered-V token (slots past topk: region 0, their keys are masked)
     const int32_t* rt = a.route + (size_t)n * R * topk;
     for (int i = tid; i < R * RSTR; i += nthreads) {
-      const int r = i / RSTR, p = i - r * RSTR;
+      const int r = (int)fdiv(a.drs, (uint32_t)i), p = i - r * RSTR;
       const int rr = p < topk ? rt[r * topk + p] : 0;
-      const int js = rr / S, is = rr - js * S;
+      const int js = (int)fdiv(a.ds, (uint32_t)rr), is = rr - js * S;
       // 2x2 regions: bit 5 carries the region-column parity of the K swizzle
       // (token offsets are 64-byte aligned)
       rk[i] = (uint16_t)(((size_t)(js * RH * W + is * RW) * 64) | (size_t)(RS == 2 ? (is & 1) << 5 : 0));
@@ -264,7 +269,7 @@ __global__ __launch_bounds__(64 * NW) void attn_image2_kernel(ImageArgs a) {
   // query pixel of this lane's column in region r (r wave-uniform), and the
   // head's Q row there, prefetched a region ahead
   auto qpix = [&](int r, int& y, int& x) {
-    const int js = r / S, is = r - js * S;
+    const int js = (int)fdiv(a.ds, (uint32_t)r), is = r - js * S;
     y = js * RH + qt / RW;
     x = is * RW + qt % RW;
   };
@@ -312,7 +317,7 @@ __global__ __launch_bounds__(64 * NW) void attn_image2_kernel(ImageArgs a) {
       f32x4 s;
 #pragma unroll
       for (int e = 0; e < 4; ++e) s[e] = pick4(tq & 1, tq & 2, st[0][e], st[1][e], st[2][e], st[3][e]);
-      if (base + 64 > L) {  // ragged last chunk
+      if (!FULL && base + 64 > L) {  // ragged last chunk
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (base + 16 * tq + 4 * grp + e >= L) s[e] = -INFINITY;
@@ -1151,6 +1156,10 @@ static ImageArgs image_args(const void* q, const void* k, const void* v, const v
   a.N = s.N; a.H = s.H; a.W = s.W; a.C = s.C; a.heads = s.heads; a.S = s.S; a.topk = s.topk;
   a.qscale = (float)(1.4426950408889634 / __builtin_sqrt((double)s.hd));
   a.rscale = (float)(1.0 / __builtin_sqrt((double)s.C));  // as the route kernels
+  a.dw = make_fastdiv((uint32_t)s.W);
+  a.dwp = make_fastdiv((uint32_t)s.W + 4);
+  a.ds = make_fastdiv((uint32_t)s.S);
+  a.drs = make_fastdiv((uint32_t)route_stride(s.topk, s.T));
   return a;
 }
 
@@ -1170,8 +1179,11 @@ hipError_t launch_attend_image(const void* q, const void* k, const void* v, cons
   a.wpk = wpk; a.route = route;
   const int units = s.N * s.heads;
   if (s.rh == 2) {
-    launch(attn_image2_kernel<kImage2Waves>, dim3((unsigned)units), dim3(64 * kImage2Waves),
-           img_lds(2, kImage2Waves, s.H, s.W, s.R, s.topk).total, st, a);
+    const size_t lds = img_lds(2, kImage2Waves, s.H, s.W, s.R, s.topk).total;
+    if (s.L % 64 == 0)
+      launch(attn_image2_kernel<kImage2Waves, true>, dim3((unsigned)units), dim3(64 * kImage2Waves), lds, st, a);
+    else
+      launch(attn_image2_kernel<kImage2Waves, false>, dim3((unsigned)units), dim3(64 * kImage2Waves), lds, st, a);
   } else {
     const size_t lds = img_lds(4, kNW4, s.H, s.W, s.R, s.topk).total;
     const dim3 g((unsigned)image4_grid(units)), blk(kThreads4);

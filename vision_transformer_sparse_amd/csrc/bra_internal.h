@@ -46,6 +46,23 @@ struct Shape {
 };
 
 constexpr int kHeadDim = 32;     // compiled head dimension
+
+// Division by a fixed d in [1, 2^16) of any n in [0, 2^16) with one
+// multiply-high: with m = ceil(2^32 / d) = (2^32 + e) / d, e < d,
+// n * m / 2^32 = n / d + n e / (d 2^32), and the second term is below 1/d,
+// which the fractional part of n / d never comes within, so the floor is
+// exact. m is made on the host (d = 1 keeps m = 0 and divides by identity).
+struct FastDiv {
+  uint32_t d, m;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  return FastDiv{d, d <= 1 ? 0u : (uint32_t)((0x100000000ull + d - 1) / d)};
+}
+#if defined(__HIPCC__)
+__device__ __forceinline__ uint32_t fdiv(const FastDiv& f, uint32_t n) {
+  return f.m ? __umulhi(n, f.m) : n;
+}
+#endif
 constexpr int kMaxRegions = 1024;
 
 // Region means; for bf16 (wpk non-null) also repacks the LCE weights for the
