@@ -531,128 +531,203 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 4 : 1) void bwd_key_kernel
 }
 
 // ---------------------------------------------------------------- LCE terms
-// One workgroup per (image, block of kLceRows rows, block of kLceCh
-// channels): the V rows and the dout rows of the block and two more on each
-// side are staged in LDS, one 16-byte piece a pixel, zero outside the image
-// (the staged rows run kLceRun columns past W + 4, also zero, so every run
-// reads inside them). Thread (channel c, group xg) walks (row, run of
-// kLceRun consecutive columns) items xg, xg + kLceXg, ..., its channel's 25
-// weights in registers; per
-// window row it reads the kLceRun + 4 values of the row once and applies all
-// five horizontal taps from registers. It sums the 25 tap terms dout[y][x] *
-// v[y+a-2][x+e-2] and the bias term (the column groups are then added in a
-// fixed order into part[block][c][26]) and writes dv's LCE term
-// sum_{a,e} w[a][e] * dout[y-a+2][x-e+2] (fp32, stored by channel block,
-// [N][C/8][H][W][8], so a block's writes are whole rows; the key side adds it
-// to the attention part).
-constexpr int kLceRows = 8;               // output rows of a block
+// One workgroup per (image, block of rows, block of kLceCh channels): the V
+// rows and the dout rows of the block and two more on each side are staged in
+// LDS channel-major, [row][channel][column] bf16 (column x at x + 2, zero
+// outside the image and for kLceRun + pad columns past W + 2), so a 32-bit
+// read is a horizontal pixel pair of one channel: one v_dot2_f32_bf16 then
+// applies two taps, and an odd-aligned pair is one v_alignbyte of two even
+// ones. Thread (channel c, group xg) walks (row, run of kLceRun = 4
+// columns) items xg, xg + XG, ... (XG column groups: 32, or 64 for images
+// at least 32 columns wide, whose eight staged rows are then walked by
+// twice the waves); per window row ta it reads the eight
+// V and eight dout values of the run's window as four even pairs each and
+// adds, over the run,
+//   the 25 tap terms dout[y][x] * v[y+ta-2][x+te-2]  (pairs of x), and
+//   dv's LCE term w[ta][te] * dout[y-ta+2][x-te+2]    (pairs of taps te),
+// plus the bias term (sum of dout). The column groups' tap sums are then
+// added in a fixed order into part[block][c][26], and dv's LCE term is
+// written in fp32 by channel block, [N][C/8][H][W][8] (a block's writes are
+// whole rows; the key side adds it to the attention part). Images up to 32
+// rows tall are one block each (the halo rows are then read once); taller
+// ones go in blocks of 8 rows.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 constexpr int kLceCh = 8;                 // channels of a block: one 16-byte piece a pixel
-constexpr int kLceXg = 256 / kLceCh;      // column groups
 constexpr int kLceRun = 4;                // consecutive columns a thread takes at once
-constexpr int kLceBatch = 8;              // staging pieces of each tensor a thread has in flight
-__host__ __device__ inline int lce_pitch(int W) { return W + 4 + kLceRun; }
-__host__ __device__ inline size_t lce_grad_lds(int W) {
-  const size_t stage = (size_t)2 * (kLceRows + 4) * lce_pitch(W) * kLceCh * 2;
-  const size_t red = (size_t)kLceXg * kLceCh * 26 * sizeof(float);
+constexpr int kLceBatch = 4;              // staged pixel pairs of each tensor a thread has in flight
+constexpr int kLceRowsTall = 8;           // rows of a block of a tall image
+constexpr int kLceRowsWhole = 32;         // images up to this height: one block
+constexpr size_t kLceStageMax = 64 * 1024;
+// staged row pitch in bf16 columns: W + 4 + kLceRun, rounded to 4 (8-byte
+// pair reads); for images at least 32 columns wide (a wave's eight column
+// groups then read one row) raised to 32 mod 64, so the eight channels'
+// 8-byte reads of a wave start 16 banks apart and take the minimum two
+// passes
+__host__ __device__ inline int lce_pitch(int W) {
+  int p = (W + 4 + kLceRun + 3) & ~3;
+  if (W >= 8 * kLceRun) p += (96 - p % 64) % 64;
+  return p;
+}
+__host__ __device__ inline size_t lce_stage_bytes(int rows, int W) {
+  return (size_t)2 * (rows + 4) * kLceCh * lce_pitch(W) * 2;
+}
+__host__ __device__ inline int lce_rows(int H, int W) {
+  return H <= kLceRowsWhole && lce_stage_bytes(H, W) <= kLceStageMax ? H : kLceRowsTall;
+}
+__host__ __device__ inline int lce_groups(int W) { return W >= 8 * kLceRun ? 64 : 32; }
+__host__ __device__ inline size_t lce_grad_lds(int H, int W) {
+  const size_t stage = lce_stage_bytes(lce_rows(H, W), W);
+  const size_t red = (size_t)lce_groups(W) * kLceCh * 26 * sizeof(float);
   return stage > red ? stage : red;
 }
 
-__global__ __launch_bounds__(256) void lce_grad_rows_kernel(const uint16_t* __restrict__ v,
-                                                            const uint16_t* __restrict__ g,
-                                                            const uint16_t* __restrict__ lw, int N, int H, int W,
-                                                            int C, float* __restrict__ part,
-                                                            float* __restrict__ dv_lce) {
+struct LceArgs {
+  const uint16_t* v;
+  const uint16_t* g;
+  const uint16_t* lw;
+  int N, H, W, C, rows;  // rows: output rows of a block
+  FastDiv dpp;           // staged pixel pairs a row (lce_pitch / 2)
+  FastDiv druns;         // runs of kLceRun columns a row
+  float* part;
+  float* dv_lce;
+};
+
+// row blocks of an image
+__host__ __device__ inline int lce_blocks(int H, int W) { return (H + lce_rows(H, W) - 1) / lce_rows(H, W); }
+
+template <int XG>
+__global__ __launch_bounds__(XG * kLceCh) void lce_grad_rows_kernel(LceArgs a) {
+  constexpr int NT = XG * kLceCh;
   extern __shared__ __attribute__((aligned(16))) char sm[];
-  const int YB = (H + kLceRows - 1) / kLceRows, CB = C / kLceCh;
+  const int H = a.H, W = a.W, C = a.C, BR = a.rows;
+  const int YB = (H + BR - 1) / BR, CB = C / kLceCh;
   // consecutive units -- the CB channel blocks of one row block, which read
   // the same 128-byte pixel lines 16 bytes each -- share an XCD and its L2
   int u = xcd_unit((int)blockIdx.x, (int)gridDim.x);
   const int cb = u % CB;
   u /= CB;
   const int yb = u % YB, n = u / YB;
-  const int y0 = yb * kLceRows, tid = threadIdx.x;
-  const int WP = lce_pitch(W), RB = kLceRows + 4;
-  uint16_t* vs = reinterpret_cast<uint16_t*>(sm);   // [RB][WP][kLceCh], column x at x + 2
-  uint16_t* gs = vs + (size_t)RB * WP * kLceCh;     // [RB][WP][kLceCh]
+  const int y0 = yb * BR, tid = threadIdx.x;
+  const int WP = lce_pitch(W), PP = WP / 2, SR = BR + 4;
+  uint32_t* vs = reinterpret_cast<uint32_t*>(sm);  // [SR][kLceCh][PP] pixel pairs
+  uint32_t* gs = vs + (size_t)SR * kLceCh * PP;
   const size_t img = (size_t)n * H * W * C;
   const uint32_t img_bytes = (uint32_t)((size_t)H * W * C * 2);
-  const Rsrc vr = rsrc(v + img, img_bytes), gr = rsrc(g + img, img_bytes);
+  const Rsrc vr = rsrc(a.v + img, img_bytes), gr = rsrc(a.g + img, img_bytes);
   const uint32_t cofs = (uint32_t)cb * kLceCh * 2;
   const int c = tid % kLceCh, xg = tid / kLceCh;
-  float wr[25];
+  // the channel's weights as dot2 operands for each window row ta: taps
+  // (4, 3) and (2, 1) against the pairs (x-2, x-1) and (x, x+1) of an output
+  // x, and tap 0 alone against (x+2, x+3) or (x+1, x+2)
+  uint32_t w43[5], w21[5], w0l[5], w0h[5];
+  {
+    const uint16_t* wc = a.lw + (size_t)(cb * kLceCh + c) * 25;
 #pragma unroll
-  for (int tap = 0; tap < 25; ++tap) wr[tap] = bf16_bits_to_float(lw[(size_t)(cb * kLceCh + c) * 25 + tap]);
-  // staging: kLceBatch pieces of each tensor a thread in flight before any is stored
-  const int pieces = RB * WP;
-  for (int e0 = tid; e0 < pieces; e0 += 256 * kLceBatch) {
-    uint4 vx[kLceBatch], gx[kLceBatch];
+    for (int ta = 0; ta < 5; ++ta) {
+      const uint32_t t0 = wc[5 * ta], t1 = wc[5 * ta + 1], t2 = wc[5 * ta + 2], t3 = wc[5 * ta + 3],
+                     t4 = wc[5 * ta + 4];
+      w43[ta] = t4 | (t3 << 16);
+      w21[ta] = t2 | (t1 << 16);
+      w0l[ta] = t0;
+      w0h[ta] = t0 << 16;
+    }
+  }
+  // staging: pixel pairs (2p - 2, 2p - 1) of staged row ry (image row
+  // y0 + ry - 2), both tensors; the eight channels of the two 16-byte
+  // pieces become eight channel pairs
+  const int units = SR * PP;
+  for (int e0 = tid; e0 < units; e0 += NT * kLceBatch) {
+    uint4 va[kLceBatch], vb[kLceBatch], ga[kLceBatch], gb[kLceBatch];
 #pragma unroll
     for (int i = 0; i < kLceBatch; ++i) {
-      const int e = e0 + 256 * i, ry = e / WP, rx = e - ry * WP;
-      const int y = y0 + ry - 2, x = rx - 2;
-      const uint32_t off =
-          e < pieces && y >= 0 && y < H && x >= 0 && x < W ? (uint32_t)((y * W + x) * C * 2) + cofs : kOut;
-      vx[i] = ld16(vr, off);
-      gx[i] = ld16(gr, off);
+      const int e = e0 + NT * i, ry = (int)fdiv(a.dpp, (uint32_t)e), p = e - ry * PP;
+      const int y = y0 + ry - 2, xa = 2 * p - 2;
+      const bool row_in = e < units && y >= 0 && y < H;
+      const uint32_t oa = row_in && xa >= 0 && xa < W ? (uint32_t)((y * W + xa) * C * 2) + cofs : kOut;
+      const uint32_t ob = row_in && xa + 1 >= 0 && xa + 1 < W ? (uint32_t)((y * W + xa + 1) * C * 2) + cofs : kOut;
+      va[i] = ld16(vr, oa);
+      vb[i] = ld16(vr, ob);
+      ga[i] = ld16(gr, oa);
+      gb[i] = ld16(gr, ob);
     }
 #pragma unroll
     for (int i = 0; i < kLceBatch; ++i) {
-      const int e = e0 + 256 * i;
-      if (e < pieces) {
-        reinterpret_cast<uint4*>(vs)[e] = vx[i];
-        reinterpret_cast<uint4*>(gs)[e] = gx[i];
+      const int e = e0 + NT * i;
+      if (e < units) {
+        const int ry = (int)fdiv(a.dpp, (uint32_t)e), p = e - ry * PP;
+        uint32_t* vd = vs + (size_t)ry * kLceCh * PP + p;
+        uint32_t* gd = gs + (size_t)ry * kLceCh * PP + p;
+        const uint32_t av[4] = {va[i].x, va[i].y, va[i].z, va[i].w}, bv[4] = {vb[i].x, vb[i].y, vb[i].z, vb[i].w};
+        const uint32_t ag[4] = {ga[i].x, ga[i].y, ga[i].z, ga[i].w}, bg[4] = {gb[i].x, gb[i].y, gb[i].z, gb[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          vd[(2 * k) * PP] = __builtin_amdgcn_perm(bv[k], av[k], 0x05040100u);
+          vd[(2 * k + 1) * PP] = __builtin_amdgcn_perm(bv[k], av[k], 0x07060302u);
+          gd[(2 * k) * PP] = __builtin_amdgcn_perm(bg[k], ag[k], 0x05040100u);
+          gd[(2 * k + 1) * PP] = __builtin_amdgcn_perm(bg[k], ag[k], 0x07060302u);
+        }
       }
     }
   }
   __syncthreads();
-  auto V = [&](int row, int col) { return bf16_bits_to_float(vs[((size_t)row * WP + col) * kLceCh + c]); };
-  auto G = [&](int row, int col) { return bf16_bits_to_float(gs[((size_t)row * WP + col) * kLceCh + c]); };
+  // the four even pairs of staged columns x0 .. x0 + 7 of row ry, channel c
+  auto pairs4 = [&](const uint32_t* base, int ry, int x0, uint32_t* o) {
+    const uint2* p = reinterpret_cast<const uint2*>(base + ((size_t)ry * kLceCh + c) * PP + x0 / 2);
+    const uint2 l = p[0], h = p[1];
+    o[0] = l.x; o[1] = l.y; o[2] = h.x; o[3] = h.y;
+  };
   float acc[26];
 #pragma unroll
   for (int i = 0; i < 26; ++i) acc[i] = 0.f;
-  const int runs = (W + kLceRun - 1) / kLceRun;  // runs of a row
-  for (int item = xg; item < kLceRows * runs; item += kLceXg) {  // (row, run) items over the column groups
-    const int ry = item / runs, x0 = (item - ry * runs) * kLceRun, y = y0 + ry;
-    {
-      float gv[kLceRun], dl[kLceRun];
+  const int runs = (int)a.druns.d;
+  const uint32_t ones = 0x3f803f80u;  // bf16 (1, 1)
+  for (int item = xg; item < BR * runs; item += XG) {  // (row, run) items over the column groups
+    const int ry = (int)fdiv(a.druns, (uint32_t)item), x0 = (item - ry * runs) * kLceRun, y = y0 + ry;
+    // dout[y][x0 .. x0+3] as pairs (staged row ry + 2, columns x0 + 2 ..)
+    const uint32_t* gcp = gs + ((size_t)(ry + 2) * kLceCh + c) * PP + x0 / 2 + 1;  // 4-byte aligned
+    const uint2 gc = make_uint2(gcp[0], gcp[1]);
+    acc[25] = dot2(gc.y, ones, dot2(gc.x, ones, acc[25]));
+    float dl[kLceRun] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < kLceRun; ++j) {
-        gv[j] = x0 + j < W ? G(ry + 2, x0 + j + 2) : 0.f;  // dout[y][x0+j] (zero past W)
-        dl[j] = 0.f;
-        acc[25] += gv[j];
-      }
-#pragma unroll
-      for (int ta = 0; ta < 5; ++ta) {
-        float vw[kLceRun + 4], gw[kLceRun + 4];
-#pragma unroll
-        for (int j = 0; j < kLceRun + 4; ++j) {
-          vw[j] = V(ry + ta, x0 + j);       // v[y+ta-2][x0+j-2]
-          gw[j] = G(ry + 4 - ta, x0 + j);   // dout[y+2-ta][x0+j-2]
-        }
-#pragma unroll
-        for (int te = 0; te < 5; ++te)
-#pragma unroll
-          for (int j = 0; j < kLceRun; ++j) {
-            acc[5 * ta + te] = fmaf(gv[j], vw[j + te], acc[5 * ta + te]);
-            // v[y][x] feeds output (y + 2 - ta, x + 2 - te) through tap (ta, te)
-            dl[j] = fmaf(wr[5 * ta + te], gw[j + 4 - te], dl[j]);
-          }
-      }
-      if (y < H)
-#pragma unroll
-        for (int j = 0; j < kLceRun; ++j)
-          if (x0 + j < W) dv_lce[((((size_t)n * CB + cb) * H + y) * W + x0 + j) * kLceCh + c] = dl[j];
+    for (int ta = 0; ta < 5; ++ta) {
+      uint32_t P[4], Q[4];
+      pairs4(vs, ry + ta, x0, P);      // v[y+ta-2][x0-2 .. x0+5]
+      pairs4(gs, ry + 4 - ta, x0, Q);  // dout[y+2-ta][x0-2 .. x0+5]
+      const uint32_t O0 = __builtin_amdgcn_alignbyte(P[1], P[0], 2), O1 = __builtin_amdgcn_alignbyte(P[2], P[1], 2),
+                     O2 = __builtin_amdgcn_alignbyte(P[3], P[2], 2);
+      const uint32_t R0 = __builtin_amdgcn_alignbyte(Q[1], Q[0], 2), R1 = __builtin_amdgcn_alignbyte(Q[2], Q[1], 2),
+                     R2 = __builtin_amdgcn_alignbyte(Q[3], Q[2], 2);
+      // tap (ta, te): dout pairs (x0, x0+1), (x0+2, x0+3) against v pairs
+      // starting at x0 + te - 2 and x0 + te
+      acc[5 * ta + 0] = dot2(gc.y, P[1], dot2(gc.x, P[0], acc[5 * ta + 0]));
+      acc[5 * ta + 1] = dot2(gc.y, O1, dot2(gc.x, O0, acc[5 * ta + 1]));
+      acc[5 * ta + 2] = dot2(gc.y, P[2], dot2(gc.x, P[1], acc[5 * ta + 2]));
+      acc[5 * ta + 3] = dot2(gc.y, O2, dot2(gc.x, O1, acc[5 * ta + 3]));
+      acc[5 * ta + 4] = dot2(gc.y, P[3], dot2(gc.x, P[2], acc[5 * ta + 4]));
+      // output x0 + j: dout at x0 + j - 2 .. x0 + j + 2 against taps 4 .. 0
+      dl[0] = dot2(Q[2], w0l[ta], dot2(Q[1], w21[ta], dot2(Q[0], w43[ta], dl[0])));
+      dl[1] = dot2(Q[2], w0h[ta], dot2(R1, w21[ta], dot2(R0, w43[ta], dl[1])));
+      dl[2] = dot2(Q[3], w0l[ta], dot2(Q[2], w21[ta], dot2(Q[1], w43[ta], dl[2])));
+      dl[3] = dot2(Q[3], w0h[ta], dot2(R2, w21[ta], dot2(R1, w43[ta], dl[3])));
     }
+    if (y < H)
+#pragma unroll
+      for (int j = 0; j < kLceRun; ++j)
+        if (x0 + j < W) a.dv_lce[((((size_t)n * CB + cb) * H + y) * W + x0 + j) * kLceCh + c] = dl[j];
   }
   __syncthreads();  // the staging area becomes the reduction area
-  float* red = reinterpret_cast<float*>(sm);  // [kLceXg][kLceCh][26]
+  float* red = reinterpret_cast<float*>(sm);  // [XG][kLceCh][26]
 #pragma unroll
   for (int i = 0; i < 26; ++i) red[((size_t)xg * kLceCh + c) * 26 + i] = acc[i];
   __syncthreads();
-  for (int e = tid; e < kLceCh * 26; e += 256) {
+  for (int e = tid; e < kLceCh * 26; e += NT) {
     float sum = 0.f;
-    for (int j = 0; j < kLceXg; ++j) sum += red[(size_t)j * kLceCh * 26 + e];
-    part[((size_t)(n * YB + yb) * C + cb * kLceCh) * 26 + e] = sum;
+    for (int j = 0; j < XG; ++j) sum += red[(size_t)j * kLceCh * 26 + e];
+    a.part[((size_t)(n * YB + yb) * C + cb * kLceCh) * 26 + e] = sum;
   }
 }
 
@@ -716,14 +791,14 @@ hipError_t launch_sides_for(const BwdArgs& a, hipStream_t st) {
 
 bool backward_supports(const Shape& s, int dtype) {
   return dtype == 1 && s.hd == 32 && s.T % 16 == 0 && s.topk <= 16 && s.R <= 1024 &&
-         lce_grad_lds(s.W) <= 96 * 1024 && (size_t)s.H * s.W * s.C * 2 < (1ull << 31);
+         lce_grad_lds(s.H, s.W) <= 96 * 1024 && (size_t)s.H * s.W * s.C * 2 < (1ull << 31);
 }
 
 size_t backward_workspace_bytes(const Shape& s) {
   const size_t stats = (size_t)s.N * s.H * s.W * s.heads * sizeof(float);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   return 2 * al(stats) + al((size_t)s.N * s.R * 4) + al((size_t)s.N * s.R * s.R * 4) +
-         al((size_t)s.N * ((s.H + kLceRows - 1) / kLceRows) * s.C * 26 * sizeof(float)) +
+         al((size_t)s.N * lce_blocks(s.H, s.W) * s.C * 26 * sizeof(float)) +
          al((size_t)s.N * s.H * s.W * s.C * sizeof(float));
 }
 
@@ -749,7 +824,7 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const vo
   int32_t* ent = reinterpret_cast<int32_t*>(p);
   p += al((size_t)s.N * s.R * s.R * 4);
   float* part = reinterpret_cast<float*>(p);
-  p += al((size_t)s.N * ((s.H + kLceRows - 1) / kLceRows) * s.C * 26 * sizeof(float));
+  p += al((size_t)s.N * lce_blocks(s.H, s.W) * s.C * 26 * sizeof(float));
   float* dvl = reinterpret_cast<float*>(p);
   a.dv_lce = dvl;
   a.inv_cnt = cnt;
@@ -763,9 +838,22 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const vo
   launch(inv_route_kernel, dim3((unsigned)(s.N * s.R)), dim3(64), 0, st, route, s.R, s.topk, cnt, ent);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int lblocks = s.N * ((s.H + kLceRows - 1) / kLceRows);
-  launch(lce_grad_rows_kernel, dim3((unsigned)(lblocks * (s.C / kLceCh))), dim3(256), lce_grad_lds(s.W), st,
-         (const uint16_t*)v, (const uint16_t*)dout, (const uint16_t*)w, s.N, s.H, s.W, s.C, part, dvl);
+  const int lblocks = s.N * lce_blocks(s.H, s.W);
+  LceArgs la;
+  la.v = (const uint16_t*)v;
+  la.g = (const uint16_t*)dout;
+  la.lw = (const uint16_t*)w;
+  la.N = s.N; la.H = s.H; la.W = s.W; la.C = s.C;
+  la.rows = lce_rows(s.H, s.W);
+  la.dpp = make_fastdiv((uint32_t)(lce_pitch(s.W) / 2));
+  la.druns = make_fastdiv((uint32_t)((s.W + kLceRun - 1) / kLceRun));
+  la.part = part;
+  la.dv_lce = dvl;
+  const dim3 lgrid((unsigned)(lblocks * (s.C / kLceCh)));
+  if (lce_groups(s.W) == 64)
+    launch(lce_grad_rows_kernel<64>, lgrid, dim3(64 * kLceCh), lce_grad_lds(s.H, s.W), st, la);
+  else
+    launch(lce_grad_rows_kernel<32>, lgrid, dim3(32 * kLceCh), lce_grad_lds(s.H, s.W), st, la);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   launch(lce_grad_sum_kernel, dim3((unsigned)((s.C * 26 + 7) / 8)), dim3(256), 0, st, (const float*)part, lblocks,
