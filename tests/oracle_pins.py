@@ -207,8 +207,8 @@ def _dense_reference(q, k, v, w, b, heads):
 
 def pin_dense_when_all_regions_routed(O):
     """topk = S^2 routes every region to every query region, so BRA equals
-    dense attention over all H*W tokens plus LCE (spec check (a)); S = 1
-    is the same special case with one region."""
+    dense attention over all H*W tokens plus LCE (the dense-attention
+    invariant); S = 1 is the same special case with one region."""
     cases = [(2, 6, 6, 8, 2, 3, 9), (1, 4, 8, 4, 1, 2, 4), (1, 5, 5, 6, 3, 1, 1), (1, 8, 8, 8, 2, 4, 16)]
     for seed, (N, H, W, C, heads, S, topk) in enumerate(cases):
         rng = _rng(200 + seed)
@@ -221,8 +221,8 @@ def pin_dense_when_all_regions_routed(O):
 
 
 def pin_softmax_rows_sum_to_one(O):
-    """North-star check (c): every query's probabilities over its gathered
-    keys sum to 1, are non-negative, and are zero nowhere."""
+    """Softmax rows: every query's probabilities over its gathered keys sum
+    to 1, are non-negative, and are zero nowhere."""
     rng = _rng(9)
     q, k, v = (rng.standard_normal((2, 6, 6, 4)) for _ in range(3))
     res = O.bra_forward(q, k, v, np.zeros((4, 5, 5)), None, 2, 3, 2, return_probs=True)
@@ -234,8 +234,8 @@ def pin_softmax_rows_sum_to_one(O):
 
 
 def pin_route_order_invariance(O):
-    """North-star check (d): permuting the order of each row's routed regions
-    does not change the output (the softmax runs over the union)."""
+    """Route-order invariance: permuting the order of each row's routed
+    regions does not change the output (the softmax runs over the union)."""
     rng = _rng(10)
     N, H, W, C, heads, S, topk = 2, 8, 8, 4, 2, 4, 5
     q, k, v = (rng.standard_normal((N, H, W, C)) for _ in range(3))
@@ -303,7 +303,7 @@ def pin_dense_attention_matches_library(O):
 
 
 def pin_dense_attention_equals_full_routing(O):
-    """North-star check (a) from the other side: BRA with every region routed
+    """The dense-attention invariant from the other side: BRA with every region routed
     (topk = S^2, S > 1, so the keys arrive in routing order, region by region)
     equals the dense path."""
     for seed, (N, H, W, C, heads, S) in enumerate([(1, 6, 6, 8, 2, 3), (2, 4, 8, 4, 2, 2)]):
